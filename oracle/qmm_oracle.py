@@ -1,0 +1,222 @@
+"""CPU oracle for the group-wise affine u4 quantized matmul (fp64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+shares no code with the HIP library; its only common ground with it is the
+seeded input generator in `synth/`.
+
+What is computed, and where the pages state it:
+  * Weights are 4-bit integer codes in groups of 64 along the input axis, each
+    group with one bf16 scale and one bf16 bias ("Sanctum-MLX", server section:
+    4-bit QuantizedLinear with group size 64; saragossa README, quantization
+    formats: MLX affine integer weights, bf16 scales/biases, u4 at ~4.5 bits per
+    weight).  The dequantized weight is w = scale * q + bias with q in 0..15.
+  * Eight codes share one uint32 along the input axis: the fused QKV weight is
+    [q_out + 2*kv_out, hidden/8] ("The Cathedral Doubled Itself", the two
+    fusions).  Inside a word, input k = 8*w + j sits at bits 4j..4j+3
+    (least-significant nibble first).  The pages do not state the nibble order;
+    this is the reading taken, and its agreement with MLX's own order is
+    parity unpinned (no MLX code or vectors are available).
+  * Fused QKV = one matmul over the row-concatenated q/k/v weights, split into
+    Q, K, V; fused gate+up = one matmul over [gate; up] followed by
+    silu(gate) * up ("The Cathedral Doubled Itself", the two fusions).  Because
+    fusion only concatenates rows, the fused result is exactly the plain
+    definition y = x . W^T evaluated per row, which is what this module does.
+  * The routed-expert variant gathers each selected expert's rows in place from
+    a 3-D expert grid ("Sanctum-MLX", server section, switch_mlp; "Four Candles
+    for the Cathedral", what's not in this batch).
+
+Dequantization to fp64 is exact: s*q has at most 12 significant bits and the
+bias adds a few more, far below 53.  The dot product uses NumPy's fp64 matmul
+(a library primitive) on row blocks to bound memory.
+
+Tolerance (the acceptance rule for a GPU value g against oracle value y):
+    |g - y| <= 1e-3 * A,   A = sum_k |x_k| * |w_k|  (+ |lin_bias| if present)
+evaluated on the GPU's fp32 output before any bf16 rounding.  Derived outputs
+(SwiGLU, expert combine, a projection fed by an upstream GPU result) carry the
+propagated bounds computed below.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+REL_TOL = 1e-3
+# max |d/dg silu(g)| = max sigma(g) * (1 + g * (1 - sigma(g))) ~= 1.09985 (at g ~= 2.40)
+SILU_LIPSCHITZ = 1.0999
+# relative allowance for the GPU's own fp32 evaluation of silu(g) * u
+SWIGLU_EVAL_REL = 2.0 ** -20
+
+
+# ---- formats ---------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64.  A bf16 value is the top half of the
+    fp32 with the same bits, so widen to 32 bits, shift up 16 and read as fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):   # signalling NaN patterns stay NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+def unpack_u4(codes) -> np.ndarray:
+    """uint32 words [..., K/8] -> codes [..., K] (int64), least-significant nibble first."""
+    c = np.asarray(codes, dtype=np.uint32)
+    shifts = (4 * np.arange(8, dtype=np.uint32))
+    q = (c[..., None] >> shifts) & np.uint32(0xF)
+    return q.reshape(*c.shape[:-1], c.shape[-1] * 8).astype(np.int64)
+
+
+def dequant(codes, scales, biases) -> np.ndarray:
+    """W[n, k] = s[n, k // 64] * q[n, k] + b[n, k // 64] in fp64, shape [rows, K]."""
+    q = unpack_u4(codes).astype(np.float64)
+    K = q.shape[-1]
+    s = bf16_to_f64(scales)
+    b = bf16_to_f64(biases)
+    if s.shape[-1] * GROUP != K or b.shape != s.shape:
+        raise ValueError("scales/biases must be [rows, K/64]")
+    s_k = np.repeat(s, GROUP, axis=-1)
+    b_k = np.repeat(b, GROUP, axis=-1)
+    return s_k * q + b_k
+
+
+# ---- plain projection --------------------------------------------------------
+
+def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
+    """y[m, n] = sum_k x[m, k] * W[n, k] (+ lin_bias[n]); returns (y, A) in fp64.
+
+    x_bits: bf16 bits [M, K] (or [K]); codes [N, K/8]; scales/biases [N, K/64];
+    lin_bias: optional bf16 bits [N].  A is the tolerance scale sum_k |x||w|."""
+    x = bf16_to_f64(x_bits)
+    squeeze = x.ndim == 1
+    if squeeze:
+        x = x[None, :]
+    N = codes.shape[0]
+    if codes.shape[1] * 8 != x.shape[1]:
+        raise ValueError("x width must equal 8 * words per row")
+    y = np.empty((x.shape[0], N))
+    A = np.empty((x.shape[0], N))
+    ax = np.abs(x)
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
+        y[:, r0:r1] = x @ W.T
+        A[:, r0:r1] = ax @ np.abs(W).T
+    if lin_bias is not None:
+        lb = bf16_to_f64(lin_bias)
+        y += lb[None, :]
+        A += np.abs(lb)[None, :]
+    if squeeze:
+        return y[0], A[0]
+    return y, A
+
+
+def linear_tol(A) -> np.ndarray:
+    return REL_TOL * np.asarray(A)
+
+
+# ---- fused QKV -------------------------------------------------------------
+
+def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=None):
+    """Rows [0, q_out) -> Q, [q_out, q_out+kv_out) -> K, [q_out+kv_out, q_out+2kv_out) -> V.
+    Returns ((q, k, v), (tq, tk, tv)): values and per-element tolerances."""
+    if codes.shape[0] != q_out + 2 * kv_out:
+        raise ValueError("fused QKV weight must have q_out + 2*kv_out rows")
+    y, A = linear(x_bits, codes, scales, biases, lin_bias)
+    t = linear_tol(A)
+    a, b = q_out, q_out + kv_out
+    return (y[..., :a], y[..., a:b], y[..., b:]), (t[..., :a], t[..., a:b], t[..., b:])
+
+
+# ---- SwiGLU ------------------------------------------------------------------
+
+def sigmoid(g) -> np.ndarray:
+    """Logistic function, evaluated without overflow: e^{min(g,0)} / (1 + e^{-|g|})."""
+    g = np.asarray(g, dtype=np.float64)
+    return np.exp(np.minimum(g, 0.0)) / (1.0 + np.exp(-np.abs(g)))
+
+
+def silu(g) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    return g * sigmoid(g)
+
+
+def swiglu(g, u) -> np.ndarray:
+    """h = silu(gate) * up (the activation applied after the two parallel matmuls)."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def swiglu_tol(g, u, tg, tu) -> np.ndarray:
+    """Bound on |h_gpu - h| when the GPU's gate and up are within tg, tu of g, u:
+    |silu(g')u' - silu(g)u| <= L*tg*(|u|+tu) + |silu(g)|*tu, plus the GPU's fp32
+    evaluation of silu and the product (SWIGLU_EVAL_REL relative)."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    h = swiglu(g, u)
+    return (SILU_LIPSCHITZ * tg * (np.abs(u) + tu) + np.abs(silu(g)) * tu
+            + SWIGLU_EVAL_REL * (np.abs(h) + SILU_LIPSCHITZ * tg * (np.abs(u) + tu) + np.abs(silu(g)) * tu))
+
+
+def gate_up_swiglu(x_bits, codes, scales, biases, I: int):
+    """Rows [0, I) are gate, [I, 2I) are up.  Returns (h, tol_h)."""
+    if codes.shape[0] != 2 * I:
+        raise ValueError("fused gate+up weight must have 2*I rows")
+    y, A = linear(x_bits, codes, scales, biases)
+    g, u = y[..., :I], y[..., I:]
+    tg, tu = linear_tol(A[..., :I]), linear_tol(A[..., I:])
+    return swiglu(g, u), swiglu_tol(g, u, tg, tu)
+
+
+# ---- routed experts ------------------------------------------------------------
+
+def moe_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: int):
+    """Stage 1: for slot k, expert e = ids[k] in [0, E): h[k] = silu(G_e x) * (U_e x) over
+    rows [0, rows/2) (gate) and [rows/2, rows) (up) of grid[e].  An id outside [0, E)
+    means no expert: h[k] = 0.  Returns (h [topk, rows/2], tol)."""
+    E = grid_codes.shape[0]
+    I = rows // 2
+    topk = len(expert_ids)
+    h = np.zeros((topk, I))
+    t = np.zeros((topk, I))
+    for k, e in enumerate(np.asarray(expert_ids).tolist()):
+        if 0 <= e < E:
+            hk, tk = gate_up_swiglu(np.asarray(x_bits).reshape(-1), grid_codes[e], grid_scales[e],
+                                    grid_biases[e], I)
+            h[k], t[k] = hk, tk
+    return h, t
+
+
+def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, expert_w,
+                     h_err=None):
+    """Stage 2: y = sum_k p_k * (D_{ids[k]} h_k), k in increasing order; ids outside [0, E)
+    contribute nothing.  h_bits: bf16 bits [topk, K] of the stage-1 output fed to both
+    sides; p: the fp32 combine weights.  Returns (y, tol).  h_err (optional [topk, K])
+    bounds how far the h actually fed to the GPU may be from h_bits; it is propagated
+    through |D|."""
+    E = grid_codes.shape[0]
+    rows = grid_codes.shape[1]
+    y = np.zeros(rows)
+    A = np.zeros(rows)
+    extra = np.zeros(rows)
+    p = np.asarray(expert_w, dtype=np.float32).astype(np.float64)
+    for k, e in enumerate(np.asarray(expert_ids).tolist()):
+        if 0 <= e < E:
+            yk, Ak = linear(np.asarray(h_bits)[k], grid_codes[e], grid_scales[e], grid_biases[e])
+            y += p[k] * yk
+            A += abs(p[k]) * Ak
+            if h_err is not None:
+                W = dequant(grid_codes[e], grid_scales[e], grid_biases[e])
+                extra += abs(p[k]) * (np.abs(W) @ np.asarray(h_err[k], np.float64))
+    return y, linear_tol(A) + extra
+
+
+def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None):
+    """A projection whose GPU input may differ from x_bits by at most x_err per element
+    (an upstream GPU result): tolerance 1e-3*A + |W| . x_err."""
+    y, A = linear(x_bits, codes, scales, biases, lin_bias)
+    W = dequant(codes, scales, biases)
+    return y, linear_tol(A) + np.asarray(x_err, np.float64) @ np.abs(W).T
+
+
+def bf16_round_bound(v) -> np.ndarray:
+    """Largest error of rounding v to bf16 (8 significant bits): half an ulp <= 2^-8 |v|."""
+    return np.ldexp(np.abs(np.asarray(v, np.float64)), -8)

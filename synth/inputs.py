@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for the u4 group-64 affine quantized matmul.
+
+This module only draws random numbers and stores them in the formats the
+library takes as input (uint32 words of packed 4-bit codes, bf16 bit
+patterns, int32 expert ids, fp32 combine weights).  It holds none of the
+method's arithmetic: it never unpacks a code, never dequantizes and never
+forms a product.  Both the CPU oracle and the GPU path read their inputs
+from here, so it is the one piece of Python they share.
+
+Distributions (the workloads of the five decode/prefill shapes):
+  * codes: every 4-bit code uniform on 0..15, independently.  A uint32 drawn
+    uniformly on [0, 2**32) has exactly that distribution in each of its eight
+    nibbles, so words are drawn directly and no packing is performed here.
+  * scales: fp32 uniform on [0.001, 0.01], rounded to bf16 (round to nearest
+    even, done by torch's float32 -> bfloat16 cast).
+  * biases: bf16(-8 * scale), which is exact (a power-of-two multiple), so that
+    the dequantized weight is scale * (code - 8).
+  * activations: fp32 standard normal, rounded to bf16.
+  * MoE routing: distinct expert ids drawn uniformly without replacement, and
+    combine weights softmax(N(0,1) logits) computed in fp64 and cast to fp32.
+    The router is upstream of the quantized matmul; its output is an input.
+
+Every stream is seeded by numpy SeedSequence([cfg, layer, proj, field, index]).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+# proj ids
+PROJ_QKV, PROJ_GATE_UP, PROJ_DOWN, PROJ_MOE_GATE_UP, PROJ_MOE_DOWN, PROJ_LINEAR = 0, 1, 2, 3, 4, 5
+# field ids
+F_CODES, F_SCALES, F_X, F_IDS, F_LOGITS, F_LINBIAS, F_BIASES = 0, 1, 2, 3, 4, 5, 6
+
+GROUP = 64          # inputs per scale/bias group
+CODES_PER_WORD = 8  # 4-bit codes per uint32
+
+
+def rng(cfg: int, layer: int, proj: int, field: int, index: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([cfg, layer, proj, field, index]))
+
+
+def to_bf16_bits(a) -> np.ndarray:
+    """fp32/fp64 array -> bf16 bit patterns (uint16), round to nearest even (torch cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32)))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values via torch's bf16 -> fp32 cast (input plumbing only)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).float().numpy()
+
+
+@dataclass
+class U4Weight:
+    """Packed weight of `rows` output rows over `K` inputs (host arrays)."""
+    codes: np.ndarray   # uint32 [rows, K/8]
+    scales: np.ndarray  # uint16 bf16 bits [rows, K/64]
+    biases: np.ndarray  # uint16 bf16 bits [rows, K/64]
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.codes.shape[1] * CODES_PER_WORD
+
+    def slice_rows(self, r0: int, r1: int) -> "U4Weight":
+        return U4Weight(self.codes[r0:r1], self.scales[r0:r1], self.biases[r0:r1])
+
+    def take_rows(self, idx) -> "U4Weight":
+        idx = np.asarray(idx)
+        return U4Weight(self.codes[idx], self.scales[idx], self.biases[idx])
+
+    @staticmethod
+    def concat(parts) -> "U4Weight":
+        return U4Weight(np.concatenate([p.codes for p in parts]),
+                        np.concatenate([p.scales for p in parts]),
+                        np.concatenate([p.biases for p in parts]))
+
+    @staticmethod
+    def stack(parts) -> "U4Weight":
+        return U4Weight(np.stack([p.codes for p in parts]),
+                        np.stack([p.scales for p in parts]),
+                        np.stack([p.biases for p in parts]))
+
+
+def gen_weight(cfg: int, layer: int, proj: int, rows: int, K: int, index: int = 0,
+               scale_lo: float = 0.001, scale_hi: float = 0.01, bias: str = "minus8") -> U4Weight:
+    """Seeded packed weight. bias='minus8' gives bias = -8*scale (the workloads' recipe);
+    bias='uniform' draws an independent bias uniform on [-scale_hi*8, scale_hi*8] (tests only)."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 64")
+    codes = rng(cfg, layer, proj, F_CODES, index).integers(0, 2 ** 32, size=(rows, K // 8), dtype=np.uint32)
+    s32 = rng(cfg, layer, proj, F_SCALES, index).uniform(scale_lo, scale_hi, size=(rows, K // GROUP)).astype(np.float32)
+    scales = to_bf16_bits(s32)
+    if bias == "minus8":
+        biases = to_bf16_bits(-8.0 * bf16_bits_to_f32(scales))
+    elif bias == "uniform":
+        b = rng(cfg, layer, proj, F_BIASES, index).uniform(-8 * scale_hi, 8 * scale_hi, size=(rows, K // GROUP))
+        biases = to_bf16_bits(b)
+    else:
+        raise ValueError(bias)
+    return U4Weight(codes, scales, biases)
+
+
+def gen_x(cfg: int, layer: int, step: int, M: int, K: int, magnitude: str = "normal") -> np.ndarray:
+    """Seeded activations as bf16 bits [M, K]. magnitude='varied' multiplies each element
+    by 10**U(-3, 3) (the varied-magnitude projection case)."""
+    g = rng(cfg, layer, 0, F_X, step)
+    x = g.standard_normal(size=(M, K), dtype=np.float32)
+    if magnitude == "varied":
+        x = x * (10.0 ** g.uniform(-3.0, 3.0, size=(M, K))).astype(np.float32)
+    elif magnitude != "normal":
+        raise ValueError(magnitude)
+    return to_bf16_bits(x)
+
+
+def gen_lin_bias(cfg: int, layer: int, rows: int) -> np.ndarray:
+    """Seeded optional additive output bias (bf16 bits [rows]) for the QKV path."""
+    return to_bf16_bits(rng(cfg, layer, PROJ_QKV, F_LINBIAS).standard_normal(rows).astype(np.float32))
+
+
+def gen_routing(cfg: int, layer: int, step: int, E: int, topk: int):
+    """topk distinct expert ids uniform over [0, E) and fp32 softmax(N(0,1)) combine weights."""
+    ids = rng(cfg, layer, PROJ_MOE_GATE_UP, F_IDS, step).choice(E, size=topk, replace=False).astype(np.int32)
+    logits = rng(cfg, layer, PROJ_MOE_GATE_UP, F_LOGITS, step).standard_normal(topk)
+    e = np.exp(logits - logits.max())
+    p = (e / e.sum()).astype(np.float32)
+    return ids, p
+
+
+def gen_expert_grid(cfg: int, layer: int, proj: int, E: int, rows: int, K: int,
+                    experts=None) -> U4Weight:
+    """3-D expert grid [E, rows, ...]; expert e is seeded by index=e, so any subset of
+    experts can be regenerated on its own.  `experts` limits generation to a subset
+    (the others are left zero), for oracle-side regeneration."""
+    codes = np.zeros((E, rows, K // 8), np.uint32)
+    scales = np.zeros((E, rows, K // GROUP), np.uint16)
+    biases = np.zeros((E, rows, K // GROUP), np.uint16)
+    for e in (range(E) if experts is None else experts):
+        w = gen_weight(cfg, layer, proj, rows, K, index=int(e))
+        codes[e], scales[e], biases[e] = w.codes, w.scales, w.biases
+    return U4Weight(codes, scales, biases)
+
+
+# ---- workload shapes -------------------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeShape:
+    name: str
+    K: int            # hidden size (input width of QKV and gate+up)
+    q_out: int
+    kv_out: int
+    I: int            # intermediate size (gate and up each have I rows)
+
+    @property
+    def qkv_rows(self) -> int:
+        return self.q_out + 2 * self.kv_out
+
+
+TINY_QKV = DecodeShape("tiny fused QKV decode (hidden 512, q 512, kv 128)", 512, 512, 128, 0)
+DENSE_14B = DecodeShape("14B-shaped decode (hidden 5120, 40 q / 8 kv heads x 128, intermediate 13824)",
+                        5120, 5120, 1024, 13824)
+DENSE_24B = DecodeShape("24B-dense-shaped decode (hidden 5120, q 4096, kv 1024, intermediate 32768)",
+                        5120, 4096, 1024, 32768)
+PREFILL_M = 2048
+DOUBLED_Q = DecodeShape("doubled-Q QKV (hidden 5120, q 24x256x2, kv 4x256)", 5120, 12288, 1024, 0)
+
+
+@dataclass(frozen=True)
+class MoEShape:
+    name: str
+    hidden: int
+    E: int
+    I: int
+    topk: int
+
+
+MOE_35B = MoEShape("35B-A3B-shaped MoE decode (hidden 2048, 256 experts, I 512, top-8)", 2048, 256, 512, 8)
+
+# config ids used as the first seed word
+CFG_TINY, CFG_14B, CFG_24B, CFG_PREFILL, CFG_MOE, CFG_TEST = 1, 2, 3, 4, 5, 9

@@ -1,0 +1,371 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: the bf16
+field definition and torch's bf16 cast, the packing definition written in the
+forward direction, pure-Python brute force with exactly rounded sums, closed
+forms for constant codes, the row-concatenation identity of the fusions, the
+SwiGLU special values and its derivative bound, and the storage figures the
+pages print.  Each is chosen so that a plausible slip in the oracle (a dropped
+bias term, a wrong nibble order or group index, a transposed operand, Q/K/V
+offsets off by one block, a sign error in the activation) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import qmm_oracle as orc
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_bf16_bits(rng, shape, lo_exp=-8, hi_exp=3):
+    """Random finite bf16 patterns built from fields (sign, exponent, fraction)."""
+    sign = rng.integers(0, 2, size=shape)
+    exp = rng.integers(127 + lo_exp, 127 + hi_exp, size=shape)
+    frac = rng.integers(0, 128, size=shape)
+    return ((sign << 15) | (exp << 7) | frac).astype(np.uint16)
+
+
+# ---- formats -----------------------------------------------------------------
+
+def test_bf16_decode_every_pattern_matches_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = orc.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_bf16_decode_matches_field_definition():
+    for bits in list(range(0, 65536, 97)) + [0x0001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x4300, 0x7F7F, 0xFF7F]:
+        v = brute.bf16_value(bits)
+        o = float(orc.bf16_to_f64(np.array([bits], np.uint16))[0])
+        if math.isnan(v):
+            assert math.isnan(o)
+        else:
+            assert o == v, hex(bits)
+    # a few values built from fields
+    assert brute.bf16_value(brute.bf16_bits(0, 127, 0)) == 1.0
+    assert brute.bf16_value(brute.bf16_bits(1, 128, 64)) == -3.0
+    assert brute.bf16_value(brute.bf16_bits(0, 134, 5)) == 133.0
+
+
+def test_generator_bf16_rounding_is_round_to_nearest_even():
+    vals = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20], np.float32)
+    got = orc.bf16_to_f64(synth.to_bf16_bits(vals))
+    assert list(got) == [1.0, 1 + 2 ** -6, 1.0, -1.0, 1 + 2 ** -7]
+
+
+def test_unpack_inverts_the_packing_definition():
+    rng = np.random.default_rng(1)
+    q = rng.integers(0, 16, size=(5, 64))
+    words = np.array([brute.pack_row(r) for r in q], dtype=np.uint32)
+    assert np.array_equal(orc.unpack_u4(words), q)
+    # code 8w+j is nibble j of word w, least significant first
+    assert orc.unpack_u4(np.array([[0x87654321]], np.uint32)).tolist() == [[1, 2, 3, 4, 5, 6, 7, 8]]
+
+
+def test_one_hot_code_lands_on_its_row_and_input():
+    N, K = 3, 128
+    for n, k in [(0, 0), (1, 9), (2, 127), (1, 64)]:
+        q = np.zeros((N, K), int)
+        q[n, k] = 15
+        words = np.array([brute.pack_row(r) for r in q], np.uint32)
+        one = brute.bf16_bits(0, 127, 0)
+        s = np.full((N, K // 64), one, np.uint16)
+        b = np.zeros((N, K // 64), np.uint16)
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = one
+        y, _ = orc.linear(x, words, s, b)
+        expect = np.zeros((1, N))
+        expect[0, n] = 15.0
+        assert np.array_equal(y, expect)
+
+
+def test_storage_matches_the_printed_bits_per_weight():
+    fig = json.load(open(os.path.join(GOLDEN, "format_figures.json")))["bits_per_weight"]
+    rows, K = 16, 4096
+    w = synth.gen_weight(synth.CFG_TEST, 0, 0, rows, K)
+    bits = 8 * (w.codes.nbytes + w.scales.nbytes + w.biases.nbytes)
+    assert w.codes.dtype == np.uint32 and w.scales.dtype == np.uint16 and w.biases.dtype == np.uint16
+    assert bits / (rows * K) == fig["u4"]
+    assert K // w.scales.shape[1] == fig["group_size"]
+    # the oracle dequantizes exactly that layout
+    W = orc.dequant(w.codes, w.scales, w.biases)
+    assert W.shape == (rows, K)
+
+
+def test_fused_weight_shape_follows_the_printed_formula():
+    fig = json.load(open(os.path.join(GOLDEN, "format_figures.json")))
+    ex = fig["fused_qkv_weight_shape"]["example"]
+    sh = synth.DENSE_14B
+    assert (sh.K, sh.q_out, sh.kv_out) == (ex["hidden"], ex["q_out"], ex["kv_out"])
+    w = synth.gen_weight(synth.CFG_TEST, 0, 0, sh.qkv_rows, sh.K)
+    assert w.codes.shape == (ex["rows"], ex["cols"])
+    d = fig["doubled_q"]
+    assert synth.DOUBLED_Q.q_out == d["n_heads"] * d["head_dim"] * 2 == d["q_out"]
+    assert synth.DOUBLED_Q.kv_out == d["kv_heads"] * d["head_dim"] == d["kv_out"]
+    assert synth.DOUBLED_Q.K == d["hidden"]
+
+
+# ---- brute force ---------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (2, 128, 3), (3, 192, 8), (1, 128, 17), (2, 64, 8)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_oracle_matches_brute_force(M, K, N, with_bias):
+    rng = np.random.default_rng(1000 * M + 10 * K + N + with_bias)
+    q = rng.integers(0, 16, size=(N, K))
+    words = np.array([brute.pack_row(r) for r in q], np.uint32)
+    s = _rand_bf16_bits(rng, (N, K // 64))
+    b = _rand_bf16_bits(rng, (N, K // 64))
+    x = _rand_bf16_bits(rng, (M, K), -4, 4)
+    lb = _rand_bf16_bits(rng, (N,)) if with_bias else None
+    y, A = orc.linear(x, words, s, b, lin_bias=lb)
+    yb, Ab = brute.project(x.tolist(), q.tolist(), s.tolist(), b.tolist(),
+                           lin_bias_bits=None if lb is None else lb.tolist())
+    yb, Ab = np.array(yb), np.array(Ab)
+    assert np.all(np.abs(y - yb) <= 1e-12 * Ab + 1e-300)
+    assert np.allclose(A, Ab, rtol=1e-12, atol=0)
+
+
+# ---- closed forms --------------------------------------------------------------
+
+@pytest.mark.parametrize("c", [0, 1, 7, 8, 9, 15])
+def test_constant_codes_closed_form(c):
+    rng = np.random.default_rng(c)
+    N, K = 4, 256
+    words = np.full((N, K // 8), c * 0x11111111, np.uint32)
+    s = _rand_bf16_bits(rng, (N, K // 64))
+    b = _rand_bf16_bits(rng, (N, K // 64))
+    x = _rand_bf16_bits(rng, (2, K), -3, 3)
+    y, _ = orc.linear(x, words, s, b)
+    xv = [[brute.bf16_value(v) for v in row] for row in x.tolist()]
+    for m in range(2):
+        xs = [math.fsum(xv[m][64 * g:64 * g + 64]) for g in range(K // 64)]
+        for n in range(N):
+            expect = math.fsum((brute.bf16_value(int(s[n, g])) * c + brute.bf16_value(int(b[n, g]))) * xs[g]
+                               for g in range(K // 64))
+            assert abs(y[m, n] - expect) <= 1e-12 * (abs(expect) + 1e-30) + 1e-13 * sum(abs(t) for t in xv[m])
+
+
+def test_constant_codes_single_group_scale():
+    """All codes c, one scale s and bias b everywhere: y = (s*c + b) * sum(x)."""
+    K, c = 512, 11
+    one_half = brute.bf16_bits(0, 126, 0)      # 0.5
+    minus3 = brute.bf16_bits(1, 128, 64)       # -3.0
+    words = np.full((1, K // 8), c * 0x11111111, np.uint32)
+    s = np.full((1, K // 64), one_half, np.uint16)
+    b = np.full((1, K // 64), minus3, np.uint16)
+    x = synth.gen_x(synth.CFG_TEST, 0, 0, 1, K)
+    y, _ = orc.linear(x, words, s, b)
+    xsum = math.fsum(brute.bf16_value(v) for v in x[0].tolist())
+    assert abs(y[0, 0] - (0.5 * c - 3.0) * xsum) <= 1e-12 * abs(xsum) * 2.5 + 1e-12
+
+
+def test_scale_and_bias_are_not_swapped_or_dropped():
+    """codes 0 -> only the bias survives; bias 0 -> only scale*code."""
+    K = 128
+    x = np.full((1, K), brute.bf16_bits(0, 127, 0), np.uint16)   # all ones
+    two = brute.bf16_bits(0, 128, 0)
+    three = brute.bf16_bits(0, 128, 64)
+    zero_words = np.zeros((1, K // 8), np.uint32)
+    y, _ = orc.linear(x, zero_words, np.full((1, 2), two, np.uint16), np.full((1, 2), three, np.uint16))
+    assert y[0, 0] == 3.0 * K
+    ones_words = np.full((1, K // 8), 0x11111111, np.uint32)
+    y, _ = orc.linear(x, ones_words, np.full((1, 2), two, np.uint16), np.zeros((1, 2), np.uint16))
+    assert y[0, 0] == 2.0 * K
+
+
+def test_group_boundaries_are_64_wide():
+    """Different scale per group: a code at input 63 uses group 0, at input 64 group 1."""
+    K = 192
+    one = brute.bf16_bits(0, 127, 0)
+    s = np.array([[brute.bf16_bits(0, 127, 0), brute.bf16_bits(0, 128, 0), brute.bf16_bits(0, 129, 0)]], np.uint16)
+    b = np.zeros((1, 3), np.uint16)
+    for k, expect in [(0, 1.0), (63, 1.0), (64, 2.0), (127, 2.0), (128, 4.0), (191, 4.0)]:
+        q = np.zeros(K, int)
+        q[k] = 1
+        words = np.array([brute.pack_row(q)], np.uint32)
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = one
+        y, _ = orc.linear(x, words, s, b)
+        assert y[0, 0] == expect, k
+
+
+# ---- fusion identities --------------------------------------------------------
+
+def test_fused_qkv_equals_three_unfused_projections():
+    K, q_out, kv_out = 256, 96, 32
+    parts = [synth.gen_weight(synth.CFG_TEST, 1, 0, r, K, index=i, bias="uniform")
+             for i, r in enumerate([q_out, kv_out, kv_out])]
+    fused = synth.U4Weight.concat(parts)
+    lb = synth.gen_lin_bias(synth.CFG_TEST, 1, q_out + 2 * kv_out)
+    x = synth.gen_x(synth.CFG_TEST, 1, 0, 3, K)
+    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, fused.codes, fused.scales, fused.biases, q_out, kv_out, lb)
+    offs = [0, q_out, q_out + kv_out, q_out + 2 * kv_out]
+    for i, (got, tol) in enumerate([(q, tq), (k, tk), (v, tv)]):
+        ref, A = orc.linear(x, parts[i].codes, parts[i].scales, parts[i].biases, lb[offs[i]:offs[i + 1]])
+        assert np.allclose(got, ref, rtol=0, atol=1e-13 * A.max())
+        assert np.allclose(tol, 1e-3 * A, rtol=1e-14)
+
+
+def test_fused_gate_up_equals_swiglu_of_unfused():
+    K, I = 192, 40
+    gate = synth.gen_weight(synth.CFG_TEST, 2, 1, I, K, index=0, bias="uniform")
+    up = synth.gen_weight(synth.CFG_TEST, 2, 1, I, K, index=1, bias="uniform")
+    fused = synth.U4Weight.concat([gate, up])
+    x = synth.gen_x(synth.CFG_TEST, 2, 0, 2, K)
+    h, _ = orc.gate_up_swiglu(x, fused.codes, fused.scales, fused.biases, I)
+    g, _ = orc.linear(x, gate.codes, gate.scales, gate.biases)
+    u, _ = orc.linear(x, up.codes, up.scales, up.biases)
+    ref = np.array([[brute.silu(float(a)) * float(c) for a, c in zip(gr, ur)] for gr, ur in zip(g, u)])
+    assert np.allclose(h, ref, rtol=1e-13, atol=1e-300)
+    # the activation goes on the gate half: swapping the halves changes the result
+    h_swapped = orc.swiglu(u, g)
+    assert not np.allclose(h, h_swapped)
+
+
+# ---- SwiGLU -------------------------------------------------------------------
+
+def test_silu_special_values_and_library_agreement():
+    g = np.concatenate([np.linspace(-800, 800, 4001), [0.0, -0.0, 1e-300, -1e-300]])
+    ours = orc.silu(g)
+    ref = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+    assert np.all(np.isfinite(ours))
+    assert np.allclose(ours, ref, rtol=1e-14, atol=1e-300)
+    assert orc.silu(0.0) == 0.0
+    assert orc.silu(50.0) == pytest.approx(50.0, rel=1e-20)
+    assert abs(orc.silu(-50.0)) < 1e-19
+    for v in [-30.0, -2.5, -1e-3, 0.25, 3.0, 40.0]:
+        assert float(orc.silu(v)) == pytest.approx(brute.silu(v), rel=1e-15)
+
+
+def test_silu_lipschitz_constant():
+    g = np.linspace(-20, 20, 2_000_001)
+    s = orc.sigmoid(g)
+    d = s * (1 + g * (1 - s))
+    assert np.max(np.abs(d)) <= orc.SILU_LIPSCHITZ
+    assert np.max(np.abs(d)) > orc.SILU_LIPSCHITZ - 2e-4
+
+
+def test_swiglu_tolerance_covers_worst_case_perturbations():
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal(20000) * 4
+    u = rng.standard_normal(20000) * 4
+    tg = np.abs(rng.standard_normal(20000)) * 1e-2
+    tu = np.abs(rng.standard_normal(20000)) * 1e-2
+    tol = orc.swiglu_tol(g, u, tg, tu)
+    h = orc.swiglu(g, u)
+    for sg in (-1, 1):
+        for su in (-1, 1):
+            hp = orc.swiglu(g + sg * tg, u + su * tu)
+            assert np.all(np.abs(hp - h) <= tol)
+    # and it is not vacuous: the bound is within a small factor of the worst case
+    worst = np.max([np.abs(orc.swiglu(g + a * tg, u + b * tu) - h) for a in (-1, 1) for b in (-1, 1)], axis=0)
+    assert np.median(tol / np.maximum(worst, 1e-300)) < 2.0
+
+
+def test_closed_form_gate_and_up_give_known_h():
+    """Gate codes all cg, up codes all cu, scale 2^-6, bias 0, x all ones: g = 2^-6*cg*K."""
+    K, I = 128, 2
+    one = brute.bf16_bits(0, 127, 0)
+    s_bits = brute.bf16_bits(0, 121, 0)   # 2^-6
+    for cg, cu in [(0, 5), (3, 15), (15, 1)]:
+        words = np.concatenate([np.full((I, K // 8), cg * 0x11111111, np.uint32),
+                                np.full((I, K // 8), cu * 0x11111111, np.uint32)])
+        s = np.full((2 * I, K // 64), s_bits, np.uint16)
+        b = np.zeros((2 * I, K // 64), np.uint16)
+        x = np.full((1, K), one, np.uint16)
+        h, _ = orc.gate_up_swiglu(x, words, s, b, I)
+        g, u = cg * K / 64.0, cu * K / 64.0
+        expect = g / (1 + math.exp(-g)) * u
+        assert np.allclose(h, expect, rtol=1e-15)
+    assert orc.swiglu(0.0, 123.0) == 0.0
+
+
+# ---- routed experts ------------------------------------------------------------
+
+def _moe_fixture(E=6, I=64, K=128, topk=3, seed=0):
+    experts_gu = [synth.gen_weight(synth.CFG_TEST, seed, synth.PROJ_MOE_GATE_UP, 2 * I, K, index=e, bias="uniform")
+                  for e in range(E)]
+    experts_d = [synth.gen_weight(synth.CFG_TEST, seed, synth.PROJ_MOE_DOWN, K, I, index=e, bias="uniform")
+                 for e in range(E)]
+    return synth.U4Weight.stack(experts_gu), synth.U4Weight.stack(experts_d), experts_gu, experts_d
+
+
+def test_moe_single_expert_reduces_to_dense():
+    gu, d, egu, ed = _moe_fixture()
+    K, I = 128, 64
+    x = synth.gen_x(synth.CFG_TEST, 3, 0, 1, K)[0]
+    for e in range(6):
+        h, th = orc.moe_gate_up(x, gu.codes, gu.scales, gu.biases, np.array([e]), 2 * I)
+        hd, td = orc.gate_up_swiglu(x, egu[e].codes, egu[e].scales, egu[e].biases, I)
+        assert np.array_equal(h[0], hd) and np.array_equal(th[0], td)
+        hb = synth.to_bf16_bits(hd)[None, :]
+        y, t = orc.moe_down_combine(hb, d.codes, d.scales, d.biases, np.array([e]), np.array([1.0], np.float32))
+        yd, Ad = orc.linear(hb[0], ed[e].codes, ed[e].scales, ed[e].biases)
+        assert np.array_equal(y, yd) and np.allclose(t, 1e-3 * Ad)
+
+
+def test_moe_combine_is_weighted_sum_and_order_free():
+    gu, d, egu, ed = _moe_fixture()
+    K, I = 128, 64
+    x = synth.gen_x(synth.CFG_TEST, 4, 0, 1, K)[0]
+    ids = np.array([4, 1, 5], np.int32)
+    p = np.array([0.5, 0.3, 0.2], np.float32)
+    h, _ = orc.moe_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * I)
+    hb = synth.to_bf16_bits(h)
+    y, t = orc.moe_down_combine(hb, d.codes, d.scales, d.biases, ids, p)
+    ref = sum(float(p[k]) * orc.linear(hb[k], ed[e].codes, ed[e].scales, ed[e].biases)[0] for k, e in enumerate(ids))
+    assert np.allclose(y, ref, rtol=1e-14, atol=1e-14 * np.abs(ref).max())
+    perm = [2, 0, 1]
+    y2, _ = orc.moe_down_combine(hb[perm], d.codes, d.scales, d.biases, ids[perm], p[perm])
+    assert np.allclose(y, y2, rtol=1e-13, atol=1e-13 * np.abs(y).max())
+
+
+def test_moe_out_of_range_id_contributes_nothing():
+    gu, d, egu, ed = _moe_fixture()
+    K, I = 128, 64
+    x = synth.gen_x(synth.CFG_TEST, 5, 0, 1, K)[0]
+    ids = np.array([2, -1, 6], np.int32)
+    h, _ = orc.moe_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * I)
+    assert np.all(h[1] == 0) and np.all(h[2] == 0) and np.any(h[0] != 0)
+    hb = synth.to_bf16_bits(np.ones((3, I)))
+    p = np.array([0.25, 0.5, 0.25], np.float32)
+    y, _ = orc.moe_down_combine(hb, d.codes, d.scales, d.biases, ids, p)
+    y_only, _ = orc.moe_down_combine(hb[:1], d.codes, d.scales, d.biases, ids[:1], p[:1])
+    assert np.array_equal(y, y_only)
+
+
+# ---- arithmetic properties ---------------------------------------------------
+
+def test_linearity_and_zero_input():
+    w = synth.gen_weight(synth.CFG_TEST, 6, 0, 33, 320)
+    x = synth.gen_x(synth.CFG_TEST, 6, 0, 2, 320)
+    y, _ = orc.linear(x, w.codes, w.scales, w.biases)
+    x2 = synth.to_bf16_bits(2.0 * orc.bf16_to_f64(x))
+    y2, _ = orc.linear(x2, w.codes, w.scales, w.biases)
+    assert np.array_equal(y2, 2.0 * y)
+    y0, A0 = orc.linear(np.zeros_like(x), w.codes, w.scales, w.biases)
+    assert np.all(y0 == 0) and np.all(A0 == 0)
+
+
+def test_generated_workload_distribution():
+    """The seeded recipe: codes uniform on 0..15, scales in [0.001, 0.01], bias = -8*scale."""
+    w = synth.gen_weight(synth.CFG_14B, 0, 0, 512, 5120)
+    q = orc.unpack_u4(w.codes)
+    counts = np.bincount(q.ravel(), minlength=16)
+    assert counts.min() > 0.95 * q.size / 16 and counts.max() < 1.05 * q.size / 16
+    s = orc.bf16_to_f64(w.scales)
+    b = orc.bf16_to_f64(w.biases)
+    assert s.min() >= 0.001 * (1 - 2 ** -8) and s.max() <= 0.01 * (1 + 2 ** -8)
+    assert np.array_equal(b, -8 * s)
+    W = orc.dequant(w.codes, w.scales, w.biases)
+    assert np.allclose(W, s.repeat(64, axis=1) * (q - 8))
