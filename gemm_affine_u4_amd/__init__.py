@@ -1,0 +1,194 @@
+"""Python binding of libqmm.so, the MI355X group-wise affine u4 quantized matmul.
+
+Argument marshalling only: every function here forwards device pointers, sizes
+and the current HIP stream to the C ABI of the same name (include/qmm.h) and
+raises QmmError on a non-zero status.  Tensors are PyTorch device tensors used
+as plain memory: bf16 arrays may be torch.bfloat16 or 16-bit integer tensors
+holding the bit patterns, codes any 32-bit integer tensor.  The library must be
+built (gemm_affine_u4_amd.build); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_gate_up_swiglu", "qmm_moe_gather",
+           "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
+           "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
+
+QMM_OUT_BF16, QMM_OUT_F32 = 0, 1
+QMM_MOE_GATE_UP_SWIGLU, QMM_MOE_DOWN_COMBINE = 0, 1
+STATUS = {"QMM_OK": 0, "QMM_ERR_NULL": 1, "QMM_ERR_SHAPE": 2, "QMM_ERR_ALIGN": 3, "QMM_ERR_ALIAS": 4,
+          "QMM_ERR_ENUM": 5, "QMM_ERR_LAUNCH": 6}
+
+_LIB = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+_SIGNATURES = {
+    "qmm_linear": [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P],
+    "qmm_fused_qkv": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _INT, _P],
+    "qmm_fused_gate_up_swiglu": [_P, _I64, _I64, _P, _P, _P, _I64, _P, _INT, _P],
+    "qmm_moe_gather": [_INT, _P, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
+    "qmm_status_str": [_INT],
+    "qmm_abi_version": [],
+}
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {qmm_status_str(status)} (status {status})")
+
+
+def load_library():
+    """Load libqmm.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gemm_affine_u4_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "qmm_status_str" else ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def qmm_status_str(status: int) -> str:
+    return load_library().qmm_status_str(int(status)).decode()
+
+
+def qmm_abi_version() -> int:
+    return load_library().qmm_abi_version()
+
+
+def _ptr(t, what: str):
+    """Device pointer of a contiguous CUDA/HIP tensor (None -> NULL); raw ints pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _out_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return QMM_OUT_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return QMM_OUT_BF16
+    raise ValueError(f"unsupported output dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise QmmError(status, fn)
+
+
+def _mk(x):
+    """(M, K) of activations [M, K] or [K]."""
+    if x.dim() == 1:
+        return 1, x.shape[0]
+    return x.shape[0], x.shape[1]
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _elems(t) -> int:
+    return 0 if t is None else t.numel()
+
+
+def _bytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check_weight(codes, scales, biases, rows: int, K: int, what: str = "weight"):
+    """The tensors must hold exactly rows x K/8 words and rows x K/64 bf16 scales/biases,
+    so the kernels never read past the end of a caller's buffer."""
+    _need(K % 64 == 0 and K > 0, f"K={K} must be a positive multiple of 64")
+    _need(_bytes(codes) == rows * K // 2, f"{what} codes must hold {rows} x {K // 8} uint32")
+    _need(_bytes(scales) == rows * (K // 64) * 2, f"{what} scales must hold {rows} x {K // 64} bf16")
+    _need(_bytes(biases) == rows * (K // 64) * 2, f"{what} biases must hold {rows} x {K // 64} bf16")
+
+
+def qmm_linear(x, codes, scales, biases, y, lin_bias=None, stream=None) -> None:
+    """y[M, N] = x[M, K] . W^T (+ lin_bias); N = codes.shape[0], out dtype from y."""
+    M, K = _mk(x)
+    N = codes.shape[0]
+    _check_weight(codes, scales, biases, N, K)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(_elems(y) == M * N, "y must have M x N elements")
+    _need(lin_bias is None or _bytes(lin_bias) == N * 2, "lin_bias must be bf16 [N]")
+    _check(load_library().qmm_linear(_ptr(x, "x"), M, K, _ptr(codes, "codes"), _ptr(scales, "scales"),
+                                     _ptr(biases, "biases"), codes.shape[0], _ptr(lin_bias, "lin_bias"),
+                                     _ptr(y, "y"), _out_dtype(y), _stream(stream)), "qmm_linear")
+
+
+def qmm_fused_qkv(x, codes, scales, biases, q, k, v, lin_bias=None, stream=None) -> None:
+    """One matmul over [q_out + 2*kv_out] rows; q_out = q.shape[-1], kv_out = k.shape[-1]."""
+    M, K = _mk(x)
+    q_out, kv_out = q.shape[-1], k.shape[-1]
+    rows = q_out + 2 * kv_out
+    _check_weight(codes, scales, biases, rows, K)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(_elems(q) == M * q_out and _elems(k) == M * kv_out and _elems(v) == M * kv_out,
+          "q, k, v must be [M, q_out], [M, kv_out], [M, kv_out]")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    _need(lin_bias is None or _bytes(lin_bias) == rows * 2, "lin_bias must be bf16 [q_out + 2*kv_out]")
+    _check(load_library().qmm_fused_qkv(_ptr(x, "x"), M, K, _ptr(codes, "codes"), _ptr(scales, "scales"),
+                                        _ptr(biases, "biases"), q.shape[-1], k.shape[-1],
+                                        _ptr(lin_bias, "lin_bias"), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
+                                        _out_dtype(q), _stream(stream)), "qmm_fused_qkv")
+
+
+def qmm_fused_gate_up_swiglu(x, codes, scales, biases, h, stream=None) -> None:
+    """h[M, I] = silu(gate) * up over [gate; up] rows; I = h.shape[-1]."""
+    M, K = _mk(x)
+    I = h.shape[-1]
+    _check_weight(codes, scales, biases, 2 * I, K)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(_elems(h) == M * I, "h must be [M, I]")
+    _check(load_library().qmm_fused_gate_up_swiglu(_ptr(x, "x"), M, K, _ptr(codes, "codes"),
+                                                   _ptr(scales, "scales"), _ptr(biases, "biases"), h.shape[-1],
+                                                   _ptr(h, "h"), _out_dtype(h), _stream(stream)),
+           "qmm_fused_gate_up_swiglu")
+
+
+def qmm_moe_gather(stage, inp, codes, scales, biases, expert_ids, out, expert_w=None, stream=None) -> None:
+    """Routed experts gathered in place from the grid codes [E, rows, K/8]."""
+    E, rows = codes.shape[0], codes.shape[1]
+    K = inp.shape[-1]
+    topk = expert_ids.shape[0]
+    _check_weight(codes, scales, biases, E * rows, K, "expert grid")
+    _need(expert_ids.numel() == topk and expert_ids.element_size() == 4, "expert_ids must be int32 [topk]")
+    if int(stage) == QMM_MOE_GATE_UP_SWIGLU:
+        _need(_bytes(inp) == K * 2, "x must be bf16 [K]")
+        _need(_elems(out) == topk * (rows // 2), "out must be [topk, rows/2]")
+    else:
+        _need(_bytes(inp) == topk * K * 2, "h must be bf16 [topk, K]")
+        _need(_elems(out) == rows, "out must be [rows]")
+        _need(expert_w is not None and _bytes(expert_w) == topk * 4, "expert_w must be fp32 [topk]")
+    _check(load_library().qmm_moe_gather(int(stage), _ptr(inp, "in"), K, _ptr(codes, "codes"),
+                                         _ptr(scales, "scales"), _ptr(biases, "biases"), E, rows,
+                                         _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"),
+                                         expert_ids.shape[0], _ptr(out, "out"), _out_dtype(out),
+                                         _stream(stream)), "qmm_moe_gather")

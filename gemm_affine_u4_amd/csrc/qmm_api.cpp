@@ -1,0 +1,186 @@
+// C ABI entry points (declared and documented in include/qmm.h): validate, then
+// enqueue the kernel for the regime (decode GEMV for M == 1, LDS-dequant + MFMA GEMM
+// for M > 1).  Nothing here allocates, synchronises or keeps state.
+#include <hip/hip_runtime_api.h>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+#include "qmm_validate.h"
+
+using qmm::Range;
+
+namespace {
+
+uint64_t u4_code_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K) / 2; }
+uint64_t u4_group_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K / 64) * 2; }
+
+bool out_dtype_ok(int d) { return d == QMM_OUT_BF16 || d == QMM_OUT_F32; }
+size_t out_elem(int d) { return d == QMM_OUT_F32 ? 4 : 2; }
+
+int check_weight(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases) {
+  if (!x || !codes || !scales || !biases) return QMM_ERR_NULL;
+  if (!qmm::aligned(x, 16) || !qmm::aligned(codes, 16) || !qmm::aligned(scales, 2) || !qmm::aligned(biases, 2))
+    return QMM_ERR_ALIGN;
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_abi_version(void) { return QMM_ABI_VERSION; }
+
+const char* qmm_status_str(int status) {
+  switch (status) {
+    case QMM_OK: return "QMM_OK";
+    case QMM_ERR_NULL: return "QMM_ERR_NULL: a required pointer is NULL";
+    case QMM_ERR_SHAPE: return "QMM_ERR_SHAPE: unsupported or inconsistent sizes";
+    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: misaligned pointer";
+    case QMM_ERR_ALIAS: return "QMM_ERR_ALIAS: an output overlaps another output or an input";
+    case QMM_ERR_ENUM: return "QMM_ERR_ENUM: unknown out_dtype or stage";
+    case QMM_ERR_LAUNCH: return "QMM_ERR_LAUNCH: kernel launch failed";
+    default: return "QMM_ERR_UNKNOWN";
+  }
+}
+
+int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
+               const uint16_t* biases, int64_t N, const uint16_t* lin_bias, void* y, int out_dtype,
+               hipStream_t stream) {
+  if (int st = check_weight(x, codes, scales, biases)) return st;
+  if (!y) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || N > (int64_t(1) << 31)) return QMM_ERR_SHAPE;
+  if (!qmm::aligned(y, out_elem(out_dtype)) || (lin_bias && !qmm::aligned(lin_bias, 2))) return QMM_ERR_ALIGN;
+  const Range outs[] = {{y, uint64_t(M * N) * out_elem(out_dtype)}};
+  const Range ins[] = {{x, uint64_t(M * K) * 2},
+                       {codes, u4_code_bytes(N, K)},
+                       {scales, u4_group_bytes(N, K)},
+                       {biases, u4_group_bytes(N, K)},
+                       {lin_bias, lin_bias ? uint64_t(N) * 2 : 0}};
+  if (qmm::any_alias(outs, 1, ins, 5)) return QMM_ERR_ALIAS;
+
+  qmm::GemvArgs a = {};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.lin_bias = lin_bias;
+  a.out0 = y;
+  a.K = K;
+  a.rows = N;
+  a.n_out = N;
+  a.f32_out = out_dtype == QMM_OUT_F32;
+  return qmm::launch_gemv(qmm::EPI_LINEAR, a, M, stream);
+}
+
+int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
+                  const uint16_t* biases, int64_t q_out, int64_t kv_out, const uint16_t* lin_bias, void* q, void* k,
+                  void* v, int out_dtype, hipStream_t stream) {
+  if (int st = check_weight(x, codes, scales, biases)) return st;
+  if (!q || !k || !v) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  const int64_t rows = q_out + 2 * kv_out;
+  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || rows > (int64_t(1) << 31))
+    return QMM_ERR_SHAPE;
+  const size_t e = out_elem(out_dtype);
+  if (!qmm::aligned(q, e) || !qmm::aligned(k, e) || !qmm::aligned(v, e) || (lin_bias && !qmm::aligned(lin_bias, 2)))
+    return QMM_ERR_ALIGN;
+  const Range outs[] = {{q, uint64_t(M * q_out) * e}, {k, uint64_t(M * kv_out) * e}, {v, uint64_t(M * kv_out) * e}};
+  const Range ins[] = {{x, uint64_t(M * K) * 2},
+                       {codes, u4_code_bytes(rows, K)},
+                       {scales, u4_group_bytes(rows, K)},
+                       {biases, u4_group_bytes(rows, K)},
+                       {lin_bias, lin_bias ? uint64_t(rows) * 2 : 0}};
+  if (qmm::any_alias(outs, 3, ins, 5)) return QMM_ERR_ALIAS;
+
+  qmm::GemvArgs a = {};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.lin_bias = lin_bias;
+  a.out0 = q;
+  a.out1 = k;
+  a.out2 = v;
+  a.K = K;
+  a.rows = rows;
+  a.q_out = q_out;
+  a.kv_out = kv_out;
+  a.f32_out = out_dtype == QMM_OUT_F32;
+  return qmm::launch_gemv(qmm::EPI_QKV, a, M, stream);
+}
+
+int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes,
+                             const uint16_t* scales, const uint16_t* biases, int64_t I, void* h, int out_dtype,
+                             hipStream_t stream) {
+  if (int st = check_weight(x, codes, scales, biases)) return st;
+  if (!h) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || I > (int64_t(1) << 30)) return QMM_ERR_SHAPE;
+  if (!qmm::aligned(h, out_elem(out_dtype))) return QMM_ERR_ALIGN;
+  const Range outs[] = {{h, uint64_t(M * I) * out_elem(out_dtype)}};
+  const Range ins[] = {{x, uint64_t(M * K) * 2},
+                       {codes, u4_code_bytes(2 * I, K)},
+                       {scales, u4_group_bytes(2 * I, K)},
+                       {biases, u4_group_bytes(2 * I, K)}};
+  if (qmm::any_alias(outs, 1, ins, 4)) return QMM_ERR_ALIAS;
+
+  qmm::GemvArgs a = {};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.out0 = h;
+  a.K = K;
+  a.rows = 2 * I;
+  a.I = I;
+  a.n_out = I;
+  a.f32_out = out_dtype == QMM_OUT_F32;
+  return qmm::launch_gemv(qmm::EPI_SWIGLU, a, M, stream);
+}
+
+int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* codes, const uint16_t* scales,
+                   const uint16_t* biases, int64_t E, int64_t rows, const int32_t* expert_ids,
+                   const float* expert_w, int64_t topk, void* out, int out_dtype, hipStream_t stream) {
+  if (stage != QMM_MOE_GATE_UP_SWIGLU && stage != QMM_MOE_DOWN_COMBINE) return QMM_ERR_ENUM;
+  if (int st = check_weight(in, codes, scales, biases)) return st;
+  if (!expert_ids || !out || (stage == QMM_MOE_DOWN_COMBINE && !expert_w)) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  if (!qmm::k_ok(K) || E < 1 || rows < 1 || topk < 1 || topk > QMM_MAX_TOPK || E > (int64_t(1) << 24) ||
+      rows > (int64_t(1) << 30))
+    return QMM_ERR_SHAPE;
+  if (stage == QMM_MOE_GATE_UP_SWIGLU && rows % 2) return QMM_ERR_SHAPE;
+  if (stage == QMM_MOE_DOWN_COMBINE && K > 5120) return QMM_ERR_SHAPE;
+  const size_t e = out_elem(out_dtype);
+  if (!qmm::aligned(out, e) || !qmm::aligned(expert_ids, 4) || (expert_w && !qmm::aligned(expert_w, 4)))
+    return QMM_ERR_ALIGN;
+  const int64_t in_elems = stage == QMM_MOE_GATE_UP_SWIGLU ? K : topk * K;
+  const int64_t out_elems = stage == QMM_MOE_GATE_UP_SWIGLU ? topk * (rows / 2) : rows;
+  const Range outs[] = {{out, uint64_t(out_elems) * e}};
+  const Range ins[] = {{in, uint64_t(in_elems) * 2},
+                       {codes, u4_code_bytes(E * rows, K)},
+                       {scales, u4_group_bytes(E * rows, K)},
+                       {biases, u4_group_bytes(E * rows, K)},
+                       {expert_ids, uint64_t(topk) * 4},
+                       {expert_w, expert_w ? uint64_t(topk) * 4 : 0}};
+  if (qmm::any_alias(outs, 1, ins, 6)) return QMM_ERR_ALIAS;
+
+  qmm::GemvArgs a = {};
+  a.x = in;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.out0 = out;
+  a.K = K;
+  a.rows = rows;
+  a.I = rows / 2;
+  a.expert_ids = expert_ids;
+  a.expert_w = expert_w;
+  a.E = E;
+  a.topk = int(topk);
+  a.f32_out = out_dtype == QMM_OUT_F32;
+  if (stage == QMM_MOE_GATE_UP_SWIGLU) return qmm::launch_moe_gate_up(a, stream);
+  return qmm::launch_moe_down(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Device helpers shared by the u4 group-64 affine kernels (gfx950 / CDNA4).
+//
+// Weight format (the library's input contract): eight 4-bit codes per uint32
+// along the input axis, code k of a row at bits 4*(k%8)..+3 of word k/8, and one
+// bf16 scale and one bf16 bias per 64 inputs, w = scale*q + bias.  The 4-bit,
+// group-64, bf16 scale/bias format is stated in "Sanctum-MLX" (server section)
+// and the saragossa README (quantization formats); the hidden/8 packing in
+// "The Cathedral Doubled Itself" (the two fusions).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagicPair = 0x43004300u;  // bf16 pair (128.0, 128.0)
+constexpr uint32_t kNibblePair = 0x000F000Fu;
+
+// Keep a constant in a VGPR so that v_and_or_b32 can take it alongside an SGPR mask
+// (a gfx9 VOP3 instruction reads at most one scalar operand and no literal).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Nibble pair t (t = 0..3) of a code word as the exact bf16 pair (128+q_t, 128+q_{t+4}):
+// the bf16 pattern 0x43 0x0q is 128 + q, since the ulp at 128 is 1.
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int t, uint32_t magic) {
+  return ((w >> (4 * t)) & kNibblePair) | magic;
+}
+
+// Activations of one 32-code chunk, permuted to match nib_pair: xp[4*j + t] holds
+// (x[8j+t], x[8j+t+4]) for word j = 0..3, t = 0..3.  d[m] holds (x[2m], x[2m+1]).
+__device__ __forceinline__ void permute_chunk(const uint32_t d[16], uint32_t xp[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    xp[4 * j + 0] = __builtin_amdgcn_perm(d[4 * j + 2], d[4 * j + 0], 0x05040100u);
+    xp[4 * j + 1] = __builtin_amdgcn_perm(d[4 * j + 2], d[4 * j + 0], 0x07060302u);
+    xp[4 * j + 2] = __builtin_amdgcn_perm(d[4 * j + 3], d[4 * j + 1], 0x05040100u);
+    xp[4 * j + 3] = __builtin_amdgcn_perm(d[4 * j + 3], d[4 * j + 1], 0x07060302u);
+  }
+}
+
+// Sum of the 32 activations of a chunk, by the same chain of dot2 operations (against
+// (1,1)) that chunk_dot128 uses against (128+q).  With all codes zero the two chains
+// differ by an exact factor 128, so q == 0 yields exactly zero after subtraction.
+__device__ __forceinline__ float chunk_xsum(const uint32_t xp[16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s = dot2_bf16(xp[i], 0x3F803F80u, s);
+  return s;
+}
+
+// sum_k x_k * (128 + q_k) over one chunk (four code words), fp32.
+__device__ __forceinline__ float chunk_dot128(const uint32_t w[4], const uint32_t xp[16], uint32_t magic) {
+  float d = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) d = dot2_bf16(nib_pair(w[j], t, magic), xp[4 * j + t], d);
+  }
+  return d;
+}
+
+// Sum over the LPR lanes of each row slot (LPR = 16 or 32) with DPP.  After return the
+// slot's total is in every lane of its last 16-lane row (lanes 16*r + 15 - ... of row r).
+template <int LPR>
+__device__ __forceinline__ float slot_reduce(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  if constexpr (LPR == 32) {
+    // row_bcast:15 into rows 1 and 3: row 1 = row0 + row1, row 3 = row2 + row3
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  }
+  return v;
+}
+
+// Lane (within the wave) that holds slot s's total after slot_reduce.
+template <int LPR>
+__device__ __forceinline__ constexpr int slot_result_lane(int s) {
+  return LPR == 32 ? 32 * s + 16 : 16 * s;
+}
+
+__device__ __forceinline__ float silu_times(float g, float u) {
+  // silu(g) * u with silu(g) = g / (1 + e^-g); e^-g -> inf gives -0, e^-g -> 0 gives g.
+  return g / (1.0f + expf(-g)) * u;
+}
+
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool f32) {
+  if (f32) {
+    static_cast<float*>(out)[idx] = v;
+  } else {
+    static_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(v);
+  }
+}
+
+}  // namespace qmm

@@ -209,12 +209,39 @@ def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, e
     return y, linear_tol(A) + extra
 
 
-def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None):
+def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None, row_block: int = 1024):
     """A projection whose GPU input may differ from x_bits by at most x_err per element
     (an upstream GPU result): tolerance 1e-3*A + |W| . x_err."""
     y, A = linear(x_bits, codes, scales, biases, lin_bias)
-    W = dequant(codes, scales, biases)
-    return y, linear_tol(A) + np.asarray(x_err, np.float64) @ np.abs(W).T
+    e = np.asarray(x_err, np.float64)
+    extra = np.empty_like(y)
+    N = codes.shape[0]
+    for r0 in range(0, N, row_block):
+        r1 = min(N, r0 + row_block)
+        W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
+        extra[..., r0:r1] = e @ np.abs(W).T
+    return y, linear_tol(A) + extra
+
+
+def f32_to_bf16_bits(v) -> np.ndarray:
+    """Round fp64/fp32 values to fp32 and then to bf16 (round to nearest, ties to even)
+    by integer arithmetic on the fp32 bit pattern; NaN is not expected here."""
+    b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_input_error(h, tol) -> np.ndarray:
+    """Bound on |RNE(h_gpu) - RNE(h)| when |h_gpu - h| <= tol, for the bf16 copy of an
+    upstream result that a downstream projection reads.  Rounding is monotonic, so the
+    GPU's rounded value lies between RNE(h - tol) and RNE(h + tol)."""
+    h = np.asarray(h, np.float64)
+    tol = np.asarray(tol, np.float64)
+    mid = bf16_to_f64(f32_to_bf16_bits(h))
+    lo = bf16_to_f64(f32_to_bf16_bits(h - tol))
+    hi = bf16_to_f64(f32_to_bf16_bits(h + tol))
+    # the fp32 rounding of h +- tol on the way may shift by half an fp32 ulp; widen by it
+    return np.maximum(np.abs(mid - lo), np.abs(hi - mid)) + np.ldexp(np.abs(h) + tol, -24)
 
 
 def bf16_round_bound(v) -> np.ndarray:

@@ -1,0 +1,163 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before anything is enqueued.  No call
+here reaches a kernel launch: every argument set is invalid on purpose, and the
+range logic is exercised through a host-only build of the validation code."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gemm_affine_u4_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+CSRC = os.path.join(ROOT, "gemm_affine_u4_amd", "csrc")
+
+A = 1 << 20  # a 16-byte aligned fake device address; never dereferenced (every call below fails validation)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qmm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["qmm_linear", "qmm_fused_qkv", "qmm_fused_gate_up_swiglu",
+                                           "qmm_moe_gather", "qmm_status_str", "qmm_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qmm.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qmm.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (qmm_\w+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings():
+    assert qmm.qmm_abi_version() == 1
+    for name, code in qmm.STATUS.items():
+        assert qmm.qmm_status_str(code).startswith(name)
+    assert qmm.qmm_status_str(99) == "QMM_ERR_UNKNOWN"
+
+
+def _linear(x=A, M=1, K=512, codes=A + (1 << 16), s=A + (1 << 18), b=A + (1 << 19), N=64, lb=None,
+            y=A + (1 << 21), od=0):
+    return qmm.load_library().qmm_linear(x, M, K, codes, s, b, N, lb, y, od, None)
+
+
+def _qkv(x=A, M=1, K=512, codes=A + (1 << 16), s=A + (1 << 18), b=A + (1 << 19), qo=64, kvo=16, lb=None,
+         q=A + (1 << 21), k=A + (1 << 21) + 4096, v=A + (1 << 21) + 8192, od=0):
+    return qmm.load_library().qmm_fused_qkv(x, M, K, codes, s, b, qo, kvo, lb, q, k, v, od, None)
+
+
+S = qmm.STATUS
+
+
+def test_null_pointers():
+    assert _linear(x=None) == S["QMM_ERR_NULL"]
+    assert _linear(codes=None) == S["QMM_ERR_NULL"]
+    assert _linear(y=None) == S["QMM_ERR_NULL"]
+    assert _qkv(k=None) == S["QMM_ERR_NULL"]
+    lib = qmm.load_library()
+    assert lib.qmm_fused_gate_up_swiglu(A, 1, 512, A + 65536, None, A + 2 ** 19, 8, A + 2 ** 21, 0, None) == 1
+    # stage 2 needs combine weights
+    assert lib.qmm_moe_gather(1, A, 512, A + 65536, A + 2 ** 18, A + 2 ** 19, 4, 64, A + 2 ** 22, None, 2,
+                              A + 2 ** 21, 0, None) == S["QMM_ERR_NULL"]
+
+
+@pytest.mark.parametrize("K", [0, 32, 100, 96, 65536 + 64, -64])
+def test_bad_K(K):
+    assert _linear(K=K) == S["QMM_ERR_SHAPE"]
+
+
+def test_bad_sizes():
+    assert _linear(M=0) == S["QMM_ERR_SHAPE"]
+    assert _linear(N=0) == S["QMM_ERR_SHAPE"]
+    assert _qkv(qo=0) == S["QMM_ERR_SHAPE"]
+    assert _qkv(kvo=0) == S["QMM_ERR_SHAPE"]
+    lib = qmm.load_library()
+    # topk out of range, odd gate+up rows, stage-2 K too large
+    assert lib.qmm_moe_gather(0, A, 512, A + 65536, A + 2 ** 18, A + 2 ** 19, 4, 64, A + 2 ** 22, None, 0,
+                              A + 2 ** 21, 0, None) == S["QMM_ERR_SHAPE"]
+    assert lib.qmm_moe_gather(0, A, 512, A + 65536, A + 2 ** 18, A + 2 ** 19, 4, 63, A + 2 ** 22, None, 2,
+                              A + 2 ** 21, 0, None) == S["QMM_ERR_SHAPE"]
+    assert lib.qmm_moe_gather(1, A, 8192, A + 65536, A + 2 ** 18, A + 2 ** 19, 4, 64, A + 2 ** 22,
+                              A + 2 ** 23, 2, A + 2 ** 21, 0, None) == S["QMM_ERR_SHAPE"]
+
+
+def test_bad_enums():
+    assert _linear(od=2) == S["QMM_ERR_ENUM"]
+    lib = qmm.load_library()
+    assert lib.qmm_moe_gather(7, A, 512, A + 65536, A + 2 ** 18, A + 2 ** 19, 4, 64, A + 2 ** 22, None, 2,
+                              A + 2 ** 21, 0, None) == S["QMM_ERR_ENUM"]
+
+
+def test_misaligned():
+    assert _linear(x=A + 2) == S["QMM_ERR_ALIGN"]
+    assert _linear(codes=A + (1 << 16) + 4) == S["QMM_ERR_ALIGN"]
+    assert _linear(s=A + (1 << 18) + 1) == S["QMM_ERR_ALIGN"]
+    assert _linear(y=A + (1 << 21) + 1) == S["QMM_ERR_ALIGN"]
+    assert _linear(y=A + (1 << 21) + 2, od=1) == S["QMM_ERR_ALIGN"]   # fp32 output needs 4 bytes
+    assert _linear(lb=A + (1 << 20) + 1) == S["QMM_ERR_ALIGN"]
+
+
+def test_overlapping_outputs_and_inputs_are_rejected():
+    # the split-view trap: K and V inside one buffer, overlapping
+    assert _qkv(k=A + (1 << 21) + 100, v=A + (1 << 21) + 128) == S["QMM_ERR_ALIAS"]
+    # Q overlapping K
+    assert _qkv(q=A + (1 << 21), k=A + (1 << 21) + 64) == S["QMM_ERR_ALIAS"]
+    # output on top of the activations or the weight
+    assert _linear(y=A) == S["QMM_ERR_ALIAS"]
+    assert _linear(y=A + (1 << 16) + 512) == S["QMM_ERR_ALIAS"]
+    assert _linear(y=A + (1 << 19) + 16) == S["QMM_ERR_ALIAS"]
+
+
+# ---- host-only build of the validation code ------------------------------------
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    d = tmp_path_factory.mktemp("shim")
+    so = str(d / "libqmm_validate_host.so")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-I", CSRC,
+           os.path.join(CSRC, "qmm_validate.cpp"), os.path.join(ROOT, "tests", "validate_shim.cpp"), "-o", so]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lib = ctypes.CDLL(so)
+    lib.shim_aligned.argtypes = [ctypes.c_void_p, ctypes.c_ulong]
+    lib.shim_k_ok.argtypes = [ctypes.c_longlong]
+    arr = ctypes.POINTER(ctypes.c_ulonglong)
+    lib.shim_any_alias.argtypes = [arr, ctypes.c_int, arr, ctypes.c_int]
+    return lib
+
+
+def _ranges(pairs):
+    flat = [v for p in pairs for v in p]
+    return (ctypes.c_ulonglong * max(1, len(flat)))(*flat), len(pairs)
+
+
+def _alias(shim, outs, ins):
+    o, no = _ranges(outs)
+    i, ni = _ranges(ins)
+    return shim.shim_any_alias(o, no, i, ni)
+
+
+def test_range_logic_touching_is_not_overlap(shim):
+    assert _alias(shim, [(1000, 100), (1100, 50)], []) == 0          # adjacent outputs
+    assert _alias(shim, [(1000, 100), (1099, 50)], []) == 1          # one byte shared
+    assert _alias(shim, [(1000, 100)], [(900, 100)]) == 0            # input ends where output starts
+    assert _alias(shim, [(1000, 100)], [(900, 101)]) == 1
+    assert _alias(shim, [(1000, 100)], [(1050, 1)]) == 1             # input inside output
+    assert _alias(shim, [(1000, 100)], [(0, 0), (5000, 10)]) == 0    # null / disjoint inputs
+    assert _alias(shim, [(1000, 0)], [(1000, 10)]) == 0              # empty output range
+    assert _alias(shim, [(1000, 10), (2000, 10), (1005, 1)], []) == 1
+
+
+def test_alignment_and_k_rules(shim):
+    assert shim.shim_aligned(4096, 16) == 1 and shim.shim_aligned(4104, 16) == 0 and shim.shim_aligned(4104, 8) == 1
+    for K, ok in [(64, 1), (128, 1), (65536, 1), (65600, 0), (0, 0), (63, 0), (96, 0), (-64, 0)]:
+        assert shim.shim_k_ok(K) == ok, K

@@ -1,0 +1,204 @@
+"""GPU parity of the decode path (M = 1 GEMV) against the fp64 oracle.
+
+Acceptance: |gpu_fp32 - oracle| <= 1e-3 * sum_k |x_k w_k| per element (propagated
+bounds for SwiGLU), on the fp32 output before bf16 rounding; the bf16 output must
+equal RNE(fp32 output) bit for bit; fused outputs equal the unfused projection on
+the same row slice bit for bit; no write lands outside an output buffer."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_affine_u4_amd as qmm
+import synth
+from oracle import qmm_oracle as orc
+from gpu_util import Guarded, assert_within, dev, dev_weight, rne_bits_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_qkv(x, w, q_out, kv_out, f32=True, lin_bias=None):
+    M = x.shape[0]
+    outs = [Guarded((M, n), f32) for n in (q_out, kv_out, kv_out)]
+    c, s, b = dev_weight(w)
+    qmm.qmm_fused_qkv(dev(x), c, s, b, outs[0].t, outs[1].t, outs[2].t,
+                      lin_bias=None if lin_bias is None else dev(lin_bias))
+    torch.cuda.synchronize()
+    return [o.values() for o in outs]
+
+
+def run_linear(x, w, f32=True, lin_bias=None):
+    y = Guarded((x.shape[0], w.rows), f32)
+    c, s, b = dev_weight(w)
+    qmm.qmm_linear(dev(x), c, s, b, y.t, lin_bias=None if lin_bias is None else dev(lin_bias))
+    torch.cuda.synchronize()
+    return y.values()
+
+
+def run_gate_up(x, w, I, f32=True):
+    h = Guarded((x.shape[0], I), f32)
+    c, s, b = dev_weight(w)
+    qmm.qmm_fused_gate_up_swiglu(dev(x), c, s, b, h.t)
+    torch.cuda.synchronize()
+    return h.values()
+
+
+# ---- fused QKV -----------------------------------------------------------------
+
+QKV_CASES = [
+    # (name, K, q_out, kv_out)
+    ("tiny fused QKV decode", synth.TINY_QKV.K, synth.TINY_QKV.q_out, synth.TINY_QKV.kv_out),
+    ("14B-shaped fused QKV", synth.DENSE_14B.K, synth.DENSE_14B.q_out, synth.DENSE_14B.kv_out),
+    ("24B-shaped fused QKV", synth.DENSE_24B.K, synth.DENSE_24B.q_out, synth.DENSE_24B.kv_out),
+    ("doubled-Q fused QKV", synth.DOUBLED_Q.K, synth.DOUBLED_Q.q_out, synth.DOUBLED_Q.kv_out),
+    ("ragged K=64", 64, 5, 3),
+    ("ragged K=576", 576, 33, 7),
+    ("ragged K=1088", 1088, 17, 1),
+    ("ragged K=5184 (split over 8 waves)", 5184, 40, 9),
+    ("K=8192 (split over 8 waves)", 8192, 64, 32),
+    ("K=45056 (split over 16 waves)", 45056, 12, 2),
+]
+
+
+@pytest.mark.parametrize("name,K,q_out,kv_out", QKV_CASES, ids=[c[0] for c in QKV_CASES])
+def test_fused_qkv_matches_oracle(name, K, q_out, kv_out):
+    say(f"[qkv] {name}: K={K} q_out={q_out} kv_out={kv_out}")
+    w = synth.gen_weight(synth.CFG_TEST, K, synth.PROJ_QKV, q_out + 2 * kv_out, K)
+    x = synth.gen_x(synth.CFG_TEST, K, 0, 1, K)
+    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, w.codes, w.scales, w.biases, q_out, kv_out)
+    g = run_qkv(x, w, q_out, kv_out, f32=True)
+    for got, ref, tol, nm in zip(g, (q, k, v), (tq, tk, tv), "QKV"):
+        assert_within(got, ref, tol, f"{name} {nm}")
+    gb = run_qkv(x, w, q_out, kv_out, f32=False)
+    for got32, got16, nm in zip(g, gb, "QKV"):
+        assert np.array_equal(got16, rne_bits_of(got32)), f"{nm}: bf16 output != RNE(fp32 output)"
+
+
+def test_fused_qkv_equals_unfused_bitwise():
+    sh = synth.DENSE_14B
+    say("[qkv] fused vs three unfused projections, 14B shape")
+    w = synth.gen_weight(synth.CFG_14B, 0, synth.PROJ_QKV, sh.qkv_rows, sh.K)
+    x = synth.gen_x(synth.CFG_14B, 0, 0, 1, sh.K)
+    fused = run_qkv(x, w, sh.q_out, sh.kv_out)
+    offs = [0, sh.q_out, sh.q_out + sh.kv_out, sh.qkv_rows]
+    for i in range(3):
+        part = run_linear(x, w.slice_rows(offs[i], offs[i + 1]))
+        assert np.array_equal(part.view(np.uint64), fused[i].view(np.uint64)), f"part {i} differs"
+
+
+def test_fused_qkv_with_linear_bias_and_varied_magnitude():
+    K, q_out, kv_out = 2048, 96, 32
+    say("[qkv] additive bias, x = N(0,1) * 10^U(-3,3)")
+    w = synth.gen_weight(synth.CFG_TEST, 7, synth.PROJ_QKV, q_out + 2 * kv_out, K, bias="uniform")
+    x = synth.gen_x(synth.CFG_TEST, 7, 0, 1, K, magnitude="varied")
+    lb = synth.gen_lin_bias(synth.CFG_TEST, 7, q_out + 2 * kv_out)
+    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, w.codes, w.scales, w.biases, q_out, kv_out, lb)
+    g = run_qkv(x, w, q_out, kv_out, lin_bias=lb)
+    for got, ref, tol, nm in zip(g, (q, k, v), (tq, tk, tv), "QKV"):
+        assert_within(got, ref, tol, f"bias+varied {nm}")
+
+
+def test_multi_row_activations():
+    K, N, M = 1024, 70, 3
+    say(f"[linear] M={M}")
+    w = synth.gen_weight(synth.CFG_TEST, 8, synth.PROJ_LINEAR, N, K)
+    x = synth.gen_x(synth.CFG_TEST, 8, 0, M, K)
+    y, A = orc.linear(x, w.codes, w.scales, w.biases)
+    got = run_linear(x, w)
+    assert_within(got, y, 1e-3 * A, "linear M=3")
+    for m in range(M):
+        assert np.array_equal(run_linear(x[m:m + 1], w)[0], got[m]), f"row {m}"
+
+
+# ---- special cases -------------------------------------------------------------------
+
+def test_zero_codes_zero_bias_and_zero_input_give_exact_zero():
+    K, N = 5120, 64
+    say("[linear] exact zeros")
+    w = synth.gen_weight(synth.CFG_TEST, 9, synth.PROJ_LINEAR, N, K)
+    x = synth.gen_x(synth.CFG_TEST, 9, 0, 1, K)
+    zero_codes = synth.U4Weight(np.zeros_like(w.codes), w.scales, np.zeros_like(w.biases))
+    assert np.all(run_linear(x, zero_codes) == 0.0)
+    assert np.all(run_linear(np.zeros_like(x), w) == 0.0)
+
+
+def test_linearity_is_exact():
+    K, N = 5120, 200
+    say("[linear] y(2x) == 2 y(x)")
+    w = synth.gen_weight(synth.CFG_TEST, 10, synth.PROJ_LINEAR, N, K)
+    x = synth.gen_x(synth.CFG_TEST, 10, 0, 1, K)
+    x2 = orc.f32_to_bf16_bits(2.0 * orc.bf16_to_f64(x))
+    assert np.array_equal(run_linear(x2, w), 2.0 * run_linear(x, w))
+
+
+def test_constant_codes_closed_form():
+    K, N = 2048, 40
+    say("[linear] constant codes")
+    for c in (0, 3, 8, 15):
+        w = synth.gen_weight(synth.CFG_TEST, 11, synth.PROJ_LINEAR, N, K)
+        w = synth.U4Weight(np.full_like(w.codes, c * 0x11111111), w.scales, w.biases)
+        x = synth.gen_x(synth.CFG_TEST, 11, c, 1, K)
+        y, A = orc.linear(x, w.codes, w.scales, w.biases)
+        assert_within(run_linear(x, w), y, 1e-3 * A, f"codes={c}")
+
+
+def test_one_hot_code_position():
+    """A single code 15 at (n, k) with x = e_k and scale 1, bias 0: only y[n] = 15."""
+    K, N = 256, 8
+    one = 0x3F80
+    for n, k in [(0, 0), (3, 5), (7, 255), (5, 64), (2, 131)]:
+        q = np.zeros((N, K), np.uint64)
+        q[n, k] = 15
+        words = np.zeros((N, K // 8), np.uint64)
+        for j in range(8):
+            words |= q[:, j::8] << np.uint64(4 * j)
+        w = synth.U4Weight(words.astype(np.uint32), np.full((N, K // 64), one, np.uint16),
+                           np.zeros((N, K // 64), np.uint16))
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = one
+        y = run_linear(x, w)
+        expect = np.zeros((1, N))
+        expect[0, n] = 15.0
+        assert np.array_equal(y, expect), (n, k)
+
+
+def test_repeat_calls_are_bitwise_deterministic():
+    sh = synth.DENSE_14B
+    w = synth.gen_weight(synth.CFG_14B, 1, synth.PROJ_GATE_UP, 2 * 512, sh.K)
+    x = synth.gen_x(synth.CFG_14B, 1, 0, 1, sh.K)
+    a = run_gate_up(x, w, 512)
+    b = run_gate_up(x, w, 512)
+    assert np.array_equal(a, b)
+
+
+# ---- fused gate+up + SwiGLU ------------------------------------------------------------
+
+GU_CASES = [
+    ("14B-shaped gate+up", synth.DENSE_14B.K, synth.DENSE_14B.I),
+    ("K=512 I=1", 512, 1),
+    ("K=2048 I=33", 2048, 33),
+    ("K=64 I=5", 64, 5),
+    ("K=8192 I=48 (split)", 8192, 48),
+]
+
+
+@pytest.mark.parametrize("name,K,I", GU_CASES, ids=[c[0] for c in GU_CASES])
+def test_gate_up_swiglu_matches_oracle(name, K, I):
+    say(f"[gate+up] {name}")
+    w = synth.gen_weight(synth.CFG_TEST, 20 + K, synth.PROJ_GATE_UP, 2 * I, K)
+    x = synth.gen_x(synth.CFG_TEST, 20 + K, 0, 1, K)
+    h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, I)
+    g = run_gate_up(x, w, I)
+    assert_within(g, h, th, name)
+    gb = run_gate_up(x, w, I, f32=False)
+    assert np.array_equal(gb, rne_bits_of(g)), "bf16 output != RNE(fp32 output)"
+
+
+def test_gate_up_equals_swiglu_of_unfused_rows():
+    K, I = 5120, 256
+    w = synth.gen_weight(synth.CFG_TEST, 30, synth.PROJ_GATE_UP, 2 * I, K, bias="uniform")
+    x = synth.gen_x(synth.CFG_TEST, 30, 0, 1, K)
+    h = run_gate_up(x, w, I)
+    g = run_linear(x, w.slice_rows(0, I))
+    u = run_linear(x, w.slice_rows(I, 2 * I))
+    ref = orc.swiglu(g, u)
+    assert np.all(np.abs(h - ref) <= 2.0 ** -20 * np.abs(ref) + 1e-30)

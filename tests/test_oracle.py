@@ -369,3 +369,23 @@ def test_generated_workload_distribution():
     assert np.array_equal(b, -8 * s)
     W = orc.dequant(w.codes, w.scales, w.biases)
     assert np.allclose(W, s.repeat(64, axis=1) * (q - 8))
+
+
+def test_oracle_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(11)
+    v = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.uniform(-30, 30, 100000),
+                        [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0, 3.3895e38]])
+    ours = orc.f32_to_bf16_bits(v)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_input_error_bounds_every_rounding_of_a_nearby_value():
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal(20000) * 3
+    tol = np.abs(rng.standard_normal(20000)) * 1e-3
+    bound = orc.bf16_input_error(h, tol)
+    base = orc.bf16_to_f64(orc.f32_to_bf16_bits(h))
+    for f in (-1.0, -0.5, 0.0, 0.5, 1.0):
+        got = orc.bf16_to_f64(orc.f32_to_bf16_bits(h + f * tol))
+        assert np.all(np.abs(got - base) <= bound)
