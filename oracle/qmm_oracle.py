@@ -31,10 +31,14 @@ bias adds a few more, far below 53.  The dot product uses NumPy's fp64 matmul
 (a library primitive) on row blocks to bound memory.
 
 Tolerance (the acceptance rule for a GPU value g against oracle value y):
-    |g - y| <= 1e-3 * A,   A = sum_k |x_k| * |w_k|  (+ |lin_bias| if present)
-evaluated on the GPU's fp32 output before any bf16 rounding.  Derived outputs
-(SwiGLU, expert combine, a projection fed by an upstream GPU result) carry the
-propagated bounds computed below.
+    |g - y| <= 1e-3 * A + 2^-12 * S,
+    A = sum_k |x_k| * |w_k|  (+ |lin_bias| if present),  S = sum_k |x_k| * |s_k|,
+evaluated on the GPU's fp32 output before any bf16 rounding.  The first term is
+the stated rule; the second is an fp32 evaluation floor that only matters for
+rows whose weights are (nearly) all exactly zero while their codes are not (see
+`tolerance`); for the workloads' inputs it is below 1e-4 of the first.  Derived
+outputs (SwiGLU, expert combine, a projection fed by an upstream GPU result)
+carry the propagated bounds computed below.
 """
 from __future__ import annotations
 
@@ -42,6 +46,7 @@ import numpy as np
 
 GROUP = 64
 REL_TOL = 1e-3
+EVAL_FLOOR = 2.0 ** -12
 # max |d/dg silu(g)| = max sigma(g) * (1 + g * (1 - sigma(g))) ~= 1.09985 (at g ~= 2.40)
 SILU_LIPSCHITZ = 1.0999
 # relative allowance for the GPU's own fp32 evaluation of silu(g) * u
@@ -81,21 +86,27 @@ def dequant(codes, scales, biases) -> np.ndarray:
 
 # ---- plain projection --------------------------------------------------------
 
-def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
-    """y[m, n] = sum_k x[m, k] * W[n, k] (+ lin_bias[n]); returns (y, A) in fp64.
-
+def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
+    """y[m, n] = sum_k x[m, k] * W[n, k] (+ lin_bias[n]) in fp64, with the two magnitude
+    sums the tolerance is built from:
+      A[m, n] = sum_k |x[m, k]| * |W[n, k]|  (+ |lin_bias[n]|)
+      S[m, n] = sum_k |x[m, k]| * |s[n, k // 64]|   (activation mass weighted by the scale,
+                                                     i.e. the size of a one-code change)
     x_bits: bf16 bits [M, K] (or [K]); codes [N, K/8]; scales/biases [N, K/64];
-    lin_bias: optional bf16 bits [N].  A is the tolerance scale sum_k |x||w|."""
+    lin_bias: optional bf16 bits [N]."""
     x = bf16_to_f64(x_bits)
     squeeze = x.ndim == 1
     if squeeze:
         x = x[None, :]
     N = codes.shape[0]
-    if codes.shape[1] * 8 != x.shape[1]:
+    K = x.shape[1]
+    if codes.shape[1] * 8 != K:
         raise ValueError("x width must equal 8 * words per row")
     y = np.empty((x.shape[0], N))
     A = np.empty((x.shape[0], N))
     ax = np.abs(x)
+    xg = ax.reshape(x.shape[0], K // GROUP, GROUP).sum(axis=2)          # [M, K/64]
+    S = xg @ np.abs(bf16_to_f64(scales)).T
     for r0 in range(0, N, row_block):
         r1 = min(N, r0 + row_block)
         W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
@@ -106,12 +117,23 @@ def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
         y += lb[None, :]
         A += np.abs(lb)[None, :]
     if squeeze:
-        return y[0], A[0]
-    return y, A
+        return y[0], A[0], S[0]
+    return y, A, S
 
 
-def linear_tol(A) -> np.ndarray:
-    return REL_TOL * np.asarray(A)
+def tolerance(A, S) -> np.ndarray:
+    """Acceptance bound of one projection output: 1e-3 * sum|x w| (the stated rule), plus
+    an fp32 evaluation floor of 2^-12 * sum|x| |s| -- 1/4096 of the effect of moving every
+    code of the row by one step.  The floor only matters when sum|x w| is (near) zero
+    while the codes are not: with every weight exactly s*q + b = 0 the stated rule would
+    demand an exact zero, which no fp32 evaluation of s*sum(x q) + b*sum(x) can promise."""
+    return REL_TOL * np.asarray(A) + EVAL_FLOOR * np.asarray(S)
+
+
+def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
+    """(y, tol) of one projection; tol per `tolerance`."""
+    y, A, S = project(x_bits, codes, scales, biases, lin_bias, row_block)
+    return y, tolerance(A, S)
 
 
 # ---- fused QKV -------------------------------------------------------------
@@ -121,8 +143,7 @@ def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=N
     Returns ((q, k, v), (tq, tk, tv)): values and per-element tolerances."""
     if codes.shape[0] != q_out + 2 * kv_out:
         raise ValueError("fused QKV weight must have q_out + 2*kv_out rows")
-    y, A = linear(x_bits, codes, scales, biases, lin_bias)
-    t = linear_tol(A)
+    y, t = linear(x_bits, codes, scales, biases, lin_bias)
     a, b = q_out, q_out + kv_out
     return (y[..., :a], y[..., a:b], y[..., b:]), (t[..., :a], t[..., a:b], t[..., b:])
 
@@ -160,9 +181,9 @@ def gate_up_swiglu(x_bits, codes, scales, biases, I: int):
     """Rows [0, I) are gate, [I, 2I) are up.  Returns (h, tol_h)."""
     if codes.shape[0] != 2 * I:
         raise ValueError("fused gate+up weight must have 2*I rows")
-    y, A = linear(x_bits, codes, scales, biases)
+    y, t = linear(x_bits, codes, scales, biases)
     g, u = y[..., :I], y[..., I:]
-    tg, tu = linear_tol(A[..., :I]), linear_tol(A[..., I:])
+    tg, tu = t[..., :I], t[..., I:]
     return swiglu(g, u), swiglu_tol(g, u, tg, tu)
 
 
@@ -195,24 +216,23 @@ def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, e
     E = grid_codes.shape[0]
     rows = grid_codes.shape[1]
     y = np.zeros(rows)
-    A = np.zeros(rows)
-    extra = np.zeros(rows)
+    t = np.zeros(rows)
     p = np.asarray(expert_w, dtype=np.float32).astype(np.float64)
     for k, e in enumerate(np.asarray(expert_ids).tolist()):
         if 0 <= e < E:
-            yk, Ak = linear(np.asarray(h_bits)[k], grid_codes[e], grid_scales[e], grid_biases[e])
+            yk, tk = linear(np.asarray(h_bits)[k], grid_codes[e], grid_scales[e], grid_biases[e])
             y += p[k] * yk
-            A += abs(p[k]) * Ak
+            t += abs(p[k]) * tk
             if h_err is not None:
                 W = dequant(grid_codes[e], grid_scales[e], grid_biases[e])
-                extra += abs(p[k]) * (np.abs(W) @ np.asarray(h_err[k], np.float64))
-    return y, linear_tol(A) + extra
+                t += abs(p[k]) * (np.abs(W) @ np.asarray(h_err[k], np.float64))
+    return y, t
 
 
 def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None, row_block: int = 1024):
     """A projection whose GPU input may differ from x_bits by at most x_err per element
     (an upstream GPU result): tolerance 1e-3*A + |W| . x_err."""
-    y, A = linear(x_bits, codes, scales, biases, lin_bias)
+    y, t = linear(x_bits, codes, scales, biases, lin_bias)
     e = np.asarray(x_err, np.float64)
     extra = np.empty_like(y)
     N = codes.shape[0]
@@ -220,7 +240,7 @@ def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None,
         r1 = min(N, r0 + row_block)
         W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
         extra[..., r0:r1] = e @ np.abs(W).T
-    return y, linear_tol(A) + extra
+    return y, t + extra
 
 
 def f32_to_bf16_bits(v) -> np.ndarray:

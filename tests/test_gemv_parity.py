@@ -1,7 +1,8 @@
 """GPU parity of the decode path (M = 1 GEMV) against the fp64 oracle.
 
-Acceptance: |gpu_fp32 - oracle| <= 1e-3 * sum_k |x_k w_k| per element (propagated
-bounds for SwiGLU), on the fp32 output before bf16 rounding; the bf16 output must
+Acceptance: |gpu_fp32 - oracle| <= 1e-3 * sum_k |x_k w_k| + 2^-12 * sum_k |x_k s_k|
+per element (the oracle's `tolerance`; propagated bounds for SwiGLU), on the fp32
+output before bf16 rounding; the bf16 output must
 equal RNE(fp32 output) bit for bit; fused outputs equal the unfused projection on
 the same row slice bit for bit; no write lands outside an output buffer."""
 import numpy as np
@@ -102,9 +103,9 @@ def test_multi_row_activations():
     say(f"[linear] M={M}")
     w = synth.gen_weight(synth.CFG_TEST, 8, synth.PROJ_LINEAR, N, K)
     x = synth.gen_x(synth.CFG_TEST, 8, 0, M, K)
-    y, A = orc.linear(x, w.codes, w.scales, w.biases)
+    y, t = orc.linear(x, w.codes, w.scales, w.biases)
     got = run_linear(x, w)
-    assert_within(got, y, 1e-3 * A, "linear M=3")
+    assert_within(got, y, t, "linear M=3")
     for m in range(M):
         assert np.array_equal(run_linear(x[m:m + 1], w)[0], got[m]), f"row {m}"
 
@@ -137,8 +138,8 @@ def test_constant_codes_closed_form():
         w = synth.gen_weight(synth.CFG_TEST, 11, synth.PROJ_LINEAR, N, K)
         w = synth.U4Weight(np.full_like(w.codes, c * 0x11111111), w.scales, w.biases)
         x = synth.gen_x(synth.CFG_TEST, 11, c, 1, K)
-        y, A = orc.linear(x, w.codes, w.scales, w.biases)
-        assert_within(run_linear(x, w), y, 1e-3 * A, f"codes={c}")
+        y, t = orc.linear(x, w.codes, w.scales, w.biases)
+        assert_within(run_linear(x, w), y, t, f"codes={c}")
 
 
 def test_one_hot_code_position():

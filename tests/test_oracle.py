@@ -127,7 +127,7 @@ def test_oracle_matches_brute_force(M, K, N, with_bias):
     b = _rand_bf16_bits(rng, (N, K // 64))
     x = _rand_bf16_bits(rng, (M, K), -4, 4)
     lb = _rand_bf16_bits(rng, (N,)) if with_bias else None
-    y, A = orc.linear(x, words, s, b, lin_bias=lb)
+    y, A, S = orc.project(x, words, s, b, lin_bias=lb)
     yb, Ab = brute.project(x.tolist(), q.tolist(), s.tolist(), b.tolist(),
                            lin_bias_bits=None if lb is None else lb.tolist())
     yb, Ab = np.array(yb), np.array(Ab)
@@ -211,9 +211,9 @@ def test_fused_qkv_equals_three_unfused_projections():
     (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, fused.codes, fused.scales, fused.biases, q_out, kv_out, lb)
     offs = [0, q_out, q_out + kv_out, q_out + 2 * kv_out]
     for i, (got, tol) in enumerate([(q, tq), (k, tk), (v, tv)]):
-        ref, A = orc.linear(x, parts[i].codes, parts[i].scales, parts[i].biases, lb[offs[i]:offs[i + 1]])
+        ref, A, S = orc.project(x, parts[i].codes, parts[i].scales, parts[i].biases, lb[offs[i]:offs[i + 1]])
         assert np.allclose(got, ref, rtol=0, atol=1e-13 * A.max())
-        assert np.allclose(tol, 1e-3 * A, rtol=1e-14)
+        assert np.allclose(tol, 1e-3 * A + 2.0 ** -12 * S, rtol=1e-14)
 
 
 def test_fused_gate_up_equals_swiglu_of_unfused():
@@ -310,8 +310,8 @@ def test_moe_single_expert_reduces_to_dense():
         assert np.array_equal(h[0], hd) and np.array_equal(th[0], td)
         hb = synth.to_bf16_bits(hd)[None, :]
         y, t = orc.moe_down_combine(hb, d.codes, d.scales, d.biases, np.array([e]), np.array([1.0], np.float32))
-        yd, Ad = orc.linear(hb[0], ed[e].codes, ed[e].scales, ed[e].biases)
-        assert np.array_equal(y, yd) and np.allclose(t, 1e-3 * Ad)
+        yd, td = orc.linear(hb[0], ed[e].codes, ed[e].scales, ed[e].biases)
+        assert np.array_equal(y, yd) and np.allclose(t, td)
 
 
 def test_moe_combine_is_weighted_sum_and_order_free():
@@ -353,7 +353,7 @@ def test_linearity_and_zero_input():
     x2 = synth.to_bf16_bits(2.0 * orc.bf16_to_f64(x))
     y2, _ = orc.linear(x2, w.codes, w.scales, w.biases)
     assert np.array_equal(y2, 2.0 * y)
-    y0, A0 = orc.linear(np.zeros_like(x), w.codes, w.scales, w.biases)
+    y0, A0 = orc.linear(np.zeros_like(x), w.codes, w.scales, w.biases)   # (y, tol): both zero
     assert np.all(y0 == 0) and np.all(A0 == 0)
 
 
@@ -389,3 +389,20 @@ def test_bf16_input_error_bounds_every_rounding_of_a_nearby_value():
     for f in (-1.0, -0.5, 0.0, 0.5, 1.0):
         got = orc.bf16_to_f64(orc.f32_to_bf16_bits(h + f * tol))
         assert np.all(np.abs(got - base) <= bound)
+
+
+def test_scale_mass_and_floor():
+    """S = sum|x||s| from its definition, and the evaluation floor is negligible next to
+    1e-3 * sum|x w| on the workloads' weights (bias = -8 * scale, codes uniform)."""
+    w = synth.gen_weight(synth.CFG_14B, 0, 0, 64, 5120)
+    x = synth.gen_x(synth.CFG_14B, 0, 0, 1, 5120)
+    y, A, S = orc.project(x, w.codes, w.scales, w.biases)
+    xv = np.abs(orc.bf16_to_f64(x[0]))
+    s = np.abs(orc.bf16_to_f64(w.scales))
+    S_def = np.array([sum(xv[k] * s[n, k // 64] for k in range(0, 5120)) for n in range(3)])
+    assert np.allclose(S[0, :3], S_def, rtol=1e-12)
+    assert np.max(orc.EVAL_FLOOR * S / (orc.REL_TOL * A)) < 0.1
+    # all-zero weights with non-zero codes: the stated rule alone would demand an exact zero
+    z = synth.U4Weight(np.full_like(w.codes, 0x88888888), w.scales, w.biases)
+    y0, A0, S0 = orc.project(x, z.codes, z.scales, z.biases)
+    assert np.all(y0 == 0) and np.all(A0 == 0) and np.all(S0 > 0)
