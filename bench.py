@@ -34,8 +34,32 @@ def _args():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--pool", type=int, default=48, help="layer copies in the rotating weight pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-steps", type=int, default=2)
+    ap.add_argument("--cpu-sample-steps", type=int, default=6)
+    ap.add_argument("--kernel-reps", type=int, default=1000,
+                    help="launches per graph when timing one kernel on its own")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["gemm_affine_u4_amd/csrc/gemv_u4.hip", "gemm_affine_u4_amd/csrc/qmm_device.h"]
+COUNTERS_SUMMARY = "profiles/gemv_u4_decode_14B_hbm_counters.md"
+
+
+def counted_traffic(key: str):
+    """HBM bytes per launch measured by the committed counter runs (FETCH_SIZE and
+    WRITE_SIZE, calibrated on a device copy), or None if the kernel sources changed
+    since they were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, COUNTERS_SUMMARY)).read()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if re.search(r"source_sha256_16: (\w+)", text).group(1) != h.hexdigest()[:16]:
+            return None
+        return int(re.search(rf"traffic_bytes_per_launch\.{key}: (\d+)", text).group(1))
+    except (OSError, AttributeError):
+        return None
 
 
 def weight_bytes(rows: int, K: int) -> int:
@@ -122,10 +146,11 @@ def main():
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
         e1.synchronize()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)  # ms
@@ -136,19 +161,20 @@ def main():
             step(i)
     torch.cuda.synchronize()
     g_step = capture(step, args.steps)
-    g_step.replay()
+    with torch.cuda.stream(stream):
+        g_step.replay()
     torch.cuda.synchronize()
     ms_total = timed_replay(g_step)
     ms_per_step = ms_total / args.steps
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     # per-kernel average duration of the dominant kernel (gate+up GEMV), same stream
-    n_k = max(200, min(args.steps, 2000))
+    n_k = args.kernel_reps
     g_gu = capture(gate_up_only, n_k)
-    g_gu.replay()
+    timed_replay(g_gu)
     ms_gu = timed_replay(g_gu) / n_k
     g_qkv = capture(qkv_only, n_k)
-    g_qkv.replay()
+    timed_replay(g_qkv)
     ms_qkv = timed_replay(g_qkv) / n_k
     ach_gu = bytes_gu / (ms_gu * 1e-3) / 1e9
     ach_qkv = bytes_qkv / (ms_qkv * 1e-3) / 1e9
@@ -187,7 +213,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "gemv_u4_kernel (fused gate+up+SwiGLU, K=5120)",
                      "achieved": round(ach_gu, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach_gu / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(ach_gu / HBM_PEAK_GBS, 4), "traffic": counted_traffic("gate_up"),
                      "bytes_per_launch": bytes_gu, "avg_launch_us": ms_gu * 1e3},
         "kernels": {"fused_qkv_gemv": {"avg_launch_us": ms_qkv * 1e3, "GB/s": round(ach_qkv, 1),
                                        "bytes_per_launch": bytes_qkv},

@@ -33,57 +33,66 @@
 namespace qmm {
 
 constexpr int kMaxWavesPerBlock = 16;
-constexpr int kUPW = 1;  // row units per wave
 
+// Activations of this lane's chunks, in registers for the whole kernel, read through a
+// buffer descriptor bounded by K: a chunk past the end of the K slice (ragged K) reads
+// zeros, so it contributes exactly nothing whatever codes, scale and bias sit there.
 template <int LPR, int CPL>
-__device__ __forceinline__ void load_x_chunks(const uint16_t* __restrict__ x, int64_t C, int ks, int li,
-                                              int64_t cidx[CPL], bool cval[CPL], uint32_t xp[CPL][16],
+__device__ __forceinline__ void load_x_chunks(__amdgpu_buffer_rsrc_t xr, uint32_t c0, uint32_t xp[CPL][16],
                                               float xs[CPL]) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const int64_t c = int64_t(ks) * (LPR * CPL) + li + LPR * i;
-    cval[i] = c < C;
-    cidx[i] = cval[i] ? c : (C - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(x + cidx[i] * 32);
+    const uint32_t off = (c0 + uint32_t(LPR * i)) * 64u;
     uint32_t d[16];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const uint4 t = src[v];
-      d[4 * v + 0] = cval[i] ? t.x : 0u;
-      d[4 * v + 1] = cval[i] ? t.y : 0u;
-      d[4 * v + 2] = cval[i] ? t.z : 0u;
-      d[4 * v + 3] = cval[i] ? t.w : 0u;
+      const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16u * v, 0, 0);
+      d[4 * v + 0] = t[0];
+      d[4 * v + 1] = t[1];
+      d[4 * v + 2] = t[2];
+      d[4 * v + 3] = t[3];
     }
     permute_chunk(d, xp[i]);
     xs[i] = chunk_xsum(xp[i]);
   }
 }
 
-// Partial dot product of one row over this lane's chunks (fp32).
+// The packed codes and the group scales/biases of one row for this lane's chunks.
 template <int CPL>
-__device__ __forceinline__ float row_partial(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                             const uint16_t* __restrict__ biases, int64_t row, int64_t words,
-                                             int64_t groups, const int64_t cidx[CPL], const bool cval[CPL],
-                                             const uint32_t xp[CPL][16], const float xs[CPL], uint32_t magic) {
+struct RowData {
   u32x4_t w[CPL];
-  uint16_t sb[CPL], bb[CPL];
-  const uint32_t* rowp = codes + row * words;
+  uint16_t s[CPL], b[CPL];
+};
+
+// Chunk c0 + LPR*i of row `row`: codes at byte row*K/2 + 16*c, scale/bias at
+// 2*(row*K/64 + c/2); consecutive chunks of a lane are LPR*16 (codes) and LPR (groups)
+// bytes apart, which the loads carry as immediate offsets.
+template <int LPR, int CPL>
+__device__ __forceinline__ void load_row(RowData<CPL>& r, __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr,
+                                         __amdgpu_buffer_rsrc_t br, uint32_t row, uint32_t row_bytes,
+                                         uint32_t row_groups, uint32_t c0) {
+  const uint32_t co = row * row_bytes + c0 * 16u;
+  const uint32_t go = (row * row_groups + (c0 >> 1)) * 2u;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rowp + cidx[i] * 4));
-    sb[i] = scales[row * groups + (cidx[i] >> 1)];
-    bb[i] = biases[row * groups + (cidx[i] >> 1)];
+    r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(cr, co + uint32_t(i * LPR * 16), 0, kLoadNT);
+    r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, go + uint32_t(i * LPR), 0, 0);
+    r.b[i] = __builtin_amdgcn_raw_buffer_load_b16(br, go + uint32_t(i * LPR), 0, 0);
   }
+}
+
+// Partial dot product of one row over this lane's chunks (fp32).
+template <int CPL>
+__device__ __forceinline__ float row_partial(const RowData<CPL>& r, const uint32_t xp[CPL][16], const float xs[CPL],
+                                             uint32_t magic) {
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const uint32_t ww[4] = {w[i][0], w[i][1], w[i][2], w[i][3]};
+    const uint32_t ww[4] = {r.w[i][0], r.w[i][1], r.w[i][2], r.w[i][3]};
     const float D = chunk_dot128(ww, xp[i], magic);
     const float d = fmaf(-128.0f, xs[i], D);
-    const float s = cval[i] ? bf16_bits_to_f32(sb[i]) : 0.f;
-    const float b = cval[i] ? bf16_bits_to_f32(bb[i]) : 0.f;
-    acc = fmaf(s, d, acc);
-    acc = fmaf(b, xs[i], acc);
+    acc = fmaf(bf16_bits_to_f32(r.s[i]), d, acc);
+    acc = fmaf(bf16_bits_to_f32(r.b[i]), xs[i], acc);
   }
   return acc;
 }
@@ -111,23 +120,32 @@ __host__ __device__ constexpr int groups_per_block() { return KS >= 4 ? 1 : 4 / 
 template <int KS>
 __host__ __device__ constexpr int threads_per_block() { return 64 * KS * groups_per_block<KS>(); }
 
-template <int LPR, int CPL, int KS, int EPI, bool MOE>
-__global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvArgs a) {
+// One wave (one row group) walks `upw` consecutive row units with DEPTH - 1 units of
+// code loads in flight ahead of the one being computed.
+#ifndef QMM_GEMV_DEPTH
+#define QMM_GEMV_DEPTH 3
+#endif
+#ifndef QMM_GEMV_WAVES_PER_CU
+#define QMM_GEMV_WAVES_PER_CU 8
+#endif
+
+template <int LPR, int CPL, int KS, int EPI, bool MOE, int DEPTH = (KS >= 16 ? 1 : QMM_GEMV_DEPTH)>
+__global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvArgs a, int64_t units, int upw) {
   constexpr int RPI = 64 / LPR;
   constexpr int P = RPI / 2;
-  constexpr int ksplit = KS;
   constexpr int G = groups_per_block<KS>();
-  __shared__ float red[kMaxWavesPerBlock * kUPW * RPI];
+  __shared__ float red[2][kMaxWavesPerBlock * RPI];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int ks = wave % ksplit;
-  const int g = wave / ksplit;
+  const int ks = wave % KS;
+  const int g = wave / KS;
   const int slot = lane / LPR;
   const int li = lane % LPR;
-  const int64_t C = a.K >> 5;
   const int64_t words = a.K >> 3;
   const int64_t groups = a.K >> 6;
+  const int64_t u_begin = (int64_t(blockIdx.x) * G + g) * upw;
+  const int64_t u_end = u_begin + upw < units ? u_begin + upw : units;
 
   const uint32_t* codes = a.codes;
   const uint16_t* scales = a.scales;
@@ -142,13 +160,11 @@ __global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvAr
     if (e < 0 || e >= a.E) {
       // no expert: this slot's h is zero
       if (ks == 0) {
-        for (int u = 0; u < kUPW; ++u) {
-          const int64_t unit = (int64_t(blockIdx.x) * G + g) * kUPW + u;
+        for (int64_t u = u_begin; u < u_end; ++u) {
           bool valid;
-          const int64_t r = unit_row<LPR, EPI>(unit, slot, a, &valid);
-          (void)r;
+          (void)unit_row<LPR, EPI>(u, slot, a, &valid);
           if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
-            store_out(a.out0, out_base + unit * P + slot, 0.f, a.f32_out);
+            store_out(a.out0, out_base + u * P + slot, 0.f, a.f32_out);
         }
       }
       return;
@@ -162,61 +178,81 @@ __global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvAr
     out_base = int64_t(blockIdx.y) * a.n_out;
   }
 
-  int64_t cidx[CPL];
-  bool cval[CPL];
+  const uint32_t row_bytes = uint32_t(a.K >> 1);
+  const uint32_t row_groups = uint32_t(groups);
+  const uint64_t nrows = uint64_t(a.rows);
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, nrows * row_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, nrows * row_groups * 2);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(biases, nrows * row_groups * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, uint64_t(a.K) * 2);
+  const uint32_t c0 = uint32_t(ks * (LPR * CPL) + li);
+
   uint32_t xp[CPL][16];
   float xs[CPL];
-  load_x_chunks<LPR, CPL>(x, C, ks, li, cidx, cval, xp, xs);
   const uint32_t magic = in_vgpr(kMagicPair);
 
-  float tot[kUPW];
-  bool rvalid[kUPW];
-  int64_t rrow[kUPW];
+  // Ring of DEPTH row buffers: unit u is computed from buf[(u - u_begin) % DEPTH], and
+  // the buffer is refilled with unit u + DEPTH right after, so DEPTH - 1 units of codes
+  // stay in flight while one is being computed.
+  RowData<CPL> buf[DEPTH];
 #pragma unroll
-  for (int u = 0; u < kUPW; ++u) {
-    const int64_t unit = (int64_t(blockIdx.x) * G + g) * kUPW + u;
-    rrow[u] = unit_row<LPR, EPI>(unit, slot, a, &rvalid[u]);
-    const float acc = row_partial<CPL>(codes, scales, biases, rrow[u], words, groups, cidx, cval, xp, xs, magic);
-    tot[u] = slot_reduce<LPR>(acc);
-  }
-
-  if constexpr (ksplit > 1) {
-    if (lane == slot_result_lane<LPR>(slot)) {
-#pragma unroll
-      for (int u = 0; u < kUPW; ++u) red[(wave * kUPW + u) * RPI + slot] = tot[u];
-    }
-    __syncthreads();
-    if (ks != 0) return;
-#pragma unroll
-    for (int u = 0; u < kUPW; ++u) {
-      float v = 0.f;
-      for (int j = 0; j < ksplit; ++j) v += red[((g * ksplit + j) * kUPW + u) * RPI + slot];
-      tot[u] = v;
+  for (int d = 0; d < DEPTH; ++d) {
+    if (u_begin + d < u_end) {
+      bool valid;
+      const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
+      load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
     }
   }
+  load_x_chunks<LPR, CPL>(xr, c0, xp, xs);
 
+  for (int64_t u0 = u_begin; u0 < u_end; u0 += DEPTH) {
 #pragma unroll
-  for (int u = 0; u < kUPW; ++u) {
-    const int64_t unit = (int64_t(blockIdx.x) * G + g) * kUPW + u;
-    float v = tot[u];
-    if constexpr (EPI == EPI_SWIGLU) {
-      const float up = __shfl_xor(v, 32);
-      if (rvalid[u] && slot < P && lane == slot_result_lane<LPR>(slot))
-        store_out(a.out0, out_base + unit * P + slot, silu_times(v, up), a.f32_out);
-    } else {
-      if (rvalid[u] && lane == slot_result_lane<LPR>(slot)) {
-        const int64_t r = rrow[u];
-        if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
-        if constexpr (EPI == EPI_QKV) {
-          if (r < a.q_out) {
-            store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
-          } else if (r < a.q_out + a.kv_out) {
-            store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t u = u0 + d;
+      if (u < u_end) {
+        float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        if (u + DEPTH < u_end) {
+          bool valid;
+          const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
+          load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
+        }
+        bool cur_valid;
+        const int64_t cur_row = unit_row<LPR, EPI>(u, slot, a, &cur_valid);
+        bool store = true;
+        if constexpr (KS > 1) {
+          float* rb = red[u & 1];
+          if (lane == slot_result_lane<LPR>(slot)) rb[wave * RPI + slot] = v;
+          __syncthreads();
+          if (ks == 0) {
+            float t = 0.f;
+            for (int j = 0; j < KS; ++j) t += rb[(g * KS + j) * RPI + slot];
+            v = t;
           } else {
-            store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
+            store = false;
           }
-        } else {
-          store_out(a.out0, out_base + r, v, a.f32_out);
+        }
+        if (store) {
+          if constexpr (EPI == EPI_SWIGLU) {
+            const float up = __shfl_xor(v, 32);
+            if (cur_valid && slot < P && lane == slot_result_lane<LPR>(slot))
+              store_out(a.out0, out_base + u * P + slot, silu_times(v, up), a.f32_out);
+          } else {
+            if (cur_valid && lane == slot_result_lane<LPR>(slot)) {
+              const int64_t r = cur_row;
+              if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
+              if constexpr (EPI == EPI_QKV) {
+                if (r < a.q_out) {
+                  store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
+                } else if (r < a.q_out + a.kv_out) {
+                  store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
+                } else {
+                  store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
+                }
+              } else {
+                store_out(a.out0, out_base + r, v, a.f32_out);
+              }
+            }
+          }
         }
       }
     }
@@ -224,61 +260,62 @@ __global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvAr
 }
 
 // Routed-expert stage 2: y[r] = sum_k p_k * (D_{e_k} h_k)[r].  A block's kw waves split
-// the routed slots (wave w takes k = w, w+kw, ...), each adding its slots in increasing
-// k; the waves' partials are then added in wave order.  No atomics.
+// the routed slots (wave w takes k = w, w+kw, ...) and walk the block's `upw` row units
+// for each; every wave adds its slots in increasing k into its own LDS slice, and the
+// slices are then added in wave order.  No atomics, so the order is fixed.
+constexpr int kMaxUnitsPerCombineBlock = 16;
+
 template <int LPR, int CPL>
-__global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a) {
+__global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units, int upw) {
   constexpr int RPI = 64 / LPR;
-  __shared__ float red[kMaxWavesPerBlock * kUPW * RPI];
+  __shared__ float red[8][kMaxUnitsPerCombineBlock][RPI];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kw = blockDim.x >> 6;
   const int slot = lane / LPR;
   const int li = lane % LPR;
-  const int64_t C = a.K >> 5;
-  const int64_t words = a.K >> 3;
-  const int64_t groups = a.K >> 6;
+  const bool result_lane = lane == slot_result_lane<LPR>(slot);
+  const int64_t u_begin = int64_t(blockIdx.x) * upw;
+  const int nu = int(u_begin + upw < units ? upw : units - u_begin);
+  const uint32_t row_bytes = uint32_t(a.K >> 1);
+  const uint32_t row_groups = uint32_t(a.K >> 6);
+  const uint64_t expert_words = uint64_t(a.rows) * uint64_t(a.K >> 3);
+  const uint64_t expert_groups = uint64_t(a.rows) * row_groups;
+  const uint32_t c0 = uint32_t(li);
   const uint32_t magic = in_vgpr(kMagicPair);
 
-  float acc_u[kUPW];
-  bool rvalid[kUPW];
-  int64_t rrow[kUPW];
-#pragma unroll
-  for (int u = 0; u < kUPW; ++u) {
-    acc_u[u] = 0.f;
-    const int64_t r = (int64_t(blockIdx.x) * kUPW + u) * RPI + slot;
-    rvalid[u] = r < a.rows;
-    rrow[u] = rvalid[u] ? r : a.rows - 1;
-  }
+  if (result_lane)
+    for (int u = 0; u < nu; ++u) red[wave][u][slot] = 0.f;
+
   for (int k = wave; k < a.topk; k += kw) {
     const int32_t e = a.expert_ids[k];
     if (e < 0 || e >= a.E) continue;  // no expert: contributes nothing
     const float p = a.expert_w[k];
-    int64_t cidx[CPL];
-    bool cval[CPL];
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes + uint64_t(e) * expert_words, expert_words * 4);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales + uint64_t(e) * expert_groups, expert_groups * 2);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases + uint64_t(e) * expert_groups, expert_groups * 2);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + int64_t(k) * a.K, uint64_t(a.K) * 2);
+    RowData<CPL> cur, nxt;
+    load_row<LPR, CPL>(cur, cr, sr, br, uint32_t(u_begin * RPI + slot), row_bytes, row_groups, c0);
     uint32_t xp[CPL][16];
     float xs[CPL];
-    load_x_chunks<LPR, CPL>(a.x + int64_t(k) * a.K, C, 0, li, cidx, cval, xp, xs);
-    const int64_t off = int64_t(e) * a.rows;
-#pragma unroll
-    for (int u = 0; u < kUPW; ++u) {
-      const float part = row_partial<CPL>(a.codes + off * words, a.scales + off * groups, a.biases + off * groups,
-                                          rrow[u], words, groups, cidx, cval, xp, xs, magic);
-      acc_u[u] = fmaf(p, slot_reduce<LPR>(part), acc_u[u]);
+    load_x_chunks<LPR, CPL>(xr, c0, xp, xs);
+    for (int u = 0; u < nu; ++u) {
+      if (u + 1 < nu)
+        load_row<LPR, CPL>(nxt, cr, sr, br, uint32_t((u_begin + u + 1) * RPI + slot), row_bytes, row_groups, c0);
+      const float v = slot_reduce<LPR>(row_partial<CPL>(cur, xp, xs, magic));
+      if (result_lane) red[wave][u][slot] = fmaf(p, v, red[wave][u][slot]);
+      cur = nxt;
     }
   }
-  if (lane == slot_result_lane<LPR>(slot)) {
-#pragma unroll
-    for (int u = 0; u < kUPW; ++u) red[(wave * kUPW + u) * RPI + slot] = acc_u[u];
-  }
   __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int u = 0; u < kUPW; ++u) {
-    if (rvalid[u] && lane == slot_result_lane<LPR>(slot)) {
+  if (wave != 0 || !result_lane) return;
+  for (int u = 0; u < nu; ++u) {
+    const int64_t r = (u_begin + u) * RPI + slot;
+    if (r < a.rows) {
       float v = 0.f;
-      for (int j = 0; j < kw; ++j) v += red[(j * kUPW + u) * RPI + slot];
-      store_out(a.out0, rrow[u], v, a.f32_out);
+      for (int j = 0; j < kw; ++j) v += red[j][u][slot];
+      store_out(a.out0, r, v, a.f32_out);
     }
   }
 }
@@ -302,7 +339,7 @@ bool gemv_shape_for_k(int64_t K, GemvShape* o) {
 static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 
 #define QMM_GEMV_CASE(L, C, K, EPI, MOE) \
-  case (L * 10000 + C * 100 + K): gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a); break;
+  case (L * 10000 + C * 100 + K): gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a, units, upw); break;
 
 #define QMM_GEMV_CASES(EPI, MOE)                                                  \
   switch (sh.lpr * 10000 + sh.cpl * 100 + sh.ksplit) {                            \
@@ -322,20 +359,29 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
     default: return 2;                                                            \
   }
 
-static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t* blocks, int* threads) {
+// Grid of the decode kernel: each wave (row group) takes `upw` consecutive units, sized
+// so that about kTargetWaves waves cover the call (a few per SIMD on 256 CUs).
+constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
+
+static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units,
+                          int* upw, int64_t* blocks, int* threads) {
   const int rpi = 64 / sh.lpr;
-  const int64_t units = (epi == EPI_SWIGLU) ? (a.I + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
+  *units = (epi == EPI_SWIGLU) ? (a.I + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
   const int G = sh.ksplit >= 4 ? 1 : 4 / sh.ksplit;  // groups_per_block<KS>()
+  const int64_t groups_wanted = (kTargetWaves / sh.ksplit + batch - 1) / batch;  // row groups per batch entry
+  int64_t u = (*units + groups_wanted - 1) / groups_wanted;
+  if (u < 1) u = 1;
+  *upw = int(u);
   *threads = 64 * sh.ksplit * G;
-  *blocks = (units + int64_t(G) * kUPW - 1) / (int64_t(G) * kUPW);
+  *blocks = (*units + int64_t(G) * u - 1) / (int64_t(G) * u);
 }
 
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
   GemvShape sh;
   if (!gemv_shape_for_k(a.K, &sh)) return 2;
-  int64_t blocks;
-  int threads;
-  gemv_geometry(sh, epi, a, &blocks, &threads);
+  int64_t blocks, units;
+  int threads, upw;
+  gemv_geometry(sh, epi, a, M, &units, &upw, &blocks, &threads);
   const dim3 grid{unsigned(blocks), unsigned(M), 1u};
   const dim3 block{unsigned(threads), 1u, 1u};
   if (epi == EPI_LINEAR) {
@@ -351,9 +397,9 @@ int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
 int launch_moe_gate_up(const GemvArgs& a, hipStream_t s) {
   GemvShape sh;
   if (!gemv_shape_for_k(a.K, &sh)) return 2;
-  int64_t blocks;
-  int threads;
-  gemv_geometry(sh, EPI_SWIGLU, a, &blocks, &threads);
+  int64_t blocks, units;
+  int threads, upw;
+  gemv_geometry(sh, EPI_SWIGLU, a, a.topk, &units, &upw, &blocks, &threads);
   const dim3 grid{unsigned(blocks), unsigned(a.topk), 1u};
   const dim3 block{unsigned(threads), 1u, 1u};
   QMM_GEMV_CASES(EPI_SWIGLU, true)
@@ -366,15 +412,19 @@ int launch_moe_down(const GemvArgs& a, hipStream_t s) {
   const int rpi = 64 / sh.lpr;
   const int64_t units = (a.rows + rpi - 1) / rpi;
   const int kw = a.topk < 8 ? a.topk : 8;
-  const dim3 grid{unsigned((units + kUPW - 1) / kUPW), 1u, 1u};
+  // about 256 blocks, at most kMaxUnitsPerCombineBlock units each
+  int64_t upw = (units + 255) / 256;
+  if (upw > kMaxUnitsPerCombineBlock) upw = kMaxUnitsPerCombineBlock;
+  if (upw < 1) upw = 1;
+  const dim3 grid{unsigned((units + upw - 1) / upw), 1u, 1u};
   const dim3 block{unsigned(64 * kw), 1u, 1u};
   switch (sh.lpr * 100 + sh.cpl) {
-    case 1601: moe_down_kernel<16, 1><<<grid, block, 0, s>>>(a); break;
-    case 3201: moe_down_kernel<32, 1><<<grid, block, 0, s>>>(a); break;
-    case 3202: moe_down_kernel<32, 2><<<grid, block, 0, s>>>(a); break;
-    case 3203: moe_down_kernel<32, 3><<<grid, block, 0, s>>>(a); break;
-    case 3204: moe_down_kernel<32, 4><<<grid, block, 0, s>>>(a); break;
-    case 3205: moe_down_kernel<32, 5><<<grid, block, 0, s>>>(a); break;
+    case 1601: moe_down_kernel<16, 1><<<grid, block, 0, s>>>(a, units, int(upw)); break;
+    case 3201: moe_down_kernel<32, 1><<<grid, block, 0, s>>>(a, units, int(upw)); break;
+    case 3202: moe_down_kernel<32, 2><<<grid, block, 0, s>>>(a, units, int(upw)); break;
+    case 3203: moe_down_kernel<32, 3><<<grid, block, 0, s>>>(a, units, int(upw)); break;
+    case 3204: moe_down_kernel<32, 4><<<grid, block, 0, s>>>(a, units, int(upw)); break;
+    case 3205: moe_down_kernel<32, 5><<<grid, block, 0, s>>>(a, units, int(upw)); break;
     default: return 2;
   }
   return finish_launch();

@@ -15,6 +15,9 @@ uint64_t u4_code_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64
 uint64_t u4_group_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K / 64) * 2; }
 
 bool out_dtype_ok(int d) { return d == QMM_OUT_BF16 || d == QMM_OUT_F32; }
+
+// The kernels address one weight matrix (one expert of a grid) with 32-bit byte offsets.
+bool matrix_fits(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K) / 2 <= 0xFFFFFFFFull; }
 size_t out_elem(int d) { return d == QMM_OUT_F32 ? 4 : 2; }
 
 int check_weight(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases) {
@@ -49,7 +52,7 @@ int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, c
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!y) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
-  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || N > (int64_t(1) << 31)) return QMM_ERR_SHAPE;
+  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(N, K)) return QMM_ERR_SHAPE;
   if (!qmm::aligned(y, out_elem(out_dtype)) || (lin_bias && !qmm::aligned(lin_bias, 2))) return QMM_ERR_ALIGN;
   const Range outs[] = {{y, uint64_t(M * N) * out_elem(out_dtype)}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
@@ -80,7 +83,7 @@ int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes
   if (!q || !k || !v) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
   const int64_t rows = q_out + 2 * kv_out;
-  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || rows > (int64_t(1) << 31))
+  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(rows, K))
     return QMM_ERR_SHAPE;
   const size_t e = out_elem(out_dtype);
   if (!qmm::aligned(q, e) || !qmm::aligned(k, e) || !qmm::aligned(v, e) || (lin_bias && !qmm::aligned(lin_bias, 2)))
@@ -116,7 +119,7 @@ int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!h) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
-  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || I > (int64_t(1) << 30)) return QMM_ERR_SHAPE;
+  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(2 * I, K)) return QMM_ERR_SHAPE;
   if (!qmm::aligned(h, out_elem(out_dtype))) return QMM_ERR_ALIGN;
   const Range outs[] = {{h, uint64_t(M * I) * out_elem(out_dtype)}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
@@ -147,7 +150,7 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* cod
   if (!expert_ids || !out || (stage == QMM_MOE_DOWN_COMBINE && !expert_w)) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
   if (!qmm::k_ok(K) || E < 1 || rows < 1 || topk < 1 || topk > QMM_MAX_TOPK || E > (int64_t(1) << 24) ||
-      rows > (int64_t(1) << 30))
+      !matrix_fits(rows, K))
     return QMM_ERR_SHAPE;
   if (stage == QMM_MOE_GATE_UP_SWIGLU && rows % 2) return QMM_ERR_SHAPE;
   if (stage == QMM_MOE_DOWN_COMBINE && K > 5120) return QMM_ERR_SHAPE;

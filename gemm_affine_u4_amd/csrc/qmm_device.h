@@ -16,6 +16,17 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMagicPair = 0x43004300u;  // bf16 pair (128.0, 128.0)
+
+// Raw buffer descriptors: loads at offsets >= num_records return zero, which is how
+// the kernels treat the ragged end of a row, a K slice or a buffer.  The range check
+// is per dword, so every buffer read here is dword-aligned and dword-sized or a bf16.
+constexpr int kBufferFlags = 0x00020000;  // dword 3 of a gfx9 raw buffer descriptor (32-bit data)
+constexpr int kLoadNT = 2;                // aux bit: non-temporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : uint32_t(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(n), kBufferFlags);
+}
 constexpr uint32_t kNibblePair = 0x000F000Fu;
 
 // Keep a constant in a VGPR so that v_and_or_b32 can take it alongside an SGPR mask

@@ -35,7 +35,9 @@
  *     throws or prints.  Arguments are validated before anything is enqueued:
  *       QMM_ERR_NULL   a required pointer is NULL;
  *       QMM_ERR_SHAPE  M < 1, K < 64, K % 64 != 0, K > QMM_MAX_K, a row count < 1,
- *                      topk outside [1, QMM_MAX_TOPK], or a shape the call cannot take;
+ *                      topk outside [1, QMM_MAX_TOPK], M > 65535, one weight matrix
+ *                      (one expert of a grid) above 4 GiB of codes, or a shape the
+ *                      call cannot take;
  *       QMM_ERR_ALIGN  x or codes not 16-byte aligned, a bf16 array not 2-byte
  *                      aligned, an fp32/int32 array or fp32 output not 4-byte aligned;
  *       QMM_ERR_ALIAS  two outputs overlap, or an output overlaps any input (the
