@@ -1,6 +1,6 @@
 // C ABI entry points (declared and documented in include/qmm.h): validate, then
-// enqueue the kernel for the regime (decode GEMV for M == 1, LDS-dequant + MFMA GEMM
-// for M > 1).  Nothing here allocates, synchronises or keeps state.
+// enqueue the kernel for the regime (decode GEMV for M <= 8, LDS-dequant + MFMA GEMM
+// above).  Nothing here allocates, synchronises or keeps state.
 #include <hip/hip_runtime_api.h>
 
 #include "qmm.h"
@@ -16,8 +16,33 @@ uint64_t u4_group_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint6
 
 bool out_dtype_ok(int d) { return d == QMM_OUT_BF16 || d == QMM_OUT_F32; }
 
-// The kernels address one weight matrix (one expert of a grid) with 32-bit byte offsets.
+// The kernels address one weight matrix (one expert of a grid) and the activations with
+// 32-bit byte offsets.
 bool matrix_fits(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K) / 2 <= 0xFFFFFFFFull; }
+bool acts_fit(int64_t M, int64_t K) { return uint64_t(M) * uint64_t(K) * 2 <= 0xFFFFFFFFull; }
+
+// Activation rows up to which the decode GEMV runs (once per row); above, the GEMM.
+constexpr int64_t kGemvMaxM = 8;
+
+qmm::GemmArgs gemm_args(const qmm::GemvArgs& g, int64_t M, int64_t N) {
+  qmm::GemmArgs a = {};
+  a.x = g.x;
+  a.codes = g.codes;
+  a.scales = g.scales;
+  a.biases = g.biases;
+  a.lin_bias = g.lin_bias;
+  a.out0 = g.out0;
+  a.out1 = g.out1;
+  a.out2 = g.out2;
+  a.M = M;
+  a.K = g.K;
+  a.N = N;
+  a.q_out = g.q_out;
+  a.kv_out = g.kv_out;
+  a.I = g.I;
+  a.f32_out = g.f32_out;
+  return a;
+}
 size_t out_elem(int d) { return d == QMM_OUT_F32 ? 4 : 2; }
 
 int check_weight(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* biases) {
@@ -52,7 +77,7 @@ int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, c
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!y) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
-  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(N, K)) return QMM_ERR_SHAPE;
+  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(N, K) || !acts_fit(M, K)) return QMM_ERR_SHAPE;
   if (!qmm::aligned(y, out_elem(out_dtype)) || (lin_bias && !qmm::aligned(lin_bias, 2))) return QMM_ERR_ALIGN;
   const Range outs[] = {{y, uint64_t(M * N) * out_elem(out_dtype)}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
@@ -73,6 +98,7 @@ int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, c
   a.rows = N;
   a.n_out = N;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_LINEAR, gemm_args(a, M, N), stream);
   return qmm::launch_gemv(qmm::EPI_LINEAR, a, M, stream);
 }
 
@@ -83,7 +109,7 @@ int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes
   if (!q || !k || !v) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
   const int64_t rows = q_out + 2 * kv_out;
-  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(rows, K))
+  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(rows, K) || !acts_fit(M, K))
     return QMM_ERR_SHAPE;
   const size_t e = out_elem(out_dtype);
   if (!qmm::aligned(q, e) || !qmm::aligned(k, e) || !qmm::aligned(v, e) || (lin_bias && !qmm::aligned(lin_bias, 2)))
@@ -110,6 +136,7 @@ int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes
   a.q_out = q_out;
   a.kv_out = kv_out;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_QKV, gemm_args(a, M, rows), stream);
   return qmm::launch_gemv(qmm::EPI_QKV, a, M, stream);
 }
 
@@ -119,7 +146,8 @@ int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!h) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
-  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(2 * I, K)) return QMM_ERR_SHAPE;
+  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(2 * I, K) || !acts_fit(M, K))
+    return QMM_ERR_SHAPE;
   if (!qmm::aligned(h, out_elem(out_dtype))) return QMM_ERR_ALIGN;
   const Range outs[] = {{h, uint64_t(M * I) * out_elem(out_dtype)}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
@@ -139,6 +167,7 @@ int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint
   a.I = I;
   a.n_out = I;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_SWIGLU, gemm_args(a, M, 2 * I), stream);
   return qmm::launch_gemv(qmm::EPI_SWIGLU, a, M, stream);
 }
 

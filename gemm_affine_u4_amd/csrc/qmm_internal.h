@@ -38,6 +38,23 @@ struct GemvArgs {
   int f32_out;
 };
 
+struct GemmArgs {
+  const uint16_t* x;       // [M][K] bf16
+  const uint32_t* codes;   // [N][K/8]
+  const uint16_t* scales;  // [N][K/64]
+  const uint16_t* biases;  // [N][K/64]
+  const uint16_t* lin_bias;  // nullable [N]
+  void* out0;              // LINEAR: y [M][N]; QKV: q [M][q_out]; SWIGLU: h [M][I]
+  void* out1;              // QKV: k [M][kv_out]
+  void* out2;              // QKV: v [M][kv_out]
+  int64_t M, K, N;         // N = weight rows (SWIGLU: 2*I)
+  int64_t q_out, kv_out, I;
+  int f32_out;
+};
+
+// Prefill GEMM (LDS dequant + MFMA).
+int launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+
 // Decode GEMV; M rows of x processed as independent GEMVs (grid.y).
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
 // Routed experts: stage 1 (gathered gate+up+SwiGLU) and stage 2 (gathered down + combine).

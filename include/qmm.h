@@ -50,10 +50,11 @@
  *     stores the fp32 value that the bf16 mode would round, so bf16 output ==
  *     RNE(fp32 output) bit for bit.
  *   - Row-major everywhere: x [M][K], y [M][N].  Inputs are assumed finite.
- *   - Decode (M == 1) runs a bandwidth-bound GEMV; M > 1 runs an LDS-dequant + MFMA
- *     GEMM ("Sanctum-MLX", "Latency testing": prefill is dominated by the quantized
- *     matmuls).  Results of the two regimes agree to the tolerance, not bit for bit
- *     (the GEMM rounds dequantized weights to bf16).
+ *   - Decode (M <= 8) runs a bandwidth-bound GEMV, once per activation row; larger M
+ *     runs an LDS-dequant + MFMA GEMM ("Sanctum-MLX", "Latency testing": prefill is
+ *     dominated by the quantized matmuls).  Results of the two regimes agree to the
+ *     tolerance, not bit for bit (the GEMM rounds dequantized weights to bf16).
+ *   - M * K * 2 (the activation bytes) must stay below 4 GiB.
  */
 #ifndef QMM_H
 #define QMM_H

@@ -36,9 +36,12 @@ Tolerance (the acceptance rule for a GPU value g against oracle value y):
 evaluated on the GPU's fp32 output before any bf16 rounding.  The first term is
 the stated rule; the second is an fp32 evaluation floor that only matters for
 rows whose weights are (nearly) all exactly zero while their codes are not (see
-`tolerance`); for the workloads' inputs it is below 1e-4 of the first.  Derived
-outputs (SwiGLU, expert combine, a projection fed by an upstream GPU result)
-carry the propagated bounds computed below.
+`tolerance`); for the workloads' inputs it is below 1e-4 of the first.  A kernel
+that rounds each dequantized weight to bf16 before multiplying (the prefill
+design, which dequantizes weight tiles to bf16) adds the exact bound of that
+rounding, sum |x| |w - bf16(w)| (`bf16_weights=True`).  Derived outputs (SwiGLU,
+expert combine, a projection fed by an upstream GPU result) carry the propagated
+bounds computed below.
 """
 from __future__ import annotations
 
@@ -86,12 +89,14 @@ def dequant(codes, scales, biases) -> np.ndarray:
 
 # ---- plain projection --------------------------------------------------------
 
-def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
-    """y[m, n] = sum_k x[m, k] * W[n, k] (+ lin_bias[n]) in fp64, with the two magnitude
-    sums the tolerance is built from:
+def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False):
+    """y[m, n] = sum_k x[m, k] * W[n, k] (+ lin_bias[n]) in fp64, with the magnitude sums
+    the tolerance is built from:
       A[m, n] = sum_k |x[m, k]| * |W[n, k]|  (+ |lin_bias[n]|)
       S[m, n] = sum_k |x[m, k]| * |s[n, k // 64]|   (activation mass weighted by the scale,
                                                      i.e. the size of a one-code change)
+    and, with bf16_weights, R[m, n] = sum_k |x[m, k]| * |W[n, k] - bf16(W[n, k])| (the
+    largest effect of rounding every dequantized weight to bf16, RNE) as a fourth value.
     x_bits: bf16 bits [M, K] (or [K]); codes [N, K/8]; scales/biases [N, K/64];
     lin_bias: optional bf16 bits [N]."""
     x = bf16_to_f64(x_bits)
@@ -104,6 +109,7 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024)
         raise ValueError("x width must equal 8 * words per row")
     y = np.empty((x.shape[0], N))
     A = np.empty((x.shape[0], N))
+    R = np.zeros((x.shape[0], N))
     ax = np.abs(x)
     xg = ax.reshape(x.shape[0], K // GROUP, GROUP).sum(axis=2)          # [M, K/64]
     S = xg @ np.abs(bf16_to_f64(scales)).T
@@ -112,13 +118,16 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024)
         W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
         y[:, r0:r1] = x @ W.T
         A[:, r0:r1] = ax @ np.abs(W).T
+        if bf16_weights:
+            R[:, r0:r1] = ax @ np.abs(W - bf16_to_f64(f32_to_bf16_bits(W))).T
     if lin_bias is not None:
         lb = bf16_to_f64(lin_bias)
         y += lb[None, :]
         A += np.abs(lb)[None, :]
+    out = (y, A, S, R) if bf16_weights else (y, A, S)
     if squeeze:
-        return y[0], A[0], S[0]
-    return y, A, S
+        return tuple(v[0] for v in out)
+    return out
 
 
 def tolerance(A, S) -> np.ndarray:
@@ -130,20 +139,25 @@ def tolerance(A, S) -> np.ndarray:
     return REL_TOL * np.asarray(A) + EVAL_FLOOR * np.asarray(S)
 
 
-def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024):
-    """(y, tol) of one projection; tol per `tolerance`."""
+def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False):
+    """(y, tol) of one projection; tol per `tolerance`.  With bf16_weights (a kernel that
+    rounds each dequantized weight to bf16 before multiplying, as the prefill design
+    does), tol also carries R = sum |x| |w - bf16(w)|, the bound of that rounding."""
+    if bf16_weights:
+        y, A, S, R = project(x_bits, codes, scales, biases, lin_bias, row_block, bf16_weights=True)
+        return y, tolerance(A, S) + R
     y, A, S = project(x_bits, codes, scales, biases, lin_bias, row_block)
     return y, tolerance(A, S)
 
 
 # ---- fused QKV -------------------------------------------------------------
 
-def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=None):
+def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=None, bf16_weights: bool = False):
     """Rows [0, q_out) -> Q, [q_out, q_out+kv_out) -> K, [q_out+kv_out, q_out+2kv_out) -> V.
     Returns ((q, k, v), (tq, tk, tv)): values and per-element tolerances."""
     if codes.shape[0] != q_out + 2 * kv_out:
         raise ValueError("fused QKV weight must have q_out + 2*kv_out rows")
-    y, t = linear(x_bits, codes, scales, biases, lin_bias)
+    y, t = linear(x_bits, codes, scales, biases, lin_bias, bf16_weights=bf16_weights)
     a, b = q_out, q_out + kv_out
     return (y[..., :a], y[..., a:b], y[..., b:]), (t[..., :a], t[..., a:b], t[..., b:])
 
@@ -177,11 +191,11 @@ def swiglu_tol(g, u, tg, tu) -> np.ndarray:
             + SWIGLU_EVAL_REL * (np.abs(h) + SILU_LIPSCHITZ * tg * (np.abs(u) + tu) + np.abs(silu(g)) * tu))
 
 
-def gate_up_swiglu(x_bits, codes, scales, biases, I: int):
+def gate_up_swiglu(x_bits, codes, scales, biases, I: int, bf16_weights: bool = False):
     """Rows [0, I) are gate, [I, 2I) are up.  Returns (h, tol_h)."""
     if codes.shape[0] != 2 * I:
         raise ValueError("fused gate+up weight must have 2*I rows")
-    y, t = linear(x_bits, codes, scales, biases)
+    y, t = linear(x_bits, codes, scales, biases, bf16_weights=bf16_weights)
     g, u = y[..., :I], y[..., I:]
     tg, tu = t[..., :I], t[..., I:]
     return swiglu(g, u), swiglu_tol(g, u, tg, tu)

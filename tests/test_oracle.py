@@ -406,3 +406,26 @@ def test_scale_mass_and_floor():
     z = synth.U4Weight(np.full_like(w.codes, 0x88888888), w.scales, w.biases)
     y0, A0, S0 = orc.project(x, z.codes, z.scales, z.biases)
     assert np.all(y0 == 0) and np.all(A0 == 0) and np.all(S0 > 0)
+
+
+def test_bf16_weight_rounding_term():
+    """R = sum |x| |w - bf16(w)|: zero for weights exact in bf16, equal to the definition
+    (torch's bf16 cast of each weight) otherwise, and never above 2^-9 * A."""
+    w = synth.gen_weight(synth.CFG_TEST, 12, 0, 24, 256, bias="uniform")
+    x = synth.gen_x(synth.CFG_TEST, 12, 0, 3, 256)
+    y, A, S, R = orc.project(x, w.codes, w.scales, w.biases, bf16_weights=True)
+    W = orc.dequant(w.codes, w.scales, w.biases)
+    Wb = torch.from_numpy(W).to(torch.bfloat16).to(torch.float64).numpy()
+    ref = np.abs(orc.bf16_to_f64(x)) @ np.abs(W - Wb).T
+    assert np.allclose(R, ref, rtol=1e-12, atol=0)
+    assert np.all(R <= 2.0 ** -9 * A) and np.any(R > 0)
+    # codes with q - 8 in {-8,-4,-2,-1,0,1,2,4} and bias -8*scale: every weight is exact
+    z = synth.gen_weight(synth.CFG_TEST, 13, 0, 8, 128)
+    allowed = np.array([0, 4, 6, 7, 8, 9, 10, 12], np.uint32)
+    q = allowed[np.random.default_rng(0).integers(0, 8, size=(8, 128))]
+    words = np.array([brute.pack_row(r) for r in q], np.uint32)
+    _, _, _, R0 = orc.project(x[:, :128], words, z.scales, z.biases, bf16_weights=True)
+    assert np.all(R0 == 0)
+    _, t_dec = orc.linear(x, w.codes, w.scales, w.biases)
+    _, t_pre = orc.linear(x, w.codes, w.scales, w.biases, bf16_weights=True)
+    assert np.allclose(t_pre - t_dec, R, rtol=1e-12, atol=1e-300)
