@@ -18,6 +18,8 @@
 // in registers.  Blocks are ordered so the tiles on one XCD (blocks are dealt to the 8
 // XCDs round-robin) walk all row tiles of a few weight tiles: the weight tile stays in
 // that XCD's L2 while the activation tiles stream.
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -28,7 +30,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;        // rows of x per block
 constexpr int kBN = 256;        // weight rows per block
-constexpr int kBK = 64;         // one group
 constexpr int kLdsRow = 72;     // bf16 per LDS row (64 + 8 padding)
 constexpr int kXcds = 8;
 
@@ -94,53 +95,54 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   const uint32_t coff = uint32_t(wrow) * (K >> 1);
   const uint32_t goff = uint32_t(wrow) * groups * 2;
 
-  u32x4_t xv[8];
-  u32x4_t cv[2];
-  uint16_t sv, bv;
-  auto load_step = [&](int ks) {
+  // Global data of one K step, in flight in registers: the x piece of this thread, its
+  // weight row's 8 code words and the group's scale and bias.  Two sets alternate, so
+  // the loads of step k+2 are issued while step k+1 is dequantized and step k multiplied.
+  struct StepRegs {
+    u32x4_t xv[8];
+    u32x4_t cv[2];
+    uint16_t sv, bv;
+  };
+  StepRegs R[2];
+  auto load_step = [&](StepRegs& r, int ks) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j] + uint32_t(ks) * 128u, 0, 0);
+    for (int j = 0; j < 8; ++j) r.xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j] + uint32_t(ks) * 128u, 0, 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      cv[j] = __builtin_amdgcn_raw_buffer_load_b128(cr, coff + uint32_t(ks) * 32u + 16u * j, 0, kLoadNT);
-    sv = __builtin_amdgcn_raw_buffer_load_b16(sr, goff + uint32_t(ks) * 2u, 0, 0);
-    bv = __builtin_amdgcn_raw_buffer_load_b16(br, goff + uint32_t(ks) * 2u, 0, 0);
+      r.cv[j] = __builtin_amdgcn_raw_buffer_load_b128(cr, coff + uint32_t(ks) * 32u + 16u * j, 0, kLoadNT);
+    r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, goff + uint32_t(ks) * 2u, 0, 0);
+    r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, goff + uint32_t(ks) * 2u, 0, 0);
   };
-  // x row -> LDS; codes -> w = s*q + b (fp32) -> bf16 -> LDS
-  auto store_step = [&](int buf) {
+  // Piece p (0..3) of a step into LDS buffer `buf`: x pieces 2p, 2p+1 and code words
+  // 2p, 2p+1 (16 codes -> w = s*q + b in fp32 -> bf16, 32 bytes).
+  auto store_piece = [&](const StepRegs& r, int buf, int p) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4_t*>(&As[buf][(32 * j + (tid >> 3)) * kLdsRow + (tid & 7) * 8]) = xv[j];
-    const float s = bf16_bits_to_f32(sv);
-    const float b = bf16_bits_to_f32(bv);
-    u32x4_t* wd = reinterpret_cast<u32x4_t*>(&Bs[buf][tid * kLdsRow]);
+    for (int j = 2 * p; j < 2 * p + 2; ++j)
+      *reinterpret_cast<u32x4_t*>(&As[buf][(32 * j + (tid >> 3)) * kLdsRow + (tid & 7) * 8]) = r.xv[j];
+    const float s = bf16_bits_to_f32(r.sv);
+    const float b = bf16_bits_to_f32(r.bv);
+    uint32_t out[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int ww = 0; ww < 2; ++ww) {
+      const uint32_t w = r.cv[p >> 1][2 * (p & 1) + ww];
+      // low and high nibbles of the four bytes, then one v_cvt_f32_ubyte{0..3} per code
+      const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
+      const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
+      float f[8];
+      f[0] = fmaf(s, ubyte_f32<0>(lo), b);
+      f[1] = fmaf(s, ubyte_f32<0>(hi), b);
+      f[2] = fmaf(s, ubyte_f32<1>(lo), b);
+      f[3] = fmaf(s, ubyte_f32<1>(hi), b);
+      f[4] = fmaf(s, ubyte_f32<2>(lo), b);
+      f[5] = fmaf(s, ubyte_f32<2>(hi), b);
+      f[6] = fmaf(s, ubyte_f32<3>(lo), b);
+      f[7] = fmaf(s, ubyte_f32<3>(hi), b);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // words 2h and 2h+1 of this 16-byte piece: 16 codes -> 16 bf16 (32 bytes)
-        uint32_t out[8];
-#pragma unroll
-        for (int ww = 0; ww < 2; ++ww) {
-          const uint32_t w = cv[j][2 * h + ww];
-          const uint32_t lo = w & 0x0F0F0F0Fu;
-          const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-          float f[8];
-          f[0] = fmaf(s, ubyte_f32<0>(lo), b);
-          f[1] = fmaf(s, ubyte_f32<0>(hi), b);
-          f[2] = fmaf(s, ubyte_f32<1>(lo), b);
-          f[3] = fmaf(s, ubyte_f32<1>(hi), b);
-          f[4] = fmaf(s, ubyte_f32<2>(lo), b);
-          f[5] = fmaf(s, ubyte_f32<2>(hi), b);
-          f[6] = fmaf(s, ubyte_f32<3>(lo), b);
-          f[7] = fmaf(s, ubyte_f32<3>(hi), b);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) out[4 * ww + e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-        }
-        wd[2 * (2 * j + h)] = u32x4_t{out[0], out[1], out[2], out[3]};
-        wd[2 * (2 * j + h) + 1] = u32x4_t{out[4], out[5], out[6], out[7]};
-      }
+      for (int e = 0; e < 4; ++e) out[4 * ww + e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
     }
+    u32x4_t* wd = reinterpret_cast<u32x4_t*>(&Bs[buf][tid * kLdsRow]);
+    wd[2 * p] = u32x4_t{out[0], out[1], out[2], out[3]};
+    wd[2 * p + 1] = u32x4_t{out[4], out[5], out[6], out[7]};
   };
 
   f32x16_t acc[4][4];
@@ -156,30 +158,58 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   };
   const int lr = lane & 31;        // operand row within a 32-row tile
   const int lk = (lane >> 5) * 8;  // first k of this lane's 8 within a 16-wide k step
+  struct Frags {
+    bf16x8_t a[4], b[4];
+  };
+  auto load_frags = [&](Frags& f, int buf, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(128 * wm + 32 * i + lr) * kLdsRow + kk + lk]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][(btile_row(j) + lr) * kLdsRow + kk + lk]);
+  };
+  auto mfma16 = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
 
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
+  // One K step: request step ks+2 into register set ks&1, multiply LDS buffer ks&1 (four
+  // 16-wide sub-steps, operand fragments of sub-step kk+1 read while kk is multiplied),
+  // and between the sub-steps dequantize step ks+1 from set NX = (ks+1)&1 into the
+  // other LDS buffer.
+  auto kstep = [&](int ks, auto nx_c) {
+    constexpr int NX = decltype(nx_c)::value;
     const int buf = ks & 1;
-    if (ks + 1 < ksteps) load_step(ks + 1);
+    const bool has_next = ks + 1 < ksteps;
+    // step ks was dequantized during the previous step, so its register set is free: request
+    // step ks+2 into it now, a whole step ahead of its use
+    if (ks + 2 < ksteps) load_step(R[NX ^ 1], ks + 2);
+    Frags f[2];
+    load_frags(f[0], buf, 0);
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      bf16x8_t av[4], bw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(128 * wm + 32 * i + lr) * kLdsRow + kk + lk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bw[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][(btile_row(j) + lr) * kLdsRow + kk + lk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bw[j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      if (q + 1 < 4) load_frags(f[(q + 1) & 1], buf, 16 * (q + 1));
+      mfma16(f[q & 1]);
+      if (has_next) store_piece(R[NX], buf ^ 1, q);
     }
-    if (ks + 1 < ksteps) store_step(buf ^ 1);
     __syncthreads();
+  };
+
+  load_step(R[0], 0);
+  if (ksteps > 1) load_step(R[1], 1);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_piece(R[0], 0, q);
+  __syncthreads();
+  // step j lives in register set j&1: even steps dequantize set 1, odd steps set 0
+  int ks = 0;
+  for (; ks + 1 < ksteps; ks += 2) {
+    kstep(ks, std::integral_constant<int, 1>{});
+    kstep(ks + 1, std::integral_constant<int, 0>{});
   }
+  if (ks < ksteps) kstep(ks, std::integral_constant<int, 1>{});
 
   // ---- epilogue -------------------------------------------------------------------
   // acc[i][j] register r of lane l: row 32i + 8(r/4) + 4(l/32) + r%4 of the wave's rows,
