@@ -5,20 +5,25 @@
 // "The Cathedral Doubled Itself" (the two fusions).
 //
 // Tile: 256 (rows of x) x 256 (rows of the weight) per block of 4 waves, one K step
-// = one 64-wide group.  Per step every thread owns one row of each operand tile:
-//   * x row: 64 bf16 (128 B) copied to LDS;
-//   * weight row: 8 code words + the group's scale and bias; each code becomes
-//     w = s*q + b in fp32 (one FMA, exact product), rounded to bf16 (RNE) into LDS.
-// Each wave then computes a 128 x 128 sub-tile with v_mfma_f32_32x32x16_bf16 (4 x 4
-// tiles of 32 x 32, fp32 accumulators), reading both operands from LDS rows padded to
-// 144 B so the 32 rows an MFMA operand spans fall in distinct bank groups.  Two LDS
-// buffers: the global loads of step k+1 are in flight while step k is multiplied.
+// = one 64-wide group.  Per step:
+//   * x tile (256 rows x 128 B) goes global -> LDS directly (buffer_load ... lds), two
+//     steps ahead, into a ring of three LDS stages;
+//   * weight tile: thread t owns weight row t (8 code words + the group's scale and
+//     bias, in registers, requested three steps ahead); each code becomes w = s*q + b in
+//     fp32 (one FMA, exact product), rounded to bf16 (RNE) into one of two LDS stages,
+//     one step ahead, between the multiplies of the current step.
+// Each wave computes a 128 x 128 sub-tile with v_mfma_f32_32x32x16_bf16 (4 x 4 tiles of
+// 32 x 32, fp32 accumulators).  LDS rows are 128 B, unpadded; slot c' (16 B) of row r
+// holds the row's chunk c' ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the rows an
+// MFMA operand read spans (16 consecutive rows at one chunk) hit distinct bank groups.
+// Five 32 KB stages fill the 160 KB of LDS.
 // For SwiGLU a block's 256 weight rows are 128 gate rows and the 128 matching up rows,
 // and each wave's columns are 64 gate + the same 64 up columns, so silu(g)*u is formed
 // in registers.  Blocks are ordered so the tiles on one XCD (blocks are dealt to the 8
 // XCDs round-robin) walk all row tiles of a few weight tiles: the weight tile stays in
 // that XCD's L2 while the activation tiles stream.
 #include <type_traits>
+#include <utility>
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
@@ -28,14 +33,39 @@ namespace qmm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256;        // rows of x per block
-constexpr int kBN = 256;        // weight rows per block
-constexpr int kLdsRow = 72;     // bf16 per LDS row (64 + 8 padding)
+constexpr int kBM = 256;                 // rows of x per block
+constexpr int kBN = 256;                 // weight rows per block
+constexpr int kRow = 64;                 // bf16 per LDS row (one 64-wide group)
+constexpr int kStage = kBM * kRow;       // bf16 per LDS stage (32 KB)
 constexpr int kXcds = 8;
+static_assert(kBM == kBN, "x and weight stages share one shape");
+
+// Bank-group swizzle of LDS row r (see the header).
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
 
 // Byte n of v as a float (v_cvt_f32_ubyte{n}).
 template <int n>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) { return float((v >> (8 * n)) & 0xFFu); }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): loop bodies that
+// index the accumulator registers with compile-time indices however large they are.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and its LDS
+// operations are done, then meet the other waves.  Written as one asm block (a compiler
+// memory barrier) because the compiler's own barrier waits for every outstanding load,
+// including the x tile requested for two steps later.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // Weight row handled by tile row t (0..255) of weight tile nt.  A row past the end
 // maps to the last real row (gate/up pair): its products land in columns that are
@@ -55,8 +85,11 @@ __device__ __forceinline__ int64_t gemm_weight_row(const GemmArgs& a, int64_t nt
 template <int EPI>
 __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t n_tiles,
                                                         int64_t tiles_per_xcd) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdsRow];
+  // One variable per x stage, and the two weight stages in a variable of their own: the
+  // compiler then knows that the x stage being filled by a direct-to-LDS load aliases
+  // neither the x stage nor the weight stage being read.
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[kStage], As1[kStage], As2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t Bs[2 * kStage];
 
   // XCD-aware tile order: the blocks dealt to XCD x take tiles x*tiles_per_xcd + j,
   // row tiles fastest.
@@ -68,83 +101,95 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t K = uint32_t(a.K);
   const uint32_t groups = K >> 6;
   const int ksteps = int(groups);
 
-  // ---- per-thread global sources ----------------------------------------------------
-  // x tile of a step: 256 rows x 128 B, read as 2048 16-byte pieces; piece e = 256 j + tid
-  // is row e / 8, bytes 16 (e % 8), so eight consecutive threads read one 128-B row.
-  // A row past M maps to row M - 1 (never stored).
+  // ---- x tile: global -> LDS ----------------------------------------------------------
+  // Instruction j (0..7) of wave w fills LDS rows 64 w + 8 j + L / 8, slot L % 8 (lane L
+  // lands at byte 16 L); that slot holds chunk (L % 8) ^ swz(row) = (L % 8) ^ (L / 8) ^ (j & 1).
+  // A row past M reads row M - 1 (never stored).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint64_t(a.M) * K * 2);
   uint32_t xoff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int64_t r = mt * kBM + 32 * j + (tid >> 3);
+    int64_t r = mt * kBM + 64 * wave + 8 * j + (lane >> 3);
     if (r >= a.M) r = a.M - 1;
-    xoff[j] = uint32_t(r) * K * 2 + uint32_t(tid & 7) * 16u;
+    const uint32_t chunk = uint32_t((lane & 7) ^ (lane >> 3) ^ (j & 1));
+    xoff[j] = uint32_t(r) * K * 2 + chunk * 16u;
   }
-  // weight tile of a step: thread tid owns weight row tid (8 code words, scale, bias)
-  const int64_t wrow = gemm_weight_row<EPI>(a, nt, tid);
+  auto x_stage = [&](auto p_c) -> uint16_t* {
+    constexpr int P = decltype(p_c)::value;
+    return P == 0 ? As0 : (P == 1 ? As1 : As2);
+  };
+  auto load_x = [&](uint16_t* dst, int ks) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (__attribute__((address_space(3))) void*)(dst + (64 * wave + 8 * j) * kRow), 16, xoff[j],
+          uint32_t(ks) * 128u, 0, 0);
+  };
+
+  // ---- weight tile: global -> registers -> dequant -> LDS -----------------------------
+  // Two lanes per weight row: in load i (0, 1) lane L reads half L / 32 (16 B, 32 codes) of
+  // the step's codes of tile row 64 w + 32 i + L % 32, so one wave load touches 32 rows.
+  // The lane then dequantizes those 32 codes into chunks 4 (L / 32) .. +3 of that row.
+  const int wh = lane >> 5;
   const uint64_t nrows = uint64_t(a.N);
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes, nrows * (K >> 1));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, nrows * groups * 2);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases, nrows * groups * 2);
-  const uint32_t coff = uint32_t(wrow) * (K >> 1);
-  const uint32_t goff = uint32_t(wrow) * groups * 2;
-
-  // Global data of one K step, in flight in registers: the x piece of this thread, its
-  // weight row's 8 code words and the group's scale and bias.  Two sets alternate, so
-  // the loads of step k+2 are issued while step k+1 is dequantized and step k multiplied.
+  uint32_t coff[2], goff[2], wdst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = 64 * wave + 32 * i + (lane & 31);
+    const int64_t wrow = gemm_weight_row<EPI>(a, nt, t);
+    coff[i] = uint32_t(wrow) * (K >> 1) + 16u * uint32_t(wh);
+    goff[i] = uint32_t(wrow) * groups * 2;
+    wdst[i] = uint32_t(t) * kRow;
+  }
+  // one step of this lane's two half rows in flight: 2 x 4 code words, scales, biases;
+  // step j lives in set j % 3
   struct StepRegs {
-    u32x4_t xv[8];
     u32x4_t cv[2];
-    uint16_t sv, bv;
+    uint16_t sv[2], bv[2];
   };
-  StepRegs R[2];
-  auto load_step = [&](StepRegs& r, int ks) {
+  StepRegs R[3];
+  auto load_w = [&](StepRegs& r, int ks) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r.xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j] + uint32_t(ks) * 128u, 0, 0);
+    for (int i = 0; i < 2; ++i) r.cv[i] = __builtin_amdgcn_raw_buffer_load_b128(cr, coff[i] + uint32_t(ks) * 32u, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      r.cv[j] = __builtin_amdgcn_raw_buffer_load_b128(cr, coff + uint32_t(ks) * 32u + 16u * j, 0, kLoadNT);
-    r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, goff + uint32_t(ks) * 2u, 0, 0);
-    r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, goff + uint32_t(ks) * 2u, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      r.sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, goff[i] + uint32_t(ks) * 2u, 0, 0);
+      r.bv[i] = __builtin_amdgcn_raw_buffer_load_b16(br, goff[i] + uint32_t(ks) * 2u, 0, 0);
+    }
   };
-  // Piece p (0..3) of a step into LDS buffer `buf`: x pieces 2p, 2p+1 and code words
-  // 2p, 2p+1 (16 codes -> w = s*q + b in fp32 -> bf16, 32 bytes).
-  auto store_piece = [&](const StepRegs& r, int buf, int p) {
-#pragma unroll
-    for (int j = 2 * p; j < 2 * p + 2; ++j)
-      *reinterpret_cast<u32x4_t*>(&As[buf][(32 * j + (tid >> 3)) * kLdsRow + (tid & 7) * 8]) = r.xv[j];
-    const float s = bf16_bits_to_f32(r.sv);
-    const float b = bf16_bits_to_f32(r.bv);
-    uint32_t out[8];
+  constexpr int kStepLoads = 8 + 2 + 4;  // vector-memory loads one step requests per lane
+  // Piece p (0..3): code words 2 (p & 1), +1 of half row p / 2 (16 codes -> w = s*q + b in
+  // fp32 -> bf16, 32 bytes) into stage `dst`.
+  auto store_piece = [&](const StepRegs& r, uint16_t* dst, int p) {
+    const int i = p >> 1;
+    const float s = bf16_bits_to_f32(r.sv[i]);
+    const float b = bf16_bits_to_f32(r.bv[i]);
+    const uint32_t rsw = swz(wdst[i] / kRow);
 #pragma unroll
     for (int ww = 0; ww < 2; ++ww) {
-      const uint32_t w = r.cv[p >> 1][2 * (p & 1) + ww];
+      const uint32_t w = r.cv[i][2 * (p & 1) + ww];
       // low and high nibbles of the four bytes, then one v_cvt_f32_ubyte{0..3} per code
       const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
       const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
-      float f[8];
-      f[0] = fmaf(s, ubyte_f32<0>(lo), b);
-      f[1] = fmaf(s, ubyte_f32<0>(hi), b);
-      f[2] = fmaf(s, ubyte_f32<1>(lo), b);
-      f[3] = fmaf(s, ubyte_f32<1>(hi), b);
-      f[4] = fmaf(s, ubyte_f32<2>(lo), b);
-      f[5] = fmaf(s, ubyte_f32<2>(hi), b);
-      f[6] = fmaf(s, ubyte_f32<3>(lo), b);
-      f[7] = fmaf(s, ubyte_f32<3>(hi), b);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[4 * ww + e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+      const u32x4_t v = {pack_bf16x2(fmaf(s, ubyte_f32<0>(lo), b), fmaf(s, ubyte_f32<0>(hi), b)),
+                         pack_bf16x2(fmaf(s, ubyte_f32<1>(lo), b), fmaf(s, ubyte_f32<1>(hi), b)),
+                         pack_bf16x2(fmaf(s, ubyte_f32<2>(lo), b), fmaf(s, ubyte_f32<2>(hi), b)),
+                         pack_bf16x2(fmaf(s, ubyte_f32<3>(lo), b), fmaf(s, ubyte_f32<3>(hi), b))};
+      const uint32_t chunk = uint32_t(4 * wh + 2 * (p & 1) + ww);
+      *reinterpret_cast<u32x4_t*>(dst + wdst[i] + (chunk ^ rsw) * 8) = v;
     }
-    u32x4_t* wd = reinterpret_cast<u32x4_t*>(&Bs[buf][tid * kLdsRow]);
-    wd[2 * p] = u32x4_t{out[0], out[1], out[2], out[3]};
-    wd[2 * p + 1] = u32x4_t{out[4], out[5], out[6], out[7]};
   };
 
+  // ---- MFMA operands from LDS ---------------------------------------------------------
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -156,107 +201,205 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     if constexpr (EPI == EPI_SWIGLU) return (j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1);
     else return 128 * wn + 32 * j;
   };
-  const int lr = lane & 31;        // operand row within a 32-row tile
-  const int lk = (lane >> 5) * 8;  // first k of this lane's 8 within a 16-wide k step
+  // Operand lane l holds row l % 32 of a 32-row tile and k 8 (l / 32) .. +7 of a 16-wide
+  // sub-step q, i.e. chunk 2q + l / 32 of the row; tiles start at multiples of 32 rows,
+  // so swz(row) = swz(l % 32) and one offset per q serves every tile of both operands.
+  const uint32_t lr = uint32_t(lane & 31);
+  uint32_t opoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) opoff[q] = lr * kRow + (uint32_t(2 * q + (lane >> 5)) ^ swz(lr)) * 8u;
   struct Frags {
     bf16x8_t a[4], b[4];
   };
-  auto load_frags = [&](Frags& f, int buf, int kk) {
+  auto load_frags = [&](Frags& f, const uint16_t* as, const uint16_t* bs, int q) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      f.a[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(128 * wm + 32 * i + lr) * kLdsRow + kk + lk]);
+      f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      f.b[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][(btile_row(j) + lr) * kLdsRow + kk + lk]);
+    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(bs + btile_row(j) * kRow + opoff[q]);
   };
   auto mfma16 = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
 
-  // One K step: request step ks+2 into register set ks&1, multiply LDS buffer ks&1 (four
-  // 16-wide sub-steps, operand fragments of sub-step kk+1 read while kk is multiplied),
-  // and between the sub-steps dequantize step ks+1 from set NX = (ks+1)&1 into the
-  // other LDS buffer.
-  auto kstep = [&](int ks, auto nx_c) {
-    constexpr int NX = decltype(nx_c)::value;
-    const int buf = ks & 1;
-    const bool has_next = ks + 1 < ksteps;
-    // step ks was dequantized during the previous step, so its register set is free: request
-    // step ks+2 into it now, a whole step ahead of its use
-    if (ks + 2 < ksteps) load_step(R[NX ^ 1], ks + 2);
-    Frags f[2];
-    load_frags(f[0], buf, 0);
+  // Instruction order inside a slot: the wave issues in order and an MFMA waits for the
+  // matrix pipe, so the dequantization's ~48 VALU ops are spread 3 per MFMA (they then
+  // run while the MFMA executes) and its two LDS stores go late in the slot.
+  auto interleave_slot = [&]() {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q + 1 < 4) load_frags(f[(q + 1) & 1], buf, 16 * (q + 1));
-      mfma16(f[q & 1]);
-      if (has_next) store_piece(R[NX], buf ^ 1, q);
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+      if (i == 13) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // 2 LDS stores
     }
-    __syncthreads();
   };
 
-  load_step(R[0], 0);
-  if (ksteps > 1) load_step(R[1], 1);
+  // K loop.  Step j's x tile lives in x stage j % 3, its dequantized weights in weight
+  // stage j & 1, its raw weights in register set j % 3.  Each step is four slots of 16
+  // MFMAs (one 16-wide sub-step each); in every slot the operand fragments of the next
+  // sub-step are read from LDS and a quarter of the next step's weights is dequantized.
+  // The one barrier of a step, X, sits before its last slot, when every fragment of the
+  // step has been read into registers: after X the step's x and weight stages are free,
+  // and the first fragments of the next step are read while the last 16 MFMAs run.
+  // Before X a wave waits for its x of the next step and the raw weights of the one after,
+  // requested after the barrier two steps back: only the loads requested after the
+  // previous barrier (kStepLoads) may still be in flight.  Requested steps are clamped to
+  // the last one, so every step issues the same loads and nothing branches; the extra
+  // copies land in stages and registers that are never read again.
+  Frags f[2];
+  auto iteration = [&](int ks, auto p_c) {
+    constexpr int P = decltype(p_c)::value;
+    const uint16_t* as = x_stage(p_c);
+    const uint16_t* bs = Bs + (ks & 1) * kStage;
+    uint16_t* bnext = Bs + ((ks + 1) & 1) * kStage;
+    // slots 0..2: sub-steps 0..2 of step ks, pieces 1..3 of step ks+1's weights
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_piece(R[0], 0, q);
-  __syncthreads();
-  // step j lives in register set j&1: even steps dequantize set 1, odd steps set 0
+    for (int q = 0; q < 3; ++q) {
+      load_frags(f[(q + 1) & 1], as, bs, q + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma16(f[q & 1]);
+      store_piece(R[(P + 1) % 3], bnext, q + 1);
+      interleave_slot();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_loads_barrier<kStepLoads>();
+    // x stage P and weight stage ks & 1 are free: request x of step ks+3 and the weights
+    // of step ks+4 (register set (ks+1) % 3, whose step was just dequantized)
+    load_x(x_stage(p_c), min(ks + 3, ksteps - 1));
+    load_w(R[(P + 1) % 3], min(ks + 4, ksteps - 1));
+    // slot 3: sub-step 3 of step ks, fragments of step ks+1's sub-step 0, piece 0 of step
+    // ks+2's weights into the freed weight stage
+    load_frags(f[0], x_stage(std::integral_constant<int, (P + 1) % 3>{}), bnext, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma16(f[1]);
+    store_piece(R[(P + 2) % 3], Bs + (ks & 1) * kStage, 0);
+    interleave_slot();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Prologue, ending in the state an iteration expects: x of steps 0 and 1 and the raw
+  // weights of steps 1 and 2 landed or in flight as if requested two and one barriers
+  // back, step 0 dequantized and published, x of step 2 and weights of step 3 requested
+  // after the last barrier, step 0's first fragments read and step 1's first piece
+  // dequantized.
+  load_x(As0, 0);
+  load_w(R[0], 0);
+  load_w(R[1], min(1, ksteps - 1));
+  __builtin_amdgcn_s_waitcnt(0);  // the compiler accounts for this full wait too
+#pragma unroll
+  for (int p = 0; p < 4; ++p) store_piece(R[0], Bs, p);
+  load_x(As1, min(1, ksteps - 1));
+  load_w(R[2], min(2, ksteps - 1));
+  wait_loads_barrier<kStepLoads>();
+  load_x(As2, min(2, ksteps - 1));
+  load_w(R[0], min(3, ksteps - 1));
+  load_frags(f[0], As0, Bs, 0);
+  store_piece(R[1], Bs + kStage, 0);
   int ks = 0;
-  for (; ks + 1 < ksteps; ks += 2) {
-    kstep(ks, std::integral_constant<int, 1>{});
-    kstep(ks + 1, std::integral_constant<int, 0>{});
+  for (; ks + 2 < ksteps; ks += 3) {
+    iteration(ks, std::integral_constant<int, 0>{});
+    iteration(ks + 1, std::integral_constant<int, 1>{});
+    iteration(ks + 2, std::integral_constant<int, 2>{});
   }
-  if (ks < ksteps) kstep(ks, std::integral_constant<int, 1>{});
+  if (ks < ksteps) iteration(ks, std::integral_constant<int, 0>{});
+  if (ks + 1 < ksteps) iteration(ks + 1, std::integral_constant<int, 1>{});
 
   // ---- epilogue -------------------------------------------------------------------
-  // acc[i][j] register r of lane l: row 32i + 8(r/4) + 4(l/32) + r%4 of the wave's rows,
-  // column 32j + l%32 of its columns.
-  const int64_t row_base = mt * kBM + 128 * wm;
-  const int col = lane & 31;
-  const int rsub = 4 * (lane >> 5);
-  if constexpr (EPI == EPI_SWIGLU) {
+  // The MFMA takes the weight fragment as its first operand, so acc[i][j] is the
+  // transposed tile: register r of lane l holds output row 32i + l%32 of the wave's rows
+  // and output column (weight row) 32j + 8(r/4) + 4(l/32) + r%4 of the wave's columns.
+  // A lane thus owns 4 consecutive columns of one row per register quad and writes them
+  // with one 8-byte (bf16) or 16-byte (fp32) store where they share a destination and the
+  // address is aligned, element by element otherwise (ragged edges, odd row strides).
+  const int64_t mrow0 = mt * kBM + 128 * wm + (lane & 31);
+  const int csub = 4 * (lane >> 5);
+  auto put = [&](void* dst, int64_t ld, int64_t cn, int64_t m, const float (&v)[4], int nvalid) {
+    const int64_t idx = m * ld + cn;
+    if (nvalid == 4 && (idx & 3) == 0) {
+      if (a.f32_out) {
+        *reinterpret_cast<float4*>(static_cast<float*>(dst) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + idx) =
+            make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                       f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t p = nt * (kBN / 2) + 64 * wn + 32 * j + col;
-      if (p >= a.I) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = row_base + 32 * i + 8 * (r >> 2) + rsub + (r & 3);
-          if (m < a.M) store_out(a.out0, m * a.I + p, silu_times(acc[i][j][r], acc[i][j + 2][r]), a.f32_out);
-        }
+      for (int e = 0; e < 4; ++e)
+        if (e < nvalid) store_out(dst, idx + e, v[e], a.f32_out);
     }
-  } else {
+  };
+  if constexpr (EPI == EPI_SWIGLU) {
+    static_for<8>([&](auto jg) {
+      constexpr int j = decltype(jg)::value / 4, g = decltype(jg)::value % 4;
+      {
+        const int64_t p0 = nt * (kBN / 2) + 64 * wn + 32 * j + 8 * g + csub;
+        if (p0 >= a.I) return;
+        const int nvalid = int(min<int64_t>(4, a.I - p0));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = nt * kBN + 128 * wn + 32 * j + col;
-      if (n >= a.N) continue;
-      const float lb = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[n]) : 0.f;
-      void* dst;
-      int64_t cn, ld;
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = mrow0 + 32 * i;
+          if (m >= a.M) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[i][j][4 * g + e], acc[i][j + 2][4 * g + e]);
+          put(a.out0, a.I, p0, m, v, nvalid);
+        }
+      }
+    });
+  } else {
+    // output column n -> destination, row stride, column there, end of its range
+    auto route = [&](int64_t n, void*& dst, int64_t& ld, int64_t& cn, int64_t& end) {
       if constexpr (EPI == EPI_QKV) {
         if (n < a.q_out) {
-          dst = a.out0; cn = n; ld = a.q_out;
+          dst = a.out0; ld = a.q_out; cn = n; end = a.q_out;
         } else if (n < a.q_out + a.kv_out) {
-          dst = a.out1; cn = n - a.q_out; ld = a.kv_out;
+          dst = a.out1; ld = a.kv_out; cn = n - a.q_out; end = a.q_out + a.kv_out;
         } else {
-          dst = a.out2; cn = n - a.q_out - a.kv_out; ld = a.kv_out;
+          dst = a.out2; ld = a.kv_out; cn = n - a.q_out - a.kv_out; end = a.N;
         }
       } else {
-        dst = a.out0; cn = n; ld = a.N;
+        dst = a.out0; ld = a.N; cn = n; end = a.N;
       }
+    };
+    static_for<16>([&](auto jg) {
+      constexpr int j = decltype(jg)::value / 4, g = decltype(jg)::value % 4;
+      {
+        const int64_t n0 = nt * kBN + 128 * wn + 32 * j + 8 * g + csub;
+        if (n0 >= a.N) return;
+        float lb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int e = 0; e < 4; ++e)
+          lb[e] = (a.lin_bias && n0 + e < a.N) ? bf16_bits_to_f32(a.lin_bias[n0 + e]) : 0.f;
+        void* dst;
+        int64_t ld, cn, end;
+        route(n0, dst, ld, cn, end);
+        const bool one_range = n0 + 3 < end;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = row_base + 32 * i + 8 * (r >> 2) + rsub + (r & 3);
-          if (m < a.M) store_out(dst, m * ld + cn, acc[i][j][r] + lb, a.f32_out);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = mrow0 + 32 * i;
+          if (m >= a.M) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + lb[e];
+          if (one_range) {
+            put(dst, ld, cn, m, v, 4);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (n0 + e >= a.N) continue;
+              void* d1;
+              int64_t ld1, cn1, end1;
+              route(n0 + e, d1, ld1, cn1, end1);
+              store_out(d1, m * ld1 + cn1, v[e], a.f32_out);
+            }
+          }
         }
-    }
+      }
+    });
   }
 }
 
