@@ -1,14 +1,24 @@
-"""Benchmark of the decode hot path: fused QKV GEMV + fused gate+up+SwiGLU GEMV at M = 1
-on 14B-shaped layers (hidden 5120, 40 q heads / 8 kv heads of 128, intermediate 13824),
-u4 group-64 weights, seeded synthetic inputs resident in HBM.
+"""Benchmark of the u4 group-64 affine quantized matmul hot path on one GPU.
 
-One step = one fused-QKV call and one fused-gate+up call on the next layer of a
-48-layer rotating pool (4.8 GB, far above the 256 MB last-level cache), each step
-with its own activation vector.  The timed region replays a HIP graph holding all
-K steps, bracketed by device synchronisation; the value is algorithmic bytes moved
-per second (packed codes + bf16 scales/biases + activations + outputs).
+Headline (`value`): the 14B-shaped decode step at M = 1, fused QKV GEMV + fused
+gate+up+SwiGLU GEMV (hidden 5120, 40 q heads / 8 kv heads of 128, intermediate 13824),
+u4 group-64 weights, seeded synthetic inputs resident in HBM.  One step = one fused-QKV
+call and one fused-gate+up call on the next layer of a 48-layer rotating pool (4.8 GB,
+far above the 256 MB last-level cache), each step with its own activation vector.  The
+timed region replays a HIP graph holding all K steps, bracketed by device
+synchronisation; the value is algorithmic bytes moved per second (packed codes + bf16
+scales/biases + activations + outputs).
 
-Prints one JSON line (see the design doc for the fields).
+Also reported, each timed the same way (HIP graphs on one stream, events around them):
+  * prefill GEMM at M = 2048 on the 14B layer (fused QKV, fused gate+up+SwiGLU) in
+    TFLOP/s against the bf16 MFMA peak, with a dense bf16 torch.matmul of the same shape
+    as context;
+  * the 24B-dense-shaped decode step (40 layers of QKV + gate+up + down, fresh x per
+    step, each layer's down on that layer's h);
+  * the 35B-A3B-shaped MoE decode layer (top-8 of 256 experts gathered in place, stage 1
+    gate+up+SwiGLU and stage 2 down + weighted combine, fresh routing per step and layer).
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -24,7 +34,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
 def _args():
@@ -37,6 +48,11 @@ def _args():
     ap.add_argument("--cpu-sample-steps", type=int, default=6)
     ap.add_argument("--kernel-reps", type=int, default=1000,
                     help="launches per graph when timing one kernel on its own")
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--step24-steps", type=int, default=20)
+    ap.add_argument("--moe-steps", type=int, default=20)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the prefill, 24B-step and MoE measurements")
     return ap.parse_args()
 
 
@@ -66,6 +82,47 @@ def weight_bytes(rows: int, K: int) -> int:
     return rows * K // 2 + 2 * rows * (K // 64) * 2
 
 
+class Timer:
+    """HIP graphs captured and replayed on one stream, timed with events on that stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def capture(self, fn, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            fn(0)  # touch once outside capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(self, g, reps=1):
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(self.stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def per_call_ms(self, fn, n):
+        """Average duration of one call of fn over a graph of n calls (after one warm replay)."""
+        g = self.capture(fn, n)
+        self.replay_ms(g)
+        ms = self.replay_ms(g) / n
+        del g
+        return ms
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -88,21 +145,9 @@ def main():
     w_qkv = synth.gen_weight(synth.CFG_14B, 0, synth.PROJ_QKV, rows_qkv, K)
     w_gu = synth.gen_weight(synth.CFG_14B, 0, synth.PROJ_GATE_UP, rows_gu, K)
 
-    def up(a):
-        return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a.view(np.int16)).to(dev)
-
-    def pool_of(w, P):
-        out = []
-        for arr in (w.codes, w.scales, w.biases):
-            t = up(arr)
-            stack = torch.empty((P,) + tuple(t.shape), dtype=t.dtype, device=dev)
-            stack.copy_(t.unsqueeze(0).expand_as(stack))
-            out.append(stack)
-        return out
-
     P = args.pool
-    pq = pool_of(w_qkv, P)
-    pg = pool_of(w_gu, P)
+    pq = pool_of(torch, dev, w_qkv, P)
+    pg = pool_of(torch, dev, w_gu, P)
     NX = 16
     xs = torch.from_numpy(np.concatenate([synth.gen_x(synth.CFG_14B, 0, s, 1, K) for s in range(NX)]).view(np.int16)).to(dev)
     q = torch.empty((1, q_out), dtype=torch.bfloat16, device=dev)
@@ -116,6 +161,7 @@ def main():
     bytes_step = bytes_qkv + bytes_gu
 
     stream = torch.cuda.Stream()
+    T = Timer(torch, stream)
 
     def step(i):
         L = i % P
@@ -131,67 +177,27 @@ def main():
         L = i % P
         qmm.qmm_fused_qkv(xs[i % NX], pq[0][L], pq[1][L], pq[2][L], q, k, v, stream=stream)
 
-    def capture(fn, n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            fn(0)  # touch once outside capture
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(n):
-                    fn(i)
-        torch.cuda.synchronize()
-        return g
-
-    def timed_replay(g, reps=1):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-        e1.synchronize()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)  # ms
-
     # warmup (eager), then the timed graph of exactly K steps
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
     torch.cuda.synchronize()
-    g_step = capture(step, args.steps)
+    g_step = T.capture(step, args.steps)
     with torch.cuda.stream(stream):
         g_step.replay()
     torch.cuda.synchronize()
-    ms_total = timed_replay(g_step)
+    ms_total = T.replay_ms(g_step)
+    del g_step
     ms_per_step = ms_total / args.steps
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     # per-kernel average duration of the dominant kernel (gate+up GEMV), same stream
-    n_k = args.kernel_reps
-    g_gu = capture(gate_up_only, n_k)
-    timed_replay(g_gu)
-    ms_gu = timed_replay(g_gu) / n_k
-    g_qkv = capture(qkv_only, n_k)
-    timed_replay(g_qkv)
-    ms_qkv = timed_replay(g_qkv) / n_k
+    ms_gu = T.per_call_ms(gate_up_only, args.kernel_reps)
+    ms_qkv = T.per_call_ms(qkv_only, args.kernel_reps)
     ach_gu = bytes_gu / (ms_gu * 1e-3) / 1e9
     ach_qkv = bytes_qkv / (ms_qkv * 1e-3) / 1e9
 
-    # plain device copy of 2 GB: the read+write ceiling a simple kernel reaches
-    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
-    src.fill_(1)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record()
-    e1.synchronize()
-    copy_gbs = 10 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    copy_gbs = device_copy_gbs(torch, dev)
 
     result = {
         "metric": "achieved HBM GB/s (% of peak) fused u4 GEMV M=1; prefill GEMM TFLOP/s",
@@ -222,10 +228,176 @@ def main():
         "device_copy_GBps": round(copy_gbs, 1),
     }
 
+    if not args.headline_only:
+        result["prefill_gemm"] = bench_prefill(torch, qmm, synth, T, dev, pq, pg, args.prefill_reps)
+        del pq, pg
+        torch.cuda.empty_cache()
+        result["decode_24B_step"] = bench_step_24b(torch, qmm, synth, T, dev, args.step24_steps)
+        torch.cuda.empty_cache()
+        result["moe_35B_layer"] = bench_moe(torch, qmm, synth, T, dev, args.moe_steps)
+        torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps, w_qkv, w_gu, bytes_step)
 
     print(json.dumps(result), flush=True)
+
+
+def up(torch, dev, a):
+    return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a.view(np.int16)).to(dev)
+
+
+def pool_of(torch, dev, w, P):
+    """P device copies of one seeded weight: [P, rows, ...] for codes, scales, biases."""
+    out = []
+    for arr in (w.codes, w.scales, w.biases):
+        t = up(torch, dev, arr)
+        stack = torch.empty((P,) + tuple(t.shape), dtype=t.dtype, device=dev)
+        stack.copy_(t.unsqueeze(0).expand_as(stack))
+        out.append(stack)
+    return out
+
+
+def device_copy_gbs(torch, dev):
+    """Plain device copy of 2 GB: the read+write ceiling a simple kernel reaches."""
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbs = 10 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def bench_prefill(torch, qmm, synth, T, dev, pq, pg, reps):
+    """Prefill GEMM at M = 2048 on the 14B layer 0: fused QKV and fused gate+up+SwiGLU,
+    plus a dense bf16 torch.matmul of each shape (context only)."""
+    sh = synth.DENSE_14B
+    M, K, I = synth.PREFILL_M, sh.K, sh.I
+    x = up(torch, dev, synth.gen_x(synth.CFG_PREFILL, 0, 0, M, K))
+    q = torch.empty((M, sh.q_out), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((M, sh.kv_out), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((M, sh.kv_out), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    st = T.stream
+    ms_qkv = T.per_call_ms(lambda i: qmm.qmm_fused_qkv(x, pq[0][0], pq[1][0], pq[2][0], q, k, v, stream=st), reps)
+    ms_gu = T.per_call_ms(lambda i: qmm.qmm_fused_gate_up_swiglu(x, pg[0][0], pg[1][0], pg[2][0], h, stream=st), reps)
+    fl_qkv = 2.0 * M * sh.qkv_rows * K
+    fl_gu = 2.0 * M * 2 * I * K
+
+    def dense(N):
+        a = torch.randn((M, K), device=dev, dtype=torch.bfloat16)
+        b = torch.randn((K, N), device=dev, dtype=torch.bfloat16)  # contiguous [K, N]
+        c = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+        ms = T.per_call_ms(lambda i: torch.matmul(a, b, out=c), reps)
+        del a, b, c
+        return ms
+
+    ms_dq, ms_dg = dense(sh.qkv_rows), dense(2 * I)
+
+    def rec(ms, fl, name):
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"kernel": name, "avg_launch_us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                "frac_of_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flop": fl}
+
+    return {"workload": f"M={M} x K={K}: fused QKV [{sh.qkv_rows} rows] and fused gate+up+SwiGLU "
+                        f"[{2 * I} rows], bf16 out, u4 g64 weights of the 14B layer",
+            "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+            "fused_qkv": rec(ms_qkv, fl_qkv, "gemm_u4_kernel<QKV>"),
+            "fused_gate_up": rec(ms_gu, fl_gu, "gemm_u4_kernel<SWIGLU>"),
+            "context_torch_bf16_matmul": {"qkv_shape": rec(ms_dq, fl_qkv, "torch.matmul bf16 (hipBLASLt)"),
+                                          "gate_up_shape": rec(ms_dg, fl_gu, "torch.matmul bf16 (hipBLASLt)")}}
+
+
+def bench_step_24b(torch, qmm, synth, T, dev, n_steps):
+    """24B-dense-shaped decode step: 40 layers of fused QKV + fused gate+up+SwiGLU + down,
+    each step with fresh x; a layer's down reads that layer's h."""
+    sh = synth.DENSE_24B
+    K, I = sh.K, sh.I
+    L = 40
+    w_qkv = synth.gen_weight(synth.CFG_24B, 0, synth.PROJ_QKV, sh.qkv_rows, K)
+    w_gu = synth.gen_weight(synth.CFG_24B, 0, synth.PROJ_GATE_UP, 2 * I, K)
+    w_dn = synth.gen_weight(synth.CFG_24B, 0, synth.PROJ_DOWN, K, I)
+    pq, pg, pd = pool_of(torch, dev, w_qkv, L), pool_of(torch, dev, w_gu, L), pool_of(torch, dev, w_dn, L)
+    del w_qkv, w_gu, w_dn
+    xs = up(torch, dev, np.concatenate([synth.gen_x(synth.CFG_24B, 0, s, 1, K) for s in range(n_steps)]))
+    q = torch.empty((1, sh.q_out), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((1, sh.kv_out), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((1, sh.kv_out), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((1, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, K), dtype=torch.bfloat16, device=dev)
+    st = T.stream
+
+    def one_step(s):
+        x = xs[s % n_steps]
+        for l in range(L):
+            qmm.qmm_fused_qkv(x, pq[0][l], pq[1][l], pq[2][l], q, k, v, stream=st)
+            qmm.qmm_fused_gate_up_swiglu(x, pg[0][l], pg[1][l], pg[2][l], h, stream=st)
+            qmm.qmm_linear(h, pd[0][l], pd[1][l], pd[2][l], y, stream=st)
+
+    g = T.capture(one_step, n_steps)
+    T.replay_ms(g)
+    ms = T.replay_ms(g) / n_steps
+    del g
+    b_layer = (weight_bytes(sh.qkv_rows, K) + K * 2 + sh.qkv_rows * 2
+               + weight_bytes(2 * I, K) + K * 2 + I * 2
+               + weight_bytes(K, I) + I * 2 + K * 2)
+    b_step = L * b_layer
+    gbs = b_step / (ms * 1e-3) / 1e9
+    return {"workload": f"24B-dense decode step M=1: {L} layers x (QKV [{sh.qkv_rows}x{K}] + gate+up "
+                        f"[{2 * I}x{K}] + down [{K}x{I}]), fresh x per step, {n_steps} steps in one graph",
+            "ms_per_step": round(ms, 4), "bytes_per_step": b_step, "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_step": 3 * L}
+
+
+def bench_moe(torch, qmm, synth, T, dev, n_steps):
+    """35B-A3B-shaped MoE decode: per layer, stage 1 (gathered gate+up+SwiGLU of the 8
+    routed experts) and stage 2 (gathered down + weighted combine), over a 40-layer pool
+    of in-place expert grids, fresh routing per step and layer."""
+    sh = synth.MOE_35B
+    H, E, Ie, topk = sh.hidden, sh.E, sh.I, sh.topk
+    L = 40
+    g_gu = synth.gen_expert_grid(synth.CFG_MOE, 0, synth.PROJ_MOE_GATE_UP, E, 2 * Ie, H)
+    g_dn = synth.gen_expert_grid(synth.CFG_MOE, 0, synth.PROJ_MOE_DOWN, E, H, Ie)
+    pgu, pdn = pool_of(torch, dev, g_gu, L), pool_of(torch, dev, g_dn, L)
+    del g_gu, g_dn
+    ids = np.zeros((n_steps, L, topk), np.int32)
+    pw = np.zeros((n_steps, L, topk), np.float32)
+    for s in range(n_steps):
+        for l in range(L):
+            ids[s, l], pw[s, l] = synth.gen_routing(synth.CFG_MOE, l, s, E, topk)
+    ids_d = torch.from_numpy(ids).to(dev)
+    pw_d = torch.from_numpy(pw).to(dev)
+    xs = up(torch, dev, np.concatenate([synth.gen_x(synth.CFG_MOE, 0, s, 1, H) for s in range(n_steps)]))
+    hk = torch.empty((topk, Ie), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((H,), dtype=torch.bfloat16, device=dev)
+    st = T.stream
+
+    def one_step(s):
+        s %= n_steps
+        for l in range(L):
+            qmm.qmm_moe_gather(qmm.QMM_MOE_GATE_UP_SWIGLU, xs[s], pgu[0][l], pgu[1][l], pgu[2][l], ids_d[s, l], hk,
+                               stream=st)
+            qmm.qmm_moe_gather(qmm.QMM_MOE_DOWN_COMBINE, hk, pdn[0][l], pdn[1][l], pdn[2][l], ids_d[s, l], y,
+                               expert_w=pw_d[s, l], stream=st)
+
+    g = T.capture(one_step, n_steps)
+    T.replay_ms(g)
+    ms_layer = T.replay_ms(g) / (n_steps * L)
+    del g
+    b_layer = (topk * (weight_bytes(2 * Ie, H) + weight_bytes(H, Ie))
+               + H * 2 + 2 * topk * Ie * 2 + H * 2 + topk * 8)
+    gbs = b_layer / (ms_layer * 1e-3) / 1e9
+    return {"workload": f"35B-A3B-shaped MoE decode M=1: top-{topk} of {E} experts, hidden {H}, expert I {Ie}, "
+                        f"{L}-layer pool, fresh routing per step and layer, {n_steps} steps in one graph",
+            "us_per_layer": round(ms_layer * 1e3, 3), "bytes_per_layer": b_layer, "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_layer": 2}
 
 
 def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step):
