@@ -123,7 +123,7 @@ __host__ __device__ constexpr int threads_per_block() { return 64 * KS * groups_
 // One wave (one row group) walks `upw` consecutive row units with DEPTH - 1 units of
 // code loads in flight ahead of the one being computed.
 #ifndef QMM_GEMV_DEPTH
-#define QMM_GEMV_DEPTH 3
+#define QMM_GEMV_DEPTH 1
 #endif
 #ifndef QMM_GEMV_WAVES_PER_CU
 #define QMM_GEMV_WAVES_PER_CU 8
@@ -259,6 +259,189 @@ __global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvAr
   }
 }
 
+// ---- single-slice decode kernel (ksplit == 1: K <= 5120) --------------------------------
+// The same per-row arithmetic and reduction order as gemv_u4_kernel (results are bit for
+// bit the same), but the activations, which every wave needs in full, are staged once
+// per block in LDS: each 32-code chunk permuted to the nibble-pair order, with its chunk
+// sum.  A wave then reads its chunks from LDS instead of issuing its own global loads
+// (the two row slots of a wave used to fetch the same activations), and its first row
+// units' codes are already in flight while the block stages them.
+constexpr int kXStride = 20;  // words per staged activation chunk (16 + 4 padding)
+constexpr int kWavesS1 = 4;   // waves (row groups) per block
+
+template <int LPR, int CPL>
+struct S1Layout {
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int C = LPR * CPL;                // chunks a row slot covers
+  static constexpr int x_words = C * kXStride + C;  // permuted activations, then chunk sums
+  static constexpr size_t lds_bytes() { return size_t(x_words) * 4; }
+};
+
+// Store of one row unit's result (slot totals after slot_reduce).
+template <int LPR, int EPI>
+__device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u, int slot, int lane,
+                                           int64_t out_base) {
+  constexpr int RPI = 64 / LPR;
+  constexpr int P = RPI / 2;
+  bool valid;
+  const int64_t r = unit_row<LPR, EPI>(u, slot, a, &valid);
+  if constexpr (EPI == EPI_SWIGLU) {
+    const float up = __shfl_xor(v, 32);
+    if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
+      store_out(a.out0, out_base + u * P + slot, silu_times(v, up), a.f32_out);
+  } else {
+    if (valid && lane == slot_result_lane<LPR>(slot)) {
+      if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
+      if constexpr (EPI == EPI_QKV) {
+        if (r < a.q_out) {
+          store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
+        } else if (r < a.q_out + a.kv_out) {
+          store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
+        } else {
+          store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
+        }
+      } else {
+        store_out(a.out0, out_base + r, v, a.f32_out);
+      }
+    }
+  }
+}
+
+#ifndef QMM_S1_DEPTH
+#define QMM_S1_DEPTH 1
+#endif
+#ifndef QMM_S1_WAVES_PER_CU
+#define QMM_S1_WAVES_PER_CU 12
+#endif
+template <int LPR, int CPL, int EPI, bool MOE, int DEPTH = QMM_S1_DEPTH>
+#ifndef QMM_S1_MINW
+#define QMM_S1_MINW 1
+#endif
+__global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(GemvArgs a, int64_t units, int upw) {
+  using Lay = S1Layout<LPR, CPL>;
+  constexpr int RPI = Lay::RPI;
+  constexpr int P = RPI / 2;
+  constexpr int C = Lay::C;
+  extern __shared__ __attribute__((aligned(16))) uint32_t s1_lds[];
+  uint32_t* xl = s1_lds;
+  float* xsl = reinterpret_cast<float*>(s1_lds + C * kXStride);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slot = lane / LPR;
+  const int li = lane % LPR;
+  const int64_t words = a.K >> 3;
+  const int64_t groups = a.K >> 6;
+  const int64_t u_begin = (int64_t(blockIdx.x) * kWavesS1 + wave) * upw;
+  const int64_t u_end = u_begin + upw < units ? u_begin + upw : units;
+
+  const uint32_t* codes = a.codes;
+  const uint16_t* scales = a.scales;
+  const uint16_t* biases = a.biases;
+  const uint16_t* x = a.x;
+  int64_t out_base;
+  if constexpr (MOE) {
+    // blockIdx.y is the routed slot k (the whole block shares it); its expert's rows are
+    // read in place from the grid.
+    const int k = blockIdx.y;
+    const int32_t e = a.expert_ids[k];
+    out_base = int64_t(k) * a.I;
+    if (e < 0 || e >= a.E) {
+      // no expert: this slot's h is zero
+      for (int64_t u = u_begin; u < u_end; ++u) {
+        bool valid;
+        (void)unit_row<LPR, EPI>(u, slot, a, &valid);
+        if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
+          store_out(a.out0, out_base + u * P + slot, 0.f, a.f32_out);
+      }
+      return;
+    }
+    const int64_t off = int64_t(e) * a.rows;
+    codes += off * words;
+    scales += off * groups;
+    biases += off * groups;
+  } else {
+    x += int64_t(blockIdx.y) * a.K;
+    out_base = int64_t(blockIdx.y) * a.n_out;
+  }
+
+  const uint32_t row_bytes = uint32_t(a.K >> 1);
+  const uint64_t nrows = uint64_t(a.rows);
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, nrows * row_bytes);
+  const uint32_t c0 = uint32_t(li);
+  const uint32_t magic = in_vgpr(kMagicPair);
+  const uint32_t row_groups = uint32_t(groups);
+  const __amdgpu_buffer_rsrc_t sr0 = make_rsrc(scales, nrows * row_groups * 2);
+  const __amdgpu_buffer_rsrc_t br0 = make_rsrc(biases, nrows * row_groups * 2);
+
+  // first row units' codes, scales and biases in flight before the staging
+  RowData<CPL> buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    if (u_begin + d < u_end) {
+      bool valid;
+      const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
+      load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0);
+    }
+  }
+
+  // stage the activations: chunk c (32 of them, zeros past K) permuted, and its sum
+  {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, uint64_t(a.K) * 2);
+    for (int c = threadIdx.x; c < C; c += 64 * kWavesS1) {
+      uint32_t d[16];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(xr, uint32_t(c) * 64u + 16u * v, 0, 0);
+        d[4 * v + 0] = t[0];
+        d[4 * v + 1] = t[1];
+        d[4 * v + 2] = t[2];
+        d[4 * v + 3] = t[3];
+      }
+      uint32_t xp[16];
+      permute_chunk(d, xp);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(xl + c * kXStride);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v] = u32x4_t{xp[4 * v], xp[4 * v + 1], xp[4 * v + 2], xp[4 * v + 3]};
+      xsl[c] = chunk_xsum(xp);
+    }
+  }
+  __syncthreads();
+
+  uint32_t xp[CPL][16];
+  float xs[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = li + LPR * i;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xl + c * kXStride);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x4_t t = src[v];
+      xp[i][4 * v + 0] = t[0];
+      xp[i][4 * v + 1] = t[1];
+      xp[i][4 * v + 2] = t[2];
+      xp[i][4 * v + 3] = t[3];
+    }
+    xs[i] = xsl[c];
+  }
+
+  for (int64_t u0 = u_begin; u0 < u_end; u0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t u = u0 + d;
+      if (u < u_end) {
+        const float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        if (u + DEPTH < u_end) {
+          bool valid;
+          const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
+          load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0);
+        }
+        gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base);
+      }
+    }
+  }
+}
+
 // Routed-expert stage 2: y[r] = sum_k p_k * (D_{e_k} h_k)[r].  A block's kw waves split
 // the routed slots (wave w takes k = w, w+kw, ...) and walk the block's `upw` row units
 // for each; every wave adds its slots in increasing k into its own LDS slice, and the
@@ -340,15 +523,19 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 
 #define QMM_GEMV_CASE(L, C, K, EPI, MOE) \
   case (L * 10000 + C * 100 + K): gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a, units, upw); break;
+#define QMM_GEMV_S1_CASE(L, C, EPI, MOE)                                                            \
+  case (L * 10000 + C * 100 + 1):                                                                  \
+    gemv_u4_s1_kernel<L, C, EPI, MOE><<<grid, block, S1Layout<L, C>::lds_bytes(), s>>>(a, units, upw); \
+    break;
 
 #define QMM_GEMV_CASES(EPI, MOE)                                                  \
   switch (sh.lpr * 10000 + sh.cpl * 100 + sh.ksplit) {                            \
-    QMM_GEMV_CASE(16, 1, 1, EPI, MOE)                                             \
-    QMM_GEMV_CASE(32, 1, 1, EPI, MOE)                                             \
-    QMM_GEMV_CASE(32, 2, 1, EPI, MOE)                                             \
-    QMM_GEMV_CASE(32, 3, 1, EPI, MOE)                                             \
-    QMM_GEMV_CASE(32, 4, 1, EPI, MOE)                                             \
-    QMM_GEMV_CASE(32, 5, 1, EPI, MOE)                                             \
+    QMM_GEMV_S1_CASE(16, 1, EPI, MOE)                                             \
+    QMM_GEMV_S1_CASE(32, 1, EPI, MOE)                                             \
+    QMM_GEMV_S1_CASE(32, 2, EPI, MOE)                                             \
+    QMM_GEMV_S1_CASE(32, 3, EPI, MOE)                                             \
+    QMM_GEMV_S1_CASE(32, 4, EPI, MOE)                                             \
+    QMM_GEMV_S1_CASE(32, 5, EPI, MOE)                                             \
     QMM_GEMV_CASE(32, 1, 8, EPI, MOE)                                             \
     QMM_GEMV_CASE(32, 2, 8, EPI, MOE)                                             \
     QMM_GEMV_CASE(32, 3, 8, EPI, MOE)                                             \
@@ -362,15 +549,18 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 // Grid of the decode kernel: each wave (row group) takes `upw` consecutive units, sized
 // so that about kTargetWaves waves cover the call (a few per SIMD on 256 CUs).
 constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
+constexpr int64_t kTargetWavesS1 = 256 * QMM_S1_WAVES_PER_CU;
 
 static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units,
                           int* upw, int64_t* blocks, int* threads) {
   const int rpi = 64 / sh.lpr;
   *units = (epi == EPI_SWIGLU) ? (a.I + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
   const int G = sh.ksplit >= 4 ? 1 : 4 / sh.ksplit;  // groups_per_block<KS>()
-  const int64_t groups_wanted = (kTargetWaves / sh.ksplit + batch - 1) / batch;  // row groups per batch entry
+  const int64_t target = sh.ksplit == 1 ? kTargetWavesS1 : kTargetWaves / sh.ksplit;
+  const int64_t groups_wanted = (target + batch - 1) / batch;  // row groups per batch entry
   int64_t u = (*units + groups_wanted - 1) / groups_wanted;
   if (u < 1) u = 1;
+
   *upw = int(u);
   *threads = 64 * sh.ksplit * G;
   *blocks = (*units + int64_t(G) * u - 1) / (int64_t(G) * u);
