@@ -317,7 +317,8 @@ template <int LPR, int CPL, int EPI, bool MOE, int DEPTH = QMM_S1_DEPTH>
 #ifndef QMM_S1_MINW
 #define QMM_S1_MINW 1
 #endif
-__global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(GemvArgs a, int64_t units, int upw) {
+__global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(GemvArgs a, int64_t per_wave,
+                                                                              int64_t extra) {
   using Lay = S1Layout<LPR, CPL>;
   constexpr int RPI = Lay::RPI;
   constexpr int P = RPI / 2;
@@ -327,13 +328,16 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   float* xsl = reinterpret_cast<float*>(s1_lds + C * kXStride);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane / LPR;
   const int li = lane % LPR;
   const int64_t words = a.K >> 3;
   const int64_t groups = a.K >> 6;
-  const int64_t u_begin = (int64_t(blockIdx.x) * kWavesS1 + wave) * upw;
-  const int64_t u_end = u_begin + upw < units ? u_begin + upw : units;
+  // the units are spread evenly over the waves: every wave takes `per_wave` consecutive
+  // units and the first `extra` waves one more
+  const int64_t gw = int64_t(blockIdx.x) * kWavesS1 + wave;
+  const int64_t u_begin = gw * per_wave + (gw < extra ? gw : extra);
+  const int64_t u_end = u_begin + per_wave + (gw < extra ? 1 : 0);
 
   const uint32_t* codes = a.codes;
   const uint16_t* scales = a.scales;
@@ -525,7 +529,7 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
   case (L * 10000 + C * 100 + K): gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a, units, upw); break;
 #define QMM_GEMV_S1_CASE(L, C, EPI, MOE)                                                            \
   case (L * 10000 + C * 100 + 1):                                                                  \
-    gemv_u4_s1_kernel<L, C, EPI, MOE><<<grid, block, S1Layout<L, C>::lds_bytes(), s>>>(a, units, upw); \
+    gemv_u4_s1_kernel<L, C, EPI, MOE><<<grid, block, S1Layout<L, C>::lds_bytes(), s>>>(a, units / upw, units % upw); \
     break;
 
 #define QMM_GEMV_CASES(EPI, MOE)                                                  \
@@ -551,6 +555,7 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
 constexpr int64_t kTargetWavesS1 = 256 * QMM_S1_WAVES_PER_CU;
 
+
 static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units,
                           int* upw, int64_t* blocks, int* threads) {
   const int rpi = 64 / sh.lpr;
@@ -564,6 +569,14 @@ static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64
   *upw = int(u);
   *threads = 64 * sh.ksplit * G;
   *blocks = (*units + int64_t(G) * u - 1) / (int64_t(G) * u);
+  if (sh.ksplit == 1) {
+    // single-slice kernel: `upw` carries the number of waves, over which the units are
+    // spread evenly (every wave slot gets work, the counts differ by at most one)
+    int64_t w = groups_wanted < *units ? groups_wanted : *units;
+    w = (w + G - 1) / G * G;
+    *upw = int(w);
+    *blocks = w / G;
+  }
 }
 
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
