@@ -32,7 +32,6 @@
 
 namespace qmm {
 
-constexpr int kMaxWavesPerBlock = 16;
 
 // Activations of this lane's chunks, in registers for the whole kernel, read through a
 // buffer descriptor bounded by K: a chunk past the end of the K slice (ragged K) reads
@@ -114,14 +113,43 @@ __device__ __forceinline__ int64_t unit_row(int64_t unit, int slot, const GemvAr
   }
 }
 
-// Waves per block: KS waves share each row group; G row groups per block.
-template <int KS>
-__host__ __device__ constexpr int groups_per_block() { return KS >= 4 ? 1 : 4 / KS; }
-template <int KS>
-__host__ __device__ constexpr int threads_per_block() { return 64 * KS * groups_per_block<KS>(); }
+// Store of one row unit's result (slot totals after slot_reduce).
+template <int LPR, int EPI>
+__device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u, int slot, int lane,
+                                           int64_t out_base) {
+  constexpr int RPI = 64 / LPR;
+  constexpr int P = RPI / 2;
+  bool valid;
+  const int64_t r = unit_row<LPR, EPI>(u, slot, a, &valid);
+  if constexpr (EPI == EPI_SWIGLU) {
+    const float up = __shfl_xor(v, 32);
+    if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
+      store_out(a.out0, out_base + u * P + slot, silu_times(v, up), a.f32_out);
+  } else {
+    if (valid && lane == slot_result_lane<LPR>(slot)) {
+      if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
+      if constexpr (EPI == EPI_QKV) {
+        if (r < a.q_out) {
+          store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
+        } else if (r < a.q_out + a.kv_out) {
+          store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
+        } else {
+          store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
+        }
+      } else {
+        store_out(a.out0, out_base + r, v, a.f32_out);
+      }
+    }
+  }
+}
 
-// One wave (one row group) walks `upw` consecutive row units with DEPTH - 1 units of
-// code loads in flight ahead of the one being computed.
+// ---- K-split decode kernel (ksplit 8 or 16: 5120 < K <= 65536) -------------------------
+// A block is one row group of KS waves; wave ks owns the K slice [ks*LPR*CPL*32, ...) of
+// every row the group handles.  After each row unit the KS partial sums meet in LDS and
+// wave 0 adds them in wave order and stores; the barrier this takes also keeps the waves
+// on the same rows at the same time (each unit's rows are then read as one contiguous
+// stretch per row), which measured faster than reducing once at the end.  The units are
+// spread evenly over the row groups.
 #ifndef QMM_GEMV_DEPTH
 #define QMM_GEMV_DEPTH 1
 #endif
@@ -129,23 +157,22 @@ __host__ __device__ constexpr int threads_per_block() { return 64 * KS * groups_
 #define QMM_GEMV_WAVES_PER_CU 8
 #endif
 
-template <int LPR, int CPL, int KS, int EPI, bool MOE, int DEPTH = (KS >= 16 ? 1 : QMM_GEMV_DEPTH)>
-__global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvArgs a, int64_t units, int upw) {
+template <int LPR, int CPL, int KS, int EPI, bool MOE, int DEPTH = QMM_GEMV_DEPTH>
+__global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t per_group, int64_t extra) {
   constexpr int RPI = 64 / LPR;
   constexpr int P = RPI / 2;
-  constexpr int G = groups_per_block<KS>();
-  __shared__ float red[2][kMaxWavesPerBlock * RPI];
+  static_assert(KS > 1, "the single-slice kernel handles ksplit 1");
+  __shared__ float red[2][KS][RPI];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int ks = wave % KS;
-  const int g = wave / KS;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane / LPR;
   const int li = lane % LPR;
   const int64_t words = a.K >> 3;
   const int64_t groups = a.K >> 6;
-  const int64_t u_begin = (int64_t(blockIdx.x) * G + g) * upw;
-  const int64_t u_end = u_begin + upw < units ? u_begin + upw : units;
+  const int64_t gi = blockIdx.x;
+  const int64_t u_begin = gi * per_group + (gi < extra ? gi : extra);
+  const int64_t u_end = u_begin + per_group + (gi < extra ? 1 : 0);
 
   const uint32_t* codes = a.codes;
   const uint16_t* scales = a.scales;
@@ -192,8 +219,7 @@ __global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvAr
   const uint32_t magic = in_vgpr(kMagicPair);
 
   // Ring of DEPTH row buffers: unit u is computed from buf[(u - u_begin) % DEPTH], and
-  // the buffer is refilled with unit u + DEPTH right after, so DEPTH - 1 units of codes
-  // stay in flight while one is being computed.
+  // the buffer is refilled with unit u + DEPTH right after.
   RowData<CPL> buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
@@ -210,49 +236,22 @@ __global__ void __launch_bounds__(threads_per_block<KS>()) gemv_u4_kernel(GemvAr
     for (int d = 0; d < DEPTH; ++d) {
       const int64_t u = u0 + d;
       if (u < u_end) {
-        float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        const float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
         if (u + DEPTH < u_end) {
           bool valid;
           const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
           load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
         }
-        bool cur_valid;
-        const int64_t cur_row = unit_row<LPR, EPI>(u, slot, a, &cur_valid);
-        bool store = true;
-        if constexpr (KS > 1) {
-          float* rb = red[u & 1];
-          if (lane == slot_result_lane<LPR>(slot)) rb[wave * RPI + slot] = v;
-          __syncthreads();
-          if (ks == 0) {
-            float t = 0.f;
-            for (int j = 0; j < KS; ++j) t += rb[(g * KS + j) * RPI + slot];
-            v = t;
-          } else {
-            store = false;
-          }
-        }
-        if (store) {
-          if constexpr (EPI == EPI_SWIGLU) {
-            const float up = __shfl_xor(v, 32);
-            if (cur_valid && slot < P && lane == slot_result_lane<LPR>(slot))
-              store_out(a.out0, out_base + u * P + slot, silu_times(v, up), a.f32_out);
-          } else {
-            if (cur_valid && lane == slot_result_lane<LPR>(slot)) {
-              const int64_t r = cur_row;
-              if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
-              if constexpr (EPI == EPI_QKV) {
-                if (r < a.q_out) {
-                  store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
-                } else if (r < a.q_out + a.kv_out) {
-                  store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
-                } else {
-                  store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
-                }
-              } else {
-                store_out(a.out0, out_base + r, v, a.f32_out);
-              }
-            }
-          }
+        // double-buffered by unit parity: the next write to this buffer comes after the
+        // next unit's barrier, which wave 0 reaches only after reading this one
+        float (*rb)[RPI] = red[u & 1];
+        if (lane == slot_result_lane<LPR>(slot)) rb[ks][slot] = v;
+        __syncthreads();
+        if (ks == 0) {
+          float t = 0.f;
+#pragma unroll
+          for (int j = 0; j < KS; ++j) t += rb[j][slot];
+          gemv_store<LPR, EPI>(a, t, u, slot, lane, out_base);
         }
       }
     }
@@ -277,35 +276,6 @@ struct S1Layout {
   static constexpr size_t lds_bytes() { return size_t(x_words) * 4; }
 };
 
-// Store of one row unit's result (slot totals after slot_reduce).
-template <int LPR, int EPI>
-__device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u, int slot, int lane,
-                                           int64_t out_base) {
-  constexpr int RPI = 64 / LPR;
-  constexpr int P = RPI / 2;
-  bool valid;
-  const int64_t r = unit_row<LPR, EPI>(u, slot, a, &valid);
-  if constexpr (EPI == EPI_SWIGLU) {
-    const float up = __shfl_xor(v, 32);
-    if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
-      store_out(a.out0, out_base + u * P + slot, silu_times(v, up), a.f32_out);
-  } else {
-    if (valid && lane == slot_result_lane<LPR>(slot)) {
-      if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
-      if constexpr (EPI == EPI_QKV) {
-        if (r < a.q_out) {
-          store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
-        } else if (r < a.q_out + a.kv_out) {
-          store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
-        } else {
-          store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
-        }
-      } else {
-        store_out(a.out0, out_base + r, v, a.f32_out);
-      }
-    }
-  }
-}
 
 #ifndef QMM_S1_DEPTH
 #define QMM_S1_DEPTH 1
@@ -525,8 +495,10 @@ bool gemv_shape_for_k(int64_t K, GemvShape* o) {
 
 static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 
-#define QMM_GEMV_CASE(L, C, K, EPI, MOE) \
-  case (L * 10000 + C * 100 + K): gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a, units, upw); break;
+#define QMM_GEMV_CASE(L, C, K, EPI, MOE)                                                                 \
+  case (L * 10000 + C * 100 + K):                                                                        \
+    gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a, units / upw, units % upw);               \
+    break;
 #define QMM_GEMV_S1_CASE(L, C, EPI, MOE)                                                            \
   case (L * 10000 + C * 100 + 1):                                                                  \
     gemv_u4_s1_kernel<L, C, EPI, MOE><<<grid, block, S1Layout<L, C>::lds_bytes(), s>>>(a, units / upw, units % upw); \
@@ -550,32 +522,30 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
     default: return 2;                                                            \
   }
 
-// Grid of the decode kernel: each wave (row group) takes `upw` consecutive units, sized
-// so that about kTargetWaves waves cover the call (a few per SIMD on 256 CUs).
+// Grid of the decode kernels.  `n` is the number of waves (single-slice kernel) or row
+// groups (K-split kernel) over which the row units are spread evenly: about
+// kTargetWavesS1 (resp. kTargetWaves) waves per call on the 256 CUs and never more
+// waves (groups) than units.
 constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
 constexpr int64_t kTargetWavesS1 = 256 * QMM_S1_WAVES_PER_CU;
 
-
-static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units,
-                          int* upw, int64_t* blocks, int* threads) {
+static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units, int* n,
+                          int64_t* blocks, int* threads) {
   const int rpi = 64 / sh.lpr;
   *units = (epi == EPI_SWIGLU) ? (a.I + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
-  const int G = sh.ksplit >= 4 ? 1 : 4 / sh.ksplit;  // groups_per_block<KS>()
-  const int64_t target = sh.ksplit == 1 ? kTargetWavesS1 : kTargetWaves / sh.ksplit;
-  const int64_t groups_wanted = (target + batch - 1) / batch;  // row groups per batch entry
-  int64_t u = (*units + groups_wanted - 1) / groups_wanted;
-  if (u < 1) u = 1;
-
-  *upw = int(u);
-  *threads = 64 * sh.ksplit * G;
-  *blocks = (*units + int64_t(G) * u - 1) / (int64_t(G) * u);
   if (sh.ksplit == 1) {
-    // single-slice kernel: `upw` carries the number of waves, over which the units are
-    // spread evenly (every wave slot gets work, the counts differ by at most one)
-    int64_t w = groups_wanted < *units ? groups_wanted : *units;
-    w = (w + G - 1) / G * G;
-    *upw = int(w);
-    *blocks = w / G;
+    const int64_t want = (kTargetWavesS1 + batch - 1) / batch;
+    int64_t w = want < *units ? want : *units;
+    w = (w + kWavesS1 - 1) / kWavesS1 * kWavesS1;
+    *n = int(w);
+    *blocks = w / kWavesS1;
+    *threads = 64 * kWavesS1;
+  } else {
+    const int64_t want = (kTargetWaves / sh.ksplit + batch - 1) / batch;
+    const int64_t g = want < *units ? want : *units;
+    *n = int(g);
+    *blocks = g;
+    *threads = 64 * sh.ksplit;
   }
 }
 
