@@ -281,7 +281,7 @@ struct S1Layout {
 #define QMM_S1_DEPTH 1
 #endif
 #ifndef QMM_S1_WAVES_PER_CU
-#define QMM_S1_WAVES_PER_CU 12
+#define QMM_S1_WAVES_PER_CU 12  // fallback if the occupancy query fails
 #endif
 template <int LPR, int CPL, int EPI, bool MOE, int DEPTH = QMM_S1_DEPTH>
 #ifndef QMM_S1_MINW
@@ -421,6 +421,9 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
 // for each; every wave adds its slots in increasing k into its own LDS slice, and the
 // slices are then added in wave order.  No atomics, so the order is fixed.
 constexpr int kMaxUnitsPerCombineBlock = 16;
+#ifndef QMM_MOE_DOWN_BLOCKS
+#define QMM_MOE_DOWN_BLOCKS 256
+#endif
 
 template <int LPR, int CPL>
 __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units, int upw) {
@@ -499,10 +502,13 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
   case (L * 10000 + C * 100 + K):                                                                        \
     gemv_u4_kernel<L, C, K, EPI, MOE><<<grid, block, 0, s>>>(a, units / upw, units % upw);               \
     break;
-#define QMM_GEMV_S1_CASE(L, C, EPI, MOE)                                                            \
-  case (L * 10000 + C * 100 + 1):                                                                  \
-    gemv_u4_s1_kernel<L, C, EPI, MOE><<<grid, block, S1Layout<L, C>::lds_bytes(), s>>>(a, units / upw, units % upw); \
-    break;
+#define QMM_GEMV_S1_CASE(L, C, EPI, MOE)                                                              \
+  case (L * 10000 + C * 100 + 1): {                                                                  \
+    const int64_t w = s1_waves(units, batch, s1_resident_waves<L, C, EPI, MOE>());                  \
+    const dim3 g1{unsigned(w / kWavesS1), unsigned(batch), 1u};                                       \
+    gemv_u4_s1_kernel<L, C, EPI, MOE>                                                                \
+        <<<g1, dim3{64u * kWavesS1, 1u, 1u}, S1Layout<L, C>::lds_bytes(), s>>>(a, units / w, units % w); \
+  } break;
 
 #define QMM_GEMV_CASES(EPI, MOE)                                                  \
   switch (sh.lpr * 10000 + sh.cpl * 100 + sh.ksplit) {                            \
@@ -522,39 +528,53 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
     default: return 2;                                                            \
   }
 
-// Grid of the decode kernels.  `n` is the number of waves (single-slice kernel) or row
-// groups (K-split kernel) over which the row units are spread evenly: about
-// kTargetWavesS1 (resp. kTargetWaves) waves per call on the 256 CUs and never more
-// waves (groups) than units.
+// Grid of the decode kernels.  The row units are spread evenly over the waves of the
+// single-slice kernel and over the row groups of the K-split kernel.  The single-slice
+// kernel gets as many waves as the GPU holds at once for that instance (its register use
+// sets the occupancy; queried once per instance) but never more waves than units; the
+// K-split kernel about kTargetWaves waves.
 constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
-constexpr int64_t kTargetWavesS1 = 256 * QMM_S1_WAVES_PER_CU;
+constexpr int64_t kCUs = 256;
+
+template <int L, int C, int EPI, bool MOE>
+static int64_t s1_resident_waves() {
+  static const int64_t waves = [] {
+    int blocks_per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, gemv_u4_s1_kernel<L, C, EPI, MOE>,
+                                                     64 * kWavesS1, S1Layout<L, C>::lds_bytes()) != hipSuccess ||
+        blocks_per_cu < 1)
+      blocks_per_cu = QMM_S1_WAVES_PER_CU / kWavesS1;
+    return kCUs * kWavesS1 * int64_t(blocks_per_cu);
+  }();
+  return waves;
+}
+
+// waves of a single-slice launch per batch entry (a multiple of the block's waves)
+static int64_t s1_waves(int64_t units, int64_t batch, int64_t resident) {
+  const int64_t want = (resident + batch - 1) / batch;
+  int64_t w = want < units ? want : units;
+  return (w + kWavesS1 - 1) / kWavesS1 * kWavesS1;
+}
 
 static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units, int* n,
                           int64_t* blocks, int* threads) {
   const int rpi = 64 / sh.lpr;
   *units = (epi == EPI_SWIGLU) ? (a.I + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
-  if (sh.ksplit == 1) {
-    const int64_t want = (kTargetWavesS1 + batch - 1) / batch;
-    int64_t w = want < *units ? want : *units;
-    w = (w + kWavesS1 - 1) / kWavesS1 * kWavesS1;
-    *n = int(w);
-    *blocks = w / kWavesS1;
-    *threads = 64 * kWavesS1;
-  } else {
-    const int64_t want = (kTargetWaves / sh.ksplit + batch - 1) / batch;
-    const int64_t g = want < *units ? want : *units;
-    *n = int(g);
-    *blocks = g;
-    *threads = 64 * sh.ksplit;
-  }
+  // K-split kernel (the single-slice cases compute their own grid)
+  const int64_t want = (kTargetWaves / sh.ksplit + batch - 1) / batch;
+  const int64_t g = want < *units ? want : *units;
+  *n = int(g);
+  *blocks = g;
+  *threads = 64 * sh.ksplit;
 }
 
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
   GemvShape sh;
   if (!gemv_shape_for_k(a.K, &sh)) return 2;
+  const int64_t batch = M;
   int64_t blocks, units;
   int threads, upw;
-  gemv_geometry(sh, epi, a, M, &units, &upw, &blocks, &threads);
+  gemv_geometry(sh, epi, a, batch, &units, &upw, &blocks, &threads);
   const dim3 grid{unsigned(blocks), unsigned(M), 1u};
   const dim3 block{unsigned(threads), 1u, 1u};
   if (epi == EPI_LINEAR) {
@@ -570,9 +590,10 @@ int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
 int launch_moe_gate_up(const GemvArgs& a, hipStream_t s) {
   GemvShape sh;
   if (!gemv_shape_for_k(a.K, &sh)) return 2;
+  const int64_t batch = a.topk;
   int64_t blocks, units;
   int threads, upw;
-  gemv_geometry(sh, EPI_SWIGLU, a, a.topk, &units, &upw, &blocks, &threads);
+  gemv_geometry(sh, EPI_SWIGLU, a, batch, &units, &upw, &blocks, &threads);
   const dim3 grid{unsigned(blocks), unsigned(a.topk), 1u};
   const dim3 block{unsigned(threads), 1u, 1u};
   QMM_GEMV_CASES(EPI_SWIGLU, true)
@@ -585,8 +606,8 @@ int launch_moe_down(const GemvArgs& a, hipStream_t s) {
   const int rpi = 64 / sh.lpr;
   const int64_t units = (a.rows + rpi - 1) / rpi;
   const int kw = a.topk < 8 ? a.topk : 8;
-  // about 256 blocks, at most kMaxUnitsPerCombineBlock units each
-  int64_t upw = (units + 255) / 256;
+  // about QMM_MOE_DOWN_BLOCKS blocks, at most kMaxUnitsPerCombineBlock units each
+  int64_t upw = (units + QMM_MOE_DOWN_BLOCKS - 1) / QMM_MOE_DOWN_BLOCKS;
   if (upw > kMaxUnitsPerCombineBlock) upw = kMaxUnitsPerCombineBlock;
   if (upw < 1) upw = 1;
   const dim3 grid{unsigned((units + upw - 1) / upw), 1u, 1u};
