@@ -217,7 +217,7 @@ def main():
                    "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
                    "bytes_per_step": bytes_step, "pool_layers": P},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "gemv_u4_kernel (fused gate+up+SwiGLU, K=5120)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_u4_s1_kernel (fused gate+up+SwiGLU, K=5120)",
                      "achieved": round(ach_gu, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach_gu / HBM_PEAK_GBS, 4), "traffic": counted_traffic("gate_up"),
                      "bytes_per_launch": bytes_gu, "avg_launch_us": ms_gu * 1e3},
