@@ -4,21 +4,22 @@
 // path feeds the matrix cores; the fused QKV split and the SwiGLU epilogue follow
 // "The Cathedral Doubled Itself" (the two fusions).
 //
-// Tile: 256 (rows of x) x 256 (rows of the weight) per block of 4 waves, one K step
-// = one 64-wide group.  Per step:
+// Tile: 256 (rows of x) x 256 (rows of the weight) per block of 8 waves (two per SIMD), one
+// K step = one 64-wide group.  Per step:
 //   * x tile (256 rows x 128 B) goes global -> LDS directly (buffer_load ... lds), two
 //     steps ahead, into a ring of three LDS stages;
-//   * weight tile: thread t owns weight row t (8 code words + the group's scale and
-//     bias, in registers, requested three steps ahead); each code becomes w = s*q + b in
-//     fp32 (one FMA, exact product), rounded to bf16 (RNE) into one of two LDS stages,
+//   * weight tile: each lane owns half of one weight row (4 code words + the group's scale
+//     and bias, in registers, requested three steps ahead); each code becomes w = s*q + b
+//     in fp32 (one FMA, exact product), rounded to bf16 (RNE) into one of two LDS stages,
 //     one step ahead, between the multiplies of the current step.
-// Each wave computes a 128 x 128 sub-tile with v_mfma_f32_32x32x16_bf16 (4 x 4 tiles of
-// 32 x 32, fp32 accumulators).  LDS rows are 128 B, unpadded; slot c' (16 B) of row r
-// holds the row's chunk c' ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the rows an
+// Each wave computes a 128 x 64 sub-tile with v_mfma_f32_32x32x16_bf16 (4 x 2 tiles of
+// 32 x 32, fp32 accumulators); with two waves per SIMD one wave's MFMAs run while the
+// other dequantizes, loads or waits.  LDS rows are 128 B, unpadded; slot c' (16 B) of row
+// r holds the row's chunk c' ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the rows an
 // MFMA operand read spans (16 consecutive rows at one chunk) hit distinct bank groups.
 // Five 32 KB stages fill the 160 KB of LDS.
 // For SwiGLU a block's 256 weight rows are 128 gate rows and the 128 matching up rows,
-// and each wave's columns are 64 gate + the same 64 up columns, so silu(g)*u is formed
+// and each wave's columns are 32 gate + the same 32 up columns, so silu(g)*u is formed
 // in registers.  Blocks are ordered so the tiles on one XCD (blocks are dealt to the 8
 // XCDs round-robin) walk all row tiles of a few weight tiles: the weight tile stays in
 // that XCD's L2 while the activation tiles stream.
@@ -83,7 +84,7 @@ __device__ __forceinline__ int64_t gemm_weight_row(const GemmArgs& a, int64_t nt
 }
 
 template <int EPI>
-__global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t n_tiles,
+__global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t n_tiles,
                                                         int64_t tiles_per_xcd) {
   // One variable per x stage, and the two weight stages in a variable of their own: the
   // compiler then knows that the x stage being filled by a direct-to-LDS load aliases
@@ -102,7 +103,7 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const uint32_t K = uint32_t(a.K);
   const uint32_t groups = K >> 6;
   const int ksteps = int(groups);
@@ -112,10 +113,10 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   // lands at byte 16 L); that slot holds chunk (L % 8) ^ swz(row) = (L % 8) ^ (L / 8) ^ (j & 1).
   // A row past M reads row M - 1 (never stored).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint64_t(a.M) * K * 2);
-  uint32_t xoff[8];
+  uint32_t xoff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int64_t r = mt * kBM + 64 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {
+    int64_t r = mt * kBM + 32 * wave + 8 * j + (lane >> 3);
     if (r >= a.M) r = a.M - 1;
     const uint32_t chunk = uint32_t((lane & 7) ^ (lane >> 3) ^ (j & 1));
     xoff[j] = uint32_t(r) * K * 2 + chunk * 16u;
@@ -126,9 +127,9 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   };
   auto load_x = [&](uint16_t* dst, int ks) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(dst + (64 * wave + 8 * j) * kRow), 16, xoff[j],
+          xr, (__attribute__((address_space(3))) void*)(dst + (32 * wave + 8 * j) * kRow), 16, xoff[j],
           uint32_t(ks) * 128u, 0, 0);
   };
 
@@ -141,65 +142,53 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes, nrows * (K >> 1));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, nrows * groups * 2);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases, nrows * groups * 2);
-  uint32_t coff[2], goff[2], wdst[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t = 64 * wave + 32 * i + (lane & 31);
-    const int64_t wrow = gemm_weight_row<EPI>(a, nt, t);
-    coff[i] = uint32_t(wrow) * (K >> 1) + 16u * uint32_t(wh);
-    goff[i] = uint32_t(wrow) * groups * 2;
-    wdst[i] = uint32_t(t) * kRow;
-  }
-  // one step of this lane's two half rows in flight: 2 x 4 code words, scales, biases;
-  // step j lives in set j % 3
+  const int wt = 32 * wave + (lane & 31);  // tile row whose half `wh` this lane owns
+  const int64_t wrow = gemm_weight_row<EPI>(a, nt, wt);
+  const uint32_t coff = uint32_t(wrow) * (K >> 1) + 16u * uint32_t(wh);
+  const uint32_t goff = uint32_t(wrow) * groups * 2;
+  const uint32_t wdst = uint32_t(wt) * kRow;
+  const uint32_t wsw = swz(uint32_t(wt));
+  // one step of this lane's half row in flight: 4 code words, scale, bias; step j lives in
+  // set j % 3
   struct StepRegs {
-    u32x4_t cv[2];
-    uint16_t sv[2], bv[2];
+    u32x4_t cv;
+    uint16_t sv, bv;
   };
   StepRegs R[3];
   auto load_w = [&](StepRegs& r, int ks) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) r.cv[i] = __builtin_amdgcn_raw_buffer_load_b128(cr, coff[i] + uint32_t(ks) * 32u, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      r.sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, goff[i] + uint32_t(ks) * 2u, 0, 0);
-      r.bv[i] = __builtin_amdgcn_raw_buffer_load_b16(br, goff[i] + uint32_t(ks) * 2u, 0, 0);
-    }
+    r.cv = __builtin_amdgcn_raw_buffer_load_b128(cr, coff + uint32_t(ks) * 32u, 0, 0);
+    r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, goff + uint32_t(ks) * 2u, 0, 0);
+    r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, goff + uint32_t(ks) * 2u, 0, 0);
   };
-  constexpr int kStepLoads = 8 + 2 + 4;  // vector-memory loads one step requests per lane
-  // Piece p (0..3): code words 2 (p & 1), +1 of half row p / 2 (16 codes -> w = s*q + b in
-  // fp32 -> bf16, 32 bytes) into stage `dst`.
+  constexpr int kStepLoads = 4 + 1 + 2;  // vector-memory loads one step requests per lane
+  // Piece p (0..3): code word p of the half row (8 codes -> w = s*q + b in fp32 -> bf16,
+  // 16 bytes) into chunk 4 wh + p of the row in stage `dst`.
   auto store_piece = [&](const StepRegs& r, uint16_t* dst, int p) {
-    const int i = p >> 1;
-    const float s = bf16_bits_to_f32(r.sv[i]);
-    const float b = bf16_bits_to_f32(r.bv[i]);
-    const uint32_t rsw = swz(wdst[i] / kRow);
-#pragma unroll
-    for (int ww = 0; ww < 2; ++ww) {
-      const uint32_t w = r.cv[i][2 * (p & 1) + ww];
-      // low and high nibbles of the four bytes, then one v_cvt_f32_ubyte{0..3} per code
-      const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
-      const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
-      const u32x4_t v = {pack_bf16x2(fmaf(s, ubyte_f32<0>(lo), b), fmaf(s, ubyte_f32<0>(hi), b)),
-                         pack_bf16x2(fmaf(s, ubyte_f32<1>(lo), b), fmaf(s, ubyte_f32<1>(hi), b)),
-                         pack_bf16x2(fmaf(s, ubyte_f32<2>(lo), b), fmaf(s, ubyte_f32<2>(hi), b)),
-                         pack_bf16x2(fmaf(s, ubyte_f32<3>(lo), b), fmaf(s, ubyte_f32<3>(hi), b))};
-      const uint32_t chunk = uint32_t(4 * wh + 2 * (p & 1) + ww);
-      *reinterpret_cast<u32x4_t*>(dst + wdst[i] + (chunk ^ rsw) * 8) = v;
-    }
+    const float s = bf16_bits_to_f32(r.sv);
+    const float b = bf16_bits_to_f32(r.bv);
+    const uint32_t w = r.cv[p];
+    // low and high nibbles of the four bytes, then one v_cvt_f32_ubyte{0..3} per code
+    const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
+    const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
+    const u32x4_t v = {pack_bf16x2(fmaf(s, ubyte_f32<0>(lo), b), fmaf(s, ubyte_f32<0>(hi), b)),
+                       pack_bf16x2(fmaf(s, ubyte_f32<1>(lo), b), fmaf(s, ubyte_f32<1>(hi), b)),
+                       pack_bf16x2(fmaf(s, ubyte_f32<2>(lo), b), fmaf(s, ubyte_f32<2>(hi), b)),
+                       pack_bf16x2(fmaf(s, ubyte_f32<3>(lo), b), fmaf(s, ubyte_f32<3>(hi), b))};
+    const uint32_t chunk = uint32_t(4 * wh + p);
+    *reinterpret_cast<u32x4_t*>(dst + wdst + (chunk ^ wsw) * 8) = v;
   };
 
   // ---- MFMA operands from LDS ---------------------------------------------------------
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
   // LDS row of the B operand for column tile j of this wave
   auto btile_row = [&](int j) -> int {
-    if constexpr (EPI == EPI_SWIGLU) return (j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1);
-    else return 128 * wn + 32 * j;
+    if constexpr (EPI == EPI_SWIGLU) return (j == 0 ? 0 : 128) + 32 * wn;
+    else return 64 * wn + 32 * j;
   };
   // Operand lane l holds row l % 32 of a 32-row tile and k 8 (l / 32) .. +7 of a 16-wide
   // sub-step q, i.e. chunk 2q + l / 32 of the row; tiles start at multiples of 32 rows,
@@ -209,41 +198,41 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 #pragma unroll
   for (int q = 0; q < 4; ++q) opoff[q] = lr * kRow + (uint32_t(2 * q + (lane >> 5)) ^ swz(lr)) * 8u;
   struct Frags {
-    bf16x8_t a[4], b[4];
+    bf16x8_t a[4], b[2];
   };
   auto load_frags = [&](Frags& f, const uint16_t* as, const uint16_t* bs, int q) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(bs + btile_row(j) * kRow + opoff[q]);
+    for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(bs + btile_row(j) * kRow + opoff[q]);
   };
   auto mfma16 = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
 
   // Instruction order inside a slot: the wave issues in order and an MFMA waits for the
-  // matrix pipe, so the dequantization's ~48 VALU ops are spread 3 per MFMA (they then
-  // run while the MFMA executes) and its two LDS stores go late in the slot.
+  // matrix pipe, so the dequantization's ~24 VALU ops are spread 3 per MFMA (they then
+  // run while the MFMA executes) and its LDS store goes late in the slot.
   auto interleave_slot = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
-      if (i == 13) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // 2 LDS stores
+      if (i == 6) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // the LDS store
     }
   };
 
   // K loop.  Step j's x tile lives in x stage j % 3, its dequantized weights in weight
-  // stage j & 1, its raw weights in register set j % 3.  Each step is four slots of 16
+  // stage j & 1, its raw weights in register set j % 3.  Each step is four slots of 8
   // MFMAs (one 16-wide sub-step each); in every slot the operand fragments of the next
   // sub-step are read from LDS and a quarter of the next step's weights is dequantized.
   // The one barrier of a step, X, sits before its last slot, when every fragment of the
   // step has been read into registers: after X the step's x and weight stages are free,
-  // and the first fragments of the next step are read while the last 16 MFMAs run.
+  // and the first fragments of the next step are read while the last 8 MFMAs run.
   // Before X a wave waits for its x of the next step and the raw weights of the one after,
   // requested after the barrier two steps back: only the loads requested after the
   // previous barrier (kStepLoads) may still be in flight.  Requested steps are clamped to
@@ -333,10 +322,10 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     }
   };
   if constexpr (EPI == EPI_SWIGLU) {
-    static_for<8>([&](auto jg) {
-      constexpr int j = decltype(jg)::value / 4, g = decltype(jg)::value % 4;
+    static_for<4>([&](auto gc) {
+      constexpr int j = 0, g = decltype(gc)::value;
       {
-        const int64_t p0 = nt * (kBN / 2) + 64 * wn + 32 * j + 8 * g + csub;
+        const int64_t p0 = nt * (kBN / 2) + 32 * wn + 8 * g + csub;
         if (p0 >= a.I) return;
         const int nvalid = int(min<int64_t>(4, a.I - p0));
 #pragma unroll
@@ -345,7 +334,7 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
           if (m >= a.M) continue;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[i][j][4 * g + e], acc[i][j + 2][4 * g + e]);
+          for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[i][j][4 * g + e], acc[i][j + 1][4 * g + e]);
           put(a.out0, a.I, p0, m, v, nvalid);
         }
       }
@@ -365,10 +354,10 @@ __global__ void __launch_bounds__(256, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
         dst = a.out0; ld = a.N; cn = n; end = a.N;
       }
     };
-    static_for<16>([&](auto jg) {
+    static_for<8>([&](auto jg) {
       constexpr int j = decltype(jg)::value / 4, g = decltype(jg)::value % 4;
       {
-        const int64_t n0 = nt * kBN + 128 * wn + 32 * j + 8 * g + csub;
+        const int64_t n0 = nt * kBN + 64 * wn + 32 * j + 8 * g + csub;
         if (n0 >= a.N) return;
         float lb[4];
 #pragma unroll
@@ -409,7 +398,7 @@ int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = m_tiles * n_tiles;
   const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
   const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
-  const dim3 block{256u, 1u, 1u};
+  const dim3 block{512u, 1u, 1u};
   if (epi == EPI_LINEAR) {
     gemm_u4_kernel<EPI_LINEAR><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else if (epi == EPI_QKV) {
