@@ -345,15 +345,27 @@ def bench_step_24b(torch, qmm, synth, T, dev, n_steps):
     T.replay_ms(g)
     ms = T.replay_ms(g) / n_steps
     del g
-    b_layer = (weight_bytes(sh.qkv_rows, K) + K * 2 + sh.qkv_rows * 2
-               + weight_bytes(2 * I, K) + K * 2 + I * 2
-               + weight_bytes(K, I) + I * 2 + K * 2)
-    b_step = L * b_layer
+    b_qkv = weight_bytes(sh.qkv_rows, K) + K * 2 + sh.qkv_rows * 2
+    b_gu = weight_bytes(2 * I, K) + K * 2 + I * 2
+    b_dn = weight_bytes(K, I) + I * 2 + K * 2
+    b_step = L * (b_qkv + b_gu + b_dn)
     gbs = b_step / (ms * 1e-3) / 1e9
+    # each projection on its own (a graph of one kind of call over the 40 layers): the
+    # whole-step graph is compared with the sum of these
+    x0 = xs[0]
+    ms_q = T.per_call_ms(lambda i: qmm.qmm_fused_qkv(x0, pq[0][i % L], pq[1][i % L], pq[2][i % L], q, k, v,
+                                                     stream=st), 4 * L)
+    ms_g = T.per_call_ms(lambda i: qmm.qmm_fused_gate_up_swiglu(x0, pg[0][i % L], pg[1][i % L], pg[2][i % L], h,
+                                                                stream=st), 4 * L)
+    ms_d = T.per_call_ms(lambda i: qmm.qmm_linear(h, pd[0][i % L], pd[1][i % L], pd[2][i % L], y, stream=st), 4 * L)
+    kern = {name: {"avg_launch_us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1)}
+            for name, t, b in (("fused_qkv", ms_q, b_qkv), ("fused_gate_up", ms_g, b_gu), ("down", ms_d, b_dn))}
     return {"workload": f"24B-dense decode step M=1: {L} layers x (QKV [{sh.qkv_rows}x{K}] + gate+up "
                         f"[{2 * I}x{K}] + down [{K}x{I}]), fresh x per step, {n_steps} steps in one graph",
             "ms_per_step": round(ms, 4), "bytes_per_step": b_step, "GB/s": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_step": 3 * L}
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_step": 3 * L,
+            "kernels": kern,
+            "step_over_kernel_sum": round(ms / (L * (ms_q + ms_g + ms_d)), 4)}
 
 
 def bench_moe(torch, qmm, synth, T, dev, n_steps):

@@ -243,6 +243,59 @@ def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, e
     return y, t
 
 
+def moe_prefill_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: int,
+                        bf16_weights: bool = True):
+    """Stage 1 over a batch of tokens (prefill): for token m and slot k with expert
+    e = ids[m, k] in [0, E), h[m, k] = silu(G_e x_m) * (U_e x_m); other pairs get h = 0.
+    Computed expert by expert, as the pages' in-place expert grid is meant to be used:
+    the (token, slot) pairs routed to e are gathered and their tokens multiplied by the
+    gate+up rows of grid[e] in one product.  bf16_weights adds the exact effect of feeding
+    bf16-rounded weights (a kernel that multiplies on the matrix cores).
+    Returns (h [M, topk, rows/2], tol)."""
+    x = np.asarray(x_bits)
+    ids = np.asarray(expert_ids)
+    M, topk = ids.shape
+    E = grid_codes.shape[0]
+    I = rows // 2
+    h = np.zeros((M, topk, I))
+    t = np.zeros((M, topk, I))
+    for e in range(E):
+        m_idx, k_idx = np.nonzero(ids == e)
+        if len(m_idx) == 0:
+            continue
+        he, te = gate_up_swiglu(x[m_idx], grid_codes[e], grid_scales[e], grid_biases[e], I,
+                                bf16_weights=bf16_weights)
+        h[m_idx, k_idx] = he
+        t[m_idx, k_idx] = te
+    return h, t
+
+
+def moe_prefill_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, expert_w,
+                             bf16_weights: bool = True):
+    """Stage 2 over a batch of tokens: y[m] = sum_k p[m, k] * (D_e h[m, k]) with
+    e = ids[m, k]; pairs with no expert contribute nothing.  h_bits: bf16 bits
+    [M, topk, K] fed to both sides; p: the fp32 combine weights [M, topk].  Computed
+    expert by expert (gathered h rows times grid[e]), then added per token.  Returns
+    (y [M, rows], tol) with tol = sum_k |p| * tol(D_e h[m, k])."""
+    hb = np.asarray(h_bits)
+    ids = np.asarray(expert_ids)
+    M, topk = ids.shape
+    E, rows = grid_codes.shape[0], grid_codes.shape[1]
+    p = np.asarray(expert_w, dtype=np.float32).astype(np.float64)
+    y = np.zeros((M, rows))
+    t = np.zeros((M, rows))
+    for e in range(E):
+        m_idx, k_idx = np.nonzero(ids == e)
+        if len(m_idx) == 0:
+            continue
+        ye, te = linear(hb[m_idx, k_idx], grid_codes[e], grid_scales[e], grid_biases[e],
+                        bf16_weights=bf16_weights)
+        pe = p[m_idx, k_idx][:, None]
+        np.add.at(y, m_idx, pe * ye)
+        np.add.at(t, m_idx, np.abs(pe) * te)
+    return y, t
+
+
 def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None, row_block: int = 1024):
     """A projection whose GPU input may differ from x_bits by at most x_err per element
     (an upstream GPU result): tolerance 1e-3*A + |W| . x_err."""

@@ -344,6 +344,52 @@ def test_moe_out_of_range_id_contributes_nothing():
     assert np.array_equal(y, y_only)
 
 
+def _prefill_routing(M, E, topk, seed, invalid=True):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+    if invalid:
+        ids[1, 0] = -1          # no expert
+        ids[M - 1, topk - 1] = E  # no expert (past the grid)
+    p = rng.dirichlet(np.ones(topk), size=M).astype(np.float32)
+    return ids, p
+
+
+def test_moe_prefill_matches_per_token_decode():
+    """Prefill (grouped by expert over all tokens) == the decode gather run token by token:
+    the grouping and scatter back to (token, slot) are pinned by a different path."""
+    gu, d, egu, ed = _moe_fixture()
+    K, I, M, topk, E = 128, 64, 7, 3, 6
+    x = synth.gen_x(synth.CFG_TEST, 7, 0, M, K)
+    ids, p = _prefill_routing(M, E, topk, seed=8)
+    h, th = orc.moe_prefill_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * I, bf16_weights=False)
+    for m in range(M):
+        hd, td = orc.moe_gate_up(x[m], gu.codes, gu.scales, gu.biases, ids[m], 2 * I)
+        assert np.allclose(h[m], hd, rtol=1e-13, atol=1e-13 * max(1.0, np.abs(hd).max()))
+        assert np.allclose(th[m], td, rtol=1e-12)
+    assert np.all(h[1, 0] == 0) and np.all(h[M - 1, topk - 1] == 0)
+    hb = synth.to_bf16_bits(h)
+    y, t = orc.moe_prefill_down_combine(hb, d.codes, d.scales, d.biases, ids, p, bf16_weights=False)
+    for m in range(M):
+        yd, td = orc.moe_down_combine(hb[m], d.codes, d.scales, d.biases, ids[m], p[m])
+        assert np.allclose(y[m], yd, rtol=1e-12, atol=1e-12 * np.abs(yd).max())
+        assert np.allclose(t[m], td, rtol=1e-12)
+
+
+def test_moe_prefill_bf16_weight_term():
+    """With bf16_weights the bound grows by exactly the weight-rounding term of each pair."""
+    gu, d, egu, ed = _moe_fixture()
+    K, I, M, topk, E = 128, 64, 5, 2, 6
+    x = synth.gen_x(synth.CFG_TEST, 9, 0, M, K)
+    ids, p = _prefill_routing(M, E, topk, seed=10, invalid=False)
+    h0, t0 = orc.moe_prefill_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * I, bf16_weights=False)
+    h1, t1 = orc.moe_prefill_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * I, bf16_weights=True)
+    assert np.array_equal(h0, h1) and np.all(t1 >= t0) and np.any(t1 > t0)
+    m, k = 2, 1
+    e = ids[m, k]
+    _, tg = orc.gate_up_swiglu(x[m], egu[e].codes, egu[e].scales, egu[e].biases, I, bf16_weights=True)
+    assert np.allclose(t1[m, k], tg, rtol=1e-12)
+
+
 # ---- arithmetic properties ---------------------------------------------------
 
 def test_linearity_and_zero_input():
