@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_gate_up_swiglu", "qmm_moe_gather",
-           "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
+           "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
            "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
@@ -33,6 +33,10 @@ _SIGNATURES = {
     "qmm_fused_qkv": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _INT, _P],
     "qmm_fused_gate_up_swiglu": [_P, _I64, _I64, _P, _P, _P, _I64, _P, _INT, _P],
     "qmm_moe_gather": [_INT, _P, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
+    "qmm_moe_prefill_workspace_bytes": [_I64, _I64, _I64, _I64],
+    "qmm_moe_route": [_P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
+    "qmm_moe_prefill": [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_size_t, _P,
+                        _INT, _P],
     "qmm_status_str": [_INT],
     "qmm_abi_version": [],
 }
@@ -54,7 +58,8 @@ def load_library():
         for name, args in _SIGNATURES.items():
             f = getattr(lib, name)
             f.argtypes = args
-            f.restype = ctypes.c_char_p if name == "qmm_status_str" else ctypes.c_int
+            f.restype = {"qmm_status_str": ctypes.c_char_p,
+                         "qmm_moe_prefill_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
         _LIB = lib
     return _LIB
 
@@ -192,3 +197,41 @@ def qmm_moe_gather(stage, inp, codes, scales, biases, expert_ids, out, expert_w=
                                          _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"),
                                          expert_ids.shape[0], _ptr(out, "out"), _out_dtype(out),
                                          _stream(stream)), "qmm_moe_gather")
+
+
+def qmm_moe_prefill_workspace_bytes(M: int, topk: int, E: int, out_rows: int = 0) -> int:
+    """Workspace bytes for M tokens x topk slots over E experts (0 = sizes out of range)."""
+    return int(load_library().qmm_moe_prefill_workspace_bytes(M, topk, E, out_rows))
+
+
+def qmm_moe_route(expert_ids, E: int, workspace, stream=None) -> None:
+    """Bucket the (token, slot) pairs of expert_ids int32 [M, topk] by expert into workspace
+    (a device uint8 tensor of qmm_moe_prefill_workspace_bytes bytes)."""
+    _need(expert_ids.dim() == 2 and expert_ids.element_size() == 4, "expert_ids must be int32 [M, topk]")
+    M, topk = expert_ids.shape
+    _check(load_library().qmm_moe_route(_ptr(expert_ids, "expert_ids"), M, topk, E, _ptr(workspace, "workspace"),
+                                        _bytes(workspace), _stream(stream)), "qmm_moe_route")
+
+
+def qmm_moe_prefill(stage, inp, codes, scales, biases, expert_ids, workspace, out, expert_w=None,
+                    stream=None) -> None:
+    """One stage of the routed experts over a batch, on a workspace routed by qmm_moe_route
+    with the same expert_ids; grid codes [E, rows, K/8].  Stage 1: inp x [M, K], out
+    h [M, topk, rows/2].  Stage 2: inp h [M, topk, K], out y [M, rows], expert_w [M, topk]."""
+    E, rows = codes.shape[0], codes.shape[1]
+    K = inp.shape[-1]
+    _need(expert_ids.dim() == 2 and expert_ids.element_size() == 4, "expert_ids must be int32 [M, topk]")
+    M, topk = expert_ids.shape
+    _check_weight(codes, scales, biases, E * rows, K, "expert grid")
+    if int(stage) == QMM_MOE_GATE_UP_SWIGLU:
+        _need(_bytes(inp) == M * K * 2, "x must be bf16 [M, K]")
+        _need(_elems(out) == M * topk * (rows // 2), "out must be [M, topk, rows/2]")
+    else:
+        _need(_bytes(inp) == M * topk * K * 2, "h must be bf16 [M, topk, K]")
+        _need(_elems(out) == M * rows, "out must be [M, rows]")
+        _need(expert_w is not None and _bytes(expert_w) == M * topk * 4, "expert_w must be fp32 [M, topk]")
+    _check(load_library().qmm_moe_prefill(int(stage), _ptr(inp, "in"), M, K, _ptr(codes, "codes"),
+                                          _ptr(scales, "scales"), _ptr(biases, "biases"), E, rows,
+                                          _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"), topk,
+                                          _ptr(workspace, "workspace"), _bytes(workspace), _ptr(out, "out"),
+                                          _out_dtype(out), _stream(stream)), "qmm_moe_prefill")

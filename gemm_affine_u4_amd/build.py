@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libqmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["qmm_api.cpp", "qmm_validate.cpp", "gemv_u4.hip", "gemm_u4.hip"]
+SOURCES = ["qmm_api.cpp", "qmm_validate.cpp", "gemv_u4.hip", "gemm_u4.hip", "moe_route.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -40,6 +40,7 @@ constexpr int kRow = 64;                 // bf16 per LDS row (one 64-wide group)
 constexpr int kStage = kBM * kRow;       // bf16 per LDS stage (32 KB)
 constexpr int kXcds = 8;
 static_assert(kBM == kBN, "x and weight stages share one shape");
+static_assert(kBM == kMoeTileRows, "the routing tiles are GEMM tiles");
 
 // Bank-group swizzle of LDS row r (see the header).
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
@@ -83,7 +84,7 @@ __device__ __forceinline__ int64_t gemm_weight_row(const GemmArgs& a, int64_t nt
   }
 }
 
-template <int EPI>
+template <int EPI, bool GATHER>
 __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t n_tiles,
                                                         int64_t tiles_per_xcd) {
   // One variable per x stage, and the two weight stages in a variable of their own: the
@@ -99,6 +100,31 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   if (tile >= m_tiles * n_tiles) return;
   const int64_t mt = tile % m_tiles;
   const int64_t nt = tile / m_tiles;
+
+  // Routed experts over a batch (GATHER): tile mt of the table is up to kBM bucketed pairs
+  // of one expert; its x rows are gathered (pair / moe_div) and its outputs go to the
+  // pairs' rows.  Otherwise the tile is x rows [mt*kBM, mt*kBM + kBM) of a dense GEMM.
+  int rows_here = kBM;
+  int pair_base = 0;
+  if constexpr (GATHER) {
+    if (mt >= a.moe_hdr[0]) return;
+    const int e = a.moe_tiles[2 * mt];
+    pair_base = a.moe_tiles[2 * mt + 1];
+    rows_here = min(kBM, a.moe_offsets[e + 1] - pair_base);
+    const int64_t er = int64_t(e) * a.N;  // first row of the expert in the grid
+    a.codes += er * (a.K >> 3);
+    a.scales += er * (a.K >> 6);
+    a.biases += er * (a.K >> 6);
+  }
+  // source row of tile row r (a row past the tile's end reads its last row; never stored)
+  auto x_row = [&](int r) -> int64_t {
+    if constexpr (GATHER) {
+      return a.moe_pairs[pair_base + min(r, rows_here - 1)] / a.moe_div;
+    } else {
+      const int64_t m = mt * kBM + r;
+      return m < a.M ? m : a.M - 1;
+    }
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,8 +142,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   uint32_t xoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t r = mt * kBM + 32 * wave + 8 * j + (lane >> 3);
-    if (r >= a.M) r = a.M - 1;
+    const int64_t r = x_row(32 * wave + 8 * j + (lane >> 3));
     const uint32_t chunk = uint32_t((lane & 7) ^ (lane >> 3) ^ (j & 1));
     xoff[j] = uint32_t(r) * K * 2 + chunk * 16u;
   }
@@ -303,8 +328,23 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   // A lane thus owns 4 consecutive columns of one row per register quad and writes them
   // with one 8-byte (bf16) or 16-byte (fp32) store where they share a destination and the
   // address is aligned, element by element otherwise (ragged edges, odd row strides).
-  const int64_t mrow0 = mt * kBM + 128 * wm + (lane & 31);
+  const int trow0 = 128 * wm + (lane & 31);  // tile row of this lane's output row, i = 0
   const int csub = 4 * (lane >> 5);
+  // output row of tile row trow0 + 32 i, false if the row does not exist; `scale` is the
+  // combine weight of a routed pair in stage 2, else 1
+  auto out_row = [&](int i, int64_t* m, float* scale) -> bool {
+    const int r = trow0 + 32 * i;
+    *scale = 1.f;
+    if constexpr (GATHER) {
+      if (r >= rows_here) return false;
+      *m = a.moe_pairs[pair_base + r];
+      if (a.moe_w) *scale = a.moe_w[*m];
+      return true;
+    } else {
+      *m = mt * kBM + r;
+      return *m < a.M;
+    }
+  };
   auto put = [&](void* dst, int64_t ld, int64_t cn, int64_t m, const float (&v)[4], int nvalid) {
     const int64_t idx = m * ld + cn;
     if (nvalid == 4 && (idx & 3) == 0) {
@@ -330,8 +370,9 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
         const int nvalid = int(min<int64_t>(4, a.I - p0));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t m = mrow0 + 32 * i;
-          if (m >= a.M) continue;
+          int64_t m;
+          float sc;
+          if (!out_row(i, &m, &sc)) continue;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[i][j][4 * g + e], acc[i][j + 1][4 * g + e]);
@@ -369,11 +410,12 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
         const bool one_range = n0 + 3 < end;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t m = mrow0 + 32 * i;
-          if (m >= a.M) continue;
+          int64_t m;
+          float sc;
+          if (!out_row(i, &m, &sc)) continue;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + lb[e];
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sc + lb[e];
           if (one_range) {
             put(dst, ld, cn, m, v, 4);
           } else {
@@ -400,11 +442,27 @@ int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
   const dim3 block{512u, 1u, 1u};
   if (epi == EPI_LINEAR) {
-    gemm_u4_kernel<EPI_LINEAR><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_LINEAR, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else if (epi == EPI_QKV) {
-    gemm_u4_kernel<EPI_QKV><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_QKV, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else {
-    gemm_u4_kernel<EPI_SWIGLU><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_SWIGLU, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
+  const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
+  const int64_t tiles = m_tiles * n_tiles;
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+  const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
+  const dim3 block{512u, 1u, 1u};
+  if (epi == EPI_SWIGLU) {
+    gemm_u4_kernel<EPI_SWIGLU, true><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+  } else if (epi == EPI_LINEAR) {
+    gemm_u4_kernel<EPI_LINEAR, true><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+  } else {
+    return 5;
   }
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }

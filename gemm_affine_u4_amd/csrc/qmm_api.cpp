@@ -9,6 +9,8 @@
 
 using qmm::Range;
 
+static_assert(QMM_MAX_EXPERTS_PREFILL == qmm::kMaxExpertsPrefill, "routing histogram size");
+
 namespace {
 
 uint64_t u4_code_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K) / 2; }
@@ -213,6 +215,68 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* cod
   a.f32_out = out_dtype == QMM_OUT_F32;
   if (stage == QMM_MOE_GATE_UP_SWIGLU) return qmm::launch_moe_gate_up(a, stream);
   return qmm::launch_moe_down(a, stream);
+}
+
+size_t qmm_moe_prefill_workspace_bytes(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
+  if (M < 1 || M > 65535 || topk < 1 || topk > QMM_MAX_TOPK || E < 1 || E > QMM_MAX_EXPERTS_PREFILL ||
+      out_rows < 0 || out_rows > (int64_t(1) << 24))
+    return 0;
+  return size_t(qmm::moe_layout(M, topk, E, out_rows).total);
+}
+
+int qmm_moe_route(const int32_t* expert_ids, int64_t M, int64_t topk, int64_t E, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  if (!expert_ids || !workspace) return QMM_ERR_NULL;
+  const size_t need = qmm_moe_prefill_workspace_bytes(M, topk, E, 0);
+  if (need == 0 || workspace_bytes < need) return QMM_ERR_SHAPE;
+  if (!qmm::aligned(expert_ids, 4) || !qmm::aligned(workspace, 256)) return QMM_ERR_ALIGN;
+  const Range outs[] = {{workspace, uint64_t(need)}};
+  const Range ins[] = {{expert_ids, uint64_t(M * topk) * 4}};
+  if (qmm::any_alias(outs, 1, ins, 1)) return QMM_ERR_ALIAS;
+  return qmm::launch_moe_route(expert_ids, M, topk, E, workspace, stream);
+}
+
+int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const uint32_t* codes,
+                    const uint16_t* scales, const uint16_t* biases, int64_t E, int64_t rows,
+                    const int32_t* expert_ids, const float* expert_w, int64_t topk, void* workspace,
+                    size_t workspace_bytes, void* out, int out_dtype, hipStream_t stream) {
+  if (stage != QMM_MOE_GATE_UP_SWIGLU && stage != QMM_MOE_DOWN_COMBINE) return QMM_ERR_ENUM;
+  if (int st = check_weight(in, codes, scales, biases)) return st;
+  if (!expert_ids || !workspace || !out || (stage == QMM_MOE_DOWN_COMBINE && !expert_w)) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  const bool s1 = stage == QMM_MOE_GATE_UP_SWIGLU;
+  const size_t need = qmm_moe_prefill_workspace_bytes(M, topk, E, s1 ? 0 : rows);
+  if (need == 0 || !qmm::k_ok(K) || rows < 1 || !matrix_fits(rows, K) || (s1 && rows % 2) ||
+      !acts_fit(s1 ? M : M * topk, K) || workspace_bytes < need)
+    return QMM_ERR_SHAPE;
+  const size_t e = out_elem(out_dtype);
+  if (!qmm::aligned(out, e) || !qmm::aligned(expert_ids, 4) || (expert_w && !qmm::aligned(expert_w, 4)) ||
+      !qmm::aligned(workspace, 256))
+    return QMM_ERR_ALIGN;
+  const int64_t P = M * topk;
+  const int64_t in_elems = s1 ? M * K : P * K;
+  const int64_t out_elems = s1 ? P * (rows / 2) : M * rows;
+  const Range outs[] = {{out, uint64_t(out_elems) * e}, {workspace, uint64_t(need)}};
+  const Range ins[] = {{in, uint64_t(in_elems) * 2},
+                       {codes, u4_code_bytes(E * rows, K)},
+                       {scales, u4_group_bytes(E * rows, K)},
+                       {biases, u4_group_bytes(E * rows, K)},
+                       {expert_ids, uint64_t(P) * 4},
+                       {expert_w, expert_w ? uint64_t(P) * 4 : 0}};
+  if (qmm::any_alias(outs, 2, ins, 6)) return QMM_ERR_ALIAS;
+
+  qmm::GemmArgs a = {};
+  a.x = in;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.M = s1 ? M : P;
+  a.K = K;
+  a.N = rows;
+  a.I = rows / 2;
+  a.f32_out = out_dtype == QMM_OUT_F32;
+  a.moe_w = s1 ? nullptr : expert_w;
+  return qmm::launch_moe_prefill(s1 ? 0 : 1, a, expert_ids, M, topk, E, workspace, out, stream);
 }
 
 }  // extern "C"

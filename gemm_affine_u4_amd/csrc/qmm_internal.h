@@ -47,13 +47,38 @@ struct GemmArgs {
   void* out0;              // LINEAR: y [M][N]; QKV: q [M][q_out]; SWIGLU: h [M][I]
   void* out1;              // QKV: k [M][kv_out]
   void* out2;              // QKV: v [M][kv_out]
-  int64_t M, K, N;         // N = weight rows (SWIGLU: 2*I)
+  int64_t M, K, N;         // N = weight rows (SWIGLU: 2*I); routed experts: rows of one expert
   int64_t q_out, kv_out, I;
   int f32_out;
+  // routed experts over a batch of tokens (gathered GEMM; null otherwise): the tile table
+  // and bucketed pairs written by the routing kernels, and x row = pair / moe_div
+  const int32_t* moe_hdr;      // [0] = number of tiles in the table
+  const int32_t* moe_tiles;    // [tiles][2] = (expert, first bucket position)
+  const int32_t* moe_offsets;  // [E+1] bucket boundaries
+  const int32_t* moe_pairs;    // [pairs] bucketed pair indices (token * topk + slot)
+  const float* moe_w;          // stage 2: combine weight of each pair; null in stage 1
+  int64_t moe_div;             // topk in stage 1 (x row of a pair), 1 in stage 2
 };
 
 // Prefill GEMM (LDS dequant + MFMA).
 int launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+// Gathered GEMM of the routed experts over a batch: m_tiles = bound on the tile table.
+int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
+
+// Routed experts over a batch (prefill): the workspace holds the bucketed routing and
+// the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
+constexpr int kMoeTileRows = 256;        // pairs per gathered GEMM tile (the GEMM's kBM)
+constexpr int kMaxExpertsPrefill = 4096; // experts the bucketing handles (LDS histogram)
+struct MoeLayout {
+  int64_t P, tmax, chunks;               // pairs, bound on tiles, routing chunks
+  uint64_t hdr, offsets, pairs, tiles, chunk, z, total;
+};
+MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows);
+int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, void* ws, hipStream_t s);
+// stage 0: gate+up+SwiGLU (g.N = 2*I expert rows, out = h [P][I]); stage 1: down + combine
+// (g.N = expert rows, out = y [M][N]).  g carries x/h, weights, K, N, I, f32_out.
+int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t M, int64_t topk, int64_t E,
+                       const void* ws, void* out, hipStream_t s);
 
 // Decode GEMV; M rows of x processed as independent GEMVs (grid.y).
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);

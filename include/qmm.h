@@ -59,6 +59,7 @@
 #ifndef QMM_H
 #define QMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -66,9 +67,10 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 1
+#define QMM_ABI_VERSION 2
 #define QMM_MAX_K 65536
 #define QMM_MAX_TOPK 64
+#define QMM_MAX_EXPERTS_PREFILL 4096
 
 enum qmm_status {
   QMM_OK = 0,
@@ -146,6 +148,66 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K,
                    const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
                    int64_t E, int64_t rows, const int32_t* expert_ids, const float* expert_w,
                    int64_t topk, void* out, int out_dtype, hipStream_t stream);
+
+/*
+ * Routed experts over a batch of tokens (prefill).  Token m has topk (token, slot)
+ * pairs p = m*topk + k, each with an expert id expert_ids[m][k] (an id outside [0, E)
+ * means "no expert"); the experts are the same in-place 3-D grid as qmm_moe_gather
+ * ("Sanctum-MLX", "Inside the server"; never concatenated: "Four Candles for the
+ * Cathedral", "What's not in this batch").  Prefill is dominated by the quantized
+ * matmuls ("Sanctum-MLX", "Latency testing"), so the pairs are bucketed by expert and
+ * each expert's weights are streamed once, through the MFMA GEMM, for all of the
+ * tokens routed to it (gathered through the bucket), instead of once per token.
+ *
+ * Three calls, in stream order:
+ *   qmm_moe_route    buckets the pairs of expert_ids by expert into the workspace
+ *                    (deterministic: by expert, then by pair index);
+ *   qmm_moe_prefill  stage QMM_MOE_GATE_UP_SWIGLU, then stage QMM_MOE_DOWN_COMBINE,
+ *                    both reading that routing.
+ * workspace: caller-owned device memory, 256-byte aligned, of at least
+ * qmm_moe_prefill_workspace_bytes(M, topk, E, out_rows) bytes, where out_rows is the
+ * row count of the down projection (0 if only stage 1 runs).  It holds the routing
+ * (written by qmm_moe_route, read by both stages) and the fp32 per-pair products of
+ * stage 2; its contents between calls are the library's.  One workspace serves one
+ * routing at a time: calls with different expert_ids on one workspace must be ordered
+ * on one stream, route before prefill.  The library still allocates nothing.
+ */
+
+/* Workspace bytes for M tokens x topk slots over E experts and a down projection of
+ * out_rows rows; 0 when M, topk, E or out_rows is out of range (M in [1, 65535],
+ * topk in [1, QMM_MAX_TOPK], E in [1, QMM_MAX_EXPERTS_PREFILL]).  Host only. */
+size_t qmm_moe_prefill_workspace_bytes(int64_t M, int64_t topk, int64_t E, int64_t out_rows);
+
+/*
+ * qmm_moe_route -- expert_ids: device int32 [M][topk].  Writes the routing into the
+ * workspace.  QMM_ERR_SHAPE for sizes out of range or a workspace below
+ * qmm_moe_prefill_workspace_bytes(M, topk, E, 0); QMM_ERR_ALIAS if the workspace
+ * overlaps expert_ids.
+ */
+int qmm_moe_route(const int32_t* expert_ids, int64_t M, int64_t topk, int64_t E,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qmm_moe_prefill -- one stage of the routed experts over M tokens.  expert_ids must be
+ * the array (same contents, M, topk, E) the workspace was routed with.
+ *   stage QMM_MOE_GATE_UP_SWIGLU: in = x [M][K] bf16; rows = 2*I (gate [0,I), up [I,2I)
+ *     of each expert); out h [M][topk][I]: h[m][k] = silu(G_e x_m) * (U_e x_m) for
+ *     e = expert_ids[m][k], zero for "no expert".  expert_w is ignored (may be NULL).
+ *   stage QMM_MOE_DOWN_COMBINE: in = h [M][topk][K] bf16 (K = I); rows = output size;
+ *     expert_w: device fp32 [M][topk]; out y [M][rows] = sum over k = 0..topk-1 of
+ *     expert_w[m][k] * (D_e h[m][k]); each product is formed in fp32 and the slots are
+ *     added in increasing k (no atomics: deterministic); "no expert" slots add nothing.
+ *     The workspace must also hold the fp32 products (out_rows = rows).
+ * Like qmm_fused_gate_up_swiglu and qmm_linear in the GEMM regime, the products use
+ * bf16-rounded dequantized weights.  Errors as at the top, plus QMM_ERR_SHAPE for a
+ * workspace that is too small and QMM_ERR_ALIAS if out or the workspace overlaps an
+ * input or each other.
+ */
+int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K,
+                    const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                    int64_t E, int64_t rows, const int32_t* expert_ids, const float* expert_w,
+                    int64_t topk, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                    hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* qmm_status_str(int status);

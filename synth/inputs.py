@@ -134,6 +134,22 @@ def gen_routing(cfg: int, layer: int, step: int, E: int, topk: int):
     return ids, p
 
 
+def gen_prefill_routing(cfg: int, layer: int, M: int, E: int, topk: int, skew: float = 0.5):
+    """Routing of M tokens: each token takes topk distinct experts, drawn without
+    replacement in proportion to a seeded per-expert popularity exp(skew * N(0,1)) (so
+    some experts get many more tokens than others, as a trained router's do), and fp32
+    softmax(N(0,1)) combine weights.  Returns (ids int32 [M, topk], p fp32 [M, topk])."""
+    pop = skew * rng(cfg, layer, PROJ_MOE_GATE_UP, F_IDS, 1 << 20).standard_normal(E)
+    # Gumbel top-k: the topk largest of log-popularity + Gumbel noise are a draw
+    # without replacement proportional to the popularity.
+    g = rng(cfg, layer, PROJ_MOE_GATE_UP, F_IDS, (1 << 20) + 1).gumbel(size=(M, E))
+    ids = np.argsort(-(pop[None, :] + g), axis=1, kind="stable")[:, :topk].astype(np.int32)
+    logits = rng(cfg, layer, PROJ_MOE_GATE_UP, F_LOGITS, 1 << 20).standard_normal((M, topk))
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return ids, p
+
+
 def gen_expert_grid(cfg: int, layer: int, proj: int, E: int, rows: int, K: int,
                     experts=None) -> U4Weight:
     """3-D expert grid [E, rows, ...]; expert e is seeded by index=e, so any subset of
@@ -182,6 +198,7 @@ class MoEShape:
 
 
 MOE_35B = MoEShape("35B-A3B-shaped MoE decode (hidden 2048, 256 experts, I 512, top-8)", 2048, 256, 512, 8)
+MOE_PREFILL_M = 2048   # tokens of the routed-expert prefill workload
 
 # config ids used as the first seed word
 CFG_TINY, CFG_14B, CFG_24B, CFG_PREFILL, CFG_MOE, CFG_TEST = 1, 2, 3, 4, 5, 9

@@ -25,7 +25,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["qmm_linear", "qmm_fused_qkv", "qmm_fused_gate_up_swiglu",
-                                           "qmm_moe_gather", "qmm_status_str", "qmm_abi_version"])
+                                           "qmm_moe_gather", "qmm_moe_prefill_workspace_bytes",
+                                           "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str",
+                                           "qmm_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert qmm.qmm_abi_version() == 1
+    assert qmm.qmm_abi_version() == 2
     for name, code in qmm.STATUS.items():
         assert qmm.qmm_status_str(code).startswith(name)
     assert qmm.qmm_status_str(99) == "QMM_ERR_UNKNOWN"
@@ -114,6 +116,67 @@ def test_overlapping_outputs_and_inputs_are_rejected():
     assert _linear(y=A) == S["QMM_ERR_ALIAS"]
     assert _linear(y=A + (1 << 16) + 512) == S["QMM_ERR_ALIAS"]
     assert _linear(y=A + (1 << 19) + 16) == S["QMM_ERR_ALIAS"]
+
+
+# ---- routed experts over a batch (prefill) --------------------------------------
+
+WS = A + (1 << 24)   # 256-byte aligned fake workspace
+
+
+def _route(ids=A, M=16, topk=2, E=4, ws=WS, nbytes=None):
+    if nbytes is None:
+        nbytes = qmm.qmm_moe_prefill_workspace_bytes(M, topk, E, 0)
+    return qmm.load_library().qmm_moe_route(ids, M, topk, E, ws, nbytes, None)
+
+
+def _prefill(stage=0, inp=A, M=16, K=512, codes=A + (1 << 16), s=A + (1 << 18), b=A + (1 << 19), E=4,
+             rows=64, ids=A + (1 << 22), ew=A + (1 << 23), topk=2, ws=WS, nbytes=None, out=A + (1 << 21), od=0):
+    if nbytes is None:
+        nbytes = qmm.qmm_moe_prefill_workspace_bytes(M, topk, E, 0 if stage == 0 else rows)
+    return qmm.load_library().qmm_moe_prefill(stage, inp, M, K, codes, s, b, E, rows, ids, ew, topk, ws, nbytes,
+                                              out, od, None)
+
+
+def test_moe_workspace_bytes():
+    wb = qmm.qmm_moe_prefill_workspace_bytes
+    assert wb(0, 8, 256) == 0 and wb(65536, 8, 256) == 0
+    assert wb(16, 0, 4) == 0 and wb(16, 65, 4) == 0
+    assert wb(16, 2, 0) == 0 and wb(16, 2, 4097) == 0
+    n0 = wb(2048, 8, 256, 0)
+    assert n0 % 256 == 0 and n0 >= 2048 * 8 * 4            # at least the bucketed pair list
+    # the stage-2 products are fp32 [M*topk][out_rows] on top of the routing
+    assert wb(2048, 8, 256, 2048) - n0 == 2048 * 8 * 2048 * 4
+    assert wb(1, 1, 1) > 0 and wb(65535, 64, 4096) > 0
+
+
+def test_moe_route_validation():
+    assert _route(ids=None) == S["QMM_ERR_NULL"]
+    assert _route(ws=None) == S["QMM_ERR_NULL"]
+    assert _route(M=0) == S["QMM_ERR_SHAPE"]
+    assert _route(E=5000) == S["QMM_ERR_SHAPE"]
+    assert _route(nbytes=qmm.qmm_moe_prefill_workspace_bytes(16, 2, 4) - 4) == S["QMM_ERR_SHAPE"]
+    assert _route(ws=WS + 128) == S["QMM_ERR_ALIGN"]
+    assert _route(ids=A + 2) == S["QMM_ERR_ALIGN"]
+    assert _route(ids=WS + 64) == S["QMM_ERR_ALIAS"]
+
+
+def test_moe_prefill_validation():
+    assert _prefill(stage=3) == S["QMM_ERR_ENUM"]
+    assert _prefill(od=4) == S["QMM_ERR_ENUM"]
+    assert _prefill(stage=1, ew=None) == S["QMM_ERR_NULL"]
+    assert _prefill(ws=None) == S["QMM_ERR_NULL"]
+    assert _prefill(ids=None) == S["QMM_ERR_NULL"]
+    assert _prefill(rows=63) == S["QMM_ERR_SHAPE"]                  # odd gate+up rows
+    assert _prefill(K=96) == S["QMM_ERR_SHAPE"]
+    assert _prefill(topk=65) == S["QMM_ERR_SHAPE"]
+    # stage 2 needs room for its fp32 products: a stage-1-sized workspace is too small
+    assert _prefill(stage=1, nbytes=qmm.qmm_moe_prefill_workspace_bytes(16, 2, 4, 0)) == S["QMM_ERR_SHAPE"]
+    assert _prefill(ws=WS + 16) == S["QMM_ERR_ALIGN"]
+    assert _prefill(inp=A + 8) == S["QMM_ERR_ALIGN"]
+    assert _prefill(out=A + (1 << 21) + 2, od=1) == S["QMM_ERR_ALIGN"]
+    assert _prefill(out=WS + 256) == S["QMM_ERR_ALIAS"]             # out inside the workspace
+    assert _prefill(ws=A + (1 << 16)) == S["QMM_ERR_ALIAS"]         # workspace on the weights
+    assert _prefill(out=A + (1 << 22)) == S["QMM_ERR_ALIAS"]        # out on the expert ids
 
 
 # ---- host-only build of the validation code ------------------------------------

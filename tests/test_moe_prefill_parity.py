@@ -1,0 +1,156 @@
+"""GPU parity of the routed experts over a batch of tokens (prefill) against the fp64
+oracle: routing + gathered gate+up+SwiGLU (stage 1), routing + gathered down + combine
+(stage 2).  Stage 2 reads an h made by the oracle (or seeded), never the GPU's stage 1.
+The GEMM rounds dequantized weights to bf16, so the oracle runs with bf16_weights."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_affine_u4_amd as qmm
+import synth
+from oracle import qmm_oracle as orc
+from gpu_util import Guarded, assert_within, dev, rne_bits_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+class Routed:
+    """A routed workspace for (ids, E) sized for a down projection of out_rows rows."""
+
+    def __init__(self, ids: np.ndarray, E: int, out_rows: int):
+        M, topk = ids.shape
+        n = qmm.qmm_moe_prefill_workspace_bytes(M, topk, E, out_rows)
+        assert n > 0
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        self.ids = dev(np.ascontiguousarray(ids, np.int32))
+        self.E = E
+        qmm.qmm_moe_route(self.ids, E, self.ws)
+
+
+def stage1(x_bits, grid, r: Routed, I, f32=True):
+    M, topk = r.ids.shape
+    out = Guarded((M, topk, I), f32)
+    qmm.qmm_moe_prefill(qmm.QMM_MOE_GATE_UP_SWIGLU, dev(x_bits), dev(grid.codes), dev(grid.scales),
+                        dev(grid.biases), r.ids, r.ws, out.t)
+    torch.cuda.synchronize()
+    return out.values()
+
+
+def stage2(h_bits, grid, r: Routed, p, f32=True):
+    M, topk = r.ids.shape
+    rows = grid.codes.shape[1]
+    out = Guarded((M, rows), f32)
+    qmm.qmm_moe_prefill(qmm.QMM_MOE_DOWN_COMBINE, dev(h_bits), dev(grid.codes), dev(grid.scales),
+                        dev(grid.biases), r.ids, r.ws, out.t, expert_w=dev(np.asarray(p, np.float32)))
+    torch.cuda.synchronize()
+    return out.values()
+
+
+def grids(shape: synth.MoEShape, cfg: int, layer: int):
+    gu = synth.gen_expert_grid(cfg, layer, synth.PROJ_MOE_GATE_UP, shape.E, 2 * shape.I, shape.hidden)
+    dn = synth.gen_expert_grid(cfg, layer, synth.PROJ_MOE_DOWN, shape.E, shape.hidden, shape.I)
+    return gu, dn
+
+
+def check_both_stages(shape, cfg, layer, M, ids, p, what):
+    gu, dn = grids(shape, cfg, layer)
+    x = synth.gen_x(cfg, layer, 0, M, shape.hidden)
+    r = Routed(ids, shape.E, shape.hidden)
+    h, th = orc.moe_prefill_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * shape.I)
+    g1 = stage1(x, gu, r, shape.I)
+    assert_within(g1, h, th, f"{what}: stage 1 h")
+    assert np.array_equal(stage1(x, gu, r, shape.I, f32=False), rne_bits_of(g1))
+    h_bits = orc.f32_to_bf16_bits(h)   # the oracle's own h, rounded, feeds both sides
+    y, ty = orc.moe_prefill_down_combine(h_bits, dn.codes, dn.scales, dn.biases, ids, p)
+    g2 = stage2(h_bits, dn, r, p)
+    assert_within(g2, y, ty, f"{what}: stage 2 y")
+    assert np.array_equal(stage2(h_bits, dn, r, p, f32=False), rne_bits_of(g2))
+    return g1, g2
+
+
+# Several GEMM tiles per expert (skewed popularity: one expert above 256 pairs, one
+# nearly empty), a ragged last tile everywhere, I and hidden not multiples of the tile.
+SMALL = synth.MoEShape("small MoE prefill (hidden 320, 8 experts, I 192, top-2)", 320, 8, 192, 2)
+
+
+def test_moe_prefill_several_tiles_per_expert():
+    M = 600
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 0, M, SMALL.E, SMALL.topk, skew=1.0)
+    counts = np.bincount(ids.ravel(), minlength=SMALL.E)
+    say(f"[moe prefill] {SMALL.name}, M={M}, pairs per expert {counts.tolist()}")
+    assert counts.max() > 256 and counts.min() < 256
+    check_both_stages(SMALL, synth.CFG_TEST, 0, M, ids, p, "several tiles")
+
+
+def test_moe_prefill_no_expert_ids_repeats_and_empty_experts():
+    shape = synth.MoEShape("small MoE prefill (hidden 256, 6 experts, I 64, top-3)", 256, 6, 64, 3)
+    M = 37
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 1, M, 4, shape.topk)   # experts 4, 5 get nothing
+    ids[1, 0] = -1
+    ids[5, 2] = shape.E        # past the grid: no expert
+    ids[9, :] = -7             # a token with no expert at all
+    ids[12, 1] = ids[12, 0]    # the same expert twice for one token
+    say(f"[moe prefill] ids with no expert, repeats, empty experts (M={M})")
+    g1, g2 = check_both_stages(shape, synth.CFG_TEST, 1, M, ids, p, "gaps")
+    assert np.all(g1[1, 0] == 0) and np.all(g1[5, 2] == 0) and np.all(g1[9] == 0)
+    assert np.array_equal(g1[12, 0], g1[12, 1])
+    assert np.all(g2[9] == 0)
+
+
+@pytest.mark.parametrize("M", [1, 9, 255, 257])
+def test_moe_prefill_small_batches(M):
+    shape = SMALL
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 2, M, shape.E, shape.topk)
+    say(f"[moe prefill] M={M}")
+    check_both_stages(shape, synth.CFG_TEST, 2, M, ids, p, f"M={M}")
+
+
+def test_moe_prefill_is_deterministic_and_workspace_reusable():
+    """The same call twice gives the same bits; a workspace routed again for other ids
+    (fewer tokens) gives what a fresh workspace gives."""
+    shape = SMALL
+    gu, dn = grids(shape, synth.CFG_TEST, 3)
+    ids_a, p_a = synth.gen_prefill_routing(synth.CFG_TEST, 3, 300, shape.E, shape.topk, skew=1.0)
+    ids_b, p_b = synth.gen_prefill_routing(synth.CFG_TEST, 4, 120, shape.E, shape.topk)
+    xa = synth.gen_x(synth.CFG_TEST, 3, 0, 300, shape.hidden)
+    xb = synth.gen_x(synth.CFG_TEST, 3, 1, 120, shape.hidden)
+    ra = Routed(ids_a, shape.E, shape.hidden)
+    a1 = stage1(xa, gu, ra, shape.I)
+    assert np.array_equal(a1, stage1(xa, gu, ra, shape.I))
+    hb = synth.gen_x(synth.CFG_TEST, 3, 2, 300 * shape.topk, shape.I).reshape(300, shape.topk, shape.I)
+    a2 = stage2(hb, dn, ra, p_a)
+    assert np.array_equal(a2, stage2(hb, dn, ra, p_a))
+    # reuse ra's workspace for ids_b
+    rb = Routed.__new__(Routed)
+    rb.ws, rb.E = ra.ws, shape.E
+    rb.ids = dev(ids_b)
+    qmm.qmm_moe_route(rb.ids, shape.E, rb.ws)
+    fresh = Routed(ids_b, shape.E, shape.hidden)
+    b1 = stage1(xb, gu, rb, shape.I)
+    assert np.array_equal(b1, stage1(xb, gu, fresh, shape.I))
+    hbb = synth.gen_x(synth.CFG_TEST, 3, 3, 120 * shape.topk, shape.I).reshape(120, shape.topk, shape.I)
+    assert np.array_equal(stage2(hbb, dn, rb, p_b), stage2(hbb, dn, fresh, p_b))
+
+
+def test_moe_prefill_35B_shape_full_batch_sampled_tokens():
+    """The 35B-A3B-shaped workload at its full batch (2048 tokens, top-8 of 256 experts),
+    in the launch configuration the bench times; the oracle checks a sample of tokens
+    (each token's outputs depend on that token's inputs and experts only)."""
+    shape = synth.MOE_35B
+    M = synth.MOE_PREFILL_M
+    cfg = synth.CFG_MOE
+    gu, dn = grids(shape, cfg, 0)
+    ids, p = synth.gen_prefill_routing(cfg, 0, M, shape.E, shape.topk)
+    x = synth.gen_x(cfg, 0, 0, M, shape.hidden)
+    # stage-2 input: seeded bf16 h of the magnitude SwiGLU outputs have here
+    h_in = synth.to_bf16_bits(0.05 * synth.bf16_bits_to_f32(synth.gen_x(cfg, 0, 1, M * shape.topk, shape.I)))
+    h_in = h_in.reshape(M, shape.topk, shape.I)
+    say(f"[moe prefill] {shape.name}, M={M}")
+    r = Routed(ids, shape.E, shape.hidden)
+    g1 = stage1(x, gu, r, shape.I)
+    g2 = stage2(h_in, dn, r, p)
+    sample = np.unique(np.r_[0, M - 1, np.random.default_rng(11).choice(M, 14, replace=False)])
+    h, th = orc.moe_prefill_gate_up(x[sample], gu.codes, gu.scales, gu.biases, ids[sample], 2 * shape.I)
+    assert_within(g1[sample], h, th, "35B stage 1 (sampled tokens)")
+    y, ty = orc.moe_prefill_down_combine(h_in[sample], dn.codes, dn.scales, dn.biases, ids[sample], p[sample])
+    assert_within(g2[sample], y, ty, "35B stage 2 (sampled tokens)")
