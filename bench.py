@@ -236,6 +236,8 @@ def main():
         torch.cuda.empty_cache()
         result["moe_35B_layer"] = bench_moe(torch, qmm, synth, T, dev, args.moe_steps)
         torch.cuda.empty_cache()
+        result["moe_35B_prefill"] = bench_moe_prefill(torch, qmm, synth, T, dev, args.prefill_reps)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps, w_qkv, w_gu, bytes_step)
@@ -410,6 +412,73 @@ def bench_moe(torch, qmm, synth, T, dev, n_steps):
                         f"{L}-layer pool, fresh routing per step and layer, {n_steps} steps in one graph",
             "us_per_layer": round(ms_layer * 1e3, 3), "bytes_per_layer": b_layer, "GB/s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_layer": 2}
+
+
+def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
+    """35B-A3B-shaped MoE prefill at 2048 tokens: routing, stage 1 (gathered gate+up+SwiGLU
+    GEMM) and stage 2 (gathered down GEMM + combine) per layer, over a 4-layer pool of
+    in-place expert grids (each layer's grids exceed the last-level cache)."""
+    sh = synth.MOE_35B
+    H, E, Ie, topk = sh.hidden, sh.E, sh.I, sh.topk
+    M = synth.MOE_PREFILL_M
+    L = 4
+    g_gu = synth.gen_expert_grid(synth.CFG_MOE, 0, synth.PROJ_MOE_GATE_UP, E, 2 * Ie, H)
+    g_dn = synth.gen_expert_grid(synth.CFG_MOE, 0, synth.PROJ_MOE_DOWN, E, H, Ie)
+    pgu, pdn = pool_of(torch, dev, g_gu, L), pool_of(torch, dev, g_dn, L)
+    del g_gu, g_dn
+    ids_np, p_np = synth.gen_prefill_routing(synth.CFG_MOE, 0, M, E, topk)
+    ids = torch.from_numpy(ids_np).to(dev)
+    pw = torch.from_numpy(p_np).to(dev)
+    x = up(torch, dev, synth.gen_x(synth.CFG_MOE, 0, 0, M, H))
+    h = torch.empty((M, topk, Ie), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(qmm.qmm_moe_prefill_workspace_bytes(M, topk, E, H), dtype=torch.uint8, device=dev)
+    st = T.stream
+
+    def route(i):
+        qmm.qmm_moe_route(ids, E, ws, stream=st)
+
+    def s1(i):
+        l = i % L
+        qmm.qmm_moe_prefill(qmm.QMM_MOE_GATE_UP_SWIGLU, x, pgu[0][l], pgu[1][l], pgu[2][l], ids, ws, h, stream=st)
+
+    def s2(i):
+        l = i % L
+        qmm.qmm_moe_prefill(qmm.QMM_MOE_DOWN_COMBINE, h, pdn[0][l], pdn[1][l], pdn[2][l], ids, ws, y,
+                            expert_w=pw, stream=st)
+
+    def layer(i):
+        route(i)
+        s1(i)
+        s2(i)
+
+    route(0)
+    torch.cuda.synchronize()
+    ms_route = T.per_call_ms(route, reps)
+    ms_s1 = T.per_call_ms(s1, reps)
+    ms_s2 = T.per_call_ms(s2, reps)
+    ms_layer = T.per_call_ms(layer, reps)
+    P = int((ids_np >= 0).sum())
+    used = np.unique(ids_np)
+    fl1 = 2.0 * P * 2 * Ie * H
+    fl2 = 2.0 * P * H * Ie
+    b1 = len(used) * weight_bytes(2 * Ie, H) + M * H * 2 + P * Ie * 2
+    b2 = len(used) * weight_bytes(H, Ie) + P * Ie * 2 + M * H * 2
+    del pgu, pdn
+
+    def rec(ms, fl, b):
+        return {"avg_us": round(ms * 1e3, 2), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                "GB/s": round(b / (ms * 1e-3) / 1e9, 1), "flop": fl, "bytes": b}
+
+    counts = np.bincount(ids_np.ravel(), minlength=E)
+    return {"workload": f"35B-A3B-shaped MoE prefill: {M} tokens x top-{topk} of {E} experts, hidden {H}, "
+                        f"expert I {Ie}; pairs per expert min {counts.min()} mean {counts.mean():.0f} "
+                        f"max {counts.max()}; {L}-layer pool",
+            "us_per_layer": round(ms_layer * 1e3, 2),
+            "TFLOP/s_per_layer": round((fl1 + fl2) / (ms_layer * 1e-3) / 1e12, 1),
+            "route": {"avg_us": round(ms_route * 1e3, 2)},
+            "gate_up_swiglu": rec(ms_s1, fl1, b1),
+            "down_combine": rec(ms_s2, fl2, b2)}
 
 
 def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step):

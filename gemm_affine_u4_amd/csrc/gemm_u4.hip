@@ -225,24 +225,32 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   struct Frags {
     bf16x8_t a[4], b[2];
   };
+  // A gathered tile often holds far fewer than kBM pairs: each wave then reads and
+  // multiplies only its 32-row blocks that hold some (act of its 4; wave-uniform branches).
+  int act = 4;
+  if constexpr (GATHER) act = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - 128 * wm + 31) / 32)));
   auto load_frags = [&](Frags& f, const uint16_t* as, const uint16_t* bs, int q) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
+      if (!GATHER || i < act) f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(bs + btile_row(j) * kRow + opoff[q]);
   };
   auto mfma16 = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
+      if (!GATHER || i < act) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+      }
   };
 
   // Instruction order inside a slot: the wave issues in order and an MFMA waits for the
   // matrix pipe, so the dequantization's ~24 VALU ops are spread 3 per MFMA (they then
   // run while the MFMA executes) and its LDS store goes late in the slot.
   auto interleave_slot = [&]() {
+    if constexpr (GATHER) return;  // the branches above split the slot: the compiler orders it
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA

@@ -14,104 +14,188 @@
 
 namespace qmm {
 
-constexpr int kRouteChunk = 1024;   // pairs per routing block
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 256;   // threads of the count and place blocks (one pair each per pass)
+constexpr int kScanThreads = 1024;   // the one block of the scan
+constexpr int kMaxChunks = 256;      // routing chunks (blocks of the count and place kernels)
 
 static __device__ __forceinline__ bool routed(int32_t e, int E) { return e >= 0 && e < E; }
 
-__global__ void __launch_bounds__(kRouteThreads) moe_route_count(const int32_t* ids, int64_t P, int E,
-                                                                 int32_t* chunk_counts) {
+// Pairs per chunk: a multiple of kRouteThreads, at most kMaxChunks chunks.
+static inline int64_t route_chunk(int64_t P) {
+  const int64_t per = (P + kMaxChunks - 1) / kMaxChunks;
+  const int64_t cs = (per + kRouteThreads - 1) / kRouteThreads * kRouteThreads;
+  return cs < kRouteThreads ? kRouteThreads : cs;
+}
+
+// counts[e][c] = pairs of chunk c routed to expert e.
+__global__ void __launch_bounds__(kRouteThreads) moe_route_count(const int32_t* __restrict__ ids, int64_t P,
+                                                                 int64_t cs, int E, int chunks,
+                                                                 int32_t* __restrict__ counts) {
   __shared__ int cnt[kMaxExpertsPrefill];
   for (int e = threadIdx.x; e < E; e += kRouteThreads) cnt[e] = 0;
   __syncthreads();
-  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
-  for (int t = threadIdx.x; t < kRouteChunk; t += kRouteThreads) {
-    const int64_t i = base + t;
-    if (i < P) {
-      const int32_t e = ids[i];
-      if (routed(e, E)) atomicAdd(&cnt[e], 1);  // counts only: their order does not matter
-    }
+  const int64_t base = int64_t(blockIdx.x) * cs;
+  const int64_t end = min(base + cs, P);
+  for (int64_t i = base + threadIdx.x; i < end; i += kRouteThreads) {
+    const int32_t e = ids[i];
+    if (routed(e, E)) atomicAdd(&cnt[e], 1);  // counts only: the order of the adds does not matter
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) chunk_counts[int64_t(blockIdx.x) * E + e] = cnt[e];
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) counts[int64_t(e) * chunks + blockIdx.x] = cnt[e];
 }
 
-// One block: per expert the total and the chunk prefix (in place), then bucket offsets and
-// the tile table (tiles of up to `bm` pairs, expert by expert), then absolute chunk bases.
-__global__ void __launch_bounds__(kRouteThreads) moe_route_scan(int32_t* chunk_counts, int chunks, int E, int bm,
-                                                                int32_t* hdr, int32_t* offsets, int32_t* tiles) {
+// Exclusive prefix sum over the block of one value per thread (kScanThreads threads);
+// returns the thread's prefix and sets *total.
+static __device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wsum[kScanThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const int ws = wsum[w];
+    before += w < wave ? ws : 0;
+    all += ws;
+  }
+  __syncthreads();  // wsum may be reused by the next call
+  *total = all;
+  return before + inc - v;
+}
+
+// One block.  (1) For each expert (one wave per expert at a time, 64 chunks per pass):
+// counts[e][c] becomes the exclusive prefix over chunks, and the expert's total is kept.
+// (2) Over the experts: bucket offsets (prefix of the totals), then the tile table: expert
+// e's bucket is cut into tiles of `bm` pairs, written at the prefix of the tile counts.
+__global__ void __launch_bounds__(kScanThreads) moe_route_scan(int32_t* __restrict__ counts, int chunks, int E,
+                                                               int bm, int32_t* __restrict__ hdr,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ tiles) {
   __shared__ int tot[kMaxExpertsPrefill];
-  __shared__ int off[kMaxExpertsPrefill];
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    int run = 0;
-    for (int c = 0; c < chunks; ++c) {
-      const int v = chunk_counts[int64_t(c) * E + e];
-      chunk_counts[int64_t(c) * E + e] = run;
-      run += v;
-    }
-    tot[e] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0, nt = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = acc;
-      offsets[e] = acc;
-      for (int s = 0; s < tot[e]; s += bm) {
-        tiles[2 * nt] = e;
-        tiles[2 * nt + 1] = acc + s;
-        ++nt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kScanThreads / 64;
+  for (int e = wave; e < E; e += kWaves) {
+    int32_t* row = counts + int64_t(e) * chunks;
+    int carry = 0;
+    for (int c0 = 0; c0 < chunks; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < chunks ? row[c] : 0;
+      int inc = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += u;
       }
-      acc += tot[e];
+      if (c < chunks) row[c] = carry + inc - v;
+      carry += __shfl(inc, 63, 64);
     }
-    offsets[E] = acc;
-    hdr[0] = nt;
-    hdr[1] = acc;
+    if (lane == 0) tot[e] = carry;
   }
   __syncthreads();
+  // each thread takes kPer consecutive experts
+  constexpr int kPer = kMaxExpertsPrefill / kScanThreads;
+  const int e0 = threadIdx.x * kPer;
+  int n_sum = 0, t_sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = e0 + j;
+    const int n = e < E ? tot[e] : 0;
+    n_sum += n;
+    t_sum += (n + bm - 1) / bm;
+  }
+  int n_all, t_all;
+  int off = block_exclusive_scan(n_sum, &n_all);
+  int tix = block_exclusive_scan(t_sum, &t_all);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = e0 + j;
+    if (e >= E) break;
+    const int n = tot[e];
+    offsets[e] = off;
+    for (int s = 0; s < n; s += bm) {
+      tiles[2 * tix] = e;
+      tiles[2 * tix + 1] = off + s;
+      ++tix;
+    }
+    off += n;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = n_all;
+    hdr[0] = t_all;
+    hdr[1] = n_all;
+  }
+}
+
+// Places the pairs of chunk c: pair i routed to e goes to offsets[e] + counts[e][c] + (pairs
+// of the chunk before i routed to e).  The chunk is taken kRouteThreads pairs at a time; a
+// running count per expert carries over between passes.
+__global__ void __launch_bounds__(kRouteThreads) moe_route_place(const int32_t* __restrict__ ids, int64_t P,
+                                                                 int64_t cs, int E, int chunks,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ pairs) {
+  __shared__ int run[kMaxExpertsPrefill];
+  __shared__ int32_t sid[kRouteThreads];
   for (int e = threadIdx.x; e < E; e += kRouteThreads)
-    for (int c = 0; c < chunks; ++c) chunk_counts[int64_t(c) * E + e] += off[e];
+    run[e] = offsets[e] + counts[int64_t(e) * chunks + blockIdx.x];
+  const int64_t base = int64_t(blockIdx.x) * cs;
+  const int64_t end = min(base + cs, P);
+  const int t = threadIdx.x;
+  for (int64_t b = base; b < end; b += kRouteThreads) {
+    const int64_t i = b + t;
+    const int32_t e = i < end ? ids[i] : -1;
+    sid[t] = e;
+    __syncthreads();  // sid written; run holds the counts before this pass
+    const bool ok = routed(e, E);
+    if (ok) {
+      int rank = 0;
+      for (int j = 0; j < t; ++j) rank += sid[j] == e;
+      pairs[run[e] + rank] = int32_t(i);
+    }
+    __syncthreads();  // every thread has read run and sid
+    if (ok) atomicAdd(&run[e], 1);
+  }
 }
 
-__global__ void __launch_bounds__(kRouteThreads) moe_route_place(const int32_t* ids, int64_t P, int E,
-                                                                 const int32_t* chunk_base, int32_t* pairs) {
-  __shared__ int32_t sid[kRouteChunk];
-  const int64_t base = int64_t(blockIdx.x) * kRouteChunk;
-  for (int t = threadIdx.x; t < kRouteChunk; t += kRouteThreads) {
-    const int64_t i = base + t;
-    sid[t] = i < P ? ids[i] : -1;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < kRouteChunk; t += kRouteThreads) {
-    const int32_t e = sid[t];
-    if (!routed(e, E)) continue;
-    int rank = 0;
-    for (int j = 0; j < t; ++j) rank += sid[j] == e;
-    pairs[chunk_base[int64_t(blockIdx.x) * E + e] + rank] = int32_t(base + t);
-  }
-}
-
-// h of the pairs with no expert is zero (the gathered GEMM writes routed pairs only).
+// h of the pairs with no expert is zero (the gathered GEMM writes routed pairs only):
+// one thread per pair, which clears its row when the pair has no expert.
 __global__ void __launch_bounds__(256) moe_zero_unrouted(const int32_t* ids, int64_t P, int E, void* h, int64_t I,
                                                          int f32) {
-  for (int64_t i = blockIdx.x; i < P; i += gridDim.x) {
-    if (routed(ids[i], E)) continue;
-    for (int64_t c = threadIdx.x; c < I; c += 256) store_out(h, i * I + c, 0.f, f32);
-  }
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= P || routed(ids[i], E)) return;
+  for (int64_t c = 0; c < I; ++c) store_out(h, i * I + c, 0.f, f32);
 }
 
 // y[m, n] = sum over the token's slots k with an expert, in increasing k, of
-// z[m*topk + k, n] (z already holds p * (D_e h) in fp32).
+// z[m*topk + k, n] (z already holds p * (D_e h) in fp32).  A thread adds 4 consecutive
+// columns (one 16-byte load per slot) when N is a multiple of 4, else one.
+template <bool VEC4>
 __global__ void __launch_bounds__(256) moe_combine(const int32_t* ids, int64_t M, int topk, int E, const float* z,
                                                    int64_t N, void* y, int f32) {
+  constexpr int W = VEC4 ? 4 : 1;
   for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
-    for (int64_t n = threadIdx.x; n < N; n += 256) {
-      float acc = 0.f;
+    for (int64_t n = int64_t(threadIdx.x) * W; n < N; n += 256 * W) {
+      float acc[W] = {};
       for (int k = 0; k < topk; ++k) {
         const int64_t pr = m * topk + k;
-        if (routed(ids[pr], E)) acc += z[pr * N + n];
+        if (!routed(ids[pr], E)) continue;
+        if constexpr (VEC4) {
+          const float4 v = *reinterpret_cast<const float4*>(z + pr * N + n);
+          acc[0] += v.x;
+          acc[1] += v.y;
+          acc[2] += v.z;
+          acc[3] += v.w;
+        } else {
+          acc[0] += z[pr * N + n];
+        }
       }
-      store_out(y, m * N + n, acc, f32);
+#pragma unroll
+      for (int e = 0; e < W; ++e) store_out(y, m * N + n + e, acc[e], f32);
     }
   }
 }
@@ -120,7 +204,8 @@ MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
   MoeLayout L;
   L.P = M * topk;
   L.tmax = (L.P + kMoeTileRows - 1) / kMoeTileRows + E;
-  L.chunks = (L.P + kRouteChunk - 1) / kRouteChunk;
+  L.chunk_pairs = route_chunk(L.P);
+  L.chunks = (L.P + L.chunk_pairs - 1) / L.chunk_pairs;
   auto up = [](uint64_t b) { return (b + 255) / 256 * 256; };
   uint64_t o = 0;
   L.hdr = o;      o = up(o + 16);
@@ -136,15 +221,16 @@ MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
 int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, void* ws, hipStream_t s) {
   const MoeLayout L = moe_layout(M, topk, E, 0);
   char* b = static_cast<char*>(ws);
-  int32_t* chunk = reinterpret_cast<int32_t*>(b + L.chunk);
+  int32_t* counts = reinterpret_cast<int32_t*>(b + L.chunk);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
   const dim3 blk{unsigned(kRouteThreads), 1u, 1u};
-  moe_route_count<<<dim3{unsigned(L.chunks), 1u, 1u}, blk, 0, s>>>(ids, L.P, int(E), chunk);
-  moe_route_scan<<<dim3{1u, 1u, 1u}, blk, 0, s>>>(chunk, int(L.chunks), int(E), kMoeTileRows,
-                                                   reinterpret_cast<int32_t*>(b + L.hdr),
-                                                   reinterpret_cast<int32_t*>(b + L.offsets),
-                                                   reinterpret_cast<int32_t*>(b + L.tiles));
-  moe_route_place<<<dim3{unsigned(L.chunks), 1u, 1u}, blk, 0, s>>>(ids, L.P, int(E), chunk,
-                                                                   reinterpret_cast<int32_t*>(b + L.pairs));
+  const dim3 grid{unsigned(L.chunks), 1u, 1u};
+  moe_route_count<<<grid, blk, 0, s>>>(ids, L.P, L.chunk_pairs, int(E), int(L.chunks), counts);
+  moe_route_scan<<<dim3{1u, 1u, 1u}, dim3{unsigned(kScanThreads), 1u, 1u}, 0, s>>>(
+      counts, int(L.chunks), int(E), kMoeTileRows, reinterpret_cast<int32_t*>(b + L.hdr), offsets,
+      reinterpret_cast<int32_t*>(b + L.tiles));
+  moe_route_place<<<grid, blk, 0, s>>>(ids, L.P, L.chunk_pairs, int(E), int(L.chunks), offsets, counts,
+                                       reinterpret_cast<int32_t*>(b + L.pairs));
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
@@ -157,7 +243,7 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
   a.moe_tiles = reinterpret_cast<const int32_t*>(b + L.tiles);
   a.moe_offsets = reinterpret_cast<const int32_t*>(b + L.offsets);
   a.moe_pairs = reinterpret_cast<const int32_t*>(b + L.pairs);
-  const unsigned zb = unsigned(L.P < 4096 ? L.P : 4096);
+  const unsigned zb = unsigned((L.P + 255) / 256);
   if (stage == 0) {
     // stage 1: h [P][I] of the routed pairs from the gathered GEMM, zeros for the others
     a.out0 = out;
@@ -174,7 +260,10 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
     a.moe_div = 1;
     if (int st = launch_gemm_moe(EPI_LINEAR, a, L.tmax, s)) return st;
     const unsigned mb = unsigned(M < 4096 ? M : 4096);
-    moe_combine<<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
+    if (a.N % 4 == 0)
+      moe_combine<true><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
+    else
+      moe_combine<false><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
   }
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }

@@ -70,7 +70,7 @@ int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
 constexpr int kMoeTileRows = 256;        // pairs per gathered GEMM tile (the GEMM's kBM)
 constexpr int kMaxExpertsPrefill = 4096; // experts the bucketing handles (LDS histogram)
 struct MoeLayout {
-  int64_t P, tmax, chunks;               // pairs, bound on tiles, routing chunks
+  int64_t P, tmax, chunk_pairs, chunks;  // pairs, bound on tiles, pairs per routing chunk, chunks
   uint64_t hdr, offsets, pairs, tiles, chunk, z, total;
 };
 MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows);
