@@ -162,6 +162,85 @@ def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=N
     return (y[..., :a], y[..., a:b], y[..., b:]), (t[..., :a], t[..., a:b], t[..., b:])
 
 
+# ---- fused QKV with rotary position embedding ------------------------------------
+#
+# The pages' unshipped second phase does the split of the fused QKV output and its
+# rotary position embedding in one kernel ("Sanctum-MLX", shipped phases table, Phase 2;
+# "The Cathedral Doubled Itself", the kernel that worked and the kernel that won't).  The
+# pages do not spell the rotation out; the readings taken here:
+#   * each head of head_dim rows is rotated in the half-split form: for i < rot/2 the
+#     pair (a, b) = (d_i, d_{i + rot/2}) becomes (a c - b s, b c + a s), dims [rot,
+#     head_dim) pass through (rot = head_dim is full rotary);
+#   * c, s come from a table cos_sin[p, i], cos_sin[p, rot/2 + i] (fp32) at the token's
+#     position p = positions[m]; the table is an input, built once by the caller;
+#   * Q and K heads are rotated, V heads are not;
+#   * with q_gate the Q section holds, per query head, head_dim query rows followed by
+#     head_dim output-gate rows ("The Cathedral Doubled Itself", the 35B port: the
+#     qwen3_5 q projection carries queries and gate together); the gate is not rotated.
+
+ROPE_EVAL_REL = 2.0 ** -21   # the GPU's fp32 evaluation of a c - b s (two products, one sum)
+
+
+def rope_head_rows(n_q: int, n_kv: int, head_dim: int, q_gate: bool):
+    """Row ranges of the fused weight: list of (kind, head, first_row) for every head, kind
+    in 'q', 'gate', 'k', 'v', in weight order."""
+    out = []
+    r = 0
+    for h in range(n_q):
+        out.append(("q", h, r))
+        r += head_dim
+        if q_gate:
+            out.append(("gate", h, r))
+            r += head_dim
+    for kind in ("k", "v"):
+        for h in range(n_kv):
+            out.append((kind, h, r))
+            r += head_dim
+    return out, r
+
+
+def rope_rotate(a, b, c, s):
+    """Half-split rotation of the pairs (a, b) by the angle whose cosine and sine are c, s."""
+    return a * c - b * s, b * c + a * s
+
+
+def qkv_rope(x_bits, codes, scales, biases, n_q: int, n_kv: int, head_dim: int, q_gate: bool, rot: int,
+             positions, cos_sin, lin_bias=None, bf16_weights: bool = False):
+    """Fused QKV projection, split into heads, Q and K heads rotated at each token's
+    position.  x_bits [M, K]; positions int [M]; cos_sin fp32 [max_pos, rot].
+    Returns ((q, gate, k, v), (tq, tg, tk, tv)), each [M, heads, head_dim] (gate None
+    unless q_gate); tolerances propagate the projection's through the rotation:
+    |c| t_a + |s| t_b, plus the GPU's fp32 evaluation (ROPE_EVAL_REL)."""
+    heads, rows = rope_head_rows(n_q, n_kv, head_dim, q_gate)
+    if codes.shape[0] != rows or head_dim % 2 or rot % 2 or not 0 < rot <= head_dim:
+        raise ValueError("inconsistent rotary QKV shape")
+    x = np.atleast_2d(np.asarray(x_bits))
+    y, t = linear(x, codes, scales, biases, lin_bias, bf16_weights=bf16_weights)
+    M = x.shape[0]
+    pos = np.asarray(positions, dtype=np.int64).reshape(M)
+    cs = np.asarray(cos_sin, dtype=np.float32).astype(np.float64)
+    half = rot // 2
+    c = cs[pos, :half][:, None, :]          # [M, 1, half]
+    s = cs[pos, half:rot][:, None, :]
+    out = {k: np.zeros((M, n_q if k in ("q", "gate") else n_kv, head_dim)) for k in ("q", "gate", "k", "v")}
+    tol = {k: np.zeros_like(v) for k, v in out.items()}
+    for kind, h, r0 in heads:
+        out[kind][:, h, :] = y[:, r0:r0 + head_dim]
+        tol[kind][:, h, :] = t[:, r0:r0 + head_dim]
+    for kind in ("q", "k"):
+        v, tv = out[kind], tol[kind]
+        a, b = v[..., :half].copy(), v[..., half:rot].copy()
+        ta, tb = tv[..., :half].copy(), tv[..., half:rot].copy()
+        ra, rb = rope_rotate(a, b, c, s)
+        v[..., :half], v[..., half:rot] = ra, rb
+        ev = ROPE_EVAL_REL * (np.abs(a * c) + np.abs(b * s) + np.abs(b * c) + np.abs(a * s))
+        tv[..., :half] = np.abs(c) * ta + np.abs(s) * tb + ev
+        tv[..., half:rot] = np.abs(c) * tb + np.abs(s) * ta + ev
+    g = out["gate"] if q_gate else None
+    tg = tol["gate"] if q_gate else None
+    return (out["q"], g, out["k"], out["v"]), (tol["q"], tg, tol["k"], tol["v"])
+
+
 # ---- SwiGLU ------------------------------------------------------------------
 
 def sigmoid(g) -> np.ndarray:

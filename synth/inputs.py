@@ -150,6 +150,27 @@ def gen_prefill_routing(cfg: int, layer: int, M: int, E: int, topk: int, skew: f
     return ids, p
 
 
+def gen_rope_table(max_pos: int, rot: int, base: float = 1.0e6) -> np.ndarray:
+    """Rotary table fp32 [max_pos, rot]: cos in [:, :rot/2], sin in [:, rot/2:], at the
+    angle fp32(p) * inv_freq_i with inv_freq_i = fp32(base^(-2i/rot)) rounded to fp32
+    (the usual construction), cos/sin of that fp32 angle rounded to fp32."""
+    half = rot // 2
+    inv = (base ** (-(2.0 * np.arange(half)) / rot)).astype(np.float32)
+    ang = (np.arange(max_pos, dtype=np.float32)[:, None] * inv[None, :]).astype(np.float32)
+    a64 = ang.astype(np.float64)
+    return np.concatenate([np.cos(a64), np.sin(a64)], axis=1).astype(np.float32)
+
+
+def gen_positions(cfg: int, layer: int, M: int, max_pos: int, contiguous: bool = True) -> np.ndarray:
+    """int32 positions of M tokens: a seeded start and M consecutive positions (a prompt
+    chunk), or M independent positions (tokens of different sequences)."""
+    g = rng(cfg, layer, PROJ_QKV, F_IDS, 1 << 21)
+    if contiguous:
+        start = int(g.integers(0, max(1, max_pos - M + 1)))
+        return np.arange(start, start + M, dtype=np.int32)
+    return g.integers(0, max_pos, size=M).astype(np.int32)
+
+
 def gen_expert_grid(cfg: int, layer: int, proj: int, E: int, rows: int, K: int,
                     experts=None) -> U4Weight:
     """3-D expert grid [E, rows, ...]; expert e is seeded by index=e, so any subset of
@@ -186,6 +207,29 @@ DENSE_24B = DecodeShape("24B-dense-shaped decode (hidden 5120, q 4096, kv 1024, 
                         5120, 4096, 1024, 32768)
 PREFILL_M = 2048
 DOUBLED_Q = DecodeShape("doubled-Q QKV (hidden 5120, q 24x256x2, kv 4x256)", 5120, 12288, 1024, 0)
+
+
+@dataclass(frozen=True)
+class RopeShape:
+    name: str
+    K: int
+    n_q: int
+    n_kv: int
+    head_dim: int
+    q_gate: bool
+    rot: int
+    base: float
+
+    @property
+    def rows(self) -> int:
+        return (self.n_q * (2 if self.q_gate else 1) + 2 * self.n_kv) * self.head_dim
+
+
+ROPE_14B = RopeShape("14B-shaped QKV + RoPE (hidden 5120, 40 q / 8 kv heads x 128, full rotary, base 1e6)",
+                     5120, 40, 8, 128, False, 128, 1.0e6)
+ROPE_GATED = RopeShape("doubled-Q QKV + RoPE (hidden 5120, 24 q heads x 256 with output gate, 4 kv heads, "
+                       "rotary 64 of 256, base 1e7)", 5120, 24, 4, 256, True, 64, 1.0e7)
+ROPE_MAX_POS = 32768
 
 
 @dataclass(frozen=True)

@@ -232,6 +232,146 @@ def test_fused_gate_up_equals_swiglu_of_unfused():
     assert not np.allclose(h, h_swapped)
 
 
+# ---- fused QKV with rotary position embedding -------------------------------------
+
+def _rope_fixture(n_q=2, n_kv=1, hd=8, q_gate=False, K=128, seed=3):
+    heads, rows = orc.rope_head_rows(n_q, n_kv, hd, q_gate)
+    w = synth.gen_weight(synth.CFG_TEST, seed, synth.PROJ_QKV, rows, K, bias="uniform")
+    lb = synth.gen_lin_bias(synth.CFG_TEST, seed, rows)
+    return w, lb, heads, rows
+
+
+def _table(angles):
+    """cos/sin table fp32 [P, rot] from angles [P, rot/2] (fp64 -> fp32)."""
+    a = np.asarray(angles, np.float64)
+    return np.concatenate([np.cos(a), np.sin(a)], axis=1).astype(np.float32)
+
+
+def _heads_of(y, heads, hd, kind):
+    return np.stack([y[:, r0:r0 + hd] for k, h, r0 in heads if k == kind], axis=1)
+
+
+@pytest.mark.parametrize("q_gate", [False, True])
+def test_rope_at_angle_zero_is_the_plain_head_split(q_gate):
+    """c = 1, s = 0: every output is the fused projection's row, split per head; the gate
+    heads are the second head_dim rows of each doubled query head."""
+    hd, rot = 8, 8
+    w, lb, heads, rows = _rope_fixture(q_gate=q_gate)
+    x = synth.gen_x(synth.CFG_TEST, 4, 0, 3, 128)
+    tab = _table(np.zeros((5, rot // 2)))
+    (q, g, k, v), (tq, tg, tk, tv) = orc.qkv_rope(x, w.codes, w.scales, w.biases, 2, 1, hd, q_gate, rot,
+                                                  [0, 4, 2], tab, lb)
+    y, t = orc.linear(x, w.codes, w.scales, w.biases, lb)
+    stride = hd * (2 if q_gate else 1)
+    assert np.array_equal(q[:, 0], y[:, 0:hd]) and np.array_equal(q[:, 1], y[:, stride:stride + hd])
+    if q_gate:
+        assert np.array_equal(g[:, 0], y[:, hd:2 * hd]) and np.array_equal(g[:, 1], y[:, 3 * hd:4 * hd])
+    else:
+        assert g is None
+    kv0 = 2 * stride
+    assert np.array_equal(k[:, 0], y[:, kv0:kv0 + hd]) and np.array_equal(v[:, 0], y[:, kv0 + hd:kv0 + 2 * hd])
+    # the tolerance is the projection's plus only the rotation's fp32 evaluation term
+    ya, yb = np.abs(y[:, 0:hd // 2]), np.abs(y[:, hd // 2:hd])
+    extra = tq[:, 0] - t[:, 0:hd]
+    assert np.all(extra >= 0) and np.all(extra <= 2.0 ** -20 * np.c_[ya + yb, ya + yb])
+
+
+def test_rope_gate_rows_hold_the_gate():
+    """A doubled query head whose gate rows are all zero (codes, scales and biases) gives a
+    gate output equal to its additive bias exactly, and queries that are not."""
+    hd, rot, K = 8, 8, 64
+    w, lb, heads, rows = _rope_fixture(n_q=1, n_kv=1, hd=hd, q_gate=True, K=K)
+    c, s_, b = w.codes.copy(), w.scales.copy(), w.biases.copy()
+    c[hd:2 * hd] = 0
+    s_[hd:2 * hd] = 0
+    b[hd:2 * hd] = 0
+    x = synth.gen_x(synth.CFG_TEST, 5, 0, 2, K)
+    (q, g, k, v), _ = orc.qkv_rope(x, c, s_, b, 1, 1, hd, True, rot, [1, 3], _table(np.full((4, rot // 2), 0.7)), lb)
+    assert np.array_equal(g[:, 0], np.broadcast_to(orc.bf16_to_f64(lb[hd:2 * hd]), (2, hd)))
+    assert not np.allclose(q[:, 0], orc.bf16_to_f64(lb[0:hd]))
+
+
+def test_rope_quarter_turn_swaps_the_halves_with_a_sign():
+    """c = 0, s = 1 (a quarter turn): rotated dims (a, b) become (-b, a) exactly, in Q and K
+    only; dims past rot and all of V pass through."""
+    hd, rot = 8, 4
+    w, lb, heads, rows = _rope_fixture(hd=hd)
+    x = synth.gen_x(synth.CFG_TEST, 6, 0, 2, 128)
+    tab = _table(np.full((3, rot // 2), np.pi / 2))
+    tab[:, :rot // 2] = 0.0          # cos exactly 0, sin exactly 1
+    tab[:, rot // 2:] = 1.0
+    (q, g, k, v), _ = orc.qkv_rope(x, w.codes, w.scales, w.biases, 2, 1, hd, False, rot, [2, 1], tab, lb)
+    y, _ = orc.linear(x, w.codes, w.scales, w.biases, lb)
+    for kind, out in (("q", q), ("k", k)):
+        ref = _heads_of(y, heads, hd, kind)
+        assert np.array_equal(out[..., 0:2], -ref[..., 2:4])
+        assert np.array_equal(out[..., 2:4], ref[..., 0:2])
+        assert np.array_equal(out[..., 4:], ref[..., 4:])
+    assert np.array_equal(v, _heads_of(y, heads, hd, "v"))
+
+
+def test_rope_is_complex_multiplication_by_the_position_phase():
+    """Half-split rotation = multiplying z_i = d_i + j d_{i+rot/2} by exp(j theta_{p,i}), with
+    theta_{p,i} = p * w_i per token position: checked with complex arithmetic and, for
+    each pair, the preserved modulus; a token at position p1 + p2 equals the token at p1
+    turned by p2 (the phase adds)."""
+    hd, rot, P = 16, 12, 40
+    w, lb, heads, rows = _rope_fixture(hd=hd, K=192, seed=4)
+    omega = 10000.0 ** (-np.arange(rot // 2) * 2.0 / rot)
+    ang = np.arange(P)[:, None] * omega[None, :]
+    tab = _table(ang)
+    x = synth.gen_x(synth.CFG_TEST, 7, 0, 3, 192)
+    x = np.concatenate([x[:1], x[:1], x[1:]])   # token 0 twice: positions 7 and 7 + 25
+    pos = np.array([7, 32, 3, 39])
+    (q, g, k, v), _ = orc.qkv_rope(x, w.codes, w.scales, w.biases, 2, 1, hd, False, rot, pos, tab, lb)
+    y, _ = orc.linear(x, w.codes, w.scales, w.biases, lb)
+    h = rot // 2
+    for kind, out in (("q", q), ("k", k)):
+        ref = _heads_of(y, heads, hd, kind)
+        z = ref[..., :h] + 1j * ref[..., h:rot]
+        cs = tab.astype(np.float64)
+        phase = (cs[pos, :h] + 1j * cs[pos, h:rot])[:, None, :]
+        zr = z * phase
+        assert np.allclose(out[..., :h], zr.real, rtol=0, atol=1e-12)
+        assert np.allclose(out[..., h:rot], zr.imag, rtol=0, atol=1e-12)
+        assert np.allclose(np.abs(out[..., :h] + 1j * out[..., h:rot]), np.abs(z), rtol=1e-6)
+        # the same token at 32 = 7 + 25 is the token at 7 turned by 25 positions
+        turn = np.exp(1j * 25 * omega)
+        assert np.allclose((out[0, :, :h] + 1j * out[0, :, h:rot]) * turn,
+                           out[1, :, :h] + 1j * out[1, :, h:rot], rtol=0, atol=1e-5 * np.abs(z).max())
+
+
+def test_rope_tolerance_covers_perturbed_inputs():
+    """Any projection values within their tolerance rotate to within the rotated tolerance."""
+    hd, rot = 8, 8
+    w, lb, heads, rows = _rope_fixture(hd=hd)
+    x = synth.gen_x(synth.CFG_TEST, 8, 0, 2, 128)
+    tab = synth.gen_rope_table(64, rot, 1e4)
+    pos = [17, 63]
+    (q, _, k, _), (tq, _, tk, _) = orc.qkv_rope(x, w.codes, w.scales, w.biases, 2, 1, hd, False, rot, pos, tab, lb)
+    y, t = orc.linear(x, w.codes, w.scales, w.biases, lb)
+    ref = _heads_of(y, heads, hd, "q")
+    tref = _heads_of(t, heads, hd, "q")
+    cs = tab.astype(np.float64)[pos]
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        e = rng.choice([-1.0, 1.0], size=ref.shape) * tref
+        yp = ref + e
+        a, b = yp[..., :4], yp[..., 4:]
+        c, s = cs[:, None, :4], cs[:, None, 4:]
+        ra, rb = a * c - b * s, b * c + a * s
+        assert np.all(np.abs(ra - q[..., :4]) <= tq[..., :4]) and np.all(np.abs(rb - q[..., 4:]) <= tq[..., 4:])
+
+
+def test_rope_table_generator():
+    """cos^2 + sin^2 = 1 to fp32 rounding, position 0 is the identity, column i turns at
+    base^(-2i/rot) radians per position."""
+    tab = synth.gen_rope_table(100, 16, 1e6).astype(np.float64)
+    assert np.allclose(tab[:, :8] ** 2 + tab[:, 8:] ** 2, 1.0, atol=1e-6)
+    assert np.array_equal(tab[0], np.r_[np.ones(8), np.zeros(8)])
+    assert np.allclose(np.arctan2(tab[1, 8:], tab[1, :8]), 1e6 ** (-np.arange(8) * 2.0 / 16), rtol=1e-6)
+
+
 # ---- SwiGLU -------------------------------------------------------------------
 
 def test_silu_special_values_and_library_agreement():
