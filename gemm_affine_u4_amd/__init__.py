@@ -12,7 +12,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_gate_up_swiglu", "qmm_moe_gather",
+__all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm_fused_gate_up_swiglu",
+           "qmm_moe_gather",
            "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
            "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
 
@@ -32,6 +33,8 @@ _SIGNATURES = {
     "qmm_linear": [_P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P],
     "qmm_fused_qkv": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _INT, _P],
     "qmm_fused_gate_up_swiglu": [_P, _I64, _I64, _P, _P, _P, _I64, _P, _INT, _P],
+    "qmm_fused_qkv_rope": [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _INT, _I64, _P, _P, _I64, _P, _P, _P, _P, _P,
+                           _INT, _P],
     "qmm_moe_gather": [_INT, _P, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
     "qmm_moe_prefill_workspace_bytes": [_I64, _I64, _I64, _I64],
     "qmm_moe_route": [_P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
@@ -163,6 +166,34 @@ def qmm_fused_qkv(x, codes, scales, biases, q, k, v, lin_bias=None, stream=None)
                                         _ptr(biases, "biases"), q.shape[-1], k.shape[-1],
                                         _ptr(lin_bias, "lin_bias"), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
                                         _out_dtype(q), _stream(stream)), "qmm_fused_qkv")
+
+
+def qmm_fused_qkv_rope(x, codes, scales, biases, q, k, v, positions, cos_sin, rot_dim: int, gate=None,
+                       lin_bias=None, stream=None) -> None:
+    """Fused QKV + split + rotary embedding.  q [M, n_q, head_dim], k/v [M, n_kv, head_dim],
+    gate [M, n_q, head_dim] when the Q section carries output-gate heads (then the weight
+    has (2*n_q + 2*n_kv)*head_dim rows); positions int32 [M]; cos_sin fp32 [max_pos, rot_dim]."""
+    M, K = _mk(x)
+    _need(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [M, heads, head_dim]")
+    n_q, hd = q.shape[1], q.shape[2]
+    n_kv = k.shape[1]
+    q_gate = 1 if gate is not None else 0
+    rows = (n_q * (1 + q_gate) + 2 * n_kv) * hd
+    _check_weight(codes, scales, biases, rows, K)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(tuple(q.shape) == (M, n_q, hd) and tuple(k.shape) == (M, n_kv, hd) and tuple(v.shape) == (M, n_kv, hd),
+          "q, k, v shapes do not match")
+    _need(gate is None or tuple(gate.shape) == (M, n_q, hd), "gate must be [M, n_q, head_dim]")
+    _need(positions.numel() == M and positions.element_size() == 4, "positions must be int32 [M]")
+    _need(cos_sin.dim() == 2 and cos_sin.shape[1] == rot_dim and cos_sin.element_size() == 4,
+          "cos_sin must be fp32 [max_pos, rot_dim]")
+    _need(lin_bias is None or _bytes(lin_bias) == rows * 2, "lin_bias must be bf16 [rows]")
+    od = _out_dtype(q)
+    _check(load_library().qmm_fused_qkv_rope(
+        _ptr(x, "x"), M, K, _ptr(codes, "codes"), _ptr(scales, "scales"), _ptr(biases, "biases"), n_q, n_kv, hd,
+        q_gate, rot_dim, _ptr(positions, "positions"), _ptr(cos_sin, "cos_sin"), cos_sin.shape[0],
+        _ptr(lin_bias, "lin_bias"), _ptr(q, "q"), _ptr(gate, "gate"), _ptr(k, "k"), _ptr(v, "v"), od,
+        _stream(stream)), "qmm_fused_qkv_rope")
 
 
 def qmm_fused_gate_up_swiglu(x, codes, scales, biases, h, stream=None) -> None:

@@ -28,6 +28,7 @@
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_rope.h"
 
 namespace qmm {
 
@@ -78,6 +79,12 @@ __device__ __forceinline__ int64_t gemm_weight_row(const GemmArgs& a, int64_t nt
     int64_t p = nt * (kBN / 2) + (t & 127);
     if (p >= a.I) p = a.I - 1;
     return t < 128 ? p : a.I + p;
+  } else if constexpr (EPI == EPI_ROPE) {
+    // rotary QKV: tile rows t and t + 128 are the two rows of pair nt*128 + t
+    int64_t p = nt * (kBN / 2) + (t & 127);
+    if (p >= (a.N >> 1)) p = (a.N >> 1) - 1;
+    const RopePair rp = rope_pair(uint32_t(p), a.rope);
+    return t < 128 ? rp.ra : rp.rb;
   } else {
     const int64_t n = nt * kBN + t;
     return n < a.N ? n : a.N - 1;
@@ -212,7 +219,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 
   // LDS row of the B operand for column tile j of this wave
   auto btile_row = [&](int j) -> int {
-    if constexpr (EPI == EPI_SWIGLU) return (j == 0 ? 0 : 128) + 32 * wn;
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_ROPE) return (j == 0 ? 0 : 128) + 32 * wn;
     else return 64 * wn + 32 * j;
   };
   // Operand lane l holds row l % 32 of a 32-row tile and k 8 (l / 32) .. +7 of a 16-wide
@@ -369,7 +376,30 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
         if (e < nvalid) store_out(dst, idx + e, v[e], a.f32_out);
     }
   };
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_ROPE) {
+    // pair p's two rows are columns p0 + e of acc[i][0] and acc[i][1]; each is rotated
+    // (or passed through) and stored into its head of q/k/v/gate
+    static_for<4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      const int64_t p0 = nt * (kBN / 2) + 32 * wn + 8 * g + csub;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t p = p0 + e;
+        if (p >= (a.N >> 1)) continue;
+        const RopePair rp = rope_pair(uint32_t(p), a.rope);
+        const float lba = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.ra]) : 0.f;
+        const float lbb = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.rb]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int64_t m;
+          float sc;
+          if (!out_row(i, &m, &sc)) continue;
+          rope_store(a.rope, a.out0, a.out1, a.out2, rp, m, acc[i][0][4 * g + e] + lba, acc[i][1][4 * g + e] + lbb,
+                     a.f32_out);
+        }
+      }
+    });
+  } else if constexpr (EPI == EPI_SWIGLU) {
     static_for<4>([&](auto gc) {
       constexpr int j = 0, g = decltype(gc)::value;
       {
@@ -444,7 +474,9 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 
 int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   const int64_t m_tiles = (a.M + kBM - 1) / kBM;
-  const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
+  const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + kBN / 2 - 1) / (kBN / 2)
+                          : epi == EPI_ROPE ? ((a.N >> 1) + kBN / 2 - 1) / (kBN / 2)
+                                            : (a.N + kBN - 1) / kBN;
   const int64_t tiles = m_tiles * n_tiles;
   const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
   const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
@@ -453,6 +485,8 @@ int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
     gemm_u4_kernel<EPI_LINEAR, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else if (epi == EPI_QKV) {
     gemm_u4_kernel<EPI_QKV, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+  } else if (epi == EPI_ROPE) {
+    gemm_u4_kernel<EPI_ROPE, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else {
     gemm_u4_kernel<EPI_SWIGLU, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   }

@@ -29,6 +29,7 @@
 // number of rows in the call.
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_rope.h"
 
 namespace qmm {
 
@@ -96,7 +97,9 @@ __device__ __forceinline__ float row_partial(const RowData<CPL>& r, const uint32
   return acc;
 }
 
-// Row of the weight handled by slot `slot` of unit `unit`, and whether it exists.
+// Row of the weight handled by slot `slot` of unit `unit`, and whether it exists.  The
+// paired epilogues (SwiGLU, rotary QKV) put the two rows of a pair in slots s and s + P,
+// 32 lanes apart.
 template <int LPR, int EPI>
 __device__ __forceinline__ int64_t unit_row(int64_t unit, int slot, const GemvArgs& a, bool* valid) {
   constexpr int RPI = 64 / LPR;
@@ -106,6 +109,12 @@ __device__ __forceinline__ int64_t unit_row(int64_t unit, int slot, const GemvAr
     *valid = pair < a.I;
     const int64_t r = slot < P ? pair : a.I + pair;
     return *valid ? r : 0;
+  } else if constexpr (EPI == EPI_ROPE) {
+    constexpr int P = RPI / 2;
+    const int64_t pair = unit * P + (slot % P);
+    *valid = pair < (a.rows >> 1);
+    const RopePair rp = rope_pair(uint32_t(*valid ? pair : 0), a.rope);
+    return slot < P ? rp.ra : rp.rb;
   } else {
     const int64_t r = unit * RPI + slot;
     *valid = r < a.rows;
@@ -125,6 +134,12 @@ __device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u
     const float up = __shfl_xor(v, 32);
     if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
       store_out(a.out0, out_base + u * P + slot, silu_times(v, up), a.f32_out);
+  } else if constexpr (EPI == EPI_ROPE) {
+    if (valid && a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
+    const float vb = __shfl_xor(v, 32);
+    if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
+      rope_store(a.rope, a.out0, a.out1, a.out2, rope_pair(uint32_t(u * P + slot), a.rope), blockIdx.y, v, vb,
+                 a.f32_out);
   } else {
     if (valid && lane == slot_result_lane<LPR>(slot)) {
       if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
@@ -559,7 +574,8 @@ static int64_t s1_waves(int64_t units, int64_t batch, int64_t resident) {
 static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64_t batch, int64_t* units, int* n,
                           int64_t* blocks, int* threads) {
   const int rpi = 64 / sh.lpr;
-  *units = (epi == EPI_SWIGLU) ? (a.I + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
+  const int64_t pairs = epi == EPI_SWIGLU ? a.I : (a.rows >> 1);
+  *units = (epi == EPI_SWIGLU || epi == EPI_ROPE) ? (pairs + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
   // K-split kernel (the single-slice cases compute their own grid)
   const int64_t want = (kTargetWaves / sh.ksplit + batch - 1) / batch;
   const int64_t g = want < *units ? want : *units;
@@ -581,6 +597,8 @@ int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
     QMM_GEMV_CASES(EPI_LINEAR, false)
   } else if (epi == EPI_QKV) {
     QMM_GEMV_CASES(EPI_QKV, false)
+  } else if (epi == EPI_ROPE) {
+    QMM_GEMV_CASES(EPI_ROPE, false)
   } else {
     QMM_GEMV_CASES(EPI_SWIGLU, false)
   }

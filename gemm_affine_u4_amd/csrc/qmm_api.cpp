@@ -43,6 +43,7 @@ qmm::GemmArgs gemm_args(const qmm::GemvArgs& g, int64_t M, int64_t N) {
   a.kv_out = g.kv_out;
   a.I = g.I;
   a.f32_out = g.f32_out;
+  a.rope = g.rope;
   return a;
 }
 size_t out_elem(int d) { return d == QMM_OUT_F32 ? 4 : 2; }
@@ -140,6 +141,63 @@ int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes
   a.f32_out = out_dtype == QMM_OUT_F32;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_QKV, gemm_args(a, M, rows), stream);
   return qmm::launch_gemv(qmm::EPI_QKV, a, M, stream);
+}
+
+int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
+                       const uint16_t* biases, int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim, int q_gate,
+                       int64_t rot_dim, const int32_t* positions, const float* cos_sin, int64_t max_pos,
+                       const uint16_t* lin_bias, void* q, void* gate, void* k, void* v, int out_dtype,
+                       hipStream_t stream) {
+  if (int st = check_weight(x, codes, scales, biases)) return st;
+  if (!q || !k || !v || !positions || !cos_sin || (q_gate && !gate)) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  const int64_t lim = int64_t(1) << 20;
+  if (M < 1 || M > 65535 || !qmm::k_ok(K) || n_q_heads < 1 || n_q_heads > lim || n_kv_heads < 1 ||
+      n_kv_heads > lim || head_dim < 2 || head_dim % 2 || head_dim > lim || (q_gate != 0 && q_gate != 1) ||
+      rot_dim < 2 || rot_dim % 2 || rot_dim > head_dim || max_pos < 1 || max_pos > (int64_t(1) << 31) - 1)
+    return QMM_ERR_SHAPE;
+  const int64_t rows = (n_q_heads * (1 + q_gate) + 2 * n_kv_heads) * head_dim;
+  if (rows > (int64_t(1) << 30) || !matrix_fits(rows, K) || !acts_fit(M, K) ||
+      uint64_t(max_pos) * uint64_t(rot_dim) > (uint64_t(1) << 40))
+    return QMM_ERR_SHAPE;
+  const size_t e = out_elem(out_dtype);
+  if (!qmm::aligned(q, e) || !qmm::aligned(k, e) || !qmm::aligned(v, e) || (q_gate && !qmm::aligned(gate, e)) ||
+      !qmm::aligned(positions, 4) || !qmm::aligned(cos_sin, 4) || (lin_bias && !qmm::aligned(lin_bias, 2)))
+    return QMM_ERR_ALIGN;
+  const uint64_t qn = uint64_t(M * n_q_heads * head_dim) * e, kvn = uint64_t(M * n_kv_heads * head_dim) * e;
+  const Range outs[] = {{q, qn}, {k, kvn}, {v, kvn}, {q_gate ? gate : nullptr, q_gate ? qn : 0}};
+  const Range ins[] = {{x, uint64_t(M * K) * 2},
+                       {codes, u4_code_bytes(rows, K)},
+                       {scales, u4_group_bytes(rows, K)},
+                       {biases, u4_group_bytes(rows, K)},
+                       {lin_bias, lin_bias ? uint64_t(rows) * 2 : 0},
+                       {positions, uint64_t(M) * 4},
+                       {cos_sin, uint64_t(max_pos) * uint64_t(rot_dim) * 4}};
+  if (qmm::any_alias(outs, 4, ins, 7)) return QMM_ERR_ALIAS;
+
+  qmm::GemvArgs a = {};
+  a.x = x;
+  a.codes = codes;
+  a.scales = scales;
+  a.biases = biases;
+  a.lin_bias = lin_bias;
+  a.out0 = q;
+  a.out1 = k;
+  a.out2 = v;
+  a.K = K;
+  a.rows = rows;
+  a.f32_out = out_dtype == QMM_OUT_F32;
+  a.rope.positions = positions;
+  a.rope.cos_sin = cos_sin;
+  a.rope.gate = q_gate ? gate : nullptr;
+  a.rope.max_pos = int32_t(max_pos);
+  a.rope.n_q = int32_t(n_q_heads);
+  a.rope.n_kv = int32_t(n_kv_heads);
+  a.rope.head_dim = int32_t(head_dim);
+  a.rope.rot = int32_t(rot_dim);
+  a.rope.q_gate = q_gate;
+  if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_ROPE, gemm_args(a, M, rows), stream);
+  return qmm::launch_gemv(qmm::EPI_ROPE, a, M, stream);
 }
 
 int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes,

@@ -5,7 +5,18 @@
 
 namespace qmm {
 
-enum Epilogue : int { EPI_LINEAR = 0, EPI_QKV = 1, EPI_SWIGLU = 2 };
+enum Epilogue : int { EPI_LINEAR = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_ROPE = 3 };
+
+// Fused QKV with rotary embedding (EPI_ROPE).  The weight is heads of head_dim rows: per
+// query head its query rows and, with q_gate, its output-gate rows; then the K heads,
+// then the V heads.  Outputs: q -> out0, k -> out1, v -> out2 ([M][heads][head_dim]),
+// gate -> `gate`.
+struct RopeArgs {
+  const int32_t* positions;  // [M] token positions (clamped to [0, max_pos) when read)
+  const float* cos_sin;      // [max_pos][rot]: cos in [0, rot/2), sin in [rot/2, rot)
+  void* gate;                // [M][n_q][head_dim] output gate (q_gate), else null
+  int32_t max_pos, n_q, n_kv, head_dim, rot, q_gate;
+};
 
 // Launch geometry of the decode kernels, a function of K only, so a row's
 // reduction order never depends on how many rows are in the call (fused and
@@ -36,6 +47,7 @@ struct GemvArgs {
   int64_t E;               // experts in the grid
   int topk;
   int f32_out;
+  RopeArgs rope;           // EPI_ROPE only
 };
 
 struct GemmArgs {
@@ -58,6 +70,7 @@ struct GemmArgs {
   const int32_t* moe_pairs;    // [pairs] bucketed pair indices (token * topk + slot)
   const float* moe_w;          // stage 2: combine weight of each pair; null in stage 1
   int64_t moe_div;             // topk in stage 1 (x row of a pair), 1 in stage 2
+  RopeArgs rope;               // EPI_ROPE only
 };
 
 // Prefill GEMM (LDS dequant + MFMA).

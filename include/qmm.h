@@ -128,6 +128,38 @@ int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K,
                              int64_t I, void* h, int out_dtype, hipStream_t stream);
 
 /*
+ * qmm_fused_qkv_rope -- the fused QKV projection with its split and rotary position
+ * embedding in the same kernel: the pages' fused split+RoPE second phase ("Sanctum-MLX",
+ * shipped phases table, Phase 2; "The Cathedral Doubled Itself", the kernel that worked
+ * and the kernel that won't), which MLX's lazy graph kept from shipping; on a HIP
+ * stream the outputs are ordinary stream-ordered results.
+ *   Weight rows, in heads of head_dim rows: for each of the n_q_heads query heads its
+ *   head_dim query rows and, when q_gate = 1, head_dim output-gate rows right after them
+ *   (the doubled q projection of "The Cathedral Doubled Itself", the 35B port); then the
+ *   n_kv_heads K heads; then the n_kv_heads V heads.
+ *   rows = (n_q_heads * (1 + q_gate) + 2 * n_kv_heads) * head_dim.
+ *   Outputs (row-major, separate buffers): q [M][n_q_heads][head_dim],
+ *   k and v [M][n_kv_heads][head_dim], gate [M][n_q_heads][head_dim] (q_gate = 1 only;
+ *   ignored otherwise).
+ *   lin_bias: nullable [rows] bf16, added to each projection before the rotation.
+ *   Rotation (Q and K heads; V and gate pass through): for i < rot_dim/2 the dims
+ *   (i, i + rot_dim/2) of a head of token m, values (a, b), become
+ *   (a*c - b*s, b*c + a*s) with c = cos_sin[p][i], s = cos_sin[p][rot_dim/2 + i],
+ *   p = positions[m]; dims [rot_dim, head_dim) pass through.
+ *   positions: device int32 [M]; values outside [0, max_pos) are clamped to that range.
+ *   cos_sin: device fp32 [max_pos][rot_dim], built once by the caller (cos in the first
+ *   half of a row, sin in the second).
+ *   head_dim and rot_dim even, 2 <= rot_dim <= head_dim; q_gate 0 or 1.  Decode (M <= 8)
+ *   runs the GEMV, larger M the GEMM, as for qmm_fused_qkv.
+ */
+int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K,
+                       const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                       int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim, int q_gate,
+                       int64_t rot_dim, const int32_t* positions, const float* cos_sin, int64_t max_pos,
+                       const uint16_t* lin_bias, void* q, void* gate, void* k, void* v,
+                       int out_dtype, hipStream_t stream);
+
+/*
  * qmm_moe_gather -- routed experts for one decode token, gathered in place from a
  * 3-D expert grid: codes [E][rows][K/8], scales/biases [E][rows][K/64] (the MoE
  * expert grid of "Sanctum-MLX", "Inside the server"; the experts are read where

@@ -24,7 +24,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["qmm_linear", "qmm_fused_qkv", "qmm_fused_gate_up_swiglu",
+    assert declared_functions() == sorted(["qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm_fused_gate_up_swiglu",
                                            "qmm_moe_gather", "qmm_moe_prefill_workspace_bytes",
                                            "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str",
                                            "qmm_abi_version"])
@@ -116,6 +116,35 @@ def test_overlapping_outputs_and_inputs_are_rejected():
     assert _linear(y=A) == S["QMM_ERR_ALIAS"]
     assert _linear(y=A + (1 << 16) + 512) == S["QMM_ERR_ALIAS"]
     assert _linear(y=A + (1 << 19) + 16) == S["QMM_ERR_ALIAS"]
+
+
+# ---- fused QKV with rotary embedding ------------------------------------------------
+
+def _rope(x=A, M=1, K=512, codes=A + (1 << 16), s=A + (1 << 18), b=A + (1 << 19), nq=2, nkv=1, hd=64, qg=0,
+          rot=64, pos=A + (1 << 22), cs=A + (1 << 23), maxpos=16, lb=None, q=A + (1 << 21), g=None,
+          k=A + (1 << 21) + 4096, v=A + (1 << 21) + 8192, od=0):
+    return qmm.load_library().qmm_fused_qkv_rope(x, M, K, codes, s, b, nq, nkv, hd, qg, rot, pos, cs, maxpos, lb,
+                                                 q, g, k, v, od, None)
+
+
+def test_rope_validation():
+    assert _rope(pos=None) == S["QMM_ERR_NULL"]
+    assert _rope(cs=None) == S["QMM_ERR_NULL"]
+    assert _rope(qg=1, g=None) == S["QMM_ERR_NULL"]      # output gate heads need a gate buffer
+    assert _rope(od=3) == S["QMM_ERR_ENUM"]
+    assert _rope(hd=63, rot=62) == S["QMM_ERR_SHAPE"]     # odd head_dim
+    assert _rope(rot=66) == S["QMM_ERR_SHAPE"]            # rot_dim > head_dim
+    assert _rope(rot=31) == S["QMM_ERR_SHAPE"]            # odd rot_dim
+    assert _rope(rot=0) == S["QMM_ERR_SHAPE"]
+    assert _rope(nkv=0) == S["QMM_ERR_SHAPE"]
+    assert _rope(qg=2, g=A + (1 << 24)) == S["QMM_ERR_SHAPE"]
+    assert _rope(maxpos=0) == S["QMM_ERR_SHAPE"]
+    assert _rope(pos=A + (1 << 22) + 2) == S["QMM_ERR_ALIGN"]
+    assert _rope(cs=A + (1 << 23) + 1) == S["QMM_ERR_ALIGN"]
+    assert _rope(k=A + (1 << 21) + 64) == S["QMM_ERR_ALIAS"]          # k overlaps q
+    assert _rope(q=A + (1 << 22)) == S["QMM_ERR_ALIAS"]               # q on the positions
+    assert _rope(v=A + (1 << 23) + 8) == S["QMM_ERR_ALIAS"]           # v on the table
+    assert _rope(qg=1, g=A + (1 << 21) + 4096 + 32) == S["QMM_ERR_ALIAS"]   # gate overlaps k
 
 
 # ---- routed experts over a batch (prefill) --------------------------------------
