@@ -229,6 +229,7 @@ def main():
     }
 
     if not args.headline_only:
+        result["qkv_rope"] = bench_rope(torch, qmm, synth, T, dev, pq, args.prefill_reps)
         result["prefill_gemm"] = bench_prefill(torch, qmm, synth, T, dev, pq, pg, args.prefill_reps)
         del pq, pg
         torch.cuda.empty_cache()
@@ -315,6 +316,47 @@ def bench_prefill(torch, qmm, synth, T, dev, pq, pg, reps):
             "fused_gate_up": rec(ms_gu, fl_gu, "gemm_u4_kernel<SWIGLU>"),
             "context_torch_bf16_matmul": {"qkv_shape": rec(ms_dq, fl_qkv, "torch.matmul bf16 (hipBLASLt)"),
                                           "gate_up_shape": rec(ms_dg, fl_gu, "torch.matmul bf16 (hipBLASLt)")}}
+
+
+def bench_rope(torch, qmm, synth, T, dev, pq, reps):
+    """Fused QKV + split + rotary embedding on the 14B layer shape (40 q / 8 kv heads x 128,
+    full rotary), decode M=1 over the rotating weight pool and prefill M=2048, each next
+    to the plain fused QKV call on the same weights (the epilogue's cost is the gap)."""
+    sh = synth.ROPE_14B
+    K, hd = sh.K, sh.head_dim
+    P = pq[0].shape[0]
+    tab = up(torch, dev, synth.gen_rope_table(synth.ROPE_MAX_POS, sh.rot, sh.base).view(np.int32)).view(torch.float32)
+    out = {}
+    for M in (1, synth.PREFILL_M):
+        x = up(torch, dev, synth.gen_x(synth.CFG_14B, 0, 0, M, K))
+        pos = torch.from_numpy(synth.gen_positions(synth.CFG_14B, 0, M, synth.ROPE_MAX_POS)).to(dev)
+        q = torch.empty((M, sh.n_q, hd), dtype=torch.bfloat16, device=dev)
+        k = torch.empty((M, sh.n_kv, hd), dtype=torch.bfloat16, device=dev)
+        v = torch.empty((M, sh.n_kv, hd), dtype=torch.bfloat16, device=dev)
+        st = T.stream
+        n = 4 * P if M == 1 else reps
+
+        def rope(i):
+            l = i % P
+            qmm.qmm_fused_qkv_rope(x, pq[0][l], pq[1][l], pq[2][l], q, k, v, pos, tab, sh.rot, stream=st)
+
+        def plain(i):
+            l = i % P
+            qmm.qmm_fused_qkv(x, pq[0][l], pq[1][l], pq[2][l], q.view(M, -1), k.view(M, -1), v.view(M, -1),
+                              stream=st)
+
+        ms_r = T.per_call_ms(rope, n)
+        ms_p = T.per_call_ms(plain, n)
+        b = weight_bytes(sh.rows, K) + M * K * 2 + M * sh.rows * 2
+        fl = 2.0 * M * sh.rows * K
+        key = "decode_M1" if M == 1 else f"prefill_M{M}"
+        out[key] = {"rope_us": round(ms_r * 1e3, 3), "plain_qkv_us": round(ms_p * 1e3, 3),
+                    "rope_over_plain": round(ms_r / ms_p, 4),
+                    ("GB/s" if M == 1 else "TFLOP/s"): round((b / (ms_r * 1e-3) / 1e9) if M == 1
+                                                             else (fl / (ms_r * 1e-3) / 1e12), 1)}
+        del x, q, k, v
+    return {"workload": f"fused QKV + RoPE, {sh.n_q} q / {sh.n_kv} kv heads x {hd}, rotary {sh.rot}, "
+                        f"K={K}; decode M=1 over a {P}-layer pool and prefill M={synth.PREFILL_M}", **out}
 
 
 def bench_step_24b(torch, qmm, synth, T, dev, n_steps):

@@ -360,9 +360,12 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
       return *m < a.M;
     }
   };
+  // 4 consecutive outputs from element idx: one vector store when all 4 exist and the
+  // address is aligned to it (the ABI only promises element alignment of the buffer)
   auto put = [&](void* dst, int64_t ld, int64_t cn, int64_t m, const float (&v)[4], int nvalid) {
     const int64_t idx = m * ld + cn;
-    if (nvalid == 4 && (idx & 3) == 0) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(dst) + uintptr_t(idx) * (a.f32_out ? 4u : 2u);
+    if (nvalid == 4 && (addr & (a.f32_out ? 15u : 7u)) == 0) {
       if (a.f32_out) {
         *reinterpret_cast<float4*>(static_cast<float*>(dst) + idx) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
@@ -377,25 +380,81 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     }
   };
   if constexpr (EPI == EPI_ROPE) {
-    // pair p's two rows are columns p0 + e of acc[i][0] and acc[i][1]; each is rotated
-    // (or passed through) and stored into its head of q/k/v/gate
+    // Pair p's two rows are columns p0 + e of acc[i][0] and acc[i][1]; each is rotated (or
+    // passed through) and stored into its head of q/k/v/gate.  When head_dim and rot are
+    // multiples of 8, the 4 pairs p0 .. p0+3 of a lane (p0 % 4 == 0) lie in one head and
+    // one region (rotated or not), so their dims are consecutive: one 16-byte read of
+    // cos and of sin, and 4-element stores.
+    const RopeArgs& ra = a.rope;
+    const bool grouped = (ra.head_dim % 8) == 0 && (ra.rot % 8) == 0;
+    int64_t mrow[4];
+    const float* trow[4];
+    bool have[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sc;
+      have[i] = out_row(i, &mrow[i], &sc);
+      const int32_t pos = have[i] ? min(max(ra.positions[mrow[i]], 0), ra.max_pos - 1) : 0;
+      trow[i] = ra.cos_sin + int64_t(pos) * ra.rot;
+    }
     static_for<4>([&](auto gc) {
       constexpr int g = decltype(gc)::value;
       const int64_t p0 = nt * (kBN / 2) + 32 * wn + 8 * g + csub;
+      if (p0 >= (a.N >> 1)) return;
+      if (grouped) {
+        const RopePair rp = rope_pair(uint32_t(p0), ra);
+        float lba[4], lbb[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t p = p0 + e;
-        if (p >= (a.N >> 1)) continue;
-        const RopePair rp = rope_pair(uint32_t(p), a.rope);
-        const float lba = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.ra]) : 0.f;
-        const float lbb = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.rb]) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          lba[e] = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.ra + e]) : 0.f;
+          lbb[e] = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.rb + e]) : 0.f;
+        }
+        void* dst;
+        int64_t nh;
+        switch (rp.buf) {
+          case ROPE_Q: dst = a.out0; nh = ra.n_q; break;
+          case ROPE_K: dst = a.out1; nh = ra.n_kv; break;
+          case ROPE_V: dst = a.out2; nh = ra.n_kv; break;
+          default: dst = ra.gate; nh = ra.n_q; break;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int64_t m;
-          float sc;
-          if (!out_row(i, &m, &sc)) continue;
-          rope_store(a.rope, a.out0, a.out1, a.out2, rp, m, acc[i][0][4 * g + e] + lba, acc[i][1][4 * g + e] + lbb,
-                     a.f32_out);
+          if (!have[i]) continue;
+          float va[4], vb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = acc[i][0][4 * g + e] + lba[e];
+            vb[e] = acc[i][1][4 * g + e] + lbb[e];
+          }
+          if (rp.ri >= 0) {
+            const float4 c = *reinterpret_cast<const float4*>(trow[i] + rp.ri);
+            const float4 sn = *reinterpret_cast<const float4*>(trow[i] + (ra.rot >> 1) + rp.ri);
+            const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x0 = va[e], x1 = vb[e];
+              va[e] = fmaf(x0, cc[e], -(x1 * ss[e]));
+              vb[e] = fmaf(x1, cc[e], x0 * ss[e]);
+            }
+          }
+          const int64_t base = (mrow[i] * nh + rp.head) * int64_t(ra.head_dim);
+          put(dst, 0, base + rp.da, 0, va, 4);
+          put(dst, 0, base + rp.db, 0, vb, 4);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t p = p0 + e;
+          if (p >= (a.N >> 1)) continue;
+          const RopePair rp = rope_pair(uint32_t(p), ra);
+          const float lba = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.ra]) : 0.f;
+          const float lbb = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.rb]) : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!have[i]) continue;
+            rope_store(ra, a.out0, a.out1, a.out2, rp, mrow[i], acc[i][0][4 * g + e] + lba,
+                       acc[i][1][4 * g + e] + lbb, a.f32_out);
+          }
         }
       }
     });

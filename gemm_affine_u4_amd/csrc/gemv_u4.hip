@@ -122,10 +122,37 @@ __device__ __forceinline__ int64_t unit_row(int64_t unit, int slot, const GemvAr
   }
 }
 
+// Operands of a unit's epilogue that come from memory, fetched together with the unit's
+// rows so that its store does not wait on a dependent load: the rotary cos/sin of the
+// lane's pair (EPI_ROPE; `trow` is the token's table row).  Nothing for the others.
+struct EpiPre {
+  float c, s;
+};
+template <int LPR, int EPI>
+__device__ __forceinline__ const float* epi_table_row(const GemvArgs& a) {
+  if constexpr (EPI == EPI_ROPE) {
+    const int32_t pos = min(max(a.rope.positions[blockIdx.y], 0), a.rope.max_pos - 1);
+    return a.rope.cos_sin + int64_t(pos) * a.rope.rot;
+  } else {
+    return nullptr;
+  }
+}
+template <int LPR, int EPI>
+__device__ __forceinline__ void epi_fetch(EpiPre& p, int64_t u, int slot, const GemvArgs& a, const float* trow) {
+  if constexpr (EPI == EPI_ROPE) {
+    constexpr int P = (64 / LPR) / 2;
+    const int64_t pair = u * P + (slot % P);
+    const RopePair rp = rope_pair(uint32_t(pair < (a.rows >> 1) ? pair : 0), a.rope);
+    const int ri = rp.ri >= 0 ? rp.ri : 0;
+    p.c = trow[ri];
+    p.s = trow[(a.rope.rot >> 1) + ri];
+  }
+}
+
 // Store of one row unit's result (slot totals after slot_reduce).
 template <int LPR, int EPI>
 __device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u, int slot, int lane,
-                                           int64_t out_base) {
+                                           int64_t out_base, const EpiPre& ep) {
   constexpr int RPI = 64 / LPR;
   constexpr int P = RPI / 2;
   bool valid;
@@ -138,8 +165,8 @@ __device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u
     if (valid && a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
     const float vb = __shfl_xor(v, 32);
     if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
-      rope_store(a.rope, a.out0, a.out1, a.out2, rope_pair(uint32_t(u * P + slot), a.rope), blockIdx.y, v, vb,
-                 a.f32_out);
+      rope_store_cs(a.rope, a.out0, a.out1, a.out2, rope_pair(uint32_t(u * P + slot), a.rope), blockIdx.y, v, vb,
+                    ep.c, ep.s, a.f32_out);
   } else {
     if (valid && lane == slot_result_lane<LPR>(slot)) {
       if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
@@ -236,12 +263,15 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
   // Ring of DEPTH row buffers: unit u is computed from buf[(u - u_begin) % DEPTH], and
   // the buffer is refilled with unit u + DEPTH right after.
   RowData<CPL> buf[DEPTH];
+  EpiPre ep[DEPTH];
+  const float* trow = epi_table_row<LPR, EPI>(a);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (u_begin + d < u_end) {
       bool valid;
       const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
       load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
+      epi_fetch<LPR, EPI>(ep[d], u_begin + d, slot, a, trow);
     }
   }
   load_x_chunks<LPR, CPL>(xr, c0, xp, xs);
@@ -252,10 +282,12 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
       const int64_t u = u0 + d;
       if (u < u_end) {
         const float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        const EpiPre cur = ep[d];
         if (u + DEPTH < u_end) {
           bool valid;
           const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
           load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
+          epi_fetch<LPR, EPI>(ep[d], u + DEPTH, slot, a, trow);
         }
         // double-buffered by unit parity: the next write to this buffer comes after the
         // next unit's barrier, which wave 0 reaches only after reading this one
@@ -266,7 +298,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
           float t = 0.f;
 #pragma unroll
           for (int j = 0; j < KS; ++j) t += rb[j][slot];
-          gemv_store<LPR, EPI>(a, t, u, slot, lane, out_base);
+          gemv_store<LPR, EPI>(a, t, u, slot, lane, out_base, cur);
         }
       }
     }
@@ -365,12 +397,15 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
 
   // first row units' codes, scales and biases in flight before the staging
   RowData<CPL> buf[DEPTH];
+  EpiPre ep[DEPTH];
+  const float* trow = epi_table_row<LPR, EPI>(a);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (u_begin + d < u_end) {
       bool valid;
       const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
       load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0);
+      epi_fetch<LPR, EPI>(ep[d], u_begin + d, slot, a, trow);
     }
   }
 
@@ -420,12 +455,14 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
       const int64_t u = u0 + d;
       if (u < u_end) {
         const float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        const EpiPre cur = ep[d];
         if (u + DEPTH < u_end) {
           bool valid;
           const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
           load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0);
+          epi_fetch<LPR, EPI>(ep[d], u + DEPTH, slot, a, trow);
         }
-        gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base);
+        gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base, cur);
       }
     }
   }

@@ -57,15 +57,12 @@ __device__ __forceinline__ RopePair rope_pair(uint32_t p, const RopeArgs& g) {
   return r;
 }
 
-// Rotates the pair's values (va at dim da, vb at dim db) of token m and stores both into
-// their head of q/k/v/gate.  (a, b) -> (a c - b s, b c + a s) in fp32.
-__device__ __forceinline__ void rope_store(const RopeArgs& g, void* q, void* k, void* v, const RopePair& r,
-                                           int64_t m, float va, float vb, bool f32) {
+// Rotates the pair's values (va at dim da, vb at dim db) of token m by (c, s), if the pair
+// rotates, and stores both into their head of q/k/v/gate.  (a, b) -> (a c - b s, b c + a s)
+// in fp32.
+__device__ __forceinline__ void rope_store_cs(const RopeArgs& g, void* q, void* k, void* v, const RopePair& r,
+                                              int64_t m, float va, float vb, float c, float s, bool f32) {
   if (r.ri >= 0) {
-    const int32_t pos = min(max(g.positions[m], 0), g.max_pos - 1);
-    const float* t = g.cos_sin + int64_t(pos) * g.rot;
-    const float c = t[r.ri];
-    const float s = t[(g.rot >> 1) + r.ri];
     const float a = va, b = vb;
     va = fmaf(a, c, -(b * s));
     vb = fmaf(b, c, a * s);
@@ -81,6 +78,19 @@ __device__ __forceinline__ void rope_store(const RopeArgs& g, void* q, void* k, 
   const int64_t base = (m * nh + r.head) * int64_t(g.head_dim);
   store_out(dst, base + r.da, va, f32);
   store_out(dst, base + r.db, vb, f32);
+}
+
+// The same, reading c and s from the table at the token's (clamped) position.
+__device__ __forceinline__ void rope_store(const RopeArgs& g, void* q, void* k, void* v, const RopePair& r,
+                                           int64_t m, float va, float vb, bool f32) {
+  float c = 1.f, s = 0.f;
+  if (r.ri >= 0) {
+    const int32_t pos = min(max(g.positions[m], 0), g.max_pos - 1);
+    const float* t = g.cos_sin + int64_t(pos) * g.rot;
+    c = t[r.ri];
+    s = t[(g.rot >> 1) + r.ri];
+  }
+  rope_store_cs(g, q, k, v, r, m, va, vb, c, s, f32);
 }
 
 }  // namespace qmm

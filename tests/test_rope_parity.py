@@ -131,3 +131,42 @@ def test_rope_full_size_decode_and_sampled_prefill(sh):
     say(f"[rope] {sh.name}: prefill M=2048 (sampled tokens)")
     sample = np.unique(np.r_[0, 2047, np.random.default_rng(5).choice(2048, 10, replace=False)])
     check(sh, synth.CFG_14B, 0, 2048, sample=sample)
+
+
+def _odd_offset(shape):
+    """A bf16 buffer view starting at element 1 of its allocation (2-byte aligned only)."""
+    n = int(np.prod(shape))
+    big = torch.zeros(n + 16, dtype=torch.int16, device="cuda")
+    return big, big[1:1 + n].view(shape)
+
+
+@pytest.mark.parametrize("M", [2, 40])
+def test_outputs_at_odd_element_offsets_match_aligned_ones(M):
+    """Outputs that are only element-aligned (the ABI's promise) get the same bits as aligned
+    ones: the epilogues fall back from vector stores by address, for the rotary QKV and a
+    plain projection, in decode and prefill."""
+    sh = SMALL
+    w, lb = weights(sh, synth.CFG_TEST, 6)
+    x = synth.gen_x(synth.CFG_TEST, 6, 0, M, sh.K)
+    pos = synth.gen_positions(synth.CFG_TEST, 6, M, MAX_POS)
+    tab = synth.gen_rope_table(MAX_POS, sh.rot, sh.base)
+    ref = run(sh, x, w, lb, pos, tab, f32=False)
+    bufs = [_odd_offset((M, n, sh.head_dim)) for n in (sh.n_q, sh.n_kv, sh.n_kv)]
+    q, k, v = (b[1] for b in bufs)
+    qmm.qmm_fused_qkv_rope(dev(x), dev(w.codes), dev(w.scales), dev(w.biases), q, k, v,
+                           dev(np.asarray(pos, np.int32)), dev(tab), sh.rot, lin_bias=dev(lb))
+    torch.cuda.synchronize()
+    say(f"[epilogue] odd-offset outputs, M={M}")
+    for got, want in zip((q, k, v), (ref[0], ref[2], ref[3])):
+        assert np.array_equal(got.cpu().numpy().view(np.uint16), want)
+    for big, _ in bufs:
+        assert int(big[0].item()) == 0 and not torch.any(big[1 + big.numel() - 16:] != 0)
+    # a plain projection
+    lw = synth.gen_weight(synth.CFG_TEST, 7, synth.PROJ_LINEAR, 200, sh.K)
+    ya = Guarded((M, 200), False)
+    qmm.qmm_linear(dev(x), dev(lw.codes), dev(lw.scales), dev(lw.biases), ya.t)
+    big, yo = _odd_offset((M, 200))
+    qmm.qmm_linear(dev(x), dev(lw.codes), dev(lw.scales), dev(lw.biases), yo)
+    torch.cuda.synchronize()
+    assert np.array_equal(yo.cpu().numpy().view(np.uint16), ya.values())
+    assert int(big[0].item()) == 0 and not torch.any(big[1 + M * 200:] != 0)
