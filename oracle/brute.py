@@ -47,6 +47,20 @@ def pack_row(codes_row) -> list:
     return words
 
 
+def pack_row_bits(codes_row, bits: int) -> list:
+    """Pack a row of `bits`-bit codes into uint32 words as one little-endian bit stream:
+    the row is the integer sum of q_k * 2**(bits*k), and word w holds its bits
+    [32w, 32w + 32).  Any width; a code may straddle two words."""
+    v = 0
+    for k, q in enumerate(codes_row):
+        q = int(q)
+        assert 0 <= q < 2 ** bits
+        v += q << (bits * k)
+    n = len(codes_row) * bits // 32
+    assert n * 32 == len(codes_row) * bits
+    return [(v >> (32 * w)) & 0xFFFFFFFF for w in range(n)]
+
+
 def project(x_bits, q, s_bits, b_bits, group: int = 64, lin_bias_bits=None):
     """y[m][n] = sum_k x[m][k] * (s[n][k//group] * q[n][k] + b[n][k//group]) (+ lin_bias[n]).
 

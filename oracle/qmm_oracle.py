@@ -74,30 +74,48 @@ def unpack_u4(codes) -> np.ndarray:
     return q.reshape(*c.shape[:-1], c.shape[-1] * 8).astype(np.int64)
 
 
-def dequant(codes, scales, biases) -> np.ndarray:
-    """W[n, k] = s[n, k // 64] * q[n, k] + b[n, k // 64] in fp64, shape [rows, K]."""
-    q = unpack_u4(codes).astype(np.float64)
+def unpack_bits(codes, bits: int) -> np.ndarray:
+    """uint32 words [..., K*bits/32] -> codes [..., K] (int64) for any code width: the row is
+    one bit stream (bit j of the stream = bit j % 32 of word j // 32) and code k is stream
+    bits [bits*k, bits*k + bits), least-significant bit first, so 3- and 6-bit codes may
+    straddle two words.  The saragossa README lists affine integer weights u2/u3/u4/u6/u8
+    ("Quantization formats"); the pages do not state the packing, and this plain bit
+    stream, which is the 4-bit order of `unpack_u4` at bits = 4, is the reading taken."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype="<u4"))
+    stream = np.unpackbits(c.view(np.uint8), axis=-1, bitorder="little")
+    K = stream.shape[-1] // bits
+    f = stream[..., :K * bits].reshape(*stream.shape[:-1], K, bits).astype(np.int64)
+    return (f << np.arange(bits, dtype=np.int64)).sum(axis=-1)
+
+
+def dequant(codes, scales, biases, bits: int = 4) -> np.ndarray:
+    """W[n, k] = s[n, k // G] * q[n, k] + b[n, k // G] in fp64, shape [rows, K], with the
+    group size G = K / (scales per row) (64 on the workloads; 32 to 128 on the pages:
+    saragossa README, "Capabilities")."""
+    q = (unpack_u4(codes) if bits == 4 else unpack_bits(codes, bits)).astype(np.float64)
     K = q.shape[-1]
     s = bf16_to_f64(scales)
     b = bf16_to_f64(biases)
-    if s.shape[-1] * GROUP != K or b.shape != s.shape:
-        raise ValueError("scales/biases must be [rows, K/64]")
-    s_k = np.repeat(s, GROUP, axis=-1)
-    b_k = np.repeat(b, GROUP, axis=-1)
+    G = K // s.shape[-1]
+    if s.shape[-1] * G != K or b.shape != s.shape:
+        raise ValueError("scales/biases must be [rows, K/G]")
+    s_k = np.repeat(s, G, axis=-1)
+    b_k = np.repeat(b, G, axis=-1)
     return s_k * q + b_k
 
 
 # ---- plain projection --------------------------------------------------------
 
-def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False):
+def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False,
+            bits: int = 4):
     """y[m, n] = sum_k x[m, k] * W[n, k] (+ lin_bias[n]) in fp64, with the magnitude sums
     the tolerance is built from:
       A[m, n] = sum_k |x[m, k]| * |W[n, k]|  (+ |lin_bias[n]|)
-      S[m, n] = sum_k |x[m, k]| * |s[n, k // 64]|   (activation mass weighted by the scale,
+      S[m, n] = sum_k |x[m, k]| * |s[n, k // G]|    (activation mass weighted by the scale,
                                                      i.e. the size of a one-code change)
     and, with bf16_weights, R[m, n] = sum_k |x[m, k]| * |W[n, k] - bf16(W[n, k])| (the
     largest effect of rounding every dequantized weight to bf16, RNE) as a fourth value.
-    x_bits: bf16 bits [M, K] (or [K]); codes [N, K/8]; scales/biases [N, K/64];
+    x_bits: bf16 bits [M, K] (or [K]); codes [N, K*bits/32]; scales/biases [N, K/G];
     lin_bias: optional bf16 bits [N]."""
     x = bf16_to_f64(x_bits)
     squeeze = x.ndim == 1
@@ -105,17 +123,18 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024,
         x = x[None, :]
     N = codes.shape[0]
     K = x.shape[1]
-    if codes.shape[1] * 8 != K:
-        raise ValueError("x width must equal 8 * words per row")
+    if codes.shape[1] * 32 != K * bits:
+        raise ValueError("x width must equal 32/bits * words per row")
+    G = K // scales.shape[1]
     y = np.empty((x.shape[0], N))
     A = np.empty((x.shape[0], N))
     R = np.zeros((x.shape[0], N))
     ax = np.abs(x)
-    xg = ax.reshape(x.shape[0], K // GROUP, GROUP).sum(axis=2)          # [M, K/64]
+    xg = ax.reshape(x.shape[0], K // G, G).sum(axis=2)                  # [M, K/G]
     S = xg @ np.abs(bf16_to_f64(scales)).T
     for r0 in range(0, N, row_block):
         r1 = min(N, r0 + row_block)
-        W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
+        W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1], bits)
         y[:, r0:r1] = x @ W.T
         A[:, r0:r1] = ax @ np.abs(W).T
         if bf16_weights:
@@ -139,25 +158,27 @@ def tolerance(A, S) -> np.ndarray:
     return REL_TOL * np.asarray(A) + EVAL_FLOOR * np.asarray(S)
 
 
-def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False):
+def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False,
+           bits: int = 4):
     """(y, tol) of one projection; tol per `tolerance`.  With bf16_weights (a kernel that
     rounds each dequantized weight to bf16 before multiplying, as the prefill design
     does), tol also carries R = sum |x| |w - bf16(w)|, the bound of that rounding."""
     if bf16_weights:
-        y, A, S, R = project(x_bits, codes, scales, biases, lin_bias, row_block, bf16_weights=True)
+        y, A, S, R = project(x_bits, codes, scales, biases, lin_bias, row_block, bf16_weights=True, bits=bits)
         return y, tolerance(A, S) + R
-    y, A, S = project(x_bits, codes, scales, biases, lin_bias, row_block)
+    y, A, S = project(x_bits, codes, scales, biases, lin_bias, row_block, bits=bits)
     return y, tolerance(A, S)
 
 
 # ---- fused QKV -------------------------------------------------------------
 
-def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=None, bf16_weights: bool = False):
+def fused_qkv(x_bits, codes, scales, biases, q_out: int, kv_out: int, lin_bias=None, bf16_weights: bool = False,
+              bits: int = 4):
     """Rows [0, q_out) -> Q, [q_out, q_out+kv_out) -> K, [q_out+kv_out, q_out+2kv_out) -> V.
     Returns ((q, k, v), (tq, tk, tv)): values and per-element tolerances."""
     if codes.shape[0] != q_out + 2 * kv_out:
         raise ValueError("fused QKV weight must have q_out + 2*kv_out rows")
-    y, t = linear(x_bits, codes, scales, biases, lin_bias, bf16_weights=bf16_weights)
+    y, t = linear(x_bits, codes, scales, biases, lin_bias, bf16_weights=bf16_weights, bits=bits)
     a, b = q_out, q_out + kv_out
     return (y[..., :a], y[..., a:b], y[..., b:]), (t[..., :a], t[..., a:b], t[..., b:])
 
@@ -270,11 +291,11 @@ def swiglu_tol(g, u, tg, tu) -> np.ndarray:
             + SWIGLU_EVAL_REL * (np.abs(h) + SILU_LIPSCHITZ * tg * (np.abs(u) + tu) + np.abs(silu(g)) * tu))
 
 
-def gate_up_swiglu(x_bits, codes, scales, biases, I: int, bf16_weights: bool = False):
+def gate_up_swiglu(x_bits, codes, scales, biases, I: int, bf16_weights: bool = False, bits: int = 4):
     """Rows [0, I) are gate, [I, 2I) are up.  Returns (h, tol_h)."""
     if codes.shape[0] != 2 * I:
         raise ValueError("fused gate+up weight must have 2*I rows")
-    y, t = linear(x_bits, codes, scales, biases, bf16_weights=bf16_weights)
+    y, t = linear(x_bits, codes, scales, biases, bf16_weights=bf16_weights, bits=bits)
     g, u = y[..., :I], y[..., I:]
     tg, tu = t[..., :I], t[..., I:]
     return swiglu(g, u), swiglu_tol(g, u, tg, tu)
@@ -282,7 +303,7 @@ def gate_up_swiglu(x_bits, codes, scales, biases, I: int, bf16_weights: bool = F
 
 # ---- routed experts ------------------------------------------------------------
 
-def moe_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: int):
+def moe_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: int, bits: int = 4):
     """Stage 1: for slot k, expert e = ids[k] in [0, E): h[k] = silu(G_e x) * (U_e x) over
     rows [0, rows/2) (gate) and [rows/2, rows) (up) of grid[e].  An id outside [0, E)
     means no expert: h[k] = 0.  Returns (h [topk, rows/2], tol)."""
@@ -294,13 +315,13 @@ def moe_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: 
     for k, e in enumerate(np.asarray(expert_ids).tolist()):
         if 0 <= e < E:
             hk, tk = gate_up_swiglu(np.asarray(x_bits).reshape(-1), grid_codes[e], grid_scales[e],
-                                    grid_biases[e], I)
+                                    grid_biases[e], I, bits=bits)
             h[k], t[k] = hk, tk
     return h, t
 
 
 def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, expert_w,
-                     h_err=None):
+                     h_err=None, bits: int = 4):
     """Stage 2: y = sum_k p_k * (D_{ids[k]} h_k), k in increasing order; ids outside [0, E)
     contribute nothing.  h_bits: bf16 bits [topk, K] of the stage-1 output fed to both
     sides; p: the fp32 combine weights.  Returns (y, tol).  h_err (optional [topk, K])
@@ -313,11 +334,11 @@ def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, e
     p = np.asarray(expert_w, dtype=np.float32).astype(np.float64)
     for k, e in enumerate(np.asarray(expert_ids).tolist()):
         if 0 <= e < E:
-            yk, tk = linear(np.asarray(h_bits)[k], grid_codes[e], grid_scales[e], grid_biases[e])
+            yk, tk = linear(np.asarray(h_bits)[k], grid_codes[e], grid_scales[e], grid_biases[e], bits=bits)
             y += p[k] * yk
             t += abs(p[k]) * tk
             if h_err is not None:
-                W = dequant(grid_codes[e], grid_scales[e], grid_biases[e])
+                W = dequant(grid_codes[e], grid_scales[e], grid_biases[e], bits)
                 t += abs(p[k]) * (np.abs(W) @ np.asarray(h_err[k], np.float64))
     return y, t
 

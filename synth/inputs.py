@@ -57,9 +57,10 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 @dataclass
 class U4Weight:
     """Packed weight of `rows` output rows over `K` inputs (host arrays)."""
-    codes: np.ndarray   # uint32 [rows, K/8]
-    scales: np.ndarray  # uint16 bf16 bits [rows, K/64]
-    biases: np.ndarray  # uint16 bf16 bits [rows, K/64]
+    codes: np.ndarray   # uint32 [rows, K*bits/32]
+    scales: np.ndarray  # uint16 bf16 bits [rows, K/group]
+    biases: np.ndarray  # uint16 bf16 bits [rows, K/group]
+    bits: int = 4
 
     @property
     def rows(self) -> int:
@@ -67,45 +68,50 @@ class U4Weight:
 
     @property
     def K(self) -> int:
-        return self.codes.shape[1] * CODES_PER_WORD
+        return self.codes.shape[-1] * 32 // self.bits
 
     def slice_rows(self, r0: int, r1: int) -> "U4Weight":
-        return U4Weight(self.codes[r0:r1], self.scales[r0:r1], self.biases[r0:r1])
+        return U4Weight(self.codes[r0:r1], self.scales[r0:r1], self.biases[r0:r1], self.bits)
 
     def take_rows(self, idx) -> "U4Weight":
         idx = np.asarray(idx)
-        return U4Weight(self.codes[idx], self.scales[idx], self.biases[idx])
+        return U4Weight(self.codes[idx], self.scales[idx], self.biases[idx], self.bits)
 
     @staticmethod
     def concat(parts) -> "U4Weight":
         return U4Weight(np.concatenate([p.codes for p in parts]),
                         np.concatenate([p.scales for p in parts]),
-                        np.concatenate([p.biases for p in parts]))
+                        np.concatenate([p.biases for p in parts]), parts[0].bits)
 
     @staticmethod
     def stack(parts) -> "U4Weight":
         return U4Weight(np.stack([p.codes for p in parts]),
                         np.stack([p.scales for p in parts]),
-                        np.stack([p.biases for p in parts]))
+                        np.stack([p.biases for p in parts]), parts[0].bits)
 
 
 def gen_weight(cfg: int, layer: int, proj: int, rows: int, K: int, index: int = 0,
-               scale_lo: float = 0.001, scale_hi: float = 0.01, bias: str = "minus8") -> U4Weight:
-    """Seeded packed weight. bias='minus8' gives bias = -8*scale (the workloads' recipe);
-    bias='uniform' draws an independent bias uniform on [-scale_hi*8, scale_hi*8] (tests only)."""
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 64")
-    codes = rng(cfg, layer, proj, F_CODES, index).integers(0, 2 ** 32, size=(rows, K // 8), dtype=np.uint32)
-    s32 = rng(cfg, layer, proj, F_SCALES, index).uniform(scale_lo, scale_hi, size=(rows, K // GROUP)).astype(np.float32)
+               scale_lo: float = 0.001, scale_hi: float = 0.01, bias: str = "minus8",
+               bits: int = 4, group: int = GROUP) -> U4Weight:
+    """Seeded packed weight: codes uint32 [rows, K*bits/32] (uniform random words, so every
+    code is uniform on 0 .. 2^bits - 1), bf16 scales and biases [rows, K/group].
+    bias='minus8' centres the codes: bias = -2^(bits-1) * scale (-8 * scale at 4 bits, the
+    workloads' recipe); bias='uniform' draws an independent bias uniform on
+    [-scale_hi*8, scale_hi*8] (tests only)."""
+    if K % 64 or K % group:
+        raise ValueError("K must be a multiple of 64 and of the group size")
+    codes = rng(cfg, layer, proj, F_CODES, index).integers(0, 2 ** 32, size=(rows, K * bits // 32),
+                                                          dtype=np.uint32)
+    s32 = rng(cfg, layer, proj, F_SCALES, index).uniform(scale_lo, scale_hi, size=(rows, K // group)).astype(np.float32)
     scales = to_bf16_bits(s32)
     if bias == "minus8":
-        biases = to_bf16_bits(-8.0 * bf16_bits_to_f32(scales))
+        biases = to_bf16_bits(-float(2 ** (bits - 1)) * bf16_bits_to_f32(scales))
     elif bias == "uniform":
-        b = rng(cfg, layer, proj, F_BIASES, index).uniform(-8 * scale_hi, 8 * scale_hi, size=(rows, K // GROUP))
+        b = rng(cfg, layer, proj, F_BIASES, index).uniform(-8 * scale_hi, 8 * scale_hi, size=(rows, K // group))
         biases = to_bf16_bits(b)
     else:
         raise ValueError(bias)
-    return U4Weight(codes, scales, biases)
+    return U4Weight(codes, scales, biases, bits)
 
 
 def gen_x(cfg: int, layer: int, step: int, M: int, K: int, magnitude: str = "normal") -> np.ndarray:
@@ -172,17 +178,17 @@ def gen_positions(cfg: int, layer: int, M: int, max_pos: int, contiguous: bool =
 
 
 def gen_expert_grid(cfg: int, layer: int, proj: int, E: int, rows: int, K: int,
-                    experts=None) -> U4Weight:
+                    experts=None, bits: int = 4, group: int = GROUP) -> U4Weight:
     """3-D expert grid [E, rows, ...]; expert e is seeded by index=e, so any subset of
     experts can be regenerated on its own.  `experts` limits generation to a subset
     (the others are left zero), for oracle-side regeneration."""
-    codes = np.zeros((E, rows, K // 8), np.uint32)
-    scales = np.zeros((E, rows, K // GROUP), np.uint16)
-    biases = np.zeros((E, rows, K // GROUP), np.uint16)
+    codes = np.zeros((E, rows, K * bits // 32), np.uint32)
+    scales = np.zeros((E, rows, K // group), np.uint16)
+    biases = np.zeros((E, rows, K // group), np.uint16)
     for e in (range(E) if experts is None else experts):
-        w = gen_weight(cfg, layer, proj, rows, K, index=int(e))
+        w = gen_weight(cfg, layer, proj, rows, K, index=int(e), bits=bits, group=group)
         codes[e], scales[e], biases[e] = w.codes, w.scales, w.biases
-    return U4Weight(codes, scales, biases)
+    return U4Weight(codes, scales, biases, bits)
 
 
 # ---- workload shapes -------------------------------------------------------

@@ -102,6 +102,69 @@ def test_storage_matches_the_printed_bits_per_weight():
     assert W.shape == (rows, K)
 
 
+@pytest.mark.parametrize("fmt", ["u8", "u6", "u4", "u3"])
+def test_storage_of_other_widths_matches_the_printed_bits_per_weight(fmt):
+    fig = json.load(open(os.path.join(GOLDEN, "format_figures.json")))["bits_per_weight"]
+    bits = int(fmt[1:])
+    rows, K = 8, 4096
+    w = synth.gen_weight(synth.CFG_TEST, 0, 0, rows, K, bits=bits, group=fig["group_size"])
+    assert 8 * (w.codes.nbytes + w.scales.nbytes + w.biases.nbytes) / (rows * K) == fig[fmt]
+    assert orc.dequant(w.codes, w.scales, w.biases, bits).shape == (rows, K)
+
+
+def test_group_sizes_span_the_printed_range():
+    fig = json.load(open(os.path.join(GOLDEN, "format_figures.json")))["group_sizes"]
+    for G in (fig["min"], 64, fig["max"]):
+        w = synth.gen_weight(synth.CFG_TEST, 0, 0, 4, 256, group=G)
+        assert w.scales.shape == (4, 256 // G)
+        W = orc.dequant(w.codes, w.scales, w.biases)
+        q = orc.unpack_u4(w.codes)
+        s = orc.bf16_to_f64(w.scales)
+        b = orc.bf16_to_f64(w.biases)
+        # input k uses the scale and bias of group k // G
+        for k in (0, G - 1, G, 255):
+            assert np.array_equal(W[:, k], s[:, k // G] * q[:, k] + b[:, k // G])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+def test_bit_stream_unpack_inverts_the_pure_python_packer(bits):
+    rng = np.random.default_rng(bits)
+    q = rng.integers(0, 2 ** bits, size=(3, 128))
+    words = np.array([brute.pack_row_bits(r, bits) for r in q], np.uint32)
+    assert words.shape == (3, 128 * bits // 32)
+    assert np.array_equal(orc.unpack_bits(words, bits), q)
+
+
+def test_bit_stream_order_by_hand():
+    """Hand-made words: 3-bit code 10 (stream bits 30..32) straddles words 0 and 1; 6-bit
+    code 5 (bits 30..35) straddles too; at 4 bits the stream order is the nibble order."""
+    q = [0] * 32
+    q[10] = 5                                     # 0b101: bits 30 and 32
+    assert brute.pack_row_bits(q, 3) == [0x40000000, 0x00000001, 0]
+    assert orc.unpack_bits(np.array([[0x40000000, 0x00000001, 0]], np.uint32), 3).tolist() == [q]
+    q6 = [0] * 16
+    q6[5] = 0b110011                              # bits 30, 31 in word 0; 34, 35 in word 1
+    assert orc.unpack_bits(np.array([[0xC0000000, 0x0000000C, 0]], np.uint32), 6).tolist() == [q6]
+    rng_words = np.random.default_rng(3).integers(0, 2 ** 32, size=(4, 16), dtype=np.uint32)
+    assert np.array_equal(orc.unpack_bits(rng_words, 4), orc.unpack_u4(rng_words))
+    assert orc.unpack_bits(np.array([[0x04030201]], np.uint32), 8).tolist() == [[1, 2, 3, 4]]
+
+
+@pytest.mark.parametrize("bits,G", [(2, 64), (3, 32), (6, 128), (8, 64), (4, 32), (4, 128)])
+def test_oracle_matches_brute_force_other_formats(bits, G):
+    M, K, N = 2, 256, 5
+    rng = np.random.default_rng(10 * bits + G)
+    q = rng.integers(0, 2 ** bits, size=(N, K))
+    words = np.array([brute.pack_row_bits(r, bits) for r in q], np.uint32)
+    s = _rand_bf16_bits(rng, (N, K // G), -10, -4)
+    b = _rand_bf16_bits(rng, (N, K // G), -8, -2)
+    x = _rand_bf16_bits(rng, (M, K), -3, 2)
+    y, A, S = orc.project(x, words, s, b, bits=bits)
+    yb, Ab = brute.project(x.tolist(), q.tolist(), s.tolist(), b.tolist(), group=G)
+    assert np.allclose(y, np.array(yb), rtol=0, atol=1e-12 * np.array(Ab).max())
+    assert np.allclose(A, np.array(Ab), rtol=1e-12)
+
+
 def test_fused_weight_shape_follows_the_printed_formula():
     fig = json.load(open(os.path.join(GOLDEN, "format_figures.json")))
     ex = fig["fused_qkv_weight_shape"]["example"]
