@@ -13,7 +13,8 @@ import ctypes
 import os
 
 __all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm_fused_gate_up_swiglu",
-           "qmm_moe_gather",
+           "qmm_moe_gather", "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
+           "qmm_moe_gather_fmt",
            "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
            "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
 
@@ -40,6 +41,10 @@ _SIGNATURES = {
     "qmm_moe_route": [_P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "qmm_moe_prefill": [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_size_t, _P,
                         _INT, _P],
+    "qmm_linear_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P],
+    "qmm_fused_qkv_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _INT, _P],
+    "qmm_fused_gate_up_swiglu_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _P, _INT, _P],
+    "qmm_moe_gather_fmt": [_INT, _I64, _INT, _P, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
     "qmm_status_str": [_INT],
     "qmm_abi_version": [],
 }
@@ -129,13 +134,14 @@ def _bytes(t) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def _check_weight(codes, scales, biases, rows: int, K: int, what: str = "weight"):
-    """The tensors must hold exactly rows x K/8 words and rows x K/64 bf16 scales/biases,
-    so the kernels never read past the end of a caller's buffer."""
-    _need(K % 64 == 0 and K > 0, f"K={K} must be a positive multiple of 64")
-    _need(_bytes(codes) == rows * K // 2, f"{what} codes must hold {rows} x {K // 8} uint32")
-    _need(_bytes(scales) == rows * (K // 64) * 2, f"{what} scales must hold {rows} x {K // 64} bf16")
-    _need(_bytes(biases) == rows * (K // 64) * 2, f"{what} biases must hold {rows} x {K // 64} bf16")
+def _check_weight(codes, scales, biases, rows: int, K: int, what: str = "weight", bits: int = 4, group: int = 64):
+    """The tensors must hold exactly rows x K*bits/32 words and rows x K/group bf16
+    scales/biases, so the kernels never read past the end of a caller's buffer."""
+    _need(K % 64 == 0 and K > 0 and K % group == 0, f"K={K} must be a positive multiple of 64 and of {group}")
+    words = K * bits // 32
+    _need(_bytes(codes) == rows * words * 4, f"{what} codes must hold {rows} x {words} uint32")
+    _need(_bytes(scales) == rows * (K // group) * 2, f"{what} scales must hold {rows} x {K // group} bf16")
+    _need(_bytes(biases) == rows * (K // group) * 2, f"{what} biases must hold {rows} x {K // group} bf16")
 
 
 def qmm_linear(x, codes, scales, biases, y, lin_bias=None, stream=None) -> None:
@@ -266,3 +272,66 @@ def qmm_moe_prefill(stage, inp, codes, scales, biases, expert_ids, workspace, ou
                                           _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"), topk,
                                           _ptr(workspace, "workspace"), _bytes(workspace), _ptr(out, "out"),
                                           _out_dtype(out), _stream(stream)), "qmm_moe_prefill")
+
+
+# ---- other formats of the affine family (code width `bits`, group size `group`) ----------
+
+def qmm_linear_fmt(bits: int, group: int, x, codes, scales, biases, y, lin_bias=None, stream=None) -> None:
+    """qmm_linear for codes of `bits` bits (one bit stream per row) and `group`-wide groups."""
+    M, K = _mk(x)
+    N = codes.shape[0]
+    _check_weight(codes, scales, biases, N, K, bits=bits, group=group)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(_elems(y) == M * N, "y must have M x N elements")
+    _need(lin_bias is None or _bytes(lin_bias) == N * 2, "lin_bias must be bf16 [N]")
+    _check(load_library().qmm_linear_fmt(int(bits), int(group), _ptr(x, "x"), M, K, _ptr(codes, "codes"),
+                                         _ptr(scales, "scales"), _ptr(biases, "biases"), N,
+                                         _ptr(lin_bias, "lin_bias"), _ptr(y, "y"), _out_dtype(y), _stream(stream)),
+           "qmm_linear_fmt")
+
+
+def qmm_fused_qkv_fmt(bits: int, group: int, x, codes, scales, biases, q, k, v, lin_bias=None, stream=None) -> None:
+    M, K = _mk(x)
+    q_out, kv_out = q.shape[-1], k.shape[-1]
+    rows = q_out + 2 * kv_out
+    _check_weight(codes, scales, biases, rows, K, bits=bits, group=group)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(_elems(q) == M * q_out and _elems(k) == M * kv_out and _elems(v) == M * kv_out, "q/k/v sizes")
+    _need(lin_bias is None or _bytes(lin_bias) == rows * 2, "lin_bias must be bf16 [rows]")
+    _check(load_library().qmm_fused_qkv_fmt(int(bits), int(group), _ptr(x, "x"), M, K, _ptr(codes, "codes"),
+                                            _ptr(scales, "scales"), _ptr(biases, "biases"), q_out, kv_out,
+                                            _ptr(lin_bias, "lin_bias"), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"),
+                                            _out_dtype(q), _stream(stream)), "qmm_fused_qkv_fmt")
+
+
+def qmm_fused_gate_up_swiglu_fmt(bits: int, group: int, x, codes, scales, biases, h, stream=None) -> None:
+    M, K = _mk(x)
+    I = h.shape[-1]
+    _check_weight(codes, scales, biases, 2 * I, K, bits=bits, group=group)
+    _need(_bytes(x) == M * K * 2, "x must be bf16 [M, K]")
+    _need(_elems(h) == M * I, "h must have M x I elements")
+    _check(load_library().qmm_fused_gate_up_swiglu_fmt(int(bits), int(group), _ptr(x, "x"), M, K,
+                                                       _ptr(codes, "codes"), _ptr(scales, "scales"),
+                                                       _ptr(biases, "biases"), I, _ptr(h, "h"), _out_dtype(h),
+                                                       _stream(stream)), "qmm_fused_gate_up_swiglu_fmt")
+
+
+def qmm_moe_gather_fmt(bits: int, group: int, stage, inp, codes, scales, biases, expert_ids, out, expert_w=None,
+                       stream=None) -> None:
+    E, rows = codes.shape[0], codes.shape[1]
+    K = inp.shape[-1]
+    topk = expert_ids.shape[0]
+    _check_weight(codes, scales, biases, E * rows, K, "expert grid", bits=bits, group=group)
+    _need(expert_ids.numel() == topk and expert_ids.element_size() == 4, "expert_ids must be int32 [topk]")
+    if int(stage) == QMM_MOE_GATE_UP_SWIGLU:
+        _need(_bytes(inp) == K * 2, "x must be bf16 [K]")
+        _need(_elems(out) == topk * (rows // 2), "out must be [topk, rows/2]")
+    else:
+        _need(_bytes(inp) == topk * K * 2, "h must be bf16 [topk, K]")
+        _need(_elems(out) == rows, "out must be [rows]")
+        _need(expert_w is not None and _bytes(expert_w) == topk * 4, "expert_w must be fp32 [topk]")
+    _check(load_library().qmm_moe_gather_fmt(int(bits), int(group), int(stage), _ptr(inp, "in"), K,
+                                             _ptr(codes, "codes"), _ptr(scales, "scales"), _ptr(biases, "biases"),
+                                             E, rows, _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"),
+                                             topk, _ptr(out, "out"), _out_dtype(out), _stream(stream)),
+           "qmm_moe_gather_fmt")

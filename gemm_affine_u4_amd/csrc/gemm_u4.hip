@@ -120,8 +120,8 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     rows_here = min(kBM, a.moe_offsets[e + 1] - pair_base);
     const int64_t er = int64_t(e) * a.N;  // first row of the expert in the grid
     a.codes += er * (a.K >> 3);
-    a.scales += er * (a.K >> 6);
-    a.biases += er * (a.K >> 6);
+    a.scales += er * (a.K >> (5 + a.gshift));
+    a.biases += er * (a.K >> (5 + a.gshift));
   }
   // source row of tile row r (a row past the tile's end reads its last row; never stored)
   auto x_row = [&](int r) -> int64_t {
@@ -138,8 +138,8 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const uint32_t K = uint32_t(a.K);
-  const uint32_t groups = K >> 6;
-  const int ksteps = int(groups);
+  const int ksteps = int(K >> 6);
+  const uint32_t groups = K >> (5 + a.gshift);  // scale/bias groups per row (group 32 << gshift)
 
   // ---- x tile: global -> LDS ----------------------------------------------------------
   // Instruction j (0..7) of wave w fills LDS rows 64 w + 8 j + L / 8, slot L % 8 (lane L
@@ -187,10 +187,12 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     uint16_t sv, bv;
   };
   StepRegs R[3];
+  // the lane's 32 codes of step ks are inputs 64 ks + 32 wh .. +31: group (2 ks + wh) >> gshift
   auto load_w = [&](StepRegs& r, int ks) {
+    const uint32_t go = goff + ((uint32_t(2 * ks + wh) >> a.gshift) << 1);
     r.cv = __builtin_amdgcn_raw_buffer_load_b128(cr, coff + uint32_t(ks) * 32u, 0, 0);
-    r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, goff + uint32_t(ks) * 2u, 0, 0);
-    r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, goff + uint32_t(ks) * 2u, 0, 0);
+    r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, go, 0, 0);
+    r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, go, 0, 0);
   };
   constexpr int kStepLoads = 4 + 1 + 2;  // vector-memory loads one step requests per lane
   // Piece p (0..3): code word p of the half row (8 codes -> w = s*q + b in fp32 -> bf16,

@@ -64,20 +64,21 @@ struct RowData {
   uint16_t s[CPL], b[CPL];
 };
 
-// Chunk c0 + LPR*i of row `row`: codes at byte row*K/2 + 16*c, scale/bias at
-// 2*(row*K/64 + c/2); consecutive chunks of a lane are LPR*16 (codes) and LPR (groups)
-// bytes apart, which the loads carry as immediate offsets.
+// Chunk c0 + LPR*i of row `row`: codes at byte row*K/2 + 16*c, scale/bias of group
+// c >> gshift (group size 32 << gshift) at 2*(row*K/G + (c >> gshift)); consecutive
+// chunks of a lane are LPR*16 (codes) and 2*(LPR >> gshift) (groups) bytes apart.
 template <int LPR, int CPL>
 __device__ __forceinline__ void load_row(RowData<CPL>& r, __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr,
                                          __amdgpu_buffer_rsrc_t br, uint32_t row, uint32_t row_bytes,
-                                         uint32_t row_groups, uint32_t c0) {
+                                         uint32_t row_groups, uint32_t c0, int gshift) {
   const uint32_t co = row * row_bytes + c0 * 16u;
-  const uint32_t go = (row * row_groups + (c0 >> 1)) * 2u;
+  const uint32_t go = (row * row_groups + (c0 >> gshift)) * 2u;
+  const uint32_t gstep = uint32_t(LPR >> gshift) * 2u;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(cr, co + uint32_t(i * LPR * 16), 0, kLoadNT);
-    r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, go + uint32_t(i * LPR), 0, 0);
-    r.b[i] = __builtin_amdgcn_raw_buffer_load_b16(br, go + uint32_t(i * LPR), 0, 0);
+    r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, go + uint32_t(i) * gstep, 0, 0);
+    r.b[i] = __builtin_amdgcn_raw_buffer_load_b16(br, go + uint32_t(i) * gstep, 0, 0);
   }
 }
 
@@ -211,7 +212,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
   const int slot = lane / LPR;
   const int li = lane % LPR;
   const int64_t words = a.K >> 3;
-  const int64_t groups = a.K >> 6;
+  const int64_t groups = a.K >> (5 + a.gshift);
   const int64_t gi = blockIdx.x;
   const int64_t u_begin = gi * per_group + (gi < extra ? gi : extra);
   const int64_t u_end = u_begin + per_group + (gi < extra ? 1 : 0);
@@ -270,7 +271,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
     if (u_begin + d < u_end) {
       bool valid;
       const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
-      load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
+      load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
       epi_fetch<LPR, EPI>(ep[d], u_begin + d, slot, a, trow);
     }
   }
@@ -286,7 +287,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
         if (u + DEPTH < u_end) {
           bool valid;
           const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
-          load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0);
+          load_row<LPR, CPL>(buf[d], cr, sr, br, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
           epi_fetch<LPR, EPI>(ep[d], u + DEPTH, slot, a, trow);
         }
         // double-buffered by unit parity: the next write to this buffer comes after the
@@ -349,7 +350,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   const int slot = lane / LPR;
   const int li = lane % LPR;
   const int64_t words = a.K >> 3;
-  const int64_t groups = a.K >> 6;
+  const int64_t groups = a.K >> (5 + a.gshift);
   // the units are spread evenly over the waves: every wave takes `per_wave` consecutive
   // units and the first `extra` waves one more
   const int64_t gw = int64_t(blockIdx.x) * kWavesS1 + wave;
@@ -404,7 +405,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
     if (u_begin + d < u_end) {
       bool valid;
       const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
-      load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0);
+      load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
       epi_fetch<LPR, EPI>(ep[d], u_begin + d, slot, a, trow);
     }
   }
@@ -459,7 +460,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
         if (u + DEPTH < u_end) {
           bool valid;
           const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
-          load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0);
+          load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
           epi_fetch<LPR, EPI>(ep[d], u + DEPTH, slot, a, trow);
         }
         gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base, cur);
@@ -490,7 +491,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units
   const int64_t u_begin = int64_t(blockIdx.x) * upw;
   const int nu = int(u_begin + upw < units ? upw : units - u_begin);
   const uint32_t row_bytes = uint32_t(a.K >> 1);
-  const uint32_t row_groups = uint32_t(a.K >> 6);
+  const uint32_t row_groups = uint32_t(a.K >> (5 + a.gshift));
   const uint64_t expert_words = uint64_t(a.rows) * uint64_t(a.K >> 3);
   const uint64_t expert_groups = uint64_t(a.rows) * row_groups;
   const uint32_t c0 = uint32_t(li);
@@ -508,13 +509,13 @@ __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units
     const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases + uint64_t(e) * expert_groups, expert_groups * 2);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + int64_t(k) * a.K, uint64_t(a.K) * 2);
     RowData<CPL> cur, nxt;
-    load_row<LPR, CPL>(cur, cr, sr, br, uint32_t(u_begin * RPI + slot), row_bytes, row_groups, c0);
+    load_row<LPR, CPL>(cur, cr, sr, br, uint32_t(u_begin * RPI + slot), row_bytes, row_groups, c0, a.gshift);
     uint32_t xp[CPL][16];
     float xs[CPL];
     load_x_chunks<LPR, CPL>(xr, c0, xp, xs);
     for (int u = 0; u < nu; ++u) {
       if (u + 1 < nu)
-        load_row<LPR, CPL>(nxt, cr, sr, br, uint32_t((u_begin + u + 1) * RPI + slot), row_bytes, row_groups, c0);
+        load_row<LPR, CPL>(nxt, cr, sr, br, uint32_t((u_begin + u + 1) * RPI + slot), row_bytes, row_groups, c0, a.gshift);
       const float v = slot_reduce<LPR>(row_partial<CPL>(cur, xp, xs, magic));
       if (result_lane) red[wave][u][slot] = fmaf(p, v, red[wave][u][slot]);
       cur = nxt;

@@ -13,18 +13,39 @@ static_assert(QMM_MAX_EXPERTS_PREFILL == qmm::kMaxExpertsPrefill, "routing histo
 
 namespace {
 
-uint64_t u4_code_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K) / 2; }
-uint64_t u4_group_bytes(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K / 64) * 2; }
-
 bool out_dtype_ok(int d) { return d == QMM_OUT_BF16 || d == QMM_OUT_F32; }
 
-// The kernels address one weight matrix (one expert of a grid) and the activations with
-// 32-bit byte offsets.
-bool matrix_fits(int64_t rows, int64_t K) { return uint64_t(rows) * uint64_t(K) / 2 <= 0xFFFFFFFFull; }
+// The kernels address the activations with 32-bit byte offsets.
 bool acts_fit(int64_t M, int64_t K) { return uint64_t(M) * uint64_t(K) * 2 <= 0xFFFFFFFFull; }
 
 // Activation rows up to which the decode GEMV runs (once per row); above, the GEMM.
 constexpr int64_t kGemvMaxM = 8;
+
+// A format of the affine family: code width and group size (the pages list u2 .. u8 at
+// group sizes 32 to 128: saragossa README, "Capabilities" and "Quantization formats").
+struct Fmt {
+  int bits;
+  int gshift;      // group = 32 << gshift
+  int64_t group;
+};
+// The widths the kernels implement; false for others, for other group sizes, and when K
+// is not a whole number of groups.
+bool fmt_ok(int bits, int64_t group, int64_t K, Fmt* f) {
+  if (bits != 4) return false;
+  int gs;
+  if (group == 32) gs = 0;
+  else if (group == 64) gs = 1;
+  else if (group == 128) gs = 2;
+  else return false;
+  if (K % group) return false;
+  *f = {bits, gs, group};
+  return true;
+}
+constexpr Fmt kU4G64 = {4, 1, 64};
+uint64_t code_bytes(int64_t rows, int64_t K, const Fmt& f) { return uint64_t(rows) * uint64_t(K) * f.bits / 8; }
+uint64_t group_bytes(int64_t rows, int64_t K, const Fmt& f) { return uint64_t(rows) * uint64_t(K / f.group) * 2; }
+// One weight matrix (one expert of a grid) is addressed with 32-bit byte offsets.
+bool codes_fit(int64_t rows, int64_t K, const Fmt& f) { return code_bytes(rows, K, f) <= 0xFFFFFFFFull; }
 
 qmm::GemmArgs gemm_args(const qmm::GemvArgs& g, int64_t M, int64_t N) {
   qmm::GemmArgs a = {};
@@ -43,6 +64,7 @@ qmm::GemmArgs gemm_args(const qmm::GemvArgs& g, int64_t M, int64_t N) {
   a.kv_out = g.kv_out;
   a.I = g.I;
   a.f32_out = g.f32_out;
+  a.gshift = g.gshift;
   a.rope = g.rope;
   return a;
 }
@@ -74,19 +96,22 @@ const char* qmm_status_str(int status) {
   }
 }
 
-int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
-               const uint16_t* biases, int64_t N, const uint16_t* lin_bias, void* y, int out_dtype,
-               hipStream_t stream) {
+int qmm_linear_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes,
+                   const uint16_t* scales, const uint16_t* biases, int64_t N, const uint16_t* lin_bias, void* y,
+                   int out_dtype, hipStream_t stream) {
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!y) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
-  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(N, K) || !acts_fit(M, K)) return QMM_ERR_SHAPE;
+  Fmt f;
+  if (M < 1 || N < 1 || !qmm::k_ok(K) || M > 65535 || !fmt_ok(bits, group_size, K, &f) || !codes_fit(N, K, f) ||
+      !acts_fit(M, K))
+    return QMM_ERR_SHAPE;
   if (!qmm::aligned(y, out_elem(out_dtype)) || (lin_bias && !qmm::aligned(lin_bias, 2))) return QMM_ERR_ALIGN;
   const Range outs[] = {{y, uint64_t(M * N) * out_elem(out_dtype)}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
-                       {codes, u4_code_bytes(N, K)},
-                       {scales, u4_group_bytes(N, K)},
-                       {biases, u4_group_bytes(N, K)},
+                       {codes, code_bytes(N, K, f)},
+                       {scales, group_bytes(N, K, f)},
+                       {biases, group_bytes(N, K, f)},
                        {lin_bias, lin_bias ? uint64_t(N) * 2 : 0}};
   if (qmm::any_alias(outs, 1, ins, 5)) return QMM_ERR_ALIAS;
 
@@ -101,27 +126,37 @@ int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, c
   a.rows = N;
   a.n_out = N;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.gshift = f.gshift;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_LINEAR, gemm_args(a, M, N), stream);
   return qmm::launch_gemv(qmm::EPI_LINEAR, a, M, stream);
 }
 
-int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
-                  const uint16_t* biases, int64_t q_out, int64_t kv_out, const uint16_t* lin_bias, void* q, void* k,
-                  void* v, int out_dtype, hipStream_t stream) {
+int qmm_linear(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
+               const uint16_t* biases, int64_t N, const uint16_t* lin_bias, void* y, int out_dtype,
+               hipStream_t stream) {
+  return qmm_linear_fmt(kU4G64.bits, kU4G64.group, x, M, K, codes, scales, biases, N, lin_bias, y, out_dtype,
+                        stream);
+}
+
+int qmm_fused_qkv_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes,
+                      const uint16_t* scales, const uint16_t* biases, int64_t q_out, int64_t kv_out,
+                      const uint16_t* lin_bias, void* q, void* k, void* v, int out_dtype, hipStream_t stream) {
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!q || !k || !v) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
   const int64_t rows = q_out + 2 * kv_out;
-  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(rows, K) || !acts_fit(M, K))
+  Fmt f;
+  if (M < 1 || q_out < 1 || kv_out < 1 || !qmm::k_ok(K) || M > 65535 || !fmt_ok(bits, group_size, K, &f) ||
+      !codes_fit(rows, K, f) || !acts_fit(M, K))
     return QMM_ERR_SHAPE;
   const size_t e = out_elem(out_dtype);
   if (!qmm::aligned(q, e) || !qmm::aligned(k, e) || !qmm::aligned(v, e) || (lin_bias && !qmm::aligned(lin_bias, 2)))
     return QMM_ERR_ALIGN;
   const Range outs[] = {{q, uint64_t(M * q_out) * e}, {k, uint64_t(M * kv_out) * e}, {v, uint64_t(M * kv_out) * e}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
-                       {codes, u4_code_bytes(rows, K)},
-                       {scales, u4_group_bytes(rows, K)},
-                       {biases, u4_group_bytes(rows, K)},
+                       {codes, code_bytes(rows, K, f)},
+                       {scales, group_bytes(rows, K, f)},
+                       {biases, group_bytes(rows, K, f)},
                        {lin_bias, lin_bias ? uint64_t(rows) * 2 : 0}};
   if (qmm::any_alias(outs, 3, ins, 5)) return QMM_ERR_ALIAS;
 
@@ -139,8 +174,16 @@ int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes
   a.q_out = q_out;
   a.kv_out = kv_out;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.gshift = f.gshift;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_QKV, gemm_args(a, M, rows), stream);
   return qmm::launch_gemv(qmm::EPI_QKV, a, M, stream);
+}
+
+int qmm_fused_qkv(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
+                  const uint16_t* biases, int64_t q_out, int64_t kv_out, const uint16_t* lin_bias, void* q, void* k,
+                  void* v, int out_dtype, hipStream_t stream) {
+  return qmm_fused_qkv_fmt(kU4G64.bits, kU4G64.group, x, M, K, codes, scales, biases, q_out, kv_out, lin_bias, q, k,
+                           v, out_dtype, stream);
 }
 
 int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes, const uint16_t* scales,
@@ -157,7 +200,7 @@ int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
       rot_dim < 2 || rot_dim % 2 || rot_dim > head_dim || max_pos < 1 || max_pos > (int64_t(1) << 31) - 1)
     return QMM_ERR_SHAPE;
   const int64_t rows = (n_q_heads * (1 + q_gate) + 2 * n_kv_heads) * head_dim;
-  if (rows > (int64_t(1) << 30) || !matrix_fits(rows, K) || !acts_fit(M, K) ||
+  if (rows > (int64_t(1) << 30) || !codes_fit(rows, K, kU4G64) || !acts_fit(M, K) ||
       uint64_t(max_pos) * uint64_t(rot_dim) > (uint64_t(1) << 40))
     return QMM_ERR_SHAPE;
   const size_t e = out_elem(out_dtype);
@@ -167,9 +210,9 @@ int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   const uint64_t qn = uint64_t(M * n_q_heads * head_dim) * e, kvn = uint64_t(M * n_kv_heads * head_dim) * e;
   const Range outs[] = {{q, qn}, {k, kvn}, {v, kvn}, {q_gate ? gate : nullptr, q_gate ? qn : 0}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
-                       {codes, u4_code_bytes(rows, K)},
-                       {scales, u4_group_bytes(rows, K)},
-                       {biases, u4_group_bytes(rows, K)},
+                       {codes, code_bytes(rows, K, kU4G64)},
+                       {scales, group_bytes(rows, K, kU4G64)},
+                       {biases, group_bytes(rows, K, kU4G64)},
                        {lin_bias, lin_bias ? uint64_t(rows) * 2 : 0},
                        {positions, uint64_t(M) * 4},
                        {cos_sin, uint64_t(max_pos) * uint64_t(rot_dim) * 4}};
@@ -187,6 +230,7 @@ int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   a.K = K;
   a.rows = rows;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.gshift = kU4G64.gshift;
   a.rope.positions = positions;
   a.rope.cos_sin = cos_sin;
   a.rope.gate = q_gate ? gate : nullptr;
@@ -200,20 +244,22 @@ int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   return qmm::launch_gemv(qmm::EPI_ROPE, a, M, stream);
 }
 
-int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes,
-                             const uint16_t* scales, const uint16_t* biases, int64_t I, void* h, int out_dtype,
-                             hipStream_t stream) {
+int qmm_fused_gate_up_swiglu_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K,
+                                 const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t I,
+                                 void* h, int out_dtype, hipStream_t stream) {
   if (int st = check_weight(x, codes, scales, biases)) return st;
   if (!h) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
-  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || !matrix_fits(2 * I, K) || !acts_fit(M, K))
+  Fmt f;
+  if (M < 1 || I < 1 || !qmm::k_ok(K) || M > 65535 || !fmt_ok(bits, group_size, K, &f) || !codes_fit(2 * I, K, f) ||
+      !acts_fit(M, K))
     return QMM_ERR_SHAPE;
   if (!qmm::aligned(h, out_elem(out_dtype))) return QMM_ERR_ALIGN;
   const Range outs[] = {{h, uint64_t(M * I) * out_elem(out_dtype)}};
   const Range ins[] = {{x, uint64_t(M * K) * 2},
-                       {codes, u4_code_bytes(2 * I, K)},
-                       {scales, u4_group_bytes(2 * I, K)},
-                       {biases, u4_group_bytes(2 * I, K)}};
+                       {codes, code_bytes(2 * I, K, f)},
+                       {scales, group_bytes(2 * I, K, f)},
+                       {biases, group_bytes(2 * I, K, f)}};
   if (qmm::any_alias(outs, 1, ins, 4)) return QMM_ERR_ALIAS;
 
   qmm::GemvArgs a = {};
@@ -227,19 +273,29 @@ int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint
   a.I = I;
   a.n_out = I;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.gshift = f.gshift;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_SWIGLU, gemm_args(a, M, 2 * I), stream);
   return qmm::launch_gemv(qmm::EPI_SWIGLU, a, M, stream);
 }
 
-int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* codes, const uint16_t* scales,
-                   const uint16_t* biases, int64_t E, int64_t rows, const int32_t* expert_ids,
-                   const float* expert_w, int64_t topk, void* out, int out_dtype, hipStream_t stream) {
+int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K, const uint32_t* codes,
+                             const uint16_t* scales, const uint16_t* biases, int64_t I, void* h, int out_dtype,
+                             hipStream_t stream) {
+  return qmm_fused_gate_up_swiglu_fmt(kU4G64.bits, kU4G64.group, x, M, K, codes, scales, biases, I, h, out_dtype,
+                                      stream);
+}
+
+int qmm_moe_gather_fmt(int bits, int64_t group_size, int stage, const uint16_t* in, int64_t K,
+                       const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t E, int64_t rows,
+                       const int32_t* expert_ids, const float* expert_w, int64_t topk, void* out, int out_dtype,
+                       hipStream_t stream) {
   if (stage != QMM_MOE_GATE_UP_SWIGLU && stage != QMM_MOE_DOWN_COMBINE) return QMM_ERR_ENUM;
   if (int st = check_weight(in, codes, scales, biases)) return st;
   if (!expert_ids || !out || (stage == QMM_MOE_DOWN_COMBINE && !expert_w)) return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  Fmt f;
   if (!qmm::k_ok(K) || E < 1 || rows < 1 || topk < 1 || topk > QMM_MAX_TOPK || E > (int64_t(1) << 24) ||
-      !matrix_fits(rows, K))
+      !fmt_ok(bits, group_size, K, &f) || !codes_fit(rows, K, f))
     return QMM_ERR_SHAPE;
   if (stage == QMM_MOE_GATE_UP_SWIGLU && rows % 2) return QMM_ERR_SHAPE;
   if (stage == QMM_MOE_DOWN_COMBINE && K > 5120) return QMM_ERR_SHAPE;
@@ -250,9 +306,9 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* cod
   const int64_t out_elems = stage == QMM_MOE_GATE_UP_SWIGLU ? topk * (rows / 2) : rows;
   const Range outs[] = {{out, uint64_t(out_elems) * e}};
   const Range ins[] = {{in, uint64_t(in_elems) * 2},
-                       {codes, u4_code_bytes(E * rows, K)},
-                       {scales, u4_group_bytes(E * rows, K)},
-                       {biases, u4_group_bytes(E * rows, K)},
+                       {codes, code_bytes(E * rows, K, f)},
+                       {scales, group_bytes(E * rows, K, f)},
+                       {biases, group_bytes(E * rows, K, f)},
                        {expert_ids, uint64_t(topk) * 4},
                        {expert_w, expert_w ? uint64_t(topk) * 4 : 0}};
   if (qmm::any_alias(outs, 1, ins, 6)) return QMM_ERR_ALIAS;
@@ -271,8 +327,16 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* cod
   a.E = E;
   a.topk = int(topk);
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.gshift = f.gshift;
   if (stage == QMM_MOE_GATE_UP_SWIGLU) return qmm::launch_moe_gate_up(a, stream);
   return qmm::launch_moe_down(a, stream);
+}
+
+int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* codes, const uint16_t* scales,
+                   const uint16_t* biases, int64_t E, int64_t rows, const int32_t* expert_ids,
+                   const float* expert_w, int64_t topk, void* out, int out_dtype, hipStream_t stream) {
+  return qmm_moe_gather_fmt(kU4G64.bits, kU4G64.group, stage, in, K, codes, scales, biases, E, rows, expert_ids,
+                            expert_w, topk, out, out_dtype, stream);
 }
 
 size_t qmm_moe_prefill_workspace_bytes(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
@@ -304,7 +368,7 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
   const bool s1 = stage == QMM_MOE_GATE_UP_SWIGLU;
   const size_t need = qmm_moe_prefill_workspace_bytes(M, topk, E, s1 ? 0 : rows);
-  if (need == 0 || !qmm::k_ok(K) || rows < 1 || !matrix_fits(rows, K) || (s1 && rows % 2) ||
+  if (need == 0 || !qmm::k_ok(K) || rows < 1 || !codes_fit(rows, K, kU4G64) || (s1 && rows % 2) ||
       !acts_fit(s1 ? M : M * topk, K) || workspace_bytes < need)
     return QMM_ERR_SHAPE;
   const size_t e = out_elem(out_dtype);
@@ -316,9 +380,9 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
   const int64_t out_elems = s1 ? P * (rows / 2) : M * rows;
   const Range outs[] = {{out, uint64_t(out_elems) * e}, {workspace, uint64_t(need)}};
   const Range ins[] = {{in, uint64_t(in_elems) * 2},
-                       {codes, u4_code_bytes(E * rows, K)},
-                       {scales, u4_group_bytes(E * rows, K)},
-                       {biases, u4_group_bytes(E * rows, K)},
+                       {codes, code_bytes(E * rows, K, kU4G64)},
+                       {scales, group_bytes(E * rows, K, kU4G64)},
+                       {biases, group_bytes(E * rows, K, kU4G64)},
                        {expert_ids, uint64_t(P) * 4},
                        {expert_w, expert_w ? uint64_t(P) * 4 : 0}};
   if (qmm::any_alias(outs, 2, ins, 6)) return QMM_ERR_ALIAS;
@@ -333,6 +397,7 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
   a.N = rows;
   a.I = rows / 2;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.gshift = kU4G64.gshift;
   a.moe_w = s1 ? nullptr : expert_w;
   return qmm::launch_moe_prefill(s1 ? 0 : 1, a, expert_ids, M, topk, E, workspace, out, stream);
 }

@@ -47,6 +47,7 @@ struct GemvArgs {
   int64_t E;               // experts in the grid
   int topk;
   int f32_out;
+  int gshift;              // group size = 32 << gshift (scales/biases per 32, 64 or 128 inputs)
   RopeArgs rope;           // EPI_ROPE only
 };
 
@@ -70,6 +71,7 @@ struct GemmArgs {
   const int32_t* moe_pairs;    // [pairs] bucketed pair indices (token * topk + slot)
   const float* moe_w;          // stage 2: combine weight of each pair; null in stage 1
   int64_t moe_div;             // topk in stage 1 (x row of a pair), 1 in stage 2
+  int gshift;                  // group size = 32 << gshift
   RopeArgs rope;               // EPI_ROPE only
 };
 

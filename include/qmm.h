@@ -241,6 +241,33 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K,
                     int64_t topk, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
                     hipStream_t stream);
 
+/*
+ * Other formats of the affine family (saragossa README, "Capabilities": u4/u6/u8 at group
+ * sizes 32-128 with bf16 scales/biases; "Quantization formats": u2/u3/u4/u6/u8 affine
+ * integer weights).  The *_fmt calls are the calls above with the code width `bits` and
+ * the group size `group_size` as their first two arguments; the plain calls are the
+ * *_fmt calls at (4, 64).  Layout: codes [rows][K*bits/32] uint32, the row one
+ * little-endian bit stream (code k = stream bits [bits*k, bits*k + bits), bit j of the
+ * stream = bit j % 32 of word j / 32; at 4 bits this is the nibble order at the top of
+ * this file); scales/biases [rows][K/group_size] bf16; w = scale*q + bias, q in
+ * 0 .. 2^bits - 1.  Supported: bits 4; group_size 32, 64 or 128 with K a multiple of 64
+ * and of group_size.  Anything else is QMM_ERR_SHAPE.
+ */
+int qmm_linear_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K,
+                   const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                   int64_t N, const uint16_t* lin_bias, void* y, int out_dtype, hipStream_t stream);
+int qmm_fused_qkv_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K,
+                      const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                      int64_t q_out, int64_t kv_out, const uint16_t* lin_bias,
+                      void* q, void* k, void* v, int out_dtype, hipStream_t stream);
+int qmm_fused_gate_up_swiglu_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K,
+                                 const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                                 int64_t I, void* h, int out_dtype, hipStream_t stream);
+int qmm_moe_gather_fmt(int bits, int64_t group_size, int stage, const uint16_t* in, int64_t K,
+                       const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                       int64_t E, int64_t rows, const int32_t* expert_ids, const float* expert_w,
+                       int64_t topk, void* out, int out_dtype, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* qmm_status_str(int status);
 

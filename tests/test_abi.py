@@ -25,6 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm_fused_gate_up_swiglu",
+                                           "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
+                                           "qmm_moe_gather_fmt",
                                            "qmm_moe_gather", "qmm_moe_prefill_workspace_bytes",
                                            "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str",
                                            "qmm_abi_version"])
@@ -116,6 +118,29 @@ def test_overlapping_outputs_and_inputs_are_rejected():
     assert _linear(y=A) == S["QMM_ERR_ALIAS"]
     assert _linear(y=A + (1 << 16) + 512) == S["QMM_ERR_ALIAS"]
     assert _linear(y=A + (1 << 19) + 16) == S["QMM_ERR_ALIAS"]
+
+
+# ---- other formats ---------------------------------------------------------------------
+
+def _linear_fmt(bits=4, group=64, K=512, **kw):
+    args = dict(x=A, M=1, codes=A + (1 << 16), s=A + (1 << 18), b=A + (1 << 19), N=64, lb=None, y=A + (1 << 21),
+                od=0)
+    args.update(kw)
+    return qmm.load_library().qmm_linear_fmt(bits, group, args["x"], args["M"], K, args["codes"], args["s"],
+                                             args["b"], args["N"], args["lb"], args["y"], args["od"], None)
+
+
+def test_format_validation():
+    for bits, group, K in [(5, 64, 512), (4, 16, 512), (4, 96, 576), (4, 256, 512), (4, 128, 320), (1, 64, 512)]:
+        assert _linear_fmt(bits, group, K) == S["QMM_ERR_SHAPE"], (bits, group, K)
+    # the plain call is the (4, 64) format: the same validation result for a bad pointer
+    assert _linear_fmt(4, 64, x=A + 2) == S["QMM_ERR_ALIGN"] == _linear(x=A + 2)
+    # group 128 with K = 512, group 32: past the shape checks (fails only on the alias below)
+    assert _linear_fmt(4, 128, 512, y=A) == S["QMM_ERR_ALIAS"]
+    assert _linear_fmt(4, 32, 512, y=A) == S["QMM_ERR_ALIAS"]
+    # the alias ranges follow the format's sizes: K=512, N=64 at group 32 -> scales 64 x 16 x 2 B
+    assert _linear_fmt(4, 32, 512, y=A + (1 << 18) + 64 * 16 * 2 - 2) == S["QMM_ERR_ALIAS"]
+    assert _linear_fmt(4, 128, 512, y=A + (1 << 18) + 64 * 4 * 2 - 2) == S["QMM_ERR_ALIAS"]
 
 
 # ---- fused QKV with rotary embedding ------------------------------------------------

@@ -1,0 +1,99 @@
+"""GPU parity of the other formats of the affine family (code width, group size) against
+the fp64 oracle: projections, fused QKV, fused gate+up and the routed-expert gather, in
+decode (GEMV) and prefill (GEMM), through the *_fmt calls of the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_affine_u4_amd as qmm
+import synth
+from oracle import qmm_oracle as orc
+from gpu_util import Guarded, assert_within, dev, rne_bits_of, say
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(4, 32), (4, 128)]
+
+
+def W(bits, G, rows, K, layer, index=0):
+    return synth.gen_weight(synth.CFG_TEST, layer, synth.PROJ_LINEAR, rows, K, index=index, bits=bits, group=G)
+
+
+def lin(bits, G, x, w, N, f32=True, lb=None):
+    M = x.shape[0]
+    y = Guarded((M, N), f32)
+    qmm.qmm_linear_fmt(bits, G, dev(x), dev(w.codes), dev(w.scales), dev(w.biases), y.t,
+                       lin_bias=None if lb is None else dev(lb))
+    torch.cuda.synchronize()
+    return y.values()
+
+
+@pytest.mark.parametrize("bits,G", FORMATS)
+@pytest.mark.parametrize("M,K,N", [(1, 512, 300), (3, 5120, 200), (1, 8192, 130), (2, 64 * 45, 77),
+                                   (40, 1024, 260), (300, 640, 129)])
+def test_linear_formats(bits, G, M, K, N):
+    if K % G:
+        pytest.skip("K is not a whole number of groups")
+    say(f"[fmt] linear u{bits} g{G} M={M} K={K} N={N}")
+    w = W(bits, G, N, K, 1)
+    lb = synth.gen_lin_bias(synth.CFG_TEST, 1, N)
+    x = synth.gen_x(synth.CFG_TEST, 1, M, M, K)
+    y, t = orc.linear(x, w.codes, w.scales, w.biases, lb, bf16_weights=M > 8, bits=bits)
+    g = lin(bits, G, x, w, N, lb=lb)
+    assert_within(g, y, t, f"u{bits} g{G} linear M={M} K={K}")
+    assert np.array_equal(lin(bits, G, x, w, N, f32=False, lb=lb), rne_bits_of(g))
+
+
+@pytest.mark.parametrize("bits,G", FORMATS)
+@pytest.mark.parametrize("M", [1, 64])
+def test_fused_qkv_and_gate_up_formats(bits, G, M):
+    K, q_out, kv_out, I = 1024, 256, 64, 192
+    say(f"[fmt] fused u{bits} g{G} M={M}")
+    x = synth.gen_x(synth.CFG_TEST, 2, M, M, K)
+    wq = W(bits, G, q_out + 2 * kv_out, K, 2)
+    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, wq.codes, wq.scales, wq.biases, q_out, kv_out,
+                                            bf16_weights=M > 8, bits=bits)
+    gq, gk, gv = Guarded((M, q_out), True), Guarded((M, kv_out), True), Guarded((M, kv_out), True)
+    qmm.qmm_fused_qkv_fmt(bits, G, dev(x), dev(wq.codes), dev(wq.scales), dev(wq.biases), gq.t, gk.t, gv.t)
+    wg = W(bits, G, 2 * I, K, 3)
+    h, th = orc.gate_up_swiglu(x, wg.codes, wg.scales, wg.biases, I, bf16_weights=M > 8, bits=bits)
+    gh = Guarded((M, I), True)
+    qmm.qmm_fused_gate_up_swiglu_fmt(bits, G, dev(x), dev(wg.codes), dev(wg.scales), dev(wg.biases), gh.t)
+    torch.cuda.synchronize()
+    for got, ref, tol, name in ((gq, q, tq, "q"), (gk, k, tk, "k"), (gv, v, tv, "v"), (gh, h, th, "h")):
+        assert_within(got.values(), ref, tol, f"u{bits} g{G} {name} M={M}")
+
+
+@pytest.mark.parametrize("bits,G", FORMATS)
+def test_moe_gather_formats(bits, G):
+    E, hidden, I, topk = 6, 512, 128, 3
+    say(f"[fmt] moe u{bits} g{G}")
+    gu = synth.gen_expert_grid(synth.CFG_TEST, 4, synth.PROJ_MOE_GATE_UP, E, 2 * I, hidden, bits=bits, group=G)
+    dn = synth.gen_expert_grid(synth.CFG_TEST, 4, synth.PROJ_MOE_DOWN, E, hidden, I, bits=bits, group=G)
+    x = synth.gen_x(synth.CFG_TEST, 4, 0, 1, hidden)[0]
+    ids = np.array([4, -1, 1], np.int32)
+    p = np.array([0.5, 0.2, 0.3], np.float32)
+    h, th = orc.moe_gate_up(x, gu.codes, gu.scales, gu.biases, ids, 2 * I, bits=bits)
+    g1 = Guarded((topk, I), True)
+    qmm.qmm_moe_gather_fmt(bits, G, qmm.QMM_MOE_GATE_UP_SWIGLU, dev(x), dev(gu.codes), dev(gu.scales),
+                           dev(gu.biases), dev(ids), g1.t)
+    hb = orc.f32_to_bf16_bits(h)
+    y, ty = orc.moe_down_combine(hb, dn.codes, dn.scales, dn.biases, ids, p, bits=bits)
+    g2 = Guarded((hidden,), True)
+    qmm.qmm_moe_gather_fmt(bits, G, qmm.QMM_MOE_DOWN_COMBINE, dev(hb), dev(dn.codes), dev(dn.scales),
+                           dev(dn.biases), dev(ids), g2.t, expert_w=dev(p))
+    torch.cuda.synchronize()
+    assert_within(g1.values(), h, th, f"u{bits} g{G} moe stage 1")
+    assert_within(g2.values(), y, ty, f"u{bits} g{G} moe stage 2")
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_fmt_at_u4_g64_is_the_plain_call_bit_for_bit(M):
+    K, N = 1024, 300
+    w = W(4, 64, N, K, 5)
+    x = synth.gen_x(synth.CFG_TEST, 5, 0, M, K)
+    a = lin(4, 64, x, w, N)
+    b = Guarded((M, N), True)
+    qmm.qmm_linear(dev(x), dev(w.codes), dev(w.scales), dev(w.biases), b.t)
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b.values())
