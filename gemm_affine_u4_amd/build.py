@@ -17,7 +17,12 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libqmm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["qmm_api.cpp", "qmm_validate.cpp", "gemv_u4.hip", "gemm_u4.hip", "moe_route.hip"]
+# (source, extra flags, object): the GEMV and GEMM sources are built once per code width.
+WIDTHS = (2, 3, 4, 6, 8)
+SOURCES = ([("qmm_api.cpp", [], "qmm_api.o"), ("qmm_validate.cpp", [], "qmm_validate.o"),
+            ("moe_route.hip", [], "moe_route.o")]
+           + [(src, [f"-DQMM_BITS={b}"], f"{src.split('.')[0]}_b{b}.o") for src in ("gemv_u4.hip", "gemm_u4.hip")
+              for b in WIDTHS])
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -26,10 +31,11 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(entry) -> str:
+    src, extra, obj_name = entry
+    obj = os.path.join(BUILD_DIR, obj_name)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

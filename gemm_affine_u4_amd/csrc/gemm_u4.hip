@@ -30,7 +30,18 @@
 #include "qmm_internal.h"
 #include "qmm_rope.h"
 
+#ifndef QMM_BITS
+#define QMM_BITS 4
+#endif
+
 namespace qmm {
+// Each code width is its own object (this file built once per width with -DQMM_BITS=N):
+// its kernels and launchers live in namespace qmm::b<N>.
+namespace QMM_BITS_NS {
+
+constexpr int kBits = QMM_BITS;
+// vector-memory loads of one lane's 32 codes of a K step (16-, 12- or 8-byte loads)
+constexpr int kCodeLoads = kBits / 4 + (kBits % 4 != 0 ? 1 : 0);
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -119,7 +130,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     pair_base = a.moe_tiles[2 * mt + 1];
     rows_here = min(kBM, a.moe_offsets[e + 1] - pair_base);
     const int64_t er = int64_t(e) * a.N;  // first row of the expert in the grid
-    a.codes += er * (a.K >> 3);
+    a.codes += er * ((a.K * kBits) >> 5);
     a.scales += er * (a.K >> (5 + a.gshift));
     a.biases += er * (a.K >> (5 + a.gshift));
   }
@@ -171,43 +182,84 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   // The lane then dequantizes those 32 codes into chunks 4 (L / 32) .. +3 of that row.
   const int wh = lane >> 5;
   const uint64_t nrows = uint64_t(a.N);
-  const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes, nrows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes, nrows * ((K * kBits) >> 3));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, nrows * groups * 2);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases, nrows * groups * 2);
   const int wt = 32 * wave + (lane & 31);  // tile row whose half `wh` this lane owns
   const int64_t wrow = gemm_weight_row<EPI>(a, nt, wt);
-  const uint32_t coff = uint32_t(wrow) * (K >> 1) + 16u * uint32_t(wh);
+  // codes of row wrow: K*bits/8 bytes; the lane's 32 codes of step ks start 4*bits bytes
+  // into the step's 8*bits
+  const uint32_t coff = uint32_t(wrow) * ((K * kBits) >> 3) + uint32_t(4 * kBits) * uint32_t(wh);
   const uint32_t goff = uint32_t(wrow) * groups * 2;
   const uint32_t wdst = uint32_t(wt) * kRow;
   const uint32_t wsw = swz(uint32_t(wt));
-  // one step of this lane's half row in flight: 4 code words, scale, bias; step j lives in
-  // set j % 3
+  // one step of this lane's half row in flight: its bits code words, scale, bias; step j
+  // lives in set j % 3
   struct StepRegs {
-    u32x4_t cv;
+    uint32_t cv[kBits];
     uint16_t sv, bv;
   };
   StepRegs R[3];
   // the lane's 32 codes of step ks are inputs 64 ks + 32 wh .. +31: group (2 ks + wh) >> gshift
   auto load_w = [&](StepRegs& r, int ks) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
     const uint32_t go = goff + ((uint32_t(2 * ks + wh) >> a.gshift) << 1);
-    r.cv = __builtin_amdgcn_raw_buffer_load_b128(cr, coff + uint32_t(ks) * 32u, 0, 0);
+    const uint32_t co = coff + uint32_t(ks) * uint32_t(8 * kBits);
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= kBits; i += 4) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(cr, co + 4u * i, 0, 0);
+      r.cv[i] = v[0];
+      r.cv[i + 1] = v[1];
+      r.cv[i + 2] = v[2];
+      r.cv[i + 3] = v[3];
+    }
+    if constexpr (kBits % 4 == 3) {
+      const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(cr, co + 4u * i, 0, 0);
+      r.cv[i] = v[0];
+      r.cv[i + 1] = v[1];
+      r.cv[i + 2] = v[2];
+    } else if constexpr (kBits % 4 == 2) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(cr, co + 4u * i, 0, 0);
+      r.cv[i] = v[0];
+      r.cv[i + 1] = v[1];
+    }
     r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, go, 0, 0);
     r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, go, 0, 0);
   };
-  constexpr int kStepLoads = 4 + 1 + 2;  // vector-memory loads one step requests per lane
-  // Piece p (0..3): code word p of the half row (8 codes -> w = s*q + b in fp32 -> bf16,
-  // 16 bytes) into chunk 4 wh + p of the row in stage `dst`.
+  constexpr int kStepLoads = 4 + kCodeLoads + 2;  // vector-memory loads one step requests per lane
+  // Piece p (0..3): codes 8p .. 8p+7 of the half row (-> w = s*q + b in fp32 -> bf16, 16
+  // bytes) into chunk 4 wh + p of the row in stage `dst`.
   auto store_piece = [&](const StepRegs& r, uint16_t* dst, int p) {
     const float s = bf16_bits_to_f32(r.sv);
     const float b = bf16_bits_to_f32(r.bv);
-    const uint32_t w = r.cv[p];
-    // low and high nibbles of the four bytes, then one v_cvt_f32_ubyte{0..3} per code
-    const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
-    const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
-    const u32x4_t v = {pack_bf16x2(fmaf(s, ubyte_f32<0>(lo), b), fmaf(s, ubyte_f32<0>(hi), b)),
-                       pack_bf16x2(fmaf(s, ubyte_f32<1>(lo), b), fmaf(s, ubyte_f32<1>(hi), b)),
-                       pack_bf16x2(fmaf(s, ubyte_f32<2>(lo), b), fmaf(s, ubyte_f32<2>(hi), b)),
-                       pack_bf16x2(fmaf(s, ubyte_f32<3>(lo), b), fmaf(s, ubyte_f32<3>(hi), b))};
+    u32x4_t v;
+    if constexpr (kBits == 4) {
+      // low and high nibbles of the four bytes of word p, one v_cvt_f32_ubyte{0..3} per code
+      const uint32_t w = r.cv[p];
+      const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
+      const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
+      v = u32x4_t{pack_bf16x2(fmaf(s, ubyte_f32<0>(lo), b), fmaf(s, ubyte_f32<0>(hi), b)),
+                  pack_bf16x2(fmaf(s, ubyte_f32<1>(lo), b), fmaf(s, ubyte_f32<1>(hi), b)),
+                  pack_bf16x2(fmaf(s, ubyte_f32<2>(lo), b), fmaf(s, ubyte_f32<2>(hi), b)),
+                  pack_bf16x2(fmaf(s, ubyte_f32<3>(lo), b), fmaf(s, ubyte_f32<3>(hi), b))};
+    } else if constexpr (kBits == 8) {
+      // the bytes of words 2p and 2p + 1 are the codes
+      const uint32_t w0 = r.cv[2 * p], w1 = r.cv[2 * p + 1];
+      v = u32x4_t{pack_bf16x2(fmaf(s, ubyte_f32<0>(w0), b), fmaf(s, ubyte_f32<1>(w0), b)),
+                  pack_bf16x2(fmaf(s, ubyte_f32<2>(w0), b), fmaf(s, ubyte_f32<3>(w0), b)),
+                  pack_bf16x2(fmaf(s, ubyte_f32<0>(w1), b), fmaf(s, ubyte_f32<1>(w1), b)),
+                  pack_bf16x2(fmaf(s, ubyte_f32<2>(w1), b), fmaf(s, ubyte_f32<3>(w1), b))};
+    } else {
+      // code k of the half row: stream bits [bits*k, bits*k + bits) (may straddle words)
+      constexpr uint32_t m = (1u << kBits) - 1u;
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = fmaf(s, float(stream_window(r.cv, kBits * (8 * p + j)) & m), b);
+      v = u32x4_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                  pack_bf16x2(f[6], f[7])};
+    }
     const uint32_t chunk = uint32_t(4 * wh + p);
     *reinterpret_cast<u32x4_t*>(dst + wdst + (chunk ^ wsw) * 8) = v;
   };
@@ -547,13 +599,18 @@ int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   } else if (epi == EPI_QKV) {
     gemm_u4_kernel<EPI_QKV, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else if (epi == EPI_ROPE) {
+#if QMM_BITS == 4
     gemm_u4_kernel<EPI_ROPE, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+#else
+    return 2;  // the rotary epilogue is built for 4-bit codes only
+#endif
   } else {
     gemm_u4_kernel<EPI_SWIGLU, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   }
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
+#if QMM_BITS == 4
 int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
   const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
   const int64_t tiles = m_tiles * n_tiles;
@@ -570,4 +627,7 @@ int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) 
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
+#endif
+
+}  // namespace QMM_BITS_NS
 }  // namespace qmm

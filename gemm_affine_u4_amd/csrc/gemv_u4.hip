@@ -31,7 +31,19 @@
 #include "qmm_internal.h"
 #include "qmm_rope.h"
 
+#ifndef QMM_BITS
+#define QMM_BITS 4
+#endif
+
 namespace qmm {
+// Each code width is its own object (this file built once per width with -DQMM_BITS=N):
+// its kernels and launchers live in namespace qmm::b<N>.
+namespace QMM_BITS_NS {
+
+constexpr int kBits = QMM_BITS;
+using Cd = Codec<kBits>;
+constexpr int kChunkBytes = 4 * kBits;  // 32 codes
+constexpr int kMaxCplSplit16 = (kBits == 2 || kBits == 4) ? 4 : 3;
 
 
 // Activations of this lane's chunks, in registers for the whole kernel, read through a
@@ -52,7 +64,7 @@ __device__ __forceinline__ void load_x_chunks(__amdgpu_buffer_rsrc_t xr, uint32_
       d[4 * v + 2] = t[2];
       d[4 * v + 3] = t[3];
     }
-    permute_chunk(d, xp[i]);
+    Cd::permute(d, xp[i]);
     xs[i] = chunk_xsum(xp[i]);
   }
 }
@@ -60,23 +72,48 @@ __device__ __forceinline__ void load_x_chunks(__amdgpu_buffer_rsrc_t xr, uint32_
 // The packed codes and the group scales/biases of one row for this lane's chunks.
 template <int CPL>
 struct RowData {
-  u32x4_t w[CPL];
+  uint32_t w[CPL][kBits];
   uint16_t s[CPL], b[CPL];
 };
 
-// Chunk c0 + LPR*i of row `row`: codes at byte row*K/2 + 16*c, scale/bias of group
-// c >> gshift (group size 32 << gshift) at 2*(row*K/G + (c >> gshift)); consecutive
-// chunks of a lane are LPR*16 (codes) and 2*(LPR >> gshift) (groups) bytes apart.
+// The kBits words of one chunk at byte `off` (16-, 12- or 8-byte loads).
+__device__ __forceinline__ void load_chunk(uint32_t (&w)[kBits], __amdgpu_buffer_rsrc_t cr, uint32_t off) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+  int i = 0;
+#pragma unroll
+  for (; i + 4 <= kBits; i += 4) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(cr, off + 4u * i, 0, kLoadNT);
+    w[i] = v[0];
+    w[i + 1] = v[1];
+    w[i + 2] = v[2];
+    w[i + 3] = v[3];
+  }
+  if constexpr (kBits % 4 == 3) {
+    const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(cr, off + 4u * i, 0, kLoadNT);
+    w[i] = v[0];
+    w[i + 1] = v[1];
+    w[i + 2] = v[2];
+  } else if constexpr (kBits % 4 == 2) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(cr, off + 4u * i, 0, kLoadNT);
+    w[i] = v[0];
+    w[i + 1] = v[1];
+  }
+}
+
+// Chunk c0 + LPR*i of row `row`: codes at byte row*K*bits/8 + 4*bits*c, scale/bias of
+// group c >> gshift (group size 32 << gshift) at 2*(row*K/G + (c >> gshift)); consecutive
+// chunks of a lane are LPR*4*bits (codes) and 2*(LPR >> gshift) (groups) bytes apart.
 template <int LPR, int CPL>
 __device__ __forceinline__ void load_row(RowData<CPL>& r, __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr,
                                          __amdgpu_buffer_rsrc_t br, uint32_t row, uint32_t row_bytes,
                                          uint32_t row_groups, uint32_t c0, int gshift) {
-  const uint32_t co = row * row_bytes + c0 * 16u;
+  const uint32_t co = row * row_bytes + c0 * uint32_t(kChunkBytes);
   const uint32_t go = (row * row_groups + (c0 >> gshift)) * 2u;
   const uint32_t gstep = uint32_t(LPR >> gshift) * 2u;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(cr, co + uint32_t(i * LPR * 16), 0, kLoadNT);
+    load_chunk(r.w[i], cr, co + uint32_t(i * LPR * kChunkBytes));
     r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, go + uint32_t(i) * gstep, 0, 0);
     r.b[i] = __builtin_amdgcn_raw_buffer_load_b16(br, go + uint32_t(i) * gstep, 0, 0);
   }
@@ -89,9 +126,7 @@ __device__ __forceinline__ float row_partial(const RowData<CPL>& r, const uint32
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const uint32_t ww[4] = {r.w[i][0], r.w[i][1], r.w[i][2], r.w[i][3]};
-    const float D = chunk_dot128(ww, xp[i], magic);
-    const float d = fmaf(-128.0f, xs[i], D);
+    const float d = Cd::dot_q(r.w[i], xp[i], xs[i], magic);  // sum x q over the chunk
     acc = fmaf(bf16_bits_to_f32(r.s[i]), d, acc);
     acc = fmaf(bf16_bits_to_f32(r.b[i]), xs[i], acc);
   }
@@ -211,7 +246,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
   const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane / LPR;
   const int li = lane % LPR;
-  const int64_t words = a.K >> 3;
+  const int64_t words = (a.K * kBits) >> 5;
   const int64_t groups = a.K >> (5 + a.gshift);
   const int64_t gi = blockIdx.x;
   const int64_t u_begin = gi * per_group + (gi < extra ? gi : extra);
@@ -248,7 +283,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
     out_base = int64_t(blockIdx.y) * a.n_out;
   }
 
-  const uint32_t row_bytes = uint32_t(a.K >> 1);
+  const uint32_t row_bytes = uint32_t((a.K * kBits) >> 3);
   const uint32_t row_groups = uint32_t(groups);
   const uint64_t nrows = uint64_t(a.rows);
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, nrows * row_bytes);
@@ -349,7 +384,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane / LPR;
   const int li = lane % LPR;
-  const int64_t words = a.K >> 3;
+  const int64_t words = (a.K * kBits) >> 5;
   const int64_t groups = a.K >> (5 + a.gshift);
   // the units are spread evenly over the waves: every wave takes `per_wave` consecutive
   // units and the first `extra` waves one more
@@ -387,7 +422,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
     out_base = int64_t(blockIdx.y) * a.n_out;
   }
 
-  const uint32_t row_bytes = uint32_t(a.K >> 1);
+  const uint32_t row_bytes = uint32_t((a.K * kBits) >> 3);
   const uint64_t nrows = uint64_t(a.rows);
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes, nrows * row_bytes);
   const uint32_t c0 = uint32_t(li);
@@ -424,7 +459,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
         d[4 * v + 3] = t[3];
       }
       uint32_t xp[16];
-      permute_chunk(d, xp);
+      Cd::permute(d, xp);
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(xl + c * kXStride);
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[v] = u32x4_t{xp[4 * v], xp[4 * v + 1], xp[4 * v + 2], xp[4 * v + 3]};
@@ -490,9 +525,9 @@ __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units
   const bool result_lane = lane == slot_result_lane<LPR>(slot);
   const int64_t u_begin = int64_t(blockIdx.x) * upw;
   const int nu = int(u_begin + upw < units ? upw : units - u_begin);
-  const uint32_t row_bytes = uint32_t(a.K >> 1);
+  const uint32_t row_bytes = uint32_t((a.K * kBits) >> 3);
   const uint32_t row_groups = uint32_t(a.K >> (5 + a.gshift));
-  const uint64_t expert_words = uint64_t(a.rows) * uint64_t(a.K >> 3);
+  const uint64_t expert_words = uint64_t(a.rows) * uint64_t((a.K * kBits) >> 5);
   const uint64_t expert_groups = uint64_t(a.rows) * row_groups;
   const uint32_t c0 = uint32_t(li);
   const uint32_t magic = in_vgpr(kMagicPair);
@@ -544,7 +579,9 @@ bool gemv_shape_for_k(int64_t K, GemvShape* o) {
   // at most 5 chunks (80 activation registers) per lane.
   const int ks = C <= 160 ? 1 : (C <= 1280 ? 8 : 16);
   const int64_t cpl = (C + 32 * ks - 1) / (32 * ks);
-  if (cpl > (ks == 16 ? 4 : 5)) return false;
+  // the 16-way split runs 1024 threads (128 registers each): 3 chunks per lane for the
+  // codes that take more than 4 words per chunk or a funnel shift per code pair
+  if (cpl > (ks == 16 ? kMaxCplSplit16 : 5)) return false;
   *o = GemvShape{32, int(cpl), ks};
   return true;
 }
@@ -563,6 +600,13 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
         <<<g1, dim3{64u * kWavesS1, 1u, 1u}, S1Layout<L, C>::lds_bytes(), s>>>(a, units / w, units % w); \
   } break;
 
+// 4 chunks per lane in the 16-way split only where they fit (kMaxCplSplit16)
+#if QMM_BITS == 2 || QMM_BITS == 4
+#define QMM_GEMV_CASE_SPLIT16_CPL4(EPI, MOE) QMM_GEMV_CASE(32, 4, 16, EPI, MOE)
+#else
+#define QMM_GEMV_CASE_SPLIT16_CPL4(EPI, MOE)
+#endif
+
 #define QMM_GEMV_CASES(EPI, MOE)                                                  \
   switch (sh.lpr * 10000 + sh.cpl * 100 + sh.ksplit) {                            \
     QMM_GEMV_S1_CASE(16, 1, EPI, MOE)                                             \
@@ -577,7 +621,7 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
     QMM_GEMV_CASE(32, 4, 8, EPI, MOE)                                             \
     QMM_GEMV_CASE(32, 5, 8, EPI, MOE)                                             \
     QMM_GEMV_CASE(32, 3, 16, EPI, MOE)                                            \
-    QMM_GEMV_CASE(32, 4, 16, EPI, MOE)                                            \
+    QMM_GEMV_CASE_SPLIT16_CPL4(EPI, MOE)                                          \
     default: return 2;                                                            \
   }
 
@@ -636,7 +680,11 @@ int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
   } else if (epi == EPI_QKV) {
     QMM_GEMV_CASES(EPI_QKV, false)
   } else if (epi == EPI_ROPE) {
+#if QMM_BITS == 4
     QMM_GEMV_CASES(EPI_ROPE, false)
+#else
+    return 2;  // the rotary epilogue is built for 4-bit codes only
+#endif
   } else {
     QMM_GEMV_CASES(EPI_SWIGLU, false)
   }
@@ -680,4 +728,5 @@ int launch_moe_down(const GemvArgs& a, hipStream_t s) {
   return finish_launch();
 }
 
+}  // namespace QMM_BITS_NS
 }  // namespace qmm

@@ -249,7 +249,7 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
     a.out0 = out;
     a.moe_w = nullptr;
     a.moe_div = topk;
-    if (int st = launch_gemm_moe(EPI_SWIGLU, a, L.tmax, s)) return st;
+    if (int st = b4::launch_gemm_moe(EPI_SWIGLU, a, L.tmax, s)) return st;
     moe_zero_unrouted<<<dim3{zb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, L.P, int(E), out, a.I, a.f32_out);
   } else {
     // stage 2: z = p * (D_e h) per routed pair (fp32, workspace), then the per-token sum
@@ -258,7 +258,7 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
     a.out0 = z;
     a.f32_out = 1;
     a.moe_div = 1;
-    if (int st = launch_gemm_moe(EPI_LINEAR, a, L.tmax, s)) return st;
+    if (int st = b4::launch_gemm_moe(EPI_LINEAR, a, L.tmax, s)) return st;
     const unsigned mb = unsigned(M < 4096 ? M : 4096);
     if (a.N % 4 == 0)
       moe_combine<true><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);

@@ -31,13 +31,15 @@ struct Fmt {
 // The widths the kernels implement; false for others, for other group sizes, and when K
 // is not a whole number of groups.
 bool fmt_ok(int bits, int64_t group, int64_t K, Fmt* f) {
-  if (bits != 4) return false;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) return false;
   int gs;
   if (group == 32) gs = 0;
   else if (group == 64) gs = 1;
   else if (group == 128) gs = 2;
   else return false;
   if (K % group) return false;
+  // the widest codes fit the decode kernel's 16-way K split up to K = 16 * 32 * 3 * 32
+  if ((bits == 3 || bits == 6 || bits == 8) && K > 49152) return false;
   *f = {bits, gs, group};
   return true;
 }
@@ -64,6 +66,7 @@ qmm::GemmArgs gemm_args(const qmm::GemvArgs& g, int64_t M, int64_t N) {
   a.kv_out = g.kv_out;
   a.I = g.I;
   a.f32_out = g.f32_out;
+  a.bits = g.bits;
   a.gshift = g.gshift;
   a.rope = g.rope;
   return a;
@@ -126,6 +129,7 @@ int qmm_linear_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, i
   a.rows = N;
   a.n_out = N;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.bits = f.bits;
   a.gshift = f.gshift;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_LINEAR, gemm_args(a, M, N), stream);
   return qmm::launch_gemv(qmm::EPI_LINEAR, a, M, stream);
@@ -174,6 +178,7 @@ int qmm_fused_qkv_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M
   a.q_out = q_out;
   a.kv_out = kv_out;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.bits = f.bits;
   a.gshift = f.gshift;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_QKV, gemm_args(a, M, rows), stream);
   return qmm::launch_gemv(qmm::EPI_QKV, a, M, stream);
@@ -230,6 +235,7 @@ int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   a.K = K;
   a.rows = rows;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.bits = 4;
   a.gshift = kU4G64.gshift;
   a.rope.positions = positions;
   a.rope.cos_sin = cos_sin;
@@ -273,6 +279,7 @@ int qmm_fused_gate_up_swiglu_fmt(int bits, int64_t group_size, const uint16_t* x
   a.I = I;
   a.n_out = I;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.bits = f.bits;
   a.gshift = f.gshift;
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_SWIGLU, gemm_args(a, M, 2 * I), stream);
   return qmm::launch_gemv(qmm::EPI_SWIGLU, a, M, stream);
@@ -327,6 +334,7 @@ int qmm_moe_gather_fmt(int bits, int64_t group_size, int stage, const uint16_t* 
   a.E = E;
   a.topk = int(topk);
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.bits = f.bits;
   a.gshift = f.gshift;
   if (stage == QMM_MOE_GATE_UP_SWIGLU) return qmm::launch_moe_gate_up(a, stream);
   return qmm::launch_moe_down(a, stream);
@@ -397,6 +405,7 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
   a.N = rows;
   a.I = rows / 2;
   a.f32_out = out_dtype == QMM_OUT_F32;
+  a.bits = 4;
   a.gshift = kU4G64.gshift;
   a.moe_w = s1 ? nullptr : expert_w;
   return qmm::launch_moe_prefill(s1 ? 0 : 1, a, expert_ids, M, topk, E, workspace, out, stream);

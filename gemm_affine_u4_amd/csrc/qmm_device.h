@@ -84,7 +84,7 @@ __device__ __forceinline__ float chunk_xsum(const uint32_t xp[16]) {
 }
 
 // sum_k x_k * (128 + q_k) over one chunk (four code words), fp32.
-__device__ __forceinline__ float chunk_dot128(const uint32_t w[4], const uint32_t xp[16], uint32_t magic) {
+__device__ __forceinline__ float chunk_dot128(const uint32_t (&w)[4], const uint32_t xp[16], uint32_t magic) {
   float d = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -93,6 +93,117 @@ __device__ __forceinline__ float chunk_dot128(const uint32_t w[4], const uint32_
   }
   return d;
 }
+
+// ---- code widths of the affine family ------------------------------------------------
+// A row is one little-endian bit stream of `BITS`-bit codes, so a chunk of 32 codes is
+// BITS words.  Codec<BITS> turns a chunk's words into exact bf16 pairs (128 + q_a,
+// 128 + q_b) for v_dot2 against activation pairs permuted to the same order, and
+// returns sum_k x_k q_k of the chunk (fp32).  `d[m]` below holds (x[2m], x[2m+1]).
+//
+// Activation pair (x[a], x[b]) from the unpermuted pairs.
+__device__ __forceinline__ uint32_t x_pair(const uint32_t d[16], int a, int b) {
+  const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
+  return __builtin_amdgcn_perm(d[b >> 1], d[a >> 1], sel);
+}
+// Bits [s, s + 32) of the stream of words w[] (s a compile-time constant after unrolling;
+// words past the chunk read as `pad`).
+template <int NW>
+__device__ __forceinline__ uint32_t stream_window(const uint32_t (&w)[NW], int s) {
+  const int i = s >> 5, sh = s & 31;
+  const uint32_t lo = i < NW ? w[i] : 0u;
+  if (sh == 0) return lo;
+  const uint32_t hi = i + 1 < NW ? w[i + 1] : 0u;
+  return __builtin_amdgcn_alignbit(hi, lo, sh);
+}
+
+template <int BITS>
+struct Codec;
+
+// 4 bits: pair (q_{8j+t}, q_{8j+t+4}) of word j is one shift-and-or (nib_pair).
+template <>
+struct Codec<4> {
+  static constexpr int kWords = 4;
+  static __device__ __forceinline__ void permute(const uint32_t d[16], uint32_t xp[16]) { permute_chunk(d, xp); }
+  static __device__ __forceinline__ float dot_q(const uint32_t (&w)[4], const uint32_t xp[16], float xs,
+                                                uint32_t magic) {
+    return fmaf(-128.0f, xs, chunk_dot128(w, xp, magic));
+  }
+};
+
+// 8 bits: each byte q = 16 h + l is taken as its two nibbles; pairs (l_{4j+u}, l_{4j+u+2})
+// and (h_{4j+u}, h_{4j+u+2}) of word j share the activation pair (x_{4j+u}, x_{4j+u+2}).
+template <>
+struct Codec<8> {
+  static constexpr int kWords = 8;
+  static __device__ __forceinline__ void permute(const uint32_t d[16], uint32_t xp[16]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xp[2 * j] = x_pair(d, 4 * j, 4 * j + 2);
+      xp[2 * j + 1] = x_pair(d, 4 * j + 1, 4 * j + 3);
+    }
+  }
+  static __device__ __forceinline__ float dot_q(const uint32_t (&w)[8], const uint32_t xp[16], float xs,
+                                                uint32_t magic) {
+    float dl = 0.f, dh = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      dl = dot2_bf16((w[j] & kNibblePair) | magic, xp[2 * j], dl);
+      dl = dot2_bf16(((w[j] >> 8) & kNibblePair) | magic, xp[2 * j + 1], dl);
+      dh = dot2_bf16(((w[j] >> 4) & kNibblePair) | magic, xp[2 * j], dh);
+      dh = dot2_bf16(((w[j] >> 12) & kNibblePair) | magic, xp[2 * j + 1], dh);
+    }
+    // sum x q = 16 (dh - 128 xs) + (dl - 128 xs); each difference is exactly 0 for zero codes
+    return fmaf(16.0f, fmaf(-128.0f, xs, dh), fmaf(-128.0f, xs, dl));
+  }
+};
+
+// 2 bits: pair (q_{16j+t}, q_{16j+t+8}) of word j: ((w >> 2t) & 0x00030003) | magic.
+template <>
+struct Codec<2> {
+  static constexpr int kWords = 2;
+  static __device__ __forceinline__ void permute(const uint32_t d[16], uint32_t xp[16]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xp[8 * j + t] = x_pair(d, 16 * j + t, 16 * j + t + 8);
+  }
+  static __device__ __forceinline__ float dot_q(const uint32_t (&w)[2], const uint32_t xp[16], float xs,
+                                                uint32_t magic) {
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) d = dot2_bf16(((w[j] >> (2 * t)) & 0x00030003u) | magic, xp[8 * j + t], d);
+    return fmaf(-128.0f, xs, d);
+  }
+};
+
+// 3 and 6 bits (codes may straddle words): pair (q_k, q_{k+16}); q_k is the low BITS of
+// the stream window at BITS*k, q_{k+16} sits at bit 16 of the window at BITS*k + 16*BITS - 16.
+template <int BITS>
+struct CodecStream {
+  static constexpr int kWords = BITS;
+  static __device__ __forceinline__ void permute(const uint32_t d[16], uint32_t xp[16]) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) xp[k] = x_pair(d, k, k + 16);
+  }
+  static __device__ __forceinline__ float dot_q(const uint32_t (&w)[BITS], const uint32_t xp[16], float xs,
+                                                uint32_t magic) {
+    constexpr uint32_t m = (1u << BITS) - 1u;
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t lo = stream_window(w, BITS * k) & m;
+      const uint32_t hi = stream_window(w, BITS * k + 16 * BITS - 16) & (m << 16);
+      d = dot2_bf16(lo | hi | magic, xp[k], d);
+    }
+    return fmaf(-128.0f, xs, d);
+  }
+};
+template <>
+struct Codec<3> : CodecStream<3> {};
+template <>
+struct Codec<6> : CodecStream<6> {};
 
 // Sum over the LPR lanes of each row slot (LPR = 16 or 32) with DPP.  After return the
 // slot's total is in every lane of its last 16-lane row (lanes 16*r + 15 - ... of row r).

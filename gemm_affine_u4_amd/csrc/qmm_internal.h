@@ -5,6 +5,12 @@
 
 namespace qmm {
 
+// The kernels of each code width (2, 3, 4, 6, 8 bits) are built as their own objects
+// from the same sources and live in namespace qmm::b<bits>.
+#define QMM_CAT2(a, b) a##b
+#define QMM_CAT(a, b) QMM_CAT2(a, b)
+#define QMM_BITS_NS QMM_CAT(b, QMM_BITS)
+
 enum Epilogue : int { EPI_LINEAR = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_ROPE = 3 };
 
 // Fused QKV with rotary embedding (EPI_ROPE).  The weight is heads of head_dim rows: per
@@ -26,7 +32,6 @@ struct GemvShape {
   int cpl;     // 32-code chunks per lane within a K slice
   int ksplit;  // waves sharing one row's K range (their partials meet in LDS)
 };
-bool gemv_shape_for_k(int64_t K, GemvShape* out);
 
 struct GemvArgs {
   const uint16_t* x;       // [M][K] bf16 (stage 2: [topk][K])
@@ -47,6 +52,7 @@ struct GemvArgs {
   int64_t E;               // experts in the grid
   int topk;
   int f32_out;
+  int bits;                // code width (2, 3, 4, 6 or 8)
   int gshift;              // group size = 32 << gshift (scales/biases per 32, 64 or 128 inputs)
   RopeArgs rope;           // EPI_ROPE only
 };
@@ -71,14 +77,48 @@ struct GemmArgs {
   const int32_t* moe_pairs;    // [pairs] bucketed pair indices (token * topk + slot)
   const float* moe_w;          // stage 2: combine weight of each pair; null in stage 1
   int64_t moe_div;             // topk in stage 1 (x row of a pair), 1 in stage 2
+  int bits;                    // code width
   int gshift;                  // group size = 32 << gshift
   RopeArgs rope;               // EPI_ROPE only
 };
 
-// Prefill GEMM (LDS dequant + MFMA).
-int launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
-// Gathered GEMM of the routed experts over a batch: m_tiles = bound on the tile table.
+// Launchers of one code width.  Decode GEMV: M rows of x as independent GEMVs (grid.y);
+// routed experts for one token: stage 1 (gathered gate+up+SwiGLU), stage 2 (gathered
+// down + combine); prefill GEMM (LDS dequant + MFMA).
+#define QMM_WIDTH_LAUNCHERS(NS)                                             \
+  namespace NS {                                                            \
+  bool gemv_shape_for_k(int64_t K, GemvShape* out);                         \
+  int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);    \
+  int launch_moe_gate_up(const GemvArgs& a, hipStream_t s);                 \
+  int launch_moe_down(const GemvArgs& a, hipStream_t s);                    \
+  int launch_gemm(int epi, const GemmArgs& a, hipStream_t s);               \
+  }
+QMM_WIDTH_LAUNCHERS(b2)
+QMM_WIDTH_LAUNCHERS(b3)
+QMM_WIDTH_LAUNCHERS(b4)
+QMM_WIDTH_LAUNCHERS(b6)
+QMM_WIDTH_LAUNCHERS(b8)
+// Gathered GEMM of the routed experts over a batch (4-bit codes): m_tiles = bound on the
+// tile table.
+namespace b4 {
 int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
+}
+
+#define QMM_BY_WIDTH(bits, CALL)                \
+  switch (bits) {                               \
+    case 2: return b2::CALL;                    \
+    case 3: return b3::CALL;                    \
+    case 4: return b4::CALL;                    \
+    case 6: return b6::CALL;                    \
+    case 8: return b8::CALL;                    \
+    default: return 2;                          \
+  }
+inline int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
+  QMM_BY_WIDTH(a.bits, launch_gemv(epi, a, M, s))
+}
+inline int launch_moe_gate_up(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_moe_gate_up(a, s)) }
+inline int launch_moe_down(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_moe_down(a, s)) }
+inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_gemm(epi, a, s)) }
 
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
@@ -95,10 +135,5 @@ int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, voi
 int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t M, int64_t topk, int64_t E,
                        const void* ws, void* out, hipStream_t s);
 
-// Decode GEMV; M rows of x processed as independent GEMVs (grid.y).
-int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
-// Routed experts: stage 1 (gathered gate+up+SwiGLU) and stage 2 (gathered down + combine).
-int launch_moe_gate_up(const GemvArgs& a, hipStream_t s);
-int launch_moe_down(const GemvArgs& a, hipStream_t s);
 
 }  // namespace qmm

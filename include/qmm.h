@@ -250,8 +250,9 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K,
  * little-endian bit stream (code k = stream bits [bits*k, bits*k + bits), bit j of the
  * stream = bit j % 32 of word j / 32; at 4 bits this is the nibble order at the top of
  * this file); scales/biases [rows][K/group_size] bf16; w = scale*q + bias, q in
- * 0 .. 2^bits - 1.  Supported: bits 4; group_size 32, 64 or 128 with K a multiple of 64
- * and of group_size.  Anything else is QMM_ERR_SHAPE.
+ * 0 .. 2^bits - 1.  Supported: bits 2, 3, 4, 6, 8; group_size 32, 64 or 128 with K a
+ * multiple of 64 and of group_size; K <= 49152 for bits 3, 6, 8 (65536 otherwise).
+ * Anything else is QMM_ERR_SHAPE.
  */
 int qmm_linear_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K,
                    const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,

@@ -12,7 +12,7 @@ from gpu_util import Guarded, assert_within, dev, rne_bits_of, say
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = [(4, 32), (4, 128)]
+FORMATS = [(4, 32), (4, 128), (8, 64), (8, 32), (6, 64), (6, 128), (3, 64), (3, 32), (2, 64), (2, 128)]
 
 
 def W(bits, G, rows, K, layer, index=0):
@@ -97,3 +97,26 @@ def test_fmt_at_u4_g64_is_the_plain_call_bit_for_bit(M):
     qmm.qmm_linear(dev(x), dev(w.codes), dev(w.scales), dev(w.biases), b.t)
     torch.cuda.synchronize()
     assert np.array_equal(a, b.values())
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+def test_largest_K_per_width(bits):
+    """The deepest K split of the decode kernel at each width's largest K, and the GEMM."""
+    K = 65536 if bits in (2, 4) else 49152
+    N = 48
+    w = W(bits, 64, N, K, 6)
+    for M in (1, 16):
+        say(f"[fmt] u{bits} K={K} M={M}")
+        x = synth.gen_x(synth.CFG_TEST, 6, M, M, K)
+        y, t = orc.linear(x, w.codes, w.scales, w.biases, bf16_weights=M > 8, bits=bits)
+        assert_within(lin(bits, 64, x, w, N), y, t, f"u{bits} K={K} M={M}")
+
+
+def test_wide_codes_past_their_largest_K_are_rejected():
+    x = torch.zeros((1, 49216), dtype=torch.int16, device="cuda")
+    for bits in (3, 6, 8):
+        w = W(bits, 64, 1, 49216, 7)
+        y = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
+        with pytest.raises(qmm.QmmError) as e:
+            qmm.qmm_linear_fmt(bits, 64, x, dev(w.codes), dev(w.scales), dev(w.biases), y)
+        assert e.value.status == qmm.STATUS["QMM_ERR_SHAPE"]
