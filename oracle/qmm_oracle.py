@@ -88,11 +88,41 @@ def unpack_bits(codes, bits: int) -> np.ndarray:
     return (f << np.arange(bits, dtype=np.int64)).sum(axis=-1)
 
 
-def dequant(codes, scales, biases, bits: int = 4) -> np.ndarray:
+E4M3 = "e4m3"
+
+
+def e4m3_to_f64(q) -> np.ndarray:
+    """fp8 e4m3 codes (0..255) -> fp64 from the format's definition: sign bit 7, exponent
+    bits 3..6 with bias 7, 3 fraction bits; exponent 0 is subnormal (m/8 * 2^-6); the
+    all-ones pattern S.1111.111 is NaN (no infinities)."""
+    q = np.asarray(q, dtype=np.int64)
+    sign = np.where(q & 0x80, -1.0, 1.0)
+    e = (q >> 3) & 0xF
+    m = (q & 0x7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    v = np.where((e == 15) & (q & 0x7 == 7), np.nan, v)
+    return sign * v
+
+
+def code_values(codes, bits) -> np.ndarray:
+    """The value each code stands for: the integer q for bits 2..8, the e4m3 number for
+    bits = E4M3 (8-bit codes; the saragossa README lists fp8 e4m3 next to the integer
+    widths, "Quantization formats", without its scaling; the reading taken is the same
+    affine form with the e4m3 value in place of q)."""
+    if bits == E4M3:
+        return e4m3_to_f64(unpack_bits(codes, 8))
+    return (unpack_u4(codes) if bits == 4 else unpack_bits(codes, bits)).astype(np.float64)
+
+
+def storage_bits(bits) -> int:
+    return 8 if bits == E4M3 else int(bits)
+
+
+def dequant(codes, scales, biases, bits=4) -> np.ndarray:
     """W[n, k] = s[n, k // G] * q[n, k] + b[n, k // G] in fp64, shape [rows, K], with the
     group size G = K / (scales per row) (64 on the workloads; 32 to 128 on the pages:
-    saragossa README, "Capabilities")."""
-    q = (unpack_u4(codes) if bits == 4 else unpack_bits(codes, bits)).astype(np.float64)
+    saragossa README, "Capabilities"); q is the code's value (`code_values`)."""
+    q = code_values(codes, bits)
     K = q.shape[-1]
     s = bf16_to_f64(scales)
     b = bf16_to_f64(biases)
@@ -123,7 +153,7 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024,
         x = x[None, :]
     N = codes.shape[0]
     K = x.shape[1]
-    if codes.shape[1] * 32 != K * bits:
+    if codes.shape[1] * 32 != K * storage_bits(bits):
         raise ValueError("x width must equal 32/bits * words per row")
     G = K // scales.shape[1]
     y = np.empty((x.shape[0], N))

@@ -100,6 +100,20 @@ def gen_weight(cfg: int, layer: int, proj: int, rows: int, K: int, index: int = 
     [-scale_hi*8, scale_hi*8] (tests only)."""
     if K % 64 or K % group:
         raise ValueError("K must be a multiple of 64 and of the group size")
+    if bits == "e4m3":
+        # fp8 e4m3 codes: uniform over the 254 finite patterns (0x7F and 0xFF are NaN),
+        # signed values, so no centring bias
+        b8 = rng(cfg, layer, proj, F_CODES, index).integers(0, 254, size=(rows, K), dtype=np.int64)
+        b8 = np.where(b8 >= 0x7F, b8 + 1, b8).astype(np.uint8)
+        codes = np.ascontiguousarray(b8).view("<u4").astype(np.uint32)
+        s32 = rng(cfg, layer, proj, F_SCALES, index).uniform(scale_lo, scale_hi, size=(rows, K // group)).astype(np.float32)
+        scales = to_bf16_bits(s32)
+        if bias == "uniform":
+            b = rng(cfg, layer, proj, F_BIASES, index).uniform(-8 * scale_hi, 8 * scale_hi, size=(rows, K // group))
+            biases = to_bf16_bits(b)
+        else:
+            biases = np.zeros_like(scales)
+        return U4Weight(codes, scales, biases, 8)
     codes = rng(cfg, layer, proj, F_CODES, index).integers(0, 2 ** 32, size=(rows, K * bits // 32),
                                                           dtype=np.uint32)
     s32 = rng(cfg, layer, proj, F_SCALES, index).uniform(scale_lo, scale_hi, size=(rows, K // group)).astype(np.float32)
@@ -182,7 +196,7 @@ def gen_expert_grid(cfg: int, layer: int, proj: int, E: int, rows: int, K: int,
     """3-D expert grid [E, rows, ...]; expert e is seeded by index=e, so any subset of
     experts can be regenerated on its own.  `experts` limits generation to a subset
     (the others are left zero), for oracle-side regeneration."""
-    codes = np.zeros((E, rows, K * bits // 32), np.uint32)
+    codes = np.zeros((E, rows, K * (8 if bits == "e4m3" else bits) // 32), np.uint32)
     scales = np.zeros((E, rows, K // group), np.uint16)
     biases = np.zeros((E, rows, K // group), np.uint16)
     for e in (range(E) if experts is None else experts):

@@ -150,6 +150,35 @@ def test_bit_stream_order_by_hand():
     assert orc.unpack_bits(np.array([[0x04030201]], np.uint32), 8).tolist() == [[1, 2, 3, 4]]
 
 
+def test_e4m3_decode_matches_torch_and_hand_values():
+    codes = np.arange(256)
+    ours = orc.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2          # 0x7F and 0xFF only
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0xB8] == -1.0
+    assert ours[0x08] == 2.0 ** -6 and ours[0x07] == 7 * 2.0 ** -9        # smallest normal, largest subnormal
+
+
+def test_e4m3_weights_dequantize_as_scaled_values():
+    w = synth.gen_weight(synth.CFG_TEST, 1, 0, 4, 128, bits="e4m3", bias="uniform")
+    assert w.codes.shape == (4, 32) and w.bits == 8
+    q = orc.unpack_bits(w.codes, 8)
+    assert not np.any((q & 0x7F) == 0x7F)                                  # no NaN codes generated
+    W = orc.dequant(w.codes, w.scales, w.biases, orc.E4M3)
+    s = orc.bf16_to_f64(w.scales)
+    b = orc.bf16_to_f64(w.biases)
+    v = orc.e4m3_to_f64(q)
+    assert np.array_equal(W, np.repeat(s, 64, 1) * v + np.repeat(b, 64, 1))
+    # brute force through the value table
+    x = _rand_bf16_bits(np.random.default_rng(7), (2, 128), -3, 2)
+    y, A, S = orc.project(x, w.codes, w.scales, w.biases, bits=orc.E4M3)
+    xv = orc.bf16_to_f64(x)
+    ref = np.array([[math.fsum(xv[m, k] * W[n, k] for k in range(128)) for n in range(4)] for m in range(2)])
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * A.max())
+
+
 @pytest.mark.parametrize("bits,G", [(2, 64), (3, 32), (6, 128), (8, 64), (4, 32), (4, 128)])
 def test_oracle_matches_brute_force_other_formats(bits, G):
     M, K, N = 2, 256, 5
