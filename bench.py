@@ -239,6 +239,8 @@ def main():
         torch.cuda.empty_cache()
         result["moe_35B_prefill"] = bench_moe_prefill(torch, qmm, synth, T, dev, args.prefill_reps)
         torch.cuda.empty_cache()
+        result["formats"] = bench_formats(torch, qmm, synth, T, dev, args.prefill_reps)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps, w_qkv, w_gu, bytes_step)
@@ -357,6 +359,49 @@ def bench_rope(torch, qmm, synth, T, dev, pq, reps):
         del x, q, k, v
     return {"workload": f"fused QKV + RoPE, {sh.n_q} q / {sh.n_kv} kv heads x {hd}, rotary {sh.rot}, "
                         f"K={K}; decode M=1 over a {P}-layer pool and prefill M={synth.PREFILL_M}", **out}
+
+
+def bench_formats(torch, qmm, synth, T, dev, reps):
+    """The other formats of the affine family on the 14B gate+up shape (27648 rows,
+    K=5120): decode M=1 (GB/s, over a rotating pool larger than the last-level cache) and
+    prefill M=2048 (TFLOP/s), for each code width at group 64 and for u4 at groups 32/128."""
+    sh = synth.DENSE_14B
+    K, I = sh.K, sh.I
+    rows = 2 * I
+    out = {}
+    x1 = up(torch, dev, synth.gen_x(synth.CFG_14B, 0, 0, 1, K))
+    xm = up(torch, dev, synth.gen_x(synth.CFG_14B, 0, 0, synth.PREFILL_M, K))
+    h1 = torch.empty((1, I), dtype=torch.bfloat16, device=dev)
+    hm = torch.empty((synth.PREFILL_M, I), dtype=torch.bfloat16, device=dev)
+    st = T.stream
+    for bits, G in ((2, 64), (3, 64), (4, 64), (6, 64), (8, 64), (qmm.QMM_FP8_E4M3, 64), (4, 32), (4, 128)):
+        fp8 = bits == qmm.QMM_FP8_E4M3
+        w = synth.gen_weight(synth.CFG_14B, 0, synth.PROJ_GATE_UP, rows, K, bits="e4m3" if fp8 else bits, group=G)
+        b = rows * K * (8 if fp8 else bits) // 8 + 2 * rows * (K // G) * 2
+        P = max(2, -(-768 * 2 ** 20 // b))
+        pool = pool_of(torch, dev, w, P)
+        del w
+
+        def dec(i):
+            l = i % P
+            qmm.qmm_fused_gate_up_swiglu_fmt(bits, G, x1, pool[0][l], pool[1][l], pool[2][l], h1, stream=st)
+
+        def pre(i):
+            qmm.qmm_fused_gate_up_swiglu_fmt(bits, G, xm, pool[0][0], pool[1][0], pool[2][0], hm, stream=st)
+
+        ms_d = T.per_call_ms(dec, 4 * P)
+        ms_p = T.per_call_ms(pre, reps)
+        bd = b + K * 2 + I * 2
+        fl = 2.0 * synth.PREFILL_M * rows * K
+        out[f"fp8e4m3_g{G}" if fp8 else f"u{bits}_g{G}"] = {"bits_per_weight": round(8 * b / (rows * K), 3),
+                                "decode_us": round(ms_d * 1e3, 3),
+                                "decode_GB/s": round(bd / (ms_d * 1e-3) / 1e9, 1),
+                                "prefill_us": round(ms_p * 1e3, 1),
+                                "prefill_TFLOP/s": round(fl / (ms_p * 1e-3) / 1e12, 1)}
+        del pool
+        torch.cuda.empty_cache()
+    return {"workload": f"fused gate+up+SwiGLU [{rows} x {K}] in each format: decode M=1 over a pool of "
+                        f">= 768 MB, prefill M={synth.PREFILL_M}", **out}
 
 
 def bench_step_24b(torch, qmm, synth, T, dev, n_steps):

@@ -16,12 +16,13 @@ __all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm
            "qmm_moe_gather", "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
            "qmm_moe_gather_fmt",
            "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
-           "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
+           "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_FP8_E4M3", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 
 QMM_OUT_BF16, QMM_OUT_F32 = 0, 1
 QMM_MOE_GATE_UP_SWIGLU, QMM_MOE_DOWN_COMBINE = 0, 1
+QMM_FP8_E4M3 = 0x108   # `bits` of the *_fmt calls for fp8 e4m3 codes
 STATUS = {"QMM_OK": 0, "QMM_ERR_NULL": 1, "QMM_ERR_SHAPE": 2, "QMM_ERR_ALIGN": 3, "QMM_ERR_ALIAS": 4,
           "QMM_ERR_ENUM": 5, "QMM_ERR_LAUNCH": 6}
 
@@ -138,7 +139,7 @@ def _check_weight(codes, scales, biases, rows: int, K: int, what: str = "weight"
     """The tensors must hold exactly rows x K*bits/32 words and rows x K/group bf16
     scales/biases, so the kernels never read past the end of a caller's buffer."""
     _need(K % 64 == 0 and K > 0 and K % group == 0, f"K={K} must be a positive multiple of 64 and of {group}")
-    words = K * bits // 32
+    words = K * (8 if bits == QMM_FP8_E4M3 else bits) // 32
     _need(_bytes(codes) == rows * words * 4, f"{what} codes must hold {rows} x {words} uint32")
     _need(_bytes(scales) == rows * (K // group) * 2, f"{what} scales must hold {rows} x {K // group} bf16")
     _need(_bytes(biases) == rows * (K // group) * 2, f"{what} biases must hold {rows} x {K // group} bf16")

@@ -22,7 +22,9 @@ WIDTHS = (2, 3, 4, 6, 8)
 SOURCES = ([("qmm_api.cpp", [], "qmm_api.o"), ("qmm_validate.cpp", [], "qmm_validate.o"),
             ("moe_route.hip", [], "moe_route.o")]
            + [(src, [f"-DQMM_BITS={b}"], f"{src.split('.')[0]}_b{b}.o") for src in ("gemv_u4.hip", "gemm_u4.hip")
-              for b in WIDTHS])
+              for b in WIDTHS]
+           + [(src, ["-DQMM_BITS=8", "-DQMM_FP8=1"], f"{src.split('.')[0]}_f8.o")
+              for src in ("gemv_u4.hip", "gemm_u4.hip")])
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

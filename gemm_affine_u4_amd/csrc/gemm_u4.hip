@@ -39,7 +39,8 @@ namespace qmm {
 // its kernels and launchers live in namespace qmm::b<N>.
 namespace QMM_BITS_NS {
 
-constexpr int kBits = QMM_BITS;
+constexpr int kBits = QMM_BITS;  // storage bits per code
+constexpr bool kFp8 = QMM_FP8;   // the 8-bit codes are fp8 e4m3 numbers
 // vector-memory loads of one lane's 32 codes of a K step (16-, 12- or 8-byte loads)
 constexpr int kCodeLoads = kBits / 4 + (kBits % 4 != 0 ? 1 : 0);
 
@@ -235,7 +236,15 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     const float s = bf16_bits_to_f32(r.sv);
     const float b = bf16_bits_to_f32(r.bv);
     u32x4_t v;
-    if constexpr (kBits == 4) {
+    if constexpr (kFp8) {
+      // codes 8p .. 8p+7 are the bytes of words 2p, 2p+1: two e4m3 -> fp32 per conversion
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      const uint32_t w0 = r.cv[2 * p], w1 = r.cv[2 * p + 1];
+      const f32x2_t c0 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false), c1 = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+      const f32x2_t c2 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false), c3 = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+      v = u32x4_t{pack_bf16x2(fmaf(s, c0[0], b), fmaf(s, c0[1], b)), pack_bf16x2(fmaf(s, c1[0], b), fmaf(s, c1[1], b)),
+                  pack_bf16x2(fmaf(s, c2[0], b), fmaf(s, c2[1], b)), pack_bf16x2(fmaf(s, c3[0], b), fmaf(s, c3[1], b))};
+    } else if constexpr (kBits == 4) {
       // low and high nibbles of the four bytes of word p, one v_cvt_f32_ubyte{0..3} per code
       const uint32_t w = r.cv[p];
       const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);

@@ -40,8 +40,13 @@ namespace qmm {
 // its kernels and launchers live in namespace qmm::b<N>.
 namespace QMM_BITS_NS {
 
-constexpr int kBits = QMM_BITS;
+constexpr int kBits = QMM_BITS;  // storage bits per code
+#if QMM_FP8
+static_assert(QMM_BITS == 8, "fp8 codes are 8 bits");
+using Cd = CodecE4M3;
+#else
 using Cd = Codec<kBits>;
+#endif
 constexpr int kChunkBytes = 4 * kBits;  // 32 codes
 constexpr int kMaxCplSplit16 = (kBits == 2 || kBits == 4) ? 4 : 3;
 

@@ -10,6 +10,7 @@
 using qmm::Range;
 
 static_assert(QMM_MAX_EXPERTS_PREFILL == qmm::kMaxExpertsPrefill, "routing histogram size");
+static_assert(QMM_FP8_E4M3 == qmm::kFmtFp8E4M3, "fp8 format code");
 
 namespace {
 
@@ -24,14 +25,16 @@ constexpr int64_t kGemvMaxM = 8;
 // A format of the affine family: code width and group size (the pages list u2 .. u8 at
 // group sizes 32 to 128: saragossa README, "Capabilities" and "Quantization formats").
 struct Fmt {
-  int bits;
+  int bits;        // format code passed to the kernels: 2, 3, 4, 6, 8 or QMM_FP8_E4M3
   int gshift;      // group = 32 << gshift
   int64_t group;
+  int storage;     // bits per code in memory
 };
 // The widths the kernels implement; false for others, for other group sizes, and when K
 // is not a whole number of groups.
 bool fmt_ok(int bits, int64_t group, int64_t K, Fmt* f) {
-  if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) return false;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8 && bits != QMM_FP8_E4M3) return false;
+  const int storage = bits == QMM_FP8_E4M3 ? 8 : bits;
   int gs;
   if (group == 32) gs = 0;
   else if (group == 64) gs = 1;
@@ -39,12 +42,12 @@ bool fmt_ok(int bits, int64_t group, int64_t K, Fmt* f) {
   else return false;
   if (K % group) return false;
   // the widest codes fit the decode kernel's 16-way K split up to K = 16 * 32 * 3 * 32
-  if ((bits == 3 || bits == 6 || bits == 8) && K > 49152) return false;
-  *f = {bits, gs, group};
+  if ((storage == 3 || storage == 6 || storage == 8) && K > 49152) return false;
+  *f = {bits, gs, group, storage};
   return true;
 }
-constexpr Fmt kU4G64 = {4, 1, 64};
-uint64_t code_bytes(int64_t rows, int64_t K, const Fmt& f) { return uint64_t(rows) * uint64_t(K) * f.bits / 8; }
+constexpr Fmt kU4G64 = {4, 1, 64, 4};
+uint64_t code_bytes(int64_t rows, int64_t K, const Fmt& f) { return uint64_t(rows) * uint64_t(K) * f.storage / 8; }
 uint64_t group_bytes(int64_t rows, int64_t K, const Fmt& f) { return uint64_t(rows) * uint64_t(K / f.group) * 2; }
 // One weight matrix (one expert of a grid) is addressed with 32-bit byte offsets.
 bool codes_fit(int64_t rows, int64_t K, const Fmt& f) { return code_bytes(rows, K, f) <= 0xFFFFFFFFull; }

@@ -202,6 +202,29 @@ struct CodecStream {
 };
 template <>
 struct Codec<3> : CodecStream<3> {};
+
+// fp8 e4m3 codes (8 bits each, word j = codes 4j .. 4j+3): two codes at a time become an
+// exact bf16 pair (v_cvt_scalef32_pk_bf16_fp8 with scale 1; bf16 holds every e4m3 value),
+// against the activation pairs in their natural order.
+struct CodecE4M3 {
+  static constexpr int kWords = 8;
+  static __device__ __forceinline__ void permute(const uint32_t d[16], uint32_t xp[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xp[i] = d[i];
+  }
+  static __device__ __forceinline__ float dot_q(const uint32_t (&w)[8], const uint32_t xp[16], float,
+                                                uint32_t) {
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, false),
+                                          __builtin_bit_cast(bf16x2_t, xp[2 * j]), d, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, true),
+                                          __builtin_bit_cast(bf16x2_t, xp[2 * j + 1]), d, false);
+    }
+    return d;
+  }
+};
 template <>
 struct Codec<6> : CodecStream<6> {};
 

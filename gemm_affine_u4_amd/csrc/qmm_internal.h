@@ -9,7 +9,16 @@ namespace qmm {
 // from the same sources and live in namespace qmm::b<bits>.
 #define QMM_CAT2(a, b) a##b
 #define QMM_CAT(a, b) QMM_CAT2(a, b)
+#ifndef QMM_FP8
+#define QMM_FP8 0
+#endif
+#if QMM_FP8
+#define QMM_BITS_NS f8
+#else
 #define QMM_BITS_NS QMM_CAT(b, QMM_BITS)
+#endif
+// Format code of fp8 e4m3 codes in GemvArgs/GemmArgs::bits (QMM_FP8_E4M3 of the C ABI).
+constexpr int kFmtFp8E4M3 = 0x108;
 
 enum Epilogue : int { EPI_LINEAR = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_ROPE = 3 };
 
@@ -52,7 +61,7 @@ struct GemvArgs {
   int64_t E;               // experts in the grid
   int topk;
   int f32_out;
-  int bits;                // code width (2, 3, 4, 6 or 8)
+  int bits;                // code width (2, 3, 4, 6 or 8) or kFmtFp8E4M3
   int gshift;              // group size = 32 << gshift (scales/biases per 32, 64 or 128 inputs)
   RopeArgs rope;           // EPI_ROPE only
 };
@@ -77,7 +86,7 @@ struct GemmArgs {
   const int32_t* moe_pairs;    // [pairs] bucketed pair indices (token * topk + slot)
   const float* moe_w;          // stage 2: combine weight of each pair; null in stage 1
   int64_t moe_div;             // topk in stage 1 (x row of a pair), 1 in stage 2
-  int bits;                    // code width
+  int bits;                    // code width or kFmtFp8E4M3
   int gshift;                  // group size = 32 << gshift
   RopeArgs rope;               // EPI_ROPE only
 };
@@ -98,6 +107,7 @@ QMM_WIDTH_LAUNCHERS(b3)
 QMM_WIDTH_LAUNCHERS(b4)
 QMM_WIDTH_LAUNCHERS(b6)
 QMM_WIDTH_LAUNCHERS(b8)
+QMM_WIDTH_LAUNCHERS(f8)
 // Gathered GEMM of the routed experts over a batch (4-bit codes): m_tiles = bound on the
 // tile table.
 namespace b4 {
@@ -111,6 +121,7 @@ int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
     case 4: return b4::CALL;                    \
     case 6: return b6::CALL;                    \
     case 8: return b8::CALL;                    \
+    case kFmtFp8E4M3: return f8::CALL;          \
     default: return 2;                          \
   }
 inline int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {

@@ -71,6 +71,8 @@ extern "C" {
 #define QMM_MAX_K 65536
 #define QMM_MAX_TOPK 64
 #define QMM_MAX_EXPERTS_PREFILL 4096
+/* `bits` of the *_fmt calls for fp8 e4m3 codes (8 bits each) */
+#define QMM_FP8_E4M3 0x108
 
 enum qmm_status {
   QMM_OK = 0,
@@ -250,9 +252,13 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K,
  * little-endian bit stream (code k = stream bits [bits*k, bits*k + bits), bit j of the
  * stream = bit j % 32 of word j / 32; at 4 bits this is the nibble order at the top of
  * this file); scales/biases [rows][K/group_size] bf16; w = scale*q + bias, q in
- * 0 .. 2^bits - 1.  Supported: bits 2, 3, 4, 6, 8; group_size 32, 64 or 128 with K a
- * multiple of 64 and of group_size; K <= 49152 for bits 3, 6, 8 (65536 otherwise).
- * Anything else is QMM_ERR_SHAPE.
+ * 0 .. 2^bits - 1.  bits = QMM_FP8_E4M3: 8-bit codes that are fp8 e4m3 numbers (sign,
+ * 4 exponent bits with bias 7, 3 fraction bits, subnormals, S.1111.111 = NaN) and
+ * w = scale * e4m3(q) + bias (the pages list fp8 e4m3 with the integer widths without its
+ * scaling; this affine form is the reading taken; codes are assumed not NaN).
+ * Supported: bits 2, 3, 4, 6, 8, QMM_FP8_E4M3; group_size 32, 64 or 128 with K a
+ * multiple of 64 and of group_size; K <= 49152 for 3-, 6- and 8-bit codes (65536
+ * otherwise).  Anything else is QMM_ERR_SHAPE.
  */
 int qmm_linear_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, int64_t K,
                    const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,

@@ -131,7 +131,8 @@ def _linear_fmt(bits=4, group=64, K=512, **kw):
 
 
 def test_format_validation():
-    for bits, group, K in [(5, 64, 512), (4, 16, 512), (4, 96, 576), (4, 256, 512), (4, 128, 320), (1, 64, 512)]:
+    for bits, group, K in [(5, 64, 512), (4, 16, 512), (4, 96, 576), (4, 256, 512), (4, 128, 320), (1, 64, 512),
+                           (qmm.QMM_FP8_E4M3, 64, 49216), (8, 64, 49216), (0x107, 64, 512)]:
         assert _linear_fmt(bits, group, K) == S["QMM_ERR_SHAPE"], (bits, group, K)
     # the plain call is the (4, 64) format: the same validation result for a bad pointer
     assert _linear_fmt(4, 64, x=A + 2) == S["QMM_ERR_ALIGN"] == _linear(x=A + 2)
