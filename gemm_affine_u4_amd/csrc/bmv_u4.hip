@@ -1,0 +1,307 @@
+// Small-batch (2 <= M <= 32) kernel for the u4 group-64 affine projections on gfx950.
+//
+// Between decode (one activation row: weight-bandwidth bound, the GEMV) and prefill
+// (hundreds of rows: matrix bound, the LDS-dequant GEMM) the work is still one pass over
+// the weights, but every weight now meets up to 16 activation rows per pass.  The GEMV's
+// dot2 chain would need every lane to hold 16 activation rows; here the matrix cores
+// take the activations instead ("Sanctum-MLX", latency testing: prefill is the matmul
+// regime) while the weights stream at the GEMV's rate.
+//
+// What is computed: y[m][n] = sum_k x[m][k] * (s[n, k/64] * q[n, k] + b[n, k/64]), with the
+// fused-QKV split and the SwiGLU epilogue of "The Cathedral Doubled Itself" (the two
+// fusions), for up to 16 activation rows per block (grid.y covers more).
+//
+// Layout of the work:
+//   * a unit is 16 weight rows (QKV / linear: 16 consecutive rows; SwiGLU: 8 gate rows
+//     and their 8 up rows); a block of 8 waves walks units with a grid stride, wave s
+//     owning the K slice [s*K/8, (s+1)*K/8) of every unit;
+//   * the unit's packed codes and its scales and biases go global -> LDS directly
+//     (buffer_load ... lds, 1 KB contiguous per wave instruction), double-buffered: unit
+//     i+1 is requested before unit i is multiplied;
+//   * the activations of a wave's slice stay in registers for the whole kernel as
+//     v_mfma_f32_16x16x32_bf16 operands (16 rows x 32 inputs per instruction), permuted to
+//     the nibble-pair order of the codes;
+//   * per 64-input group a lane turns 16 codes of its column into exact bf16 (128 + q)
+//     pairs (no rounding of any weight), two MFMAs give D[m][n] = sum x (128 + q) over the
+//     group, and the group's scale and bias enter in fp32 as
+//     y += s * (D - 128 * xs) + b * xs, with xs[m] = sum x over the group (an MFMA against
+//     ones);
+//   * the 8 slice partials of a unit meet in LDS and wave 0 adds them in slice order.
+// Every output depends only on its own activation row, K and the unit layout, so a row's
+// result does not depend on the other rows of the batch or on M.
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace bmv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kSlices = 8;  // waves per block, one K slice each
+constexpr int kUnit = 16;   // weight rows per unit (the MFMA's columns)
+constexpr int kRows = 16;   // activation rows per block (the MFMA's rows)
+
+// LDS of one unit buffer at K = 512 * GPS (GPS = groups per slice, even):
+//   codes [16 rows][K/32 chunks of 16 B]; chunk c of row r sits in slot c ^ (r & 15), so
+//   the 16 rows a wave reads at one chunk hit 16 different bank groups;
+//   scales [16][K/64] bf16, then biases [16][K/64] bf16, each padded to whole KB.
+template <int GPS>
+struct Layout {
+  static constexpr int K = 512 * GPS;
+  static constexpr int row_bytes = K / 2;
+  static constexpr int code_bytes = kUnit * row_bytes;  // 4 KB * GPS
+  static constexpr int sb_row = K / 32;                 // bytes of bf16 scales per row
+  static constexpr int sb_bytes = kUnit * sb_row;
+  static constexpr int sb_pad = (sb_bytes + 1023) / 1024 * 1024;
+  static constexpr int buf_bytes = code_bytes + 2 * sb_pad;
+  static constexpr int code_dma = code_bytes / 1024;  // 1 KB wave instructions per unit
+  static constexpr int sb_dma = sb_pad / 1024;
+  // wave s requests code instructions s, s + 8, ... (GPS/2 of them) and one instruction
+  // of scales (s < sb_dma) or biases (s - sb_dma < sb_dma), or a padding load
+  static constexpr int code_per_wave = code_dma / kSlices;
+  static constexpr int dma_per_wave = code_per_wave + 1;
+  static constexpr int red_off = 2 * buf_bytes;          // slice partials [8][64 lanes][4]
+  static constexpr int dump_off = red_off + kSlices * 64 * 16;  // target of padding loads
+  static constexpr int lds_bytes = dump_off + 1024;
+  static_assert(code_dma % kSlices == 0, "GPS is even");
+  static_assert(2 * sb_dma <= kSlices, "one scale or bias instruction per wave");
+  static_assert(code_bytes % 1024 == 0, "a unit's codes are whole KB");
+  static_assert(lds_bytes <= 160 * 1024, "LDS");
+};
+
+// Global row of LDS row r of unit u (past the end: the last real row, never stored).
+template <int EPI>
+__device__ __forceinline__ int64_t unit_row(const GemvArgs& a, int64_t u, int r) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    int64_t p = u * (kUnit / 2) + (r & 7);
+    if (p >= a.I) p = a.I - 1;
+    return r < 8 ? p : a.I + p;
+  } else {
+    const int64_t n = u * kUnit + r;
+    return n < a.rows ? n : a.rows - 1;
+  }
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and its LDS
+// operations are done, then meet the other waves (one asm block: the compiler's own
+// barrier would also wait for the unit requested ahead).
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int GPS, int EPI>
+__global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units) {
+  using L = Layout<GPS>;
+  constexpr int K = L::K;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::lds_bytes];
+
+  const int lane = threadIdx.x & 63;
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // K slice of this wave
+  const int col = lane & 15;  // MFMA column: LDS row of the unit
+  const int kb = lane >> 4;   // 8-input block of the MFMA's 32 inputs
+  const int64_t mb = blockIdx.y;
+  const int64_t rows_here = M - mb * kRows < kRows ? M - mb * kRows : kRows;
+  const uint64_t nrows = uint64_t(a.rows);
+
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes, nrows * uint64_t(L::row_bytes));
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, nrows * uint64_t(L::sb_row));
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases, nrows * uint64_t(L::sb_row));
+
+  // ---- unit -> LDS ------------------------------------------------------------------
+  // Code instruction i = 8t + s (lane L: byte 1024 i + 16 L of the unit's codes, i.e. row
+  // r, slot c) reads chunk c ^ (r & 15) of row r; the row and the in-row byte offset of
+  // each of the wave's instructions are fixed for the kernel.
+  int crow[L::code_per_wave];
+  uint32_t cofs[L::code_per_wave];
+#pragma unroll
+  for (int t = 0; t < L::code_per_wave; ++t) {
+    const uint32_t o = 1024u * uint32_t(t * kSlices + s) + 16u * uint32_t(lane);
+    const int r = int(o / L::row_bytes);
+    const uint32_t c = (o % L::row_bytes) / 16u;
+    crow[t] = r;
+    cofs[t] = 16u * (c ^ uint32_t(r & 15));
+  }
+  // scale/bias instruction of this wave: region byte 1024 j + 16 L
+  const bool sb_bias = s >= L::sb_dma;
+  const int sb_j = sb_bias ? s - L::sb_dma : s;
+  const bool sb_any = s < 2 * L::sb_dma;
+  const uint32_t sb_o = 1024u * uint32_t(sb_j) + 16u * uint32_t(lane);
+  const int sb_r = int(sb_o / L::sb_row);
+  const uint32_t sb_in = sb_o % L::sb_row;
+  const __amdgpu_buffer_rsrc_t sbr = sb_bias ? br : sr;
+  auto request = [&](int64_t u, int buf) {
+    uint8_t* base = lds + buf * L::buf_bytes;
+#pragma unroll
+    for (int t = 0; t < L::code_per_wave; ++t) {
+      const uint32_t off = uint32_t(unit_row<EPI>(a, u, crow[t])) * uint32_t(L::row_bytes) + cofs[t];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          cr, (__attribute__((address_space(3))) void*)(base + 1024 * (t * kSlices + s)), 16, off, 0, 0, 0);
+    }
+    // past the scales (padding of the region) or no instruction for this wave: a load
+    // beyond every buffer returns zero
+    const uint32_t off = sb_any && sb_o < uint32_t(L::sb_bytes)
+                             ? uint32_t(unit_row<EPI>(a, u, sb_r)) * uint32_t(L::sb_row) + sb_in
+                             : 0xFFFFFFF0u;
+    uint8_t* dst = sb_any ? base + L::code_bytes + (sb_bias ? L::sb_pad : 0) + 1024 * sb_j : lds + L::dump_off;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sbr, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+  };
+
+  int64_t u = blockIdx.x;
+  if (u >= units) return;
+  request(u, 0);
+
+  // ---- activations of this slice: MFMA operands, permuted to the nibble-pair order ----
+  // Operand lane (row m = lane % 16, block kb) of group g, MFMA h holds inputs
+  // 64 G + 16 kb + 8 h .. +7 with G = s*GPS + g: the 8 codes its column's lane decodes
+  // from code word h of that lane's 16 codes.
+  bf16x8_t xa[GPS][2];
+  {
+    const uint16_t* xb = a.x + mb * kRows * K;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, uint64_t(rows_here) * K * 2);
+#pragma unroll
+    for (int g = 0; g < GPS; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t k0 = uint32_t(64 * (s * GPS + g) + 16 * kb + 8 * h);
+        const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t(col) * K + k0) * 2u, 0, 0);
+        const u32x4_t p = {__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
+                           __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
+        xa[g][h] = __builtin_bit_cast(bf16x8_t, p);
+      }
+  }
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const uint32_t magic = in_vgpr(kMagicPair);
+  float* red = reinterpret_cast<float*>(lds + L::red_off);
+
+  for (int it = 0;; ++it) {
+    const int buf = it & 1;
+    const int64_t un = u + gridDim.x;
+    const bool more = un < units;
+    if (more) {
+      request(un, buf ^ 1);
+      wait_loads_barrier<L::dma_per_wave>();
+    } else {
+      wait_loads_barrier<0>();
+    }
+
+    // ---- this wave's slice of unit u ----------------------------------------------------
+    const uint8_t* bb = lds + buf * L::buf_bytes;
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(bb + L::code_bytes) + col * (L::sb_row / 2);
+    const uint16_t* bi = reinterpret_cast<const uint16_t*>(bb + L::code_bytes + L::sb_pad) + col * (L::sb_row / 2);
+    f32x4_t y = {};
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+      const int G = s * GPS + g;
+      // codes 16 kb .. 16 kb + 15 of group G of this lane's column: half (kb & 1) of chunk
+      // 2G + kb/2
+      const uint32_t c = uint32_t(2 * G + (kb >> 1));
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bb + col * L::row_bytes + 16 * (c ^ uint32_t(col)) + 8 * (kb & 1));
+      const float sv = bf16_bits_to_f32(sc[G]);
+      const float bv = bf16_bits_to_f32(bi[G]);
+      // xs[r] = sum of the group's 64 inputs of row 4 kb + r (the MFMA against ones puts
+      // that row's sum in every column; recomputed per unit, the matrix pipe is idle)
+      f32x4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g][0], ones, f32x4_t{}, 0, 0, 0);
+      xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g][1], ones, xs, 0, 0, 0);
+      f32x4_t d = {};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t q = {nib_pair(w[h], 0, magic), nib_pair(w[h], 1, magic), nib_pair(w[h], 2, magic),
+                           nib_pair(w[h], 3, magic)};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g][h], __builtin_bit_cast(bf16x8_t, q), d, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float dq = fmaf(-128.0f, xs[r], d[r]);  // sum x q (exact 0 for all-zero codes)
+        y[r] = fmaf(sv, dq, y[r]);
+        y[r] = fmaf(bv, xs[r], y[r]);
+      }
+    }
+    *reinterpret_cast<f32x4_t*>(red + (s * 64 + lane) * 4) = y;
+    __syncthreads();
+
+    // ---- wave 0: slices in order, epilogue ---------------------------------------------
+    if (s == 0) {
+      f32x4_t t = *reinterpret_cast<const f32x4_t*>(red + lane * 4);
+#pragma unroll
+      for (int j = 1; j < kSlices; ++j) {
+        const f32x4_t p = *reinterpret_cast<const f32x4_t*>(red + (j * 64 + lane) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] += p[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mb * kRows + 4 * kb + r;  // activation row of t[r]
+        const bool mrow = 4 * kb + r < rows_here;
+        if constexpr (EPI == EPI_SWIGLU) {
+          const float up = __shfl_xor(t[r], 8);  // column col + 8: the up row of the pair
+          const int64_t p = u * (kUnit / 2) + col;
+          if (mrow && col < 8 && p < a.I) store_out(a.out0, m * a.n_out + p, silu_times(t[r], up), a.f32_out);
+        } else {
+          const int64_t n = u * kUnit + col;
+          if (mrow && n < a.rows) {
+            float v = t[r];
+            if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
+            if constexpr (EPI == EPI_QKV) {
+              if (n < a.q_out) {
+                store_out(a.out0, m * a.q_out + n, v, a.f32_out);
+              } else if (n < a.q_out + a.kv_out) {
+                store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
+              } else {
+                store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
+              }
+            } else {
+              store_out(a.out0, m * a.n_out + n, v, a.f32_out);
+            }
+          }
+        }
+      }
+    }
+    if (!more) break;
+    u = un;
+  }
+}
+
+// Instantiated K = 512 * GPS.
+#define QMM_BMV_GPS(X) X(2) X(4) X(6) X(8) X(10) X(12) X(14) X(16)
+
+}  // namespace bmv
+
+bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
+  if (a.bits != 4 || a.gshift != 1 || M < 2 || M > kBmvMaxM || a.K % 512) return false;
+  if (epi != EPI_LINEAR && epi != EPI_QKV && epi != EPI_SWIGLU) return false;
+  switch (a.K / 512) {
+#define QMM_BMV_CASE(G) case G:
+    QMM_BMV_GPS(QMM_BMV_CASE)
+#undef QMM_BMV_CASE
+      return true;
+    default:
+      return false;
+  }
+}
+
+int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {
+  if (!bmv_supports(epi, a, M)) return 2;
+  const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)
+                                          : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
+  constexpr int64_t kCUs = 256;
+  const dim3 grid{unsigned(units < kCUs ? units : kCUs), unsigned((M + bmv::kRows - 1) / bmv::kRows), 1u};
+  const dim3 block{64u * bmv::kSlices, 1u, 1u};
+  switch (a.K / 512) {
+#define QMM_BMV_CASE(G)                                                                       \
+  case G:                                                                                     \
+    if (epi == EPI_LINEAR) bmv::bmv_u4_kernel<G, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units); \
+    else if (epi == EPI_QKV) bmv::bmv_u4_kernel<G, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);  \
+    else bmv::bmv_u4_kernel<G, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);                 \
+    break;
+    QMM_BMV_GPS(QMM_BMV_CASE)
+#undef QMM_BMV_CASE
+    default:
+      return 2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+}  // namespace qmm

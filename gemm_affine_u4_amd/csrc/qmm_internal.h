@@ -131,6 +131,13 @@ inline int launch_moe_gate_up(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a
 inline int launch_moe_down(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_moe_down(a, s)) }
 inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_gemm(epi, a, s)) }
 
+// Small batches (2 <= M <= kBmvMaxM) of the 4-bit group-64 projections whose K is a
+// multiple of 512 up to 8192: one pass over the weights, the activations on the matrix
+// cores (bmv_u4.hip).  Linear, fused QKV and fused gate+up+SwiGLU.
+constexpr int64_t kBmvMaxM = 32;
+bool bmv_supports(int epi, const GemvArgs& a, int64_t M);
+int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
+
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
 constexpr int kMoeTileRows = 256;        // pairs per gathered GEMM tile (the GEMM's kBM)
