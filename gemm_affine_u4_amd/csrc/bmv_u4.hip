@@ -16,8 +16,8 @@
 //     and their 8 up rows); a block of 8 waves walks units with a grid stride, wave s
 //     owning the K slice [s*K/8, (s+1)*K/8) of every unit;
 //   * the unit's packed codes and its scales and biases go global -> LDS directly
-//     (buffer_load ... lds, 1 KB contiguous per wave instruction), double-buffered: unit
-//     i+1 is requested before unit i is multiplied;
+//     (buffer_load ... lds, 1 KB contiguous per wave instruction) into a ring of 2 to 4
+//     unit buffers: while unit i is multiplied, the next ones are in flight;
 //   * the activations of a wave's slice stay in registers for the whole kernel as
 //     v_mfma_f32_16x16x32_bf16 operands (16 rows x 32 inputs per instruction), permuted to
 //     the nibble-pair order of the codes;
@@ -26,7 +26,8 @@
 //     group, and the group's scale and bias enter in fp32 as
 //     y += s * (D - 128 * xs) + b * xs, with xs[m] = sum x over the group (an MFMA against
 //     ones);
-//   * the 8 slice partials of a unit meet in LDS and wave 0 adds them in slice order.
+//   * the 8 slice partials of a unit meet in LDS and are added in slice order, each
+//     output by one lane of one of the 8 waves.
 // Every output depends only on its own activation row, K and the unit layout, so a row's
 // result does not depend on the other rows of the batch or on M.
 #include "qmm_device.h"
@@ -62,25 +63,27 @@ struct Layout {
   // of scales (s < sb_dma) or biases (s - sb_dma < sb_dma), or a padding load
   static constexpr int code_per_wave = code_dma / kSlices;
   static constexpr int dma_per_wave = code_per_wave + 1;
-  static constexpr int red_off = 2 * buf_bytes;          // slice partials [8][64 lanes][4]
+  // unit buffers: as many as fit (up to 4), so up to nbuf - 1 units are in flight
+  static constexpr int fixed = kSlices * 64 * 16 + 1024;
+  static constexpr int nbuf = (160 * 1024 - fixed) / buf_bytes < 4 ? (160 * 1024 - fixed) / buf_bytes : 4;
+  static constexpr int red_off = nbuf * buf_bytes;       // slice partials [8][64 lanes][4]
   static constexpr int dump_off = red_off + kSlices * 64 * 16;  // target of padding loads
   static constexpr int lds_bytes = dump_off + 1024;
   static_assert(code_dma % kSlices == 0, "GPS is even");
   static_assert(2 * sb_dma <= kSlices, "one scale or bias instruction per wave");
   static_assert(code_bytes % 1024 == 0, "a unit's codes are whole KB");
-  static_assert(lds_bytes <= 160 * 1024, "LDS");
+  static_assert(nbuf >= 2 && lds_bytes <= 160 * 1024, "LDS");
 };
 
 // Global row of LDS row r of unit u (past the end: the last real row, never stored).
+// 32-bit: the codes of a weight are below 4 GiB, so every row index and offset fits.
 template <int EPI>
-__device__ __forceinline__ int64_t unit_row(const GemvArgs& a, int64_t u, int r) {
+__device__ __forceinline__ uint32_t unit_row(uint32_t rows, uint32_t I, uint32_t u, int r) {
   if constexpr (EPI == EPI_SWIGLU) {
-    int64_t p = u * (kUnit / 2) + (r & 7);
-    if (p >= a.I) p = a.I - 1;
-    return r < 8 ? p : a.I + p;
+    const uint32_t p = min(u * (kUnit / 2) + uint32_t(r & 7), I - 1);
+    return r < 8 ? p : I + p;
   } else {
-    const int64_t n = u * kUnit + r;
-    return n < a.rows ? n : a.rows - 1;
+    return min(u * kUnit + uint32_t(r), rows - 1);
   }
 }
 
@@ -90,6 +93,16 @@ __device__ __forceinline__ int64_t unit_row(const GemvArgs& a, int64_t u, int r)
 template <int N>
 __device__ __forceinline__ void wait_loads_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// The same with N = ahead * PER (ahead < 4, block-uniform).
+template <int PER>
+__device__ __forceinline__ void wait_units_barrier(int ahead) {
+  switch (ahead) {
+    case 0: wait_loads_barrier<0>(); break;
+    case 1: wait_loads_barrier<PER>(); break;
+    case 2: wait_loads_barrier<2 * PER>(); break;
+    default: wait_loads_barrier<3 * PER>(); break;
+  }
 }
 
 template <int GPS, int EPI>
@@ -105,6 +118,7 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
   const int64_t mb = blockIdx.y;
   const int64_t rows_here = M - mb * kRows < kRows ? M - mb * kRows : kRows;
   const uint64_t nrows = uint64_t(a.rows);
+  const uint32_t rows32 = uint32_t(a.rows), I32 = uint32_t(a.I);
 
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes, nrows * uint64_t(L::row_bytes));
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, nrows * uint64_t(L::sb_row));
@@ -136,14 +150,14 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
     uint8_t* base = lds + buf * L::buf_bytes;
 #pragma unroll
     for (int t = 0; t < L::code_per_wave; ++t) {
-      const uint32_t off = uint32_t(unit_row<EPI>(a, u, crow[t])) * uint32_t(L::row_bytes) + cofs[t];
+      const uint32_t off = unit_row<EPI>(rows32, I32, uint32_t(u), crow[t]) * uint32_t(L::row_bytes) + cofs[t];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           cr, (__attribute__((address_space(3))) void*)(base + 1024 * (t * kSlices + s)), 16, off, 0, 0, 0);
     }
     // past the scales (padding of the region) or no instruction for this wave: a load
     // beyond every buffer returns zero
     const uint32_t off = sb_any && sb_o < uint32_t(L::sb_bytes)
-                             ? uint32_t(unit_row<EPI>(a, u, sb_r)) * uint32_t(L::sb_row) + sb_in
+                             ? unit_row<EPI>(rows32, I32, uint32_t(u), sb_r) * uint32_t(L::sb_row) + sb_in
                              : 0xFFFFFFF0u;
     uint8_t* dst = sb_any ? base + L::code_bytes + (sb_bias ? L::sb_pad : 0) + 1024 * sb_j : lds + L::dump_off;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sbr, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
@@ -151,7 +165,11 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
 
   int64_t u = blockIdx.x;
   if (u >= units) return;
-  request(u, 0);
+  const int64_t stride = gridDim.x;
+  // units u, u + stride, ..., u + (nbuf - 2) stride into buffers 0 .. nbuf - 2
+#pragma unroll
+  for (int b = 0; b < L::nbuf - 1; ++b)
+    if (u + b * stride < units) request(u + b * stride, b);
 
   // ---- activations of this slice: MFMA operands, permuted to the nibble-pair order ----
   // Operand lane (row m = lane % 16, block kb) of group g, MFMA h holds inputs
@@ -177,15 +195,13 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
   float* red = reinterpret_cast<float*>(lds + L::red_off);
 
   for (int it = 0;; ++it) {
-    const int buf = it & 1;
-    const int64_t un = u + gridDim.x;
-    const bool more = un < units;
-    if (more) {
-      request(un, buf ^ 1);
-      wait_loads_barrier<L::dma_per_wave>();
-    } else {
-      wait_loads_barrier<0>();
-    }
+    const int buf = it % L::nbuf;
+    // request the unit nbuf - 1 steps ahead into the buffer freed by the previous step,
+    // then wait for this unit (the later units' loads may stay in flight)
+    const int64_t ua = u + (L::nbuf - 1) * stride;
+    if (ua < units) request(ua, (it + L::nbuf - 1) % L::nbuf);
+    const int64_t later = (units - 1 - u) / stride;  // units after u for this block
+    wait_units_barrier<L::dma_per_wave>(int(later < L::nbuf - 1 ? later : L::nbuf - 1));
 
     // ---- this wave's slice of unit u ----------------------------------------------------
     const uint8_t* bb = lds + buf * L::buf_bytes;
@@ -222,45 +238,50 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
     *reinterpret_cast<f32x4_t*>(red + (s * 64 + lane) * 4) = y;
     __syncthreads();
 
-    // ---- wave 0: slices in order, epilogue ---------------------------------------------
-    if (s == 0) {
-      f32x4_t t = *reinterpret_cast<const f32x4_t*>(red + lane * 4);
+    // ---- the 8 slice partials in slice order, epilogue: split over the waves -----------
+    // red[j][l][r] is slice j's partial of activation row 4 (l / 16) + r, column l % 16.
+    auto slice_sum = [&](int l, int r) {
+      float t = 0.f;
 #pragma unroll
-      for (int j = 1; j < kSlices; ++j) {
-        const f32x4_t p = *reinterpret_cast<const f32x4_t*>(red + (j * 64 + lane) * 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] += p[r];
+      for (int j = 0; j < kSlices; ++j) t += red[(j * 64 + l) * 4 + r];
+      return t;
+    };
+    if constexpr (EPI == EPI_SWIGLU) {
+      // 8 gate columns x 16 rows: wave s, lane < 16 takes gate column g % 8 of block g / 8
+      // (g = (16 s + lane) / 4) at r = lane % 4, with its up column 8 further
+      if (lane < 16) {
+        const int g = (16 * s + lane) >> 2, r = lane & 3;
+        const int l = (g & 7) + 16 * (g >> 3);
+        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
+        const int64_t p = u * (kUnit / 2) + (l & 15);
+        if (4 * (l >> 4) + r < rows_here && p < a.I)
+          store_out(a.out0, m * a.n_out + p, silu_times(slice_sum(l, r), slice_sum(l + 8, r)), a.f32_out);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = mb * kRows + 4 * kb + r;  // activation row of t[r]
-        const bool mrow = 4 * kb + r < rows_here;
-        if constexpr (EPI == EPI_SWIGLU) {
-          const float up = __shfl_xor(t[r], 8);  // column col + 8: the up row of the pair
-          const int64_t p = u * (kUnit / 2) + col;
-          if (mrow && col < 8 && p < a.I) store_out(a.out0, m * a.n_out + p, silu_times(t[r], up), a.f32_out);
-        } else {
-          const int64_t n = u * kUnit + col;
-          if (mrow && n < a.rows) {
-            float v = t[r];
-            if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
-            if constexpr (EPI == EPI_QKV) {
-              if (n < a.q_out) {
-                store_out(a.out0, m * a.q_out + n, v, a.f32_out);
-              } else if (n < a.q_out + a.kv_out) {
-                store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
-              } else {
-                store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
-              }
+    } else {
+      // 16 columns x 16 rows: wave s, lane < 32 takes partial lane 8 s + lane / 4, r = lane % 4
+      if (lane < 32) {
+        const int l = 8 * s + (lane >> 2), r = lane & 3;
+        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
+        const int64_t n = u * kUnit + (l & 15);
+        if (4 * (l >> 4) + r < rows_here && n < a.rows) {
+          float v = slice_sum(l, r);
+          if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
+          if constexpr (EPI == EPI_QKV) {
+            if (n < a.q_out) {
+              store_out(a.out0, m * a.q_out + n, v, a.f32_out);
+            } else if (n < a.q_out + a.kv_out) {
+              store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
             } else {
-              store_out(a.out0, m * a.n_out + n, v, a.f32_out);
+              store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
             }
+          } else {
+            store_out(a.out0, m * a.n_out + n, v, a.f32_out);
           }
         }
       }
     }
-    if (!more) break;
-    u = un;
+    u += stride;
+    if (u >= units) break;
   }
 }
 
