@@ -126,7 +126,7 @@ class Timer:
 def main():
     args = _args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 (no multi-GPU path is built)",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
 
@@ -231,6 +231,7 @@ def main():
     if not args.headline_only:
         result["qkv_rope"] = bench_rope(torch, qmm, synth, T, dev, pq, args.prefill_reps)
         result["prefill_gemm"] = bench_prefill(torch, qmm, synth, T, dev, pq, pg, args.prefill_reps)
+        result["small_batch"] = bench_small_batch(torch, qmm, synth, T, dev, pq, pg)
         del pq, pg
         torch.cuda.empty_cache()
         result["decode_24B_step"] = bench_step_24b(torch, qmm, synth, T, dev, args.step24_steps)
@@ -318,6 +319,34 @@ def bench_prefill(torch, qmm, synth, T, dev, pq, pg, reps):
             "fused_gate_up": rec(ms_gu, fl_gu, "gemm_u4_kernel<SWIGLU>"),
             "context_torch_bf16_matmul": {"qkv_shape": rec(ms_dq, fl_qkv, "torch.matmul bf16 (hipBLASLt)"),
                                           "gate_up_shape": rec(ms_dg, fl_gu, "torch.matmul bf16 (hipBLASLt)")}}
+
+
+def bench_small_batch(torch, qmm, synth, T, dev, pq, pg):
+    """Decode of a small batch (M activation rows) on the 14B layer: fused QKV and fused
+    gate+up+SwiGLU over the rotating weight pool, per M; M = 1 is the GEMV, 2..32 the
+    small-batch kernel, above it the prefill GEMM."""
+    sh = synth.DENSE_14B
+    K, I = sh.K, sh.I
+    P = pq[0].shape[0]
+    st = T.stream
+    wbytes = (sh.qkv_rows + 2 * I) * (K // 2 + (K // 64) * 4)
+    out = {}
+    for M in (1, 2, 4, 8, 16, 32, 64):
+        x = up(torch, dev, synth.gen_x(synth.CFG_14B, 0, 0, M, K))
+        q = torch.empty((M, sh.q_out), dtype=torch.bfloat16, device=dev)
+        k = torch.empty((M, sh.kv_out), dtype=torch.bfloat16, device=dev)
+        v = torch.empty((M, sh.kv_out), dtype=torch.bfloat16, device=dev)
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+        ms_q = T.per_call_ms(lambda i: qmm.qmm_fused_qkv(x, pq[0][i % P], pq[1][i % P], pq[2][i % P], q, k, v,
+                                                         stream=st), 2 * P)
+        ms_g = T.per_call_ms(lambda i: qmm.qmm_fused_gate_up_swiglu(x, pg[0][i % P], pg[1][i % P], pg[2][i % P], h,
+                                                                    stream=st), 2 * P)
+        us = (ms_q + ms_g) * 1e3
+        out[f"M={M}"] = {"qkv_us": round(ms_q * 1e3, 2), "gate_up_us": round(ms_g * 1e3, 2),
+                         "weights_GB/s": round(wbytes / (us * 1e-6) / 1e9, 1),
+                         "kernel": "gemv" if M == 1 else ("bmv" if M <= 32 else "gemm")}
+    return {"workload": "14B layer decode of M sequences: fused QKV [7168 x 5120] + fused gate+up+SwiGLU "
+                        "[27648 x 5120], u4 g64, rotating 48-layer pool", **out}
 
 
 def bench_rope(torch, qmm, synth, T, dev, pq, reps):
