@@ -13,8 +13,8 @@
 //
 // Layout of the work:
 //   * a unit is 16 weight rows (QKV / linear: 16 consecutive rows; SwiGLU: 8 gate rows
-//     and their 8 up rows); a block of 8 waves walks units with a grid stride, wave s
-//     owning the K slice [s*K/8, (s+1)*K/8) of every unit;
+//     and their 8 up rows); a block of S waves walks units with a grid stride, wave s
+//     owning the K slice [s*K/S, (s+1)*K/S) of every unit;
 //   * the unit's packed codes and its scales and biases go global -> LDS directly
 //     (buffer_load ... lds, 1 KB contiguous per wave instruction) into a ring of 2 to 4
 //     unit buffers: while unit i is multiplied, the next ones are in flight;
@@ -26,8 +26,8 @@
 //     group, and the group's scale and bias enter in fp32 as
 //     y += s * (D - 128 * xs) + b * xs, with xs[m] = sum x over the group (an MFMA against
 //     ones);
-//   * the 8 slice partials of a unit meet in LDS and are added in slice order, each
-//     output by one lane of one of the 8 waves.
+//   * the slice partials of a unit meet in LDS and are added in slice order, each output
+//     by one lane of one of the waves.
 // Every output depends only on its own activation row, K and the unit layout, so a row's
 // result does not depend on the other rows of the batch or on M.
 #include "qmm_device.h"
@@ -40,17 +40,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kSlices = 8;  // waves per block, one K slice each
 constexpr int kUnit = 16;   // weight rows per unit (the MFMA's columns)
 constexpr int kRows = 16;   // activation rows per block (the MFMA's rows)
 
-// LDS of one unit buffer at K = 512 * GPS (GPS = groups per slice, even):
+// LDS of one unit buffer for S waves (K slices) of GPS groups each, K = 64 * S * GPS:
 //   codes [16 rows][K/32 chunks of 16 B]; chunk c of row r sits in slot c ^ (r & 15), so
 //   the 16 rows a wave reads at one chunk hit 16 different bank groups;
 //   scales [16][K/64] bf16, then biases [16][K/64] bf16, each padded to whole KB.
-template <int GPS>
+template <int S, int GPS>
 struct Layout {
-  static constexpr int K = 512 * GPS;
+  static constexpr int kSlices = S;
+  static constexpr int K = 64 * S * GPS;
   static constexpr int row_bytes = K / 2;
   static constexpr int code_bytes = kUnit * row_bytes;  // 4 KB * GPS
   static constexpr int sb_row = K / 32;                 // bytes of bf16 scales per row
@@ -59,9 +59,9 @@ struct Layout {
   static constexpr int buf_bytes = code_bytes + 2 * sb_pad;
   static constexpr int code_dma = code_bytes / 1024;  // 1 KB wave instructions per unit
   static constexpr int sb_dma = sb_pad / 1024;
-  // wave s requests code instructions s, s + 8, ... (GPS/2 of them) and one instruction
-  // of scales (s < sb_dma) or biases (s - sb_dma < sb_dma), or a padding load
-  static constexpr int code_per_wave = code_dma / kSlices;
+  // wave s requests code instructions s, s + S, ... (padding loads past the last) and one
+  // instruction of scales (s < sb_dma) or biases (s - sb_dma < sb_dma), or a padding load
+  static constexpr int code_per_wave = (code_dma + S - 1) / S;
   static constexpr int dma_per_wave = code_per_wave + 1;
   // unit buffers: as many as fit (up to 4), so up to nbuf - 1 units are in flight
   static constexpr int fixed = kSlices * 64 * 16 + 1024;
@@ -69,7 +69,6 @@ struct Layout {
   static constexpr int red_off = nbuf * buf_bytes;       // slice partials [8][64 lanes][4]
   static constexpr int dump_off = red_off + kSlices * 64 * 16;  // target of padding loads
   static constexpr int lds_bytes = dump_off + 1024;
-  static_assert(code_dma % kSlices == 0, "GPS is even");
   static_assert(2 * sb_dma <= kSlices, "one scale or bias instruction per wave");
   static_assert(code_bytes % 1024 == 0, "a unit's codes are whole KB");
   static_assert(nbuf >= 2 && lds_bytes <= 160 * 1024, "LDS");
@@ -105,10 +104,11 @@ __device__ __forceinline__ void wait_units_barrier(int ahead) {
   }
 }
 
-template <int GPS, int EPI>
-__global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units) {
-  using L = Layout<GPS>;
+template <int S, int GPS, int EPI>
+__global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units) {
+  using L = Layout<S, GPS>;
   constexpr int K = L::K;
+  constexpr int kSlices = S;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::lds_bytes];
 
   const int lane = threadIdx.x & 63;
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
     const uint32_t o = 1024u * uint32_t(t * kSlices + s) + 16u * uint32_t(lane);
     const int r = int(o / L::row_bytes);
     const uint32_t c = (o % L::row_bytes) / 16u;
-    crow[t] = r;
+    crow[t] = r < kUnit ? r : 0;  // past the unit's codes: a padding load
     cofs[t] = 16u * (c ^ uint32_t(r & 15));
   }
   // scale/bias instruction of this wave: region byte 1024 j + 16 L
@@ -150,9 +150,12 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
     uint8_t* base = lds + buf * L::buf_bytes;
 #pragma unroll
     for (int t = 0; t < L::code_per_wave; ++t) {
-      const uint32_t off = unit_row<EPI>(rows32, I32, uint32_t(u), crow[t]) * uint32_t(L::row_bytes) + cofs[t];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          cr, (__attribute__((address_space(3))) void*)(base + 1024 * (t * kSlices + s)), 16, off, 0, 0, 0);
+      const int i = t * kSlices + s;  // wave-uniform
+      const bool real = L::code_dma % kSlices == 0 || i < L::code_dma;
+      const uint32_t off = real ? unit_row<EPI>(rows32, I32, uint32_t(u), crow[t]) * uint32_t(L::row_bytes) + cofs[t]
+                                : 0xFFFFFFF0u;
+      uint8_t* dst = real ? base + 1024 * i : lds + L::dump_off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
     }
     // past the scales (padding of the region) or no instruction for this wave: a load
     // beyond every buffer returns zero
@@ -247,10 +250,11 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
       return t;
     };
     if constexpr (EPI == EPI_SWIGLU) {
-      // 8 gate columns x 16 rows: wave s, lane < 16 takes gate column g % 8 of block g / 8
-      // (g = (16 s + lane) / 4) at r = lane % 4, with its up column 8 further
-      if (lane < 16) {
-        const int g = (16 * s + lane) >> 2, r = lane & 3;
+      // 8 gate columns x 16 rows = 128 outputs, 128/S per wave: lane < 128/S takes gate
+      // column g % 8 of block g / 8 (g = ((128/S) s + lane) / 4) at r = lane % 4, with its up
+      // column 8 further
+      if (lane < 128 / kSlices) {
+        const int g = ((128 / kSlices) * s + lane) >> 2, r = lane & 3;
         const int l = (g & 7) + 16 * (g >> 3);
         const int64_t m = mb * kRows + 4 * (l >> 4) + r;
         const int64_t p = u * (kUnit / 2) + (l & 15);
@@ -258,9 +262,10 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
           store_out(a.out0, m * a.n_out + p, silu_times(slice_sum(l, r), slice_sum(l + 8, r)), a.f32_out);
       }
     } else {
-      // 16 columns x 16 rows: wave s, lane < 32 takes partial lane 8 s + lane / 4, r = lane % 4
-      if (lane < 32) {
-        const int l = 8 * s + (lane >> 2), r = lane & 3;
+      // 16 columns x 16 rows = 256 outputs, 256/S per wave: lane < 256/S takes partial lane
+      // (64/S) s + lane / 4, r = lane % 4
+      if (lane < 256 / kSlices) {
+        const int l = (64 / kSlices) * s + (lane >> 2), r = lane & 3;
         const int64_t m = mb * kRows + 4 * (l >> 4) + r;
         const int64_t n = u * kUnit + (l & 15);
         if (4 * (l >> 4) + r < rows_here && n < a.rows) {
@@ -285,15 +290,18 @@ __global__ void __launch_bounds__(64 * kSlices, 1) bmv_u4_kernel(GemvArgs a, int
   }
 }
 
-// Instantiated K = 512 * GPS.
+// Instantiated: 8 waves per block (16 measured slower: 28.8 against 27.0 us on the 14B
+// gate+up at M = 4), K = 512 * GPS.
+constexpr int kSlicesUsed = 8;
+constexpr int kKStep = 64 * kSlicesUsed;  // K is a multiple of this
 #define QMM_BMV_GPS(X) X(2) X(4) X(6) X(8) X(10) X(12) X(14) X(16)
 
 }  // namespace bmv
 
 bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
-  if (a.bits != 4 || a.gshift != 1 || M < 2 || M > kBmvMaxM || a.K % 512) return false;
+  if (a.bits != 4 || a.gshift != 1 || M < 2 || M > kBmvMaxM || a.K % bmv::kKStep) return false;
   if (epi != EPI_LINEAR && epi != EPI_QKV && epi != EPI_SWIGLU) return false;
-  switch (a.K / 512) {
+  switch (a.K / bmv::kKStep) {
 #define QMM_BMV_CASE(G) case G:
     QMM_BMV_GPS(QMM_BMV_CASE)
 #undef QMM_BMV_CASE
@@ -309,13 +317,16 @@ int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {
                                           : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
   constexpr int64_t kCUs = 256;
   const dim3 grid{unsigned(units < kCUs ? units : kCUs), unsigned((M + bmv::kRows - 1) / bmv::kRows), 1u};
-  const dim3 block{64u * bmv::kSlices, 1u, 1u};
-  switch (a.K / 512) {
-#define QMM_BMV_CASE(G)                                                                       \
-  case G:                                                                                     \
-    if (epi == EPI_LINEAR) bmv::bmv_u4_kernel<G, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units); \
-    else if (epi == EPI_QKV) bmv::bmv_u4_kernel<G, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);  \
-    else bmv::bmv_u4_kernel<G, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);                 \
+  const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
+  switch (a.K / bmv::kKStep) {
+#define QMM_BMV_CASE(G)                                                                                   \
+  case G:                                                                                                 \
+    if (epi == EPI_LINEAR)                                                                                \
+      bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units);            \
+    else if (epi == EPI_QKV)                                                                              \
+      bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);               \
+    else                                                                                                  \
+      bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);            \
     break;
     QMM_BMV_GPS(QMM_BMV_CASE)
 #undef QMM_BMV_CASE
