@@ -311,6 +311,26 @@ bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
   }
 }
 
+// Above 32 rows the kernel runs one 16-row pass per grid row and reads the weights once
+// per pass; it is still taken where the prefill GEMM would leave most of the GPU idle (a
+// grid of few 256 x 256 tiles, each walking all of K).  Estimates from the measured rates
+// (14B / 24B shapes): a pass streams the weights at ~2.9 TB/s and takes at least 8 us; a
+// GEMM round of up to 256 tiles takes ~1.5 us per 64-input step.
+#ifndef QMM_BMV_FORCE
+#define QMM_BMV_FORCE 0
+#endif
+bool bmv_preferred(int epi, const GemvArgs& a, int64_t M) {
+  if (!bmv_supports(epi, a, M)) return false;
+  if (M <= 32 || QMM_BMV_FORCE) return true;
+  const double wbytes = double(a.rows) * double(a.K) * (0.5 + 4.0 / 64.0);
+  const double pass_us = wbytes / 2.9e6 > 8.0 ? wbytes / 2.9e6 : 8.0;
+  const double bmv_us = double((M + bmv::kRows - 1) / bmv::kRows) * pass_us;
+  const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + 127) / 128 : (a.rows + 255) / 256;
+  const int64_t rounds = ((M + 255) / 256 * n_tiles + 255) / 256;
+  const double gemm_us = double(rounds) * double(a.K / 64) * 1.5;
+  return bmv_us < gemm_us;
+}
+
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {
   if (!bmv_supports(epi, a, M)) return 2;
   const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)

@@ -134,7 +134,7 @@ int qmm_linear_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M, i
   a.f32_out = out_dtype == QMM_OUT_F32;
   a.bits = f.bits;
   a.gshift = f.gshift;
-  if (qmm::bmv_supports(qmm::EPI_LINEAR, a, M)) return qmm::launch_bmv(qmm::EPI_LINEAR, a, M, stream);
+  if (qmm::bmv_preferred(qmm::EPI_LINEAR, a, M)) return qmm::launch_bmv(qmm::EPI_LINEAR, a, M, stream);
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_LINEAR, gemm_args(a, M, N), stream);
   return qmm::launch_gemv(qmm::EPI_LINEAR, a, M, stream);
 }
@@ -184,7 +184,7 @@ int qmm_fused_qkv_fmt(int bits, int64_t group_size, const uint16_t* x, int64_t M
   a.f32_out = out_dtype == QMM_OUT_F32;
   a.bits = f.bits;
   a.gshift = f.gshift;
-  if (qmm::bmv_supports(qmm::EPI_QKV, a, M)) return qmm::launch_bmv(qmm::EPI_QKV, a, M, stream);
+  if (qmm::bmv_preferred(qmm::EPI_QKV, a, M)) return qmm::launch_bmv(qmm::EPI_QKV, a, M, stream);
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_QKV, gemm_args(a, M, rows), stream);
   return qmm::launch_gemv(qmm::EPI_QKV, a, M, stream);
 }
@@ -286,7 +286,7 @@ int qmm_fused_gate_up_swiglu_fmt(int bits, int64_t group_size, const uint16_t* x
   a.f32_out = out_dtype == QMM_OUT_F32;
   a.bits = f.bits;
   a.gshift = f.gshift;
-  if (qmm::bmv_supports(qmm::EPI_SWIGLU, a, M)) return qmm::launch_bmv(qmm::EPI_SWIGLU, a, M, stream);
+  if (qmm::bmv_preferred(qmm::EPI_SWIGLU, a, M)) return qmm::launch_bmv(qmm::EPI_SWIGLU, a, M, stream);
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_SWIGLU, gemm_args(a, M, 2 * I), stream);
   return qmm::launch_gemv(qmm::EPI_SWIGLU, a, M, stream);
 }

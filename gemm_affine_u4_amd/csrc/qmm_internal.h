@@ -132,10 +132,13 @@ inline int launch_moe_down(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bi
 inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_gemm(epi, a, s)) }
 
 // Small batches (2 <= M <= kBmvMaxM) of the 4-bit group-64 projections whose K is a
-// multiple of 512 up to 8192: one pass over the weights, the activations on the matrix
-// cores (bmv_u4.hip).  Linear, fused QKV and fused gate+up+SwiGLU.
-constexpr int64_t kBmvMaxM = 32;
+// multiple of 512 up to 8192: the weights streamed once per 16 activation rows, the
+// activations on the matrix cores (bmv_u4.hip).  Linear, fused QKV and fused
+// gate+up+SwiGLU.  bmv_preferred: taken for M <= 32, and above where it beats the
+// prefill GEMM's estimate.
+constexpr int64_t kBmvMaxM = 256;
 bool bmv_supports(int epi, const GemvArgs& a, int64_t M);
+bool bmv_preferred(int epi, const GemvArgs& a, int64_t M);
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
 
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and

@@ -1,6 +1,6 @@
-"""GPU parity of the small-batch path (2 <= M <= 32, u4 group 64, K a multiple of 512 up
-to 8192: activations on the matrix cores, one pass over the weights) against the fp64
-oracle.
+"""GPU parity of the small-batch path (u4 group 64, K a multiple of 512 up to 8192:
+activations on the matrix cores, the weights streamed once per 16 rows; taken for
+2 <= M <= 32 and above where the prefill GEMM would be slower) against the fp64 oracle.
 
 Acceptance as for the decode GEMV (the oracle's `tolerance`, propagated for SwiGLU): the
 path rounds no weight, so the bound without the bf16-weight term applies.  Also: a row's
@@ -130,3 +130,31 @@ def test_14B_shapes_against_sampled_rows():
     sub = synth.U4Weight(w.codes[rows], w.scales[rows], w.biases[rows])
     h, th = orc.gate_up_swiglu(x, sub.codes, sub.scales, sub.biases, len(cols))
     assert_within(got[:, cols], h, th, "14B gate+up sampled")
+
+
+def test_many_passes_14B_qkv():
+    """M = 96 on the 14B fused QKV (7168 rows): six 16-row passes, which the dispatch
+    prefers to the 28-tile prefill GEMM.  Sampled columns against the oracle on those
+    rows; the rows of the last pass equal the same rows of a one-pass call bit for bit."""
+    M, sh = 96, synth.DENSE_14B
+    say(f"[bmv] 14B qkv M={M}")
+    w = synth.gen_weight(synth.CFG_14B, 1, synth.PROJ_QKV, sh.qkv_rows, sh.K)
+    x = synth.gen_x(synth.CFG_14B, 1, 0, M, sh.K)
+    q, k, v = run_qkv(x, w, sh.q_out, sh.kv_out)
+    full = np.concatenate([q, k, v], axis=1)
+    cols = np.sort(np.random.default_rng(6).choice(sh.qkv_rows, 64, replace=False))
+    sub = synth.U4Weight(w.codes[cols], w.scales[cols], w.biases[cols])
+    y, t = orc.linear(x, sub.codes, sub.scales, sub.biases)
+    assert_within(full[:, cols], y, t, "14B qkv M=96 sampled")
+    q2, k2, v2 = run_qkv(x[80:96], w, sh.q_out, sh.kv_out)
+    assert np.array_equal(np.concatenate([q2, k2, v2], axis=1), full[80:96])
+
+
+def test_ragged_last_pass():
+    """M = 37 (passes of 16, 16 and 5 rows) on a 24B-shaped gate+up slice."""
+    M, K, I = 37, 5120, 300
+    say(f"[bmv] gate+up M={M} K={K} I={I}")
+    w = synth.gen_weight(synth.CFG_TEST, 440, synth.PROJ_GATE_UP, 2 * I, K)
+    x = synth.gen_x(synth.CFG_TEST, 440, 0, M, K)
+    h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, I)
+    assert_within(run_gate_up(x, w, I), h, th, f"gate+up M={M}")
