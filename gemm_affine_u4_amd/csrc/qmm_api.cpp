@@ -1,6 +1,6 @@
 // C ABI entry points (declared and documented in include/qmm.h): validate, then
-// enqueue the kernel for the regime (decode GEMV for M <= 8, LDS-dequant + MFMA GEMM
-// above).  Nothing here allocates, synchronises or keeps state.
+// enqueue the kernel for the regime (decode GEMV, small-batch MFMA kernel, LDS-dequant +
+// MFMA GEMM; see include/qmm.h).  Nothing here allocates, synchronises or keeps state.
 #include <hip/hip_runtime_api.h>
 
 #include "qmm.h"

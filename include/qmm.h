@@ -50,10 +50,15 @@
  *     stores the fp32 value that the bf16 mode would round, so bf16 output ==
  *     RNE(fp32 output) bit for bit.
  *   - Row-major everywhere: x [M][K], y [M][N].  Inputs are assumed finite.
- *   - Decode (M <= 8) runs a bandwidth-bound GEMV, once per activation row; larger M
- *     runs an LDS-dequant + MFMA GEMM ("Sanctum-MLX", "Latency testing": prefill is
- *     dominated by the quantized matmuls).  Results of the two regimes agree to the
- *     tolerance, not bit for bit (the GEMM rounds dequantized weights to bf16).
+ *   - M = 1 runs a bandwidth-bound GEMV.  For 4-bit group-64 linear / fused QKV / fused
+ *     gate+up with K a multiple of 512 up to 8192, 2 <= M <= 32 (and up to 256 where it
+ *     is estimated faster than the GEMM) runs a small-batch kernel that streams the
+ *     weights once per 16 activation rows with the activations on the matrix cores;
+ *     otherwise M <= 8 runs the GEMV once per activation row and larger M an
+ *     LDS-dequant + MFMA GEMM ("Sanctum-MLX", "Latency testing": prefill is dominated by
+ *     the quantized matmuls).  The regimes agree to the tolerance, not bit for bit (the
+ *     GEMM rounds dequantized weights to bf16; the reduction orders differ).  Within one
+ *     regime a row's result does not depend on the other rows of the call.
  *   - M * K * 2 (the activation bytes) must stay below 4 GiB.
  */
 #ifndef QMM_H
