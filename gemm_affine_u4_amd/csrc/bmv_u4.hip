@@ -47,6 +47,9 @@ constexpr int kRows = 16;   // activation rows per block (the MFMA's rows)
 //   codes [16 rows][K/32 chunks of 16 B]; chunk c of row r sits in slot c ^ (r & 15), so
 //   the 16 rows a wave reads at one chunk hit 16 different bank groups;
 //   scales [16][K/64] bf16, then biases [16][K/64] bf16, each padded to whole KB.
+#ifndef QMM_BMV_DEFER
+#define QMM_BMV_DEFER 1
+#endif
 template <int S, int GPS>
 struct Layout {
   static constexpr int kSlices = S;
@@ -63,11 +66,18 @@ struct Layout {
   // instruction of scales (s < sb_dma) or biases (s - sb_dma < sb_dma), or a padding load
   static constexpr int code_per_wave = (code_dma + S - 1) / S;
   static constexpr int dma_per_wave = code_per_wave + 1;
-  // unit buffers: as many as fit (up to 4), so up to nbuf - 1 units are in flight
-  static constexpr int fixed = kSlices * 64 * 16 + 1024;
-  static constexpr int nbuf = (160 * 1024 - fixed) / buf_bytes < 4 ? (160 * 1024 - fixed) / buf_bytes : 4;
-  static constexpr int red_off = nbuf * buf_bytes;       // slice partials [8][64 lanes][4]
-  static constexpr int dump_off = red_off + kSlices * 64 * 16;  // target of padding loads
+  // unit buffers: as many as fit (up to 4); slice partials [S][64 lanes][4], two of them
+  // when a unit's sums and stores wait until the next unit's barrier (deferred: needs 3
+  // unit buffers, since a unit buffer is then refilled two steps after it was read)
+  static constexpr int red_bytes = kSlices * 64 * 16;
+  static constexpr int nbuf_of(int reds) {
+    return (160 * 1024 - reds * red_bytes - 1024) / buf_bytes < 4 ? (160 * 1024 - reds * red_bytes - 1024) / buf_bytes : 4;
+  }
+  static constexpr bool deferred = QMM_BMV_DEFER && nbuf_of(2) >= 3;
+  static constexpr int nbuf = nbuf_of(deferred ? 2 : 1);
+  static constexpr int lookahead = deferred ? nbuf - 2 : nbuf - 1;  // units in flight ahead
+  static constexpr int red_off = nbuf * buf_bytes;
+  static constexpr int dump_off = red_off + (deferred ? 2 : 1) * red_bytes;  // target of padding loads
   static constexpr int lds_bytes = dump_off + 1024;
   static_assert(2 * sb_dma <= kSlices, "one scale or bias instruction per wave");
   static_assert(code_bytes % 1024 == 0, "a unit's codes are whole KB");
@@ -169,9 +179,10 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   int64_t u = blockIdx.x;
   if (u >= units) return;
   const int64_t stride = gridDim.x;
-  // units u, u + stride, ..., u + (nbuf - 2) stride into buffers 0 .. nbuf - 2
+  // the block's units j = 0, 1, ... (unit u + j * stride) live in buffer j % nbuf; units
+  // 0 .. lookahead - 1 are requested here, unit j + lookahead at step j
 #pragma unroll
-  for (int b = 0; b < L::nbuf - 1; ++b)
+  for (int b = 0; b < L::lookahead; ++b)
     if (u + b * stride < units) request(u + b * stride, b);
 
   // ---- activations of this slice: MFMA operands, permuted to the nibble-pair order ----
@@ -197,14 +208,68 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   const uint32_t magic = in_vgpr(kMagicPair);
   float* red = reinterpret_cast<float*>(lds + L::red_off);
 
-  for (int it = 0;; ++it) {
+  // sums of the S slice partials in slice order and the epilogue of unit uu, each output
+  // by one lane of one of the waves; rb[j][l][r] is slice j's partial of activation row
+  // 4 (l / 16) + r, column l % 16
+  auto epilogue = [&](int64_t uu, const float* rb) {
+    auto slice_sum = [&](int l, int r) {
+      float t = 0.f;
+#pragma unroll
+      for (int j = 0; j < kSlices; ++j) t += rb[(j * 64 + l) * 4 + r];
+      return t;
+    };
+    if constexpr (EPI == EPI_SWIGLU) {
+      // 8 gate columns x 16 rows = 128 outputs, 128/S per wave: lane < 128/S takes gate
+      // column g % 8 of block g / 8 (g = ((128/S) s + lane) / 4) at r = lane % 4, with its up
+      // column 8 further
+      if (lane < 128 / kSlices) {
+        const int g = ((128 / kSlices) * s + lane) >> 2, r = lane & 3;
+        const int l = (g & 7) + 16 * (g >> 3);
+        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
+        const int64_t p = uu * (kUnit / 2) + (l & 15);
+        if (4 * (l >> 4) + r < rows_here && p < a.I)
+          store_out(a.out0, m * a.n_out + p, silu_times(slice_sum(l, r), slice_sum(l + 8, r)), a.f32_out);
+      }
+    } else {
+      // 16 columns x 16 rows = 256 outputs, 256/S per wave: lane < 256/S takes partial lane
+      // (64/S) s + lane / 4, r = lane % 4
+      if (lane < 256 / kSlices) {
+        const int l = (64 / kSlices) * s + (lane >> 2), r = lane & 3;
+        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
+        const int64_t n = uu * kUnit + (l & 15);
+        if (4 * (l >> 4) + r < rows_here && n < a.rows) {
+          float v = slice_sum(l, r);
+          if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
+          if constexpr (EPI == EPI_QKV) {
+            if (n < a.q_out) {
+              store_out(a.out0, m * a.q_out + n, v, a.f32_out);
+            } else if (n < a.q_out + a.kv_out) {
+              store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
+            } else {
+              store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
+            }
+          } else {
+            store_out(a.out0, m * a.n_out + n, v, a.f32_out);
+          }
+        }
+      }
+    }
+  };
+
+  int it = 0;
+  for (;; ++it) {
     const int buf = it % L::nbuf;
-    // request the unit nbuf - 1 steps ahead into the buffer freed by the previous step,
-    // then wait for this unit (the later units' loads may stay in flight)
-    const int64_t ua = u + (L::nbuf - 1) * stride;
-    if (ua < units) request(ua, (it + L::nbuf - 1) % L::nbuf);
+    // request unit it + lookahead, then wait for unit it (the later units' loads may stay
+    // in flight); buffer (it + lookahead) % nbuf held unit it - 1 (without deferral: every
+    // wave has passed the barrier after reading it) or unit it - 2 (deferred: read before
+    // the last barrier)
+    const int64_t ua = u + L::lookahead * stride;
+    if (ua < units) request(ua, (it + L::lookahead) % L::nbuf);
     const int64_t later = (units - 1 - u) / stride;  // units after u for this block
-    wait_units_barrier<L::dma_per_wave>(int(later < L::nbuf - 1 ? later : L::nbuf - 1));
+    wait_units_barrier<L::dma_per_wave>(int(later < L::lookahead ? later : L::lookahead));
+    if constexpr (L::deferred) {
+      if (it > 0) epilogue(u - stride, red + ((it - 1) & 1) * (L::red_bytes / 4));
+    }
 
     // ---- this wave's slice of unit u ----------------------------------------------------
     const uint8_t* bb = lds + buf * L::buf_bytes;
@@ -238,55 +303,21 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
         y[r] = fmaf(bv, xs[r], y[r]);
       }
     }
-    *reinterpret_cast<f32x4_t*>(red + (s * 64 + lane) * 4) = y;
-    __syncthreads();
-
-    // ---- the 8 slice partials in slice order, epilogue: split over the waves -----------
-    // red[j][l][r] is slice j's partial of activation row 4 (l / 16) + r, column l % 16.
-    auto slice_sum = [&](int l, int r) {
-      float t = 0.f;
-#pragma unroll
-      for (int j = 0; j < kSlices; ++j) t += red[(j * 64 + l) * 4 + r];
-      return t;
-    };
-    if constexpr (EPI == EPI_SWIGLU) {
-      // 8 gate columns x 16 rows = 128 outputs, 128/S per wave: lane < 128/S takes gate
-      // column g % 8 of block g / 8 (g = ((128/S) s + lane) / 4) at r = lane % 4, with its up
-      // column 8 further
-      if (lane < 128 / kSlices) {
-        const int g = ((128 / kSlices) * s + lane) >> 2, r = lane & 3;
-        const int l = (g & 7) + 16 * (g >> 3);
-        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
-        const int64_t p = u * (kUnit / 2) + (l & 15);
-        if (4 * (l >> 4) + r < rows_here && p < a.I)
-          store_out(a.out0, m * a.n_out + p, silu_times(slice_sum(l, r), slice_sum(l + 8, r)), a.f32_out);
-      }
+    if constexpr (L::deferred) {
+      // partials of this unit into red buffer it & 1; summed and stored after the next
+      // step's barrier (or after the loop)
+      *reinterpret_cast<f32x4_t*>(red + (it & 1) * (L::red_bytes / 4) + (s * 64 + lane) * 4) = y;
     } else {
-      // 16 columns x 16 rows = 256 outputs, 256/S per wave: lane < 256/S takes partial lane
-      // (64/S) s + lane / 4, r = lane % 4
-      if (lane < 256 / kSlices) {
-        const int l = (64 / kSlices) * s + (lane >> 2), r = lane & 3;
-        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
-        const int64_t n = u * kUnit + (l & 15);
-        if (4 * (l >> 4) + r < rows_here && n < a.rows) {
-          float v = slice_sum(l, r);
-          if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
-          if constexpr (EPI == EPI_QKV) {
-            if (n < a.q_out) {
-              store_out(a.out0, m * a.q_out + n, v, a.f32_out);
-            } else if (n < a.q_out + a.kv_out) {
-              store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
-            } else {
-              store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
-            }
-          } else {
-            store_out(a.out0, m * a.n_out + n, v, a.f32_out);
-          }
-        }
-      }
+      *reinterpret_cast<f32x4_t*>(red + (s * 64 + lane) * 4) = y;
+      __syncthreads();
+      epilogue(u, red);
     }
     u += stride;
     if (u >= units) break;
+  }
+  if constexpr (L::deferred) {
+    __syncthreads();
+    epilogue(u - stride, red + (it & 1) * (L::red_bytes / 4));
   }
 }
 
