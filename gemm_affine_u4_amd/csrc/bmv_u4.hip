@@ -1,4 +1,5 @@
-// Small-batch (2 <= M <= 32) kernel for the u4 group-64 affine projections on gfx950.
+// Small-batch kernel (2 <= M <= 32, and up to 256 where the prefill GEMM's grid would be
+// small) for the u4 group-64 affine projections on gfx950.
 //
 // Between decode (one activation row: weight-bandwidth bound, the GEMV) and prefill
 // (hundreds of rows: matrix bound, the LDS-dequant GEMM) the work is still one pass over
@@ -27,7 +28,8 @@
 //     y += s * (D - 128 * xs) + b * xs, with xs[m] = sum x over the group (an MFMA against
 //     ones);
 //   * the slice partials of a unit meet in LDS and are added in slice order, each output
-//     by one lane of one of the waves.
+//     by one lane of one of the waves, after the next unit's barrier (two partial buffers:
+//     one barrier per unit) where LDS holds three unit buffers, else after a second one.
 // Every output depends only on its own activation row, K and the unit layout, so a row's
 // result does not depend on the other rows of the batch or on M.
 #include "qmm_device.h"
@@ -135,9 +137,11 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases, nrows * uint64_t(L::sb_row));
 
   // ---- unit -> LDS ------------------------------------------------------------------
-  // Code instruction i = 8t + s (lane L: byte 1024 i + 16 L of the unit's codes, i.e. row
+  // Code instruction i = S t + s (lane L: byte 1024 i + 16 L of the unit's codes, i.e. row
   // r, slot c) reads chunk c ^ (r & 15) of row r; the row and the in-row byte offset of
-  // each of the wave's instructions are fixed for the kernel.
+  // each of the wave's instructions are fixed for the kernel.  Padding loads (i past the
+  // unit's codes, or no scale/bias instruction for this wave) use an offset past the
+  // descriptors' ranges, so they read nothing, and land in a dump area of LDS.
   int crow[L::code_per_wave];
   uint32_t cofs[L::code_per_wave];
 #pragma unroll
