@@ -43,7 +43,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kUnit = 16;   // weight rows per unit (the MFMA's columns)
-constexpr int kRows = 16;   // activation rows per block (the MFMA's rows)
+constexpr int kRows = 16;   // activation rows per MFMA tile (a block holds MB tiles)
 
 // LDS of one unit buffer for S waves (K slices) of GPS groups each, K = 64 * S * GPS:
 //   codes [16 rows][K/32 chunks of 16 B]; chunk c of row r sits in slot c ^ (r & 15), so
@@ -52,7 +52,7 @@ constexpr int kRows = 16;   // activation rows per block (the MFMA's rows)
 #ifndef QMM_BMV_DEFER
 #define QMM_BMV_DEFER 1
 #endif
-template <int S, int GPS>
+template <int S, int GPS, int MB>
 struct Layout {
   static constexpr int kSlices = S;
   static constexpr int K = 64 * S * GPS;
@@ -68,10 +68,10 @@ struct Layout {
   // instruction of scales (s < sb_dma) or biases (s - sb_dma < sb_dma), or a padding load
   static constexpr int code_per_wave = (code_dma + S - 1) / S;
   static constexpr int dma_per_wave = code_per_wave + 1;
-  // unit buffers: as many as fit (up to 4); slice partials [S][64 lanes][4], two of them
+  // unit buffers: as many as fit (up to 4); slice partials [S][MB][64 lanes][4], two of them
   // when a unit's sums and stores wait until the next unit's barrier (deferred: needs 3
   // unit buffers, since a unit buffer is then refilled two steps after it was read)
-  static constexpr int red_bytes = kSlices * 64 * 16;
+  static constexpr int red_bytes = kSlices * MB * 64 * 16;
   static constexpr int nbuf_of(int reds) {
     return (160 * 1024 - reds * red_bytes - 1024) / buf_bytes < 4 ? (160 * 1024 - reds * red_bytes - 1024) / buf_bytes : 4;
   }
@@ -116,9 +116,10 @@ __device__ __forceinline__ void wait_units_barrier(int ahead) {
   }
 }
 
-template <int S, int GPS, int EPI>
+template <int S, int GPS, int MB, int EPI>
 __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units) {
-  using L = Layout<S, GPS>;
+  using L = Layout<S, GPS, MB>;
+  constexpr int R = kRows * MB;  // activation rows per block
   constexpr int K = L::K;
   constexpr int kSlices = S;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::lds_bytes];
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   const int col = lane & 15;  // MFMA column: LDS row of the unit
   const int kb = lane >> 4;   // 8-input block of the MFMA's 32 inputs
   const int64_t mb = blockIdx.y;
-  const int64_t rows_here = M - mb * kRows < kRows ? M - mb * kRows : kRows;
+  const int64_t rows_here = M - mb * R < R ? M - mb * R : R;
   const uint64_t nrows = uint64_t(a.rows);
   const uint32_t rows32 = uint32_t(a.rows), I32 = uint32_t(a.I);
 
@@ -190,59 +191,65 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     if (u + b * stride < units) request(u + b * stride, b);
 
   // ---- activations of this slice: MFMA operands, permuted to the nibble-pair order ----
-  // Operand lane (row m = lane % 16, block kb) of group g, MFMA h holds inputs
+  // Operand lane (row m = lane % 16 of tile t, block kb) of group g, MFMA h holds inputs
   // 64 G + 16 kb + 8 h .. +7 with G = s*GPS + g: the 8 codes its column's lane decodes
   // from code word h of that lane's 16 codes.
-  bf16x8_t xa[GPS][2];
+  bf16x8_t xa[MB][GPS][2];
   {
-    const uint16_t* xb = a.x + mb * kRows * K;
+    const uint16_t* xb = a.x + mb * R * K;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, uint64_t(rows_here) * K * 2);
 #pragma unroll
-    for (int g = 0; g < GPS; ++g)
+    for (int t = 0; t < MB; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t k0 = uint32_t(64 * (s * GPS + g) + 16 * kb + 8 * h);
-        const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t(col) * K + k0) * 2u, 0, 0);
-        const u32x4_t p = {__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
-                           __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
-        xa[g][h] = __builtin_bit_cast(bf16x8_t, p);
-      }
+      for (int g = 0; g < GPS; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t k0 = uint32_t(64 * (s * GPS + g) + 16 * kb + 8 * h);
+          const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t(kRows * t + col) * K + k0) * 2u, 0, 0);
+          const u32x4_t p = {__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
+                             __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
+          xa[t][g][h] = __builtin_bit_cast(bf16x8_t, p);
+        }
   }
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const uint32_t magic = in_vgpr(kMagicPair);
   float* red = reinterpret_cast<float*>(lds + L::red_off);
 
   // sums of the S slice partials in slice order and the epilogue of unit uu, each output
-  // by one lane of one of the waves; rb[j][l][r] is slice j's partial of activation row
-  // 4 (l / 16) + r, column l % 16
+  // by one lane of one of the waves; rb[j][t][l][r] is slice j's partial of activation row
+  // 16 t + 4 (l / 16) + r, column l % 16
   auto epilogue = [&](int64_t uu, const float* rb) {
-    auto slice_sum = [&](int l, int r) {
-      float t = 0.f;
+    auto slice_sum = [&](int t, int l, int r) {
+      float v = 0.f;
 #pragma unroll
-      for (int j = 0; j < kSlices; ++j) t += rb[(j * 64 + l) * 4 + r];
-      return t;
+      for (int j = 0; j < kSlices; ++j) v += rb[((j * MB + t) * 64 + l) * 4 + r];
+      return v;
     };
     if constexpr (EPI == EPI_SWIGLU) {
-      // 8 gate columns x 16 rows = 128 outputs, 128/S per wave: lane < 128/S takes gate
-      // column g % 8 of block g / 8 (g = ((128/S) s + lane) / 4) at r = lane % 4, with its up
-      // column 8 further
-      if (lane < 128 / kSlices) {
-        const int g = ((128 / kSlices) * s + lane) >> 2, r = lane & 3;
+      // 8 gate columns x R rows = 128 MB outputs, 128 MB / S per wave: output o of tile
+      // t = o / 128 is gate column g % 8 of block g / 8 (g = (o % 128) / 4) at r = o % 4,
+      // with its up column 8 further
+      if (lane < 128 * MB / kSlices) {
+        const int o = (128 * MB / kSlices) * s + lane;
+        const int t = o >> 7, g = (o & 127) >> 2, r = o & 3;
         const int l = (g & 7) + 16 * (g >> 3);
-        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
+        const int mr = kRows * t + 4 * (l >> 4) + r;  // row within the block
         const int64_t p = uu * (kUnit / 2) + (l & 15);
-        if (4 * (l >> 4) + r < rows_here && p < a.I)
-          store_out(a.out0, m * a.n_out + p, silu_times(slice_sum(l, r), slice_sum(l + 8, r)), a.f32_out);
+        if (mr < rows_here && p < a.I)
+          store_out(a.out0, (mb * R + mr) * a.n_out + p, silu_times(slice_sum(t, l, r), slice_sum(t, l + 8, r)),
+                    a.f32_out);
       }
     } else {
-      // 16 columns x 16 rows = 256 outputs, 256/S per wave: lane < 256/S takes partial lane
-      // (64/S) s + lane / 4, r = lane % 4
-      if (lane < 256 / kSlices) {
-        const int l = (64 / kSlices) * s + (lane >> 2), r = lane & 3;
-        const int64_t m = mb * kRows + 4 * (l >> 4) + r;
+      // 16 columns x R rows = 256 MB outputs, 256 MB / S per wave: output o of tile
+      // t = o / 256 is partial lane (o % 256) / 4 at r = o % 4
+      if (lane < 256 * MB / kSlices) {
+        const int o = (256 * MB / kSlices) * s + lane;
+        const int t = o >> 8, l = (o & 255) >> 2, r = o & 3;
+        const int mr = kRows * t + 4 * (l >> 4) + r;
+        const int64_t m = mb * R + mr;
         const int64_t n = uu * kUnit + (l & 15);
-        if (4 * (l >> 4) + r < rows_here && n < a.rows) {
-          float v = slice_sum(l, r);
+        if (mr < rows_here && n < a.rows) {
+          float v = slice_sum(t, l, r);
           if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
           if constexpr (EPI == EPI_QKV) {
             if (n < a.q_out) {
@@ -279,7 +286,7 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     const uint8_t* bb = lds + buf * L::buf_bytes;
     const uint16_t* sc = reinterpret_cast<const uint16_t*>(bb + L::code_bytes) + col * (L::sb_row / 2);
     const uint16_t* bi = reinterpret_cast<const uint16_t*>(bb + L::code_bytes + L::sb_pad) + col * (L::sb_row / 2);
-    f32x4_t y = {};
+    f32x4_t y[MB] = {};
 #pragma unroll
     for (int g = 0; g < GPS; ++g) {
       const int G = s * GPS + g;
@@ -289,30 +296,39 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
       const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bb + col * L::row_bytes + 16 * (c ^ uint32_t(col)) + 8 * (kb & 1));
       const float sv = bf16_bits_to_f32(sc[G]);
       const float bv = bf16_bits_to_f32(bi[G]);
-      // xs[r] = sum of the group's 64 inputs of row 4 kb + r (the MFMA against ones puts
-      // that row's sum in every column; recomputed per unit, the matrix pipe is idle)
-      f32x4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g][0], ones, f32x4_t{}, 0, 0, 0);
-      xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g][1], ones, xs, 0, 0, 0);
-      f32x4_t d = {};
+      u32x4_t q[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t q = {nib_pair(w[h], 0, magic), nib_pair(w[h], 1, magic), nib_pair(w[h], 2, magic),
-                           nib_pair(w[h], 3, magic)};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[g][h], __builtin_bit_cast(bf16x8_t, q), d, 0, 0, 0);
-      }
+      for (int h = 0; h < 2; ++h)
+        q[h] = u32x4_t{nib_pair(w[h], 0, magic), nib_pair(w[h], 1, magic), nib_pair(w[h], 2, magic),
+                       nib_pair(w[h], 3, magic)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float dq = fmaf(-128.0f, xs[r], d[r]);  // sum x q (exact 0 for all-zero codes)
-        y[r] = fmaf(sv, dq, y[r]);
-        y[r] = fmaf(bv, xs[r], y[r]);
+      for (int t = 0; t < MB; ++t) {
+        // xs[r] = sum of the group's 64 inputs of row 4 kb + r of tile t (the MFMA against
+        // ones puts that row's sum in every column; recomputed per unit, the matrix pipe is
+        // idle)
+        f32x4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][0], ones, f32x4_t{}, 0, 0, 0);
+        xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][1], ones, xs, 0, 0, 0);
+        f32x4_t d = {};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][h], __builtin_bit_cast(bf16x8_t, q[h]), d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dq = fmaf(-128.0f, xs[r], d[r]);  // sum x q (exact 0 for all-zero codes)
+          y[t][r] = fmaf(sv, dq, y[t][r]);
+          y[t][r] = fmaf(bv, xs[r], y[t][r]);
+        }
       }
     }
     if constexpr (L::deferred) {
       // partials of this unit into red buffer it & 1; summed and stored after the next
       // step's barrier (or after the loop)
-      *reinterpret_cast<f32x4_t*>(red + (it & 1) * (L::red_bytes / 4) + (s * 64 + lane) * 4) = y;
+#pragma unroll
+      for (int t = 0; t < MB; ++t)
+        *reinterpret_cast<f32x4_t*>(red + (it & 1) * (L::red_bytes / 4) + ((s * MB + t) * 64 + lane) * 4) = y[t];
     } else {
-      *reinterpret_cast<f32x4_t*>(red + (s * 64 + lane) * 4) = y;
+#pragma unroll
+      for (int t = 0; t < MB; ++t) *reinterpret_cast<f32x4_t*>(red + ((s * MB + t) * 64 + lane) * 4) = y[t];
       __syncthreads();
       epilogue(u, red);
     }
@@ -326,10 +342,20 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
 }
 
 // Instantiated: 8 waves per block (16 measured slower: 28.8 against 27.0 us on the 14B
-// gate+up at M = 4), K = 512 * GPS.
+// gate+up at M = 4), K = 512 * GPS; two 16-row tiles per block (MB = 2, one code decode
+// for 32 activation rows) where the registers allow it (K <= 5120).
 constexpr int kSlicesUsed = 8;
 constexpr int kKStep = 64 * kSlicesUsed;  // K is a multiple of this
+constexpr int kMaxGpsTwoTiles = 10;
+#ifndef QMM_BMV_TWO_TILES
+#define QMM_BMV_TWO_TILES 1
+#endif
 #define QMM_BMV_GPS(X) X(2) X(4) X(6) X(8) X(10) X(12) X(14) X(16)
+
+// Row tiles per block for M rows at K = 512 * gps.
+inline int tiles_for(int64_t M, int64_t gps) {
+  return QMM_BMV_TWO_TILES && M > kRows && gps <= kMaxGpsTwoTiles ? 2 : 1;
+}
 
 }  // namespace bmv
 
@@ -346,42 +372,58 @@ bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
   }
 }
 
-// Above 32 rows the kernel runs one 16-row pass per grid row and reads the weights once
-// per pass; it is still taken where the prefill GEMM would leave most of the GPU idle (a
-// grid of few 256 x 256 tiles, each walking all of K).  Estimates from the measured rates
-// (14B / 24B shapes): a pass streams the weights at ~2.9 TB/s and takes at least 8 us; a
-// GEMM round of up to 256 tiles takes ~1.5 us per 64-input step.
+// Above 32 rows the kernel runs one pass of 16 or 32 rows per grid row and reads the
+// weights once per pass; it is still taken where the prefill GEMM would leave most of the
+// GPU idle (a grid of few 256 x 256 tiles, each walking all of K).  Estimates from the
+// measured rates (14B / 24B shapes): a 16-row pass streams the weights at ~2.9 TB/s and
+// takes at least 8 us, a 32-row pass 1.45 times that; a GEMM round of up to 256 tiles
+// takes ~1.5 us per 64-input step.
 #ifndef QMM_BMV_FORCE
 #define QMM_BMV_FORCE 0
 #endif
 bool bmv_preferred(int epi, const GemvArgs& a, int64_t M) {
   if (!bmv_supports(epi, a, M)) return false;
   if (M <= 32 || QMM_BMV_FORCE) return true;
+  const int mb = bmv::tiles_for(M, a.K / bmv::kKStep);
   const double wbytes = double(a.rows) * double(a.K) * (0.5 + 4.0 / 64.0);
-  const double pass_us = wbytes / 2.9e6 > 8.0 ? wbytes / 2.9e6 : 8.0;
-  const double bmv_us = double((M + bmv::kRows - 1) / bmv::kRows) * pass_us;
+  const double pass_us = (wbytes / 2.9e6 > 8.0 ? wbytes / 2.9e6 : 8.0) * (mb == 2 ? 1.45 : 1.0);
+  const int64_t rows_per_pass = bmv::kRows * mb;
+  const double bmv_us = double((M + rows_per_pass - 1) / rows_per_pass) * pass_us;
   const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + 127) / 128 : (a.rows + 255) / 256;
   const int64_t rounds = ((M + 255) / 256 * n_tiles + 255) / 256;
   const double gemm_us = double(rounds) * double(a.K / 64) * 1.5;
   return bmv_us < gemm_us;
 }
 
+template <int G, int MB>
+static void launch_bmv_tiles(int epi, const GemvArgs& a, int64_t M, int64_t units, hipStream_t st) {
+  constexpr int64_t kCUs = 256;
+  const dim3 grid{unsigned(units < kCUs ? units : kCUs), unsigned((M + bmv::kRows * MB - 1) / (bmv::kRows * MB)), 1u};
+  const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
+  if (epi == EPI_LINEAR)
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units);
+  else if (epi == EPI_QKV)
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);
+  else
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);
+}
+
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {
   if (!bmv_supports(epi, a, M)) return 2;
   const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)
                                           : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
-  constexpr int64_t kCUs = 256;
-  const dim3 grid{unsigned(units < kCUs ? units : kCUs), unsigned((M + bmv::kRows - 1) / bmv::kRows), 1u};
-  const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
-  switch (a.K / bmv::kKStep) {
-#define QMM_BMV_CASE(G)                                                                                   \
-  case G:                                                                                                 \
-    if (epi == EPI_LINEAR)                                                                                \
-      bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units);            \
-    else if (epi == EPI_QKV)                                                                              \
-      bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);               \
-    else                                                                                                  \
-      bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);            \
+  const int64_t gps = a.K / bmv::kKStep;
+  const bool two = bmv::tiles_for(M, gps) == 2;
+  switch (gps) {
+#define QMM_BMV_CASE(G)                                                               \
+  case G:                                                                             \
+    if constexpr (G <= bmv::kMaxGpsTwoTiles) {                                        \
+      if (two) {                                                                      \
+        launch_bmv_tiles<G, 2>(epi, a, M, units, st);                                 \
+        break;                                                                        \
+      }                                                                               \
+    }                                                                                 \
+    launch_bmv_tiles<G, 1>(epi, a, M, units, st);                                     \
     break;
     QMM_BMV_GPS(QMM_BMV_CASE)
 #undef QMM_BMV_CASE
