@@ -132,7 +132,7 @@ inline int launch_moe_down(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bi
 inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_gemm(epi, a, s)) }
 
 // Small batches (2 <= M <= kBmvMaxM) of the 4-bit group-64 projections whose K is a
-// multiple of 512 up to 8192: the weights streamed once per 16 activation rows, the
+// multiple of 512 up to 8192: the weights streamed once per 16 or 32 activation rows, the
 // activations on the matrix cores (bmv_u4.hip).  Linear, fused QKV and fused
 // gate+up+SwiGLU.  bmv_preferred: taken for M <= 32, and above where it beats the
 // prefill GEMM's estimate.

@@ -53,7 +53,7 @@
  *   - M = 1 runs a bandwidth-bound GEMV.  For 4-bit group-64 linear / fused QKV / fused
  *     gate+up with K a multiple of 512 up to 8192, 2 <= M <= 32 (and up to 256 where it
  *     is estimated faster than the GEMM) runs a small-batch kernel that streams the
- *     weights once per 16 activation rows with the activations on the matrix cores;
+ *     weights once per 16 or 32 activation rows with the activations on the matrix cores;
  *     otherwise M <= 8 runs the GEMV once per activation row and larger M an
  *     LDS-dequant + MFMA GEMM ("Sanctum-MLX", "Latency testing": prefill is dominated by
  *     the quantized matmuls).  The regimes agree to the tolerance, not bit for bit (the

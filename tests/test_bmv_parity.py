@@ -1,5 +1,5 @@
 """GPU parity of the small-batch path (u4 group 64, K a multiple of 512 up to 8192:
-activations on the matrix cores, the weights streamed once per 16 rows; taken for
+activations on the matrix cores, the weights streamed once per 16 or 32 rows; taken for
 2 <= M <= 32 and above where the prefill GEMM would be slower) against the fp64 oracle.
 
 Acceptance as for the decode GEMV (the oracle's `tolerance`, propagated for SwiGLU): the
