@@ -322,14 +322,17 @@ def bench_prefill(torch, qmm, synth, T, dev, pq, pg, reps):
 
 
 def bench_small_batch(torch, qmm, synth, T, dev, pq, pg):
-    """Decode of a small batch (M activation rows) on the 14B layer: fused QKV and fused
-    gate+up+SwiGLU over the rotating weight pool, per M; M = 1 is the GEMV, 2..32 the
-    small-batch kernel, above it the prefill GEMM."""
+    """Decode of a small batch (M activation rows) on the 14B layer: fused QKV (plain and
+    with rotary embedding) and fused gate+up+SwiGLU over the rotating weight pool, per M;
+    M = 1 is the GEMV, 2..32 the small-batch kernel, above it whichever of the
+    small-batch kernel and the prefill GEMM is estimated faster."""
     sh = synth.DENSE_14B
+    rs = synth.ROPE_14B  # the same 7168-row fused QKV, with its rotary layout
     K, I = sh.K, sh.I
     P = pq[0].shape[0]
     st = T.stream
     wbytes = (sh.qkv_rows + 2 * I) * (K // 2 + (K // 64) * 4)
+    tab = up(torch, dev, synth.gen_rope_table(synth.ROPE_MAX_POS, rs.rot, rs.base).view(np.int32)).view(torch.float32)
     out = {}
     for M in (1, 2, 4, 8, 16, 32, 64):
         x = up(torch, dev, synth.gen_x(synth.CFG_14B, 0, 0, M, K))
@@ -341,10 +344,16 @@ def bench_small_batch(torch, qmm, synth, T, dev, pq, pg):
                                                          stream=st), 2 * P)
         ms_g = T.per_call_ms(lambda i: qmm.qmm_fused_gate_up_swiglu(x, pg[0][i % P], pg[1][i % P], pg[2][i % P], h,
                                                                     stream=st), 2 * P)
+        pos = torch.from_numpy(synth.gen_positions(synth.CFG_14B, 0, M, synth.ROPE_MAX_POS).astype(np.int32)).to(dev)
+        qr, kr, vr = (q.view(M, rs.n_q, rs.head_dim), k.view(M, rs.n_kv, rs.head_dim),
+                      v.view(M, rs.n_kv, rs.head_dim))
+        ms_r = T.per_call_ms(lambda i: qmm.qmm_fused_qkv_rope(x, pq[0][i % P], pq[1][i % P], pq[2][i % P], qr, kr, vr,
+                                                              pos, tab, rs.rot, stream=st), 2 * P)
         us = (ms_q + ms_g) * 1e3
-        out[f"M={M}"] = {"qkv_us": round(ms_q * 1e3, 2), "gate_up_us": round(ms_g * 1e3, 2),
+        out[f"M={M}"] = {"qkv_us": round(ms_q * 1e3, 2), "qkv_rope_us": round(ms_r * 1e3, 2),
+                         "gate_up_us": round(ms_g * 1e3, 2),
                          "weights_GB/s": round(wbytes / (us * 1e-6) / 1e9, 1),
-                         "kernel": "gemv" if M == 1 else ("bmv" if M <= 32 else "gemm")}
+                         "kernel": "gemv" if M == 1 else ("bmv" if M <= 32 else "bmv or gemm (estimate)")}
     return {"workload": "14B layer decode of M sequences: fused QKV [7168 x 5120] + fused gate+up+SwiGLU "
                         "[27648 x 5120], u4 g64, rotating 48-layer pool", **out}
 

@@ -10,11 +10,13 @@
 //
 // What is computed: y[m][n] = sum_k x[m][k] * (s[n, k/64] * q[n, k] + b[n, k/64]), with the
 // fused-QKV split and the SwiGLU epilogue of "The Cathedral Doubled Itself" (the two
-// fusions), for up to 16 activation rows per block (grid.y covers more).
+// fusions) and the rotary QKV epilogue (qmm_rope.h), for 16 or 32 activation rows per
+// block (grid.y covers more).
 //
 // Layout of the work:
 //   * a unit is 16 weight rows (QKV / linear: 16 consecutive rows; SwiGLU: 8 gate rows
-//     and their 8 up rows); a block of S waves walks units with a grid stride, wave s
+//     and their 8 up rows; rotary QKV: the two rows of 8 rotating pairs); a block of S
+//     waves walks units with a grid stride, wave s
 //     owning the K slice [s*K/S, (s+1)*K/S) of every unit;
 //   * the unit's packed codes and its scales and biases go global -> LDS directly
 //     (buffer_load ... lds, 1 KB contiguous per wave instruction) into a ring of 2 to 4
@@ -34,6 +36,7 @@
 // result does not depend on the other rows of the batch or on M.
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_rope.h"
 
 namespace qmm {
 namespace bmv {
@@ -88,9 +91,14 @@ struct Layout {
 
 // Global row of LDS row r of unit u (past the end: the last real row, never stored).
 // 32-bit: the codes of a weight are below 4 GiB, so every row index and offset fits.
+// Rotary QKV: unit u is pairs 8u .. 8u+7, which (head_dim and rot multiples of 16) share
+// one head and one region, so their first rows are ra0 .. ra0+7 and their partners
+// rb0 .. rb0+7 (ra0, rb0 of pair 8u, passed in as `I` and `rows`).
 template <int EPI>
 __device__ __forceinline__ uint32_t unit_row(uint32_t rows, uint32_t I, uint32_t u, int r) {
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_ROPE) {
+    return r < 8 ? I + uint32_t(r) : rows + uint32_t(r - 8);
+  } else if constexpr (EPI == EPI_SWIGLU) {
     const uint32_t p = min(u * (kUnit / 2) + uint32_t(r & 7), I - 1);
     return r < 8 ? p : I + p;
   } else {
@@ -163,11 +171,17 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   const __amdgpu_buffer_rsrc_t sbr = sb_bias ? br : sr;
   auto request = [&](int64_t u, int buf) {
     uint8_t* base = lds + buf * L::buf_bytes;
+    uint32_t rows_arg = rows32, i_arg = I32;
+    if constexpr (EPI == EPI_ROPE) {
+      const RopePair rp = rope_pair(uint32_t(u) * 8u, a.rope);  // block-uniform
+      i_arg = uint32_t(rp.ra);
+      rows_arg = uint32_t(rp.rb);
+    }
 #pragma unroll
     for (int t = 0; t < L::code_per_wave; ++t) {
       const int i = t * kSlices + s;  // wave-uniform
       const bool real = L::code_dma % kSlices == 0 || i < L::code_dma;
-      const uint32_t off = real ? unit_row<EPI>(rows32, I32, uint32_t(u), crow[t]) * uint32_t(L::row_bytes) + cofs[t]
+      const uint32_t off = real ? unit_row<EPI>(rows_arg, i_arg, uint32_t(u), crow[t]) * uint32_t(L::row_bytes) + cofs[t]
                                 : 0xFFFFFFF0u;
       uint8_t* dst = real ? base + 1024 * i : lds + L::dump_off;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
@@ -175,7 +189,7 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     // past the scales (padding of the region) or no instruction for this wave: a load
     // beyond every buffer returns zero
     const uint32_t off = sb_any && sb_o < uint32_t(L::sb_bytes)
-                             ? unit_row<EPI>(rows32, I32, uint32_t(u), sb_r) * uint32_t(L::sb_row) + sb_in
+                             ? unit_row<EPI>(rows_arg, i_arg, uint32_t(u), sb_r) * uint32_t(L::sb_row) + sb_in
                              : 0xFFFFFFF0u;
     uint8_t* dst = sb_any ? base + L::code_bytes + (sb_bias ? L::sb_pad : 0) + 1024 * sb_j : lds + L::dump_off;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sbr, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
@@ -225,7 +239,33 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
       for (int j = 0; j < kSlices; ++j) v += rb[((j * MB + t) * 64 + l) * 4 + r];
       return v;
     };
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_ROPE) {
+      // like SwiGLU below: the 8 first rows of the unit's pairs and their partners 8
+      // columns further; each pair of each row is rotated by the row's position and
+      // stored into its head
+      if (lane < 128 * MB / kSlices) {
+        const int o = (128 * MB / kSlices) * s + lane;
+        const int t = o >> 7, g = (o & 127) >> 2, r = o & 3;
+        const int l = (g & 7) + 16 * (g >> 3);
+        const int mr = kRows * t + 4 * (l >> 4) + r;
+        if (mr < rows_here) {
+          const int64_t m = mb * R + mr;
+          RopePair rp = rope_pair(uint32_t(uu) * 8u, a.rope);
+          const int e = l & 15;  // pair 8 uu + e
+          rp.ra += e;
+          rp.rb += e;
+          rp.da += e;
+          rp.db += e;
+          if (rp.ri >= 0) rp.ri += e;
+          float va = slice_sum(t, l, r), vb = slice_sum(t, l + 8, r);
+          if (a.lin_bias) {
+            va += bf16_bits_to_f32(a.lin_bias[rp.ra]);
+            vb += bf16_bits_to_f32(a.lin_bias[rp.rb]);
+          }
+          rope_store(a.rope, a.out0, a.out1, a.out2, rp, m, va, vb, a.f32_out);
+        }
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
       // 8 gate columns x R rows = 128 MB outputs, 128 MB / S per wave: output o of tile
       // t = o / 128 is gate column g % 8 of block g / 8 (g = (o % 128) / 4) at r = o % 4,
       // with its up column 8 further
@@ -361,7 +401,9 @@ inline int tiles_for(int64_t M, int64_t gps) {
 
 bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
   if (a.bits != 4 || a.gshift != 1 || M < 2 || M > kBmvMaxM || a.K % bmv::kKStep) return false;
-  if (epi != EPI_LINEAR && epi != EPI_QKV && epi != EPI_SWIGLU) return false;
+  if (epi != EPI_LINEAR && epi != EPI_QKV && epi != EPI_SWIGLU && epi != EPI_ROPE) return false;
+  // rotary: units of 8 pairs within one head and one region
+  if (epi == EPI_ROPE && (a.rope.head_dim % 16 || a.rope.rot % 16)) return false;
   switch (a.K / bmv::kKStep) {
 #define QMM_BMV_CASE(G) case G:
     QMM_BMV_GPS(QMM_BMV_CASE)
@@ -389,7 +431,9 @@ bool bmv_preferred(int epi, const GemvArgs& a, int64_t M) {
   const double pass_us = (wbytes / 2.9e6 > 8.0 ? wbytes / 2.9e6 : 8.0) * (mb == 2 ? 1.45 : 1.0);
   const int64_t rows_per_pass = bmv::kRows * mb;
   const double bmv_us = double((M + rows_per_pass - 1) / rows_per_pass) * pass_us;
-  const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + 127) / 128 : (a.rows + 255) / 256;
+  const int64_t n_tiles = epi == EPI_SWIGLU  ? (a.I + 127) / 128
+                          : epi == EPI_ROPE  ? ((a.rows >> 1) + 127) / 128
+                                             : (a.rows + 255) / 256;
   const int64_t rounds = ((M + 255) / 256 * n_tiles + 255) / 256;
   const double gemm_us = double(rounds) * double(a.K / 64) * 1.5;
   return bmv_us < gemm_us;
@@ -404,13 +448,18 @@ static void launch_bmv_tiles(int epi, const GemvArgs& a, int64_t M, int64_t unit
     bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units);
   else if (epi == EPI_QKV)
     bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);
+  else if (epi == EPI_ROPE)
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_ROPE><<<grid, block, 0, st>>>(a, M, units);
   else
     bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);
 }
 
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {
   if (!bmv_supports(epi, a, M)) return 2;
+  // SwiGLU: 8 gate/up pairs per unit; rotary QKV: 8 rotating pairs (rows/2 is a multiple
+  // of 8 here); otherwise 16 rows
   const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)
+                        : epi == EPI_ROPE ? (a.rows >> 1) / (bmv::kUnit / 2)
                                           : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
   const int64_t gps = a.K / bmv::kKStep;
   const bool two = bmv::tiles_for(M, gps) == 2;

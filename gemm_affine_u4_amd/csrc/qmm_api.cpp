@@ -251,6 +251,7 @@ int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K, const uint32_t* 
   a.rope.head_dim = int32_t(head_dim);
   a.rope.rot = int32_t(rot_dim);
   a.rope.q_gate = q_gate;
+  if (qmm::bmv_preferred(qmm::EPI_ROPE, a, M)) return qmm::launch_bmv(qmm::EPI_ROPE, a, M, stream);
   if (M > kGemvMaxM) return qmm::launch_gemm(qmm::EPI_ROPE, gemm_args(a, M, rows), stream);
   return qmm::launch_gemv(qmm::EPI_ROPE, a, M, stream);
 }

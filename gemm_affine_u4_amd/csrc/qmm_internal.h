@@ -133,8 +133,8 @@ inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH
 
 // Small batches (2 <= M <= kBmvMaxM) of the 4-bit group-64 projections whose K is a
 // multiple of 512 up to 8192: the weights streamed once per 16 or 32 activation rows, the
-// activations on the matrix cores (bmv_u4.hip).  Linear, fused QKV and fused
-// gate+up+SwiGLU.  bmv_preferred: taken for M <= 32, and above where it beats the
+// activations on the matrix cores (bmv_u4.hip).  Linear, fused QKV, fused gate+up+SwiGLU
+// and fused QKV with rotary embedding (head_dim and rot multiples of 16).  bmv_preferred: taken for M <= 32, and above where it beats the
 // prefill GEMM's estimate.
 constexpr int64_t kBmvMaxM = 256;
 bool bmv_supports(int epi, const GemvArgs& a, int64_t M);

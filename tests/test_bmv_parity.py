@@ -158,3 +158,39 @@ def test_ragged_last_pass():
     x = synth.gen_x(synth.CFG_TEST, 440, 0, M, K)
     h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, I)
     assert_within(run_gate_up(x, w, I), h, th, f"gate+up M={M}")
+
+
+@pytest.mark.parametrize("M", [2, 16, 33])
+@pytest.mark.parametrize("sh", [synth.ROPE_14B, synth.ROPE_GATED], ids=["14B", "gated"])
+def test_fused_qkv_rope(sh, M):
+    """Fused QKV + split + rotary embedding through the small-batch kernel (units of 8
+    rotating pairs): against the oracle, and bf16 = RNE(fp32)."""
+    say(f"[bmv] qkv+rope {sh.name} M={M}")
+    max_pos = 4096
+    w = synth.gen_weight(synth.CFG_TEST, 450 + M, synth.PROJ_QKV, sh.rows, sh.K)
+    lb = synth.gen_lin_bias(synth.CFG_TEST, 450 + M, sh.rows)
+    x = synth.gen_x(synth.CFG_TEST, 450 + M, 0, M, sh.K)
+    pos = synth.gen_positions(synth.CFG_TEST, 450 + M, M, max_pos, contiguous=False)
+    tab = synth.gen_rope_table(max_pos, sh.rot, sh.base)
+
+    def run(f32):
+        outs = [Guarded((M, sh.n_q, sh.head_dim), f32), Guarded((M, sh.n_kv, sh.head_dim), f32),
+                Guarded((M, sh.n_kv, sh.head_dim), f32)]
+        g = Guarded((M, sh.n_q, sh.head_dim), f32) if sh.q_gate else None
+        qmm.qmm_fused_qkv_rope(dev(x), dev(w.codes), dev(w.scales), dev(w.biases), outs[0].t, outs[1].t, outs[2].t,
+                               dev(np.asarray(pos, np.int32)), dev(tab), sh.rot, gate=g.t if g else None,
+                               lin_bias=dev(lb))
+        torch.cuda.synchronize()
+        return outs[0].values(), (g.values() if g else None), outs[1].values(), outs[2].values()
+
+    got = run(True)
+    ref, tol = orc.qkv_rope(x, w.codes, w.scales, w.biases, sh.n_q, sh.n_kv, sh.head_dim, sh.q_gate, sh.rot,
+                            pos, tab, lb)
+    for name, g, r, t in zip(("q", "gate", "k", "v"), got, ref, tol):
+        if r is None:
+            assert g is None
+            continue
+        assert_within(g, r, t, f"{sh.name} M={M} {name}")
+    for g32, g16 in zip(got, run(False)):
+        if g32 is not None:
+            assert np.array_equal(g16, rne_bits_of(g32))
