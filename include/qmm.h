@@ -156,8 +156,9 @@ int qmm_fused_gate_up_swiglu(const uint16_t* x, int64_t M, int64_t K,
  *   positions: device int32 [M]; values outside [0, max_pos) are clamped to that range.
  *   cos_sin: device fp32 [max_pos][rot_dim], built once by the caller (cos in the first
  *   half of a row, sin in the second).
- *   head_dim and rot_dim even, 2 <= rot_dim <= head_dim; q_gate 0 or 1.  Decode (M <= 8)
- *   runs the GEMV, larger M the GEMM, as for qmm_fused_qkv.
+ *   head_dim and rot_dim even, 2 <= rot_dim <= head_dim; q_gate 0 or 1.  The regimes are
+ *   those of qmm_fused_qkv (the small-batch kernel needs head_dim and rot_dim multiples
+ *   of 16 as well).
  */
 int qmm_fused_qkv_rope(const uint16_t* x, int64_t M, int64_t K,
                        const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,

@@ -1,7 +1,9 @@
 """GPU parity of the fused QKV + split + rotary embedding (qmm_fused_qkv_rope) against the
-fp64 oracle, for decode (GEMV, M <= 8) and prefill (GEMM), full and partial rotary, with
-and without the per-head output gate; plus two exact identities: at angle zero the
-outputs are the plain fused QKV outputs bit for bit, and bf16 output = RNE(fp32 output)."""
+fp64 oracle, in every regime (the GEMV at M = 1 and, where the small-batch kernel does
+not apply, up to M = 8; the small-batch kernel; the prefill GEMM), full and partial
+rotary, with and without the per-head output gate; plus two exact identities: at angle
+zero the outputs are the plain fused QKV outputs bit for bit, and bf16 output =
+RNE(fp32 output)."""
 import numpy as np
 import pytest
 import torch
