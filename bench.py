@@ -583,6 +583,23 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
     ms_s1 = T.per_call_ms(s1, reps)
     ms_s2 = T.per_call_ms(s2, reps)
     ms_layer = T.per_call_ms(layer, reps)
+    # small batches (the first Ms tokens of the same routing): pair by pair, no bucketing
+    small = {}
+    for Ms in (1, 4, 16, 64):
+        ids_s, x_s, h_s, y_s, pw_s = ids[:Ms], x[:Ms], h[:Ms], y[:Ms], pw[:Ms]
+
+        def layer_s(i, ids_s=ids_s, x_s=x_s, h_s=h_s, y_s=y_s, pw_s=pw_s):
+            l = i % L
+            qmm.qmm_moe_route(ids_s, E, ws, stream=st)
+            qmm.qmm_moe_prefill(qmm.QMM_MOE_GATE_UP_SWIGLU, x_s, pgu[0][l], pgu[1][l], pgu[2][l], ids_s, ws, h_s,
+                                stream=st)
+            qmm.qmm_moe_prefill(qmm.QMM_MOE_DOWN_COMBINE, h_s, pdn[0][l], pdn[1][l], pdn[2][l], ids_s, ws, y_s,
+                                expert_w=pw_s, stream=st)
+        u_s = len(np.unique(ids_np[:Ms]))
+        b_s = u_s * (weight_bytes(2 * Ie, H) + weight_bytes(H, Ie))
+        ms_s = T.per_call_ms(layer_s, reps)
+        small[f"M={Ms}"] = {"us_per_layer": round(ms_s * 1e3, 2), "experts_used": u_s,
+                            "expert_weight_GB/s": round(b_s / (ms_s * 1e-3) / 1e9, 1)}
     P = int((ids_np >= 0).sum())
     used = np.unique(ids_np)
     fl1 = 2.0 * P * 2 * Ie * H
@@ -603,7 +620,9 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
             "TFLOP/s_per_layer": round((fl1 + fl2) / (ms_layer * 1e-3) / 1e12, 1),
             "route": {"avg_us": round(ms_route * 1e3, 2)},
             "gate_up_swiglu": rec(ms_s1, fl1, b1),
-            "down_combine": rec(ms_s2, fl2, b2)}
+            "down_combine": rec(ms_s2, fl2, b2),
+            "small_batches": {"note": "route + both stages per layer for the first M tokens of the same "
+                                      "routing; M * topk <= 768 runs pair by pair", **small}}
 
 
 def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step):

@@ -263,10 +263,12 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
   const uint16_t* x = a.x;
   int64_t out_base;
   if constexpr (MOE) {
-    // blockIdx.y is the routed slot k; its expert's rows are read in place from the grid.
+    // blockIdx.y is the routed slot k; its expert's rows are read in place from the grid,
+    // its activation row is k / moe_div (several tokens) or the one row.
     const int k = blockIdx.y;
     const int32_t e = a.expert_ids[k];
     out_base = int64_t(k) * a.I;
+    if (a.moe_div > 0) x += (int64_t(k) / a.moe_div) * a.K;
     if (e < 0 || e >= a.E) {
       // no expert: this slot's h is zero
       if (ks == 0) {
@@ -404,10 +406,12 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   int64_t out_base;
   if constexpr (MOE) {
     // blockIdx.y is the routed slot k (the whole block shares it); its expert's rows are
-    // read in place from the grid.
+    // read in place from the grid, its activation row is k / moe_div (several tokens) or
+    // the one row.
     const int k = blockIdx.y;
     const int32_t e = a.expert_ids[k];
     out_base = int64_t(k) * a.I;
+    if (a.moe_div > 0) x += (int64_t(k) / a.moe_div) * a.K;
     if (e < 0 || e >= a.E) {
       // no expert: this slot's h is zero
       for (int64_t u = u_begin; u < u_end; ++u) {
@@ -509,7 +513,8 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   }
 }
 
-// Routed-expert stage 2: y[r] = sum_k p_k * (D_{e_k} h_k)[r].  A block's kw waves split
+// Routed-expert stage 2: y[r] = sum_k p_k * (D_{e_k} h_k)[r], for each token (blockIdx.y)
+// of its topk slots.  A block's kw waves split
 // the routed slots (wave w takes k = w, w+kw, ...) and walk the block's `upw` row units
 // for each; every wave adds its slots in increasing k into its own LDS slice, and the
 // slices are then added in wave order.  No atomics, so the order is fixed.
@@ -540,14 +545,16 @@ __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units
   if (result_lane)
     for (int u = 0; u < nu; ++u) red[wave][u][slot] = 0.f;
 
+  // blockIdx.y is the token: its slots are pairs token*topk + k of ids, weights and h
+  const int64_t pair0 = int64_t(blockIdx.y) * a.topk;
   for (int k = wave; k < a.topk; k += kw) {
-    const int32_t e = a.expert_ids[k];
+    const int32_t e = a.expert_ids[pair0 + k];
     if (e < 0 || e >= a.E) continue;  // no expert: contributes nothing
-    const float p = a.expert_w[k];
+    const float p = a.expert_w[pair0 + k];
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes + uint64_t(e) * expert_words, expert_words * 4);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales + uint64_t(e) * expert_groups, expert_groups * 2);
     const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases + uint64_t(e) * expert_groups, expert_groups * 2);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + int64_t(k) * a.K, uint64_t(a.K) * 2);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + (pair0 + k) * a.K, uint64_t(a.K) * 2);
     RowData<CPL> cur, nxt;
     load_row<LPR, CPL>(cur, cr, sr, br, uint32_t(u_begin * RPI + slot), row_bytes, row_groups, c0, a.gshift);
     uint32_t xp[CPL][16];
@@ -568,7 +575,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units
     if (r < a.rows) {
       float v = 0.f;
       for (int j = 0; j < kw; ++j) v += red[j][u][slot];
-      store_out(a.out0, r, v, a.f32_out);
+      store_out(a.out0, int64_t(blockIdx.y) * a.rows + r, v, a.f32_out);
     }
   }
 }
@@ -719,7 +726,7 @@ int launch_moe_down(const GemvArgs& a, hipStream_t s) {
   int64_t upw = (units + QMM_MOE_DOWN_BLOCKS - 1) / QMM_MOE_DOWN_BLOCKS;
   if (upw > kMaxUnitsPerCombineBlock) upw = kMaxUnitsPerCombineBlock;
   if (upw < 1) upw = 1;
-  const dim3 grid{unsigned((units + upw - 1) / upw), 1u, 1u};
+  const dim3 grid{unsigned((units + upw - 1) / upw), unsigned(a.moe_tokens > 0 ? a.moe_tokens : 1), 1u};
   const dim3 block{unsigned(64 * kw), 1u, 1u};
   switch (sh.lpr * 100 + sh.cpl) {
     case 1601: moe_down_kernel<16, 1><<<grid, block, 0, s>>>(a, units, int(upw)); break;

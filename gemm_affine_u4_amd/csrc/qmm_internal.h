@@ -59,7 +59,9 @@ struct GemvArgs {
   const int32_t* expert_ids;  // MoE (nullable otherwise)
   const float* expert_w;      // MoE stage 2
   int64_t E;               // experts in the grid
-  int topk;
+  int64_t moe_div;         // stage 1: activation row of slot k is k / moe_div (0: one row)
+  int64_t moe_tokens;      // stage 2: tokens, topk slots each (0: one token)
+  int topk;                // stage 1: slots (grid.y); stage 2: slots per token
   int f32_out;
   int bits;                // code width (2, 3, 4, 6 or 8) or kFmtFp8E4M3
   int gshift;              // group size = 32 << gshift (scales/biases per 32, 64 or 128 inputs)

@@ -204,6 +204,11 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K,
  *                    (deterministic: by expert, then by pair index);
  *   qmm_moe_prefill  stage QMM_MOE_GATE_UP_SWIGLU, then stage QMM_MOE_DOWN_COMBINE,
  *                    both reading that routing.
+ * A small batch (M * topk <= 768 pairs: most experts then see one token or none) runs
+ * pair by pair instead, on the kernels of qmm_moe_gather: stage 1 one SwiGLU GEMV per
+ * (token, slot) pair, stage 2 each token's weighted sum over its slots (expert I <= 5120;
+ * a wider one is routed by stage 2 itself and runs the GEMM).  The stages then read
+ * expert_ids directly and qmm_moe_route does nothing, so the call order above still holds.
  * workspace: caller-owned device memory, 256-byte aligned, of at least
  * qmm_moe_prefill_workspace_bytes(M, topk, E, out_rows) bytes, where out_rows is the
  * row count of the down projection (0 if only stage 1 runs).  It holds the routing

@@ -154,3 +154,14 @@ def test_moe_prefill_35B_shape_full_batch_sampled_tokens():
     assert_within(g1[sample], h, th, "35B stage 1 (sampled tokens)")
     y, ty = orc.moe_prefill_down_combine(h_in[sample], dn.codes, dn.scales, dn.biases, ids[sample], p[sample])
     assert_within(g2[sample], y, ty, "35B stage 2 (sampled tokens)")
+
+
+def test_small_batch_pair_path_and_wide_expert():
+    """Few pairs (M * topk <= 768) run the decode gather kernels pair by pair and the
+    routing call does nothing; a down projection wider than those kernels take (expert
+    I = 5632 > 5120) makes stage 2 route on its own and run the gathered GEMM."""
+    shape = synth.MoEShape("wide-expert MoE (hidden 128, 4 experts, I 5632, top-2)", 128, 4, 5632, 2)
+    M = 5
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 7, M, shape.E, shape.topk)
+    say(f"[moe prefill] {shape.name}, M={M}")
+    check_both_stages(shape, synth.CFG_TEST, 7, M, ids, p, "wide expert")
