@@ -583,9 +583,9 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
     ms_s1 = T.per_call_ms(s1, reps)
     ms_s2 = T.per_call_ms(s2, reps)
     ms_layer = T.per_call_ms(layer, reps)
-    # small batches (the first Ms tokens of the same routing): pair by pair, no bucketing
+    # smaller batches (the first Ms tokens of the same routing)
     small = {}
-    for Ms in (1, 4, 16, 64):
+    for Ms in (1, 4, 16, 64, 256, 512):
         ids_s, x_s, h_s, y_s, pw_s = ids[:Ms], x[:Ms], h[:Ms], y[:Ms], pw[:Ms]
 
         def layer_s(i, ids_s=ids_s, x_s=x_s, h_s=h_s, y_s=y_s, pw_s=pw_s):
@@ -622,7 +622,8 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
             "gate_up_swiglu": rec(ms_s1, fl1, b1),
             "down_combine": rec(ms_s2, fl2, b2),
             "small_batches": {"note": "route + both stages per layer for the first M tokens of the same "
-                                      "routing; M * topk <= 768 runs pair by pair", **small}}
+                                      "routing; M * topk <= 512 runs pair by pair, up to 24 pairs per expert "
+                                      "on the gathered small-batch kernel, above on the gathered GEMM", **small}}
 
 
 def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step):

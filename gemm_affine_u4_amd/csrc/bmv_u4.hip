@@ -124,8 +124,13 @@ __device__ __forceinline__ void wait_units_barrier(int ahead) {
   }
 }
 
-template <int S, int GPS, int MB, int EPI>
-__global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units) {
+// GATHER (routed experts over a batch): block y is tile y of the routing's tile table
+// (up to 256 bucketed pairs of one expert), taken in passes of R pairs.  The activation
+// row of a pair is pair / gth.div; the outputs go to the pairs' rows (stage 2: times the
+// pair's combine weight, fp32).
+// gth: the routing (tile table, bucket offsets, bucketed pairs), combine weights, x rows.
+template <int S, int GPS, int MB, int EPI, bool GATHER>
+__global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units, BmvGather gth) {
   using L = Layout<S, GPS, MB>;
   constexpr int R = kRows * MB;  // activation rows per block
   constexpr int K = L::K;
@@ -137,7 +142,21 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   const int col = lane & 15;  // MFMA column: LDS row of the unit
   const int kb = lane >> 4;   // 8-input block of the MFMA's 32 inputs
   const int64_t mb = blockIdx.y;
-  const int64_t rows_here = M - mb * R < R ? M - mb * R : R;
+  int64_t rows_here = M - mb * R < R ? M - mb * R : R;
+  int64_t first = 0, end = 0;  // GATHER: bucket positions of the pass's first pair, tile end
+  if constexpr (GATHER) {
+    if (mb >= gth.hdr[0]) return;
+    const int e = gth.tiles[2 * mb];
+    first = gth.tiles[2 * mb + 1];
+    end = min(int64_t(gth.offsets[e + 1]), first + kMoeTileRows);
+    if (first >= end) return;
+    rows_here = end - first < R ? end - first : R;
+    // the expert's rows, in place in the grid
+    const int64_t er = int64_t(e) * a.rows;
+    a.codes += er * (K / 8);
+    a.scales += er * (K / 64);
+    a.biases += er * (K / 64);
+  }
   const uint64_t nrows = uint64_t(a.rows);
   const uint32_t rows32 = uint32_t(a.rows), I32 = uint32_t(a.I);
 
@@ -195,189 +214,219 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sbr, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
   };
 
-  int64_t u = blockIdx.x;
-  if (u >= units) return;
+  if (int64_t(blockIdx.x) >= units) return;
   const int64_t stride = gridDim.x;
-  // the block's units j = 0, 1, ... (unit u + j * stride) live in buffer j % nbuf; units
-  // 0 .. lookahead - 1 are requested here, unit j + lookahead at step j
+  // GATHER: the passes of the tile one after the other, over the same units (the second
+  // pass reads them from L2)
+  for (;;) {
+    int64_t u = blockIdx.x;
+    // the block's units j = 0, 1, ... (unit u + j * stride) live in buffer j % nbuf; units
+    // 0 .. lookahead - 1 are requested here, unit j + lookahead at step j
 #pragma unroll
-  for (int b = 0; b < L::lookahead; ++b)
-    if (u + b * stride < units) request(u + b * stride, b);
+    for (int b = 0; b < L::lookahead; ++b)
+      if (u + b * stride < units) request(u + b * stride, b);
 
-  // ---- activations of this slice: MFMA operands, permuted to the nibble-pair order ----
-  // Operand lane (row m = lane % 16 of tile t, block kb) of group g, MFMA h holds inputs
-  // 64 G + 16 kb + 8 h .. +7 with G = s*GPS + g: the 8 codes its column's lane decodes
-  // from code word h of that lane's 16 codes.
-  bf16x8_t xa[MB][GPS][2];
-  {
-    const uint16_t* xb = a.x + mb * R * K;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, uint64_t(rows_here) * K * 2);
-#pragma unroll
-    for (int t = 0; t < MB; ++t)
-#pragma unroll
-      for (int g = 0; g < GPS; ++g)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t k0 = uint32_t(64 * (s * GPS + g) + 16 * kb + 8 * h);
-          const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t(kRows * t + col) * K + k0) * 2u, 0, 0);
-          const u32x4_t p = {__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
-                             __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
-          xa[t][g][h] = __builtin_bit_cast(bf16x8_t, p);
-        }
-  }
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-  const uint32_t magic = in_vgpr(kMagicPair);
-  float* red = reinterpret_cast<float*>(lds + L::red_off);
-
-  // sums of the S slice partials in slice order and the epilogue of unit uu, each output
-  // by one lane of one of the waves; rb[j][t][l][r] is slice j's partial of activation row
-  // 16 t + 4 (l / 16) + r, column l % 16
-  auto epilogue = [&](int64_t uu, const float* rb) {
-    auto slice_sum = [&](int t, int l, int r) {
-      float v = 0.f;
-#pragma unroll
-      for (int j = 0; j < kSlices; ++j) v += rb[((j * MB + t) * 64 + l) * 4 + r];
-      return v;
-    };
-    if constexpr (EPI == EPI_ROPE) {
-      // like SwiGLU below: the 8 first rows of the unit's pairs and their partners 8
-      // columns further; each pair of each row is rotated by the row's position and
-      // stored into its head
-      if (lane < 128 * MB / kSlices) {
-        const int o = (128 * MB / kSlices) * s + lane;
-        const int t = o >> 7, g = (o & 127) >> 2, r = o & 3;
-        const int l = (g & 7) + 16 * (g >> 3);
-        const int mr = kRows * t + 4 * (l >> 4) + r;
-        if (mr < rows_here) {
-          const int64_t m = mb * R + mr;
-          RopePair rp = rope_pair(uint32_t(uu) * 8u, a.rope);
-          const int e = l & 15;  // pair 8 uu + e
-          rp.ra += e;
-          rp.rb += e;
-          rp.da += e;
-          rp.db += e;
-          if (rp.ri >= 0) rp.ri += e;
-          float va = slice_sum(t, l, r), vb = slice_sum(t, l + 8, r);
-          if (a.lin_bias) {
-            va += bf16_bits_to_f32(a.lin_bias[rp.ra]);
-            vb += bf16_bits_to_f32(a.lin_bias[rp.rb]);
-          }
-          rope_store(a.rope, a.out0, a.out1, a.out2, rp, m, va, vb, a.f32_out);
-        }
-      }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      // 8 gate columns x R rows = 128 MB outputs, 128 MB / S per wave: output o of tile
-      // t = o / 128 is gate column g % 8 of block g / 8 (g = (o % 128) / 4) at r = o % 4,
-      // with its up column 8 further
-      if (lane < 128 * MB / kSlices) {
-        const int o = (128 * MB / kSlices) * s + lane;
-        const int t = o >> 7, g = (o & 127) >> 2, r = o & 3;
-        const int l = (g & 7) + 16 * (g >> 3);
-        const int mr = kRows * t + 4 * (l >> 4) + r;  // row within the block
-        const int64_t p = uu * (kUnit / 2) + (l & 15);
-        if (mr < rows_here && p < a.I)
-          store_out(a.out0, (mb * R + mr) * a.n_out + p, silu_times(slice_sum(t, l, r), slice_sum(t, l + 8, r)),
-                    a.f32_out);
-      }
-    } else {
-      // 16 columns x R rows = 256 MB outputs, 256 MB / S per wave: output o of tile
-      // t = o / 256 is partial lane (o % 256) / 4 at r = o % 4
-      if (lane < 256 * MB / kSlices) {
-        const int o = (256 * MB / kSlices) * s + lane;
-        const int t = o >> 8, l = (o & 255) >> 2, r = o & 3;
-        const int mr = kRows * t + 4 * (l >> 4) + r;
-        const int64_t m = mb * R + mr;
-        const int64_t n = uu * kUnit + (l & 15);
-        if (mr < rows_here && n < a.rows) {
-          float v = slice_sum(t, l, r);
-          if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
-          if constexpr (EPI == EPI_QKV) {
-            if (n < a.q_out) {
-              store_out(a.out0, m * a.q_out + n, v, a.f32_out);
-            } else if (n < a.q_out + a.kv_out) {
-              store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
-            } else {
-              store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
-            }
-          } else {
-            store_out(a.out0, m * a.n_out + n, v, a.f32_out);
-          }
-        }
-      }
-    }
-  };
-
-  int it = 0;
-  for (;; ++it) {
-    const int buf = it % L::nbuf;
-    // request unit it + lookahead, then wait for unit it (the later units' loads may stay
-    // in flight); buffer (it + lookahead) % nbuf held unit it - 1 (without deferral: every
-    // wave has passed the barrier after reading it) or unit it - 2 (deferred: read before
-    // the last barrier)
-    const int64_t ua = u + L::lookahead * stride;
-    if (ua < units) request(ua, (it + L::lookahead) % L::nbuf);
-    const int64_t later = (units - 1 - u) / stride;  // units after u for this block
-    wait_units_barrier<L::dma_per_wave>(int(later < L::lookahead ? later : L::lookahead));
-    if constexpr (L::deferred) {
-      if (it > 0) epilogue(u - stride, red + ((it - 1) & 1) * (L::red_bytes / 4));
-    }
-
-    // ---- this wave's slice of unit u ----------------------------------------------------
-    const uint8_t* bb = lds + buf * L::buf_bytes;
-    const uint16_t* sc = reinterpret_cast<const uint16_t*>(bb + L::code_bytes) + col * (L::sb_row / 2);
-    const uint16_t* bi = reinterpret_cast<const uint16_t*>(bb + L::code_bytes + L::sb_pad) + col * (L::sb_row / 2);
-    f32x4_t y[MB] = {};
-#pragma unroll
-    for (int g = 0; g < GPS; ++g) {
-      const int G = s * GPS + g;
-      // codes 16 kb .. 16 kb + 15 of group G of this lane's column: half (kb & 1) of chunk
-      // 2G + kb/2
-      const uint32_t c = uint32_t(2 * G + (kb >> 1));
-      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bb + col * L::row_bytes + 16 * (c ^ uint32_t(col)) + 8 * (kb & 1));
-      const float sv = bf16_bits_to_f32(sc[G]);
-      const float bv = bf16_bits_to_f32(bi[G]);
-      u32x4_t q[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        q[h] = u32x4_t{nib_pair(w[h], 0, magic), nib_pair(w[h], 1, magic), nib_pair(w[h], 2, magic),
-                       nib_pair(w[h], 3, magic)};
+    // ---- activations of this slice: MFMA operands, permuted to the nibble-pair order ----
+    // Operand lane (row m = lane % 16 of tile t, block kb) of group g, MFMA h holds inputs
+    // 64 G + 16 kb + 8 h .. +7 with G = s*GPS + g: the 8 codes its column's lane decodes
+    // from code word h of that lane's 16 codes.
+    bf16x8_t xa[MB][GPS][2];
+    {
+      // byte offset of block row m's activations (rows past the block's: past the buffer,
+      // read as zeros); GATHER reads the pairs' rows through the bucket
+      const uint16_t* xb = GATHER ? a.x : a.x + mb * R * K;
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, uint64_t(GATHER ? gth.x_rows : rows_here) * K * 2);
+      uint32_t xrow[MB];
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
-        // xs[r] = sum of the group's 64 inputs of row 4 kb + r of tile t (the MFMA against
-        // ones puts that row's sum in every column; recomputed per unit, the matrix pipe is
-        // idle)
-        f32x4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][0], ones, f32x4_t{}, 0, 0, 0);
-        xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][1], ones, xs, 0, 0, 0);
-        f32x4_t d = {};
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][h], __builtin_bit_cast(bf16x8_t, q[h]), d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float dq = fmaf(-128.0f, xs[r], d[r]);  // sum x q (exact 0 for all-zero codes)
-          y[t][r] = fmaf(sv, dq, y[t][r]);
-          y[t][r] = fmaf(bv, xs[r], y[t][r]);
-        }
+        const int m = kRows * t + col;
+        if constexpr (GATHER)
+          xrow[t] = m < rows_here ? uint32_t(gth.pairs[first + m] / gth.div) * uint32_t(K) * 2u : 0xFFFFFFF0u;
+        else
+          xrow[t] = uint32_t(m) * uint32_t(K) * 2u;
       }
-    }
-    if constexpr (L::deferred) {
-      // partials of this unit into red buffer it & 1; summed and stored after the next
-      // step's barrier (or after the loop)
 #pragma unroll
       for (int t = 0; t < MB; ++t)
-        *reinterpret_cast<f32x4_t*>(red + (it & 1) * (L::red_bytes / 4) + ((s * MB + t) * 64 + lane) * 4) = y[t];
-    } else {
 #pragma unroll
-      for (int t = 0; t < MB; ++t) *reinterpret_cast<f32x4_t*>(red + ((s * MB + t) * 64 + lane) * 4) = y[t];
-      __syncthreads();
-      epilogue(u, red);
+        for (int g = 0; g < GPS; ++g)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t k0 = uint32_t(64 * (s * GPS + g) + 16 * kb + 8 * h);
+            const uint32_t off = xrow[t] == 0xFFFFFFF0u ? xrow[t] : xrow[t] + k0 * 2u;
+            const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            const u32x4_t p = {__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
+                               __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
+            xa[t][g][h] = __builtin_bit_cast(bf16x8_t, p);
+          }
     }
-    u += stride;
-    if (u >= units) break;
-  }
-  if constexpr (L::deferred) {
-    __syncthreads();
-    epilogue(u - stride, red + (it & 1) * (L::red_bytes / 4));
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    const uint32_t magic = in_vgpr(kMagicPair);
+    float* red = reinterpret_cast<float*>(lds + L::red_off);
+
+    // sums of the S slice partials in slice order and the epilogue of unit uu, each output
+    // by one lane of one of the waves; rb[j][t][l][r] is slice j's partial of activation row
+    // 16 t + 4 (l / 16) + r, column l % 16
+    // output row of block row mr: the batch row, or (GATHER) the pair's row
+    auto out_row = [&](int mr) -> int64_t {
+      if constexpr (GATHER) return gth.pairs[first + mr];
+      else return mb * R + mr;
+    };
+    auto epilogue = [&](int64_t uu, const float* rb) {
+      auto slice_sum = [&](int t, int l, int r) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < kSlices; ++j) v += rb[((j * MB + t) * 64 + l) * 4 + r];
+        return v;
+      };
+      if constexpr (EPI == EPI_ROPE) {
+        // like SwiGLU below: the 8 first rows of the unit's pairs and their partners 8
+        // columns further; each pair of each row is rotated by the row's position and
+        // stored into its head
+        if (lane < 128 * MB / kSlices) {
+          const int o = (128 * MB / kSlices) * s + lane;
+          const int t = o >> 7, g = (o & 127) >> 2, r = o & 3;
+          const int l = (g & 7) + 16 * (g >> 3);
+          const int mr = kRows * t + 4 * (l >> 4) + r;
+          if (mr < rows_here) {
+            const int64_t m = mb * R + mr;  // (no gathered rotary path)
+            RopePair rp = rope_pair(uint32_t(uu) * 8u, a.rope);
+            const int e = l & 15;  // pair 8 uu + e
+            rp.ra += e;
+            rp.rb += e;
+            rp.da += e;
+            rp.db += e;
+            if (rp.ri >= 0) rp.ri += e;
+            float va = slice_sum(t, l, r), vb = slice_sum(t, l + 8, r);
+            if (a.lin_bias) {
+              va += bf16_bits_to_f32(a.lin_bias[rp.ra]);
+              vb += bf16_bits_to_f32(a.lin_bias[rp.rb]);
+            }
+            rope_store(a.rope, a.out0, a.out1, a.out2, rp, m, va, vb, a.f32_out);
+          }
+        }
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        // 8 gate columns x R rows = 128 MB outputs, 128 MB / S per wave: output o of tile
+        // t = o / 128 is gate column g % 8 of block g / 8 (g = (o % 128) / 4) at r = o % 4,
+        // with its up column 8 further
+        if (lane < 128 * MB / kSlices) {
+          const int o = (128 * MB / kSlices) * s + lane;
+          const int t = o >> 7, g = (o & 127) >> 2, r = o & 3;
+          const int l = (g & 7) + 16 * (g >> 3);
+          const int mr = kRows * t + 4 * (l >> 4) + r;  // row within the block
+          const int64_t p = uu * (kUnit / 2) + (l & 15);
+          if (mr < rows_here && p < a.I)
+            store_out(a.out0, out_row(mr) * a.n_out + p, silu_times(slice_sum(t, l, r), slice_sum(t, l + 8, r)),
+                      a.f32_out);
+        }
+      } else {
+        // 16 columns x R rows = 256 MB outputs, 256 MB / S per wave: output o of tile
+        // t = o / 256 is partial lane (o % 256) / 4 at r = o % 4
+        if (lane < 256 * MB / kSlices) {
+          const int o = (256 * MB / kSlices) * s + lane;
+          const int t = o >> 8, l = (o & 255) >> 2, r = o & 3;
+          const int mr = kRows * t + 4 * (l >> 4) + r;
+          const int64_t n = uu * kUnit + (l & 15);
+          if (mr < rows_here && n < a.rows) {
+            const int64_t m = out_row(mr);
+            float v = slice_sum(t, l, r);
+            if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
+            if constexpr (GATHER) v *= gth.w ? gth.w[m] : 1.f;  // stage 2: the pair's weight
+            if constexpr (EPI == EPI_QKV) {
+              if (n < a.q_out) {
+                store_out(a.out0, m * a.q_out + n, v, a.f32_out);
+              } else if (n < a.q_out + a.kv_out) {
+                store_out(a.out1, m * a.kv_out + (n - a.q_out), v, a.f32_out);
+              } else {
+                store_out(a.out2, m * a.kv_out + (n - a.q_out - a.kv_out), v, a.f32_out);
+              }
+            } else {
+              store_out(a.out0, m * a.n_out + n, v, a.f32_out);
+            }
+          }
+        }
+      }
+    };
+
+    int it = 0;
+    for (;; ++it) {
+      const int buf = it % L::nbuf;
+      // request unit it + lookahead, then wait for unit it (the later units' loads may stay
+      // in flight); buffer (it + lookahead) % nbuf held unit it - 1 (without deferral: every
+      // wave has passed the barrier after reading it) or unit it - 2 (deferred: read before
+      // the last barrier)
+      const int64_t ua = u + L::lookahead * stride;
+      if (ua < units) request(ua, (it + L::lookahead) % L::nbuf);
+      const int64_t later = (units - 1 - u) / stride;  // units after u for this block
+      wait_units_barrier<L::dma_per_wave>(int(later < L::lookahead ? later : L::lookahead));
+      if constexpr (L::deferred) {
+        if (it > 0) epilogue(u - stride, red + ((it - 1) & 1) * (L::red_bytes / 4));
+      }
+
+      // ---- this wave's slice of unit u ----------------------------------------------------
+      const uint8_t* bb = lds + buf * L::buf_bytes;
+      const uint16_t* sc = reinterpret_cast<const uint16_t*>(bb + L::code_bytes) + col * (L::sb_row / 2);
+      const uint16_t* bi = reinterpret_cast<const uint16_t*>(bb + L::code_bytes + L::sb_pad) + col * (L::sb_row / 2);
+      f32x4_t y[MB] = {};
+#pragma unroll
+      for (int g = 0; g < GPS; ++g) {
+        const int G = s * GPS + g;
+        // codes 16 kb .. 16 kb + 15 of group G of this lane's column: half (kb & 1) of chunk
+        // 2G + kb/2
+        const uint32_t c = uint32_t(2 * G + (kb >> 1));
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bb + col * L::row_bytes + 16 * (c ^ uint32_t(col)) + 8 * (kb & 1));
+        const float sv = bf16_bits_to_f32(sc[G]);
+        const float bv = bf16_bits_to_f32(bi[G]);
+        u32x4_t q[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          q[h] = u32x4_t{nib_pair(w[h], 0, magic), nib_pair(w[h], 1, magic), nib_pair(w[h], 2, magic),
+                         nib_pair(w[h], 3, magic)};
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+          // xs[r] = sum of the group's 64 inputs of row 4 kb + r of tile t (the MFMA against
+          // ones puts that row's sum in every column; recomputed per unit, the matrix pipe is
+          // idle)
+          f32x4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][0], ones, f32x4_t{}, 0, 0, 0);
+          xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][1], ones, xs, 0, 0, 0);
+          f32x4_t d = {};
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][h], __builtin_bit_cast(bf16x8_t, q[h]), d, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float dq = fmaf(-128.0f, xs[r], d[r]);  // sum x q (exact 0 for all-zero codes)
+            y[t][r] = fmaf(sv, dq, y[t][r]);
+            y[t][r] = fmaf(bv, xs[r], y[t][r]);
+          }
+        }
+      }
+      if constexpr (L::deferred) {
+        // partials of this unit into red buffer it & 1; summed and stored after the next
+        // step's barrier (or after the loop)
+#pragma unroll
+        for (int t = 0; t < MB; ++t)
+          *reinterpret_cast<f32x4_t*>(red + (it & 1) * (L::red_bytes / 4) + ((s * MB + t) * 64 + lane) * 4) = y[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < MB; ++t) *reinterpret_cast<f32x4_t*>(red + ((s * MB + t) * 64 + lane) * 4) = y[t];
+        __syncthreads();
+        epilogue(u, red);
+      }
+      u += stride;
+      if (u >= units) break;
+    }
+    if constexpr (L::deferred) {
+      __syncthreads();
+      epilogue(u - stride, red + (it & 1) * (L::red_bytes / 4));
+    }
+    if constexpr (!GATHER) {
+      break;
+    } else {
+      first += R;
+      if (first >= end) break;
+      rows_here = end - first < R ? end - first : R;
+      __syncthreads();
+    }
   }
 }
 
@@ -390,7 +439,7 @@ constexpr int kMaxGpsTwoTiles = 10;
 #ifndef QMM_BMV_TWO_TILES
 #define QMM_BMV_TWO_TILES 1
 #endif
-#define QMM_BMV_GPS(X) X(2) X(4) X(6) X(8) X(10) X(12) X(14) X(16)
+#define QMM_BMV_GPS(X) X(1) X(2) X(4) X(6) X(8) X(10) X(12) X(14) X(16)
 
 // Row tiles per block for M rows at K = 512 * gps.
 inline int tiles_for(int64_t M, int64_t gps) {
@@ -444,14 +493,61 @@ static void launch_bmv_tiles(int epi, const GemvArgs& a, int64_t M, int64_t unit
   constexpr int64_t kCUs = 256;
   const dim3 grid{unsigned(units < kCUs ? units : kCUs), unsigned((M + bmv::kRows * MB - 1) / (bmv::kRows * MB)), 1u};
   const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
+  const BmvGather none = {};
   if (epi == EPI_LINEAR)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR, false><<<grid, block, 0, st>>>(a, M, units, none);
   else if (epi == EPI_QKV)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_QKV, false><<<grid, block, 0, st>>>(a, M, units, none);
   else if (epi == EPI_ROPE)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_ROPE><<<grid, block, 0, st>>>(a, M, units);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_ROPE, false><<<grid, block, 0, st>>>(a, M, units, none);
   else
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU, false><<<grid, block, 0, st>>>(a, M, units, none);
+}
+
+// Routed experts: a block per routing tile and about 8 units of its expert, for the
+// tile's passes of 32 pairs (K <= 5120) or 16.
+template <int G, int MB>
+static void launch_bmv_moe_tiles(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t units,
+                                 hipStream_t st) {
+  const dim3 grid{unsigned((units + 7) / 8), unsigned(m_tiles), 1u};
+  const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
+  if (epi == EPI_SWIGLU)
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU, true><<<grid, block, 0, st>>>(a, 0, units, g);
+  else
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR, true><<<grid, block, 0, st>>>(a, 0, units, g);
+}
+
+bool bmv_moe_supports(int epi, const GemvArgs& a) {
+  if (a.bits != 4 || a.gshift != 1 || a.K % bmv::kKStep || (epi != EPI_SWIGLU && epi != EPI_LINEAR)) return false;
+  switch (a.K / bmv::kKStep) {
+#define QMM_BMV_CASE(G) case G:
+    QMM_BMV_GPS(QMM_BMV_CASE)
+#undef QMM_BMV_CASE
+      return true;
+    default:
+      return false;
+  }
+}
+
+int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, hipStream_t st) {
+  if (!bmv_moe_supports(epi, a)) return 2;
+  const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)
+                                          : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
+  const int64_t gps = a.K / bmv::kKStep;
+  switch (gps) {
+#define QMM_BMV_CASE(G)                                                               \
+  case G:                                                                             \
+    if constexpr (G <= bmv::kMaxGpsTwoTiles)                                          \
+      launch_bmv_moe_tiles<G, 2>(epi, a, g, m_tiles, units, st);                      \
+    else                                                                              \
+      launch_bmv_moe_tiles<G, 1>(epi, a, g, m_tiles, units, st);                      \
+    break;
+    QMM_BMV_GPS(QMM_BMV_CASE)
+#undef QMM_BMV_CASE
+    default:
+      return 2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {

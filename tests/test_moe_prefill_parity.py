@@ -157,7 +157,7 @@ def test_moe_prefill_35B_shape_full_batch_sampled_tokens():
 
 
 def test_small_batch_pair_path_and_wide_expert():
-    """Few pairs (M * topk <= 768) run the decode gather kernels pair by pair and the
+    """Few pairs (M * topk <= 512) run the decode gather kernels pair by pair and the
     routing call does nothing; a down projection wider than those kernels take (expert
     I = 5632 > 5120) makes stage 2 route on its own and run the gathered GEMM."""
     shape = synth.MoEShape("wide-expert MoE (hidden 128, 4 experts, I 5632, top-2)", 128, 4, 5632, 2)
@@ -165,3 +165,30 @@ def test_small_batch_pair_path_and_wide_expert():
     ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 7, M, shape.E, shape.topk)
     say(f"[moe prefill] {shape.name}, M={M}")
     check_both_stages(shape, synth.CFG_TEST, 7, M, ids, p, "wide expert")
+
+
+def test_moe_prefill_small_batch_kernel_passes_and_tiles():
+    """Up to 24 pairs per expert on average (here 1200 pairs over 64 experts) the routed
+    stages run on the small-batch kernel, in passes of 32 pairs per routing tile: one
+    expert takes slot 0 of 300 tokens (two tiles, the second ragged), the others a few
+    pairs each (one ragged pass), one pair has no expert; K = 1024 and K = 512."""
+    shape = synth.MoEShape("MoE prefill (hidden 1024, 64 experts, I 512, top-3)", 1024, 64, 512, 3)
+    M = 400
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 8, M, shape.E, shape.topk)
+    ids[:300, 0] = 5
+    ids[7, 2] = -1
+    counts = np.bincount(ids[ids >= 0].ravel(), minlength=shape.E)
+    say(f"[moe prefill] {shape.name}, M={M}, pairs per expert max {counts.max()} min {counts.min()}")
+    assert counts.max() > 256 and M * shape.topk <= 24 * shape.E
+    g1, _ = check_both_stages(shape, synth.CFG_TEST, 8, M, ids, p, "small-batch kernel")
+    assert np.all(g1[7, 2] == 0)
+
+
+def test_moe_prefill_35B_shape_128_tokens():
+    """The 35B-A3B shape at 128 tokens (1024 pairs over 256 experts): both stages on the
+    small-batch kernel (K = 2048 and K = 512)."""
+    shape = synth.MOE_35B
+    M = 128
+    ids, p = synth.gen_prefill_routing(synth.CFG_MOE, 1, M, shape.E, shape.topk)
+    say(f"[moe prefill] {shape.name}, M={M}")
+    check_both_stages(shape, synth.CFG_MOE, 1, M, ids, p, "35B M=128")
