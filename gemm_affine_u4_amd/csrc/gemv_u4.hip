@@ -193,7 +193,7 @@ __device__ __forceinline__ void epi_fetch(EpiPre& p, int64_t u, int slot, const 
 // Store of one row unit's result (slot totals after slot_reduce).
 template <int LPR, int EPI>
 __device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u, int slot, int lane,
-                                           int64_t out_base, const EpiPre& ep) {
+                                           int64_t out_base, const EpiPre& ep, int64_t m) {
   constexpr int RPI = 64 / LPR;
   constexpr int P = RPI / 2;
   bool valid;
@@ -206,18 +206,18 @@ __device__ __forceinline__ void gemv_store(const GemvArgs& a, float v, int64_t u
     if (valid && a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
     const float vb = __shfl_xor(v, 32);
     if (valid && slot < P && lane == slot_result_lane<LPR>(slot))
-      rope_store_cs(a.rope, a.out0, a.out1, a.out2, rope_pair(uint32_t(u * P + slot), a.rope), blockIdx.y, v, vb,
+      rope_store_cs(a.rope, a.out0, a.out1, a.out2, rope_pair(uint32_t(u * P + slot), a.rope), m, v, vb,
                     ep.c, ep.s, a.f32_out);
   } else {
     if (valid && lane == slot_result_lane<LPR>(slot)) {
       if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[r]);
       if constexpr (EPI == EPI_QKV) {
         if (r < a.q_out) {
-          store_out(a.out0, int64_t(blockIdx.y) * a.q_out + r, v, a.f32_out);
+          store_out(a.out0, m * a.q_out + r, v, a.f32_out);
         } else if (r < a.q_out + a.kv_out) {
-          store_out(a.out1, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out), v, a.f32_out);
+          store_out(a.out1, m * a.kv_out + (r - a.q_out), v, a.f32_out);
         } else {
-          store_out(a.out2, int64_t(blockIdx.y) * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
+          store_out(a.out2, m * a.kv_out + (r - a.q_out - a.kv_out), v, a.f32_out);
         }
       } else {
         store_out(a.out0, out_base + r, v, a.f32_out);
@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
           float t = 0.f;
 #pragma unroll
           for (int j = 0; j < KS; ++j) t += rb[j][slot];
-          gemv_store<LPR, EPI>(a, t, u, slot, lane, out_base, cur);
+          gemv_store<LPR, EPI>(a, t, u, slot, lane, out_base, cur, blockIdx.y);
         }
       }
     }
@@ -373,7 +373,10 @@ struct S1Layout {
 #ifndef QMM_S1_WAVES_PER_CU
 #define QMM_S1_WAVES_PER_CU 12  // fallback if the occupancy query fails
 #endif
-template <int LPR, int CPL, int EPI, bool MOE, int DEPTH = QMM_S1_DEPTH>
+// NR activation rows per block (two: both rows' results from one read of the weights,
+// each row computed exactly as alone); the first row's activations stay in registers,
+// the second's are read from the block's LDS copy per row unit.
+template <int LPR, int CPL, int EPI, bool MOE, int NR = 1, int DEPTH = QMM_S1_DEPTH>
 #ifndef QMM_S1_MINW
 #define QMM_S1_MINW 1
 #endif
@@ -383,8 +386,9 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   constexpr int RPI = Lay::RPI;
   constexpr int P = RPI / 2;
   constexpr int C = Lay::C;
+  static_assert(NR == 1 || (NR == 2 && !MOE && EPI != EPI_ROPE), "two rows: plain projections only");
   extern __shared__ __attribute__((aligned(16))) uint32_t s1_lds[];
-  uint32_t* xl = s1_lds;
+  uint32_t* xl = s1_lds;  // row r at s1_lds + r * x_words
   float* xsl = reinterpret_cast<float*>(s1_lds + C * kXStride);
 
   const int lane = threadIdx.x & 63;
@@ -427,9 +431,10 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
     scales += off * groups;
     biases += off * groups;
   } else {
-    x += int64_t(blockIdx.y) * a.K;
-    out_base = int64_t(blockIdx.y) * a.n_out;
+    x += int64_t(blockIdx.y) * NR * a.K;
+    out_base = int64_t(blockIdx.y) * NR * a.n_out;
   }
+  const int64_t m0 = int64_t(blockIdx.y) * NR;  // activation row of the block's first row
 
   const uint32_t row_bytes = uint32_t((a.K * kBits) >> 3);
   const uint64_t nrows = uint64_t(a.rows);
@@ -455,8 +460,11 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   }
 
   // stage the activations: chunk c (32 of them, zeros past K) permuted, and its sum
-  {
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, uint64_t(a.K) * 2);
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + rr * a.K, uint64_t(a.K) * 2);
+    uint32_t* xlr = xl + rr * Lay::x_words;
+    float* xslr = xsl + rr * Lay::x_words;
     for (int c = threadIdx.x; c < C; c += 64 * kWavesS1) {
       uint32_t d[16];
 #pragma unroll
@@ -469,10 +477,10 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
       }
       uint32_t xp[16];
       Cd::permute(d, xp);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(xl + c * kXStride);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(xlr + c * kXStride);
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[v] = u32x4_t{xp[4 * v], xp[4 * v + 1], xp[4 * v + 2], xp[4 * v + 3]};
-      xsl[c] = chunk_xsum(xp);
+      xslr[c] = chunk_xsum(xp);
     }
   }
   __syncthreads();
@@ -493,13 +501,51 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
     }
     xs[i] = xsl[c];
   }
+  float xs1[CPL];
+  if constexpr (NR == 2) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) xs1[i] = xsl[Lay::x_words + li + LPR * i];
+  }
 
   for (int64_t u0 = u_begin; u0 < u_end; u0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int64_t u = u0 + d;
       if (u < u_end) {
-        const float v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        float v, v1 = 0.f;
+        if constexpr (NR == 2) {
+          // the sums of row_partial for both rows, chunk by chunk (one decode of the codes
+          // serves both), the second row's activations read from LDS per chunk
+          float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) {
+            // an offset the compiler cannot see through, so that the reads stay here instead
+            // of being hoisted out of the loop into 16 * CPL more registers
+            uint32_t xo = uint32_t(Lay::x_words + (li + LPR * i) * kXStride);
+            asm volatile("" : "+v"(xo));
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xl + xo);
+            uint32_t xq[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4_t t = src[q];
+              xq[4 * q + 0] = t[0];
+              xq[4 * q + 1] = t[1];
+              xq[4 * q + 2] = t[2];
+              xq[4 * q + 3] = t[3];
+            }
+            const float sv = bf16_bits_to_f32(buf[d].s[i]), bv = bf16_bits_to_f32(buf[d].b[i]);
+            const float d0 = Cd::dot_q(buf[d].w[i], xp[i], xs[i], magic);
+            const float d1 = Cd::dot_q(buf[d].w[i], xq, xs1[i], magic);
+            acc0 = fmaf(sv, d0, acc0);
+            acc0 = fmaf(bv, xs[i], acc0);
+            acc1 = fmaf(sv, d1, acc1);
+            acc1 = fmaf(bv, xs1[i], acc1);
+          }
+          v = slot_reduce<LPR>(acc0);
+          v1 = slot_reduce<LPR>(acc1);
+        } else {
+          v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
+        }
         const EpiPre cur = ep[d];
         if (u + DEPTH < u_end) {
           bool valid;
@@ -507,7 +553,8 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
           load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
           epi_fetch<LPR, EPI>(ep[d], u + DEPTH, slot, a, trow);
         }
-        gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base, cur);
+        gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base, cur, m0);
+        if constexpr (NR == 2) gemv_store<LPR, EPI>(a, v1, u, slot, lane, out_base + a.n_out, cur, m0 + 1);
       }
     }
   }
@@ -645,12 +692,12 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
 constexpr int64_t kCUs = 256;
 
-template <int L, int C, int EPI, bool MOE>
+template <int L, int C, int EPI, bool MOE, int NR = 1>
 static int64_t s1_resident_waves() {
   static const int64_t waves = [] {
     int blocks_per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, gemv_u4_s1_kernel<L, C, EPI, MOE>,
-                                                     64 * kWavesS1, S1Layout<L, C>::lds_bytes()) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, gemv_u4_s1_kernel<L, C, EPI, MOE, NR>,
+                                                     64 * kWavesS1, NR * S1Layout<L, C>::lds_bytes()) != hipSuccess ||
         blocks_per_cu < 1)
       blocks_per_cu = QMM_S1_WAVES_PER_CU / kWavesS1;
     return kCUs * kWavesS1 * int64_t(blocks_per_cu);
@@ -678,9 +725,40 @@ static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64
   *threads = 64 * sh.ksplit;
 }
 
+// Both rows of an M = 2 call in one single-slice launch (gemv_two_rows).
+template <int EPI>
+static int launch_s1_two_rows(const GemvShape& sh, const GemvArgs& a, int64_t units, hipStream_t s) {
+  switch (sh.lpr * 100 + sh.cpl) {
+#define QMM_S1_TWO_ROWS_CASE(L, C)                                                                      \
+  case L * 100 + C: {                                                                                   \
+    const int64_t w = s1_waves(units, 1, s1_resident_waves<L, C, EPI, false, 2>());                     \
+    gemv_u4_s1_kernel<L, C, EPI, false, 2><<<dim3{unsigned(w / kWavesS1), 1u, 1u}, dim3{64u * kWavesS1, 1u, 1u}, \
+                                             2 * S1Layout<L, C>::lds_bytes(), s>>>(a, units / w, units % w);    \
+  } break;
+    QMM_S1_TWO_ROWS_CASE(16, 1)
+    QMM_S1_TWO_ROWS_CASE(32, 1)
+    QMM_S1_TWO_ROWS_CASE(32, 2)
+    QMM_S1_TWO_ROWS_CASE(32, 3)
+    QMM_S1_TWO_ROWS_CASE(32, 4)
+    QMM_S1_TWO_ROWS_CASE(32, 5)
+#undef QMM_S1_TWO_ROWS_CASE
+    default:
+      return 2;
+  }
+  return finish_launch();
+}
+
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
   GemvShape sh;
   if (!gemv_shape_for_k(a.K, &sh)) return 2;
+  if (gemv_two_rows(epi, a.K, M) && sh.ksplit == 1) {
+    int64_t blocks, units;
+    int threads, upw;
+    gemv_geometry(sh, epi, a, 1, &units, &upw, &blocks, &threads);
+    if (epi == EPI_LINEAR) return launch_s1_two_rows<EPI_LINEAR>(sh, a, units, s);
+    if (epi == EPI_QKV) return launch_s1_two_rows<EPI_QKV>(sh, a, units, s);
+    if (epi == EPI_SWIGLU) return launch_s1_two_rows<EPI_SWIGLU>(sh, a, units, s);
+  }
   const int64_t batch = M;
   int64_t blocks, units;
   int threads, upw;

@@ -205,3 +205,36 @@ def test_gate_up_equals_swiglu_of_unfused_rows():
     u = run_linear(x, w.slice_rows(I, 2 * I))
     ref = orc.swiglu(g, u)
     assert np.all(np.abs(h - ref) <= 2.0 ** -20 * np.abs(ref) + 1e-30)
+
+
+# ---- two activation rows on one read of the weights ------------------------------------
+
+@pytest.mark.parametrize("K", [64, 576, 2048, 5120])
+def test_two_rows_equal_single_row_calls(K):
+    """M = 2 with K <= 5120 runs both rows in one launch of the single-slice kernel (the
+    second row's activations read from LDS): each row equals its own M = 1 call bit for
+    bit, for the linear, fused QKV and fused gate+up+SwiGLU projections, and the oracle
+    within tolerance."""
+    say(f"[two rows] K={K}")
+    w = synth.gen_weight(synth.CFG_TEST, 9, synth.PROJ_LINEAR, 150, K)
+    x = synth.gen_x(synth.CFG_TEST, 9, 0, 2, K)
+    got = run_linear(x, w)
+    y, t = orc.linear(x, w.codes, w.scales, w.biases)
+    assert_within(got, y, t, f"linear M=2 K={K}")
+    assert np.array_equal(run_linear(x, w, f32=False), rne_bits_of(got))
+    q_out, kv_out = 96, 27
+    for m in range(2):
+        assert np.array_equal(run_linear(x[m:m + 1], w)[0], got[m]), f"linear row {m}"
+    wq = synth.gen_weight(synth.CFG_TEST, 9, synth.PROJ_QKV, q_out + 2 * kv_out, K)
+    qkv2 = run_qkv(x, wq, q_out, kv_out)
+    for m in range(2):
+        one = run_qkv(x[m:m + 1], wq, q_out, kv_out)
+        for a, b in zip(qkv2, one):
+            assert np.array_equal(a[m], b[0]), f"qkv row {m}"
+    I = 77
+    wg = synth.gen_weight(synth.CFG_TEST, 9, synth.PROJ_GATE_UP, 2 * I, K)
+    h2 = run_gate_up(x, wg, I)
+    h, th = orc.gate_up_swiglu(x, wg.codes, wg.scales, wg.biases, I)
+    assert_within(h2, h, th, f"gate+up M=2 K={K}")
+    for m in range(2):
+        assert np.array_equal(run_gate_up(x[m:m + 1], wg, I)[0], h2[m]), f"gate+up row {m}"
