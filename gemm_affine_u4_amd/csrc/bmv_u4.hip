@@ -1,5 +1,7 @@
-// Small-batch kernel (2 <= M <= 32, and up to 256 where the prefill GEMM's grid would be
-// small) for the u4 group-64 affine projections on gfx950.
+// Small-batch kernel (up to 32 activation rows, and up to 256 where the prefill GEMM's
+// grid would be small; M = 2 only where the two-row GEMV does not apply) for the u4
+// group-64 affine projections on gfx950, and the same kernel over the routing of a batch
+// of routed experts (GATHER: passes of up to 32 bucketed pairs of one expert).
 //
 // Between decode (one activation row: weight-bandwidth bound, the GEMV) and prefill
 // (hundreds of rows: matrix bound, the LDS-dequant GEMM) the work is still one pass over
