@@ -353,7 +353,7 @@ def bench_small_batch(torch, qmm, synth, T, dev, pq, pg):
         out[f"M={M}"] = {"qkv_us": round(ms_q * 1e3, 2), "qkv_rope_us": round(ms_r * 1e3, 2),
                          "gate_up_us": round(ms_g * 1e3, 2),
                          "weights_GB/s": round(wbytes / (us * 1e-6) / 1e9, 1),
-                         "kernel": "gemv" if M == 1 else ("gemv, two rows (qkv_rope: bmv)" if M == 2
+                         "kernel": "gemv" if M == 1 else ("gemv, two rows" if M == 2
                                                           else "bmv" if M <= 32 else "bmv or gemm (estimate)")}
     return {"workload": "14B layer decode of M sequences: fused QKV [7168 x 5120] + fused gate+up+SwiGLU "
                         "[27648 x 5120], u4 g64, rotating 48-layer pool", **out}

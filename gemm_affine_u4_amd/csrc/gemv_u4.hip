@@ -170,9 +170,9 @@ struct EpiPre {
   float c, s;
 };
 template <int LPR, int EPI>
-__device__ __forceinline__ const float* epi_table_row(const GemvArgs& a) {
+__device__ __forceinline__ const float* epi_table_row(const GemvArgs& a, int64_t m) {
   if constexpr (EPI == EPI_ROPE) {
-    const int32_t pos = min(max(a.rope.positions[blockIdx.y], 0), a.rope.max_pos - 1);
+    const int32_t pos = min(max(a.rope.positions[m], 0), a.rope.max_pos - 1);
     return a.rope.cos_sin + int64_t(pos) * a.rope.rot;
   } else {
     return nullptr;
@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(64 * KS) gemv_u4_kernel(GemvArgs a, int64_t pe
   // the buffer is refilled with unit u + DEPTH right after.
   RowData<CPL> buf[DEPTH];
   EpiPre ep[DEPTH];
-  const float* trow = epi_table_row<LPR, EPI>(a);
+  const float* trow = epi_table_row<LPR, EPI>(a, blockIdx.y);
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (u_begin + d < u_end) {
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   constexpr int RPI = Lay::RPI;
   constexpr int P = RPI / 2;
   constexpr int C = Lay::C;
-  static_assert(NR == 1 || (NR == 2 && !MOE && EPI != EPI_ROPE), "two rows: plain projections only");
+  static_assert(NR == 1 || (NR == 2 && !MOE), "two rows: not the routed experts");
   extern __shared__ __attribute__((aligned(16))) uint32_t s1_lds[];
   uint32_t* xl = s1_lds;  // row r at s1_lds + r * x_words
   float* xsl = reinterpret_cast<float*>(s1_lds + C * kXStride);
@@ -447,8 +447,9 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
 
   // first row units' codes, scales and biases in flight before the staging
   RowData<CPL> buf[DEPTH];
-  EpiPre ep[DEPTH];
-  const float* trow = epi_table_row<LPR, EPI>(a);
+  EpiPre ep[DEPTH], ep1[DEPTH];  // ep1: the second row's (NR = 2)
+  const float* trow = epi_table_row<LPR, EPI>(a, m0);
+  const float* trow1 = NR == 2 ? epi_table_row<LPR, EPI>(a, m0 + 1) : nullptr;
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     if (u_begin + d < u_end) {
@@ -456,6 +457,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
       const int64_t row = unit_row<LPR, EPI>(u_begin + d, slot, a, &valid);
       load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
       epi_fetch<LPR, EPI>(ep[d], u_begin + d, slot, a, trow);
+      if constexpr (NR == 2) epi_fetch<LPR, EPI>(ep1[d], u_begin + d, slot, a, trow1);
     }
   }
 
@@ -546,15 +548,16 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
         } else {
           v = slot_reduce<LPR>(row_partial<CPL>(buf[d], xp, xs, magic));
         }
-        const EpiPre cur = ep[d];
+        const EpiPre cur = ep[d], cur1 = ep1[d];
         if (u + DEPTH < u_end) {
           bool valid;
           const int64_t row = unit_row<LPR, EPI>(u + DEPTH, slot, a, &valid);
           load_row<LPR, CPL>(buf[d], cr, sr0, br0, uint32_t(row), row_bytes, row_groups, c0, a.gshift);
           epi_fetch<LPR, EPI>(ep[d], u + DEPTH, slot, a, trow);
+          if constexpr (NR == 2) epi_fetch<LPR, EPI>(ep1[d], u + DEPTH, slot, a, trow1);
         }
         gemv_store<LPR, EPI>(a, v, u, slot, lane, out_base, cur, m0);
-        if constexpr (NR == 2) gemv_store<LPR, EPI>(a, v1, u, slot, lane, out_base + a.n_out, cur, m0 + 1);
+        if constexpr (NR == 2) gemv_store<LPR, EPI>(a, v1, u, slot, lane, out_base + a.n_out, cur1, m0 + 1);
       }
     }
   }
@@ -758,6 +761,9 @@ int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
     if (epi == EPI_LINEAR) return launch_s1_two_rows<EPI_LINEAR>(sh, a, units, s);
     if (epi == EPI_QKV) return launch_s1_two_rows<EPI_QKV>(sh, a, units, s);
     if (epi == EPI_SWIGLU) return launch_s1_two_rows<EPI_SWIGLU>(sh, a, units, s);
+#if QMM_BITS == 4
+    if (epi == EPI_ROPE) return launch_s1_two_rows<EPI_ROPE>(sh, a, units, s);
+#endif
   }
   const int64_t batch = M;
   int64_t blocks, units;

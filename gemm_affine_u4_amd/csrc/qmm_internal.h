@@ -133,14 +133,14 @@ inline int launch_moe_gate_up(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a
 inline int launch_moe_down(const GemvArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_moe_down(a, s)) }
 inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH(a.bits, launch_gemm(epi, a, s)) }
 
-// M = 2 on the single-slice decode kernel (K <= 5120, any code width, not the rotary
-// epilogue): both activation rows against one read of the weights, each row computed
-// exactly as alone.
+// M = 2 on the single-slice decode kernel (K <= 5120, any code width; the rotary
+// epilogue for 4-bit codes, like the GEMV itself): both activation rows against one read
+// of the weights, each row computed exactly as alone.
 #ifndef QMM_GEMV_TWO_ROWS
 #define QMM_GEMV_TWO_ROWS 1
 #endif
 inline bool gemv_two_rows(int epi, int64_t K, int64_t M) {
-  return QMM_GEMV_TWO_ROWS && M == 2 && K >= 64 && K <= 5120 && K % 64 == 0 && epi != EPI_ROPE;
+  return QMM_GEMV_TWO_ROWS && M == 2 && K >= 64 && K <= 5120 && K % 64 == 0;
 }
 
 // Small batches (2 <= M <= kBmvMaxM) of the 4-bit group-64 projections whose K is a

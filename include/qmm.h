@@ -50,8 +50,8 @@
  *     stores the fp32 value that the bf16 mode would round, so bf16 output ==
  *     RNE(fp32 output) bit for bit.
  *   - Row-major everywhere: x [M][K], y [M][N].  Inputs are assumed finite.
- *   - M = 1 runs a bandwidth-bound GEMV; M = 2 with K <= 5120 (any format, not the
- *     rotary epilogue) runs the same GEMV for both rows against one read of the weights,
+ *   - M = 1 runs a bandwidth-bound GEMV; M = 2 with K <= 5120 (any format) runs the
+ *     same GEMV for both rows against one read of the weights,
  *     each row bit-identical to its own M = 1 call.  For 4-bit group-64 linear / fused
  *     QKV / fused gate+up with K a multiple of 512 up to 8192, otherwise
  *     2 <= M <= 32 (and up to 256 where it

@@ -172,3 +172,21 @@ def test_outputs_at_odd_element_offsets_match_aligned_ones(M):
     torch.cuda.synchronize()
     assert np.array_equal(yo.cpu().numpy().view(np.uint16), ya.values())
     assert int(big[0].item()) == 0 and not torch.any(big[1 + M * 200:] != 0)
+
+
+@pytest.mark.parametrize("sh", [SMALL, SMALL_GATED], ids=["full", "gated"])
+def test_rope_two_rows_equal_single_row_calls(sh):
+    """M = 2 (K <= 5120) runs both rows in one launch of the GEMV, each with its own
+    position: the oracle within tolerance, and each row equal to its own M = 1 call bit
+    for bit."""
+    check(sh, synth.CFG_TEST, 23, 2, contiguous=False)
+    w, lb = weights(sh, synth.CFG_TEST, 23)
+    x = synth.gen_x(synth.CFG_TEST, 23, 0, 2, sh.K)
+    pos = synth.gen_positions(synth.CFG_TEST, 23, 2, MAX_POS, False)
+    tab = synth.gen_rope_table(MAX_POS, sh.rot, sh.base)
+    both = run(sh, x, w, lb, pos, tab)
+    for m in range(2):
+        one = run(sh, x[m:m + 1], w, lb, pos[m:m + 1], tab)
+        for a, b in zip(both, one):
+            if a is not None:
+                assert np.array_equal(a[m], b[0]), f"row {m}"
