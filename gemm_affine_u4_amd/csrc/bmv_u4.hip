@@ -263,17 +263,20 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     }
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     // xs[r] = sum of group g's 64 inputs of row 4 kb + r of tile t (the MFMA against ones
-    // puts that row's sum in every column): kept in registers where they fit (one tile,
-    // K <= 5120), else recomputed per unit (the same two MFMAs, so the same values)
-    constexpr bool kXsKept = MB == 1 && GPS <= 10;
+    // puts that row's sum in every column): kept in registers where they fit (one tile
+    // and K <= 5120, two tiles and K <= 3072), else recomputed per unit (the same two
+    // MFMAs, so the same values)
+    constexpr bool kXsKept = GPS * MB <= 12 && GPS <= 10;
     auto group_xs = [&](int t, int g) {
       const f32x4_t v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][0], ones, f32x4_t{}, 0, 0, 0);
       return __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t][g][1], ones, v, 0, 0, 0);
     };
-    f32x4_t xs_kept[kXsKept ? GPS : 1];
+    f32x4_t xs_kept[kXsKept ? MB : 1][kXsKept ? GPS : 1];
     if constexpr (kXsKept) {
 #pragma unroll
-      for (int g = 0; g < GPS; ++g) xs_kept[g] = group_xs(0, g);
+      for (int t = 0; t < MB; ++t)
+#pragma unroll
+        for (int g = 0; g < GPS; ++g) xs_kept[t][g] = group_xs(t, g);
     }
     const uint32_t magic = in_vgpr(kMagicPair);
     float* red = reinterpret_cast<float*>(lds + L::red_off);
@@ -399,7 +402,7 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
 #pragma unroll
         for (int t = 0; t < MB; ++t) {
           f32x4_t xs;
-          if constexpr (kXsKept) xs = xs_kept[g];
+          if constexpr (kXsKept) xs = xs_kept[t][g];
           else xs = group_xs(t, g);
           f32x4_t d = {};
 #pragma unroll

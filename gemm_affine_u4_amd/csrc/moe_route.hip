@@ -240,7 +240,7 @@ int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, voi
 // The gathered stages on the small-batch kernel (passes of up to 32 pairs of one expert,
 // each streaming the expert's rows) while experts average at most kMoeBmvPairsPerExpert
 // pairs, else on the gathered GEMM (256-pair tiles).  35B-A3B shape (256 experts, top-8):
-// per layer 239 against 374 us at 128 tokens, 302 against 382 at 512, 443 against 418
+// per layer 224 against 374 us at 128 tokens, 284 against 382 at 512, 443 against 418
 // at 1024.
 constexpr int64_t kMoeBmvPairsPerExpert = 24;
 static int launch_moe_stage(int epi, const GemmArgs& a, int64_t x_rows, int64_t tmax, bool few_per_expert,
