@@ -624,7 +624,8 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
             "down_combine": rec(ms_s2, fl2, b2),
             "small_batches": {"note": "route + both stages per layer for the first M tokens of the same "
                                       "routing; M * topk <= 512 runs pair by pair, up to 24 pairs per expert "
-                                      "on the gathered small-batch kernel, above on the gathered GEMM", **small}}
+                                      "(stage 2: 40) on the gathered small-batch kernel, above on the "
+                                      "gathered GEMM", **small}}
 
 
 def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step):

@@ -238,11 +238,12 @@ int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, voi
 #define QMM_MOE_BMV 1
 #endif
 // The gathered stages on the small-batch kernel (passes of up to 32 pairs of one expert,
-// each streaming the expert's rows) while experts average at most kMoeBmvPairsPerExpert
-// pairs, else on the gathered GEMM (256-pair tiles).  35B-A3B shape (256 experts, top-8):
-// per layer 224 against 374 us at 128 tokens, 284 against 382 at 512, 443 against 418
-// at 1024.
-constexpr int64_t kMoeBmvPairsPerExpert = 24;
+// each streaming the expert's rows) while experts average at most 24 pairs (stage 1) or
+// 40 pairs (stage 2, whose K = I is short), else on the gathered GEMM (256-pair tiles).
+// 35B-A3B shape (256 experts, top-8): per layer 224 against 374 us at 128 tokens, 284
+// against 382 at 512; at 1024 tokens stage 1 228 on the GEMM against 237, stage 2 155
+// on the small-batch kernel against 169.
+constexpr int64_t kMoeBmvPairsPerExpert[2] = {24, 40};
 static int launch_moe_stage(int epi, const GemmArgs& a, int64_t x_rows, int64_t tmax, bool few_per_expert,
                             hipStream_t s) {
   if (QMM_MOE_BMV && few_per_expert) {
@@ -278,7 +279,7 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
   a.moe_offsets = reinterpret_cast<const int32_t*>(b + L.offsets);
   a.moe_pairs = reinterpret_cast<const int32_t*>(b + L.pairs);
   const unsigned zb = unsigned((L.P + 255) / 256);
-  const bool few = L.P <= kMoeBmvPairsPerExpert * E;
+  const bool few = L.P <= kMoeBmvPairsPerExpert[stage == 0 ? 0 : 1] * E;
   if (stage == 0) {
     // stage 1: h [P][I] of the routed pairs from the gathered GEMM, zeros for the others
     a.out0 = out;

@@ -207,9 +207,9 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K,
  *                    (deterministic: by expert, then by pair index);
  *   qmm_moe_prefill  stage QMM_MOE_GATE_UP_SWIGLU, then stage QMM_MOE_DOWN_COMBINE,
  *                    both reading that routing.
- * Up to 24 pairs per expert on average (M * topk <= 24 E) the two stages run on the
- * small-batch kernel, in passes of up to 32 pairs of one expert; above, on the gathered
- * GEMM (tiles of 256 pairs).  Both read the routing the same way and give the same
+ * Up to 24 pairs per expert on average (M * topk <= 24 E; stage 2: 40 E) the stages run
+ * on the small-batch kernel, in passes of up to 32 pairs of one expert; above, on the
+ * gathered GEMM (tiles of 256 pairs).  Both read the routing the same way and give the same
  * results up to rounding order.
  * A small batch (M * topk <= 512 pairs: most experts then see one token or none) runs
  * pair by pair instead, on the kernels of qmm_moe_gather: stage 1 one SwiGLU GEMV per
