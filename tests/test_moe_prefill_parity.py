@@ -184,6 +184,18 @@ def test_moe_prefill_small_batch_kernel_passes_and_tiles():
     assert np.all(g1[7, 2] == 0)
 
 
+def test_moe_prefill_stage1_gemm_stage2_small_batch_kernel():
+    """Between 24 and 40 pairs per expert on average (here 1200 pairs over 32 experts)
+    stage 1 runs the gathered GEMM and stage 2 (K = I = 512) the gathered small-batch
+    kernel; both against the oracle."""
+    shape = synth.MoEShape("MoE prefill (hidden 1024, 32 experts, I 512, top-3)", 1024, 32, 512, 3)
+    M = 400
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 9, M, shape.E, shape.topk)
+    assert 24 * shape.E < M * shape.topk <= 40 * shape.E
+    say(f"[moe prefill] {shape.name}, M={M}")
+    check_both_stages(shape, synth.CFG_TEST, 9, M, ids, p, "GEMM + small-batch kernel")
+
+
 def test_moe_prefill_35B_shape_128_tokens():
     """The 35B-A3B shape at 128 tokens (1024 pairs over 256 experts): both stages on the
     small-batch kernel (K = 2048 and K = 512)."""
