@@ -520,12 +520,12 @@ static void launch_bmv_tiles(int epi, const GemvArgs& a, int64_t M, int64_t unit
     bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU, false><<<grid, block, 0, st>>>(a, M, units, none);
 }
 
-// Routed experts: a block per routing tile and about 8 units of its expert, for the
-// tile's passes of 32 pairs (K <= 5120) or 16.
+// Routed experts: a block per routing tile and `upb` units of its expert, for the tile's
+// passes of 32 pairs (K <= 5120) or 16.
 template <int G, int MB>
 static void launch_bmv_moe_tiles(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t units,
-                                 hipStream_t st) {
-  const dim3 grid{unsigned((units + 7) / 8), unsigned(m_tiles), 1u};
+                                 int64_t upb, hipStream_t st) {
+  const dim3 grid{unsigned((units + upb - 1) / upb), unsigned(m_tiles), 1u};
   const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
   if (epi == EPI_SWIGLU)
     bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU, true><<<grid, block, 0, st>>>(a, 0, units, g);
@@ -545,8 +545,8 @@ bool bmv_moe_supports(int epi, const GemvArgs& a) {
   }
 }
 
-int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, hipStream_t st) {
-  if (!bmv_moe_supports(epi, a)) return 2;
+int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t upb, hipStream_t st) {
+  if (!bmv_moe_supports(epi, a) || upb < 1) return 2;
   const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)
                                           : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
   const int64_t gps = a.K / bmv::kKStep;
@@ -554,9 +554,9 @@ int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_til
 #define QMM_BMV_CASE(G)                                                               \
   case G:                                                                             \
     if constexpr (G <= bmv::kMaxGpsTwoTiles)                                          \
-      launch_bmv_moe_tiles<G, 2>(epi, a, g, m_tiles, units, st);                      \
+      launch_bmv_moe_tiles<G, 2>(epi, a, g, m_tiles, units, upb, st);                 \
     else                                                                              \
-      launch_bmv_moe_tiles<G, 1>(epi, a, g, m_tiles, units, st);                      \
+      launch_bmv_moe_tiles<G, 1>(epi, a, g, m_tiles, units, upb, st);                 \
     break;
     QMM_BMV_GPS(QMM_BMV_CASE)
 #undef QMM_BMV_CASE

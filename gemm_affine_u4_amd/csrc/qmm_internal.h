@@ -166,7 +166,8 @@ struct BmvGather {
   int64_t x_rows;          // rows of the activations
 };
 bool bmv_moe_supports(int epi, const GemvArgs& a);
-int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, hipStream_t s);
+// upb: weight units (16 rows) per block; the grid is ceil(units / upb) x m_tiles.
+int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t upb, hipStream_t s);
 
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
