@@ -22,12 +22,12 @@ bool acts_fit(int64_t M, int64_t K) { return uint64_t(M) * uint64_t(K) * 2 <= 0x
 // Activation rows up to which the decode GEMV runs (once per row); above, the GEMM.
 constexpr int64_t kGemvMaxM = 8;
 #ifndef QMM_MOE_PAIRS_BY_GEMV
-#define QMM_MOE_PAIRS_BY_GEMV 512
+#define QMM_MOE_PAIRS_BY_GEMV 448
 #endif
 // Routed experts over a batch: up to this many (token, slot) pairs run pair by pair
 // (measured on the 35B-A3B shape, route included: at 32 tokens x top-8 the layer takes
-// 102 us pair by pair against 148 us through the routed path, at 64 tokens 203 against
-// 197 us).
+// 101 us pair by pair against 167 us through the routed path, at 64 tokens 200 against
+// 179 us; the pair path grows ~0.39 us per pair, the routed one stays near 170 us).
 constexpr int64_t kMoePairsByGemv = QMM_MOE_PAIRS_BY_GEMV;
 
 // A format of the affine family: code width and group size (the pages list u2 .. u8 at

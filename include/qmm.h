@@ -211,7 +211,7 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K,
  * on the small-batch kernel, in passes of up to 32 pairs of one expert; above, on the
  * gathered GEMM (tiles of 256 pairs).  Both read the routing the same way and give the same
  * results up to rounding order.
- * A small batch (M * topk <= 512 pairs: most experts then see one token or none) runs
+ * A small batch (M * topk <= 448 pairs: most experts then see one token or none) runs
  * pair by pair instead, on the kernels of qmm_moe_gather: stage 1 one SwiGLU GEMV per
  * (token, slot) pair, stage 2 each token's weighted sum over its slots (expert I <= 5120;
  * a wider one is routed by stage 2 itself and runs the GEMM).  The stages then read

@@ -157,7 +157,7 @@ def test_moe_prefill_35B_shape_full_batch_sampled_tokens():
 
 
 def test_small_batch_pair_path_and_wide_expert():
-    """Few pairs (M * topk <= 512) run the decode gather kernels pair by pair and the
+    """Few pairs (M * topk <= 448) run the decode gather kernels pair by pair and the
     routing call does nothing; a down projection wider than those kernels take (expert
     I = 5632 > 5120) makes stage 2 route on its own and run the gathered GEMM."""
     shape = synth.MoEShape("wide-expert MoE (hidden 128, 4 experts, I 5632, top-2)", 128, 4, 5632, 2)
