@@ -489,7 +489,7 @@ bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
 #define QMM_BMV_FORCE 0
 #endif
 bool bmv_preferred(int epi, const GemvArgs& a, int64_t M) {
-  if (!bmv_supports(epi, a, M) || gemv_two_rows(epi, a.K, M)) return false;
+  if (!bmv_supports(epi, a, M) || gemv_two_rows(a.K, M)) return false;
   if (M <= 32 || QMM_BMV_FORCE) return true;
   const int mb = bmv::tiles_for(M, a.K / bmv::kKStep);
   const double wbytes = double(a.rows) * double(a.K) * (0.5 + 4.0 / 64.0);

@@ -754,7 +754,7 @@ static int launch_s1_two_rows(const GemvShape& sh, const GemvArgs& a, int64_t un
 int launch_gemv(int epi, const GemvArgs& a, int64_t M, hipStream_t s) {
   GemvShape sh;
   if (!gemv_shape_for_k(a.K, &sh)) return 2;
-  if (gemv_two_rows(epi, a.K, M) && sh.ksplit == 1) {
+  if (gemv_two_rows(a.K, M) && sh.ksplit == 1) {
     int64_t blocks, units;
     int threads, upw;
     gemv_geometry(sh, epi, a, 1, &units, &upw, &blocks, &threads);

@@ -139,7 +139,7 @@ inline int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) { QMM_BY_WIDTH
 #ifndef QMM_GEMV_TWO_ROWS
 #define QMM_GEMV_TWO_ROWS 1
 #endif
-inline bool gemv_two_rows(int epi, int64_t K, int64_t M) {
+inline bool gemv_two_rows(int64_t K, int64_t M) {
   return QMM_GEMV_TWO_ROWS && M == 2 && K >= 64 && K <= 5120 && K % 64 == 0;
 }
 
