@@ -49,6 +49,10 @@ def test_linear_formats(bits, G, M, K, N):
     g = lin(bits, G, x, w, N, lb=lb)
     assert_within(g, y, t, f"u{bits} g{G} linear M={M} K={K}")
     assert np.array_equal(lin(bits, G, x, w, N, f32=False, lb=lb), rne_bits_of(g))
+    if M == 2:
+        # both rows in one launch of the GEMV, each equal to its own M = 1 call
+        for m in range(2):
+            assert np.array_equal(lin(bits, G, x[m:m + 1], w, N, lb=lb)[0], g[m]), f"row {m}"
 
 
 @pytest.mark.parametrize("bits,G", FORMATS)
