@@ -17,6 +17,8 @@ namespace qmm {
 constexpr int kRouteThreads = 256;   // threads of the count and place blocks (one pair each per pass)
 constexpr int kScanThreads = 1024;   // the one block of the scan
 constexpr int kMaxChunks = 256;      // routing chunks (blocks of the count and place kernels)
+constexpr int kScanBatch = 16;       // chunks up to which a scan thread takes a whole expert row
+constexpr int kWaveBatch = 8;        // experts a scan wave loads at once above that
 
 static __device__ __forceinline__ bool routed(int32_t e, int E) { return e >= 0 && e < E; }
 
@@ -68,8 +70,9 @@ static __device__ int block_exclusive_scan(int v, int* total) {
   return before + inc - v;
 }
 
-// One block.  (1) For each expert (one wave per expert at a time, 64 chunks per pass):
-// counts[e][c] becomes the exclusive prefix over chunks, and the expert's total is kept.
+// One block.  (1) For each expert (a thread each up to kScanBatch chunks, else a wave
+// each): counts[e][c] becomes the exclusive prefix over chunks, and the expert's total is
+// kept.
 // (2) Over the experts: bucket offsets (prefix of the totals), then the tile table: expert
 // e's bucket is cut into tiles of `bm` pairs, written at the prefix of the tile counts.
 __global__ void __launch_bounds__(kScanThreads) moe_route_scan(int32_t* __restrict__ counts, int chunks, int E,
@@ -77,24 +80,61 @@ __global__ void __launch_bounds__(kScanThreads) moe_route_scan(int32_t* __restri
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ tiles) {
   __shared__ int tot[kMaxExpertsPrefill];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kWaves = kScanThreads / 64;
-  for (int e = wave; e < E; e += kWaves) {
-    int32_t* row = counts + int64_t(e) * chunks;
-    int carry = 0;
-    for (int c0 = 0; c0 < chunks; c0 += 64) {
-      const int c = c0 + lane;
-      const int v = c < chunks ? row[c] : 0;
-      int inc = v;
+  if (chunks <= kScanBatch) {
+    // few chunks: one thread per expert, a serial exclusive prefix over its row (all of
+    // the row's loads in flight at once; indices clamped into the row, so no branches)
+    for (int e = threadIdx.x; e < E; e += kScanThreads) {
+      int32_t* row = counts + int64_t(e) * chunks;
+      int v[kScanBatch];
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += u;
+      for (int j = 0; j < kScanBatch; ++j) v[j] = row[j < chunks ? j : chunks - 1];
+      int run = 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (j < chunks) {
+          row[j] = run;
+          run += v[j];
+        }
       }
-      if (c < chunks) row[c] = carry + inc - v;
-      carry += __shfl(inc, 63, 64);
+      tot[e] = run;
     }
-    if (lane == 0) tot[e] = carry;
+  } else {
+    // many chunks: a wave per expert (64 chunks per pass, a shuffle scan), kWaveBatch
+    // experts' loads issued together so that a wave waits once per batch
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int kWaves = kScanThreads / 64;
+    for (int e0 = wave * kWaveBatch; e0 < E; e0 += kWaves * kWaveBatch) {
+      int carry[kWaveBatch];
+#pragma unroll
+      for (int j = 0; j < kWaveBatch; ++j) carry[j] = 0;
+      for (int c0 = 0; c0 < chunks; c0 += 64) {
+        const int c = c0 + lane;
+        const int cc = c < chunks ? c : chunks - 1;
+        int v[kWaveBatch], ex[kWaveBatch];
+#pragma unroll
+        for (int j = 0; j < kWaveBatch; ++j) v[j] = counts[int64_t(e0 + j < E ? e0 + j : E - 1) * chunks + cc];
+#pragma unroll
+        for (int j = 0; j < kWaveBatch; ++j) {
+          const int vj = c < chunks && e0 + j < E ? v[j] : 0;
+          int inc = vj;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += u;
+          }
+          ex[j] = carry[j] + inc - vj;
+          carry[j] += __shfl(inc, 63, 64);
+        }
+#pragma unroll
+        for (int j = 0; j < kWaveBatch; ++j)
+          if (c < chunks && e0 + j < E) counts[int64_t(e0 + j) * chunks + c] = ex[j];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kWaveBatch; ++j)
+          if (e0 + j < E) tot[e0 + j] = carry[j];
+      }
+    }
   }
   __syncthreads();
   // each thread takes kPer consecutive experts
