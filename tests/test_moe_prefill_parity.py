@@ -196,6 +196,16 @@ def test_moe_prefill_stage1_gemm_stage2_small_batch_kernel():
     check_both_stages(shape, synth.CFG_TEST, 9, M, ids, p, "GEMM + small-batch kernel")
 
 
+def test_moe_prefill_many_chunks_and_ragged_expert_count():
+    """4800 pairs (19 routing chunks: the scan's wave-per-expert path) over 100 experts
+    (not a multiple of the scan's batch of 8), skewed, some experts empty."""
+    shape = synth.MoEShape("MoE prefill (hidden 320, 100 experts, I 192, top-4)", 320, 100, 192, 4)
+    M = 1200
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 10, M, 90, shape.topk, skew=1.0)  # experts 90.. empty
+    say(f"[moe prefill] {shape.name}, M={M}")
+    check_both_stages(shape, synth.CFG_TEST, 10, M, ids, p, "many chunks")
+
+
 def test_moe_prefill_35B_shape_128_tokens():
     """The 35B-A3B shape at 128 tokens (1024 pairs over 256 experts): both stages on the
     small-batch kernel (K = 2048 and K = 512)."""
