@@ -206,6 +206,17 @@ def test_moe_prefill_many_chunks_and_ragged_expert_count():
     check_both_stages(shape, synth.CFG_TEST, 10, M, ids, p, "many chunks")
 
 
+def test_moe_prefill_small_batch_kernel_one_tile_passes():
+    """Stage 1 at K = 6144 runs the small-batch kernel with one 16-row tile per pass (two
+    tiles need K <= 5120): 600 pairs over 32 experts, passes of 16 pairs."""
+    shape = synth.MoEShape("MoE prefill (hidden 6144, 32 experts, I 512, top-2)", 6144, 32, 512, 2)
+    M = 300
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 11, M, shape.E, shape.topk, skew=1.0)
+    assert 448 < M * shape.topk <= 24 * shape.E
+    say(f"[moe prefill] {shape.name}, M={M}")
+    check_both_stages(shape, synth.CFG_TEST, 11, M, ids, p, "one-tile passes")
+
+
 def test_moe_prefill_35B_shape_128_tokens():
     """The 35B-A3B shape at 128 tokens (1024 pairs over 256 experts): both stages on the
     small-batch kernel (K = 2048 and K = 512)."""
