@@ -226,9 +226,13 @@ def test_two_rows_equal_single_row_calls(K):
     for m in range(2):
         assert np.array_equal(run_linear(x[m:m + 1], w)[0], got[m]), f"linear row {m}"
     wq = synth.gen_weight(synth.CFG_TEST, 9, synth.PROJ_QKV, q_out + 2 * kv_out, K)
-    qkv2 = run_qkv(x, wq, q_out, kv_out)
+    lb = synth.gen_lin_bias(synth.CFG_TEST, 9, q_out + 2 * kv_out)
+    qkv2 = run_qkv(x, wq, q_out, kv_out, lin_bias=lb)
+    ref, tol = orc.fused_qkv(x, wq.codes, wq.scales, wq.biases, q_out, kv_out, lb)
+    for name, g, r, t in zip("qkv", qkv2, ref, tol):
+        assert_within(g, r, t, f"qkv M=2 K={K} {name}")
     for m in range(2):
-        one = run_qkv(x[m:m + 1], wq, q_out, kv_out)
+        one = run_qkv(x[m:m + 1], wq, q_out, kv_out, lin_bias=lb)
         for a, b in zip(qkv2, one):
             assert np.array_equal(a[m], b[0]), f"qkv row {m}"
     I = 77
