@@ -30,7 +30,7 @@
 //     pairs (no rounding of any weight), two MFMAs give D[m][n] = sum x (128 + q) over the
 //     group, and the group's scale and bias enter in fp32 as
 //     y += s * (D - 128 * xs) + b * xs, with xs[m] = sum x over the group (an MFMA against
-//     ones);
+//     ones, once per kernel where the registers allow, else once per unit);
 //   * the slice partials of a unit meet in LDS and are added in slice order, each output
 //     by one lane of one of the waves, after the next unit's barrier (two partial buffers:
 //     one barrier per unit) where LDS holds three unit buffers, else after a second one.
