@@ -31,17 +31,20 @@ bias adds a few more, far below 53.  The dot product uses NumPy's fp64 matmul
 (a library primitive) on row blocks to bound memory.
 
 Tolerance (the acceptance rule for a GPU value g against oracle value y):
-    |g - y| <= 1e-3 * A + 2^-12 * S,
-    A = sum_k |x_k| * |w_k|  (+ |lin_bias| if present),  S = sum_k |x_k| * |s_k|,
-evaluated on the GPU's fp32 output before any bf16 rounding.  The first term is
-the stated rule; the second is an fp32 evaluation floor that only matters for
-rows whose weights are (nearly) all exactly zero while their codes are not (see
-`tolerance`); for the workloads' inputs it is below 1e-4 of the first.  A kernel
-that rounds each dequantized weight to bf16 before multiplying (the prefill
-design, which dequantizes weight tiles to bf16) adds the exact bound of that
-rounding, sum |x| |w - bf16(w)| (`bf16_weights=True`).  Derived outputs (SwiGLU,
-expert combine, a projection fed by an upstream GPU result) carry the propagated
-bounds computed below.
+    |g - y| <= 1e-3 * A,   A = sum_k |x_k| * |w_k|  (+ |lin_bias| if present),
+evaluated on the GPU's fp32 output before any bf16 rounding: the stated rule, with
+nothing added, for every workload.  Two documented additions exist for cases where
+the stated rule asks for more than any fp32 evaluation of the design can deliver:
+  * `eval_floor`: rows whose weights are all exactly zero while their codes are not
+    (constant codes 8 with bias -8*scale) make A = 0, so the rule would demand an exact
+    zero; the per-group scale/bias reuse evaluates s*sum(x q) + b*sum(x) in fp32, which
+    cannot promise one.  The floor is the worst-case first-order error bound of that
+    evaluation, derived in `eval_floor`; only tests of such degenerate rows add it.
+  * `bf16_weights=True`: a kernel that rounds each dequantized weight to bf16 before
+    multiplying (the prefill design) adds the exact bound of that rounding,
+    sum |x| |w - bf16(w)|; at short K (K < 512) the stated rule alone can sit below
+    that one rounding for a few elements per million, so only short-K tests add it.
+Derived outputs (SwiGLU, expert combine) carry the propagated bounds computed below.
 """
 from __future__ import annotations
 
@@ -49,7 +52,7 @@ import numpy as np
 
 GROUP = 64
 REL_TOL = 1e-3
-EVAL_FLOOR = 2.0 ** -12
+FP32_U = 2.0 ** -24          # unit roundoff of fp32 (round to nearest)
 # max |d/dg silu(g)| = max sigma(g) * (1 + g * (1 - sigma(g))) ~= 1.09985 (at g ~= 2.40)
 SILU_LIPSCHITZ = 1.0999
 # relative allowance for the GPU's own fp32 evaluation of silu(g) * u
@@ -143,8 +146,9 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024,
       A[m, n] = sum_k |x[m, k]| * |W[n, k]|  (+ |lin_bias[n]|)
       S[m, n] = sum_k |x[m, k]| * |s[n, k // G]|    (activation mass weighted by the scale,
                                                      i.e. the size of a one-code change)
+      B[m, n] = sum_k |x[m, k]| * |b[n, k // G]|    (the same for the bias)
     and, with bf16_weights, R[m, n] = sum_k |x[m, k]| * |W[n, k] - bf16(W[n, k])| (the
-    largest effect of rounding every dequantized weight to bf16, RNE) as a fourth value.
+    largest effect of rounding every dequantized weight to bf16, RNE) as a fifth value.
     x_bits: bf16 bits [M, K] (or [K]); codes [N, K*bits/32]; scales/biases [N, K/G];
     lin_bias: optional bf16 bits [N]."""
     x = bf16_to_f64(x_bits)
@@ -162,6 +166,7 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024,
     ax = np.abs(x)
     xg = ax.reshape(x.shape[0], K // G, G).sum(axis=2)                  # [M, K/G]
     S = xg @ np.abs(bf16_to_f64(scales)).T
+    B = xg @ np.abs(bf16_to_f64(biases)).T
     for r0 in range(0, N, row_block):
         r1 = min(N, r0 + row_block)
         W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1], bits)
@@ -173,31 +178,51 @@ def project(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024,
         lb = bf16_to_f64(lin_bias)
         y += lb[None, :]
         A += np.abs(lb)[None, :]
-    out = (y, A, S, R) if bf16_weights else (y, A, S)
+    out = (y, A, S, B, R) if bf16_weights else (y, A, S, B)
     if squeeze:
         return tuple(v[0] for v in out)
     return out
 
 
-def tolerance(A, S) -> np.ndarray:
-    """Acceptance bound of one projection output: 1e-3 * sum|x w| (the stated rule), plus
-    an fp32 evaluation floor of 2^-12 * sum|x| |s| -- 1/4096 of the effect of moving every
-    code of the row by one step.  The floor only matters when sum|x w| is (near) zero
-    while the codes are not: with every weight exactly s*q + b = 0 the stated rule would
-    demand an exact zero, which no fp32 evaluation of s*sum(x q) + b*sum(x) can promise."""
-    return REL_TOL * np.asarray(A) + EVAL_FLOOR * np.asarray(S)
+def tolerance(A) -> np.ndarray:
+    """Acceptance bound of one projection output: the stated rule, 1e-3 * sum|x w|."""
+    return REL_TOL * np.asarray(A)
+
+
+def eval_floor(S, B) -> np.ndarray:
+    """Worst-case first-order error of evaluating one 4-bit projection output in fp32 the
+    way the decode design does (per-group scale/bias reuse, "Sanctum-MLX" and the pages'
+    affine u4 format; the bias term reduces to b * sum(x)), for rows where the stated rule
+    demands an exact zero.  S = sum_k |x_k| |s_k|, B = sum_k |x_k| |b_k|.
+
+    Per chunk of 32 inputs with scale s and bias b the value is t = s*(D - 128 X) + b*X,
+    D = sum x (128 + q) and X = sum x, each a chain of 32 products (exact in fp32: bf16
+    times an 8-bit integer) added with at most 32 roundings; a rounding of a partial sum
+    of terms bounded by T costs at most u*T, u = 2^-24.  So
+        |D - D*| <= 32 u (128 + 15) sum|x|,     |X - X*| <= 32 u sum|x|,
+        |fl(D - 128 X) - sum x q| <= (32*143 + 128*32 + 15) u sum|x| = 8687 u sum|x|,
+    and t adds |b| 32 u sum|x|.  Accumulating the chunk terms of a row (two fused
+    multiply-adds per chunk, at most 5 chunks per lane, 5 lane-sum steps, up to 16 K
+    slices: at most 31 roundings of partial sums bounded by sum (15|s| + |b|) |x|) adds
+    31 u (15 S + B).  Total: (8687 + 465) u S + (32 + 31) u B = 9152 u S + 63 u B."""
+    return FP32_U * (9152.0 * np.asarray(S) + 63.0 * np.asarray(B))
 
 
 def linear(x_bits, codes, scales, biases, lin_bias=None, row_block: int = 1024, bf16_weights: bool = False,
-           bits: int = 4):
-    """(y, tol) of one projection; tol per `tolerance`.  With bf16_weights (a kernel that
-    rounds each dequantized weight to bf16 before multiplying, as the prefill design
-    does), tol also carries R = sum |x| |w - bf16(w)|, the bound of that rounding."""
+           bits: int = 4, floor: bool = False):
+    """(y, tol) of one projection; tol = 1e-3 * sum|x w| (`tolerance`).  With bf16_weights
+    (a kernel that rounds each dequantized weight to bf16 before multiplying, as the
+    prefill design does) tol also carries R = sum |x| |w - bf16(w)|, the bound of that
+    rounding; with floor (rows of exactly zero weights) the fp32 evaluation floor
+    `eval_floor` of the 4-bit decode design."""
+    out = project(x_bits, codes, scales, biases, lin_bias, row_block, bf16_weights=bf16_weights, bits=bits)
+    y, A, S, B = out[:4]
+    t = tolerance(A)
+    if floor:
+        t = t + eval_floor(S, B)
     if bf16_weights:
-        y, A, S, R = project(x_bits, codes, scales, biases, lin_bias, row_block, bf16_weights=True, bits=bits)
-        return y, tolerance(A, S) + R
-    y, A, S = project(x_bits, codes, scales, biases, lin_bias, row_block, bits=bits)
-    return y, tolerance(A, S)
+        t = t + out[4]
+    return y, t
 
 
 # ---- fused QKV -------------------------------------------------------------
@@ -350,13 +375,10 @@ def moe_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: 
     return h, t
 
 
-def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, expert_w,
-                     h_err=None, bits: int = 4):
+def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, expert_w, bits: int = 4):
     """Stage 2: y = sum_k p_k * (D_{ids[k]} h_k), k in increasing order; ids outside [0, E)
     contribute nothing.  h_bits: bf16 bits [topk, K] of the stage-1 output fed to both
-    sides; p: the fp32 combine weights.  Returns (y, tol).  h_err (optional [topk, K])
-    bounds how far the h actually fed to the GPU may be from h_bits; it is propagated
-    through |D|."""
+    sides; p: the fp32 combine weights.  Returns (y, tol)."""
     E = grid_codes.shape[0]
     rows = grid_codes.shape[1]
     y = np.zeros(rows)
@@ -367,14 +389,11 @@ def moe_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, e
             yk, tk = linear(np.asarray(h_bits)[k], grid_codes[e], grid_scales[e], grid_biases[e], bits=bits)
             y += p[k] * yk
             t += abs(p[k]) * tk
-            if h_err is not None:
-                W = dequant(grid_codes[e], grid_scales[e], grid_biases[e], bits)
-                t += abs(p[k]) * (np.abs(W) @ np.asarray(h_err[k], np.float64))
     return y, t
 
 
 def moe_prefill_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids, rows: int,
-                        bf16_weights: bool = True):
+                        bf16_weights: bool = False):
     """Stage 1 over a batch of tokens (prefill): for token m and slot k with expert
     e = ids[m, k] in [0, E), h[m, k] = silu(G_e x_m) * (U_e x_m); other pairs get h = 0.
     Computed expert by expert, as the pages' in-place expert grid is meant to be used:
@@ -401,7 +420,7 @@ def moe_prefill_gate_up(x_bits, grid_codes, grid_scales, grid_biases, expert_ids
 
 
 def moe_prefill_down_combine(h_bits, grid_codes, grid_scales, grid_biases, expert_ids, expert_w,
-                             bf16_weights: bool = True):
+                             bf16_weights: bool = False):
     """Stage 2 over a batch of tokens: y[m] = sum_k p[m, k] * (D_e h[m, k]) with
     e = ids[m, k]; pairs with no expert contribute nothing.  h_bits: bf16 bits
     [M, topk, K] fed to both sides; p: the fp32 combine weights [M, topk].  Computed
@@ -426,41 +445,9 @@ def moe_prefill_down_combine(h_bits, grid_codes, grid_scales, grid_biases, exper
     return y, t
 
 
-def linear_with_input_error(x_bits, codes, scales, biases, x_err, lin_bias=None, row_block: int = 1024):
-    """A projection whose GPU input may differ from x_bits by at most x_err per element
-    (an upstream GPU result): tolerance 1e-3*A + |W| . x_err."""
-    y, t = linear(x_bits, codes, scales, biases, lin_bias)
-    e = np.asarray(x_err, np.float64)
-    extra = np.empty_like(y)
-    N = codes.shape[0]
-    for r0 in range(0, N, row_block):
-        r1 = min(N, r0 + row_block)
-        W = dequant(codes[r0:r1], scales[r0:r1], biases[r0:r1])
-        extra[..., r0:r1] = e @ np.abs(W).T
-    return y, t + extra
-
-
 def f32_to_bf16_bits(v) -> np.ndarray:
     """Round fp64/fp32 values to fp32 and then to bf16 (round to nearest, ties to even)
     by integer arithmetic on the fp32 bit pattern; NaN is not expected here."""
     b = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
     r = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
     return r.astype(np.uint16)
-
-
-def bf16_input_error(h, tol) -> np.ndarray:
-    """Bound on |RNE(h_gpu) - RNE(h)| when |h_gpu - h| <= tol, for the bf16 copy of an
-    upstream result that a downstream projection reads.  Rounding is monotonic, so the
-    GPU's rounded value lies between RNE(h - tol) and RNE(h + tol)."""
-    h = np.asarray(h, np.float64)
-    tol = np.asarray(tol, np.float64)
-    mid = bf16_to_f64(f32_to_bf16_bits(h))
-    lo = bf16_to_f64(f32_to_bf16_bits(h - tol))
-    hi = bf16_to_f64(f32_to_bf16_bits(h + tol))
-    # the fp32 rounding of h +- tol on the way may shift by half an fp32 ulp; widen by it
-    return np.maximum(np.abs(mid - lo), np.abs(hi - mid)) + np.ldexp(np.abs(h) + tol, -24)
-
-
-def bf16_round_bound(v) -> np.ndarray:
-    """Largest error of rounding v to bf16 (8 significant bits): half an ulp <= 2^-8 |v|."""
-    return np.ldexp(np.abs(np.asarray(v, np.float64)), -8)

@@ -72,6 +72,19 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def bf16_term(M: int, K: int, heavy_tailed: bool = False) -> bool:
+    """Whether a check adds the oracle's bf16-weight term (`bf16_weights`): only where the
+    prefill GEMM runs (M > 8), which rounds each dequantized weight to bf16, and only where
+    the stated 1e-3 rule alone can be narrower than that one rounding: at short K (K < 512)
+    for a few elements per million, and at any K where the terms of a row are heavy-tailed
+    (fp8 e4m3 codes, whose values span 2^-9 .. 448, or activations spread over six decades):
+    a few large terms then carry the sum and their rounding errors do not average out (seen
+    with fp8 at K = 640: 1.08 times the stated rule, matching the bf16-weight product
+    computed in fp64).  Elsewhere the rounding errors of a row largely cancel and every check
+    uses the stated rule alone."""
+    return M > 8 and (K < 512 or heavy_tailed)
+
+
 def assert_within(gpu, ref, tol, what: str):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)

@@ -8,7 +8,7 @@ import torch
 import gemm_affine_u4_amd as qmm
 import synth
 from oracle import qmm_oracle as orc
-from gpu_util import Guarded, assert_within, dev, rne_bits_of, say
+from gpu_util import bf16_term, Guarded, assert_within, dev, rne_bits_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_linear_formats(bits, G, M, K, N):
     w = W(bits, G, N, K, 1)
     lb = synth.gen_lin_bias(synth.CFG_TEST, 1, N)
     x = synth.gen_x(synth.CFG_TEST, 1, M, M, K)
-    y, t = orc.linear(x, w.codes, w.scales, w.biases, lb, bf16_weights=M > 8, bits=ob(bits))
+    y, t = orc.linear(x, w.codes, w.scales, w.biases, lb, bf16_weights=bf16_term(M, K, bits == FP8), bits=ob(bits))
     g = lin(bits, G, x, w, N, lb=lb)
     assert_within(g, y, t, f"u{bits} g{G} linear M={M} K={K}")
     assert np.array_equal(lin(bits, G, x, w, N, f32=False, lb=lb), rne_bits_of(g))
@@ -63,11 +63,11 @@ def test_fused_qkv_and_gate_up_formats(bits, G, M):
     x = synth.gen_x(synth.CFG_TEST, 2, M, M, K)
     wq = W(bits, G, q_out + 2 * kv_out, K, 2)
     (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, wq.codes, wq.scales, wq.biases, q_out, kv_out,
-                                            bf16_weights=M > 8, bits=ob(bits))
+                                            bf16_weights=bf16_term(M, K, bits == FP8), bits=ob(bits))
     gq, gk, gv = Guarded((M, q_out), True), Guarded((M, kv_out), True), Guarded((M, kv_out), True)
     qmm.qmm_fused_qkv_fmt(bits, G, dev(x), dev(wq.codes), dev(wq.scales), dev(wq.biases), gq.t, gk.t, gv.t)
     wg = W(bits, G, 2 * I, K, 3)
-    h, th = orc.gate_up_swiglu(x, wg.codes, wg.scales, wg.biases, I, bf16_weights=M > 8, bits=ob(bits))
+    h, th = orc.gate_up_swiglu(x, wg.codes, wg.scales, wg.biases, I, bf16_weights=bf16_term(M, K, bits == FP8), bits=ob(bits))
     gh = Guarded((M, I), True)
     qmm.qmm_fused_gate_up_swiglu_fmt(bits, G, dev(x), dev(wg.codes), dev(wg.scales), dev(wg.biases), gh.t)
     torch.cuda.synchronize()
@@ -119,7 +119,7 @@ def test_largest_K_per_width(bits):
     for M in (1, 16):
         say(f"[fmt] u{bits} K={K} M={M}")
         x = synth.gen_x(synth.CFG_TEST, 6, M, M, K)
-        y, t = orc.linear(x, w.codes, w.scales, w.biases, bf16_weights=M > 8, bits=ob(bits))
+        y, t = orc.linear(x, w.codes, w.scales, w.biases, bf16_weights=bf16_term(M, K, bits == FP8), bits=ob(bits))
         assert_within(lin(bits, 64, x, w, N), y, t, f"u{bits} K={K} M={M}")
 
 

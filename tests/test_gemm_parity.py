@@ -1,13 +1,13 @@
 """GPU parity of the prefill path (M > 8: LDS dequant + MFMA GEMM) against the fp64 oracle.
 
-Same acceptance rule as the decode path (the oracle's `tolerance`, propagated for
-SwiGLU), on the fp32 output before bf16 rounding, plus the exact bound of the one
-extra rounding the prefill design makes: each dequantized weight is rounded to bf16
-before the MFMA (tiles dequantized to bf16 in LDS), which the oracle carries as
-sum |x| |w - bf16(w)| (`bf16_weights=True`; zero for the exactly representable case
-below, which keeps the stated bound).  The GEMM is therefore not bit-equal to the
-decode GEMV; both are checked against the oracle, and a GEMM row is also compared
-with the GEMV on that row."""
+Same acceptance rule as the decode path: the stated 1e-3 * sum|x w| (propagated for
+SwiGLU), on the fp32 output before bf16 rounding.  The prefill design rounds each
+dequantized weight to bf16 before the MFMA (tiles dequantized to bf16 in LDS); at short
+K (< 512) the check adds that rounding's exact bound, sum |x| |w - bf16(w)|
+(`bf16_term`), and from K = 512 up, the 14B shapes included, it uses the stated rule
+alone.  The GEMM is therefore not bit-equal to the decode GEMV; both are checked against
+the oracle, a GEMM row is also compared with the GEMV on that row, and the fused
+gate+up GEMM equals SwiGLU of the two unfused GEMM projections."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +15,7 @@ import torch
 import gemm_affine_u4_amd as qmm
 import synth
 from oracle import qmm_oracle as orc
-from gpu_util import Guarded, assert_within, dev, dev_weight, rne_bits_of, say
+from gpu_util import bf16_term, Guarded, assert_within, dev, dev_weight, rne_bits_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def test_prefill_fused_qkv_14B_shape():
     say(f"[gemm] fused QKV prefill M={M} K={sh.K} rows={sh.qkv_rows}")
     w = synth.gen_weight(synth.CFG_PREFILL, 0, synth.PROJ_QKV, sh.qkv_rows, sh.K)
     x = synth.gen_x(synth.CFG_PREFILL, 0, 0, M, sh.K)
-    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, w.codes, w.scales, w.biases, sh.q_out, sh.kv_out, bf16_weights=True)
+    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, w.codes, w.scales, w.biases, sh.q_out, sh.kv_out)
     g = run_qkv(x, w, sh.q_out, sh.kv_out)
     for got, ref, tol, nm in zip(g, (q, k, v), (tq, tk, tv), "QKV"):
         assert_within(got, ref, tol, f"prefill {nm}")
@@ -72,11 +72,21 @@ def test_prefill_gate_up_14B_shape():
     say(f"[gemm] fused gate+up prefill M={M} K={sh.K} I={sh.I}")
     w = synth.gen_weight(synth.CFG_PREFILL, 0, synth.PROJ_GATE_UP, 2 * sh.I, sh.K)
     x = synth.gen_x(synth.CFG_PREFILL, 0, 0, M, sh.K)
-    h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, sh.I, bf16_weights=True)
+    h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, sh.I)
     g = run_gate_up(x, w, sh.I)
     assert_within(g, h, th, "prefill h")
     gb = run_gate_up(x, w, sh.I, f32=False)
     assert np.array_equal(gb, rne_bits_of(g)), "bf16 output != RNE(fp32 output)"
+    # the fused gate+up GEMM against SwiGLU of the two unfused GEMM projections ("The
+    # Cathedral Doubled Itself", the two fusions: one matmul over [gate; up] then
+    # SiLU * multiply): the gate and up accumulators are the unfused values bit for bit,
+    # so only the fp32 evaluation of silu(g) * u separates them
+    gl = run_linear(x, w.slice_rows(0, sh.I))
+    ul = run_linear(x, w.slice_rows(sh.I, 2 * sh.I))
+    ref = orc.swiglu(gl, ul)
+    rel = np.abs(g - ref) / np.maximum(np.abs(ref), 1e-30)
+    say(f"  fused vs swiglu(unfused): max rel {rel.max():.3g}")
+    assert np.all(np.abs(g - ref) <= 2.0 ** -20 * np.abs(ref) + 1e-30)
 
 
 RAGGED = [
@@ -95,7 +105,8 @@ def test_prefill_ragged_qkv(name, M, K, q_out, kv_out):
     w = synth.gen_weight(synth.CFG_TEST, 100 + M, synth.PROJ_QKV, q_out + 2 * kv_out, K, bias="uniform")
     x = synth.gen_x(synth.CFG_TEST, 100 + M, 0, M, K)
     lb = synth.gen_lin_bias(synth.CFG_TEST, 100 + M, q_out + 2 * kv_out)
-    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, w.codes, w.scales, w.biases, q_out, kv_out, lb, bf16_weights=True)
+    (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, w.codes, w.scales, w.biases, q_out, kv_out, lb,
+                                            bf16_weights=bf16_term(M, K))
     g = run_qkv(x, w, q_out, kv_out, lin_bias=lb)
     for got, ref, tol, nm in zip(g, (q, k, v), (tq, tk, tv), "QKV"):
         assert_within(got, ref, tol, f"{name} {nm}")
@@ -106,7 +117,7 @@ def test_prefill_ragged_gate_up(M, K, I):
     say(f"[gemm] gate+up M={M} K={K} I={I}")
     w = synth.gen_weight(synth.CFG_TEST, 200 + M, synth.PROJ_GATE_UP, 2 * I, K)
     x = synth.gen_x(synth.CFG_TEST, 200 + M, 0, M, K, magnitude="varied")
-    h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, I, bf16_weights=True)
+    h, th = orc.gate_up_swiglu(x, w.codes, w.scales, w.biases, I, bf16_weights=bf16_term(M, K, heavy_tailed=True))
     assert_within(run_gate_up(x, w, I), h, th, f"gate+up M={M} K={K} I={I}")
 
 
@@ -116,7 +127,7 @@ def test_prefill_linear_down_shape_and_determinism():
     say(f"[gemm] linear M={M} K={K} N={N}")
     w = synth.gen_weight(synth.CFG_TEST, 300, synth.PROJ_DOWN, N, K)
     x = synth.gen_x(synth.CFG_TEST, 300, 0, M, K)
-    y, t = orc.linear(x, w.codes, w.scales, w.biases, bf16_weights=True)
+    y, t = orc.linear(x, w.codes, w.scales, w.biases)
     a = run_linear(x, w)
     assert_within(a, y, t, "down M=64")
     assert np.array_equal(a, run_linear(x, w))

@@ -173,7 +173,7 @@ def test_e4m3_weights_dequantize_as_scaled_values():
     assert np.array_equal(W, np.repeat(s, 64, 1) * v + np.repeat(b, 64, 1))
     # brute force through the value table
     x = _rand_bf16_bits(np.random.default_rng(7), (2, 128), -3, 2)
-    y, A, S = orc.project(x, w.codes, w.scales, w.biases, bits=orc.E4M3)
+    y, A, S, B = orc.project(x, w.codes, w.scales, w.biases, bits=orc.E4M3)
     xv = orc.bf16_to_f64(x)
     ref = np.array([[math.fsum(xv[m, k] * W[n, k] for k in range(128)) for n in range(4)] for m in range(2)])
     assert np.allclose(y, ref, rtol=0, atol=1e-12 * A.max())
@@ -188,7 +188,7 @@ def test_oracle_matches_brute_force_other_formats(bits, G):
     s = _rand_bf16_bits(rng, (N, K // G), -10, -4)
     b = _rand_bf16_bits(rng, (N, K // G), -8, -2)
     x = _rand_bf16_bits(rng, (M, K), -3, 2)
-    y, A, S = orc.project(x, words, s, b, bits=bits)
+    y, A, S, B = orc.project(x, words, s, b, bits=bits)
     yb, Ab = brute.project(x.tolist(), q.tolist(), s.tolist(), b.tolist(), group=G)
     assert np.allclose(y, np.array(yb), rtol=0, atol=1e-12 * np.array(Ab).max())
     assert np.allclose(A, np.array(Ab), rtol=1e-12)
@@ -219,7 +219,7 @@ def test_oracle_matches_brute_force(M, K, N, with_bias):
     b = _rand_bf16_bits(rng, (N, K // 64))
     x = _rand_bf16_bits(rng, (M, K), -4, 4)
     lb = _rand_bf16_bits(rng, (N,)) if with_bias else None
-    y, A, S = orc.project(x, words, s, b, lin_bias=lb)
+    y, A, S, B = orc.project(x, words, s, b, lin_bias=lb)
     yb, Ab = brute.project(x.tolist(), q.tolist(), s.tolist(), b.tolist(),
                            lin_bias_bits=None if lb is None else lb.tolist())
     yb, Ab = np.array(yb), np.array(Ab)
@@ -303,9 +303,9 @@ def test_fused_qkv_equals_three_unfused_projections():
     (q, k, v), (tq, tk, tv) = orc.fused_qkv(x, fused.codes, fused.scales, fused.biases, q_out, kv_out, lb)
     offs = [0, q_out, q_out + kv_out, q_out + 2 * kv_out]
     for i, (got, tol) in enumerate([(q, tq), (k, tk), (v, tv)]):
-        ref, A, S = orc.project(x, parts[i].codes, parts[i].scales, parts[i].biases, lb[offs[i]:offs[i + 1]])
+        ref, A, S, B = orc.project(x, parts[i].codes, parts[i].scales, parts[i].biases, lb[offs[i]:offs[i + 1]])
         assert np.allclose(got, ref, rtol=0, atol=1e-13 * A.max())
-        assert np.allclose(tol, 1e-3 * A + 2.0 ** -12 * S, rtol=1e-14)
+        assert np.allclose(tol, 1e-3 * A, rtol=1e-14)
 
 
 def test_fused_gate_up_equals_swiglu_of_unfused():
@@ -658,32 +658,76 @@ def test_oracle_bf16_rounding_matches_torch():
     assert np.array_equal(ours, ref)
 
 
-def test_bf16_input_error_bounds_every_rounding_of_a_nearby_value():
-    rng = np.random.default_rng(12)
-    h = rng.standard_normal(20000) * 3
-    tol = np.abs(rng.standard_normal(20000)) * 1e-3
-    bound = orc.bf16_input_error(h, tol)
-    base = orc.bf16_to_f64(orc.f32_to_bf16_bits(h))
-    for f in (-1.0, -0.5, 0.0, 0.5, 1.0):
-        got = orc.bf16_to_f64(orc.f32_to_bf16_bits(h + f * tol))
-        assert np.all(np.abs(got - base) <= bound)
-
-
 def test_scale_mass_and_floor():
-    """S = sum|x||s| from its definition, and the evaluation floor is negligible next to
-    1e-3 * sum|x w| on the workloads' weights (bias = -8 * scale, codes uniform)."""
+    """S = sum|x||s| and B = sum|x||b| from their definitions; the derived evaluation floor is
+    0.14 of the stated term 1e-3 * sum|x w| on the workloads' weights (bias = -8 * scale,
+    codes uniform: A ~ 4 S and B = 8 S), which is why no workload check adds it; on all-zero
+    weights with non-zero codes A is 0 and only the floor remains."""
     w = synth.gen_weight(synth.CFG_14B, 0, 0, 64, 5120)
     x = synth.gen_x(synth.CFG_14B, 0, 0, 1, 5120)
-    y, A, S = orc.project(x, w.codes, w.scales, w.biases)
+    y, A, S, B = orc.project(x, w.codes, w.scales, w.biases)
     xv = np.abs(orc.bf16_to_f64(x[0]))
     s = np.abs(orc.bf16_to_f64(w.scales))
+    b = np.abs(orc.bf16_to_f64(w.biases))
     S_def = np.array([sum(xv[k] * s[n, k // 64] for k in range(0, 5120)) for n in range(3)])
+    B_def = np.array([sum(xv[k] * b[n, k // 64] for k in range(0, 5120)) for n in range(3)])
     assert np.allclose(S[0, :3], S_def, rtol=1e-12)
-    assert np.max(orc.EVAL_FLOOR * S / (orc.REL_TOL * A)) < 0.1
+    assert np.allclose(B[0, :3], B_def, rtol=1e-12)
+    ratio = orc.eval_floor(S, B) / (orc.REL_TOL * A)
+    assert 0.12 < np.median(ratio) < 0.16
+    _, t_plain = orc.linear(x, w.codes, w.scales, w.biases)
+    assert np.array_equal(t_plain, orc.REL_TOL * A)
     # all-zero weights with non-zero codes: the stated rule alone would demand an exact zero
     z = synth.U4Weight(np.full_like(w.codes, 0x88888888), w.scales, w.biases)
-    y0, A0, S0 = orc.project(x, z.codes, z.scales, z.biases)
+    y0, A0, S0, B0 = orc.project(x, z.codes, z.scales, z.biases)
     assert np.all(y0 == 0) and np.all(A0 == 0) and np.all(S0 > 0)
+    _, t0 = orc.linear(x, z.codes, z.scales, z.biases, floor=True)
+    assert np.array_equal(t0, orc.eval_floor(S0, B0))
+
+
+def _f32_chunk_eval(xv, q, s, b):
+    """The decode design's fp32 evaluation of one row, written out with float32 steps in the
+    least favourable rounding grouping (every product added on its own): per chunk of 32
+    inputs D = sum x (128 + q) and X = sum x in input order, t = s*(D - 128 X) + b*X, chunk
+    terms added in order.  Test helper only (not the oracle, not the GPU code)."""
+    f = np.float32
+    acc = f(0)
+    for c0 in range(0, len(xv), 32):
+        D = f(0)
+        X = f(0)
+        for k in range(c0, c0 + 32):
+            D = f(D + f(xv[k]) * f(128 + int(q[k])))
+            X = f(X + f(xv[k]))
+        d = f(D - f(128) * X)
+        g = (c0 // 64)
+        acc = f(acc + f(s[g]) * d)
+        acc = f(acc + f(b[g]) * X)
+    return float(acc)
+
+
+@pytest.mark.parametrize("case", ["same-sign", "zero-weights", "random"])
+def test_eval_floor_bounds_an_fp32_evaluation(case):
+    """The floor is an upper bound of the fp32 evaluation error of the per-group scale/bias
+    form, on inputs chosen to make the cancellation D - 128 X as large as it gets (all x
+    of one sign, constant code 8 so every weight is exactly zero, or random codes)."""
+    rng = np.random.default_rng({"same-sign": 1, "zero-weights": 2, "random": 3}[case])
+    K = 2048
+    mag = np.exp(rng.uniform(-3, 3, K))          # spread magnitudes: partial sums round unevenly
+    x = orc.f32_to_bf16_bits((np.abs(rng.standard_normal(K)) + 0.5) * mag)
+    xv = orc.bf16_to_f64(x)
+    q = np.full(K, 8) if case == "zero-weights" else rng.integers(0, 16, K)
+    if case == "same-sign":
+        q = rng.integers(12, 16, K)
+    s_bits = orc.f32_to_bf16_bits(rng.uniform(0.001, 0.01, K // 64))
+    b_bits = orc.f32_to_bf16_bits(-8.0 * orc.bf16_to_f64(s_bits))
+    words = np.array([brute.pack_row(q)], np.uint32)
+    y, A, S, B = orc.project(x, words, s_bits[None], b_bits[None])
+    got = _f32_chunk_eval(xv, q, orc.bf16_to_f64(s_bits), orc.bf16_to_f64(b_bits))
+    err = abs(got - y)
+    floor = orc.eval_floor(S, B)
+    assert err <= floor
+    if case == "zero-weights":
+        assert y == 0.0 and err > 0.0      # the stated rule alone would reject this
 
 
 def test_bf16_weight_rounding_term():
@@ -691,7 +735,7 @@ def test_bf16_weight_rounding_term():
     (torch's bf16 cast of each weight) otherwise, and never above 2^-9 * A."""
     w = synth.gen_weight(synth.CFG_TEST, 12, 0, 24, 256, bias="uniform")
     x = synth.gen_x(synth.CFG_TEST, 12, 0, 3, 256)
-    y, A, S, R = orc.project(x, w.codes, w.scales, w.biases, bf16_weights=True)
+    y, A, S, B, R = orc.project(x, w.codes, w.scales, w.biases, bf16_weights=True)
     W = orc.dequant(w.codes, w.scales, w.biases)
     Wb = torch.from_numpy(W).to(torch.bfloat16).to(torch.float64).numpy()
     ref = np.abs(orc.bf16_to_f64(x)) @ np.abs(W - Wb).T
@@ -702,7 +746,7 @@ def test_bf16_weight_rounding_term():
     allowed = np.array([0, 4, 6, 7, 8, 9, 10, 12], np.uint32)
     q = allowed[np.random.default_rng(0).integers(0, 8, size=(8, 128))]
     words = np.array([brute.pack_row(r) for r in q], np.uint32)
-    _, _, _, R0 = orc.project(x[:, :128], words, z.scales, z.biases, bf16_weights=True)
+    _, _, _, _, R0 = orc.project(x[:, :128], words, z.scales, z.biases, bf16_weights=True)
     assert np.all(R0 == 0)
     _, t_dec = orc.linear(x, w.codes, w.scales, w.biases)
     _, t_pre = orc.linear(x, w.codes, w.scales, w.biases, bf16_weights=True)

@@ -11,7 +11,7 @@ import torch
 import gemm_affine_u4_amd as qmm
 import synth
 from oracle import qmm_oracle as orc
-from gpu_util import Guarded, assert_within, dev, rne_bits_of, say
+from gpu_util import bf16_term, Guarded, assert_within, dev, rne_bits_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,7 @@ def check(sh, cfg, layer, M, contiguous=True, sample=None, with_bias=True):
     got = run(sh, x, w, lb, pos, tab)
     rows = np.arange(M) if sample is None else sample
     ref, tol = orc.qkv_rope(x[rows], w.codes, w.scales, w.biases, sh.n_q, sh.n_kv, sh.head_dim, sh.q_gate,
-                            sh.rot, pos[rows], tab, lb, bf16_weights=M > 8)
+                            sh.rot, pos[rows], tab, lb, bf16_weights=bf16_term(M, sh.K))
     for name, g, r, t in zip(("q", "gate", "k", "v"), got, ref, tol):
         if r is None:
             assert g is None
