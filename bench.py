@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--pool", type=int, default=48, help="layer copies in the rotating weight pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-steps", type=int, default=6)
+    ap.add_argument("--cpu-sample-steps", type=int, default=2)
     ap.add_argument("--kernel-reps", type=int, default=1000,
                     help="launches per graph when timing one kernel on its own")
     ap.add_argument("--prefill-reps", type=int, default=20)
@@ -198,6 +198,7 @@ def main():
     ach_qkv = bytes_qkv / (ms_qkv * 1e-3) / 1e9
 
     copy_gbs = device_copy_gbs(torch, dev)
+    read_ceiling = hbm_read_ceiling(torch, dev, T)
 
     result = {
         "metric": "achieved HBM GB/s (% of peak) fused u4 GEMV M=1; prefill GEMM TFLOP/s",
@@ -226,9 +227,13 @@ def main():
                     "fused_gate_up_gemv": {"avg_launch_us": ms_gu * 1e3, "GB/s": round(ach_gu, 1),
                                            "bytes_per_launch": bytes_gu}},
         "device_copy_GBps": round(copy_gbs, 1),
+        "hbm_read_ceiling_GBps": read_ceiling,
     }
+    c100 = read_ceiling["100MB"]["GB/s"]
+    result["pct_of_read_ceiling_100MB"] = round(100 * value / c100, 2)
 
     if not args.headline_only:
+        result["mfma_ceiling"] = mfma_ceiling(torch, dev, T)
         result["qkv_rope"] = bench_rope(torch, qmm, synth, T, dev, pq, args.prefill_reps)
         result["prefill_gemm"] = bench_prefill(torch, qmm, synth, T, dev, pq, pg, args.prefill_reps)
         result["small_batch"] = bench_small_batch(torch, qmm, synth, T, dev, pq, pg)
@@ -262,6 +267,75 @@ def pool_of(torch, dev, w, P):
         stack.copy_(t.unsqueeze(0).expand_as(stack))
         out.append(stack)
     return out
+
+
+def _ceiling_lib():
+    import ctypes
+    path = os.path.join(ROOT, "gemm_affine_u4_amd", "libqmm_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m gemm_affine_u4_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.qmm_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.qmm_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def hbm_read_ceiling(torch, dev, T):
+    """Plain streaming read (no compute, 16-byte non-temporal loads) per launch size, timed
+    like the kernels: a HIP graph of launches, each on its own slice of a 2 GiB pool (8x the
+    last-level cache), and one 4 GiB buffer.  Best over launch shapes (waves per CU, 1 KB
+    loads in flight per wave, a contiguous slice per wave or interleaved groups): the rate a
+    single launch of that many bytes reaches on this GPU, the ceiling a GEMV of that size
+    per launch can approach."""
+    lib = _ceiling_lib()
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    st = T.stream.cuda_stream
+    shapes = [(256 * b, u, il) for b in (2, 4, 8) for u in (2, 4) for il in (0, 1)]
+
+    def best_of(fn_for, n, nbytes):
+        best = None
+        for blocks, unroll, il in shapes:
+            ms = T.per_call_ms(fn_for(blocks, unroll, il), n)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks // 256 * 4, unroll, il, ms * 1e3)
+        return {"GB/s": round(best[0], 1), "us": round(best[4], 2), "waves_per_cu": best[1],
+                "loads_in_flight_per_wave": best[2], "partition": "interleaved" if best[3] else "contiguous"}
+
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    pool.fill_(1)
+    out = {}
+    for name, nbytes in [("20MB", 20 << 20), ("80MB", 80 << 20), ("100MB", 100 << 20), ("168MB", 168 << 20)]:
+        nsl = (2 << 30) // nbytes
+
+        def fn_for(blocks, unroll, il, nbytes=nbytes, nsl=nsl):
+            return lambda i: lib.qmm_ceiling_read(pool.data_ptr() + (i % nsl) * nbytes, nbytes, blocks, unroll, il,
+                                                  sink.data_ptr(), st)
+        out[name] = best_of(fn_for, max(2 * nsl, 40), nbytes)
+    del pool
+    torch.cuda.empty_cache()
+    big = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    out["4GiB"] = best_of(lambda b, u, il: (lambda i: lib.qmm_ceiling_read(big.data_ptr(), 4 << 30, b, u, il,
+                                                                          sink.data_ptr(), st)), 4, 4 << 30)
+    del big
+    torch.cuda.empty_cache()
+    return out
+
+
+def mfma_ceiling(torch, dev, T):
+    """Register-only loop of v_mfma_f32_32x32x16_bf16 (four independent accumulators per wave,
+    8 waves per SIMD): the bf16 matrix rate this GPU sustains, next to the published peak."""
+    lib = _ceiling_lib()
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    st = T.stream.cuda_stream
+    blocks, iters = 256 * 8, 4000
+    ms = T.per_call_ms(lambda i: lib.qmm_ceiling_mfma(blocks, iters, sink.data_ptr(), st), 5)
+    flop = blocks * 4 * 4 * iters * 32768.0
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"TFLOP/s": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "kernel": "v_mfma_f32_32x32x16_bf16 register loop, 32 waves per CU"}
 
 
 def device_copy_gbs(torch, dev):
@@ -628,24 +702,54 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
                                       "gathered GEMM", **small}}
 
 
-def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step):
-    """The fp64 oracle, as it stands, on the same layer: n_steps full decode steps."""
-    from threadpoolctl import threadpool_limits
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(n_steps, w_qkv, w_gu, bytes_step, runs: int = 5):
+    """The fp64 oracle, as it stands, on the same layer: one run = n_steps full decode steps
+    (fused QKV + fused gate+up+SwiGLU), median of `runs` runs, with BLAS on every available
+    core and on one thread.  The oracle's dequantization is NumPy elementwise work (one
+    thread); its dot products are BLAS calls, which use the BLAS thread count."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     import synth
     from oracle import qmm_oracle as orc
 
     sh = synth.DENSE_14B
     x = synth.gen_x(synth.CFG_14B, 0, 0, 1, sh.K)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for _ in range(n_steps):
-            orc.fused_qkv(x, w_qkv.codes, w_qkv.scales, w_qkv.biases, sh.q_out, sh.kv_out)
-            orc.gate_up_swiglu(x, w_gu.codes, w_gu.scales, w_gu.biases, sh.I)
-        dt = time.perf_counter() - t0
-    return {"value": round(bytes_step * n_steps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_steps} full 14B-shaped decode steps (fused QKV + gate+up+SwiGLU), fp64 NumPy, "
-                      f"BLAS limited to 1 thread; {dt:.1f} s",
-            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+
+    def timed(threads):
+        ts = []
+        with threadpool_limits(limits=threads):
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                for _ in range(n_steps):
+                    orc.fused_qkv(x, w_qkv.codes, w_qkv.scales, w_qkv.biases, sh.q_out, sh.kv_out)
+                    orc.gate_up_swiglu(x, w_gu.codes, w_gu.scales, w_gu.biases, sh.I)
+                ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    t_all = timed(avail)
+    t_one = timed(1)
+    blas = [{"api": d.get("internal_api"), "num_threads": d.get("num_threads")} for d in threadpool_info()]
+    gbs_all = bytes_step * n_steps / t_all / 1e9
+    gbs_one = bytes_step * n_steps / t_one / 1e9
+    return {"value": round(gbs_all, 4), "unit": "GB/s", "cores": avail, "kind": "oracle",
+            "sample": f"{n_steps} full 14B-shaped decode steps (fused QKV + gate+up+SwiGLU) per run, fp64 NumPy, "
+                      f"median of {runs} runs; BLAS on {avail} threads: {t_all:.2f} s per run",
+            "one_thread": {"value": round(gbs_one, 4), "unit": "GB/s", "cores": 1,
+                           "seconds_per_run": round(t_one, 3)},
+            "seconds_per_run": round(t_all, 3),
+            "host": _cpu_model(), "host_cpus": os.cpu_count(), "affinity_cpus": avail, "blas": blas,
+            "env": {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+                    if k in os.environ}}
 
 
 if __name__ == "__main__":

@@ -1,4 +1,6 @@
-"""Build libqmm.so (the C-ABI library) for gfx950 with hipcc, in-tree.
+"""Build libqmm.so (the C-ABI library) for gfx950 with hipcc, in-tree, and
+libqmm_ceiling.so (the benchmark's measurement kernels: plain streaming read and
+register-only MFMA loop).
 
     python -m gemm_affine_u4_amd.build        # or __graft_entry__.build()
 """
@@ -15,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libqmm.so")
+CEILING_OUT = os.path.join(PKG, "libqmm_ceiling.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 # (source, extra flags, object): the GEMV and GEMM sources are built once per code width.
@@ -48,16 +51,24 @@ def _compile(entry) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+CEILING = ("ceiling.hip", [], "ceiling.o")
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES + [CEILING]))
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], CEILING_OUT)
     return OUT
 
 

@@ -482,9 +482,10 @@ bool bmv_supports(int epi, const GemvArgs& a, int64_t M) {
 // Above 32 rows the kernel runs one pass of 16 or 32 rows per grid row and reads the
 // weights once per pass; it is still taken where the prefill GEMM would leave most of the
 // GPU idle (a grid of few 256 x 256 tiles, each walking all of K).  Estimates from the
-// measured rates (14B / 24B shapes): a 16-row pass streams the weights at ~2.9 TB/s and
-// takes at least 8 us, a 32-row pass 1.45 times that; a GEMM round of up to 256 tiles
-// takes ~1.5 us per 64-input step.
+// rates measured on a 256-CU MI355X (14B / 24B shapes), scaled by the device's compute
+// units: a 16-row pass streams the weights at ~11.3 KB/us per CU (2.9 TB/s on 256 CUs) and
+// takes at least 8 us, a 32-row pass 1.45 times that; a GEMM round of one tile per CU takes
+// ~1.5 us per 64-input step.
 #ifndef QMM_BMV_FORCE
 #define QMM_BMV_FORCE 0
 #endif
@@ -493,21 +494,23 @@ bool bmv_preferred(int epi, const GemvArgs& a, int64_t M) {
   if (M <= 32 || QMM_BMV_FORCE) return true;
   const int mb = bmv::tiles_for(M, a.K / bmv::kKStep);
   const double wbytes = double(a.rows) * double(a.K) * (0.5 + 4.0 / 64.0);
-  const double pass_us = (wbytes / 2.9e6 > 8.0 ? wbytes / 2.9e6 : 8.0) * (mb == 2 ? 1.45 : 1.0);
+  const int64_t cus = device_cus();
+  const double bytes_per_us = 11328.0 * double(cus);
+  const double pass_us = (wbytes / bytes_per_us > 8.0 ? wbytes / bytes_per_us : 8.0) * (mb == 2 ? 1.45 : 1.0);
   const int64_t rows_per_pass = bmv::kRows * mb;
   const double bmv_us = double((M + rows_per_pass - 1) / rows_per_pass) * pass_us;
   const int64_t n_tiles = epi == EPI_SWIGLU  ? (a.I + 127) / 128
                           : epi == EPI_ROPE  ? ((a.rows >> 1) + 127) / 128
                                              : (a.rows + 255) / 256;
-  const int64_t rounds = ((M + 255) / 256 * n_tiles + 255) / 256;
+  const int64_t rounds = ((M + 255) / 256 * n_tiles + cus - 1) / cus;
   const double gemm_us = double(rounds) * double(a.K / 64) * 1.5;
   return bmv_us < gemm_us;
 }
 
 template <int G, int MB>
 static void launch_bmv_tiles(int epi, const GemvArgs& a, int64_t M, int64_t units, hipStream_t st) {
-  constexpr int64_t kCUs = 256;
-  const dim3 grid{unsigned(units < kCUs ? units : kCUs), unsigned((M + bmv::kRows * MB - 1) / (bmv::kRows * MB)), 1u};
+  const int64_t cus = device_cus();
+  const dim3 grid{unsigned(units < cus ? units : cus), unsigned((M + bmv::kRows * MB - 1) / (bmv::kRows * MB)), 1u};
   const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
   const BmvGather none = {};
   if (epi == EPI_LINEAR)

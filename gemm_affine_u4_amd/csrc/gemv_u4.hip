@@ -691,21 +691,20 @@ static int finish_launch() { return hipGetLastError() == hipSuccess ? 0 : 6; }
 // single-slice kernel and over the row groups of the K-split kernel.  The single-slice
 // kernel gets as many waves as the GPU holds at once for that instance (its register use
 // sets the occupancy; queried once per instance) but never more waves than units; the
-// K-split kernel about kTargetWaves waves.
-constexpr int64_t kTargetWaves = 256 * QMM_GEMV_WAVES_PER_CU;
-constexpr int64_t kCUs = 256;
+// K-split kernel about QMM_GEMV_WAVES_PER_CU waves per compute unit.
+static int64_t target_waves() { return int64_t(device_cus()) * QMM_GEMV_WAVES_PER_CU; }
 
 template <int L, int C, int EPI, bool MOE, int NR = 1>
 static int64_t s1_resident_waves() {
-  static const int64_t waves = [] {
-    int blocks_per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, gemv_u4_s1_kernel<L, C, EPI, MOE, NR>,
-                                                     64 * kWavesS1, NR * S1Layout<L, C>::lds_bytes()) != hipSuccess ||
-        blocks_per_cu < 1)
-      blocks_per_cu = QMM_S1_WAVES_PER_CU / kWavesS1;
-    return kCUs * kWavesS1 * int64_t(blocks_per_cu);
+  static const int64_t blocks_per_cu = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, gemv_u4_s1_kernel<L, C, EPI, MOE, NR>, 64 * kWavesS1,
+                                                     NR * S1Layout<L, C>::lds_bytes()) != hipSuccess ||
+        b < 1)
+      b = QMM_S1_WAVES_PER_CU / kWavesS1;
+    return int64_t(b);
   }();
-  return waves;
+  return int64_t(device_cus()) * kWavesS1 * blocks_per_cu;
 }
 
 // waves of a single-slice launch per batch entry (a multiple of the block's waves)
@@ -721,7 +720,7 @@ static void gemv_geometry(const GemvShape& sh, int epi, const GemvArgs& a, int64
   const int64_t pairs = epi == EPI_SWIGLU ? a.I : (a.rows >> 1);
   *units = (epi == EPI_SWIGLU || epi == EPI_ROPE) ? (pairs + rpi / 2 - 1) / (rpi / 2) : (a.rows + rpi - 1) / rpi;
   // K-split kernel (the single-slice cases compute their own grid)
-  const int64_t want = (kTargetWaves / sh.ksplit + batch - 1) / batch;
+  const int64_t want = (target_waves() / sh.ksplit + batch - 1) / batch;
   const int64_t g = want < *units ? want : *units;
   *n = int(g);
   *blocks = g;

@@ -3,11 +3,31 @@
 // MFMA GEMM; see include/qmm.h).  Nothing here allocates, synchronises or keeps state.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+
 #include "qmm.h"
 #include "qmm_internal.h"
 #include "qmm_validate.h"
 
 using qmm::Range;
+
+namespace qmm {
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (dev >= 0) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+}  // namespace qmm
 
 static_assert(QMM_MAX_EXPERTS_PREFILL == qmm::kMaxExpertsPrefill, "routing histogram size");
 static_assert(QMM_FP8_E4M3 == qmm::kFmtFp8E4M3, "fp8 format code");

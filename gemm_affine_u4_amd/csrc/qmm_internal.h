@@ -22,6 +22,10 @@ constexpr int kFmtFp8E4M3 = 0x108;
 
 enum Epilogue : int { EPI_LINEAR = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_ROPE = 3 };
 
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount), queried once
+// per device; 256 if the query fails.  The launch geometries are sized from it.
+int device_cus();
+
 // Fused QKV with rotary embedding (EPI_ROPE).  The weight is heads of head_dim rows: per
 // query head its query rows and, with q_gate, its output-gate rows; then the K heads,
 // then the V heads.  Outputs: q -> out0, k -> out1, v -> out2 ([M][heads][head_dim]),
