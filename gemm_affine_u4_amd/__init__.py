@@ -15,7 +15,8 @@ import os
 __all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm_fused_gate_up_swiglu",
            "qmm_moe_gather", "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
            "qmm_moe_gather_fmt",
-           "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
+           "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_moe_prefill_noalloc",
+           "QMM_NOALLOC_SCRATCH_BYTES", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
            "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_FP8_E4M3", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
 QMM_OUT_BF16, QMM_OUT_F32 = 0, 1
 QMM_MOE_GATE_UP_SWIGLU, QMM_MOE_DOWN_COMBINE = 0, 1
 QMM_FP8_E4M3 = 0x108   # `bits` of the *_fmt calls for fp8 e4m3 codes
+QMM_NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's scratch array of qmm_moe_prefill_noalloc
 STATUS = {"QMM_OK": 0, "QMM_ERR_NULL": 1, "QMM_ERR_SHAPE": 2, "QMM_ERR_ALIGN": 3, "QMM_ERR_ALIAS": 4,
           "QMM_ERR_ENUM": 5, "QMM_ERR_LAUNCH": 6}
 
@@ -42,6 +44,7 @@ _SIGNATURES = {
     "qmm_moe_route": [_P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "qmm_moe_prefill": [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_size_t, _P,
                         _INT, _P],
+    "qmm_moe_prefill_noalloc": [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
     "qmm_linear_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P],
     "qmm_fused_qkv_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _INT, _P],
     "qmm_fused_gate_up_swiglu_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _P, _INT, _P],
@@ -273,6 +276,28 @@ def qmm_moe_prefill(stage, inp, codes, scales, biases, expert_ids, workspace, ou
                                           _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"), topk,
                                           _ptr(workspace, "workspace"), _bytes(workspace), _ptr(out, "out"),
                                           _out_dtype(out), _stream(stream)), "qmm_moe_prefill")
+
+
+def qmm_moe_prefill_noalloc(stage, inp, codes, scales, biases, expert_ids, out, expert_w=None, stream=None) -> None:
+    """qmm_moe_prefill without a workspace (the library's own scratch array; no
+    qmm_moe_route call first): for callers that cannot allocate.  Same arguments otherwise."""
+    E, rows = codes.shape[0], codes.shape[1]
+    K = inp.shape[-1]
+    _need(expert_ids.dim() == 2 and expert_ids.element_size() == 4, "expert_ids must be int32 [M, topk]")
+    M, topk = expert_ids.shape
+    _check_weight(codes, scales, biases, E * rows, K, "expert grid")
+    if int(stage) == QMM_MOE_GATE_UP_SWIGLU:
+        _need(_bytes(inp) == M * K * 2, "x must be bf16 [M, K]")
+        _need(_elems(out) == M * topk * (rows // 2), "out must be [M, topk, rows/2]")
+    else:
+        _need(_bytes(inp) == M * topk * K * 2, "h must be bf16 [M, topk, K]")
+        _need(_elems(out) == M * rows, "out must be [M, rows]")
+        _need(expert_w is not None and _bytes(expert_w) == M * topk * 4, "expert_w must be fp32 [M, topk]")
+    _check(load_library().qmm_moe_prefill_noalloc(int(stage), _ptr(inp, "in"), M, K, _ptr(codes, "codes"),
+                                                  _ptr(scales, "scales"), _ptr(biases, "biases"), E, rows,
+                                                  _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"), topk,
+                                                  _ptr(out, "out"), _out_dtype(out), _stream(stream)),
+           "qmm_moe_prefill_noalloc")
 
 
 # ---- other formats of the affine family (code width `bits`, group size `group`) ----------

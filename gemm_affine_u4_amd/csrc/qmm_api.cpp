@@ -407,15 +407,32 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
                     const uint16_t* scales, const uint16_t* biases, int64_t E, int64_t rows,
                     const int32_t* expert_ids, const float* expert_w, int64_t topk, void* workspace,
                     size_t workspace_bytes, void* out, int out_dtype, hipStream_t stream) {
+  return qmm::moe_prefill_entry(stage, in, M, K, codes, scales, biases, E, rows, expert_ids, expert_w, topk,
+                                workspace, workspace_bytes, nullptr, out, out_dtype, stream);
+}
+
+}  // extern "C"
+
+namespace qmm {
+
+int moe_prefill_entry(int stage, const uint16_t* in, int64_t M, int64_t K, const uint32_t* codes,
+                      const uint16_t* scales, const uint16_t* biases, int64_t E, int64_t rows,
+                      const int32_t* expert_ids, const float* expert_w, int64_t topk, void* workspace,
+                      size_t workspace_bytes, void* (*scratch)(size_t), void* out, int out_dtype,
+                      hipStream_t stream) {
+  const bool route_first = scratch != nullptr;
   if (stage != QMM_MOE_GATE_UP_SWIGLU && stage != QMM_MOE_DOWN_COMBINE) return QMM_ERR_ENUM;
   if (int st = check_weight(in, codes, scales, biases)) return st;
-  if (!expert_ids || !workspace || !out || (stage == QMM_MOE_DOWN_COMBINE && !expert_w)) return QMM_ERR_NULL;
+  if (!expert_ids || (!workspace && !route_first) || !out || (stage == QMM_MOE_DOWN_COMBINE && !expert_w))
+    return QMM_ERR_NULL;
   if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
   const bool s1 = stage == QMM_MOE_GATE_UP_SWIGLU;
   const size_t need = qmm_moe_prefill_workspace_bytes(M, topk, E, s1 ? 0 : rows);
   if (need == 0 || !qmm::k_ok(K) || rows < 1 || !codes_fit(rows, K, kU4G64) || (s1 && rows % 2) ||
       !acts_fit(s1 ? M : M * topk, K) || workspace_bytes < need)
     return QMM_ERR_SHAPE;
+  // the library's scratch is located only once the sizes are known to fit it
+  if (route_first && !(workspace = scratch(need))) return QMM_ERR_LAUNCH;
   const size_t e = out_elem(out_dtype);
   if (!qmm::aligned(out, e) || !qmm::aligned(expert_ids, 4) || (expert_w && !qmm::aligned(expert_w, 4)) ||
       !qmm::aligned(workspace, 256))
@@ -462,8 +479,8 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
     return qmm::launch_moe_down(g, stream);
   }
   // a small batch whose stage 2 the pair-by-pair kernels cannot take (K > 5120): route it
-  // here, since qmm_moe_route did not
-  if (P <= kMoePairsByGemv)
+  // here, since qmm_moe_route did not; likewise every call that routes for itself
+  if (P <= kMoePairsByGemv || route_first)
     if (int st = qmm::launch_moe_route(expert_ids, M, topk, E, workspace, stream)) return st;
 
   qmm::GemmArgs a = {};
@@ -482,4 +499,4 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const u
   return qmm::launch_moe_prefill(s1 ? 0 : 1, a, expert_ids, M, topk, E, workspace, out, stream);
 }
 
-}  // extern "C"
+}  // namespace qmm

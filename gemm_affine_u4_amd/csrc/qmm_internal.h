@@ -1,6 +1,7 @@
 // Host-side launch interface between the C ABI (qmm_api.cpp) and the kernels.
 #pragma once
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace qmm {
@@ -187,6 +188,17 @@ int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, voi
 // (g.N = expert rows, out = y [M][N]).  g carries x/h, weights, K, N, I, f32_out.
 int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t M, int64_t topk, int64_t E,
                        const void* ws, void* out, hipStream_t s);
+
+// qmm_moe_prefill with its checks.  scratch == null: `workspace` is the caller's buffer of
+// workspace_bytes, routed by an earlier qmm_moe_route.  scratch != null: workspace is
+// ignored; once the sizes are validated against workspace_bytes (the scratch's size),
+// scratch(bytes needed) locates the library's own buffer (null: QMM_ERR_LAUNCH), and the
+// call buckets expert_ids into it itself before the stage.
+int moe_prefill_entry(int stage, const uint16_t* in, int64_t M, int64_t K, const uint32_t* codes,
+                      const uint16_t* scales, const uint16_t* biases, int64_t E, int64_t rows,
+                      const int32_t* expert_ids, const float* expert_w, int64_t topk, void* workspace,
+                      size_t workspace_bytes, void* (*scratch)(size_t), void* out, int out_dtype,
+                      hipStream_t stream);
 
 
 }  // namespace qmm

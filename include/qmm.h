@@ -22,7 +22,8 @@
  * Conventions shared by every entry point.
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
  *     allocates nothing, keeps no pointer after returning, holds no mutable global
- *     state and never copies, concatenates or repacks a weight: a fused weight is
+ *     state (one exception: the scratch array of qmm_moe_prefill_noalloc, below) and
+ *     never copies, concatenates or repacks a weight: a fused weight is
  *     built once by the caller, and the unfused copies can then be dropped
  *     ("2026-05-15: Four Candles for the Cathedral", "#1 -- Drop the fallback
  *     weights").
@@ -79,6 +80,8 @@ extern "C" {
 #define QMM_MAX_K 65536
 #define QMM_MAX_TOPK 64
 #define QMM_MAX_EXPERTS_PREFILL 4096
+/* size of the library's own device scratch array used by qmm_moe_prefill_noalloc */
+#define QMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 /* `bits` of the *_fmt calls for fp8 e4m3 codes (8 bits each) */
 #define QMM_FP8_E4M3 0x108
 
@@ -260,6 +263,29 @@ int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K,
                     int64_t E, int64_t rows, const int32_t* expert_ids, const float* expert_w,
                     int64_t topk, void* workspace, size_t workspace_bytes, void* out, int out_dtype,
                     hipStream_t stream);
+
+/*
+ * qmm_moe_prefill_noalloc -- qmm_moe_prefill for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same stage, arguments (without the workspace), kernels and results as
+ * qmm_moe_prefill, bit for bit; instead of a caller workspace it uses the library's own
+ * file-scope device array of QMM_NOALLOC_SCRATCH_BYTES on the current device (allocated
+ * with the library's code on that device and held until the process ends; its device
+ * address is looked up on the first call on each device), and each call buckets expert_ids
+ * into it itself, so no qmm_moe_route call precedes it.  The call allocates nothing.
+ *   Limit: qmm_moe_prefill_workspace_bytes(M, topk, E, stage 1 ? 0 : rows) must not
+ *   exceed QMM_NOALLOC_SCRATCH_BYTES (64 MiB: stage 1 of any batch up to 65535 tokens;
+ *   stage 2 while pairs * rows * 4 bytes of products fit, e.g. ~4000 (token, slot) pairs
+ *   at 2048 output rows); larger sizes return QMM_ERR_SHAPE before anything is enqueued.
+ *   Every call on a GPU shares that GPU's one array and leaves its contents behind: two
+ *   calls that may run at the same time on one GPU (different streams, or different host
+ *   threads without ordering) race on it and give undefined results.  Calls ordered on
+ *   one stream are safe.  QMM_ERR_LAUNCH if the array cannot be located on the device.
+ */
+int qmm_moe_prefill_noalloc(int stage, const uint16_t* in, int64_t M, int64_t K,
+                            const uint32_t* codes, const uint16_t* scales, const uint16_t* biases,
+                            int64_t E, int64_t rows, const int32_t* expert_ids, const float* expert_w,
+                            int64_t topk, void* out, int out_dtype, hipStream_t stream);
 
 /*
  * Other formats of the affine family (saragossa README, "Capabilities": u4/u6/u8 at group

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
                                            "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
                                            "qmm_moe_gather_fmt",
                                            "qmm_moe_gather", "qmm_moe_prefill_workspace_bytes",
-                                           "qmm_moe_route", "qmm_moe_prefill", "qmm_status_str",
+                                           "qmm_moe_route", "qmm_moe_prefill", "qmm_moe_prefill_noalloc",
+                                           "qmm_status_str",
                                            "qmm_abi_version"])
 
 
@@ -71,6 +72,23 @@ def test_null_pointers():
     # stage 2 needs combine weights
     assert lib.qmm_moe_gather(1, A, 512, A + 65536, A + 2 ** 18, A + 2 ** 19, 4, 64, A + 2 ** 22, None, 2,
                               A + 2 ** 21, 0, None) == S["QMM_ERR_NULL"]
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_call():
+    """qmm_moe_prefill_noalloc checks the workspace the call would need against its scratch
+    size (QMM_NOALLOC_SCRATCH_BYTES) before it looks the scratch up or enqueues anything:
+    stage 2 of 2048 tokens x top-8 into 2048 output rows needs 134 MB of products."""
+    lib = qmm.load_library()
+    need = lib.qmm_moe_prefill_workspace_bytes(2048, 8, 256, 2048)
+    assert need > qmm.QMM_NOALLOC_SCRATCH_BYTES
+    st = lib.qmm_moe_prefill_noalloc(1, A, 2048, 512, A + 2 ** 24, A + 2 ** 26, A + 2 ** 27, 256, 2048,
+                                     A + 2 ** 28, A + 2 ** 29, 8, A + 2 ** 30, 1, None)
+    assert st == S["QMM_ERR_SHAPE"]
+    # bad stage and NULL pointers are reported as for qmm_moe_prefill
+    assert lib.qmm_moe_prefill_noalloc(2, A, 4, 512, A + 2 ** 24, A + 2 ** 26, A + 2 ** 27, 8, 64,
+                                       A + 2 ** 28, A + 2 ** 29, 2, A + 2 ** 30, 1, None) == S["QMM_ERR_ENUM"]
+    assert lib.qmm_moe_prefill_noalloc(1, A, 4, 512, A + 2 ** 24, A + 2 ** 26, A + 2 ** 27, 8, 64,
+                                       A + 2 ** 28, None, 2, A + 2 ** 30, 1, None) == S["QMM_ERR_NULL"]
 
 
 @pytest.mark.parametrize("K", [0, 32, 100, 96, 65536 + 64, -64])
