@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -56,8 +57,9 @@ def _args():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["gemm_affine_u4_amd/csrc/gemv_u4.hip", "gemm_affine_u4_amd/csrc/qmm_device.h"]
-COUNTERS_SUMMARY = "profiles/gemv_u4_decode_14B_hbm_counters.md"
+KERNEL_SOURCES = ["gemm_affine_u4_amd/csrc/gemv_step.hip", "gemm_affine_u4_amd/csrc/qmm_step.h",
+                  "gemm_affine_u4_amd/csrc/qmm_device.h"]
+COUNTERS_SUMMARY = "profiles/gemv_step_decode_14B_hbm_counters.md"
 
 
 def counted_traffic(key: str):
@@ -163,7 +165,24 @@ def main():
     stream = torch.cuda.Stream()
     T = Timer(torch, stream)
 
+    # the step: fused QKV and fused gate+up+SwiGLU of one token in one launch (a planned
+    # decode step); step i reads layer i % P of the pool and activation row i % NX, so one
+    # plan per (layer, row) pair that occurs
+    NP = P * NX // math.gcd(P, NX)
+    plans = []
+    for j in range(NP):
+        L, x = j % P, xs[j % NX]
+        pr = [qmm.step_fused_qkv(x, pq[0][L], pq[1][L], pq[2][L], q, k, v),
+              qmm.step_gate_up_swiglu(x, pg[0][L], pg[1][L], pg[2][L], h)]
+        mem = torch.empty(qmm.qmm_step_plan_bytes(pr), dtype=torch.uint8, device=dev)
+        qmm.qmm_step_plan(pr, mem, stream=stream)
+        plans.append((pr, mem))
+
     def step(i):
+        pr, mem = plans[i % NP]
+        qmm.qmm_step_run(pr, mem, stream=stream)
+
+    def per_call_step(i):
         L = i % P
         x = xs[i % NX]
         qmm.qmm_fused_qkv(x, pq[0][L], pq[1][L], pq[2][L], q, k, v, stream=stream)
@@ -190,8 +209,10 @@ def main():
     del g_step
     ms_per_step = ms_total / args.steps
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    # one launch per step: the step kernel's average launch duration is the step time
 
-    # per-kernel average duration of the dominant kernel (gate+up GEMV), same stream
+    # the same work as two per-call launches, and each of them alone
+    ms_pc = T.per_call_ms(per_call_step, args.kernel_reps)
     ms_gu = T.per_call_ms(gate_up_only, args.kernel_reps)
     ms_qkv = T.per_call_ms(qkv_only, args.kernel_reps)
     ach_gu = bytes_gu / (ms_gu * 1e-3) / 1e9
@@ -214,15 +235,21 @@ def main():
         "dtype": "u4 weights, bf16 activations, fp32 accumulate",
         "data": "synthetic (seeded: codes uniform 0..15, scales U[0.001,0.01] bf16, bias=-8*scale, x~N(0,1) bf16)",
         "config": {"workload": "14B-shaped decode M=1: fused QKV [7168 x 5120] + fused gate+up+SwiGLU "
-                               "[27648 x 5120], u4 g64, 48-layer rotating pool",
+                               "[27648 x 5120], u4 g64, 48-layer rotating pool, one planned launch per step",
                    "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
                    "bytes_per_step": bytes_step, "pool_layers": P},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "gemv_u4_s1_kernel (fused gate+up+SwiGLU, K=5120)",
-                     "achieved": round(ach_gu, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach_gu / HBM_PEAK_GBS, 4), "traffic": counted_traffic("gate_up"),
-                     "bytes_per_launch": bytes_gu, "avg_launch_us": ms_gu * 1e3},
-        "kernels": {"fused_qkv_gemv": {"avg_launch_us": ms_qkv * 1e3, "GB/s": round(ach_qkv, 1),
+        "roofline": {"bound": "hbm",
+                     "kernel": "gemv_step_single_inline_kernel<true> (the whole step in one launch: fused QKV "
+                               "+ fused gate+up+SwiGLU, K=5120)",
+                     "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counted_traffic("step"),
+                     "bytes_per_launch": bytes_step, "avg_launch_us": ms_per_step * 1e3},
+        "kernels": {"one_launch_step": {"avg_launch_us": ms_per_step * 1e3, "GB/s": round(value, 1),
+                                        "bytes_per_launch": bytes_step},
+                    "per_call_step": {"us_per_step": ms_pc * 1e3, "launches": 2,
+                                      "GB/s": round(bytes_step / (ms_pc * 1e-3) / 1e9, 1)},
+                    "fused_qkv_gemv": {"avg_launch_us": ms_qkv * 1e3, "GB/s": round(ach_qkv, 1),
                                        "bytes_per_launch": bytes_qkv},
                     "fused_gate_up_gemv": {"avg_launch_us": ms_gu * 1e3, "GB/s": round(ach_gu, 1),
                                            "bytes_per_launch": bytes_gu}},
@@ -519,7 +546,9 @@ def bench_formats(torch, qmm, synth, T, dev, reps):
 
 def bench_step_24b(torch, qmm, synth, T, dev, n_steps):
     """24B-dense-shaped decode step: 40 layers of fused QKV + fused gate+up+SwiGLU + down,
-    each step with fresh x; a layer's down reads that layer's h."""
+    each step with fresh x; a layer's down reads that layer's h.  Run as a planned step
+    (two launches: every QKV and gate+up, then every down) and, for comparison, as one
+    launch per projection."""
     sh = synth.DENSE_24B
     K, I = sh.K, sh.I
     L = 40
@@ -529,45 +558,71 @@ def bench_step_24b(torch, qmm, synth, T, dev, n_steps):
     pq, pg, pd = pool_of(torch, dev, w_qkv, L), pool_of(torch, dev, w_gu, L), pool_of(torch, dev, w_dn, L)
     del w_qkv, w_gu, w_dn
     xs = up(torch, dev, np.concatenate([synth.gen_x(synth.CFG_24B, 0, s, 1, K) for s in range(n_steps)]))
-    q = torch.empty((1, sh.q_out), dtype=torch.bfloat16, device=dev)
-    k = torch.empty((1, sh.kv_out), dtype=torch.bfloat16, device=dev)
-    v = torch.empty((1, sh.kv_out), dtype=torch.bfloat16, device=dev)
-    h = torch.empty((1, I), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((1, K), dtype=torch.bfloat16, device=dev)
+    # per-layer outputs: a planned step's outputs may not overlap, and a layer's down reads
+    # that layer's h
+    qs = torch.empty((L, sh.q_out), dtype=torch.bfloat16, device=dev)
+    ks = torch.empty((L, sh.kv_out), dtype=torch.bfloat16, device=dev)
+    vs = torch.empty((L, sh.kv_out), dtype=torch.bfloat16, device=dev)
+    hs = torch.empty((L, I), dtype=torch.bfloat16, device=dev)
+    ys = torch.empty((L, K), dtype=torch.bfloat16, device=dev)
     st = T.stream
 
-    def one_step(s):
-        x = xs[s % n_steps]
+    # the planned step: level 0 = every layer's QKV and gate+up (they read x), level 1 =
+    # every layer's down (it waits for its layer's gate+up): two launches per step
+    plans = []
+    for s_ in range(n_steps):
+        x = xs[s_]
+        pr = []
         for l in range(L):
-            qmm.qmm_fused_qkv(x, pq[0][l], pq[1][l], pq[2][l], q, k, v, stream=st)
-            qmm.qmm_fused_gate_up_swiglu(x, pg[0][l], pg[1][l], pg[2][l], h, stream=st)
-            qmm.qmm_linear(h, pd[0][l], pd[1][l], pd[2][l], y, stream=st)
+            pr.append(qmm.step_fused_qkv(x, pq[0][l], pq[1][l], pq[2][l], qs[l], ks[l], vs[l]))
+            pr.append(qmm.step_gate_up_swiglu(x, pg[0][l], pg[1][l], pg[2][l], hs[l]))
+            pr.append(qmm.step_linear(hs[l], pd[0][l], pd[1][l], pd[2][l], ys[l], wait_for=len(pr) - 1))
+        mem = torch.empty(qmm.qmm_step_plan_bytes(pr), dtype=torch.uint8, device=dev)
+        qmm.qmm_step_plan(pr, mem, stream=st)
+        plans.append((pr, mem))
+
+    def one_step(s_):
+        pr, mem = plans[s_ % n_steps]
+        qmm.qmm_step_run(pr, mem, stream=st)
+
+    def per_call_step(s_):
+        x = xs[s_ % n_steps]
+        for l in range(L):
+            qmm.qmm_fused_qkv(x, pq[0][l], pq[1][l], pq[2][l], qs[l], ks[l], vs[l], stream=st)
+            qmm.qmm_fused_gate_up_swiglu(x, pg[0][l], pg[1][l], pg[2][l], hs[l], stream=st)
+            qmm.qmm_linear(hs[l], pd[0][l], pd[1][l], pd[2][l], ys[l], stream=st)
 
     g = T.capture(one_step, n_steps)
     T.replay_ms(g)
     ms = T.replay_ms(g) / n_steps
+    del g
+    g = T.capture(per_call_step, n_steps)
+    T.replay_ms(g)
+    ms_pc = T.replay_ms(g) / n_steps
     del g
     b_qkv = weight_bytes(sh.qkv_rows, K) + K * 2 + sh.qkv_rows * 2
     b_gu = weight_bytes(2 * I, K) + K * 2 + I * 2
     b_dn = weight_bytes(K, I) + I * 2 + K * 2
     b_step = L * (b_qkv + b_gu + b_dn)
     gbs = b_step / (ms * 1e-3) / 1e9
-    # each projection on its own (a graph of one kind of call over the 40 layers): the
-    # whole-step graph is compared with the sum of these
+    # each projection on its own (a graph of one kind of call over the 40 layers)
     x0 = xs[0]
-    ms_q = T.per_call_ms(lambda i: qmm.qmm_fused_qkv(x0, pq[0][i % L], pq[1][i % L], pq[2][i % L], q, k, v,
-                                                     stream=st), 4 * L)
-    ms_g = T.per_call_ms(lambda i: qmm.qmm_fused_gate_up_swiglu(x0, pg[0][i % L], pg[1][i % L], pg[2][i % L], h,
-                                                                stream=st), 4 * L)
-    ms_d = T.per_call_ms(lambda i: qmm.qmm_linear(h, pd[0][i % L], pd[1][i % L], pd[2][i % L], y, stream=st), 4 * L)
+    ms_q = T.per_call_ms(lambda i: qmm.qmm_fused_qkv(x0, pq[0][i % L], pq[1][i % L], pq[2][i % L], qs[0], ks[0],
+                                                     vs[0], stream=st), 4 * L)
+    ms_g = T.per_call_ms(lambda i: qmm.qmm_fused_gate_up_swiglu(x0, pg[0][i % L], pg[1][i % L], pg[2][i % L],
+                                                                hs[0], stream=st), 4 * L)
+    ms_d = T.per_call_ms(lambda i: qmm.qmm_linear(hs[0], pd[0][i % L], pd[1][i % L], pd[2][i % L], ys[0],
+                                                  stream=st), 4 * L)
     kern = {name: {"avg_launch_us": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1)}
             for name, t, b in (("fused_qkv", ms_q, b_qkv), ("fused_gate_up", ms_g, b_gu), ("down", ms_d, b_dn))}
     return {"workload": f"24B-dense decode step M=1: {L} layers x (QKV [{sh.qkv_rows}x{K}] + gate+up "
                         f"[{2 * I}x{K}] + down [{K}x{I}]), fresh x per step, {n_steps} steps in one graph",
             "ms_per_step": round(ms, 4), "bytes_per_step": b_step, "GB/s": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_step": 3 * L,
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_step": 2,
+            "per_call": {"ms_per_step": round(ms_pc, 4), "launches_per_step": 3 * L,
+                         "GB/s": round(b_step / (ms_pc * 1e-3) / 1e9, 1)},
             "kernels": kern,
-            "step_over_kernel_sum": round(ms / (L * (ms_q + ms_g + ms_d)), 4)}
+            "per_call_step_over_kernel_sum": round(ms_pc / (L * (ms_q + ms_g + ms_d)), 4)}
 
 
 def bench_moe(torch, qmm, synth, T, dev, n_steps):

@@ -16,7 +16,9 @@ __all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm
            "qmm_moe_gather", "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
            "qmm_moe_gather_fmt",
            "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_moe_prefill_noalloc",
-           "QMM_NOALLOC_SCRATCH_BYTES", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
+           "QMM_NOALLOC_SCRATCH_BYTES", "StepProj", "step_linear", "step_fused_qkv", "step_gate_up_swiglu",
+           "qmm_step_plan_bytes", "qmm_step_plan", "qmm_step_run",
+           "QMM_STEP_LINEAR", "QMM_STEP_QKV", "QMM_STEP_GATE_UP_SWIGLU", "qmm_status_str", "qmm_abi_version", "load_library", "LIB_PATH",
            "QMM_OUT_BF16", "QMM_OUT_F32", "QMM_FP8_E4M3", "QMM_MOE_GATE_UP_SWIGLU", "QMM_MOE_DOWN_COMBINE", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmm.so")
@@ -25,11 +27,22 @@ QMM_OUT_BF16, QMM_OUT_F32 = 0, 1
 QMM_MOE_GATE_UP_SWIGLU, QMM_MOE_DOWN_COMBINE = 0, 1
 QMM_FP8_E4M3 = 0x108   # `bits` of the *_fmt calls for fp8 e4m3 codes
 QMM_NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's scratch array of qmm_moe_prefill_noalloc
+QMM_STEP_LINEAR, QMM_STEP_QKV, QMM_STEP_GATE_UP_SWIGLU = 0, 1, 2
 STATUS = {"QMM_OK": 0, "QMM_ERR_NULL": 1, "QMM_ERR_SHAPE": 2, "QMM_ERR_ALIGN": 3, "QMM_ERR_ALIAS": 4,
           "QMM_ERR_ENUM": 5, "QMM_ERR_LAUNCH": 6}
 
 _LIB = None
 _P = ctypes.c_void_p
+
+
+class StepProj(ctypes.Structure):
+    """qmm_step_proj of the C ABI (one projection of a decode step)."""
+    _fields_ = [("kind", ctypes.c_int32), ("wait_for", ctypes.c_int32), ("K", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("q_out", ctypes.c_int64), ("kv_out", ctypes.c_int64),
+                ("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("lin_bias", ctypes.c_void_p), ("out0", ctypes.c_void_p),
+                ("out1", ctypes.c_void_p), ("out2", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 
@@ -49,6 +62,9 @@ _SIGNATURES = {
     "qmm_fused_qkv_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _INT, _P],
     "qmm_fused_gate_up_swiglu_fmt": [_INT, _I64, _P, _I64, _I64, _P, _P, _P, _I64, _P, _INT, _P],
     "qmm_moe_gather_fmt": [_INT, _I64, _INT, _P, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
+    "qmm_step_plan_bytes": [_P, ctypes.c_int32],
+    "qmm_step_plan": [_P, ctypes.c_int32, _P, ctypes.c_size_t, _P],
+    "qmm_step_run": [_P, ctypes.c_int32, _P, _P],
     "qmm_status_str": [_INT],
     "qmm_abi_version": [],
 }
@@ -71,7 +87,8 @@ def load_library():
             f = getattr(lib, name)
             f.argtypes = args
             f.restype = {"qmm_status_str": ctypes.c_char_p,
-                         "qmm_moe_prefill_workspace_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
+                         "qmm_moe_prefill_workspace_bytes": ctypes.c_size_t,
+                         "qmm_step_plan_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
         _LIB = lib
     return _LIB
 
@@ -298,6 +315,71 @@ def qmm_moe_prefill_noalloc(stage, inp, codes, scales, biases, expert_ids, out, 
                                                   _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"), topk,
                                                   _ptr(out, "out"), _out_dtype(out), _stream(stream)),
            "qmm_moe_prefill_noalloc")
+
+
+# ---- a decode step in one launch --------------------------------------------------------
+
+def step_linear(x, codes, scales, biases, y, lin_bias=None, wait_for: int = -1) -> StepProj:
+    """A projection y [N] = W x (+ lin_bias) of a decode step (x [K] bf16)."""
+    K = x.numel()
+    N = codes.shape[0]
+    _check_weight(codes, scales, biases, N, K)
+    _need(_bytes(x) == K * 2 and _elems(y) == N, "x must be bf16 [K], y [N]")
+    _need(lin_bias is None or _bytes(lin_bias) == N * 2, "lin_bias must be bf16 [N]")
+    return StepProj(QMM_STEP_LINEAR, wait_for, K, N, 0, 0, _ptr(x, "x"), _ptr(codes, "codes"),
+                    _ptr(scales, "scales"), _ptr(biases, "biases"), _ptr(lin_bias, "lin_bias"), _ptr(y, "y"),
+                    None, None, _out_dtype(y), 0)
+
+
+def step_fused_qkv(x, codes, scales, biases, q, k, v, lin_bias=None, wait_for: int = -1) -> StepProj:
+    """A fused QKV projection of a decode step: q [q_out], k and v [kv_out]."""
+    K = x.numel()
+    q_out, kv_out = q.numel(), k.numel()
+    rows = q_out + 2 * kv_out
+    _check_weight(codes, scales, biases, rows, K)
+    _need(_bytes(x) == K * 2 and v.numel() == kv_out, "x must be bf16 [K], v as k")
+    _need(lin_bias is None or _bytes(lin_bias) == rows * 2, "lin_bias must be bf16 [rows]")
+    _need(_out_dtype(q) == _out_dtype(k) == _out_dtype(v), "q, k, v must share a dtype")
+    return StepProj(QMM_STEP_QKV, wait_for, K, rows, q_out, kv_out, _ptr(x, "x"), _ptr(codes, "codes"),
+                    _ptr(scales, "scales"), _ptr(biases, "biases"), _ptr(lin_bias, "lin_bias"), _ptr(q, "q"),
+                    _ptr(k, "k"), _ptr(v, "v"), _out_dtype(q), 0)
+
+
+def step_gate_up_swiglu(x, codes, scales, biases, h, wait_for: int = -1) -> StepProj:
+    """A fused gate+up+SwiGLU projection of a decode step: h [I] over 2I weight rows."""
+    K = x.numel()
+    I = h.numel()
+    _check_weight(codes, scales, biases, 2 * I, K)
+    _need(_bytes(x) == K * 2, "x must be bf16 [K]")
+    return StepProj(QMM_STEP_GATE_UP_SWIGLU, wait_for, K, 2 * I, 0, 0, _ptr(x, "x"), _ptr(codes, "codes"),
+                    _ptr(scales, "scales"), _ptr(biases, "biases"), None, _ptr(h, "h"), None, None,
+                    _out_dtype(h), 0)
+
+
+def _step_array(projs):
+    arr = (StepProj * len(projs))(*projs)
+    return arr, len(projs)
+
+
+def qmm_step_plan_bytes(projs) -> int:
+    arr, n = _step_array(projs)
+    return int(load_library().qmm_step_plan_bytes(ctypes.cast(arr, ctypes.c_void_p), n))
+
+
+def qmm_step_plan(projs, plan, stream=None) -> None:
+    """Write the plan of `projs` (StepProj list) into `plan` (a device uint8 tensor of at
+    least qmm_step_plan_bytes(projs) bytes); synchronises the stream."""
+    arr, n = _step_array(projs)
+    _check(load_library().qmm_step_plan(ctypes.cast(arr, ctypes.c_void_p), n, _ptr(plan, "plan"), _bytes(plan),
+                                        _stream(stream)), "qmm_step_plan")
+
+
+def qmm_step_run(projs, plan, stream=None) -> None:
+    """One run of a planned decode step (projs exactly as given to qmm_step_plan): one
+    launch per dependency level and kind."""
+    arr, n = _step_array(projs)
+    _check(load_library().qmm_step_run(ctypes.cast(arr, ctypes.c_void_p), n, _ptr(plan, "plan"), _stream(stream)),
+           "qmm_step_run")
 
 
 # ---- other formats of the affine family (code width `bits`, group size `group`) ----------

@@ -403,6 +403,129 @@ int qmm_moe_route(const int32_t* expert_ids, int64_t M, int64_t topk, int64_t E,
   return qmm::launch_moe_route(expert_ids, M, topk, E, workspace, stream);
 }
 
+// ---- decode step in one launch -----------------------------------------------------------
+
+namespace {
+
+constexpr int32_t kMaxStepProjections = 4096;
+
+// Per-projection checks of qmm_step_plan, in the order of the per-call entry points.
+int check_step_proj(const qmm_step_proj& p, int32_t index) {
+  if (p.kind != QMM_STEP_LINEAR && p.kind != QMM_STEP_QKV && p.kind != QMM_STEP_GATE_UP_SWIGLU) return QMM_ERR_ENUM;
+  if (int st = check_weight(p.x, p.codes, p.scales, p.biases)) return st;
+  if (!p.out0 || (p.kind == QMM_STEP_QKV && (!p.out1 || !p.out2))) return QMM_ERR_NULL;
+  if (!out_dtype_ok(p.out_dtype)) return QMM_ERR_ENUM;
+  if (p.reserved != 0 || p.wait_for < -1 || p.wait_for >= index || !qmm::k_ok(p.K) || p.K <= 512 ||
+      p.rows < 1 || p.rows > (int64_t(1) << 30) || !codes_fit(p.rows, p.K, kU4G64))
+    return QMM_ERR_SHAPE;
+  if (p.kind == QMM_STEP_QKV && (p.q_out < 1 || p.kv_out < 1 || p.q_out + 2 * p.kv_out != p.rows))
+    return QMM_ERR_SHAPE;
+  if (p.kind == QMM_STEP_GATE_UP_SWIGLU && (p.rows % 2 || p.lin_bias)) return QMM_ERR_SHAPE;
+  if (!qmm::step::shape_ok(p)) return QMM_ERR_SHAPE;
+  const size_t e = out_elem(p.out_dtype);
+  if (!qmm::aligned(p.out0, e) || (p.kind == QMM_STEP_QKV && (!qmm::aligned(p.out1, e) || !qmm::aligned(p.out2, e))) ||
+      (p.lin_bias && !qmm::aligned(p.lin_bias, 2)))
+    return QMM_ERR_ALIGN;
+  return QMM_OK;
+}
+
+// The output ranges of a projection (1 or 3).
+int step_outputs(const qmm_step_proj& p, Range* r) {
+  const uint64_t e = out_elem(p.out_dtype);
+  if (p.kind == QMM_STEP_QKV) {
+    r[0] = {p.out0, uint64_t(p.q_out) * e};
+    r[1] = {p.out1, uint64_t(p.kv_out) * e};
+    r[2] = {p.out2, uint64_t(p.kv_out) * e};
+    return 3;
+  }
+  r[0] = {p.out0, uint64_t(p.kind == QMM_STEP_GATE_UP_SWIGLU ? p.rows / 2 : p.rows) * e};
+  return 1;
+}
+
+// The input ranges of a projection (x first).
+int step_inputs(const qmm_step_proj& p, Range* r) {
+  r[0] = {p.x, uint64_t(p.K) * 2};
+  r[1] = {p.codes, code_bytes(p.rows, p.K, kU4G64)};
+  r[2] = {p.scales, group_bytes(p.rows, p.K, kU4G64)};
+  r[3] = {p.biases, group_bytes(p.rows, p.K, kU4G64)};
+  r[4] = {p.lin_bias, p.lin_bias ? uint64_t(p.rows) * 2 : 0};
+  return 5;
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return qmm::any_alias(&a, 1, &b, 1);
+}
+
+}  // namespace
+
+size_t qmm_step_plan_bytes(const qmm_step_proj* projs, int32_t n) {
+  if (!projs || n < 1 || n > kMaxStepProjections) return 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const qmm_step_proj& p = projs[i];
+    if ((p.kind != QMM_STEP_LINEAR && p.kind != QMM_STEP_QKV && p.kind != QMM_STEP_GATE_UP_SWIGLU) ||
+        !qmm::k_ok(p.K) || p.K <= 512 || p.rows < 1 || p.rows > (int64_t(1) << 30))
+      return 0;
+  }
+  return size_t(qmm::step::plan_bytes(projs, n));
+}
+
+int qmm_step_plan(const qmm_step_proj* projs, int32_t n, void* plan, size_t plan_bytes, hipStream_t stream) {
+  if (!projs || !plan) return QMM_ERR_NULL;
+  if (n < 1 || n > kMaxStepProjections) return QMM_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i)
+    if (int st = check_step_proj(projs[i], i)) return st;
+  const size_t need = qmm_step_plan_bytes(projs, n);
+  if (need == 0 || plan_bytes < need) return QMM_ERR_SHAPE;
+  if (!qmm::aligned(plan, 256)) return QMM_ERR_ALIGN;
+  // outputs: disjoint from each other, from the plan and from every input, except that the
+  // x of a projection may lie in the outputs of the projection it waits for
+  const Range pr = {plan, uint64_t(need)};
+  for (int32_t i = 0; i < n; ++i) {
+    Range oi[3], ii[5];
+    const int no = step_outputs(projs[i], oi);
+    const int ni = step_inputs(projs[i], ii);
+    for (int a = 0; a < no; ++a) {
+      if (overlap(oi[a], pr)) return QMM_ERR_ALIAS;
+      for (int b = a + 1; b < no; ++b)
+        if (overlap(oi[a], oi[b])) return QMM_ERR_ALIAS;
+    }
+    for (int b = 0; b < ni; ++b)
+      if (overlap(ii[b], pr)) return QMM_ERR_ALIAS;
+    for (int32_t j = 0; j < n; ++j) {
+      Range oj[3];
+      const int noj = step_outputs(projs[j], oj);
+      for (int a = 0; a < noj; ++a) {
+        if (j > i)
+          for (int b = 0; b < no; ++b)
+            if (overlap(oj[a], oi[b])) return QMM_ERR_ALIAS;
+        for (int b = 0; b < ni; ++b) {
+          const bool allowed = b == 0 && projs[i].wait_for == j;
+          if (!allowed && overlap(oj[a], ii[b])) return QMM_ERR_ALIAS;
+        }
+      }
+    }
+  }
+  return qmm::step::build_and_upload(projs, n, plan, need, stream);
+}
+
+int qmm_step_run(const qmm_step_proj* projs, int32_t n, const void* plan, hipStream_t stream) {
+  if (!projs || !plan) return QMM_ERR_NULL;
+  if (n < 1 || n > kMaxStepProjections) return QMM_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i) {
+    const qmm_step_proj& p = projs[i];
+    if ((p.kind != QMM_STEP_LINEAR && p.kind != QMM_STEP_QKV && p.kind != QMM_STEP_GATE_UP_SWIGLU) ||
+        p.wait_for < -1 || p.wait_for >= i || !qmm::k_ok(p.K) || p.K <= 512 || p.rows < 1 ||
+        p.rows > (int64_t(1) << 30) || !qmm::step::shape_ok(p))
+      return QMM_ERR_SHAPE;
+    // small launches take the pointers from here, not from the plan
+    if (!p.x || !p.codes || !p.scales || !p.biases || !p.out0 ||
+        (p.kind == QMM_STEP_QKV && (!p.out1 || !p.out2)))
+      return QMM_ERR_NULL;
+  }
+  if (!qmm::aligned(plan, 256)) return QMM_ERR_ALIGN;
+  return qmm::step::launch(projs, n, plan, stream);
+}
+
 int qmm_moe_prefill(int stage, const uint16_t* in, int64_t M, int64_t K, const uint32_t* codes,
                     const uint16_t* scales, const uint16_t* biases, int64_t E, int64_t rows,
                     const int32_t* expert_ids, const float* expert_w, int64_t topk, void* workspace,

@@ -23,6 +23,20 @@ constexpr int kFmtFp8E4M3 = 0x108;
 
 enum Epilogue : int { EPI_LINEAR = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_ROPE = 3 };
 
+}  // namespace qmm
+struct qmm_step_proj;
+namespace qmm {
+
+// Decode step in few launches (gemv_step.hip): plan size (0 if a projection cannot be
+// planned), whether a projection's K can be planned, plan writing (validated arguments) and
+// the launches of a run.
+namespace step {
+uint64_t plan_bytes(const qmm_step_proj* projs, int n);
+bool shape_ok(const qmm_step_proj& p);
+int build_and_upload(const qmm_step_proj* projs, int n, void* plan, uint64_t bytes, hipStream_t stream);
+int launch(const qmm_step_proj* projs, int n, const void* plan, hipStream_t stream);
+}  // namespace step
+
 // Compute units of the current device (hipDeviceAttributeMultiprocessorCount), queried once
 // per device; 256 if the query fails.  The launch geometries are sized from it.
 int device_cus();

@@ -288,6 +288,78 @@ int qmm_moe_prefill_noalloc(int stage, const uint16_t* in, int64_t M, int64_t K,
                             int64_t topk, void* out, int out_dtype, hipStream_t stream);
 
 /*
+ * A decode step in few launches: several 4-bit group-64 projections of one token (M = 1) run
+ * by one launch per dependency level and kind instead of one launch per projection (the
+ * pages' case for fusing: 96 launches cost ~3 ms per decode step, "The Cathedral Doubled
+ * Itself", "The two fusions"; one command buffer per token, saragossa README, "Design
+ * principles").  A projection may read the output of an earlier projection of the same step
+ * (the down projection reading its layer's h): it names that projection in wait_for and runs
+ * in a later launch of the same run.  Launches: the projections that read no other
+ * projection's output form level 0, a projection reading one of level l is of level l + 1;
+ * each level is one launch for its projections with K <= 5120 and one for those with a
+ * larger K (split over 8 waves; over 16 above K = 40960).  The 14B-shaped step (fused QKV +
+ * fused gate+up) is one launch; 40 24B-shaped layers (QKV, gate+up, down) are two.  Nothing
+ * waits inside a launch: ordering inside one launch would cost device-scope atomics and
+ * cache write-backs per wave, measured at far more than a launch.
+ *
+ * Every output equals, bit for bit, what the per-call entry point returns for the same
+ * projection at M = 1 (qmm_linear, qmm_fused_qkv, qmm_fused_gate_up_swiglu).
+ *
+ * Two calls:
+ *   qmm_step_plan  validates the projections and writes a plan into caller-owned device
+ *                  memory of qmm_step_plan_bytes bytes (once, outside graph capture: it
+ *                  copies from the host and synchronises `stream`);
+ *   qmm_step_run   enqueues a run (its launches, no allocation, no host synchronisation;
+ *                  capturable in a HIP graph), as often as needed, with the same
+ *                  projections: each run reads the inputs' current contents and
+ *                  overwrites the outputs.
+ */
+enum qmm_step_kind { QMM_STEP_LINEAR = 0, QMM_STEP_QKV = 1, QMM_STEP_GATE_UP_SWIGLU = 2 };
+
+typedef struct qmm_step_proj {
+  int32_t kind;            /* QMM_STEP_LINEAR, QMM_STEP_QKV or QMM_STEP_GATE_UP_SWIGLU */
+  int32_t wait_for;        /* index of an earlier projection whose output this one's x
+                              reads (it then runs in a later launch), or -1 */
+  int64_t K;               /* inputs: a multiple of 64, 576 <= K <= QMM_MAX_K */
+  int64_t rows;            /* weight rows: N (LINEAR), q_out + 2*kv_out (QKV), 2*I (GATE_UP) */
+  int64_t q_out, kv_out;   /* QKV only (ignored otherwise) */
+  const uint16_t* x;       /* [K] bf16 */
+  const uint32_t* codes;   /* [rows][K/8] */
+  const uint16_t* scales;  /* [rows][K/64] bf16 */
+  const uint16_t* biases;  /* [rows][K/64] bf16 */
+  const uint16_t* lin_bias;  /* nullable [rows] bf16 additive bias; LINEAR and QKV only */
+  void* out0;              /* LINEAR: y [rows]; QKV: q [q_out]; GATE_UP: h [rows/2] */
+  void* out1;              /* QKV: k [kv_out]; else ignored */
+  void* out2;              /* QKV: v [kv_out]; else ignored */
+  int32_t out_dtype;       /* QMM_OUT_BF16 or QMM_OUT_F32 */
+  int32_t reserved;        /* must be 0 */
+} qmm_step_proj;
+
+/* Device bytes of the plan of these n projections (0 if n is outside [1, 4096] or a
+ * projection's kind or sizes cannot be planned).  Host only; reads kind, wait_for, K, rows. */
+size_t qmm_step_plan_bytes(const qmm_step_proj* projs, int32_t n);
+
+/*
+ * qmm_step_plan -- projs: host array [n].  plan: device memory, 256-byte aligned, of at
+ * least qmm_step_plan_bytes(projs, n) bytes, owned by the caller and left alone between
+ * runs.  Checks every projection as the per-call entry points do (QMM_ERR_NULL,
+ * QMM_ERR_SHAPE, QMM_ERR_ALIGN, QMM_ERR_ENUM, QMM_ERR_ALIAS), plus: wait_for must be -1 or
+ * the index of an earlier projection; outputs may not overlap each other, the plan, or any
+ * input, except that a projection's x may lie in the outputs of the projection it waits
+ * for.  Then writes the plan (a host-to-device copy on `stream`, followed by
+ * hipStreamSynchronize(stream)).  QMM_ERR_LAUNCH if the copy fails.
+ */
+int qmm_step_plan(const qmm_step_proj* projs, int32_t n, void* plan, size_t plan_bytes, hipStream_t stream);
+
+/*
+ * qmm_step_run -- enqueue one run of a plan: projs and n exactly as given to qmm_step_plan
+ * for this plan (host, read in full and not checked again: a launch of at most four
+ * projections carries them in its kernel arguments, a larger one reads them from the plan).
+ * One kernel launch per (level, kind) in order on `stream`; nothing is allocated or copied.
+ */
+int qmm_step_run(const qmm_step_proj* projs, int32_t n, const void* plan, hipStream_t stream);
+
+/*
  * Other formats of the affine family (saragossa README, "Capabilities": u4/u6/u8 at group
  * sizes 32-128 with bf16 scales/biases; "Quantization formats": u2/u3/u4/u6/u8 affine
  * integer weights).  The *_fmt calls are the calls above with the code width `bits` and

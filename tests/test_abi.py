@@ -29,6 +29,7 @@ def test_header_declares_the_entry_points():
                                            "qmm_moe_gather_fmt",
                                            "qmm_moe_gather", "qmm_moe_prefill_workspace_bytes",
                                            "qmm_moe_route", "qmm_moe_prefill", "qmm_moe_prefill_noalloc",
+                                           "qmm_step_plan_bytes", "qmm_step_plan", "qmm_step_run",
                                            "qmm_status_str",
                                            "qmm_abi_version"])
 
