@@ -625,10 +625,39 @@ def bench_step_24b(torch, qmm, synth, T, dev, n_steps):
             "per_call_step_over_kernel_sum": round(ms_pc / (L * (ms_q + ms_g + ms_d)), 4)}
 
 
+def read_ceiling_sequence(torch, dev, T, sizes):
+    """The plain streaming read (qmm_ceiling_read) as a sequence of launches of the given
+    byte sizes, each on its own slice of a 2 GiB pool, timed like the kernels (a HIP graph):
+    microseconds per sequence, best over launch shapes.  The ceiling of a path that is that
+    many launches of those sizes."""
+    lib = _ceiling_lib()
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    st = T.stream.cuda_stream
+    sizes = [(b + 1023) // 1024 * 1024 for b in sizes]
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    pool.fill_(1)
+    per_seq = sum(sizes)
+    nseq = (2 << 30) // per_seq
+    best = None
+    for blocks in (256, 512, 1024, 2048):
+        for unroll in (1, 2, 4):
+            def fn(i, blocks=blocks, unroll=unroll):
+                base = pool.data_ptr() + (i % nseq) * per_seq
+                for b in sizes:
+                    lib.qmm_ceiling_read(base, b, blocks, unroll, 1, sink.data_ptr(), st)
+                    base += b
+            us = T.per_call_ms(fn, min(nseq, 200)) * 1e3
+            best = us if best is None else min(best, us)
+    del pool
+    torch.cuda.empty_cache()
+    return best
+
+
 def bench_moe(torch, qmm, synth, T, dev, n_steps):
     """35B-A3B-shaped MoE decode: per layer, stage 1 (gathered gate+up+SwiGLU of the 8
     routed experts) and stage 2 (gathered down + weighted combine), over a 40-layer pool
-    of in-place expert grids, fresh routing per step and layer."""
+    of in-place expert grids, fresh routing per step and layer (the layer call
+    qmm_moe_layer: two launches)."""
     sh = synth.MOE_35B
     H, E, Ie, topk = sh.hidden, sh.E, sh.I, sh.topk
     L = 40
@@ -648,25 +677,27 @@ def bench_moe(torch, qmm, synth, T, dev, n_steps):
     y = torch.empty((H,), dtype=torch.bfloat16, device=dev)
     st = T.stream
 
-    def one_step(s):
+    def layer_call(s):
         s %= n_steps
         for l in range(L):
-            qmm.qmm_moe_gather(qmm.QMM_MOE_GATE_UP_SWIGLU, xs[s], pgu[0][l], pgu[1][l], pgu[2][l], ids_d[s, l], hk,
-                               stream=st)
-            qmm.qmm_moe_gather(qmm.QMM_MOE_DOWN_COMBINE, hk, pdn[0][l], pdn[1][l], pdn[2][l], ids_d[s, l], y,
-                               expert_w=pw_d[s, l], stream=st)
+            qmm.qmm_moe_layer(xs[s], pgu[0][l], pgu[1][l], pgu[2][l], pdn[0][l], pdn[1][l], pdn[2][l], ids_d[s, l],
+                              pw_d[s, l], hk, y, stream=st)
 
-    g = T.capture(one_step, n_steps)
+    g = T.capture(layer_call, n_steps)
     T.replay_ms(g)
     ms_layer = T.replay_ms(g) / (n_steps * L)
     del g
     b_layer = (topk * (weight_bytes(2 * Ie, H) + weight_bytes(H, Ie))
                + H * 2 + 2 * topk * Ie * 2 + H * 2 + topk * 8)
     gbs = b_layer / (ms_layer * 1e-3) / 1e9
+    b1 = topk * weight_bytes(2 * Ie, H) + H * 2 + topk * Ie * 2 + topk * 4
+    ceil_us = read_ceiling_sequence(torch, dev, T, [b1, b_layer - b1])
     return {"workload": f"35B-A3B-shaped MoE decode M=1: top-{topk} of {E} experts, hidden {H}, expert I {Ie}, "
                         f"{L}-layer pool, fresh routing per step and layer, {n_steps} steps in one graph",
             "us_per_layer": round(ms_layer * 1e3, 3), "bytes_per_layer": b_layer, "GB/s": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_layer": 2}
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "launches_per_layer": 2,
+            "read_ceiling_two_launches_us": round(ceil_us, 3),
+            "frac_of_read_ceiling": round(ceil_us / (ms_layer * 1e3), 4)}
 
 
 def bench_moe_prefill(torch, qmm, synth, T, dev, reps):

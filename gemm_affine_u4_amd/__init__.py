@@ -14,7 +14,7 @@ import os
 
 __all__ = ["QmmError", "qmm_linear", "qmm_fused_qkv", "qmm_fused_qkv_rope", "qmm_fused_gate_up_swiglu",
            "qmm_moe_gather", "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
-           "qmm_moe_gather_fmt",
+           "qmm_moe_gather_fmt", "qmm_moe_layer",
            "qmm_moe_prefill_workspace_bytes", "qmm_moe_route", "qmm_moe_prefill", "qmm_moe_prefill_noalloc",
            "QMM_NOALLOC_SCRATCH_BYTES", "StepProj", "step_linear", "step_fused_qkv", "step_gate_up_swiglu",
            "qmm_step_plan_bytes", "qmm_step_plan", "qmm_step_run",
@@ -54,6 +54,7 @@ _SIGNATURES = {
                            _INT, _P],
     "qmm_moe_gather": [_INT, _P, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _INT, _P],
     "qmm_moe_prefill_workspace_bytes": [_I64, _I64, _I64, _I64],
+    "qmm_moe_layer": [_P, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _INT, _P],
     "qmm_moe_route": [_P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P],
     "qmm_moe_prefill": [_INT, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_size_t, _P,
                         _INT, _P],
@@ -255,6 +256,31 @@ def qmm_moe_gather(stage, inp, codes, scales, biases, expert_ids, out, expert_w=
                                          _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"),
                                          expert_ids.shape[0], _ptr(out, "out"), _out_dtype(out),
                                          _stream(stream)), "qmm_moe_gather")
+
+
+def qmm_moe_layer(x, gu_codes, gu_scales, gu_biases, dn_codes, dn_scales, dn_biases, expert_ids, expert_w, h, y,
+                  stream=None) -> None:
+    """Both stages of the routed experts for one decode token in one call: x [K] bf16,
+    gate+up grid [E, 2I, K/8], down grid [E, K, I/8], h [topk, I] bf16 (written), y [K]
+    (bf16 or fp32)."""
+    E, rows1 = gu_codes.shape[0], gu_codes.shape[1]
+    K = x.shape[-1]
+    I = rows1 // 2
+    topk = expert_ids.shape[0]
+    _check_weight(gu_codes, gu_scales, gu_biases, E * rows1, K, "gate+up expert grid")
+    _need(dn_codes.shape[0] == E and dn_codes.shape[1] == K, "down grid must be [E, K, I/8]")
+    _check_weight(dn_codes, dn_scales, dn_biases, E * K, I, "down expert grid")
+    _need(_bytes(x) == K * 2, "x must be bf16 [K]")
+    _need(expert_ids.numel() == topk and expert_ids.element_size() == 4, "expert_ids must be int32 [topk]")
+    _need(_bytes(expert_w) == topk * 4, "expert_w must be fp32 [topk]")
+    _need(_bytes(h) == topk * I * 2, "h must be bf16 [topk, I]")
+    _need(_elems(y) == K, "y must be [K]")
+    _check(load_library().qmm_moe_layer(_ptr(x, "x"), K, _ptr(gu_codes, "gu_codes"), _ptr(gu_scales, "gu_scales"),
+                                        _ptr(gu_biases, "gu_biases"), _ptr(dn_codes, "dn_codes"),
+                                        _ptr(dn_scales, "dn_scales"), _ptr(dn_biases, "dn_biases"), E, I,
+                                        _ptr(expert_ids, "expert_ids"), _ptr(expert_w, "expert_w"), topk,
+                                        _ptr(h, "h"), _ptr(y, "y"), _out_dtype(y), _stream(stream)),
+           "qmm_moe_layer")
 
 
 def qmm_moe_prefill_workspace_bytes(M: int, topk: int, E: int, out_rows: int = 0) -> int:

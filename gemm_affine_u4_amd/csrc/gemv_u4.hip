@@ -376,18 +376,17 @@ struct S1Layout {
 // NR activation rows per block (two: both rows' results from one read of the weights,
 // each row computed exactly as alone); the first row's activations stay in registers,
 // the second's are read from the block's LDS copy per row unit.
-template <int LPR, int CPL, int EPI, bool MOE, int NR = 1, int DEPTH = QMM_S1_DEPTH>
-#ifndef QMM_S1_MINW
-#define QMM_S1_MINW 1
-#endif
-__global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(GemvArgs a, int64_t per_wave,
-                                                                              int64_t extra) {
+// The body of the single-slice kernel for block (bx, by) of a grid of WPB-wave blocks (0:
+// blockDim.x / 64), shared by gemv_u4_s1_kernel and the stage-1 blocks of the one-launch
+// MoE layer.
+template <int LPR, int CPL, int EPI, bool MOE, int NR, int DEPTH, int WPB>
+__device__ __forceinline__ void s1_body(const GemvArgs& a, int64_t per_wave, int64_t extra, uint32_t bx,
+                                        uint32_t by, uint32_t* s1_lds) {
   using Lay = S1Layout<LPR, CPL>;
   constexpr int RPI = Lay::RPI;
   constexpr int P = RPI / 2;
   constexpr int C = Lay::C;
   static_assert(NR == 1 || (NR == 2 && !MOE), "two rows: not the routed experts");
-  extern __shared__ __attribute__((aligned(16))) uint32_t s1_lds[];
   uint32_t* xl = s1_lds;  // row r at s1_lds + r * x_words
   float* xsl = reinterpret_cast<float*>(s1_lds + C * kXStride);
 
@@ -399,7 +398,8 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   const int64_t groups = a.K >> (5 + a.gshift);
   // the units are spread evenly over the waves: every wave takes `per_wave` consecutive
   // units and the first `extra` waves one more
-  const int64_t gw = int64_t(blockIdx.x) * kWavesS1 + wave;
+  const int wpb = WPB > 0 ? WPB : int(blockDim.x >> 6);  // WPB = 0: the block's own size
+  const int64_t gw = int64_t(bx) * wpb + wave;
   const int64_t u_begin = gw * per_wave + (gw < extra ? gw : extra);
   const int64_t u_end = u_begin + per_wave + (gw < extra ? 1 : 0);
 
@@ -409,10 +409,10 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   const uint16_t* x = a.x;
   int64_t out_base;
   if constexpr (MOE) {
-    // blockIdx.y is the routed slot k (the whole block shares it); its expert's rows are
+    // `by` is the routed slot k (the whole block shares it); its expert's rows are
     // read in place from the grid, its activation row is k / moe_div (several tokens) or
     // the one row.
-    const int k = blockIdx.y;
+    const int k = by;
     const int32_t e = a.expert_ids[k];
     out_base = int64_t(k) * a.I;
     if (a.moe_div > 0) x += (int64_t(k) / a.moe_div) * a.K;
@@ -431,10 +431,10 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
     scales += off * groups;
     biases += off * groups;
   } else {
-    x += int64_t(blockIdx.y) * NR * a.K;
-    out_base = int64_t(blockIdx.y) * NR * a.n_out;
+    x += int64_t(by) * NR * a.K;
+    out_base = int64_t(by) * NR * a.n_out;
   }
-  const int64_t m0 = int64_t(blockIdx.y) * NR;  // activation row of the block's first row
+  const int64_t m0 = int64_t(by) * NR;  // activation row of the block's first row
 
   const uint32_t row_bytes = uint32_t((a.K * kBits) >> 3);
   const uint64_t nrows = uint64_t(a.rows);
@@ -467,7 +467,7 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + rr * a.K, uint64_t(a.K) * 2);
     uint32_t* xlr = xl + rr * Lay::x_words;
     float* xslr = xsl + rr * Lay::x_words;
-    for (int c = threadIdx.x; c < C; c += 64 * kWavesS1) {
+    for (int c = threadIdx.x; c < C; c += 64 * wpb) {
       uint32_t d[16];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -563,12 +563,23 @@ __global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(
   }
 }
 
+#ifndef QMM_S1_MINW
+#define QMM_S1_MINW 1
+#endif
+template <int LPR, int CPL, int EPI, bool MOE, int NR = 1, int DEPTH = QMM_S1_DEPTH>
+__global__ void __launch_bounds__(64 * kWavesS1, QMM_S1_MINW) gemv_u4_s1_kernel(GemvArgs a, int64_t per_wave,
+                                                                              int64_t extra) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t s1_lds[];
+  s1_body<LPR, CPL, EPI, MOE, NR, DEPTH, kWavesS1>(a, per_wave, extra, blockIdx.x, blockIdx.y, s1_lds);
+}
+
 // Routed-expert stage 2: y[r] = sum_k p_k * (D_{e_k} h_k)[r], for each token (blockIdx.y)
 // of its topk slots.  A block's kw waves split
 // the routed slots (wave w takes k = w, w+kw, ...) and walk the block's `upw` row units
 // for each; every wave adds its slots in increasing k into its own LDS slice, and the
 // slices are then added in wave order.  No atomics, so the order is fixed.
 constexpr int kMaxUnitsPerCombineBlock = 16;
+constexpr int kDownGroup = 4;  // row units whose loads a wave requests together
 #ifndef QMM_MOE_DOWN_BLOCKS
 #define QMM_MOE_DOWN_BLOCKS 256
 #endif
@@ -605,17 +616,24 @@ __global__ void __launch_bounds__(512) moe_down_kernel(GemvArgs a, int64_t units
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales + uint64_t(e) * expert_groups, expert_groups * 2);
     const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases + uint64_t(e) * expert_groups, expert_groups * 2);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x + (pair0 + k) * a.K, uint64_t(a.K) * 2);
-    RowData<CPL> cur, nxt;
-    load_row<LPR, CPL>(cur, cr, sr, br, uint32_t(u_begin * RPI + slot), row_bytes, row_groups, c0, a.gshift);
+    // the units in groups of kDownGroup, every load of a group (and, with the first, the
+    // slot's h) requested before any of its arithmetic: one memory round trip per group
     uint32_t xp[CPL][16];
     float xs[CPL];
-    load_x_chunks<LPR, CPL>(xr, c0, xp, xs);
-    for (int u = 0; u < nu; ++u) {
-      if (u + 1 < nu)
-        load_row<LPR, CPL>(nxt, cr, sr, br, uint32_t((u_begin + u + 1) * RPI + slot), row_bytes, row_groups, c0, a.gshift);
-      const float v = slot_reduce<LPR>(row_partial<CPL>(cur, xp, xs, magic));
-      if (result_lane) red[wave][u][slot] = fmaf(p, v, red[wave][u][slot]);
-      cur = nxt;
+    for (int g0 = 0; g0 < nu; g0 += kDownGroup) {
+      RowData<CPL> buf[kDownGroup];
+#pragma unroll
+      for (int j = 0; j < kDownGroup; ++j)
+        if (g0 + j < nu)
+          load_row<LPR, CPL>(buf[j], cr, sr, br, uint32_t((u_begin + g0 + j) * RPI + slot), row_bytes, row_groups,
+                             c0, a.gshift);
+      if (g0 == 0) load_x_chunks<LPR, CPL>(xr, c0, xp, xs);
+#pragma unroll
+      for (int j = 0; j < kDownGroup; ++j)
+        if (g0 + j < nu) {
+          const float v = slot_reduce<LPR>(row_partial<CPL>(buf[j], xp, xs, magic));
+          if (result_lane) red[wave][g0 + j][slot] = fmaf(p, v, red[wave][g0 + j][slot]);
+        }
     }
   }
   __syncthreads();
@@ -822,6 +840,7 @@ int launch_moe_down(const GemvArgs& a, hipStream_t s) {
   }
   return finish_launch();
 }
+
 
 }  // namespace QMM_BITS_NS
 }  // namespace qmm

@@ -382,6 +382,68 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K, const uint32_t* cod
                             expert_w, topk, out, out_dtype, stream);
 }
 
+int qmm_moe_layer(const uint16_t* x, int64_t K, const uint32_t* gu_codes, const uint16_t* gu_scales,
+                  const uint16_t* gu_biases, const uint32_t* dn_codes, const uint16_t* dn_scales,
+                  const uint16_t* dn_biases, int64_t E, int64_t I, const int32_t* expert_ids, const float* expert_w,
+                  int64_t topk, uint16_t* h, void* y, int out_dtype, hipStream_t stream) {
+  if (int st = check_weight(x, gu_codes, gu_scales, gu_biases)) return st;
+  if (!dn_codes || !dn_scales || !dn_biases || !expert_ids || !expert_w || !h || !y) return QMM_ERR_NULL;
+  if (!out_dtype_ok(out_dtype)) return QMM_ERR_ENUM;
+  const Fmt& f = kU4G64;
+  if (!qmm::k_ok(K) || !qmm::k_ok(I) || I > 5120 || E < 1 || E > (int64_t(1) << 24) || topk < 1 ||
+      topk > QMM_MAX_TOPK || !codes_fit(2 * I, K, f) || !codes_fit(K, I, f))
+    return QMM_ERR_SHAPE;
+  const size_t e = out_elem(out_dtype);
+  if (!qmm::aligned(dn_codes, 16) || !qmm::aligned(dn_scales, 2) || !qmm::aligned(dn_biases, 2) ||
+      !qmm::aligned(h, 16) || !qmm::aligned(y, e) || !qmm::aligned(expert_ids, 4) || !qmm::aligned(expert_w, 4))
+    return QMM_ERR_ALIGN;
+  const Range outs[] = {{h, uint64_t(topk * I) * 2}, {y, uint64_t(K) * e}};
+  const Range ins[] = {{x, uint64_t(K) * 2},
+                       {gu_codes, code_bytes(E * 2 * I, K, f)},
+                       {gu_scales, group_bytes(E * 2 * I, K, f)},
+                       {gu_biases, group_bytes(E * 2 * I, K, f)},
+                       {dn_codes, code_bytes(E * K, I, f)},
+                       {dn_scales, group_bytes(E * K, I, f)},
+                       {dn_biases, group_bytes(E * K, I, f)},
+                       {expert_ids, uint64_t(topk) * 4},
+                       {expert_w, uint64_t(topk) * 4}};
+  if (qmm::any_alias(outs, 2, ins, 9)) return QMM_ERR_ALIAS;
+
+  // the two stages exactly as qmm_moe_gather takes them
+  qmm::GemvArgs a1 = {};
+  a1.x = x;
+  a1.codes = gu_codes;
+  a1.scales = gu_scales;
+  a1.biases = gu_biases;
+  a1.out0 = h;
+  a1.K = K;
+  a1.rows = 2 * I;
+  a1.I = I;
+  a1.expert_ids = expert_ids;
+  a1.E = E;
+  a1.topk = int(topk);
+  a1.bits = f.bits;
+  a1.gshift = f.gshift;
+  qmm::GemvArgs a2 = {};
+  a2.x = h;
+  a2.codes = dn_codes;
+  a2.scales = dn_scales;
+  a2.biases = dn_biases;
+  a2.out0 = y;
+  a2.K = I;
+  a2.rows = K;
+  a2.I = K / 2;
+  a2.expert_ids = expert_ids;
+  a2.expert_w = expert_w;
+  a2.E = E;
+  a2.topk = int(topk);
+  a2.f32_out = out_dtype == QMM_OUT_F32;
+  a2.bits = f.bits;
+  a2.gshift = f.gshift;
+  if (int st = qmm::launch_moe_gate_up(a1, stream)) return st;
+  return qmm::launch_moe_down(a2, stream);
+}
+
 size_t qmm_moe_prefill_workspace_bytes(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
   if (M < 1 || M > 65535 || topk < 1 || topk > QMM_MAX_TOPK || E < 1 || E > QMM_MAX_EXPERTS_PREFILL ||
       out_rows < 0 || out_rows > (int64_t(1) << 24))

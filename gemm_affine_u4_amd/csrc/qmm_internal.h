@@ -135,6 +135,8 @@ namespace b4 {
 int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
 }
 
+
+
 #define QMM_BY_WIDTH(bits, CALL)                \
   switch (bits) {                               \
     case 2: return b2::CALL;                    \

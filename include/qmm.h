@@ -196,6 +196,23 @@ int qmm_moe_gather(int stage, const uint16_t* in, int64_t K,
                    int64_t topk, void* out, int out_dtype, hipStream_t stream);
 
 /*
+ * qmm_moe_layer -- both stages of qmm_moe_gather for one decode token, in one call (4-bit
+ * codes, group 64; the in-place expert grids of "Sanctum-MLX", "Inside the server"):
+ *   h = stage QMM_MOE_GATE_UP_SWIGLU of x: gate+up grid gu_* [E][2I][K/8] and [E][2I][K/64],
+ *       h [topk][I] bf16, written;
+ *   y = stage QMM_MOE_DOWN_COMBINE of h: down grid dn_* [E][K][I/8] and [E][K][I/64],
+ *       expert_w fp32 [topk], y [K] in out_dtype.
+ * Two launches on `stream` (stage 1, then stage 2, as the two qmm_moe_gather calls); h and
+ * y equal those calls' results bit for bit.
+ * Shapes: K and I multiples of 64, I <= 5120, topk <= QMM_MAX_TOPK; QMM_ERR_ALIAS if h or y
+ * overlap each other or an input.
+ */
+int qmm_moe_layer(const uint16_t* x, int64_t K, const uint32_t* gu_codes, const uint16_t* gu_scales,
+                  const uint16_t* gu_biases, const uint32_t* dn_codes, const uint16_t* dn_scales,
+                  const uint16_t* dn_biases, int64_t E, int64_t I, const int32_t* expert_ids, const float* expert_w,
+                  int64_t topk, uint16_t* h, void* y, int out_dtype, hipStream_t stream);
+
+/*
  * Routed experts over a batch of tokens (prefill).  Token m has topk (token, slot)
  * pairs p = m*topk + k, each with an expert id expert_ids[m][k] (an id outside [0, E)
  * means "no expert"); the experts are the same in-place 3-D grid as qmm_moe_gather

@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
                                            "qmm_linear_fmt", "qmm_fused_qkv_fmt", "qmm_fused_gate_up_swiglu_fmt",
                                            "qmm_moe_gather_fmt",
                                            "qmm_moe_gather", "qmm_moe_prefill_workspace_bytes",
+                                           "qmm_moe_layer",
                                            "qmm_moe_route", "qmm_moe_prefill", "qmm_moe_prefill_noalloc",
                                            "qmm_step_plan_bytes", "qmm_step_plan", "qmm_step_run",
                                            "qmm_status_str",
@@ -251,6 +252,25 @@ def test_moe_prefill_validation():
     assert _prefill(out=WS + 256) == S["QMM_ERR_ALIAS"]             # out inside the workspace
     assert _prefill(ws=A + (1 << 16)) == S["QMM_ERR_ALIAS"]         # workspace on the weights
     assert _prefill(out=A + (1 << 22)) == S["QMM_ERR_ALIAS"]        # out on the expert ids
+
+
+def _layer(x=A, K=512, gc=A + (1 << 16), gs=A + (1 << 18), gb=A + (1 << 19), dc=A + (1 << 20), ds=A + (1 << 21),
+           db=A + (1 << 22), E=4, I=128, ids=A + (1 << 23), ew=A + (1 << 24), topk=2, h=A + (1 << 25),
+           y=A + (1 << 26), od=0):
+    return qmm.load_library().qmm_moe_layer(x, K, gc, gs, gb, dc, ds, db, E, I, ids, ew, topk, h, y, od, None)
+
+
+def test_moe_layer_validation():
+    for kw in ("x", "gc", "dc", "db", "ids", "ew", "h", "y"):
+        assert _layer(**{kw: None}) == S["QMM_ERR_NULL"], kw
+    assert _layer(od=3) == S["QMM_ERR_ENUM"]
+    assert _layer(K=96) == S["QMM_ERR_SHAPE"]
+    assert _layer(I=5184) == S["QMM_ERR_SHAPE"]                   # stage 2 in one K slice only
+    assert _layer(topk=0) == S["QMM_ERR_SHAPE"] and _layer(topk=65) == S["QMM_ERR_SHAPE"]
+    assert _layer(E=0) == S["QMM_ERR_SHAPE"]
+    assert _layer(h=A + (1 << 25) + 2) == S["QMM_ERR_ALIGN"]
+    assert _layer(y=A + 8) == S["QMM_ERR_ALIAS"]                   # y on x
+    assert _layer(h=A + (1 << 26) + 64) == S["QMM_ERR_ALIAS"]      # h over y
 
 
 # ---- host-only build of the validation code ------------------------------------
