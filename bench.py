@@ -54,11 +54,15 @@ def _args():
     ap.add_argument("--moe-steps", type=int, default=20)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the prefill, 24B-step and MoE measurements")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary (" + COUNTERS_SUMMARY + ") from the counter "
+                         "collections of two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE), "
+                         "then exit; needs no GPU")
     return ap.parse_args()
 
 
 KERNEL_SOURCES = ["gemm_affine_u4_amd/csrc/gemv_step.hip", "gemm_affine_u4_amd/csrc/qmm_step.h",
-                  "gemm_affine_u4_amd/csrc/qmm_device.h"]
+                  "gemm_affine_u4_amd/csrc/gemv_u4.hip", "gemm_affine_u4_amd/csrc/qmm_device.h"]
 COUNTERS_SUMMARY = "profiles/gemv_step_decode_14B_hbm_counters.md"
 
 
@@ -66,18 +70,94 @@ def counted_traffic(key: str):
     """HBM bytes per launch measured by the committed counter runs (FETCH_SIZE and
     WRITE_SIZE, calibrated on a device copy), or None if the kernel sources changed
     since they were taken."""
-    import hashlib
     import re
     try:
         text = open(os.path.join(ROOT, COUNTERS_SUMMARY)).read()
-        h = hashlib.sha256()
-        for f in KERNEL_SOURCES:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        if re.search(r"source_sha256_16: (\w+)", text).group(1) != h.hexdigest()[:16]:
+        if re.search(r"source_sha256_16: (\w+)", text).group(1) != _source_hash():
             return None
         return int(re.search(rf"traffic_bytes_per_launch\.{key}: (\d+)", text).group(1))
     except (OSError, AttributeError):
         return None
+
+
+COUNTER_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {c} --output-format csv "
+               "-d $REPO/gpurun_out/prof_{n} -o {n} -- python3 $REPO/bench.py --steps 20 --warmup 2 "
+               "--kernel-reps 20 --no-cpu-baseline --headline-only")
+
+
+def _source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> str:
+    """HBM bytes per launch of the decode kernels from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the bench's 2 GiB device copy
+    (2 GiB read and 2 GiB written); writes COUNTERS_SUMMARY and returns its text."""
+    import csv
+    sh = __import__("synth").DENSE_14B
+    K, I, rows_qkv = sh.K, sh.I, sh.qkv_rows
+    b_qkv = weight_bytes(rows_qkv, K) + K * 2 + rows_qkv * 2
+    b_gu = weight_bytes(2 * I, K) + K * 2 + I * 2
+
+    def values(path, match):
+        v = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if match in r["Kernel_Name"]]
+        if not v:
+            raise SystemExit(f"{path}: no dispatch of {match}")
+        return v
+
+    def mean_of(path, match):
+        v = values(path, match)
+        return sum(v) / len(v), len(v)
+
+    def copies(path):
+        # the bench's ten 2 GiB device copies: the ten largest readings of the copy kernel
+        # (the plans' host-to-device uploads run it too, on a few KB)
+        v = sorted(values(path, "__amd_rocclr_copyBuffer"))[-10:]
+        if len(v) < 10 or v[0] < 0.9 * v[-1]:
+            raise SystemExit(f"{path}: the ten device copies are not the largest copy dispatches")
+        return sum(v) / len(v)
+
+    known = 2 * 2 ** 30 / 1024
+    cf, cw = copies(fetch_csv), copies(write_csv)
+    ff, fw = known / cf, known / cw
+    lines = [f"copy calibration: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB for a 2 GiB device copy -> "
+             f"factors fetch {ff:.4f}, write {fw:.4f}"]
+    keys = []
+    for key, what, match, alg in [
+            ("step", "one-launch 14B step (fused QKV + fused gate+up+SwiGLU, K=5120)",
+             "qmm::step::gemv_step_single_inline_kernel<true>", b_qkv + b_gu),
+            ("gate_up", "per-call fused gate+up+SwiGLU GEMV (K=5120, I=13824)",
+             "qmm::b4::gemv_u4_s1_kernel<32, 5, 2, false, 1, 1>", b_gu),
+            ("qkv", "per-call fused QKV GEMV (K=5120, 7168 rows)", "qmm::b4::gemv_u4_s1_kernel<32, 5, 1, false, 1, 1>",
+             b_qkv)]:
+        fk, nf = mean_of(fetch_csv, match)
+        wk, nw = mean_of(write_csv, match)
+        t = (fk * ff + wk * fw) * 1024
+        lines.append(f"{what}: FETCH_SIZE {fk:.1f} KiB x {ff:.4f} + WRITE_SIZE {wk:.1f} KiB x {fw:.4f} = "
+                     f"{t:.0f} B per launch; algorithmic {alg} B; ratio {t / alg:.4f} (n={nf},{nw})")
+        keys.append(f"traffic_bytes_per_launch.{key}: {t:.0f}")
+    h = _source_hash()
+    text = "\n".join([
+        "# Decode GEMV kernels, 14B-shaped step — HBM traffic counters (rocprofv3 --pmc)", "",
+        "Two counter runs, one counter each (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch):", "",
+        "    " + COUNTER_CMD.format(c="FETCH_SIZE", n="fetch"),
+        "    " + COUNTER_CMD.format(c="WRITE_SIZE", n="write"), "",
+        "Summarised by `python3 bench.py --summarize-counters <fetch_counter_collection.csv> "
+        "<write_counter_collection.csv>`.  Calibration: bench.py runs ten 2 GiB device-to-device copies "
+        "(`__amd_rocclr_copyBuffer`, 2 GiB read and 2 GiB written each); the counters' readings for that copy "
+        "give the factors applied to the kernels.  Traffic per launch = the mean over all launches of that "
+        "kernel (the 48-layer pool rotates, so every launch streams its weights from HBM).", "",
+        *["    " + ln for ln in lines], "",
+        "Machine-readable (read by bench.py; valid only while the kernel sources hash to the value below, "
+        "otherwise bench.py reports traffic as null):", "",
+        f"    source_sha256_16: {h}", *["    " + k for k in keys], ""])
+    with open(os.path.join(ROOT, COUNTERS_SUMMARY), "w") as f:
+        f.write(text)
+    return text
 
 
 def weight_bytes(rows: int, K: int) -> int:
@@ -127,6 +207,9 @@ class Timer:
 
 def main():
     args = _args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "one GPU only: --gpus must be 1 (no multi-GPU path is built)",
                           "n_gpus_requested": args.gpus}))
