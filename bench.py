@@ -66,13 +66,13 @@ KERNEL_SOURCES = ["gemm_affine_u4_amd/csrc/gemv_step.hip", "gemm_affine_u4_amd/c
 COUNTERS_SUMMARY = "profiles/gemv_step_decode_14B_hbm_counters.md"
 
 
-def counted_traffic(key: str):
+def counted_traffic(key: str, summary: str = None):
     """HBM bytes per launch measured by the committed counter runs (FETCH_SIZE and
     WRITE_SIZE, calibrated on a device copy), or None if the kernel sources changed
     since they were taken."""
     import re
     try:
-        text = open(os.path.join(ROOT, COUNTERS_SUMMARY)).read()
+        text = open(summary or os.path.join(ROOT, COUNTERS_SUMMARY)).read()
         if re.search(r"source_sha256_16: (\w+)", text).group(1) != _source_hash():
             return None
         return int(re.search(rf"traffic_bytes_per_launch\.{key}: (\d+)", text).group(1))
@@ -93,7 +93,7 @@ def _source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> str:
+def summarize_counters(fetch_csv: str, write_csv: str, out: str = None) -> str:
     """HBM bytes per launch of the decode kernels from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the bench's 2 GiB device copy
     (2 GiB read and 2 GiB written); writes COUNTERS_SUMMARY and returns its text."""
@@ -124,6 +124,8 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> str:
     known = 2 * 2 ** 30 / 1024
     cf, cw = copies(fetch_csv), copies(write_csv)
     ff, fw = known / cf, known / cw
+    if not (0.25 <= ff <= 8 and 0.25 <= fw <= 8):
+        raise SystemExit(f"calibration factors {ff:.4g}, {fw:.4g}: the 2 GiB device copies are missing")
     lines = [f"copy calibration: FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB for a 2 GiB device copy -> "
              f"factors fetch {ff:.4f}, write {fw:.4f}"]
     keys = []
@@ -155,7 +157,7 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> str:
         "Machine-readable (read by bench.py; valid only while the kernel sources hash to the value below, "
         "otherwise bench.py reports traffic as null):", "",
         f"    source_sha256_16: {h}", *["    " + k for k in keys], ""])
-    with open(os.path.join(ROOT, COUNTERS_SUMMARY), "w") as f:
+    with open(out or os.path.join(ROOT, COUNTERS_SUMMARY), "w") as f:
         f.write(text)
     return text
 

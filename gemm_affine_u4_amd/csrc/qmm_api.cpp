@@ -525,7 +525,8 @@ size_t qmm_step_plan_bytes(const qmm_step_proj* projs, int32_t n) {
   for (int32_t i = 0; i < n; ++i) {
     const qmm_step_proj& p = projs[i];
     if ((p.kind != QMM_STEP_LINEAR && p.kind != QMM_STEP_QKV && p.kind != QMM_STEP_GATE_UP_SWIGLU) ||
-        !qmm::k_ok(p.K) || p.K <= 512 || p.rows < 1 || p.rows > (int64_t(1) << 30))
+        p.wait_for < -1 || p.wait_for >= i || !qmm::k_ok(p.K) || p.K <= 512 || p.rows < 1 ||
+        p.rows > (int64_t(1) << 30))
       return 0;
   }
   return size_t(qmm::step::plan_bytes(projs, n));

@@ -352,8 +352,9 @@ typedef struct qmm_step_proj {
   int32_t reserved;        /* must be 0 */
 } qmm_step_proj;
 
-/* Device bytes of the plan of these n projections (0 if n is outside [1, 4096] or a
- * projection's kind or sizes cannot be planned).  Host only; reads kind, wait_for, K, rows. */
+/* Device bytes of the plan of these n projections (0 if n is outside [1, 4096], or a
+ * projection's kind, wait_for or sizes cannot be planned).  Host only; reads kind,
+ * wait_for, K, rows. */
 size_t qmm_step_plan_bytes(const qmm_step_proj* projs, int32_t n);
 
 /*

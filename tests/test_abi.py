@@ -273,6 +273,48 @@ def test_moe_layer_validation():
     assert _layer(h=A + (1 << 26) + 64) == S["QMM_ERR_ALIAS"]      # h over y
 
 
+def _proj(kind=1, wait_for=-1, K=1024, rows=96, q_out=64, kv_out=16, x=A, codes=A + (1 << 16), s=A + (1 << 18),
+          b=A + (1 << 19), lb=None, o0=A + (1 << 21), o1=A + (1 << 22), o2=A + (1 << 23), od=0, reserved=0):
+    return qmm.StepProj(kind, wait_for, K, rows, q_out, kv_out, x, codes, s, b, lb, o0, o1, o2, od, reserved)
+
+
+def _plan(projs, plan=A + (1 << 24), nbytes=1 << 20):
+    arr = (qmm.StepProj * len(projs))(*projs)
+    return qmm.load_library().qmm_step_plan(ctypes.cast(arr, ctypes.c_void_p), len(projs), plan, nbytes, None)
+
+
+def _run(projs, plan=A + (1 << 24)):
+    arr = (qmm.StepProj * len(projs))(*projs) if projs else None
+    return qmm.load_library().qmm_step_run(ctypes.cast(arr, ctypes.c_void_p) if arr else None, len(projs), plan,
+                                           None)
+
+
+def test_step_validation_before_any_device_call():
+    pb = qmm.qmm_step_plan_bytes
+    assert pb([_proj(kind=7)]) == 0
+    assert pb([_proj(K=512, rows=96)]) == 0 and pb([_proj(K=1000)]) == 0     # K > 512, a multiple of 64
+    assert pb([_proj(), _proj(wait_for=1)]) == 0                             # waits for itself
+    assert pb([_proj(wait_for=-2)]) == 0 and pb([_proj(rows=0)]) == 0
+    assert _plan([]) == S["QMM_ERR_SHAPE"]
+    assert _plan([_proj(kind=7)]) == S["QMM_ERR_ENUM"]
+    assert _plan([_proj(x=None)]) == S["QMM_ERR_NULL"]
+    assert _plan([_proj(o1=None)]) == S["QMM_ERR_NULL"]                        # QKV needs three outputs
+    assert _plan([_proj(od=5)]) == S["QMM_ERR_ENUM"]
+    assert _plan([_proj(reserved=1)]) == S["QMM_ERR_SHAPE"]
+    assert _plan([_proj(), _proj(wait_for=1)]) == S["QMM_ERR_SHAPE"]
+    assert _plan([_proj(q_out=60)]) == S["QMM_ERR_SHAPE"]                     # q + 2 kv != rows
+    assert _plan([_proj(kind=2, rows=97)]) == S["QMM_ERR_SHAPE"]              # gate+up rows even
+    assert _plan([_proj(kind=2, rows=96, lb=A + (1 << 20))]) == S["QMM_ERR_SHAPE"]  # no bias on gate+up
+    assert _plan([_proj(K=65536 * 2)]) == S["QMM_ERR_SHAPE"]
+    assert _plan([_proj(x=A + 8)]) == S["QMM_ERR_ALIGN"]
+    assert _plan([_proj(od=1, o0=A + (1 << 21) + 2)]) == S["QMM_ERR_ALIGN"]
+    assert _run([]) == S["QMM_ERR_NULL"]
+    assert _run([_proj(kind=9)]) == S["QMM_ERR_SHAPE"]
+    assert _run([_proj(), _proj(wait_for=3)]) == S["QMM_ERR_SHAPE"]
+    assert _run([_proj(codes=None)]) == S["QMM_ERR_NULL"]
+    assert _run([_proj()], plan=A + 64) == S["QMM_ERR_ALIGN"]
+
+
 # ---- host-only build of the validation code ------------------------------------
 
 @pytest.fixture(scope="module")
