@@ -24,7 +24,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 WIDTHS = (2, 3, 4, 6, 8)
 SOURCES = ([("qmm_api.cpp", [], "qmm_api.o"), ("qmm_validate.cpp", [], "qmm_validate.o"),
             ("moe_route.hip", [], "moe_route.o"), ("bmv_u4.hip", [], "bmv_u4.o"),
-            ("qmm_noalloc.hip", [], "qmm_noalloc.o"), ("gemv_step.hip", [], "gemv_step.o")]
+            ("qmm_noalloc.hip", [], "qmm_noalloc.o"), ("gemv_step.hip", [], "gemv_step.o"),
+            ("moe_gemm.hip", [], "moe_gemm.o")]
            + [(src, [f"-DQMM_BITS={b}"], f"{src.split('.')[0]}_b{b}.o") for src in ("gemv_u4.hip", "gemm_u4.hip")
               for b in WIDTHS]
            + [(src, ["-DQMM_BITS=8", "-DQMM_FP8=1"], f"{src.split('.')[0]}_f8.o")

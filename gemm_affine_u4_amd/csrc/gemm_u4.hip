@@ -53,7 +53,7 @@ constexpr int kRow = 64;                 // bf16 per LDS row (one 64-wide group)
 constexpr int kStage = kBM * kRow;       // bf16 per LDS stage (32 KB)
 constexpr int kXcds = 8;
 static_assert(kBM == kBN, "x and weight stages share one shape");
-static_assert(kBM == kMoeTileRows, "the routing tiles are GEMM tiles");
+static_assert(kMoeTileRows <= kBM, "a routing tile fits one GEMM tile");
 
 // Bank-group swizzle of LDS row r (see the header).
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     if (mt >= a.moe_hdr[0]) return;
     const int e = a.moe_tiles[2 * mt];
     pair_base = a.moe_tiles[2 * mt + 1];
-    rows_here = min(kBM, a.moe_offsets[e + 1] - pair_base);
+    rows_here = min(kMoeTileRows, a.moe_offsets[e + 1] - pair_base);
     const int64_t er = int64_t(e) * a.N;  // first row of the expert in the grid
     a.codes += er * ((a.K * kBits) >> 5);
     a.scales += er * (a.K >> (5 + a.gshift));

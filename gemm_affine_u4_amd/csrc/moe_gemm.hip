@@ -1,0 +1,476 @@
+// Routed experts over a batch of tokens (prefill): the two gathered projections of a layer
+// (gate+up+SwiGLU, then down) on the matrix cores, weight-stationary.
+//
+// The pages keep every expert's weights in place in the grid and pick experts by index
+// ("Four Candles for the Cathedral", what's not in this batch); prefill is matmul-bound
+// ("Sanctum-MLX", latency testing).  After bucketing, an expert of a 35B-A3B-shaped layer
+// holds a few dozen (token, slot) pairs, so its weights are large next to its activations:
+// the kernel is built so that each weight is read and dequantized exactly once per routing
+// tile, and the activations of the tile's pairs are what is shared through LDS.
+//
+// A block (4 waves) takes one routing tile (up to 128 pairs of one expert) and one slab of
+// 128 of the expert's weight rows, and walks K one 64-wide group per step:
+//   * each wave owns 32 weight rows and holds them, dequantized, as the A operand of
+//     v_mfma_f32_32x32x16_bf16: lane l reads 16 bytes (32 codes) of row l % 32 per step,
+//     half l / 32 of the group, and turns them into w = s*q + b in fp32, rounded to bf16
+//     (the same weights as the LDS-dequant GEMM), straight into registers;
+//   * the tile's activation rows (gathered through the bucket) go global -> LDS directly
+//     (buffer_load ... lds) two steps ahead, into a ring of three stages, and every wave
+//     reads them as the B operands of its multiplies: one 32 x 32 accumulator per 32 pairs.
+// Since MFMA lane l pairs k-slot 8 (l / 32) + t of A with the same slot of B, the slots of
+// a 16-wide multiply may stand for any 16 inputs of the group, as long as both operands
+// agree: multiply j takes inputs 32 h + 8 j .. +7 from the lanes of half h, so a lane's A
+// fragment for multiply j is one code word and its B fragment one 16-byte chunk of the row.
+// The number of 32-pair blocks of a tile (1..4) is a template parameter of the loop, so the
+// multiplies and the loads of a step are fixed and the wait counts are constants.
+#include <type_traits>
+#include <utility>
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace moe_mm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 4;                      // waves per block
+constexpr int kSlab = 32 * kWaves;             // weight rows per block
+constexpr int kMaxMB = kMoeTileRows / 32;      // 32-pair blocks per routing tile
+constexpr int kRow = 64;                       // bf16 per LDS row (one group of one pair)
+constexpr int kStage = kMoeTileRows * kRow;    // bf16 per activation stage
+constexpr int kXcds = 8;
+static_assert(kMaxMB >= 1 && kMaxMB <= 4, "one tile is at most 4 blocks of 32 pairs");
+#ifndef QMM_MOE_XDIST
+#define QMM_MOE_XDIST 1
+#endif
+#ifndef QMM_MOE_XSTAGES
+#define QMM_MOE_XSTAGES 2
+#endif
+#ifndef QMM_MOE_SDIST
+#define QMM_MOE_SDIST 4
+#endif
+// Steps ahead at which the activations (through LDS) and the scale and bias chunks (8
+// groups, into registers) are requested, and the ring the activations land in.  The codes
+// go through LDS too, two steps (64 bytes of a row) at a time, one such chunk ahead.
+constexpr int kXDist = QMM_MOE_XDIST;
+constexpr int kXStages = QMM_MOE_XSTAGES;
+constexpr int kSDist = QMM_MOE_SDIST;
+constexpr int kChunk = 8;                   // groups per scale/bias load (16 bytes)
+constexpr int kCodeSteps = 2;               // steps per code chunk
+constexpr int kCodeRow = 32 * kCodeSteps;   // bytes of one row in a code chunk
+constexpr int kCodeBuf = kSlab * kCodeRow;  // bytes per code chunk buffer (two buffers)
+static_assert(kXStages > kXDist && kXDist >= 1 && kXDist <= 2, "activation ring");
+static_assert(kSDist >= kXDist && kSDist <= kChunk, "request order the wait counts rely on");
+constexpr int gcd_(int a, int b) { return b == 0 ? a : gcd_(b, a % b); }
+constexpr int lcm_(int a, int b) { return a / gcd_(a, b) * b; }
+// steps until the activation ring, the code buffers and the scale chunks all repeat
+constexpr int kUnroll = lcm_(lcm_(kXStages, 2 * kCodeSteps), kChunk);
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Bank-group swizzle of LDS row r: slot c of row r holds the row's 16-byte chunk c ^ swz(r),
+// so the 32 rows one operand read spans (at one chunk) hit distinct bank groups.
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
+
+template <int n>
+__device__ __forceinline__ float ubyte_f32(uint32_t v) { return float((v >> (8 * n)) & 0xFFu); }
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and its LDS
+// reads are done, then meet the other waves (one asm block: the compiler's own barrier
+// would wait for the loads requested for later steps too).
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Codes 0..7 of word w (one per nibble, first code in the low nibble) as 8 bf16 weights
+// s*q + b (fp32 FMA, exact product, then RNE): one MFMA operand fragment.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float s, float b) {
+  const uint32_t lo = in_vgpr(w & 0x0F0F0F0Fu);
+  const uint32_t hi = in_vgpr((w >> 4) & 0x0F0F0F0Fu);
+  const u32x4_t v = {pack_bf16x2(fmaf(s, ubyte_f32<0>(lo), b), fmaf(s, ubyte_f32<0>(hi), b)),
+                     pack_bf16x2(fmaf(s, ubyte_f32<1>(lo), b), fmaf(s, ubyte_f32<1>(hi), b)),
+                     pack_bf16x2(fmaf(s, ubyte_f32<2>(lo), b), fmaf(s, ubyte_f32<2>(hi), b)),
+                     pack_bf16x2(fmaf(s, ubyte_f32<3>(lo), b), fmaf(s, ubyte_f32<3>(hi), b))};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Scales and biases of 8 consecutive groups of one row (bf16 pairs).
+struct ChunkRegs {
+  u32x4_t s, b;
+};
+// Scale and bias of one group (bf16 bits, zero-extended).
+struct GroupRegs {
+  uint32_t s, b;
+};
+
+// 4 consecutive outputs starting at element idx of dst: one vector store when all exist and
+// the address is aligned to it, else element stores.
+__device__ __forceinline__ void put4(void* dst, int64_t idx, const float (&v)[4], int nvalid, bool f32) {
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(dst) + uintptr_t(idx) * (f32 ? 4u : 2u);
+  if (nvalid == 4 && (addr & (f32 ? 15u : 7u)) == 0) {
+    if (f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(dst) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + idx) =
+          make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                     f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < nvalid) store_out(dst, idx + e, v[e], f32);
+  }
+}
+
+// Requests of step t (negative: before step 0), in this order: the activations of step
+// t + kXDist (MB wave instructions, 8 rows each), half of the code chunk of steps
+// 2 (t/2 + 1) .. +1 (one instruction), then SC8: on chunk steps the scale and bias chunk
+// of steps 8c .. 8c+7 (requested kSDist steps before step 8c); otherwise the scale and
+// bias of step t + 1.
+template <bool SC8>
+constexpr bool chunk_step(int t) { return SC8 && ((t + kSDist) % kChunk + kChunk) % kChunk == 0; }
+template <bool SC8>
+constexpr int tail_loads(int t) { return SC8 ? (chunk_step<SC8>(t) ? 2 : 0) : 2; }
+template <int MB, bool SC8>
+constexpr int step_loads(int t) { return MB + 1 + tail_loads<SC8>(t); }
+// At the top of step ks (position P in the unrolled loop; P and ks agree modulo 8) its
+// activations (requested at step ks - kXDist) and its code chunk (both halves, the later
+// one at step 2 floor(ks/2) - 1) must have landed; loads complete in order, so what may
+// still be outstanding is what was requested after the later of the two.
+template <int MB, bool SC8, int P>
+constexpr int wait_count() {
+  int after_x = 1 + tail_loads<SC8>(P - kXDist);
+  for (int u = P - kXDist + 1; u < P; ++u) after_x += step_loads<MB, SC8>(u);
+  const int u0 = (P % 2 == 0) ? P - 1 : P - 2;
+  int after_c = tail_loads<SC8>(u0);
+  for (int u = u0 + 1; u < P; ++u) after_c += step_loads<MB, SC8>(u);
+  return after_x < after_c ? after_x : after_c;
+}
+
+// Where a block's work sits: its routing tile and weight slab.
+struct TileJob {
+  int e;          // expert
+  int pair_base;  // first bucket position of the tile
+  int P;          // pairs in the tile (1 .. kMoeTileRows)
+  int slab;       // weight slab
+};
+
+// The tile loop for a tile of MB blocks of 32 pairs.  SC8: the scales and biases are read
+// 8 groups (16 bytes) at a time, which needs rows of a multiple of 8 groups (K % 512 == 0)
+// for alignment; otherwise one group per step.
+template <int EPI, int MB, bool SC8>
+__device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, uint16_t* xs_all,
+                                          unsigned char* cs_all) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t K = uint32_t(a.K);
+  const int ksteps = int(K >> 6);
+  const int last = ksteps - 1;
+  const uint32_t groups = K >> 6;
+  const int m = lane & 31;  // A row (weight row of the wave) and B column (pair of a block)
+  const int h = lane >> 5;  // half of the group this lane's k-slots cover
+
+  // ---- weight rows ------------------------------------------------------------------
+  // SwiGLU: the wave's 32 A rows are 16 gate rows and their 16 up rows, A row r being gate
+  // (bit 3 of r clear) or up (set) of h index i0 + 8 (r >> 4) + (r & 7); an accumulator's
+  // registers 8g + e and 8g + 4 + e (e < 4) then hold gate and up of one index.
+  // Linear: A row r is weight row slab*128 + 32 wave + r.  Rows past the end read the last
+  // row (their outputs are never stored).
+  auto weight_row = [&](int r) -> int64_t {
+    if constexpr (EPI == EPI_SWIGLU) {
+      int64_t i = int64_t(jb.slab) * (kSlab / 2) + 16 * wave + 8 * (r >> 4) + (r & 7);
+      if (i >= a.I) i = a.I - 1;
+      return ((r >> 3) & 1) ? a.I + i : i;
+    } else {
+      const int64_t n = int64_t(jb.slab) * kSlab + 32 * wave + r;
+      return n < a.N ? n : a.N - 1;
+    }
+  };
+  const int64_t er = int64_t(jb.e) * a.N;  // first row of the expert in the grid
+  const uint64_t nrows = uint64_t(a.N);
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.codes + er * (K >> 3), nrows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales + er * groups, nrows * groups * 2);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases + er * groups, nrows * groups * 2);
+  const uint32_t goff = uint32_t(weight_row(m)) * groups * 2u;  // the lane's row's scales
+
+  // Codes: global -> LDS, a chunk of two steps (64 bytes of a row) at a time, into two
+  // buffers of the block's 128 rows x 64 bytes.  At step t a wave requests half (rows
+  // 16 (t % 2) .. +15 of its 32) of chunk t/2 + 1: lane L takes row 16 (t % 2) + L / 4 and
+  // lands in slot L % 4 of it, which holds the row's 16-byte piece (L % 4) ^ cswz(row), so
+  // that the 16 rows an operand read spans (at one piece) hit distinct bank groups.  A wave
+  // only ever reads its own rows.
+  auto cswz = [](uint32_t r) -> uint32_t { return (r >> 2) & 3u; };
+  uint32_t cdoff[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 16 * hh + (lane >> 2);
+    const uint32_t piece = uint32_t(lane & 3) ^ cswz(uint32_t(32 * wave + r));
+    cdoff[hh] = uint32_t(weight_row(r)) * (K >> 1) + piece * 16u;
+  }
+  auto load_codes = [&](int t) {  // t >= -2
+    const int hh = (t + 2) & 1;
+    const int c = min((t + 2) >> 1, last >> 1);
+    unsigned char* dst = cs_all + (c & 1) * kCodeBuf + (32 * wave + 16 * hh) * kCodeRow;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (__attribute__((address_space(3))) void*)dst, 16, cdoff[hh],
+                                             uint32_t(c) * uint32_t(kCodeRow), 0, 0);
+  };
+  // the lane's 16 bytes of step ks: row 32 wave + m, piece 2 (ks % 2) + h
+  const uint32_t crow = uint32_t(32 * wave + m);
+  auto read_codes = [&](int ks) -> u32x4_t {
+    const uint32_t piece = uint32_t(2 * (ks & 1) + h) ^ cswz(crow);
+    return *reinterpret_cast<const u32x4_t*>(cs_all + ((ks >> 1) & 1) * kCodeBuf + crow * kCodeRow + piece * 16u);
+  };
+  const int last_chunk = int(groups / kChunk) - 1;
+  auto load_chunk = [&](ChunkRegs& r, int c) {
+    r.s = __builtin_amdgcn_raw_buffer_load_b128(sr, goff + uint32_t(c) * 16u, 0, 0);
+    r.b = __builtin_amdgcn_raw_buffer_load_b128(br, goff + uint32_t(c) * 16u, 0, 0);
+  };
+  auto load_group = [&](GroupRegs& r, int g) {
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(sr, goff + uint32_t(g) * 2u, 0, 0);
+    r.b = __builtin_amdgcn_raw_buffer_load_b16(br, goff + uint32_t(g) * 2u, 0, 0);
+  };
+
+  // ---- the tile's activation rows: global -> LDS ------------------------------------
+  // Instruction j (j < MB) of wave w fills LDS rows 8 (MB w + j) + L / 8, slot L % 8 (lane
+  // L lands at byte 16 L), i.e. chunk (L % 8) ^ swz(row) of that pair's row.  Rows past the
+  // tile's pairs read its last pair (never stored).
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint64_t(a.M) * K * 2);
+  uint32_t xoff[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int r = 8 * (MB * wave + j) + (lane >> 3);
+    const int64_t xrow = a.moe_pairs[jb.pair_base + min(r, jb.P - 1)] / a.moe_div;
+    const uint32_t chunk = uint32_t(lane & 7) ^ swz(uint32_t(r));
+    xoff[j] = uint32_t(xrow) * K * 2u + chunk * 16u;
+  }
+  auto stage = [&](int p) -> uint16_t* { return xs_all + p * kStage; };
+  auto load_x = [&](uint16_t* dst, int ks) {
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (__attribute__((address_space(3))) void*)(dst + 8 * (MB * wave + j) * kRow), 16, xoff[j],
+          uint32_t(ks) * 128u, 0, 0);
+  };
+
+  // B operand of multiply j for block b: row 32 b + m, chunk 4 h + j (swz(32 b + m) = swz(m))
+  uint32_t boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) boff[j] = uint32_t(m) * kRow + ((uint32_t(4 * h + j) ^ swz(uint32_t(m))) * 8u);
+
+  f32x16_t acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = f32x16_t{};
+
+  // Step ks: activations in stage ks % kXStages, codes in code buffer (ks / 2) % 2, scale
+  // and bias in chunk `cur` (SC8) or in group set ks % 2.  After the barrier at its top
+  // (every wave is done with the previous step) the stage read kXStages - kXDist steps back
+  // takes the activations of step ks + kXDist and the code buffer of the previous chunk
+  // takes half of the next chunk; at the first step of a scale chunk the chunk requested
+  // kSDist steps back becomes `cur`.  Requested steps and chunks are clamped to the last
+  // one, so every step issues the loads the wait counts assume (the extra copies are never
+  // read).
+  ChunkRegs cur, next;
+  GroupRegs G[2];
+  auto requests = [&](int t, auto p_c) {
+    constexpr int P = decltype(p_c)::value;  // t's position modulo kUnroll (t may be < 0)
+    if (t + kXDist >= 0) load_x(stage((P + kXDist) % kXStages), min(t + kXDist, last));
+    __builtin_amdgcn_sched_barrier(0);  // the wait counts need this order
+    if (t >= -2) load_codes(t);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SC8) {
+      if constexpr (chunk_step<SC8>(P)) {
+        if (t + kSDist >= 0) load_chunk(next, min((t + kSDist) / kChunk, last_chunk));
+      }
+    } else {
+      if (t + 1 >= 0) load_group(G[(P + 1) & 1], min(t + 1, last));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto step = [&](int ks, auto p_c) {
+    constexpr int P = decltype(p_c)::value;
+    constexpr int kWait = wait_count<MB, SC8, P>();
+    wait_loads_barrier<kWait>();
+    if constexpr (SC8 && P % kChunk == 0) {
+      // taken here and not before, or the compiler may wait for the chunk right after
+      // requesting it
+      asm volatile("" : "+v"(next.s), "+v"(next.b));
+      cur = next;
+    }
+    const u32x4_t codes = read_codes(ks);
+    requests(ks, p_c);
+    float s, bb;
+    if constexpr (SC8) {
+      constexpr int i = P % kChunk;
+      const uint32_t sw = cur.s[i / 2], bw = cur.b[i / 2];
+      s = __uint_as_float((i & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+      bb = __uint_as_float((i & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+    } else {
+      GroupRegs& g = G[P & 1];
+      asm volatile("" : "+v"(g.s), "+v"(g.b));
+      s = __uint_as_float(g.s << 16);
+      bb = __uint_as_float(g.b << 16);
+    }
+    const uint16_t* xs = stage(P % kXStages);
+    // multiply j: its B fragments were read and its A fragment dequantized in phase j - 1
+    bf16x8_t xb[2][MB];
+    bf16x8_t wa[2];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) xb[0][b] = *reinterpret_cast<const bf16x8_t*>(xs + 32 * b * kRow + boff[0]);
+    wa[0] = dequant8(codes[0], s, bb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < 3) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          xb[(j + 1) & 1][b] = *reinterpret_cast<const bf16x8_t*>(xs + 32 * b * kRow + boff[j + 1]);
+        wa[(j + 1) & 1] = dequant8(codes[j + 1], s, bb);
+      }
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[j & 1], xb[j & 1][b], acc[b], 0, 0, 0);
+      // Order inside the phase: the next fragments' LDS reads first (their latency runs
+      // under the multiplies), then each multiply followed by a share of the next
+      // dequantization (~23 VALU ops), which issues while the multiply executes.
+      if (j < 3) {
+        __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (24 + MB - 1) / MB, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue: the requests of the steps before step 0, as those steps would have made them
+  // (so the wait counts hold from the first step on).
+  constexpr int kLead = SC8 ? kSDist : 2;
+  static_for<kLead>([&](auto tc) {
+    constexpr int t = decltype(tc)::value - kLead;  // -kLead .. -1
+    requests(t, std::integral_constant<int, ((t % kUnroll) + kUnroll) % kUnroll>{});
+  });
+  int ks = 0;
+  for (; ks + kUnroll <= ksteps; ks += kUnroll)
+    static_for<kUnroll>([&](auto pc) { step(ks + decltype(pc)::value, pc); });
+  static_for<kUnroll - 1>([&](auto pc) {
+    if (ks + decltype(pc)::value < ksteps) step(ks + decltype(pc)::value, pc);
+  });
+  // The copies requested past the last step are never read; without a use the compiler
+  // drops those loads, and the wait counts above, which count every step's loads, would no
+  // longer cover the activations.  The clamped extra LDS loads still write this block's LDS:
+  // let everything land before the block exits.
+  if constexpr (SC8) asm volatile("" ::"v"(next.s), "v"(next.b));
+  else asm volatile("" ::"v"(G[0].s), "v"(G[0].b), "v"(G[1].s), "v"(G[1].b));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue ---------------------------------------------------------------------
+  // Register 4g + e (g < 4, e < 4) of acc[b] in lane l holds A row 8g + 4h + e of the
+  // wave against pair 32 b + m of the tile.
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int q = 32 * b + m;
+    if (q >= jb.P) continue;
+    const int64_t pr = a.moe_pairs[jb.pair_base + q];
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int64_t i0 = int64_t(jb.slab) * (kSlab / 2) + 16 * wave + 8 * g + 4 * h;
+        if (i0 >= a.I) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[b][8 * g + e], acc[b][8 * g + 4 + e]);
+        put4(a.out0, pr * a.I + i0, v, int(min<int64_t>(4, a.I - i0)), a.f32_out);
+      }
+    } else {
+      const float sc = a.moe_w ? a.moe_w[pr] : 1.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n0 = int64_t(jb.slab) * kSlab + 32 * wave + 8 * g + 4 * h;
+        if (n0 >= a.N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = acc[b][4 * g + e] * sc + ((a.lin_bias && n0 + e < a.N) ? bf16_bits_to_f32(a.lin_bias[n0 + e]) : 0.f);
+        put4(a.out0, pr * a.N + n0, v, int(min<int64_t>(4, a.N - n0)), a.f32_out);
+      }
+    }
+  }
+}
+
+// Block order: the table's tiles x slabs, in that order, cut into 8 equal contiguous ranges,
+// range x for the blocks dealt to XCD x (blocks go to the XCDs round-robin): an XCD takes
+// every slab of a run of tiles, so a tile's activation rows stay in its L2, and the tiles
+// actually routed (known on the device only) spread over all eight.
+template <int EPI>
+__global__ void __launch_bounds__(256, 3) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
+  __shared__ __attribute__((aligned(1024))) uint16_t xs[kXStages * kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char cs[2 * kCodeBuf];
+  const int64_t total = int64_t(a.moe_hdr[0]) * slabs;
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t j = blockIdx.x / kXcds;
+  if (j >= per_xcd) return;
+  const int64_t t = int64_t(blockIdx.x % kXcds) * per_xcd + j;
+  if (t >= total) return;
+  TileJob jb;
+  const int64_t tile = t / slabs;
+  jb.slab = int(t - tile * slabs);
+  jb.e = a.moe_tiles[2 * tile];
+  jb.pair_base = a.moe_tiles[2 * tile + 1];
+  jb.P = __builtin_amdgcn_readfirstlane(min(kMoeTileRows, a.moe_offsets[jb.e + 1] - jb.pair_base));
+  if ((a.K >> 6) % kChunk == 0) {
+    switch ((jb.P + 31) >> 5) {
+      case 1: tile_body<EPI, 1, true>(a, jb, xs, cs); break;
+      case 2: tile_body<EPI, 2, true>(a, jb, xs, cs); break;
+      case 3: tile_body<EPI, 3, true>(a, jb, xs, cs); break;
+      default: tile_body<EPI, 4, true>(a, jb, xs, cs); break;
+    }
+  } else {
+    switch ((jb.P + 31) >> 5) {
+      case 1: tile_body<EPI, 1, false>(a, jb, xs, cs); break;
+      case 2: tile_body<EPI, 2, false>(a, jb, xs, cs); break;
+      case 3: tile_body<EPI, 3, false>(a, jb, xs, cs); break;
+      default: tile_body<EPI, 4, false>(a, jb, xs, cs); break;
+    }
+  }
+}
+
+}  // namespace moe_mm
+
+bool moe_gemm_supports(const GemmArgs& a) {
+  // group 64, K a whole number of groups, and every buffer offset in 32 bits
+  const uint64_t K = uint64_t(a.K);
+  return K >= 64 && K % 64 == 0 && uint64_t(a.M) * K * 2u < 0xFFFFFFF0ull &&
+         uint64_t(a.N) * K / 2u < 0xFFFFFFF0ull && a.N >= 1;
+}
+
+int launch_moe_gemm(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
+  const int64_t slabs = epi == EPI_SWIGLU ? (a.I + moe_mm::kSlab / 2 - 1) / (moe_mm::kSlab / 2)
+                                          : (a.N + moe_mm::kSlab - 1) / moe_mm::kSlab;
+  const int64_t blocks = (m_tiles * slabs + moe_mm::kXcds - 1) / moe_mm::kXcds * moe_mm::kXcds;
+  if (blocks > 0x7FFFFFFF) return 2;
+  const dim3 grid{unsigned(blocks), 1u, 1u};
+  const dim3 block{unsigned(64 * moe_mm::kWaves), 1u, 1u};
+  if (epi == EPI_SWIGLU) {
+    moe_mm::moe_gemm_kernel<EPI_SWIGLU><<<grid, block, 0, s>>>(a, slabs);
+  } else if (epi == EPI_LINEAR) {
+    moe_mm::moe_gemm_kernel<EPI_LINEAR><<<grid, block, 0, s>>>(a, slabs);
+  } else {
+    return 5;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+}  // namespace qmm

@@ -277,6 +277,9 @@ int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, voi
 #ifndef QMM_MOE_BMV
 #define QMM_MOE_BMV 1
 #endif
+#ifndef QMM_MOE_MM
+#define QMM_MOE_MM 1
+#endif
 // The gathered stages on the small-batch kernel (passes of up to 32 pairs of one expert,
 // each streaming the expert's rows) while experts average at most 24 pairs (stage 1) or
 // 40 pairs (stage 2, whose K = I is short), else on the gathered GEMM (256-pair tiles).
@@ -310,6 +313,7 @@ static int launch_moe_stage(int epi, const GemmArgs& a, int64_t x_rows, int64_t 
       return launch_bmv_moe(epi, v, gth, tmax, upb, s);
     }
   }
+  if (QMM_MOE_MM && moe_gemm_supports(a)) return launch_moe_gemm(epi, a, tmax, s);
   return b4::launch_gemm_moe(epi, a, tmax, s);
 }
 

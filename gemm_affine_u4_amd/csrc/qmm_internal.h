@@ -134,6 +134,10 @@ QMM_WIDTH_LAUNCHERS(f8)
 namespace b4 {
 int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
 }
+// The weight-stationary gathered kernel of the same stages (moe_gemm.hip): each block one
+// routing tile x one slab of 128 expert rows (SWIGLU: 64 gate + their 64 up rows).
+bool moe_gemm_supports(const GemmArgs& a);
+int launch_moe_gemm(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
 
 
 
@@ -192,7 +196,7 @@ int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_til
 
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
-constexpr int kMoeTileRows = 256;        // pairs per gathered GEMM tile (the GEMM's kBM)
+constexpr int kMoeTileRows = 128;        // pairs per routing tile
 constexpr int kMaxExpertsPrefill = 4096; // experts the bucketing handles (LDS histogram)
 struct MoeLayout {
   int64_t P, tmax, chunk_pairs, chunks;  // pairs, bound on tiles, pairs per routing chunk, chunks
