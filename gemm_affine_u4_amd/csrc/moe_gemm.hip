@@ -39,7 +39,6 @@ constexpr int kWaves = 4;                      // waves per block
 constexpr int kSlab = 32 * kWaves;             // weight rows per block
 constexpr int kMaxMB = kMoeTileRows / 32;      // 32-pair blocks per routing tile
 constexpr int kRow = 64;                       // bf16 per LDS row (one group of one pair)
-constexpr int kStage = kMoeTileRows * kRow;    // bf16 per activation stage
 constexpr int kXcds = 8;
 static_assert(kMaxMB >= 1 && kMaxMB <= 4, "one tile is at most 4 blocks of 32 pairs");
 #ifndef QMM_MOE_XDIST
@@ -47,6 +46,9 @@ static_assert(kMaxMB >= 1 && kMaxMB <= 4, "one tile is at most 4 blocks of 32 pa
 #endif
 #ifndef QMM_MOE_XSTAGES
 #define QMM_MOE_XSTAGES 2
+#endif
+#ifndef QMM_MOE_MIX
+#define QMM_MOE_MIX 1
 #endif
 #ifndef QMM_MOE_SDIST
 #define QMM_MOE_SDIST 4
@@ -60,13 +62,19 @@ constexpr int kSDist = QMM_MOE_SDIST;
 constexpr int kChunk = 8;                   // groups per scale/bias load (16 bytes)
 constexpr int kCodeSteps = 2;               // steps per code chunk
 constexpr int kCodeRow = 32 * kCodeSteps;   // bytes of one row in a code chunk
-constexpr int kCodeBuf = kSlab * kCodeRow;  // bytes per code chunk buffer (two buffers)
+constexpr int kCodeBuf = kSlab * kCodeRow;  // bytes per code chunk buffer
+// LDS of a block: the activation stages (MB * 4 KB each) and the code chunk ring, whose depth
+// depends on the tile: 4 chunks (requested 5-6 steps ahead) where the stages leave room, else 2.
+constexpr int kLds = 48 * 1024;
+template <int MB>
+constexpr int code_chunks() { return kXStages * MB * 32 * kRow * 2 + 4 * kCodeBuf <= kLds ? 4 : 2; }
 static_assert(kXStages > kXDist && kXDist >= 1 && kXDist <= 2, "activation ring");
+static_assert(kXStages * kMaxMB * 32 * kRow * 2 + 2 * kCodeBuf <= kLds, "LDS of the largest tile");
 static_assert(kSDist >= kXDist && kSDist <= kChunk, "request order the wait counts rely on");
 constexpr int gcd_(int a, int b) { return b == 0 ? a : gcd_(b, a % b); }
 constexpr int lcm_(int a, int b) { return a / gcd_(a, b) * b; }
 // steps until the activation ring, the code buffers and the scale chunks all repeat
-constexpr int kUnroll = lcm_(lcm_(kXStages, 2 * kCodeSteps), kChunk);
+constexpr int kUnroll = lcm_(lcm_(kXStages, 4 * kCodeSteps), kChunk);
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
 template <typename F, int... I>
@@ -105,6 +113,24 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float s, float b) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// The same 8 weights from fp16 code pairs: nibbles t and t + 4 of w go into the mantissa of
+// the fp16 pair 1024 + q (0x6400 | q, exact), and one v_fma_mix_f32 per code gives
+// s * (1024 + q) + (b - 1024 s) in fp32, which is s*q + b rounded once, as above, whenever
+// b - 1024 s is exact in fp32 (b = 0 or |b| >= about |s| / 64; otherwise it differs from it
+// by at most |s| * 2^-14).  19 VALU ops per 8 codes instead of 23.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8_t dequant8_mix(uint32_t w, float s, float b1024, uint32_t nib, uint32_t magic) {
+  f16x2_t d[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) d[t] = __builtin_bit_cast(f16x2_t, ((w >> (4 * t)) & nib) | magic);
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) f[k] = fmaf(s, float(d[k % 4][k / 4]), b1024);
+  const u32x4_t v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // Scales and biases of 8 consecutive groups of one row (bf16 pairs).
 struct ChunkRegs {
   u32x4_t s, b;
@@ -135,7 +161,7 @@ __device__ __forceinline__ void put4(void* dst, int64_t idx, const float (&v)[4]
 
 // Requests of step t (negative: before step 0), in this order: the activations of step
 // t + kXDist (MB wave instructions, 8 rows each), half of the code chunk of steps
-// 2 (t/2 + 1) .. +1 (one instruction), then SC8: on chunk steps the scale and bias chunk
+// 2 (t/2 + NC - 1) .. +1 (one instruction), then SC8: on chunk steps the scale and bias chunk
 // of steps 8c .. 8c+7 (requested kSDist steps before step 8c); otherwise the scale and
 // bias of step t + 1.
 template <bool SC8>
@@ -150,9 +176,11 @@ constexpr int step_loads(int t) { return MB + 1 + tail_loads<SC8>(t); }
 // still be outstanding is what was requested after the later of the two.
 template <int MB, bool SC8, int P>
 constexpr int wait_count() {
+  constexpr int NC = code_chunks<MB>();
   int after_x = 1 + tail_loads<SC8>(P - kXDist);
   for (int u = P - kXDist + 1; u < P; ++u) after_x += step_loads<MB, SC8>(u);
-  const int u0 = (P % 2 == 0) ? P - 1 : P - 2;
+  // chunk c = floor(P/2) is requested at steps 2 (c - NC + 1) and 2 (c - NC + 1) + 1
+  const int u0 = 2 * (P >> 1) - 2 * NC + 3;
   int after_c = tail_loads<SC8>(u0);
   for (int u = u0 + 1; u < P; ++u) after_c += step_loads<MB, SC8>(u);
   return after_x < after_c ? after_x : after_c;
@@ -170,8 +198,12 @@ struct TileJob {
 // 8 groups (16 bytes) at a time, which needs rows of a multiple of 8 groups (K % 512 == 0)
 // for alignment; otherwise one group per step.
 template <int EPI, int MB, bool SC8>
-__device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, uint16_t* xs_all,
-                                          unsigned char* cs_all) {
+__device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, unsigned char* lds) {
+  constexpr int NC = code_chunks<MB>();
+  constexpr int kXStageBytes = MB * 32 * kRow * 2;
+  static_assert(kXStages * kXStageBytes + NC * kCodeBuf <= kLds, "LDS of the tile");
+  uint16_t* xs_all = reinterpret_cast<uint16_t*>(lds);
+  unsigned char* cs_all = lds + kXStages * kXStageBytes;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,9 +237,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.biases + er * groups, nrows * groups * 2);
   const uint32_t goff = uint32_t(weight_row(m)) * groups * 2u;  // the lane's row's scales
 
-  // Codes: global -> LDS, a chunk of two steps (64 bytes of a row) at a time, into two
-  // buffers of the block's 128 rows x 64 bytes.  At step t a wave requests half (rows
-  // 16 (t % 2) .. +15 of its 32) of chunk t/2 + 1: lane L takes row 16 (t % 2) + L / 4 and
+  // Codes: global -> LDS, a chunk of two steps (64 bytes of a row) at a time, into a ring of
+  // NC buffers of the block's 128 rows x 64 bytes.  At step t a wave requests half (rows
+  // 16 (t % 2) .. +15 of its 32) of chunk t/2 + NC - 1: lane L takes row 16 (t % 2) + L / 4 and
   // lands in slot L % 4 of it, which holds the row's 16-byte piece (L % 4) ^ cswz(row), so
   // that the 16 rows an operand read spans (at one piece) hit distinct bank groups.  A wave
   // only ever reads its own rows.
@@ -219,10 +251,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
     const uint32_t piece = uint32_t(lane & 3) ^ cswz(uint32_t(32 * wave + r));
     cdoff[hh] = uint32_t(weight_row(r)) * (K >> 1) + piece * 16u;
   }
-  auto load_codes = [&](int t) {  // t >= -2
-    const int hh = (t + 2) & 1;
-    const int c = min((t + 2) >> 1, last >> 1);
-    unsigned char* dst = cs_all + (c & 1) * kCodeBuf + (32 * wave + 16 * hh) * kCodeRow;
+  auto load_codes = [&](int t) {  // t >= -2 (NC - 1)
+    const int hh = t & 1;
+    const int c = min((t + 2 * (NC - 1)) >> 1, last >> 1);
+    unsigned char* dst = cs_all + (c % NC) * kCodeBuf + (32 * wave + 16 * hh) * kCodeRow;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (__attribute__((address_space(3))) void*)dst, 16, cdoff[hh],
                                              uint32_t(c) * uint32_t(kCodeRow), 0, 0);
   };
@@ -230,7 +262,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   const uint32_t crow = uint32_t(32 * wave + m);
   auto read_codes = [&](int ks) -> u32x4_t {
     const uint32_t piece = uint32_t(2 * (ks & 1) + h) ^ cswz(crow);
-    return *reinterpret_cast<const u32x4_t*>(cs_all + ((ks >> 1) & 1) * kCodeBuf + crow * kCodeRow + piece * 16u);
+    return *reinterpret_cast<const u32x4_t*>(cs_all + ((ks >> 1) % NC) * kCodeBuf + crow * kCodeRow + piece * 16u);
   };
   const int last_chunk = int(groups / kChunk) - 1;
   auto load_chunk = [&](ChunkRegs& r, int c) {
@@ -255,7 +287,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
     const uint32_t chunk = uint32_t(lane & 7) ^ swz(uint32_t(r));
     xoff[j] = uint32_t(xrow) * K * 2u + chunk * 16u;
   }
-  auto stage = [&](int p) -> uint16_t* { return xs_all + p * kStage; };
+  auto stage = [&](int p) -> uint16_t* { return xs_all + p * (kXStageBytes / 2); };
   auto load_x = [&](uint16_t* dst, int ks) {
 #pragma unroll
     for (int j = 0; j < MB; ++j)
@@ -272,22 +304,23 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   f32x16_t acc[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) acc[b] = f32x16_t{};
+  const uint32_t nib = in_vgpr(0x000F000Fu), magic = in_vgpr(0x64006400u);
 
-  // Step ks: activations in stage ks % kXStages, codes in code buffer (ks / 2) % 2, scale
+  // Step ks: activations in stage ks % kXStages, codes in code buffer (ks / 2) % NC, scale
   // and bias in chunk `cur` (SC8) or in group set ks % 2.  After the barrier at its top
   // (every wave is done with the previous step) the stage read kXStages - kXDist steps back
-  // takes the activations of step ks + kXDist and the code buffer of the previous chunk
-  // takes half of the next chunk; at the first step of a scale chunk the chunk requested
-  // kSDist steps back becomes `cur`.  Requested steps and chunks are clamped to the last
-  // one, so every step issues the loads the wait counts assume (the extra copies are never
-  // read).
+  // takes the activations of step ks + kXDist, and the code buffer read by the previous
+  // chunk takes half of chunk ks/2 + NC - 1; at the first step of a scale chunk the chunk
+  // requested kSDist steps back becomes `cur`.  Requested steps and chunks are clamped to
+  // the last one, so every step issues the loads the wait counts assume (the extra copies
+  // are never read, or rewrite a buffer with the bytes it already holds).
   ChunkRegs cur, next;
   GroupRegs G[2];
   auto requests = [&](int t, auto p_c) {
     constexpr int P = decltype(p_c)::value;  // t's position modulo kUnroll (t may be < 0)
     if (t + kXDist >= 0) load_x(stage((P + kXDist) % kXStages), min(t + kXDist, last));
     __builtin_amdgcn_sched_barrier(0);  // the wait counts need this order
-    if (t >= -2) load_codes(t);
+    if (t >= -2 * (NC - 1)) load_codes(t);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SC8) {
       if constexpr (chunk_step<SC8>(P)) {
@@ -328,14 +361,20 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
     bf16x8_t wa[2];
 #pragma unroll
     for (int b = 0; b < MB; ++b) xb[0][b] = *reinterpret_cast<const bf16x8_t*>(xs + 32 * b * kRow + boff[0]);
-    wa[0] = dequant8(codes[0], s, bb);
+#if QMM_MOE_MIX
+    const float b1024 = fmaf(-1024.f, s, bb);
+#define QMM_DEQ(w) dequant8_mix(w, s, b1024, nib, magic)
+#else
+#define QMM_DEQ(w) dequant8(w, s, bb)
+#endif
+    wa[0] = QMM_DEQ(codes[0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j < 3) {
 #pragma unroll
         for (int b = 0; b < MB; ++b)
           xb[(j + 1) & 1][b] = *reinterpret_cast<const bf16x8_t*>(xs + 32 * b * kRow + boff[j + 1]);
-        wa[(j + 1) & 1] = dequant8(codes[j + 1], s, bb);
+        wa[(j + 1) & 1] = QMM_DEQ(codes[j + 1]);
       }
 #pragma unroll
       for (int b = 0; b < MB; ++b)
@@ -355,9 +394,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
     }
   };
 
+#undef QMM_DEQ
   // Prologue: the requests of the steps before step 0, as those steps would have made them
   // (so the wait counts hold from the first step on).
-  constexpr int kLead = SC8 ? kSDist : 2;
+  constexpr int kLead = (SC8 && kSDist > 2 * (NC - 1)) ? kSDist : 2 * (NC - 1);
   static_for<kLead>([&](auto tc) {
     constexpr int t = decltype(tc)::value - kLead;  // -kLead .. -1
     requests(t, std::integral_constant<int, ((t % kUnroll) + kUnroll) % kUnroll>{});
@@ -410,14 +450,23 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   }
 }
 
+// The tile loop instance for the tile's number of 32-pair blocks.
+template <int EPI, bool SC8>
+__device__ __forceinline__ void run_tile(const GemmArgs& a, const TileJob& jb, unsigned char* lds) {
+  const int mb = (jb.P + 31) >> 5;
+  if (kMaxMB <= 1 || mb <= 1) tile_body<EPI, 1, SC8>(a, jb, lds);
+  else if (kMaxMB <= 2 || mb == 2) tile_body<EPI, (kMaxMB < 2 ? 1 : 2), SC8>(a, jb, lds);
+  else if (kMaxMB <= 3 || mb == 3) tile_body<EPI, (kMaxMB < 3 ? 1 : 3), SC8>(a, jb, lds);
+  else tile_body<EPI, (kMaxMB < 4 ? 1 : 4), SC8>(a, jb, lds);
+}
+
 // Block order: the table's tiles x slabs, in that order, cut into 8 equal contiguous ranges,
 // range x for the blocks dealt to XCD x (blocks go to the XCDs round-robin): an XCD takes
 // every slab of a run of tiles, so a tile's activation rows stay in its L2, and the tiles
 // actually routed (known on the device only) spread over all eight.
 template <int EPI>
 __global__ void __launch_bounds__(256, 3) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[kXStages * kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char cs[2 * kCodeBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
   const int64_t total = int64_t(a.moe_hdr[0]) * slabs;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const int64_t j = blockIdx.x / kXcds;
@@ -431,19 +480,9 @@ __global__ void __launch_bounds__(256, 3) moe_gemm_kernel(GemmArgs a, int64_t sl
   jb.pair_base = a.moe_tiles[2 * tile + 1];
   jb.P = __builtin_amdgcn_readfirstlane(min(kMoeTileRows, a.moe_offsets[jb.e + 1] - jb.pair_base));
   if ((a.K >> 6) % kChunk == 0) {
-    switch ((jb.P + 31) >> 5) {
-      case 1: tile_body<EPI, 1, true>(a, jb, xs, cs); break;
-      case 2: tile_body<EPI, 2, true>(a, jb, xs, cs); break;
-      case 3: tile_body<EPI, 3, true>(a, jb, xs, cs); break;
-      default: tile_body<EPI, 4, true>(a, jb, xs, cs); break;
-    }
+    run_tile<EPI, true>(a, jb, lds);
   } else {
-    switch ((jb.P + 31) >> 5) {
-      case 1: tile_body<EPI, 1, false>(a, jb, xs, cs); break;
-      case 2: tile_body<EPI, 2, false>(a, jb, xs, cs); break;
-      case 3: tile_body<EPI, 3, false>(a, jb, xs, cs); break;
-      default: tile_body<EPI, 4, false>(a, jb, xs, cs); break;
-    }
+    run_tile<EPI, false>(a, jb, lds);
   }
 }
 

@@ -196,7 +196,10 @@ int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_til
 
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
-constexpr int kMoeTileRows = 128;        // pairs per routing tile
+#ifndef QMM_MOE_TILE_ROWS
+#define QMM_MOE_TILE_ROWS 128
+#endif
+constexpr int kMoeTileRows = QMM_MOE_TILE_ROWS;  // pairs per routing tile (a multiple of 32, <= 128)
 constexpr int kMaxExpertsPrefill = 4096; // experts the bucketing handles (LDS histogram)
 struct MoeLayout {
   int64_t P, tmax, chunk_pairs, chunks;  // pairs, bound on tiles, pairs per routing chunk, chunks
