@@ -870,7 +870,7 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
             "small_batches": {"note": "route + both stages per layer for the first M tokens of the same "
                                       "routing; M * topk <= 448 runs pair by pair, up to 24 pairs per expert "
                                       "(stage 2: 40) on the gathered small-batch kernel, above on the "
-                                      "gathered GEMM", **small}}
+                                      "weight-stationary gathered kernel", **small}}
 
 
 def _cpu_model():

@@ -1,7 +1,6 @@
 // Small-batch kernel (up to 32 activation rows, and up to 256 where the prefill GEMM's
 // grid would be small; M = 2 only where the two-row GEMV does not apply) for the u4
-// group-64 affine projections on gfx950, and the same kernel over the routing of a batch
-// of routed experts (GATHER: passes of up to 32 bucketed pairs of one expert).
+// group-64 affine projections on gfx950.
 //
 // Between decode (one activation row: weight-bandwidth bound, the GEMV) and prefill
 // (hundreds of rows: matrix bound, the LDS-dequant GEMM) the work is still one pass over
@@ -126,13 +125,8 @@ __device__ __forceinline__ void wait_units_barrier(int ahead) {
   }
 }
 
-// GATHER (routed experts over a batch): block y is tile y of the routing's tile table
-// (up to 256 bucketed pairs of one expert), taken in passes of R pairs.  The activation
-// row of a pair is pair / gth.div; the outputs go to the pairs' rows (stage 2: times the
-// pair's combine weight, fp32).
-// gth: the routing (tile table, bucket offsets, bucketed pairs), combine weights, x rows.
-template <int S, int GPS, int MB, int EPI, bool GATHER>
-__global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units, BmvGather gth) {
+template <int S, int GPS, int MB, int EPI>
+__global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M, int64_t units) {
   using L = Layout<S, GPS, MB>;
   constexpr int R = kRows * MB;  // activation rows per block
   constexpr int K = L::K;
@@ -144,21 +138,7 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
   const int col = lane & 15;  // MFMA column: LDS row of the unit
   const int kb = lane >> 4;   // 8-input block of the MFMA's 32 inputs
   const int64_t mb = blockIdx.y;
-  int64_t rows_here = M - mb * R < R ? M - mb * R : R;
-  int64_t first = 0, end = 0;  // GATHER: bucket positions of the pass's first pair, tile end
-  if constexpr (GATHER) {
-    if (mb >= gth.hdr[0]) return;
-    const int e = gth.tiles[2 * mb];
-    first = gth.tiles[2 * mb + 1];
-    end = min(int64_t(gth.offsets[e + 1]), first + kMoeTileRows);
-    if (first >= end) return;
-    rows_here = end - first < R ? end - first : R;
-    // the expert's rows, in place in the grid
-    const int64_t er = int64_t(e) * a.rows;
-    a.codes += er * (K / 8);
-    a.scales += er * (K / 64);
-    a.biases += er * (K / 64);
-  }
+  const int64_t rows_here = M - mb * R < R ? M - mb * R : R;
   const uint64_t nrows = uint64_t(a.rows);
   const uint32_t rows32 = uint32_t(a.rows), I32 = uint32_t(a.I);
 
@@ -218,9 +198,7 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
 
   if (int64_t(blockIdx.x) >= units) return;
   const int64_t stride = gridDim.x;
-  // GATHER: the passes of the tile one after the other, over the same units (the second
-  // pass reads them from L2)
-  for (;;) {
+  {
     int64_t u = blockIdx.x;
     // the block's units j = 0, 1, ... (unit u + j * stride) live in buffer j % nbuf; units
     // 0 .. lookahead - 1 are requested here, unit j + lookahead at step j
@@ -235,18 +213,12 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     bf16x8_t xa[MB][GPS][2];
     {
       // byte offset of block row m's activations (rows past the block's: past the buffer,
-      // read as zeros); GATHER reads the pairs' rows through the bucket
-      const uint16_t* xb = GATHER ? a.x : a.x + mb * R * K;
-      const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, uint64_t(GATHER ? gth.x_rows : rows_here) * K * 2);
+      // read as zeros)
+      const uint16_t* xb = a.x + mb * R * K;
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, uint64_t(rows_here) * K * 2);
       uint32_t xrow[MB];
 #pragma unroll
-      for (int t = 0; t < MB; ++t) {
-        const int m = kRows * t + col;
-        if constexpr (GATHER)
-          xrow[t] = m < rows_here ? uint32_t(gth.pairs[first + m] / gth.div) * uint32_t(K) * 2u : 0xFFFFFFF0u;
-        else
-          xrow[t] = uint32_t(m) * uint32_t(K) * 2u;
-      }
+      for (int t = 0; t < MB; ++t) xrow[t] = uint32_t(kRows * t + col) * uint32_t(K) * 2u;
 #pragma unroll
       for (int t = 0; t < MB; ++t)
 #pragma unroll
@@ -284,11 +256,8 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
     // sums of the S slice partials in slice order and the epilogue of unit uu, each output
     // by one lane of one of the waves; rb[j][t][l][r] is slice j's partial of activation row
     // 16 t + 4 (l / 16) + r, column l % 16
-    // output row of block row mr: the batch row, or (GATHER) the pair's row
-    auto out_row = [&](int mr) -> int64_t {
-      if constexpr (GATHER) return gth.pairs[first + mr];
-      else return mb * R + mr;
-    };
+    // output row of block row mr
+    auto out_row = [&](int mr) -> int64_t { return mb * R + mr; };
     auto epilogue = [&](int64_t uu, const float* rb) {
       auto slice_sum = [&](int t, int l, int r) {
         float v = 0.f;
@@ -348,7 +317,6 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
             const int64_t m = out_row(mr);
             float v = slice_sum(t, l, r);
             if (a.lin_bias) v += bf16_bits_to_f32(a.lin_bias[n]);
-            if constexpr (GATHER) v *= gth.w ? gth.w[m] : 1.f;  // stage 2: the pair's weight
             if constexpr (EPI == EPI_QKV) {
               if (n < a.q_out) {
                 store_out(a.out0, m * a.q_out + n, v, a.f32_out);
@@ -435,14 +403,6 @@ __global__ void __launch_bounds__(64 * S, 1) bmv_u4_kernel(GemvArgs a, int64_t M
       __syncthreads();
       epilogue(u - stride, red + (it & 1) * (L::red_bytes / 4));
     }
-    if constexpr (!GATHER) {
-      break;
-    } else {
-      first += R;
-      if (first >= end) break;
-      rows_here = end - first < R ? end - first : R;
-      __syncthreads();
-    }
   }
 }
 
@@ -512,61 +472,14 @@ static void launch_bmv_tiles(int epi, const GemvArgs& a, int64_t M, int64_t unit
   const int64_t cus = device_cus();
   const dim3 grid{unsigned(units < cus ? units : cus), unsigned((M + bmv::kRows * MB - 1) / (bmv::kRows * MB)), 1u};
   const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
-  const BmvGather none = {};
   if (epi == EPI_LINEAR)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR, false><<<grid, block, 0, st>>>(a, M, units, none);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR><<<grid, block, 0, st>>>(a, M, units);
   else if (epi == EPI_QKV)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_QKV, false><<<grid, block, 0, st>>>(a, M, units, none);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_QKV><<<grid, block, 0, st>>>(a, M, units);
   else if (epi == EPI_ROPE)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_ROPE, false><<<grid, block, 0, st>>>(a, M, units, none);
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_ROPE><<<grid, block, 0, st>>>(a, M, units);
   else
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU, false><<<grid, block, 0, st>>>(a, M, units, none);
-}
-
-// Routed experts: a block per routing tile and `upb` units of its expert, for the tile's
-// passes of 32 pairs (K <= 5120) or 16.
-template <int G, int MB>
-static void launch_bmv_moe_tiles(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t units,
-                                 int64_t upb, hipStream_t st) {
-  const dim3 grid{unsigned((units + upb - 1) / upb), unsigned(m_tiles), 1u};
-  const dim3 block{64u * bmv::kSlicesUsed, 1u, 1u};
-  if (epi == EPI_SWIGLU)
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU, true><<<grid, block, 0, st>>>(a, 0, units, g);
-  else
-    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_LINEAR, true><<<grid, block, 0, st>>>(a, 0, units, g);
-}
-
-bool bmv_moe_supports(int epi, const GemvArgs& a) {
-  if (a.bits != 4 || a.gshift != 1 || a.K % bmv::kKStep || (epi != EPI_SWIGLU && epi != EPI_LINEAR)) return false;
-  switch (a.K / bmv::kKStep) {
-#define QMM_BMV_CASE(G) case G:
-    QMM_BMV_GPS(QMM_BMV_CASE)
-#undef QMM_BMV_CASE
-      return true;
-    default:
-      return false;
-  }
-}
-
-int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t upb, hipStream_t st) {
-  if (!bmv_moe_supports(epi, a) || upb < 1) return 2;
-  const int64_t units = epi == EPI_SWIGLU ? (a.I + bmv::kUnit / 2 - 1) / (bmv::kUnit / 2)
-                                          : (a.rows + bmv::kUnit - 1) / bmv::kUnit;
-  const int64_t gps = a.K / bmv::kKStep;
-  switch (gps) {
-#define QMM_BMV_CASE(G)                                                               \
-  case G:                                                                             \
-    if constexpr (G <= bmv::kMaxGpsTwoTiles)                                          \
-      launch_bmv_moe_tiles<G, 2>(epi, a, g, m_tiles, units, upb, st);                 \
-    else                                                                              \
-      launch_bmv_moe_tiles<G, 1>(epi, a, g, m_tiles, units, upb, st);                 \
-    break;
-    QMM_BMV_GPS(QMM_BMV_CASE)
-#undef QMM_BMV_CASE
-    default:
-      return 2;
-  }
-  return hipGetLastError() == hipSuccess ? 0 : 6;
+    bmv::bmv_u4_kernel<bmv::kSlicesUsed, G, MB, EPI_SWIGLU><<<grid, block, 0, st>>>(a, M, units);
 }
 
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t st) {

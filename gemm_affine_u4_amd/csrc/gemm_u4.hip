@@ -53,7 +53,6 @@ constexpr int kRow = 64;                 // bf16 per LDS row (one 64-wide group)
 constexpr int kStage = kBM * kRow;       // bf16 per LDS stage (32 KB)
 constexpr int kXcds = 8;
 static_assert(kBM == kBN, "x and weight stages share one shape");
-static_assert(kMoeTileRows <= kBM, "a routing tile fits one GEMM tile");
 
 // Bank-group swizzle of LDS row r (see the header).
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
@@ -103,7 +102,7 @@ __device__ __forceinline__ int64_t gemm_weight_row(const GemmArgs& a, int64_t nt
   }
 }
 
-template <int EPI, bool GATHER>
+template <int EPI>
 __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t n_tiles,
                                                         int64_t tiles_per_xcd) {
   // One variable per x stage, and the two weight stages in a variable of their own: the
@@ -120,29 +119,11 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   const int64_t mt = tile % m_tiles;
   const int64_t nt = tile / m_tiles;
 
-  // Routed experts over a batch (GATHER): tile mt of the table is up to kBM bucketed pairs
-  // of one expert; its x rows are gathered (pair / moe_div) and its outputs go to the
-  // pairs' rows.  Otherwise the tile is x rows [mt*kBM, mt*kBM + kBM) of a dense GEMM.
-  int rows_here = kBM;
-  int pair_base = 0;
-  if constexpr (GATHER) {
-    if (mt >= a.moe_hdr[0]) return;
-    const int e = a.moe_tiles[2 * mt];
-    pair_base = a.moe_tiles[2 * mt + 1];
-    rows_here = min(kMoeTileRows, a.moe_offsets[e + 1] - pair_base);
-    const int64_t er = int64_t(e) * a.N;  // first row of the expert in the grid
-    a.codes += er * ((a.K * kBits) >> 5);
-    a.scales += er * (a.K >> (5 + a.gshift));
-    a.biases += er * (a.K >> (5 + a.gshift));
-  }
-  // source row of tile row r (a row past the tile's end reads its last row; never stored)
+  // source row of tile row r (x rows [mt*kBM, mt*kBM + kBM); a row past M reads row M - 1,
+  // never stored)
   auto x_row = [&](int r) -> int64_t {
-    if constexpr (GATHER) {
-      return a.moe_pairs[pair_base + min(r, rows_here - 1)] / a.moe_div;
-    } else {
-      const int64_t m = mt * kBM + r;
-      return m < a.M ? m : a.M - 1;
-    }
+    const int64_t m = mt * kBM + r;
+    return m < a.M ? m : a.M - 1;
   };
 
   const int tid = threadIdx.x;
@@ -295,32 +276,23 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   struct Frags {
     bf16x8_t a[4], b[2];
   };
-  // A gathered tile often holds far fewer than kBM pairs: each wave then reads and
-  // multiplies only its 32-row blocks that hold some (act of its 4; wave-uniform branches).
-  int act = 4;
-  if constexpr (GATHER) act = __builtin_amdgcn_readfirstlane(min(4, max(0, (rows_here - 128 * wm + 31) / 32)));
   auto load_frags = [&](Frags& f, const uint16_t* as, const uint16_t* bs, int q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (!GATHER || i < act) f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(bs + btile_row(j) * kRow + opoff[q]);
   };
   auto mfma16 = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (!GATHER || i < act) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
 
   // Instruction order inside a slot: the wave issues in order and an MFMA waits for the
   // matrix pipe, so the dequantization's ~24 VALU ops are spread 3 per MFMA (they then
   // run while the MFMA executes) and its LDS store goes late in the slot.
   auto interleave_slot = [&]() {
-    if constexpr (GATHER) return;  // the branches above split the slot: the compiler orders it
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
@@ -408,20 +380,10 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   // address is aligned, element by element otherwise (ragged edges, odd row strides).
   const int trow0 = 128 * wm + (lane & 31);  // tile row of this lane's output row, i = 0
   const int csub = 4 * (lane >> 5);
-  // output row of tile row trow0 + 32 i, false if the row does not exist; `scale` is the
-  // combine weight of a routed pair in stage 2, else 1
-  auto out_row = [&](int i, int64_t* m, float* scale) -> bool {
-    const int r = trow0 + 32 * i;
-    *scale = 1.f;
-    if constexpr (GATHER) {
-      if (r >= rows_here) return false;
-      *m = a.moe_pairs[pair_base + r];
-      if (a.moe_w) *scale = a.moe_w[*m];
-      return true;
-    } else {
-      *m = mt * kBM + r;
-      return *m < a.M;
-    }
+  // output row of tile row trow0 + 32 i, false if the row does not exist
+  auto out_row = [&](int i, int64_t* m) -> bool {
+    *m = mt * kBM + trow0 + 32 * i;
+    return *m < a.M;
   };
   // 4 consecutive outputs from element idx: one vector store when all 4 exist and the
   // address is aligned to it (the ABI only promises element alignment of the buffer)
@@ -455,8 +417,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     bool have[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float sc;
-      have[i] = out_row(i, &mrow[i], &sc);
+      have[i] = out_row(i, &mrow[i]);
       const int32_t pos = have[i] ? min(max(ra.positions[mrow[i]], 0), ra.max_pos - 1) : 0;
       trow[i] = ra.cos_sin + int64_t(pos) * ra.rot;
     }
@@ -531,8 +492,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           int64_t m;
-          float sc;
-          if (!out_row(i, &m, &sc)) continue;
+          if (!out_row(i, &m)) continue;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[i][j][4 * g + e], acc[i][j + 1][4 * g + e]);
@@ -571,11 +531,10 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           int64_t m;
-          float sc;
-          if (!out_row(i, &m, &sc)) continue;
+          if (!out_row(i, &m)) continue;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] * sc + lb[e];
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e] + lb[e];
           if (one_range) {
             put(dst, ld, cn, m, v, 4);
           } else {
@@ -604,39 +563,20 @@ int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
   const dim3 block{512u, 1u, 1u};
   if (epi == EPI_LINEAR) {
-    gemm_u4_kernel<EPI_LINEAR, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_LINEAR><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else if (epi == EPI_QKV) {
-    gemm_u4_kernel<EPI_QKV, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_QKV><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   } else if (epi == EPI_ROPE) {
 #if QMM_BITS == 4
-    gemm_u4_kernel<EPI_ROPE, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_ROPE><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
 #else
     return 2;  // the rotary epilogue is built for 4-bit codes only
 #endif
   } else {
-    gemm_u4_kernel<EPI_SWIGLU, false><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+    gemm_u4_kernel<EPI_SWIGLU><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
   }
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
-
-#if QMM_BITS == 4
-int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
-  const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + kBN / 2 - 1) / (kBN / 2) : (a.N + kBN - 1) / kBN;
-  const int64_t tiles = m_tiles * n_tiles;
-  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-  const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
-  const dim3 block{512u, 1u, 1u};
-  if (epi == EPI_SWIGLU) {
-    gemm_u4_kernel<EPI_SWIGLU, true><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
-  } else if (epi == EPI_LINEAR) {
-    gemm_u4_kernel<EPI_LINEAR, true><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
-  } else {
-    return 5;
-  }
-  return hipGetLastError() == hipSuccess ? 0 : 6;
-}
-
-#endif
 
 }  // namespace QMM_BITS_NS
 }  // namespace qmm

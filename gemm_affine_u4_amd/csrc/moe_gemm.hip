@@ -496,6 +496,7 @@ bool moe_gemm_supports(const GemmArgs& a) {
 }
 
 int launch_moe_gemm(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
+  if (!moe_gemm_supports(a)) return 2;
   const int64_t slabs = epi == EPI_SWIGLU ? (a.I + moe_mm::kSlab / 2 - 1) / (moe_mm::kSlab / 2)
                                           : (a.N + moe_mm::kSlab - 1) / moe_mm::kSlab;
   const int64_t blocks = (m_tiles * slabs + moe_mm::kXcds - 1) / moe_mm::kXcds * moe_mm::kXcds;

@@ -274,49 +274,6 @@ int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, voi
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
-#ifndef QMM_MOE_BMV
-#define QMM_MOE_BMV 1
-#endif
-#ifndef QMM_MOE_MM
-#define QMM_MOE_MM 1
-#endif
-// The gathered stages on the small-batch kernel (passes of up to 32 pairs of one expert,
-// each streaming the expert's rows) while experts average at most 24 pairs (stage 1) or
-// 40 pairs (stage 2, whose K = I is short), else on the gathered GEMM (256-pair tiles).
-// 35B-A3B shape (256 experts, top-8): per layer 191 against 374 us at 128 tokens, 284
-// against 382 at 512; at 1024 tokens stage 1 228 on the GEMM against 237, stage 2 155
-// on the small-batch kernel against 169.
-constexpr int64_t kMoeBmvPairsPerExpert[2] = {24, 40};
-// Units per block of the small-batch kernel: 32 where nearly every tile is one pass (up to
-// 8 pairs per expert on average: fewer, longer blocks, 128 tokens 221 -> 191 us per
-// layer), else 8 (tiles of several passes make long blocks; 16 or 32 there lose up to
-// 15 % on stage 2 at 512 tokens).
-static int launch_moe_stage(int epi, const GemmArgs& a, int64_t x_rows, int64_t tmax, bool few_per_expert,
-                            int64_t upb, hipStream_t s) {
-  if (QMM_MOE_BMV && few_per_expert) {
-    GemvArgs v = {};
-    v.x = a.x;
-    v.codes = a.codes;
-    v.scales = a.scales;
-    v.biases = a.biases;
-    v.lin_bias = a.lin_bias;
-    v.out0 = a.out0;
-    v.K = a.K;
-    v.rows = a.N;
-    v.I = a.I;
-    v.n_out = epi == EPI_SWIGLU ? a.I : a.N;
-    v.f32_out = a.f32_out;
-    v.bits = a.bits;
-    v.gshift = a.gshift;
-    if (bmv_moe_supports(epi, v) && uint64_t(x_rows) * uint64_t(a.K) * 2u < 0xFFFFFFF0ull && tmax <= 65535) {
-      const BmvGather gth = {a.moe_hdr, a.moe_tiles, a.moe_offsets, a.moe_pairs, a.moe_w, a.moe_div, x_rows};
-      return launch_bmv_moe(epi, v, gth, tmax, upb, s);
-    }
-  }
-  if (QMM_MOE_MM && moe_gemm_supports(a)) return launch_moe_gemm(epi, a, tmax, s);
-  return b4::launch_gemm_moe(epi, a, tmax, s);
-}
-
 int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t M, int64_t topk, int64_t E,
                        const void* ws, void* out, hipStream_t s) {
   const MoeLayout L = moe_layout(M, topk, E, stage == 0 ? 0 : g.N);
@@ -327,14 +284,12 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
   a.moe_offsets = reinterpret_cast<const int32_t*>(b + L.offsets);
   a.moe_pairs = reinterpret_cast<const int32_t*>(b + L.pairs);
   const unsigned zb = unsigned((L.P + 255) / 256);
-  const bool few = L.P <= kMoeBmvPairsPerExpert[stage == 0 ? 0 : 1] * E;
-  const int64_t upb = L.P <= 8 * E ? 32 : 8;
   if (stage == 0) {
-    // stage 1: h [P][I] of the routed pairs from the gathered GEMM, zeros for the others
+    // stage 1: h [P][I] of the routed pairs from the gathered kernel, zeros for the others
     a.out0 = out;
     a.moe_w = nullptr;
     a.moe_div = topk;
-    if (int st = launch_moe_stage(EPI_SWIGLU, a, M, L.tmax, few, upb, s)) return st;
+    if (int st = launch_moe_gemm(EPI_SWIGLU, a, L.tmax, s)) return st;
     moe_zero_unrouted<<<dim3{zb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, L.P, int(E), out, a.I, a.f32_out);
   } else {
     // stage 2: z = p * (D_e h) per routed pair (fp32, workspace), then the per-token sum
@@ -343,7 +298,7 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
     a.out0 = z;
     a.f32_out = 1;
     a.moe_div = 1;
-    if (int st = launch_moe_stage(EPI_LINEAR, a, L.P, L.tmax, few, upb, s)) return st;
+    if (int st = launch_moe_gemm(EPI_LINEAR, a, L.tmax, s)) return st;
     const unsigned mb = unsigned(M < 4096 ? M : 4096);
     if (a.N % 4 == 0)
       moe_combine<true><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);

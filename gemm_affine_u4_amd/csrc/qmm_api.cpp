@@ -42,12 +42,12 @@ bool acts_fit(int64_t M, int64_t K) { return uint64_t(M) * uint64_t(K) * 2 <= 0x
 // Activation rows up to which the decode GEMV runs (once per row); above, the GEMM.
 constexpr int64_t kGemvMaxM = 8;
 #ifndef QMM_MOE_PAIRS_BY_GEMV
-#define QMM_MOE_PAIRS_BY_GEMV 448
+#define QMM_MOE_PAIRS_BY_GEMV 288
 #endif
 // Routed experts over a batch: up to this many (token, slot) pairs run pair by pair
 // (measured on the 35B-A3B shape, route included: at 32 tokens x top-8 the layer takes
-// 101 us pair by pair against 167 us through the routed path, at 64 tokens 200 against
-// 179 us; the pair path grows ~0.39 us per pair, the routed one stays near 170 us).
+// 110 us pair by pair against 119 us through the routed path, at 40 tokens 139 against
+// 123 us; the pair path grows ~0.39 us per pair, the routed one ~0.1 us).
 constexpr int64_t kMoePairsByGemv = QMM_MOE_PAIRS_BY_GEMV;
 
 // A format of the affine family: code width and group size (the pages list u2 .. u8 at

@@ -129,13 +129,9 @@ QMM_WIDTH_LAUNCHERS(b4)
 QMM_WIDTH_LAUNCHERS(b6)
 QMM_WIDTH_LAUNCHERS(b8)
 QMM_WIDTH_LAUNCHERS(f8)
-// Gathered GEMM of the routed experts over a batch (4-bit codes): m_tiles = bound on the
-// tile table.
-namespace b4 {
-int launch_gemm_moe(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
-}
-// The weight-stationary gathered kernel of the same stages (moe_gemm.hip): each block one
-// routing tile x one slab of 128 expert rows (SWIGLU: 64 gate + their 64 up rows).
+// The routed experts over a batch (4-bit codes, group 64; moe_gemm.hip): each block one
+// routing tile x one slab of 128 expert rows (SWIGLU: 64 gate + their 64 up rows);
+// m_tiles = bound on the tile table.
 bool moe_gemm_supports(const GemmArgs& a);
 int launch_moe_gemm(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
 
@@ -177,23 +173,6 @@ constexpr int64_t kBmvMaxM = 256;
 bool bmv_supports(int epi, const GemvArgs& a, int64_t M);
 bool bmv_preferred(int epi, const GemvArgs& a, int64_t M);
 int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
-// The same kernel over the routing of a batch of routed experts (the MoE prefill stages):
-// a block per pass of up to 32 bucketed pairs of one routing tile, over its expert's rows
-// (a.rows rows per expert, a.codes etc. the grid base).  Stage 1 (EPI_SWIGLU) writes h
-// rows of the pairs; stage 2 (EPI_LINEAR) writes w[pair] * (D_e h) in fp32.
-struct BmvGather {
-  const int32_t* hdr;      // [0] = tiles in the table
-  const int32_t* tiles;    // [tiles][2] = (expert, first bucket position)
-  const int32_t* offsets;  // [E+1] bucket boundaries
-  const int32_t* pairs;    // bucketed pair indices
-  const float* w;          // stage 2: combine weight per pair; null in stage 1
-  int64_t div;             // activation row of a pair = pair / div
-  int64_t x_rows;          // rows of the activations
-};
-bool bmv_moe_supports(int epi, const GemvArgs& a);
-// upb: weight units (16 rows) per block; the grid is ceil(units / upb) x m_tiles.
-int launch_bmv_moe(int epi, const GemvArgs& a, const BmvGather& g, int64_t m_tiles, int64_t upb, hipStream_t s);
-
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
 #ifndef QMM_MOE_TILE_ROWS

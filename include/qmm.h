@@ -219,7 +219,7 @@ int qmm_moe_layer(const uint16_t* x, int64_t K, const uint32_t* gu_codes, const 
  * ("Sanctum-MLX", "Inside the server"; never concatenated: "Four Candles for the
  * Cathedral", "What's not in this batch").  Prefill is dominated by the quantized
  * matmuls ("Sanctum-MLX", "Latency testing"), so the pairs are bucketed by expert and
- * each expert's weights are streamed once, through the MFMA GEMM, for all of the
+ * each expert's weights are streamed once, through the matrix cores, for all of the
  * tokens routed to it (gathered through the bucket), instead of once per token.
  *
  * Three calls, in stream order:
@@ -227,14 +227,12 @@ int qmm_moe_layer(const uint16_t* x, int64_t K, const uint32_t* gu_codes, const 
  *                    (deterministic: by expert, then by pair index);
  *   qmm_moe_prefill  stage QMM_MOE_GATE_UP_SWIGLU, then stage QMM_MOE_DOWN_COMBINE,
  *                    both reading that routing.
- * Up to 24 pairs per expert on average (M * topk <= 24 E; stage 2: 40 E) the stages run
- * on the small-batch kernel, in passes of up to 32 pairs of one expert; above, on the
- * gathered GEMM (tiles of 256 pairs).  Both read the routing the same way and give the same
- * results up to rounding order.
- * A small batch (M * topk <= 448 pairs: most experts then see one token or none) runs
+ * The stages run on a gathered kernel over routing tiles of up to 128 pairs of one expert,
+ * each expert row dequantized once per tile.
+ * A small batch (M * topk <= 288 pairs: most experts then see one token or none) runs
  * pair by pair instead, on the kernels of qmm_moe_gather: stage 1 one SwiGLU GEMV per
  * (token, slot) pair, stage 2 each token's weighted sum over its slots (expert I <= 5120;
- * a wider one is routed by stage 2 itself and runs the GEMM).  The stages then read
+ * a wider one is routed by stage 2 itself and runs the gathered kernel).  The stages then read
  * expert_ids directly and qmm_moe_route does nothing, so the call order above still holds.
  * workspace: caller-owned device memory, 256-byte aligned, of at least
  * qmm_moe_prefill_workspace_bytes(M, topk, E, out_rows) bytes, where out_rows is the

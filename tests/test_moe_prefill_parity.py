@@ -71,7 +71,7 @@ def check_both_stages(shape, cfg, layer, M, ids, p, what):
     return g1, g2
 
 
-# Several GEMM tiles per expert (skewed popularity: one expert above 256 pairs, one
+# Several routing tiles per expert (skewed popularity: one expert above 256 pairs, one
 # nearly empty), a ragged last tile everywhere, I and hidden not multiples of the tile.
 SMALL = synth.MoEShape("small MoE prefill (hidden 320, 8 experts, I 192, top-2)", 320, 8, 192, 2)
 
@@ -162,9 +162,9 @@ def test_moe_prefill_35B_shape_full_batch_sampled_tokens():
 
 
 def test_small_batch_pair_path_and_wide_expert():
-    """Few pairs (M * topk <= 448) run the decode gather kernels pair by pair and the
+    """Few pairs (M * topk <= 288) run the decode gather kernels pair by pair and the
     routing call does nothing; a down projection wider than those kernels take (expert
-    I = 5632 > 5120) makes stage 2 route on its own and run the gathered GEMM."""
+    I = 5632 > 5120) makes stage 2 route on its own and run the routed kernel."""
     shape = synth.MoEShape("wide-expert MoE (hidden 128, 4 experts, I 5632, top-2)", 128, 4, 5632, 2)
     M = 5
     ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 7, M, shape.E, shape.topk)
@@ -172,11 +172,10 @@ def test_small_batch_pair_path_and_wide_expert():
     check_both_stages(shape, synth.CFG_TEST, 7, M, ids, p, "wide expert")
 
 
-def test_moe_prefill_small_batch_kernel_passes_and_tiles():
-    """Up to 24 pairs per expert on average (here 1200 pairs over 64 experts) the routed
-    stages run on the small-batch kernel, in passes of 32 pairs per routing tile: one
-    expert takes slot 0 of 300 tokens (two tiles, the second ragged), the others a few
-    pairs each (one ragged pass), one pair has no expert; K = 1024 and K = 512."""
+def test_moe_prefill_one_hot_expert_among_small_ones():
+    """1200 pairs over 64 experts: one expert takes slot 0 of 300 tokens (three routing
+    tiles of up to 128 pairs, the last ragged), the others a few pairs each (one ragged
+    32-pair block), one pair has no expert; K = 1024 and K = 512."""
     shape = synth.MoEShape("MoE prefill (hidden 1024, 64 experts, I 512, top-3)", 1024, 64, 512, 3)
     M = 400
     ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 8, M, shape.E, shape.topk)
@@ -184,21 +183,19 @@ def test_moe_prefill_small_batch_kernel_passes_and_tiles():
     ids[7, 2] = -1
     counts = np.bincount(ids[ids >= 0].ravel(), minlength=shape.E)
     say(f"[moe prefill] {shape.name}, M={M}, pairs per expert max {counts.max()} min {counts.min()}")
-    assert counts.max() > 256 and M * shape.topk <= 24 * shape.E
-    g1, _ = check_both_stages(shape, synth.CFG_TEST, 8, M, ids, p, "small-batch kernel")
+    assert counts.max() > 256
+    g1, _ = check_both_stages(shape, synth.CFG_TEST, 8, M, ids, p, "one hot expert")
     assert np.all(g1[7, 2] == 0)
 
 
-def test_moe_prefill_stage1_gemm_stage2_small_batch_kernel():
-    """Between 24 and 40 pairs per expert on average (here 1200 pairs over 32 experts)
-    stage 1 runs the gathered GEMM and stage 2 (K = I = 512) the gathered small-batch
-    kernel; both against the oracle."""
+def test_moe_prefill_hidden_1024_37_pairs_per_expert():
+    """1200 pairs over 32 experts (about 37 each: tiles of one or two 32-pair blocks),
+    hidden 1024 (16 K steps, two scale chunks per row) and I = 512."""
     shape = synth.MoEShape("MoE prefill (hidden 1024, 32 experts, I 512, top-3)", 1024, 32, 512, 3)
     M = 400
     ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 9, M, shape.E, shape.topk)
-    assert 24 * shape.E < M * shape.topk <= 40 * shape.E
     say(f"[moe prefill] {shape.name}, M={M}")
-    check_both_stages(shape, synth.CFG_TEST, 9, M, ids, p, "GEMM + small-batch kernel")
+    check_both_stages(shape, synth.CFG_TEST, 9, M, ids, p, "hidden 1024")
 
 
 def test_moe_prefill_many_chunks_and_ragged_expert_count():
@@ -211,20 +208,20 @@ def test_moe_prefill_many_chunks_and_ragged_expert_count():
     check_both_stages(shape, synth.CFG_TEST, 10, M, ids, p, "many chunks")
 
 
-def test_moe_prefill_small_batch_kernel_one_tile_passes():
-    """Stage 1 at K = 6144 runs the small-batch kernel with one 16-row tile per pass (two
-    tiles need K <= 5120): 600 pairs over 32 experts, passes of 16 pairs."""
+def test_moe_prefill_long_k():
+    """Stage 1 at K = 6144 (96 K steps, 12 scale chunks per row): 600 pairs over 32
+    experts, skewed."""
     shape = synth.MoEShape("MoE prefill (hidden 6144, 32 experts, I 512, top-2)", 6144, 32, 512, 2)
     M = 300
     ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 11, M, shape.E, shape.topk, skew=1.0)
-    assert 448 < M * shape.topk <= 24 * shape.E
+    assert 288 < M * shape.topk
     say(f"[moe prefill] {shape.name}, M={M}")
-    check_both_stages(shape, synth.CFG_TEST, 11, M, ids, p, "one-tile passes")
+    check_both_stages(shape, synth.CFG_TEST, 11, M, ids, p, "long K")
 
 
 def test_moe_prefill_35B_shape_128_tokens():
-    """The 35B-A3B shape at 128 tokens (1024 pairs over 256 experts): both stages on the
-    small-batch kernel (K = 2048 and K = 512)."""
+    """The 35B-A3B shape at 128 tokens (1024 pairs over 256 experts, about 4 each: tiles of
+    one 32-pair block), routed (K = 2048 and K = 512)."""
     shape = synth.MOE_35B
     M = 128
     ids, p = synth.gen_prefill_routing(synth.CFG_MOE, 1, M, shape.E, shape.topk)

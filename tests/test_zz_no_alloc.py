@@ -54,11 +54,11 @@ def run_pair(gu, dn, ids, p, x, h_in, shape):
 
 
 CASES = [
-    # (name, shape, cfg, layer, M first, M second, skew): the routed paths (gathered GEMM,
-    # gathered small-batch kernel) and the pair-by-pair path, each twice with a smaller batch
-    ("several GEMM tiles per expert", SMALL, synth.CFG_TEST, 40, 2000, 700, 1.0),
-    ("35B-A3B shape, small-batch kernel", synth.MOE_35B, synth.CFG_MOE, 0, 256, 96, 0.5),
-    ("35B-A3B shape, pair by pair", synth.MOE_35B, synth.CFG_MOE, 1, 40, 9, 0.5),
+    # (name, shape, cfg, layer, M first, M second, skew): the routed path (many pairs and
+    # few pairs per expert) and the pair-by-pair path, each twice with a smaller batch
+    ("several routing tiles per expert", SMALL, synth.CFG_TEST, 40, 2000, 700, 1.0),
+    ("35B-A3B shape, few pairs per expert", synth.MOE_35B, synth.CFG_MOE, 0, 256, 96, 0.5),
+    ("35B-A3B shape, pair by pair", synth.MOE_35B, synth.CFG_MOE, 1, 32, 9, 0.5),
 ]
 
 
