@@ -198,6 +198,20 @@ def test_moe_prefill_hidden_1024_37_pairs_per_expert():
     check_both_stages(shape, synth.CFG_TEST, 9, M, ids, p, "hidden 1024")
 
 
+def test_moe_prefill_routed_shortest_k():
+    """The routed kernel at its shortest K: stage 1 at K = 128 (two steps, one code chunk)
+    and stage 2 at K = 64 (one step), 600 pairs over 6 experts, one pair without an
+    expert."""
+    shape = synth.MoEShape("MoE prefill (hidden 128, 6 experts, I 64, top-2)", 128, 6, 64, 2)
+    M = 300
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 12, M, shape.E, shape.topk, skew=1.0)
+    ids[3, 1] = -1
+    assert M * shape.topk > 288
+    say(f"[moe prefill] {shape.name}, M={M}")
+    g1, _ = check_both_stages(shape, synth.CFG_TEST, 12, M, ids, p, "shortest K")
+    assert np.all(g1[3, 1] == 0)
+
+
 def test_moe_prefill_many_chunks_and_ragged_expert_count():
     """4800 pairs (19 routing chunks: the scan's wave-per-expert path) over 100 experts
     (not a multiple of the scan's batch of 8), skewed, some experts empty."""
