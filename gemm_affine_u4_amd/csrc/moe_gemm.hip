@@ -47,9 +47,6 @@ static_assert(kMaxMB >= 1 && kMaxMB <= 4, "one tile is at most 4 blocks of 32 pa
 #ifndef QMM_MOE_XSTAGES
 #define QMM_MOE_XSTAGES 2
 #endif
-#ifndef QMM_MOE_SILU
-#define QMM_MOE_SILU silu_times_fast
-#endif
 #ifndef QMM_MOE_MIX
 #define QMM_MOE_MIX 1
 #endif
@@ -132,14 +129,6 @@ __device__ __forceinline__ bf16x8_t dequant8_mix(uint32_t w, float s, float b102
   const u32x4_t v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                      pack_bf16x2(f[6], f[7])};
   return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// silu(g) * u with the hardware exponential and reciprocal (about 2 ulp each; the IEEE
-// division and the full-range expf of silu_times cost ~30 more VALU ops per output).
-// e^-g -> inf gives a reciprocal of 0 and so -0, e^-g -> 0 gives g.
-__device__ __forceinline__ float silu_times_fast(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // Scales and biases of 8 consecutive groups of one row (bf16 pairs).
@@ -442,7 +431,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
         if (i0 >= a.I) continue;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = QMM_MOE_SILU(acc[b][8 * g + e], acc[b][8 * g + 4 + e]);
+        for (int e = 0; e < 4; ++e) v[e] = silu_times(acc[b][8 * g + e], acc[b][8 * g + 4 + e]);
         put4(a.out0, pr * a.I + i0, v, int(min<int64_t>(4, a.I - i0)), a.f32_out);
       }
     } else {

@@ -249,9 +249,24 @@ __device__ __forceinline__ constexpr int slot_result_lane(int s) {
   return LPR == 32 ? 32 * s + 16 : 16 * s;
 }
 
+// silu(g) * u, silu(g) = g / (1 + e^-g), with the hardware base-2 exponential and
+// reciprocal (each within about an ulp) rather than the full-range expf and the IEEE
+// division (~30 more VALU ops per output).  The exponent -g log2(e) is carried as a rounded
+// head and its residual (the product's rounding error and the constant's second word),
+// applied to first order, so the relative error stays within a few ulp for every g (2.4e-7
+// measured over g in [-120, 120] wherever the result is a normal fp32, against 1.8e-7 for
+// the expf / division form).  The exponent is capped at 126: beyond it the residual grows
+// and e overflows to inf, whose reciprocal 0 gives -0 (as g / (1 + inf) does); below -126
+// e is 0 (or denormal) and the result g.
 __device__ __forceinline__ float silu_times(float g, float u) {
-  // silu(g) * u with silu(g) = g / (1 + e^-g); e^-g -> inf gives -0, e^-g -> 0 gives g.
-  return g / (1.0f + expf(-g)) * u;
+  constexpr float kLog2e = 1.44269502f;        // log2(e) rounded to fp32
+  constexpr float kLog2eLo = 1.925963033e-8f;  // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147181f;
+  const float x = fminf(-g * kLog2e, 126.0f);
+  const float xl = fmaf(-g, kLog2e, -x) + (-g) * kLog2eLo;
+  const float e0 = __builtin_amdgcn_exp2f(x);
+  const float e = x > -126.0f ? fmaf(e0, xl * kLn2, e0) : e0;
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool f32) {
