@@ -868,9 +868,9 @@ def bench_moe_prefill(torch, qmm, synth, T, dev, reps):
             "gate_up_swiglu": rec(ms_s1, fl1, b1),
             "down_combine": rec(ms_s2, fl2, b2),
             "small_batches": {"note": "route + both stages per layer for the first M tokens of the same "
-                                      "routing; M * topk <= 448 runs pair by pair, up to 24 pairs per expert "
-                                      "(stage 2: 40) on the gathered small-batch kernel, above on the "
-                                      "weight-stationary gathered kernel", **small}}
+                                      "routing; M * topk <= 288 runs pair by pair on the decode gather "
+                                      "kernels, above it the batch is routed onto the weight-stationary "
+                                      "gathered kernel", **small}}
 
 
 def _cpu_model():
