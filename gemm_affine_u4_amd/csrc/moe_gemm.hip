@@ -188,10 +188,10 @@ constexpr int wait_count() {
 
 // Where a block's work sits: its routing tile and weight slab.
 struct TileJob {
-  int e;          // expert
-  int pair_base;  // first bucket position of the tile
-  int P;          // pairs in the tile (1 .. kMoeTileRows)
-  int slab;       // weight slab
+  int e;                 // expert
+  int P;                 // pairs in the tile (1 .. kMoeTileRows)
+  int slab;              // weight slab
+  const int32_t* pairs;  // the tile's pair indices (LDS)
 };
 
 // The tile loop for a tile of MB blocks of 32 pairs.  SC8: the scales and biases are read
@@ -283,7 +283,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
 #pragma unroll
   for (int j = 0; j < MB; ++j) {
     const int r = 8 * (MB * wave + j) + (lane >> 3);
-    const int64_t xrow = a.moe_pairs[jb.pair_base + min(r, jb.P - 1)] / a.moe_div;
+    const int64_t xrow = jb.pairs[min(r, jb.P - 1)] / a.moe_div;
     const uint32_t chunk = uint32_t(lane & 7) ^ swz(uint32_t(r));
     xoff[j] = uint32_t(xrow) * K * 2u + chunk * 16u;
   }
@@ -423,7 +423,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   for (int b = 0; b < MB; ++b) {
     const int q = 32 * b + m;
     if (q >= jb.P) continue;
-    const int64_t pr = a.moe_pairs[jb.pair_base + q];
+    const int64_t pr = jb.pairs[q];
     if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -460,25 +460,47 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const TileJob& jb, u
   else tile_body<EPI, (kMaxMB < 4 ? 1 : 4), SC8>(a, jb, lds);
 }
 
-// Block order: the table's tiles x slabs, in that order, cut into 8 equal contiguous ranges,
-// range x for the blocks dealt to XCD x (blocks go to the XCDs round-robin): an XCD takes
-// every slab of a run of tiles, so a tile's activation rows stay in its L2, and the tiles
-// actually routed (known on the device only) spread over all eight.
+// Stage 1's h of a pair with no expert is zero (tiles write routed pairs only): the blocks
+// without a tile take the pairs in turn, block q of nq.
+__device__ __forceinline__ void zero_unrouted(const GemmArgs& a, int64_t q, int64_t nq) {
+  const int64_t P = a.M * a.moe_div;
+  for (int64_t i = q * blockDim.x + threadIdx.x; i < P; i += nq * blockDim.x) {
+    const int32_t e = a.moe_ids[i];
+    if (e >= 0 && e < a.moe_E) continue;
+    for (int64_t c = 0; c < a.I; ++c) store_out(a.out0, i * a.I + c, 0.f, a.f32_out);
+  }
+}
+
+// Block b runs on XCD b % 8 (blocks go to the XCDs round-robin) and takes tile
+// 8 (j / slabs) + b % 8 and slab j % slabs of it, j = b / 8: every slab of a tile on one XCD,
+// so the tile's activation rows stay in that XCD's L2, and consecutive tiles on consecutive
+// XCDs, so the tiles actually routed (a prefix of the records whose length only the device
+// knows) spread over all eight.  The tile is known from the block index alone, so the
+// table's length, the record head and the pair indices come in one memory round trip.
 template <int EPI>
 __global__ void __launch_bounds__(256, 3) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
-  const int64_t total = int64_t(a.moe_hdr[0]) * slabs;
-  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  // one LDS object: with a second one beside the pool the compiler waits for the pool's
+  // direct-to-LDS loads before every LDS read (vmcnt), which undoes the prefetch
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds + kMoeTileRows * 4];
+  int32_t* plist = reinterpret_cast<int32_t*>(lds + kLds);
   const int64_t j = blockIdx.x / kXcds;
-  if (j >= per_xcd) return;
-  const int64_t t = int64_t(blockIdx.x % kXcds) * per_xcd + j;
-  if (t >= total) return;
-  TileJob jb;
-  const int64_t tile = t / slabs;
-  jb.slab = int(t - tile * slabs);
-  jb.e = a.moe_tiles[2 * tile];
-  jb.pair_base = a.moe_tiles[2 * tile + 1];
-  jb.P = __builtin_amdgcn_readfirstlane(min(kMoeTileRows, a.moe_offsets[jb.e + 1] - jb.pair_base));
+  const int64_t jt = j / slabs;
+  const int64_t tile = jt * kXcds + blockIdx.x % kXcds;
+  const int slab = int(j - jt * slabs);
+  const int32_t* rec = a.moe_recs + tile * kMoeRecInts;
+  const int tiles = a.moe_hdr[0];
+  const int e = rec[0];
+  const int n = rec[1];
+  if (threadIdx.x < kMoeTileRows) plist[threadIdx.x] = rec[kMoeRecHead + threadIdx.x];
+  if (tile >= tiles) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int64_t records = int64_t(gridDim.x) / kXcds / slabs * kXcds;
+      zero_unrouted(a, (tile - tiles) * slabs + slab, (records - tiles) * slabs);
+    }
+    return;
+  }
+  __syncthreads();
+  const TileJob jb{e, __builtin_amdgcn_readfirstlane(n), slab, plist};
   if ((a.K >> 6) % kChunk == 0) {
     run_tile<EPI, true>(a, jb, lds);
   } else {
@@ -499,7 +521,8 @@ int launch_moe_gemm(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s) 
   if (!moe_gemm_supports(a)) return 2;
   const int64_t slabs = epi == EPI_SWIGLU ? (a.I + moe_mm::kSlab / 2 - 1) / (moe_mm::kSlab / 2)
                                           : (a.N + moe_mm::kSlab - 1) / moe_mm::kSlab;
-  const int64_t blocks = (m_tiles * slabs + moe_mm::kXcds - 1) / moe_mm::kXcds * moe_mm::kXcds;
+  if (m_tiles % moe_mm::kXcds) return 2;
+  const int64_t blocks = m_tiles * slabs;
   if (blocks > 0x7FFFFFFF) return 2;
   const dim3 grid{unsigned(blocks), 1u, 1u};
   const dim3 block{unsigned(64 * moe_mm::kWaves), 1u, 1u};

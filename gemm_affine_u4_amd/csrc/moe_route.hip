@@ -1,14 +1,18 @@
 // Routed experts over a batch of tokens (prefill), the parts around the gathered GEMM:
-// bucketing the (token, slot) pairs by expert, zeroing the h of pairs with no expert,
-// and the per-token combine of the stage-2 products.  The pages keep the expert grid in
-// place and select experts by index ("Four Candles for the Cathedral", what's not in
-// this batch); prefill needs the selection the other way round, expert -> tokens, so
-// that each expert's weights are streamed once for all of its tokens.
+// bucketing the (token, slot) pairs by expert into tile records, and the per-token combine
+// of the stage-2 products.  The pages keep the expert grid in place and select experts by
+// index ("Four Candles for the Cathedral", what's not in this batch); prefill needs the
+// selection the other way round, expert -> tokens, so that each expert's weights are
+// streamed once for all of its tokens.
 //
-// Bucketing is deterministic: a pair's position inside its expert's bucket is the number
-// of pairs before it (in pair order token * topk + slot) routed to the same expert.  It
-// takes three small kernels: per-chunk expert histograms, one block turning them into
-// bucket offsets, chunk bases and the tile table, and per-chunk placement.
+// Expert e's bucket (its n_e pairs) fills tiles tb(e) .. tb(e) + ceil(n_e / 128) - 1, tb the
+// prefix of the tile counts over the experts; bucket position pos lands in tile
+// tb(e) + pos / 128, slot pos % 128, and each tile's record carries its expert, pair count
+// and pair indices, so that a GEMM block reads all it needs about its tile in one memory
+// round trip.  Up to 16384 pairs and 1024 experts one block does it all in one launch,
+// in LDS; above that three kernels (per-chunk histograms, one block for the prefixes and
+// record heads, per-chunk placement) do, with positions in pair order (token * topk +
+// slot) inside a bucket.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -19,6 +23,13 @@ constexpr int kScanThreads = 1024;   // the one block of the scan
 constexpr int kMaxChunks = 256;      // routing chunks (blocks of the count and place kernels)
 constexpr int kScanBatch = 16;       // chunks up to which a scan thread takes a whole expert row
 constexpr int kWaveBatch = 8;        // experts a scan wave loads at once above that
+// One block does the whole routing up to kOneMaxP pairs and kOneMaxE experts.
+constexpr int kOneMaxP = 16384;
+constexpr int kOneMaxE = kScanThreads;
+constexpr int kOneRegs = kOneMaxP / kScanThreads;              // pairs per thread (in registers)
+constexpr int kOneMaxTiles = kOneMaxP / kMoeTileRows + kOneMaxE;  // fewer tiles than this
+constexpr int kCopyBatch = 8;                                   // slots per thread per copy-out pass
+static_assert(kOneMaxP < (1 << 16) && kOneMaxTiles < (1 << 15), "packed prefixes");
 
 static __device__ __forceinline__ bool routed(int32_t e, int E) { return e >= 0 && e < E; }
 
@@ -70,15 +81,22 @@ static __device__ int block_exclusive_scan(int v, int* total) {
   return before + inc - v;
 }
 
+// The heads of expert e's records: tiles tb .. tb + ceil(n / kMoeTileRows) - 1, each with
+// the expert and its number of pairs.
+static __device__ void write_heads(int32_t* __restrict__ recs, int e, int n, int tb) {
+  for (int j = 0; j * kMoeTileRows < n; ++j)
+    *reinterpret_cast<int4*>(recs + int64_t(tb + j) * kMoeRecInts) = make_int4(e, min(kMoeTileRows, n - j * kMoeTileRows), 0, 0);
+}
+
 // One block.  (1) For each expert (a thread each up to kScanBatch chunks, else a wave
 // each): counts[e][c] becomes the exclusive prefix over chunks, and the expert's total is
 // kept.
-// (2) Over the experts: bucket offsets (prefix of the totals), then the tile table: expert
-// e's bucket is cut into tiles of `bm` pairs, written at the prefix of the tile counts.
+// (2) Over the experts: the first tile of each expert's records (prefix of the tile
+// counts) and the record heads.
 __global__ void __launch_bounds__(kScanThreads) moe_route_scan(int32_t* __restrict__ counts, int chunks, int E,
-                                                               int bm, int32_t* __restrict__ hdr,
-                                                               int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ tiles) {
+                                                               int32_t* __restrict__ hdr,
+                                                               int32_t* __restrict__ tbase,
+                                                               int32_t* __restrict__ recs) {
   __shared__ int tot[kMaxExpertsPrefill];
   if (chunks <= kScanBatch) {
     // few chunks: one thread per expert, a serial exclusive prefix over its row (all of
@@ -146,43 +164,41 @@ __global__ void __launch_bounds__(kScanThreads) moe_route_scan(int32_t* __restri
     const int e = e0 + j;
     const int n = e < E ? tot[e] : 0;
     n_sum += n;
-    t_sum += (n + bm - 1) / bm;
+    t_sum += (n + kMoeTileRows - 1) / kMoeTileRows;
   }
   int n_all, t_all;
-  int off = block_exclusive_scan(n_sum, &n_all);
+  block_exclusive_scan(n_sum, &n_all);
   int tix = block_exclusive_scan(t_sum, &t_all);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = e0 + j;
     if (e >= E) break;
     const int n = tot[e];
-    offsets[e] = off;
-    for (int s = 0; s < n; s += bm) {
-      tiles[2 * tix] = e;
-      tiles[2 * tix + 1] = off + s;
-      ++tix;
-    }
-    off += n;
+    tbase[e] = tix;
+    write_heads(recs, e, n, tix);
+    tix += (n + kMoeTileRows - 1) / kMoeTileRows;
   }
   if (threadIdx.x == 0) {
-    offsets[E] = n_all;
     hdr[0] = t_all;
     hdr[1] = n_all;
   }
 }
 
-// Places the pairs of chunk c: pair i routed to e goes to offsets[e] + counts[e][c] + (pairs
+// Places the pairs of chunk c: pair i routed to e takes bucket position counts[e][c] + (pairs
 // of the chunk before i routed to e).  The chunk is taken kRouteThreads pairs at a time; a
 // running count per expert carries over between passes.
 __global__ void __launch_bounds__(kRouteThreads) moe_route_place(const int32_t* __restrict__ ids, int64_t P,
                                                                  int64_t cs, int E, int chunks,
-                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ tbase,
                                                                  const int32_t* __restrict__ counts,
-                                                                 int32_t* __restrict__ pairs) {
+                                                                 int32_t* __restrict__ recs) {
   __shared__ int run[kMaxExpertsPrefill];
+  __shared__ int tb[kMaxExpertsPrefill];
   __shared__ int32_t sid[kRouteThreads];
-  for (int e = threadIdx.x; e < E; e += kRouteThreads)
-    run[e] = offsets[e] + counts[int64_t(e) * chunks + blockIdx.x];
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    run[e] = counts[int64_t(e) * chunks + blockIdx.x];
+    tb[e] = tbase[e];
+  }
   const int64_t base = int64_t(blockIdx.x) * cs;
   const int64_t end = min(base + cs, P);
   const int t = threadIdx.x;
@@ -195,20 +211,99 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_place(const int32_t* 
     if (ok) {
       int rank = 0;
       for (int j = 0; j < t; ++j) rank += sid[j] == e;
-      pairs[run[e] + rank] = int32_t(i);
+      const int pos = run[e] + rank;
+      recs[int64_t(tb[e] + pos / kMoeTileRows) * kMoeRecInts + kMoeRecHead + pos % kMoeTileRows] = int32_t(i);
     }
     __syncthreads();  // every thread has read run and sid
     if (ok) atomicAdd(&run[e], 1);
   }
 }
 
-// h of the pairs with no expert is zero (the gathered GEMM writes routed pairs only):
-// one thread per pair, which clears its row when the pair has no expert.
-__global__ void __launch_bounds__(256) moe_zero_unrouted(const int32_t* ids, int64_t P, int E, void* h, int64_t I,
-                                                         int f32) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= P || routed(ids[i], E)) return;
-  for (int64_t c = 0; c < I; ++c) store_out(h, i * I + c, 0.f, f32);
+// All of the routing in one block (P <= kOneMaxP pairs, E <= kOneMaxE experts), in LDS.
+// (1) Per-expert counts (LDS atomics); thread t takes pairs t, t + 1024, ..., kept in
+// registers.  (2) Prefixes over the experts of the counts (the buckets' offsets in one flat
+// bucket array) and of the tile counts (each expert's first tile); the record heads and
+// the table's length are written.  (3) Each pair takes the next free position of its
+// expert's bucket (an LDS atomic) and is written there.  (4) The tiles' pair slots are
+// copied out, 64 consecutive slots of one record per wave store.  The order inside a
+// bucket is whatever order the atomics took, so it may differ from call to call; every
+// result is the same, since a pair's outputs are computed with the same operations
+// wherever it sits in a tile.
+__global__ void __launch_bounds__(kScanThreads) moe_route_one(const int32_t* __restrict__ ids, int P, int E,
+                                                              int32_t* __restrict__ hdr,
+                                                              int32_t* __restrict__ recs) {
+  // The loops below have no branches, so that their LDS operations stay in flight together
+  // instead of one round trip each: a lane whose pair has no expert (or is past the end)
+  // counts and places it in a spare word of its own (spread over the banks), never read.
+  __shared__ int cnt[kOneMaxE + 64];         // pairs per expert, then its next free bucket position
+  __shared__ int32_t bucket[kOneMaxP + 64];  // the pairs, bucket after bucket
+  __shared__ int tile_off[kOneMaxTiles + 1]; // bucket position of each tile's first pair
+  const int tid = threadIdx.x;
+  const int spare = kOneMaxE + (tid & 63);
+  for (int e = tid; e < kOneMaxE + 64; e += kScanThreads) cnt[e] = 0;
+  int32_t v[kOneRegs];  // the pair's expert, or the lane's spare word
+#pragma unroll
+  for (int k = 0; k < kOneRegs; ++k) {
+    const int32_t e = ids[min(tid + k * kScanThreads, P - 1)];
+    v[k] = tid + k * kScanThreads < P && routed(e, E) ? e : spare;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kOneRegs; ++k) atomicAdd(&cnt[v[k]], 1);  // counts: the order of the adds does not matter
+  __syncthreads();
+  const int n = tid < E ? cnt[tid] : 0;
+  const int t = (n + kMoeTileRows - 1) / kMoeTileRows;
+  // both prefixes in one scan: pairs in the low 16 bits, tiles above (n_all <= 16384,
+  // t_all < 1152, so neither field carries into the other)
+  int packed_all;
+  const int packed = block_exclusive_scan(n | (t << 16), &packed_all);
+  const int off = packed & 0xFFFF, tb = packed >> 16;
+  const int n_all = packed_all & 0xFFFF, t_all = packed_all >> 16;
+  if (tid < E) {
+    cnt[tid] = off;
+    write_heads(recs, tid, n, tb);
+    for (int j = 0; j < t; ++j) tile_off[tb + j] = off + j * kMoeTileRows;
+  }
+  if (tid == 0) {
+    tile_off[t_all] = n_all;
+    hdr[0] = t_all;
+    hdr[1] = n_all;
+  }
+  __syncthreads();
+  // all of a thread's atomics first, then its writes, so that the atomics' round trips overlap
+  int pos[kOneRegs];
+#pragma unroll
+  for (int k = 0; k < kOneRegs; ++k) pos[k] = atomicAdd(&cnt[v[k]], 1);
+#pragma unroll
+  for (int k = 0; k < kOneRegs; ++k) bucket[v[k] < E ? pos[k] : kOneMaxP + (tid & 63)] = tid + k * kScanThreads;
+  __syncthreads();
+  // copy-out: 4 slots (16 bytes) per lane and store, kCopyBatch of them per thread at a
+  // time (their LDS reads in flight together); a tile ends where the next one starts (the
+  // next expert's bucket, for its last tile), and the slots of a partial group past the
+  // tile's end take any value (slots past a record's pair count are never read)
+  const int quads = t_all * (kMoeTileRows / 4);
+  for (int f0 = 0; f0 < quads; f0 += kCopyBatch * kScanThreads) {
+    int4 val[kCopyBatch];
+    bool ok[kCopyBatch];
+#pragma unroll
+    for (int k = 0; k < kCopyBatch; ++k) {
+      const int f = f0 + k * kScanThreads + tid;
+      const int tile = f < quads ? f / (kMoeTileRows / 4) : 0;
+      const int lo = tile_off[tile], hi = tile_off[tile + 1];
+      const int at = lo + 4 * (f % (kMoeTileRows / 4));
+      ok[k] = (f < quads) & (at < hi);
+      const int a0 = ok[k] ? at : 0;
+      val[k] = make_int4(bucket[a0], bucket[min(a0 + 1, kOneMaxP - 1)], bucket[min(a0 + 2, kOneMaxP - 1)],
+                         bucket[min(a0 + 3, kOneMaxP - 1)]);
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyBatch; ++k) {
+      const int f = f0 + k * kScanThreads + tid;
+      if (ok[k])
+        *reinterpret_cast<int4*>(recs + int64_t(f / (kMoeTileRows / 4)) * kMoeRecInts + kMoeRecHead +
+                                 4 * (f % (kMoeTileRows / 4))) = val[k];
+    }
+  }
 }
 
 // y[m, n] = sum over the token's slots k with an expert, in increasing k, of
@@ -243,15 +338,15 @@ __global__ void __launch_bounds__(256) moe_combine(const int32_t* ids, int64_t M
 MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
   MoeLayout L;
   L.P = M * topk;
-  L.tmax = (L.P + kMoeTileRows - 1) / kMoeTileRows + E;
+  // every expert's last tile may be partial: fewer than P / 128 + E tiles in all
+  L.recs_n = ((L.P + kMoeTileRows - 1) / kMoeTileRows + E + 7) / 8 * 8;
   L.chunk_pairs = route_chunk(L.P);
   L.chunks = (L.P + L.chunk_pairs - 1) / L.chunk_pairs;
   auto up = [](uint64_t b) { return (b + 255) / 256 * 256; };
   uint64_t o = 0;
   L.hdr = o;      o = up(o + 16);
-  L.offsets = o;  o = up(o + uint64_t(E + 1) * 4);
-  L.pairs = o;    o = up(o + uint64_t(L.P) * 4);
-  L.tiles = o;    o = up(o + uint64_t(L.tmax) * 8);
+  L.recs = o;     o = up(o + uint64_t(L.recs_n) * kMoeRecInts * 4);
+  L.tbase = o;    o = up(o + uint64_t(E) * 4);
   L.chunk = o;    o = up(o + uint64_t(L.chunks) * uint64_t(E) * 4);
   L.z = o;        o = up(o + uint64_t(L.P) * uint64_t(out_rows) * 4);
   L.total = o;
@@ -261,16 +356,21 @@ MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows) {
 int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, void* ws, hipStream_t s) {
   const MoeLayout L = moe_layout(M, topk, E, 0);
   char* b = static_cast<char*>(ws);
+  int32_t* hdr = reinterpret_cast<int32_t*>(b + L.hdr);
+  int32_t* recs = reinterpret_cast<int32_t*>(b + L.recs);
+  if (L.P <= kOneMaxP && E <= kOneMaxE) {
+    moe_route_one<<<dim3{1u, 1u, 1u}, dim3{unsigned(kScanThreads), 1u, 1u}, 0, s>>>(ids, int(L.P), int(E), hdr,
+                                                                                   recs);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+  }
   int32_t* counts = reinterpret_cast<int32_t*>(b + L.chunk);
-  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* tbase = reinterpret_cast<int32_t*>(b + L.tbase);
   const dim3 blk{unsigned(kRouteThreads), 1u, 1u};
   const dim3 grid{unsigned(L.chunks), 1u, 1u};
   moe_route_count<<<grid, blk, 0, s>>>(ids, L.P, L.chunk_pairs, int(E), int(L.chunks), counts);
-  moe_route_scan<<<dim3{1u, 1u, 1u}, dim3{unsigned(kScanThreads), 1u, 1u}, 0, s>>>(
-      counts, int(L.chunks), int(E), kMoeTileRows, reinterpret_cast<int32_t*>(b + L.hdr), offsets,
-      reinterpret_cast<int32_t*>(b + L.tiles));
-  moe_route_place<<<grid, blk, 0, s>>>(ids, L.P, L.chunk_pairs, int(E), int(L.chunks), offsets, counts,
-                                       reinterpret_cast<int32_t*>(b + L.pairs));
+  moe_route_scan<<<dim3{1u, 1u, 1u}, dim3{unsigned(kScanThreads), 1u, 1u}, 0, s>>>(counts, int(L.chunks), int(E),
+                                                                                  hdr, tbase, recs);
+  moe_route_place<<<grid, blk, 0, s>>>(ids, L.P, L.chunk_pairs, int(E), int(L.chunks), tbase, counts, recs);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
@@ -280,31 +380,29 @@ int launch_moe_prefill(int stage, const GemmArgs& g, const int32_t* ids, int64_t
   const char* b = static_cast<const char*>(ws);
   GemmArgs a = g;
   a.moe_hdr = reinterpret_cast<const int32_t*>(b + L.hdr);
-  a.moe_tiles = reinterpret_cast<const int32_t*>(b + L.tiles);
-  a.moe_offsets = reinterpret_cast<const int32_t*>(b + L.offsets);
-  a.moe_pairs = reinterpret_cast<const int32_t*>(b + L.pairs);
-  const unsigned zb = unsigned((L.P + 255) / 256);
+  a.moe_recs = reinterpret_cast<const int32_t*>(b + L.recs);
   if (stage == 0) {
-    // stage 1: h [P][I] of the routed pairs from the gathered kernel, zeros for the others
+    // stage 1: h [P][I] of the routed pairs from the gathered kernel, whose idle blocks
+    // write the zeros of the others
     a.out0 = out;
     a.moe_w = nullptr;
     a.moe_div = topk;
-    if (int st = launch_moe_gemm(EPI_SWIGLU, a, L.tmax, s)) return st;
-    moe_zero_unrouted<<<dim3{zb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, L.P, int(E), out, a.I, a.f32_out);
-  } else {
-    // stage 2: z = p * (D_e h) per routed pair (fp32, workspace), then the per-token sum
-    float* z = reinterpret_cast<float*>(const_cast<char*>(b) + L.z);
-    const int f32_y = a.f32_out;
-    a.out0 = z;
-    a.f32_out = 1;
-    a.moe_div = 1;
-    if (int st = launch_moe_gemm(EPI_LINEAR, a, L.tmax, s)) return st;
-    const unsigned mb = unsigned(M < 4096 ? M : 4096);
-    if (a.N % 4 == 0)
-      moe_combine<true><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
-    else
-      moe_combine<false><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
+    a.moe_ids = ids;
+    a.moe_E = E;
+    return launch_moe_gemm(EPI_SWIGLU, a, L.recs_n, s);
   }
+  // stage 2: z = p * (D_e h) per routed pair (fp32, workspace), then the per-token sum
+  float* z = reinterpret_cast<float*>(const_cast<char*>(b) + L.z);
+  const int f32_y = a.f32_out;
+  a.out0 = z;
+  a.f32_out = 1;
+  a.moe_div = 1;
+  if (int st = launch_moe_gemm(EPI_LINEAR, a, L.recs_n, s)) return st;
+  const unsigned mb = unsigned(M < 4096 ? M : 4096);
+  if (a.N % 4 == 0)
+    moe_combine<true><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
+  else
+    moe_combine<false><<<dim3{mb, 1u, 1u}, dim3{256u, 1u, 1u}, 0, s>>>(ids, M, int(topk), int(E), z, a.N, out, f32_y);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 

@@ -99,14 +99,14 @@ struct GemmArgs {
   int64_t M, K, N;         // N = weight rows (SWIGLU: 2*I); routed experts: rows of one expert
   int64_t q_out, kv_out, I;
   int f32_out;
-  // routed experts over a batch of tokens (gathered GEMM; null otherwise): the tile table
-  // and bucketed pairs written by the routing kernels, and x row = pair / moe_div
-  const int32_t* moe_hdr;      // [0] = number of tiles in the table
-  const int32_t* moe_tiles;    // [tiles][2] = (expert, first bucket position)
-  const int32_t* moe_offsets;  // [E+1] bucket boundaries
-  const int32_t* moe_pairs;    // [pairs] bucketed pair indices (token * topk + slot)
+  // routed experts over a batch of tokens (gathered GEMM; null otherwise): the tile
+  // records written by the routing kernels, and x row = pair / moe_div
+  const int32_t* moe_hdr;      // [0] = number of tiles, [1] = routed pairs
+  const int32_t* moe_recs;     // [tiles][kMoeRecInts]: expert, pairs n, 0, 0, then n pair indices
   const float* moe_w;          // stage 2: combine weight of each pair; null in stage 1
   int64_t moe_div;             // topk in stage 1 (x row of a pair), 1 in stage 2
+  const int32_t* moe_ids;      // stage 1: expert of each pair (the idle blocks zero unrouted h)
+  int64_t moe_E;               // stage 1: experts in the grid
   int bits;                    // code width or kFmtFp8E4M3
   int gshift;                  // group size = 32 << gshift
   RopeArgs rope;               // EPI_ROPE only
@@ -131,7 +131,7 @@ QMM_WIDTH_LAUNCHERS(b8)
 QMM_WIDTH_LAUNCHERS(f8)
 // The routed experts over a batch (4-bit codes, group 64; moe_gemm.hip): each block one
 // routing tile x one slab of 128 expert rows (SWIGLU: 64 gate + their 64 up rows);
-// m_tiles = bound on the tile table.
+// m_tiles = the number of tile records (a multiple of 8).
 bool moe_gemm_supports(const GemmArgs& a);
 int launch_moe_gemm(int epi, const GemmArgs& a, int64_t m_tiles, hipStream_t s);
 
@@ -180,9 +180,15 @@ int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
 #endif
 constexpr int kMoeTileRows = QMM_MOE_TILE_ROWS;  // pairs per routing tile (a multiple of 32, <= 128)
 constexpr int kMaxExpertsPrefill = 4096; // experts the bucketing handles (LDS histogram)
+// A routing tile's record: expert, number of pairs n (1 .. kMoeTileRows), two unused words,
+// then the tile's pair indices (token * topk + slot) in bucket order; slots past n unused.
+constexpr int kMoeRecHead = 4;
+constexpr int kMoeRecInts = kMoeRecHead + kMoeTileRows;
 struct MoeLayout {
-  int64_t P, tmax, chunk_pairs, chunks;  // pairs, bound on tiles, pairs per routing chunk, chunks
-  uint64_t hdr, offsets, pairs, tiles, chunk, z, total;
+  // pairs, records (a bound on the tiles, rounded up to a multiple of 8), pairs per routing
+  // chunk and chunks (the multi-block routing only)
+  int64_t P, recs_n, chunk_pairs, chunks;
+  uint64_t hdr, recs, tbase, chunk, z, total;
 };
 MoeLayout moe_layout(int64_t M, int64_t topk, int64_t E, int64_t out_rows);
 int launch_moe_route(const int32_t* ids, int64_t M, int64_t topk, int64_t E, void* ws, hipStream_t s);

@@ -241,3 +241,50 @@ def test_moe_prefill_35B_shape_128_tokens():
     ids, p = synth.gen_prefill_routing(synth.CFG_MOE, 1, M, shape.E, shape.topk)
     say(f"[moe prefill] {shape.name}, M={M}")
     check_both_stages(shape, synth.CFG_MOE, 1, M, ids, p, "35B M=128")
+
+
+def test_moe_prefill_1500_experts():
+    """1500 experts (hidden 128, I 64, top-2, 400 tokens: most experts get no pair, none
+    more than a few): above 1024 experts the routing runs as three kernels even for few
+    pairs; a pair with no expert."""
+    shape = synth.MoEShape("MoE prefill (hidden 128, 1500 experts, I 64, top-2)", 128, 1500, 64, 2)
+    M = 400
+    ids, p = synth.gen_prefill_routing(synth.CFG_TEST, 10, M, shape.E, shape.topk, skew=1.0)
+    ids[3, 1] = -1
+    say(f"[moe prefill] {shape.name}, M={M}, experts used {len(np.unique(ids[ids >= 0]))}")
+    g1, _ = check_both_stages(shape, synth.CFG_TEST, 10, M, ids, p, "1500 experts")
+    assert np.all(g1[3, 1] == 0)
+
+
+def test_moe_prefill_routing_above_16384_pairs():
+    """Above 16384 (token, slot) pairs the routing runs as three kernels (bucket positions
+    in pair order) instead of one block (positions in the order its atomics took): 8256
+    tokens x top-8 of 64 experts (hidden 128, I 64), ~1000 pairs per expert.  The oracle
+    checks a sample of tokens of both stages; the first 2048 tokens alone (16384 pairs, one
+    block) give the same bits for those tokens, since a pair's outputs do not depend on
+    where it sits in its expert's tiles."""
+    shape = synth.MoEShape("MoE prefill (hidden 128, 64 experts, I 64, top-8)", 128, 64, 64, 8)
+    M, Ms = 8256, 2048
+    cfg = synth.CFG_TEST
+    ids, p = synth.gen_prefill_routing(cfg, 12, M, shape.E, shape.topk)
+    ids[100, 5] = -1
+    assert M * shape.topk > 16384 and Ms * shape.topk == 16384
+    gu, dn = grids(shape, cfg, 12)
+    x = synth.gen_x(cfg, 12, 0, M, shape.hidden)
+    h_in = synth.to_bf16_bits(0.05 * synth.bf16_bits_to_f32(synth.gen_x(cfg, 12, 1, M * shape.topk, shape.I)))
+    h_in = h_in.reshape(M, shape.topk, shape.I)
+    say(f"[moe prefill] {shape.name}, M={M} and its first {Ms} tokens")
+    r = Routed(ids, shape.E, shape.hidden)
+    g1 = stage1(x, gu, r, shape.I)
+    g2 = stage2(h_in, dn, r, p)
+    assert np.all(g1[100, 5] == 0)
+    sample = np.unique(np.r_[0, 100, M - 1, np.random.default_rng(12).choice(M, 13, replace=False)])
+    h, th = orc.moe_prefill_gate_up(x[sample], gu.codes, gu.scales, gu.biases, ids[sample], 2 * shape.I,
+                                     bf16_weights=bf16_term(M, shape.hidden))
+    assert_within(g1[sample], h, th, "16384+ pairs, stage 1 (sampled tokens)")
+    y, ty = orc.moe_prefill_down_combine(h_in[sample], dn.codes, dn.scales, dn.biases, ids[sample], p[sample],
+                                         bf16_weights=bf16_term(M, shape.I))
+    assert_within(g2[sample], y, ty, "16384+ pairs, stage 2 (sampled tokens)")
+    rs = Routed(ids[:Ms], shape.E, shape.hidden)
+    assert np.array_equal(stage1(x[:Ms], gu, rs, shape.I), g1[:Ms])
+    assert np.array_equal(stage2(h_in[:Ms], dn, rs, p[:Ms]), g2[:Ms])
