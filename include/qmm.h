@@ -223,8 +223,9 @@ int qmm_moe_layer(const uint16_t* x, int64_t K, const uint32_t* gu_codes, const 
  * tokens routed to it (gathered through the bucket), instead of once per token.
  *
  * Three calls, in stream order:
- *   qmm_moe_route    buckets the pairs of expert_ids by expert into the workspace
- *                    (deterministic: by expert, then by pair index);
+ *   qmm_moe_route    buckets the pairs of expert_ids by expert into the workspace, as
+ *                    records of routing tiles (the order of the pairs inside an
+ *                    expert's bucket is not fixed; no result depends on it);
  *   qmm_moe_prefill  stage QMM_MOE_GATE_UP_SWIGLU, then stage QMM_MOE_DOWN_COMBINE,
  *                    both reading that routing.
  * The stages run on a gathered kernel over routing tiles of up to 128 pairs of one expert,
