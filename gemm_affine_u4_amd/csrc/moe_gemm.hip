@@ -8,20 +8,20 @@
 // the kernel is built so that each weight is read and dequantized exactly once per routing
 // tile, and the activations of the tile's pairs are what is shared through LDS.
 //
-// A block (4 waves) takes one routing tile (up to 128 pairs of one expert) and one slab of
+// A block (4 waves) takes one routing tile (up to 96 pairs of one expert) and one slab of
 // 128 of the expert's weight rows, and walks K one 64-wide group per step:
 //   * each wave owns 32 weight rows and holds them, dequantized, as the A operand of
 //     v_mfma_f32_32x32x16_bf16: lane l reads 16 bytes (32 codes) of row l % 32 per step,
 //     half l / 32 of the group, and turns them into w = s*q + b in fp32, rounded to bf16
 //     (the same weights as the LDS-dequant GEMM), straight into registers;
 //   * the tile's activation rows (gathered through the bucket) go global -> LDS directly
-//     (buffer_load ... lds) two steps ahead, into a ring of three stages, and every wave
+//     (buffer_load ... lds) one step ahead, into a ring of two stages, and every wave
 //     reads them as the B operands of its multiplies: one 32 x 32 accumulator per 32 pairs.
 // Since MFMA lane l pairs k-slot 8 (l / 32) + t of A with the same slot of B, the slots of
 // a 16-wide multiply may stand for any 16 inputs of the group, as long as both operands
 // agree: multiply j takes inputs 32 h + 8 j .. +7 from the lanes of half h, so a lane's A
 // fragment for multiply j is one code word and its B fragment one 16-byte chunk of the row.
-// The number of 32-pair blocks of a tile (1..4) is a template parameter of the loop, so the
+// The number of 32-pair blocks of a tile (1..3) is a template parameter of the loop, so the
 // multiplies and the loads of a step are fixed and the wait counts are constants.
 #include <type_traits>
 #include <utility>
@@ -64,10 +64,28 @@ constexpr int kCodeSteps = 2;               // steps per code chunk
 constexpr int kCodeRow = 32 * kCodeSteps;   // bytes of one row in a code chunk
 constexpr int kCodeBuf = kSlab * kCodeRow;  // bytes per code chunk buffer
 // LDS of a block: the activation stages (MB * 4 KB each) and the code chunk ring, whose depth
-// depends on the tile: 4 chunks (requested 5-6 steps ahead) where the stages leave room, else 2.
-constexpr int kLds = 48 * 1024;
+// depends on the tile: 4 chunks (requested 5-6 steps ahead) where the stages leave room, else
+// 3 or 2.
+// LDS pool and blocks per CU: 40 KB and 4 (16 waves per CU, at most 128 registers each;
+// tiles of up to 96 pairs, whose activation stages leave room for a code ring) measured
+// 1-10 us per layer faster than 48 KB and 3 with tiles of up to 128 pairs, and 5 blocks
+// of 32 KB (96 registers: spills) slower.
+#ifndef QMM_MOE_LDS_KB
+#define QMM_MOE_LDS_KB 40
+#endif
+#ifndef QMM_MOE_BLOCKS_PER_CU
+#define QMM_MOE_BLOCKS_PER_CU 4
+#endif
+constexpr int kLds = QMM_MOE_LDS_KB * 1024;
+constexpr int kBlocksPerCU = QMM_MOE_BLOCKS_PER_CU;
+// the pair list sits beside the pool, or (when that would cost a block per CU) in the pool,
+// read into registers before the pool's first loads
+constexpr bool kPairsInPool = (kLds + kMoeTileRows * 4) * kBlocksPerCU > 160 * 1024;
 template <int MB>
-constexpr int code_chunks() { return kXStages * MB * 32 * kRow * 2 + 4 * kCodeBuf <= kLds ? 4 : 2; }
+constexpr int code_chunks() {
+  return kXStages * MB * 32 * kRow * 2 + 4 * kCodeBuf <= kLds ? 4
+       : kXStages * MB * 32 * kRow * 2 + 3 * kCodeBuf <= kLds ? 3 : 2;
+}
 static_assert(kXStages > kXDist && kXDist >= 1 && kXDist <= 2, "activation ring");
 static_assert(kXStages * kMaxMB * 32 * kRow * 2 + 2 * kCodeBuf <= kLds, "LDS of the largest tile");
 static_assert(kSDist >= kXDist && kSDist <= kChunk, "request order the wait counts rely on");
@@ -287,6 +305,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
     const uint32_t chunk = uint32_t(lane & 7) ^ swz(uint32_t(r));
     xoff[j] = uint32_t(xrow) * K * 2u + chunk * 16u;
   }
+  // the pairs of the lane's output columns, for the epilogue (kept in registers only when
+  // the list sits in the pool, which the loads below overwrite)
+  int32_t pairs_of[MB];
+  if constexpr (kPairsInPool) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) pairs_of[b] = jb.pairs[min(32 * b + m, jb.P - 1)];
+    __syncthreads();  // every wave has read the list before the pool fills
+  }
   auto stage = [&](int p) -> uint16_t* { return xs_all + p * (kXStageBytes / 2); };
   auto load_x = [&](uint16_t* dst, int ks) {
 #pragma unroll
@@ -423,7 +449,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   for (int b = 0; b < MB; ++b) {
     const int q = 32 * b + m;
     if (q >= jb.P) continue;
-    const int64_t pr = jb.pairs[q];
+    const int64_t pr = kPairsInPool ? pairs_of[b] : jb.pairs[q];
     if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -478,11 +504,11 @@ __device__ __forceinline__ void zero_unrouted(const GemmArgs& a, int64_t q, int6
 // knows) spread over all eight.  The tile is known from the block index alone, so the
 // table's length, the record head and the pair indices come in one memory round trip.
 template <int EPI>
-__global__ void __launch_bounds__(256, 3) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
+__global__ void __launch_bounds__(256, kBlocksPerCU) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
   // one LDS object: with a second one beside the pool the compiler waits for the pool's
   // direct-to-LDS loads before every LDS read (vmcnt), which undoes the prefetch
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds + kMoeTileRows * 4];
-  int32_t* plist = reinterpret_cast<int32_t*>(lds + kLds);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds + (kPairsInPool ? 0 : kMoeTileRows * 4)];
+  int32_t* plist = reinterpret_cast<int32_t*>(lds + (kPairsInPool ? 0 : kLds));
   const int64_t j = blockIdx.x / kXcds;
   const int64_t jt = j / slabs;
   const int64_t tile = jt * kXcds + blockIdx.x % kXcds;

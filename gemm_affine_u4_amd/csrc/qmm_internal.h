@@ -176,7 +176,7 @@ int launch_bmv(int epi, const GemvArgs& a, int64_t M, hipStream_t s);
 // Routed experts over a batch (prefill): the workspace holds the bucketed routing and
 // the fp32 stage-2 products; all offsets in bytes, 256-byte aligned.
 #ifndef QMM_MOE_TILE_ROWS
-#define QMM_MOE_TILE_ROWS 128
+#define QMM_MOE_TILE_ROWS 96
 #endif
 constexpr int kMoeTileRows = QMM_MOE_TILE_ROWS;  // pairs per routing tile (a multiple of 32, <= 128)
 constexpr int kMaxExpertsPrefill = 4096; // experts the bucketing handles (LDS histogram)

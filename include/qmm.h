@@ -228,7 +228,7 @@ int qmm_moe_layer(const uint16_t* x, int64_t K, const uint32_t* gu_codes, const 
  *                    expert's bucket is not fixed; no result depends on it);
  *   qmm_moe_prefill  stage QMM_MOE_GATE_UP_SWIGLU, then stage QMM_MOE_DOWN_COMBINE,
  *                    both reading that routing.
- * The stages run on a gathered kernel over routing tiles of up to 128 pairs of one expert,
+ * The stages run on a gathered kernel over routing tiles of up to 96 pairs of one expert,
  * each expert row dequantized once per tile.
  * A small batch (M * topk <= 288 pairs: most experts then see one token or none) runs
  * pair by pair instead, on the kernels of qmm_moe_gather: stage 1 one SwiGLU GEMV per
