@@ -47,12 +47,15 @@ constexpr int kCodeLoads = kBits / 4 + (kBits % 4 != 0 ? 1 : 0);
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256;                 // rows of x per block
-constexpr int kBN = 256;                 // weight rows per block
+constexpr int kBM = 256;                 // rows of x per tile
+constexpr int kBN = 256;                 // weight rows per tile
 constexpr int kRow = 64;                 // bf16 per LDS row (one 64-wide group)
-constexpr int kStage = kBM * kRow;       // bf16 per LDS stage (32 KB)
+constexpr int kStage = kBN * kRow;       // bf16 per weight stage (32 KB)
 constexpr int kXcds = 8;
-static_assert(kBM == kBN, "x and weight stages share one shape");
+#ifndef QMM_GEMM_SPLIT_TAIL
+#define QMM_GEMM_SPLIT_TAIL 1
+#endif
+constexpr bool kSplitTail = QMM_GEMM_SPLIT_TAIL;  // the last partial round as half-height blocks
 
 // Bank-group swizzle of LDS row r (see the header).
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
@@ -76,6 +79,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // operations are done, then meet the other waves.  Written as one asm block (a compiler
 // memory barrier) because the compiler's own barrier waits for every outstanding load,
 // including the x tile requested for two steps later.
+// 16 bytes per lane from buffer r (offset voff + soff) straight into LDS at dst (one wave
+// instruction).  A plain function: with the builtin written in the kernel template itself,
+// where its arguments depend on the template parameters, the host pass dropped the kernel's
+// specializations and left their launch stubs undefined.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_loads_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -102,27 +113,37 @@ __device__ __forceinline__ int64_t gemm_weight_row(const GemmArgs& a, int64_t nt
   }
 }
 
-template <int EPI>
-__global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t n_tiles,
-                                                        int64_t tiles_per_xcd) {
+// BM = kBM: a block computes a whole 256 x 256 tile.  BM = kBM / 2: a block computes half
+// of one (128 rows of x, rows 128 h .. of the tile for half h) against the whole weight tile,
+// which it dequantizes in full: used for a last round of tiles that would leave more than
+// half of the CUs idle, so that it runs in about the time of the half-height blocks.
+template <int EPI, int BM>
+__global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_tiles, int64_t tile0,
+                                                        int64_t units, int64_t units_per_xcd) {
+  constexpr int kSplit = kBM / BM;      // blocks per tile
+  constexpr int kI = BM / 64;           // 32-row x sub-tiles per wave (4 or 2)
+  constexpr int kXStage = BM * kRow;    // bf16 per x stage
   // One variable per x stage, and the two weight stages in a variable of their own: the
   // compiler then knows that the x stage being filled by a direct-to-LDS load aliases
   // neither the x stage nor the weight stage being read.
-  __shared__ __attribute__((aligned(1024))) uint16_t As0[kStage], As1[kStage], As2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[kXStage], As1[kXStage], As2[kXStage];
   __shared__ __attribute__((aligned(1024))) uint16_t Bs[2 * kStage];
 
-  // XCD-aware tile order: the blocks dealt to XCD x take tiles x*tiles_per_xcd + j,
-  // row tiles fastest.
+  // XCD-aware order: the blocks dealt to XCD x take units x*units_per_xcd + j (a unit is a
+  // tile, or half of one; the halves of a tile are consecutive, so they share the XCD and its
+  // L2 copy of the weight tile), tiles from tile0 on, row tiles fastest.
   const int64_t bid = blockIdx.x;
-  const int64_t tile = (bid % kXcds) * tiles_per_xcd + bid / kXcds;
-  if (tile >= m_tiles * n_tiles) return;
+  const int64_t unit = (bid % kXcds) * units_per_xcd + bid / kXcds;
+  if (unit >= units) return;
+  const int64_t tile = tile0 + unit / kSplit;
   const int64_t mt = tile % m_tiles;
   const int64_t nt = tile / m_tiles;
+  const int64_t xrow0 = mt * kBM + (unit % kSplit) * BM;  // first x row of the block
 
-  // source row of tile row r (x rows [mt*kBM, mt*kBM + kBM); a row past M reads row M - 1,
+  // source row of block row r (x rows [xrow0, xrow0 + BM); a row past M reads row M - 1,
   // never stored)
   auto x_row = [&](int r) -> int64_t {
-    const int64_t m = mt * kBM + r;
+    const int64_t m = xrow0 + r;
     return m < a.M ? m : a.M - 1;
   };
 
@@ -135,14 +156,14 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   const uint32_t groups = K >> (5 + a.gshift);  // scale/bias groups per row (group 32 << gshift)
 
   // ---- x tile: global -> LDS ----------------------------------------------------------
-  // Instruction j (0..7) of wave w fills LDS rows 64 w + 8 j + L / 8, slot L % 8 (lane L
-  // lands at byte 16 L); that slot holds chunk (L % 8) ^ swz(row) = (L % 8) ^ (L / 8) ^ (j & 1).
+  // Instruction j (j < kI) of wave w fills LDS rows (BM / 8) w + 8 j + L / 8, slot L % 8 (lane
+  // L lands at byte 16 L); that slot holds chunk (L % 8) ^ swz(row) = (L % 8) ^ (L / 8) ^ (j & 1).
   // A row past M reads row M - 1 (never stored).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint64_t(a.M) * K * 2);
-  uint32_t xoff[4];
+  uint32_t xoff[kI];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t r = x_row(32 * wave + 8 * j + (lane >> 3));
+  for (int j = 0; j < kI; ++j) {
+    const int64_t r = x_row((BM / 8) * wave + 8 * j + (lane >> 3));
     const uint32_t chunk = uint32_t((lane & 7) ^ (lane >> 3) ^ (j & 1));
     xoff[j] = uint32_t(r) * K * 2 + chunk * 16u;
   }
@@ -152,10 +173,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   };
   auto load_x = [&](uint16_t* dst, int ks) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(dst + (32 * wave + 8 * j) * kRow), 16, xoff[j],
-          uint32_t(ks) * 128u, 0, 0);
+    for (int j = 0; j < kI; ++j) load_lds16(xr, dst + ((BM / 8) * wave + 8 * j) * kRow, xoff[j], uint32_t(ks) * 128u);
   };
 
   // ---- weight tile: global -> registers -> dequant -> LDS -----------------------------
@@ -210,7 +228,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     r.sv = __builtin_amdgcn_raw_buffer_load_b16(sr, go, 0, 0);
     r.bv = __builtin_amdgcn_raw_buffer_load_b16(br, go, 0, 0);
   };
-  constexpr int kStepLoads = 4 + kCodeLoads + 2;  // vector-memory loads one step requests per lane
+  constexpr int kStepLoads = kI + kCodeLoads + 2;  // vector-memory loads one step requests per lane
   // Piece p (0..3): codes 8p .. 8p+7 of the half row (-> w = s*q + b in fp32 -> bf16, 16
   // bytes) into chunk 4 wh + p of the row in stage `dst`.
   auto store_piece = [&](const StepRegs& r, uint16_t* dst, int p) {
@@ -255,9 +273,9 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   };
 
   // ---- MFMA operands from LDS ---------------------------------------------------------
-  f32x16_t acc[4][2];
+  f32x16_t acc[kI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
@@ -274,17 +292,17 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
 #pragma unroll
   for (int q = 0; q < 4; ++q) opoff[q] = lr * kRow + (uint32_t(2 * q + (lane >> 5)) ^ swz(lr)) * 8u;
   struct Frags {
-    bf16x8_t a[4], b[2];
+    bf16x8_t a[kI], b[2];
   };
   auto load_frags = [&](Frags& f, const uint16_t* as, const uint16_t* bs, int q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + (128 * wm + 32 * i) * kRow + opoff[q]);
+    for (int i = 0; i < kI; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(as + ((BM / 2) * wm + 32 * i) * kRow + opoff[q]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t*>(bs + btile_row(j) * kRow + opoff[q]);
   };
   auto mfma16 = [&](const Frags& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
@@ -293,11 +311,12 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   // matrix pipe, so the dequantization's ~24 VALU ops are spread 3 per MFMA (they then
   // run while the MFMA executes) and its LDS store goes late in the slot.
   auto interleave_slot = [&]() {
+    constexpr int kMfma = 2 * kI;  // MFMAs per slot
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
-      if (i == 6) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // the LDS store
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 24 / kMfma, 0);    // its share of the VALU
+      if (i == kMfma - 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // the LDS store
     }
   };
 
@@ -378,11 +397,11 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   // A lane thus owns 4 consecutive columns of one row per register quad and writes them
   // with one 8-byte (bf16) or 16-byte (fp32) store where they share a destination and the
   // address is aligned, element by element otherwise (ragged edges, odd row strides).
-  const int trow0 = 128 * wm + (lane & 31);  // tile row of this lane's output row, i = 0
+  const int trow0 = (BM / 2) * wm + (lane & 31);  // block row of this lane's output row, i = 0
   const int csub = 4 * (lane >> 5);
   // output row of tile row trow0 + 32 i, false if the row does not exist
   auto out_row = [&](int i, int64_t* m) -> bool {
-    *m = mt * kBM + trow0 + 32 * i;
+    *m = xrow0 + trow0 + 32 * i;
     return *m < a.M;
   };
   // 4 consecutive outputs from element idx: one vector store when all 4 exist and the
@@ -416,7 +435,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
     const float* trow[4];
     bool have[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kI; ++i) {
       have[i] = out_row(i, &mrow[i]);
       const int32_t pos = have[i] ? min(max(ra.positions[mrow[i]], 0), ra.max_pos - 1) : 0;
       trow[i] = ra.cos_sin + int64_t(pos) * ra.rot;
@@ -442,7 +461,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
           default: dst = ra.gate; nh = ra.n_q; break;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kI; ++i) {
           if (!have[i]) continue;
           float va[4], vb[4];
 #pragma unroll
@@ -474,7 +493,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
           const float lba = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.ra]) : 0.f;
           const float lbb = a.lin_bias ? bf16_bits_to_f32(a.lin_bias[rp.rb]) : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < kI; ++i) {
             if (!have[i]) continue;
             rope_store(ra, a.out0, a.out1, a.out2, rp, mrow[i], acc[i][0][4 * g + e] + lba,
                        acc[i][1][4 * g + e] + lbb, a.f32_out);
@@ -490,7 +509,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
         if (p0 >= a.I) return;
         const int nvalid = int(min<int64_t>(4, a.I - p0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kI; ++i) {
           int64_t m;
           if (!out_row(i, &m)) continue;
           float v[4];
@@ -529,7 +548,7 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
         route(n0, dst, ld, cn, end);
         const bool one_range = n0 + 3 < end;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kI; ++i) {
           int64_t m;
           if (!out_row(i, &m)) continue;
           float v[4];
@@ -553,29 +572,54 @@ __global__ void __launch_bounds__(512, 1) gemm_u4_kernel(GemmArgs a, int64_t m_t
   }
 }
 
+// One launch over tiles [tile0, tile0 + tiles) of the grid, each as one block (half = false)
+// or as two half-height blocks.
+static int launch_tiles(int epi, bool half, const GemmArgs& a, int64_t m_tiles, int64_t tile0, int64_t tiles,
+                        hipStream_t s) {
+  const int64_t split = half ? 2 : 1;
+  const int64_t units = tiles * split;
+  // whole tiles per XCD range, so that the halves of a tile land on one XCD
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds * split;
+  const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
+  const dim3 block{512u, 1u, 1u};
+#define QMM_GEMM_LAUNCH(E)                                                                          \
+  do {                                                                                              \
+    if (half) gemm_u4_kernel<E, kBM / 2><<<grid, block, 0, s>>>(a, m_tiles, tile0, units, per_xcd); \
+    else gemm_u4_kernel<E, kBM><<<grid, block, 0, s>>>(a, m_tiles, tile0, units, per_xcd);          \
+  } while (0)
+  if (epi == EPI_LINEAR) {
+    QMM_GEMM_LAUNCH(EPI_LINEAR);
+  } else if (epi == EPI_QKV) {
+    QMM_GEMM_LAUNCH(EPI_QKV);
+  } else if (epi == EPI_ROPE) {
+#if QMM_BITS == 4
+    QMM_GEMM_LAUNCH(EPI_ROPE);
+#else
+    return 2;  // the rotary epilogue is built for 4-bit codes only
+#endif
+  } else {
+    QMM_GEMM_LAUNCH(EPI_SWIGLU);
+  }
+#undef QMM_GEMM_LAUNCH
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// One block per CU: after the whole rounds of tiles, a remainder of at most half the CUs
+// runs as half-height blocks (two per tile) in a launch of its own, which fills up to all
+// of the CUs and takes about the time of one such block instead of a whole tile.
 int launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   const int64_t m_tiles = (a.M + kBM - 1) / kBM;
   const int64_t n_tiles = epi == EPI_SWIGLU ? (a.I + kBN / 2 - 1) / (kBN / 2)
                           : epi == EPI_ROPE ? ((a.N >> 1) + kBN / 2 - 1) / (kBN / 2)
                                             : (a.N + kBN - 1) / kBN;
   const int64_t tiles = m_tiles * n_tiles;
-  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-  const dim3 grid{unsigned(per_xcd * kXcds), 1u, 1u};
-  const dim3 block{512u, 1u, 1u};
-  if (epi == EPI_LINEAR) {
-    gemm_u4_kernel<EPI_LINEAR><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
-  } else if (epi == EPI_QKV) {
-    gemm_u4_kernel<EPI_QKV><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
-  } else if (epi == EPI_ROPE) {
-#if QMM_BITS == 4
-    gemm_u4_kernel<EPI_ROPE><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
-#else
-    return 2;  // the rotary epilogue is built for 4-bit codes only
-#endif
-  } else {
-    gemm_u4_kernel<EPI_SWIGLU><<<grid, block, 0, s>>>(a, m_tiles, n_tiles, per_xcd);
+  const int64_t cus = device_cus();
+  const int64_t rem = tiles % cus;
+  if (kSplitTail && tiles > cus && rem > 0 && 2 * rem <= cus) {
+    if (int st = launch_tiles(epi, false, a, m_tiles, 0, tiles - rem, s)) return st;
+    return launch_tiles(epi, true, a, m_tiles, tiles - rem, rem, s);
   }
-  return hipGetLastError() == hipSuccess ? 0 : 6;
+  return launch_tiles(epi, false, a, m_tiles, 0, tiles, s);
 }
 
 }  // namespace QMM_BITS_NS
