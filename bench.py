@@ -207,6 +207,11 @@ class Timer:
         return ms
 
 
+def _progress(msg):
+    """One line per finished leg on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = _args()
     if args.summarize_counters:
@@ -293,6 +298,7 @@ def main():
     ms_total = T.replay_ms(g_step)
     del g_step
     ms_per_step = ms_total / args.steps
+    _progress(f"headline step: {ms_per_step * 1e3:.2f} us")
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     # one launch per step: the step kernel's average launch duration is the step time
 
@@ -305,6 +311,7 @@ def main():
 
     copy_gbs = device_copy_gbs(torch, dev)
     read_ceiling = hbm_read_ceiling(torch, dev, T)
+    _progress("per-call kernels and read ceilings done")
 
     result = {
         "metric": "achieved HBM GB/s (% of peak) fused u4 GEMV M=1; prefill GEMM TFLOP/s",
@@ -346,22 +353,31 @@ def main():
 
     if not args.headline_only:
         result["mfma_ceiling"] = mfma_ceiling(torch, dev, T)
+        _progress("mfma_ceiling done")
         result["qkv_rope"] = bench_rope(torch, qmm, synth, T, dev, pq, args.prefill_reps)
+        _progress("qkv_rope done")
         result["prefill_gemm"] = bench_prefill(torch, qmm, synth, T, dev, pq, pg, args.prefill_reps)
+        _progress("prefill_gemm done")
         result["small_batch"] = bench_small_batch(torch, qmm, synth, T, dev, pq, pg)
+        _progress("small_batch done")
         del pq, pg
         torch.cuda.empty_cache()
         result["decode_24B_step"] = bench_step_24b(torch, qmm, synth, T, dev, args.step24_steps)
+        _progress("decode_24B_step done")
         torch.cuda.empty_cache()
         result["moe_35B_layer"] = bench_moe(torch, qmm, synth, T, dev, args.moe_steps)
+        _progress("moe_35B_layer done")
         torch.cuda.empty_cache()
         result["moe_35B_prefill"] = bench_moe_prefill(torch, qmm, synth, T, dev, args.prefill_reps)
+        _progress("moe_35B_prefill done")
         torch.cuda.empty_cache()
         result["formats"] = bench_formats(torch, qmm, synth, T, dev, args.prefill_reps)
+        _progress("formats done")
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_steps, w_qkv, w_gu, bytes_step)
+        _progress("cpu_baseline done")
 
     print(json.dumps(result), flush=True)
 
