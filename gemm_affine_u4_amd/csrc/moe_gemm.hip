@@ -8,8 +8,8 @@
 // the kernel is built so that each weight is read and dequantized exactly once per routing
 // tile, and the activations of the tile's pairs are what is shared through LDS.
 //
-// A block (4 waves) takes one routing tile (up to 96 pairs of one expert) and one slab of
-// 128 of the expert's weight rows, and walks K one 64-wide group per step:
+// A block (8 waves) takes one routing tile (up to 96 pairs of one expert) and one slab of
+// 256 of the expert's weight rows, and walks K one 64-wide group per step:
 //   * each wave owns 32 weight rows and holds them, dequantized, as the A operand of
 //     v_mfma_f32_32x32x16_bf16: lane l reads 16 bytes (32 codes) of row l % 32 per step,
 //     half l / 32 of the group, and turns them into w = s*q + b in fp32, rounded to bf16
@@ -35,8 +35,17 @@ namespace moe_mm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;                      // waves per block
+#ifndef QMM_MOE_WAVES
+#define QMM_MOE_WAVES 8
+#endif
+constexpr int kWaves = QMM_MOE_WAVES;          // waves per block (4 or 8)
 constexpr int kSlab = 32 * kWaves;             // weight rows per block
+static_assert(kWaves == 4 || kWaves == 8, "waves per block");
+// activation load instructions per wave and step for a tile of MB blocks of 32 pairs: the
+// tile's 4 MB groups of 8 rows spread over the waves (with 8 waves and an odd MB some waves
+// also load a group another wave loads, the same bytes into the same slot)
+template <int MB>
+constexpr int x_loads() { return (4 * MB + kWaves - 1) / kWaves; }
 constexpr int kMaxMB = kMoeTileRows / 32;      // 32-pair blocks per routing tile
 constexpr int kRow = 64;                       // bf16 per LDS row (one group of one pair)
 constexpr int kXcds = 8;
@@ -66,15 +75,20 @@ constexpr int kCodeBuf = kSlab * kCodeRow;  // bytes per code chunk buffer
 // LDS of a block: the activation stages (MB * 4 KB each) and the code chunk ring, whose depth
 // depends on the tile: 4 chunks (requested 5-6 steps ahead) where the stages leave room, else
 // 3 or 2.
-// LDS pool and blocks per CU: 40 KB and 4 (16 waves per CU, at most 128 registers each;
-// tiles of up to 96 pairs, whose activation stages leave room for a code ring) measured
-// 1-10 us per layer faster than 48 KB and 3 with tiles of up to 128 pairs, and 5 blocks
-// of 32 KB (96 registers: spills) slower.
+// Waves per block, LDS pool and blocks per CU: 8 waves (256 weight rows), 56 KB and 2 (16
+// waves per CU, at most 128 registers each; the smallest pool the largest tile fits, so the
+// code ring is 2 chunks deep for tiles of 33-96 pairs and 3 below) measured 10-13 us per
+// 35B-A3B layer at 2048 tokens faster than 4 waves (128 rows) with 40 KB and 4 blocks: the
+// 8 waves share one copy of the tile's activations per step, and there are half as many
+// blocks, each paying its lookup, prologue and epilogue once.  64 and 72 KB pools (deeper
+// code rings) measured 2-6 us slower than 56, 80 KB no faster than 4 waves.  With 4 waves:
+// 40 KB and 4 blocks measured 1-10 us per layer faster than 48 KB and 3 with tiles of up
+// to 128 pairs, and 5 blocks of 32 KB (96 registers: spills) slower.
 #ifndef QMM_MOE_LDS_KB
-#define QMM_MOE_LDS_KB 40
+#define QMM_MOE_LDS_KB 56
 #endif
 #ifndef QMM_MOE_BLOCKS_PER_CU
-#define QMM_MOE_BLOCKS_PER_CU 4
+#define QMM_MOE_BLOCKS_PER_CU 2
 #endif
 constexpr int kLds = QMM_MOE_LDS_KB * 1024;
 constexpr int kBlocksPerCU = QMM_MOE_BLOCKS_PER_CU;
@@ -187,7 +201,7 @@ constexpr bool chunk_step(int t) { return SC8 && ((t + kSDist) % kChunk + kChunk
 template <bool SC8>
 constexpr int tail_loads(int t) { return SC8 ? (chunk_step<SC8>(t) ? 2 : 0) : 2; }
 template <int MB, bool SC8>
-constexpr int step_loads(int t) { return MB + 1 + tail_loads<SC8>(t); }
+constexpr int step_loads(int t) { return x_loads<MB>() + 1 + tail_loads<SC8>(t); }
 // At the top of step ks (position P in the unrolled loop; P and ks agree modulo 8) its
 // activations (requested at step ks - kXDist) and its code chunk (both halves, the later
 // one at step 2 floor(ks/2) - 1) must have landed; loads complete in order, so what may
@@ -256,7 +270,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   const uint32_t goff = uint32_t(weight_row(m)) * groups * 2u;  // the lane's row's scales
 
   // Codes: global -> LDS, a chunk of two steps (64 bytes of a row) at a time, into a ring of
-  // NC buffers of the block's 128 rows x 64 bytes.  At step t a wave requests half (rows
+  // NC buffers of the block's kSlab rows x 64 bytes.  At step t a wave requests half (rows
   // 16 (t % 2) .. +15 of its 32) of chunk t/2 + NC - 1: lane L takes row 16 (t % 2) + L / 4 and
   // lands in slot L % 4 of it, which holds the row's 16-byte piece (L % 4) ^ cswz(row), so
   // that the 16 rows an operand read spans (at one piece) hit distinct bank groups.  A wave
@@ -293,14 +307,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   };
 
   // ---- the tile's activation rows: global -> LDS ------------------------------------
-  // Instruction j (j < MB) of wave w fills LDS rows 8 (MB w + j) + L / 8, slot L % 8 (lane
-  // L lands at byte 16 L), i.e. chunk (L % 8) ^ swz(row) of that pair's row.  Rows past the
-  // tile's pairs read its last pair (never stored).
+  // Instruction j (j < x_loads) of wave w fills the LDS rows of group xgroup(w, j): rows
+  // 8 group + L / 8, slot L % 8 (lane L lands at byte 16 L), i.e. chunk (L % 8) ^ swz(row)
+  // of that pair's row.  Rows past the tile's pairs read its last pair (never stored).
+  constexpr int JX = x_loads<MB>();
+  auto xgroup = [&](int j) -> int { return kWaves == 4 ? MB * wave + j : (wave + kWaves * j) % (4 * MB); };
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, uint64_t(a.M) * K * 2);
-  uint32_t xoff[MB];
+  uint32_t xoff[JX];
 #pragma unroll
-  for (int j = 0; j < MB; ++j) {
-    const int r = 8 * (MB * wave + j) + (lane >> 3);
+  for (int j = 0; j < JX; ++j) {
+    const int r = 8 * xgroup(j) + (lane >> 3);
     const int64_t xrow = jb.pairs[min(r, jb.P - 1)] / a.moe_div;
     const uint32_t chunk = uint32_t(lane & 7) ^ swz(uint32_t(r));
     xoff[j] = uint32_t(xrow) * K * 2u + chunk * 16u;
@@ -316,9 +332,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs& a, const TileJob& jb, 
   auto stage = [&](int p) -> uint16_t* { return xs_all + p * (kXStageBytes / 2); };
   auto load_x = [&](uint16_t* dst, int ks) {
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
+    for (int j = 0; j < JX; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (__attribute__((address_space(3))) void*)(dst + 8 * (MB * wave + j) * kRow), 16, xoff[j],
+          xr, (__attribute__((address_space(3))) void*)(dst + 8 * xgroup(j) * kRow), 16, xoff[j],
           uint32_t(ks) * 128u, 0, 0);
   };
 
@@ -504,7 +520,8 @@ __device__ __forceinline__ void zero_unrouted(const GemmArgs& a, int64_t q, int6
 // knows) spread over all eight.  The tile is known from the block index alone, so the
 // table's length, the record head and the pair indices come in one memory round trip.
 template <int EPI>
-__global__ void __launch_bounds__(256, kBlocksPerCU) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
+// (the second bound is the waves per SIMD: kBlocksPerCU blocks of kWaves waves over 4 SIMDs)
+__global__ void __launch_bounds__(64 * kWaves, kBlocksPerCU * kWaves / 4) moe_gemm_kernel(GemmArgs a, int64_t slabs) {
   // one LDS object: with a second one beside the pool the compiler waits for the pool's
   // direct-to-LDS loads before every LDS read (vmcnt), which undoes the prefetch
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds + (kPairsInPool ? 0 : kMoeTileRows * 4)];
