@@ -38,9 +38,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #ifndef QMM_MOE_WAVES
 #define QMM_MOE_WAVES 8
 #endif
-constexpr int kWaves = QMM_MOE_WAVES;          // waves per block (4 or 8)
+constexpr int kWaves = QMM_MOE_WAVES;          // waves per block (4, 8 or 16)
 constexpr int kSlab = 32 * kWaves;             // weight rows per block
-static_assert(kWaves == 4 || kWaves == 8, "waves per block");
+static_assert(kWaves == 4 || kWaves == 8 || kWaves == 16, "waves per block");
 // activation load instructions per wave and step for a tile of MB blocks of 32 pairs: the
 // tile's 4 MB groups of 8 rows spread over the waves (with 8 waves and an odd MB some waves
 // also load a group another wave loads, the same bytes into the same slot)
@@ -81,7 +81,10 @@ constexpr int kCodeBuf = kSlab * kCodeRow;  // bytes per code chunk buffer
 // 35B-A3B layer at 2048 tokens faster than 4 waves (128 rows) with 40 KB and 4 blocks: the
 // 8 waves share one copy of the tile's activations per step, and there are half as many
 // blocks, each paying its lookup, prologue and epilogue once.  64 and 72 KB pools (deeper
-// code rings) measured 2-6 us slower than 56, 80 KB no faster than 4 waves.  With 4 waves:
+// code rings) measured 2-6 us slower than 56, 80 KB no faster than 4 waves; 16 waves (512
+// rows, one block per CU, 88 or 120 KB) 15-30 us slower; with 8 waves, routing tiles of up
+// to 128 pairs (64 or 72 KB) 10-20 us and of up to 64 (48 or 56 KB) 5-15 us slower than of
+// up to 96.  With 4 waves:
 // 40 KB and 4 blocks measured 1-10 us per layer faster than 48 KB and 3 with tiles of up
 // to 128 pairs, and 5 blocks of 32 KB (96 registers: spills) slower.
 #ifndef QMM_MOE_LDS_KB
