@@ -548,12 +548,37 @@ static bool two_x_per_block(const qmm_step_proj* projs, const std::vector<int>& 
   return true;
 }
 
-// Grid of each launch and, for single-slice launches, whether the LDS variant runs it; the
-// same at planning and at every run (the plan's per-block tables are for this grid).
+// Grid of each launch and, for single-slice launches, whether the LDS variant runs it and the
+// dynamic LDS that holds it to two blocks per CU (0: as many as the registers allow); the same
+// at planning and at every run (the plan's per-block tables are for this grid).
 struct Geometry {
   int64_t units, blocks;
   bool lds;
+  size_t pad;
 };
+
+// Long single-slice launches run two blocks (8 waves) per CU instead of three: measured on
+// MI355X with QKV + gate+up of L 24B-shaped layers per launch (K = 5120), three blocks per CU
+// are faster up to 412 MB per launch (206 MB: 41.9 against 43.5-44.3 us), two from 826 MB on
+// (137-139 against 142 us; 8.26 GB: 1.263 against 1.327 ms, 6.54 against 6.22 TB/s).  The
+// switch is at kLongUnitsPerWave positions per wave at three blocks per CU (~560 MB at K =
+// 5120); the 14B-shaped step (100 MB, ~6 per wave) keeps three.
+constexpr int64_t kLongUnitsPerWave = 32;
+constexpr size_t kLongBlockLds = 64 * 1024;  // a block's LDS with the padding: 2 per CU fit, 3 do not
+
+// Dynamic LDS that makes a block of kernel k take kLongBlockLds, or 0 if that does not leave
+// exactly two blocks per CU (then the launch keeps its register-bound occupancy).
+template <typename Kernel>
+static size_t long_pad(Kernel k) {
+  hipFuncAttributes at{};
+  if (hipFuncGetAttributes(&at, reinterpret_cast<const void*>(k)) != hipSuccess || at.sharedSizeBytes >= kLongBlockLds)
+    return 0;
+  const size_t pad = kLongBlockLds - at.sharedSizeBytes;
+  int b = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, k, 64 * kWavesPerBlockSingle, pad) != hipSuccess || b != 2)
+    return 0;
+  return pad;
+}
 
 static std::vector<Geometry> geometry(const qmm_step_proj* projs, const std::vector<Shape>& sh,
                                       const std::vector<HostLaunch>& launches) {
@@ -562,6 +587,10 @@ static std::vector<Geometry> geometry(const qmm_step_proj* projs, const std::vec
   static const int64_t bpc_s8 = blocks_per_cu(gemv_step_split_kernel<8, false>, 512, 2);
   static const int64_t bpc_s8w = blocks_per_cu(gemv_step_split_kernel<8, true>, 512, 1);
   static const int64_t bpc_s16 = blocks_per_cu(gemv_step_split_kernel<16, false>, 1024, 1);
+  static const size_t pad_lds = long_pad(gemv_step_single_kernel<true>);
+  static const size_t pad_mem = long_pad(gemv_step_single_kernel<false>);
+  static const size_t pad_lds_in = long_pad(gemv_step_single_inline_kernel<true>);
+  static const size_t pad_mem_in = long_pad(gemv_step_single_inline_kernel<false>);
   const int64_t cus = device_cus();
   std::vector<Geometry> g(launches.size());
   for (size_t l = 0; l < launches.size(); ++l) {
@@ -569,13 +598,23 @@ static std::vector<Geometry> geometry(const qmm_step_proj* projs, const std::vec
     for (int i : launches[l].projs) units += sh[i].units;
     g[l].units = units;
     g[l].lds = false;
+    g[l].pad = 0;
     const int kind = launches[l].kind;
     if (kind == kSingle) {
-      // every wave of the grid resident at once, but no more waves than positions
+      // every wave of the grid resident at once, but no more waves than positions; long
+      // launches two blocks per CU (the padding holds them there)
       const int64_t need = (units + kWavesPerBlockSingle - 1) / kWavesPerBlockSingle;
-      int64_t blocks = std::min(cus * bpc_lds, need);
+      const bool inl = launches[l].projs.size() <= size_t(kInlineProjs);
+      const bool lng = units >= kLongUnitsPerWave * cus * bpc_lds * kWavesPerBlockSingle;
+      const size_t pl = lng ? (inl ? pad_lds_in : pad_lds) : 0, pm = lng ? (inl ? pad_mem_in : pad_mem) : 0;
+      int64_t blocks = std::min(cus * (pl ? 2 : bpc_lds), need);
       g[l].lds = two_x_per_block(projs, launches[l].projs, sh, blocks);
-      if (!g[l].lds) blocks = std::min(cus * bpc_mem, need);
+      if (g[l].lds) {
+        g[l].pad = pl;
+      } else {
+        blocks = std::min(cus * (pm ? 2 : bpc_mem), need);
+        g[l].pad = pm;
+      }
       g[l].blocks = blocks;
     } else {
       const int64_t bpc = kind == kSplit8 ? bpc_s8 : (kind == kSplit8Wide ? bpc_s8w : bpc_s16);
@@ -730,8 +769,8 @@ int launch(const qmm_step_proj* projs, int n, const void* plan, hipStream_t s) {
       il.n_seg = int32_t(ids.size());
       if (kind == kSingle) {
         const dim3 block{64u * kWavesPerBlockSingle, 1u, 1u};
-        if (geo[l].lds) gemv_step_single_inline_kernel<true><<<grid, block, 0, s>>>(il, per, extra);
-        else gemv_step_single_inline_kernel<false><<<grid, block, 0, s>>>(il, per, extra);
+        if (geo[l].lds) gemv_step_single_inline_kernel<true><<<grid, block, geo[l].pad, s>>>(il, per, extra);
+        else gemv_step_single_inline_kernel<false><<<grid, block, geo[l].pad, s>>>(il, per, extra);
       } else if (kind == kSplit8) {
         gemv_step_split_inline_kernel<8, false><<<grid, dim3{512u, 1u, 1u}, 0, s>>>(il, per, extra);
       } else if (kind == kSplit8Wide) {
@@ -745,8 +784,8 @@ int launch(const qmm_step_proj* projs, int n, const void* plan, hipStream_t s) {
       const BlockSegs* bk = reinterpret_cast<const BlockSegs*>(pl + lay.blk_off) + blk0;
       if (kind == kSingle) {
         const dim3 block{64u * kWavesPerBlockSingle, 1u, 1u};
-        if (geo[l].lds) gemv_step_single_kernel<true><<<grid, block, 0, s>>>(pj, sg, bk, per, extra);
-        else gemv_step_single_kernel<false><<<grid, block, 0, s>>>(pj, sg, bk, per, extra);
+        if (geo[l].lds) gemv_step_single_kernel<true><<<grid, block, geo[l].pad, s>>>(pj, sg, bk, per, extra);
+        else gemv_step_single_kernel<false><<<grid, block, geo[l].pad, s>>>(pj, sg, bk, per, extra);
       } else if (kind == kSplit8) {
         gemv_step_split_kernel<8, false><<<grid, dim3{512u, 1u, 1u}, 0, s>>>(pj, sg, bk, per, extra);
       } else if (kind == kSplit8Wide) {

@@ -119,7 +119,9 @@ def dense_step_projs(layers, sh, xd, outs):
 
 def test_24B_step_with_down_waiting_for_h():
     """Three 24B-dense-shaped layers in one run (two launches): each layer's down projection
-    (K = 32768, split over 8 waves) reads the h its layer's gate+up wrote in the same run."""
+    (K = 32768, split over 8 waves) reads the h its layer's gate+up wrote in the same run.
+    The first launch (QKV and gate+up of three layers, 107520 positions, 620 MB) is a long
+    launch, which the planner runs at two blocks per CU on a 256-CU GPU."""
     sh = synth.DENSE_24B
     L = 3
     layers = [Layer(sh, synth.CFG_24B, l) for l in range(L)]
