@@ -181,10 +181,11 @@ __device__ __forceinline__ void x_from_lds(uint32_t xp[CPL][16], float xs[CPL], 
   }
 }
 
-// This wave's positions [p, end) of one projection (positions = row units, the projection's
-// first at seg_begin), with the activations from the block's LDS copy xl (LDS_X) or from
-// memory.  `before_x` runs once the first unit's weights are requested and before the
-// activations are read (the block's staging, on the wave's first projection).  Returns end.
+// This wave's positions p, p + 4, ... below end of one projection (positions = row units,
+// the projection's first at seg_begin), with the activations from the block's LDS copy xl
+// (LDS_X) or from memory.  `before_x` runs once the first unit's weights are requested and
+// before the activations are read (the block's staging, on the wave's first projection).
+// Returns the wave's first position at or past end.
 template <int CPL, bool SWIGLU, bool LDS_X, typename BeforeX>
 __device__ __forceinline__ int64_t run_single(const Proj P, int64_t p, int64_t seg_begin, int64_t end,
                                               const uint32_t* xl, BeforeX&& before_x) {
@@ -212,11 +213,12 @@ __device__ __forceinline__ int64_t run_single(const Proj P, int64_t p, int64_t s
   float xs[CPL];
   if constexpr (LDS_X) x_from_lds<CPL>(xp, xs, xl, c0);
   else load_x<CPL>(xp, xs, make_rsrc(uni_ptr(P.x), uint64_t(uni(P.K)) * 2), c0);
-  for (; p < end; ++p, ++u) {
+  constexpr int64_t W = kWavesPerBlockSingle;  // the block's waves take its positions in turn
+  for (; p < end; p += W, u += uint32_t(W)) {
     const float v = slot_reduce<LPR>(unit_partial<CPL>(buf, xp, xs, magic));
-    if (p + 1 < end) {
+    if (p + W < end) {
       bool valid;
-      const uint32_t r = unit_row<SWIGLU>(P, u + 1, slot, &valid);
+      const uint32_t r = unit_row<SWIGLU>(P, u + uint32_t(W), slot, &valid);
       load_unit<CPL>(buf, cr, sr, br, valid ? r : 0u, row_bytes, row_groups, c0);
     }
     bool valid;
@@ -228,7 +230,7 @@ __device__ __forceinline__ int64_t run_single(const Proj P, int64_t p, int64_t s
       if (valid && result_lane) store_qkv(P, r, P.lin_bias ? v + bf16_bits_to_f32(P.lin_bias[r]) : v);
     }
   }
-  return end;
+  return p;
 }
 
 // Where a launch's projections come from.  TableSrc: the plan's tables in device memory
@@ -263,8 +265,11 @@ struct InlineSrc {
   __device__ __forceinline__ int last_seg(int64_t p1) const { return seg_of(p1 - 1); }
 };
 
-// One single-slice launch: the positions spread evenly over the grid's waves in contiguous
-// ranges (`per` each, the first `extra` waves one more).  LDS_X: the block first stages, once,
+// One single-slice launch: the positions spread evenly over the grid's blocks in contiguous
+// ranges (`per` per wave, the first `extra` waves one more, summed over the block's waves),
+// which the block's 4 waves take in turn (wave w: the range's positions w, w + 4, ...; at any
+// time the block reads 4 adjacent row units: measured 0.3-0.5 % faster than a contiguous
+// range per wave, on the 14B and the 24B steps).  LDS_X: the block first stages, once,
 // the activations of the (at most two) projections its waves start and end in, and the
 // planner takes this variant only where no block's range reaches a third activation vector;
 // else every wave reads its activations from memory at each projection it enters.  (One
@@ -274,9 +279,8 @@ __device__ __forceinline__ void single_body(const Src& src, int64_t per, int64_t
   __shared__ __attribute__((aligned(16))) uint32_t xl[LDS_X ? 2 : 1][LDS_X ? kXWords : 4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto first_of = [&](int64_t gw) { return gw * per + (gw < extra ? gw : extra); };
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlockSingle + wave;
-  int64_t p = uni64(first_of(w));
-  const int64_t pend = uni64(first_of(w + 1));
+  int64_t p = uni64(first_of(int64_t(blockIdx.x) * kWavesPerBlockSingle)) + wave;
+  const int64_t pend = uni64(first_of(int64_t(blockIdx.x + 1) * kWavesPerBlockSingle));
   const int64_t bp0 = first_of(int64_t(blockIdx.x) * kWavesPerBlockSingle);
   const int64_t bp1 = first_of(int64_t(blockIdx.x + 1) * kWavesPerBlockSingle);
   // the segments of the block's first and last positions (the projections whose
